@@ -1,0 +1,29 @@
+"""fp64 CPU oracle of the gated delta rule.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute anything in this package: only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with
+the HIP path (no kernels, headers, helpers, tables or pre/post-processing).
+
+Sources (cited by page title and section):
+  * "Gated Delta Networks: Improving Mamba2 with Delta Rule" (paper review),
+    sections "Method", "Key idea", "Background", "Goal" -- the recurrence,
+    its two limits and the test-time-SGD reading.
+  * "Linear Attention Architectures: Mechanisms, Trade-offs, and Cross-Layer
+    Routing" (abstract) -- names the per-channel (Kimi-Delta-style) gate
+    without defining it.
+
+Parity status per function is listed in ``gdn_oracle.__doc__``.
+"""
+
+from .gdn_oracle import (  # noqa: F401
+    gdn_fwd,
+    gdn_fwd_chain,
+    gdn_decode,
+    gdn_bwd,
+    gdn_bwd_chain,
+    gdn_chunked_bruteforce,
+    gdn_sgd_form,
+    delta_rule_ungated,
+    normwise_rel_err,
+)

@@ -1,0 +1,347 @@
+"""Plain fp64 numpy oracle of the gated delta rule (TEST INFRASTRUCTURE).
+
+Only tests, the smoke check and the CPU-baseline leg of the benchmark may use
+this module; the HIP library never does.  Every function works on fp64 numpy
+arrays that are exact upcasts of the values handed to the GPU.
+
+Definition followed ("Gated Delta Networks: Improving Mamba2 with Delta Rule",
+paper review, section "Method"): the state update is
+
+    S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+
+with S_t of shape dv x dk (the write v k^T fixes the orientation).  The state
+is stored transposed, M = S^T (dk x dv), and the per-token step reads
+
+    Mt  = a_t * M_{t-1}                      (a_t = exp(log alpha_t))
+    e_t = beta_t (v_t - Mt^T k_t)
+    M_t = Mt + k_t e_t^T
+    o_t = M_t^T q_t                          (output of the updated state)
+
+Readings where the pages are silent (each is listed in the design notes):
+  * the output o_t = S_t q_t is read with the updated state, no 1/sqrt(dk)
+    scale (the pages never write the output);
+  * the gate arrives as log alpha; alpha_t decays the old state before the
+    rank-1 correction and the fresh write beta v k^T is not decayed ("Method":
+    decay is applied before the correction; "Key idea": alpha -> 0 erases);
+  * the per-channel (Kimi-Delta-style) gate puts Diag(alpha_t) in place of the
+    scalar: it scales the dk rows of M.  Parity with any external definition
+    of that gate is UNPINNED (the pages only name it); the pins fix that the
+    all-equal-channels case equals the scalar gate.
+  * the backward is the gradient of <dO, o> + <dS_final, S_final> with respect
+    to q, k, v, beta, log alpha and S_0 (the pages give no backward).
+
+Parity pins (tests/test_oracle_pins.py): chunked brute-force form, orthonormal
+retrieval, beta = 0 gate product, DeltaNet limit, norm bound, alpha -> 0
+erasure, gated-linear-attention limit, SGD reading, T = 1 closed form,
+equal-channel reduction, boundary semantics, finite differences for the
+adjoint, plus a hand-worked golden example.  Nothing here is "parity
+unpinned" except the per-channel gate's match to an external definition.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GATES = ("none", "scalar", "channel")
+
+
+# --------------------------------------------------------------------------
+# helpers (no method arithmetic)
+# --------------------------------------------------------------------------
+
+def _segments(B: int, T: int, cu_seqlens):
+    """Yield (b, start, end, seq_index) for dense [B,T] or varlen packing."""
+    if cu_seqlens is None:
+        for b in range(B):
+            yield b, 0, T, b
+    else:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        assert B == 1 and cu[0] == 0 and cu[-1] == T
+        for n in range(len(cu) - 1):
+            yield 0, int(cu[n]), int(cu[n + 1]), n
+
+
+def _gate_rows(log_alpha_t, gate: str, dk: int):
+    """Per-row multiplier of the state for one token (vector of length dk)."""
+    if gate == "none":
+        return np.ones(dk)
+    if gate == "scalar":
+        return np.full(dk, np.exp(float(log_alpha_t)))
+    if gate == "channel":
+        return np.exp(np.asarray(log_alpha_t, dtype=np.float64))
+    raise ValueError(gate)
+
+
+def normwise_rel_err(x, y, floor_frac: float = 1e-30):
+    """max over leading slices of max|x-y| / max|y| (see README of tests).
+
+    ``x`` and ``y`` have the same shape; the error is evaluated per slice of the
+    last two axes when they exist.  A slice whose reference is below 1e-30 is
+    judged by absolute error relative to the global max |y|.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    assert x.shape == y.shape, (x.shape, y.shape)
+    if x.size == 0:
+        return 0.0
+    gmax = float(np.max(np.abs(y)))
+    if x.ndim <= 2:
+        x2, y2 = x.reshape(1, -1), y.reshape(1, -1)
+    else:
+        x2 = x.reshape(-1, x.shape[-2] * x.shape[-1])
+        y2 = y.reshape(-1, y.shape[-2] * y.shape[-1])
+    worst = 0.0
+    for xs, ys in zip(x2, y2):
+        ref = float(np.max(np.abs(ys)))
+        diff = float(np.max(np.abs(xs - ys)))
+        if not np.isfinite(diff):
+            return float("inf")
+        if ref < floor_frac:
+            err = diff / gmax if gmax > 0 else diff
+        else:
+            err = diff / ref
+        worst = max(worst, err)
+    return worst
+
+
+# --------------------------------------------------------------------------
+# forward: the token-by-token recurrence ("Method")
+# --------------------------------------------------------------------------
+
+def gdn_fwd_chain(q, k, v, beta, log_alpha, m0, gate: str):
+    """One (sequence, head): q,k [T,dk], v [T,dv], beta [T], log_alpha [T] /
+    [T,dk] / None, m0 [dk,dv].  Returns (o [T,dv], M_T [dk,dv])."""
+    T, dk = k.shape
+    dv = v.shape[1]
+    M = np.array(m0, dtype=np.float64, copy=True)
+    o = np.zeros((T, dv))
+    for t in range(T):
+        a = _gate_rows(None if log_alpha is None else log_alpha[t], gate, dk)
+        Mt = a[:, None] * M                      # decay the old state first
+        e = beta[t] * (v[t] - Mt.T @ k[t])       # error of the decayed state
+        M = Mt + np.outer(k[t], e)               # rank-1 delta correction
+        o[t] = M.T @ q[t]                        # read the updated state
+    return o, M
+
+
+def gdn_fwd(q, k, v, beta, log_alpha, s0=None, gate: str = "scalar",
+            cu_seqlens=None):
+    """Whole batch.  q,k [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H];
+    log_alpha [B,T,H] (scalar), [B,T,H,dk] (channel) or None (gate none);
+    s0 [B|N,H,dk,dv] or None (zeros).  cu_seqlens [N+1] packs N sequences
+    into B = 1.  Returns o [B,T,H,dv] and s_final [B|N,H,dk,dv]."""
+    assert gate in GATES
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    nseq = B if cu_seqlens is None else len(cu_seqlens) - 1
+    o = np.zeros((B, T, H, dv))
+    sf = np.zeros((nseq, H, dk, dv))
+    for b, t0, t1, n in _segments(B, T, cu_seqlens):
+        for h in range(H):
+            m0 = np.zeros((dk, dv)) if s0 is None else s0[n, h]
+            la = None if gate == "none" else log_alpha[b, t0:t1, h]
+            o[b, t0:t1, h], sf[n, h] = gdn_fwd_chain(
+                q[b, t0:t1, h], k[b, t0:t1, h], v[b, t0:t1, h],
+                beta[b, t0:t1, h], la, m0, gate)
+    return o, sf
+
+
+def gdn_decode(q, k, v, beta, log_alpha, state, gate: str = "scalar"):
+    """One token per (sequence, head): q,k [N,H,dk], v [N,H,dv], beta [N,H],
+    log_alpha [N,H] / [N,H,dk] / None, state [N,H,dk,dv].  Returns
+    (o [N,H,dv], new state); the input state is not modified."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((N, H, dv))
+    new = np.array(state, dtype=np.float64, copy=True)
+    for n in range(N):
+        for h in range(H):
+            la = None if gate == "none" else log_alpha[n, h][None]
+            oo, mm = gdn_fwd_chain(q[n, h][None], k[n, h][None], v[n, h][None],
+                                   beta[n, h][None], la, state[n, h], gate)
+            o[n, h] = oo[0]
+            new[n, h] = mm
+    return o, new
+
+
+# --------------------------------------------------------------------------
+# independent forms used only to pin the recurrence
+# --------------------------------------------------------------------------
+
+def delta_rule_ungated(q, k, v, beta, m0):
+    """Plain delta rule with no gate at all ("Key idea": alpha -> 1 recovers
+    the pure delta rule).  Written as an associative-memory update: read the
+    current value stored under key k, move it toward v by beta."""
+    M = np.array(m0, dtype=np.float64, copy=True)
+    o = np.zeros((k.shape[0], v.shape[1]))
+    for t in range(k.shape[0]):
+        stored = M.T @ k[t]
+        M = M + beta[t] * np.outer(k[t], v[t] - stored)
+        o[t] = M.T @ q[t]
+    return o, M
+
+
+def gdn_sgd_form(q, k, v, beta, log_alpha, m0, gate: str):
+    """Test-time-SGD reading ("Method"): the state is a fast weight decayed
+    by alpha_t (adaptive weight decay), then one gradient step of learning
+    rate beta_t on the loss 0.5 * ||Mt^T k_t - v_t||^2."""
+    T, dk = k.shape
+    M = np.array(m0, dtype=np.float64, copy=True)
+    o = np.zeros((T, v.shape[1]))
+    for t in range(T):
+        a = _gate_rows(None if log_alpha is None else log_alpha[t], gate, dk)
+        W = M * a[:, None]
+        residual = W.T @ k[t] - v[t]             # prediction error
+        grad = np.outer(k[t], residual)          # d/dW of 0.5*||W^T k - v||^2
+        M = W - beta[t] * grad
+        o[t] = M.T @ q[t]
+    return o, M
+
+
+def gdn_chunked_bruteforce(q, k, v, beta, log_alpha, m0, gate: str, C: int):
+    """Chunkwise form of one chain with an explicit dense inverse.
+
+    Within a chunk of c tokens, g is the inclusive chunk-local cumulative
+    log-gate, gamma = exp(g), and (scalar gate)
+        A_ri = beta_r exp(g_r - g_i) k_r.k_i   (i < r),  T = (I + A)^-1
+        U = T diag(beta) V,   W = T diag(beta*gamma) K,   E = U - W M0
+        O = diag(gamma) Q M0 + (Q K^T o Gamma) E,  Gamma_ri = exp(g_r-g_i), i<=r
+        M_c = gamma_c M0 + (K o exp(g_c - g))^T E
+    For the per-channel gate every exp(g_r - g_i) x.y becomes
+    sum_c x_c y_c exp(g_rc - g_ic) and gamma multiplies channels.
+    These equations are the unrolled recurrence (WY representation + UT
+    transform named in "Method"); this routine checks them, not the GPU.
+    """
+    T, dk = k.shape
+    dv = v.shape[1]
+    M = np.array(m0, dtype=np.float64, copy=True)
+    o = np.zeros((T, dv))
+    for s in range(0, T, C):
+        e_ = min(T, s + C)
+        c = e_ - s
+        K, Q, V, bt = k[s:e_], q[s:e_], v[s:e_], beta[s:e_]
+        if gate == "none":
+            g = np.zeros((c, dk))
+        elif gate == "scalar":
+            g = np.repeat(np.cumsum(log_alpha[s:e_])[:, None], dk, axis=1)
+        else:
+            g = np.cumsum(log_alpha[s:e_], axis=0)
+        # pairwise decays D[r,i,c] = exp(g_rc - g_ic) for i <= r, 0 otherwise
+        A = np.zeros((c, c))
+        P = np.zeros((c, c))
+        for r in range(c):
+            for i in range(r + 1):
+                d = np.exp(g[r] - g[i])
+                P[r, i] = np.sum(Q[r] * K[i] * d)
+                if i < r:
+                    A[r, i] = bt[r] * np.sum(K[r] * K[i] * d)
+        Tm = np.linalg.inv(np.eye(c) + A)
+        U = Tm @ (bt[:, None] * V)
+        W = Tm @ (bt[:, None] * K * np.exp(g))
+        E = U - W @ M
+        o[s:e_] = (Q * np.exp(g)) @ M + P @ E
+        M = np.exp(g[-1])[:, None] * M + (K * np.exp(g[-1][None, :] - g)).T @ E
+    return o, M
+
+
+# --------------------------------------------------------------------------
+# backward: adjoint of the token recurrence (derived by hand from "Method")
+# --------------------------------------------------------------------------
+
+def gdn_bwd_chain(q, k, v, beta, log_alpha, m0, do, dmT, gate: str,
+                  ckpt: int = 64):
+    """Adjoint of one chain.  Loss L = sum_t <dO_t, o_t> + <dmT, M_T>.
+
+    With D = Diag(a_t), P = I - beta_t k_t k_t^T, Mt = D M_{t-1} and
+    G = dL/dM_t (accumulated from the future):
+        G   += q_t dO_t^T
+        dq_t = M_t dO_t
+        dv_t = beta_t G^T k_t
+        dbeta_t = (G^T k_t) . (v_t - Mt^T k_t)
+        dk_t = -beta_t (G Mt^T + Mt G^T) k_t + beta_t G v_t
+        dla_t[i] = a_i sum_j (P G)_ij (M_{t-1})_ij   (scalar: summed over i)
+        G    = D P G
+    and dM_0 = G at the end.  States are checkpointed every ``ckpt`` tokens
+    and recomputed segment by segment in reverse.
+    Returns dq, dk, dv, dbeta, dla (None for gate none), dm0."""
+    T, dk = k.shape
+    dv = v.shape[1]
+    # forward pass storing checkpoints M_{s} at segment starts
+    starts = list(range(0, T, ckpt)) if T > 0 else []
+    ck = {}
+    M = np.array(m0, dtype=np.float64, copy=True)
+    for t in range(T):
+        if t % ckpt == 0:
+            ck[t] = M.copy()
+        a = _gate_rows(None if log_alpha is None else log_alpha[t], gate, dk)
+        Mt = a[:, None] * M
+        e = beta[t] * (v[t] - Mt.T @ k[t])
+        M = Mt + np.outer(k[t], e)
+    dq = np.zeros((T, dk))
+    dkk = np.zeros((T, dk))
+    dvv = np.zeros((T, dv))
+    db = np.zeros(T)
+    dla = None if gate == "none" else np.zeros(np.shape(log_alpha))
+    G = np.zeros((dk, dv)) if dmT is None else np.array(dmT, dtype=np.float64)
+    for s in reversed(starts):
+        e_ = min(T, s + ckpt)
+        # recompute the states of this segment: prev[t-s] = M_{t-1}
+        prev = []
+        M = ck[s].copy()
+        for t in range(s, e_):
+            prev.append(M.copy())
+            a = _gate_rows(None if log_alpha is None else log_alpha[t], gate, dk)
+            Mt = a[:, None] * M
+            e = beta[t] * (v[t] - Mt.T @ k[t])
+            M = Mt + np.outer(k[t], e)
+        post = prev[1:] + [M]                    # post[t-s] = M_t
+        for t in reversed(range(s, e_)):
+            Mprev = prev[t - s]
+            Mcur = post[t - s]
+            a = _gate_rows(None if log_alpha is None else log_alpha[t], gate, dk)
+            Mt = a[:, None] * Mprev
+            kt, vt, bt = k[t], v[t], beta[t]
+            G = G + np.outer(q[t], do[t])
+            dq[t] = Mcur @ do[t]
+            Gk = G.T @ kt
+            dvv[t] = bt * Gk
+            db[t] = Gk @ (vt - Mt.T @ kt)
+            dkk[t] = -bt * (G @ (Mt.T @ kt) + Mt @ (G.T @ kt)) + bt * (G @ vt)
+            PG = G - bt * np.outer(kt, kt @ G)
+            if gate == "scalar":
+                dla[t] = a[0] * np.sum(PG * Mprev)
+            elif gate == "channel":
+                dla[t] = a * np.sum(PG * Mprev, axis=1)
+            G = a[:, None] * PG
+    return dq, dkk, dvv, db, dla, G
+
+
+def gdn_bwd(q, k, v, beta, log_alpha, s0, do, ds_final=None,
+            gate: str = "scalar", cu_seqlens=None):
+    """Batch adjoint.  Shapes as in :func:`gdn_fwd`; do [B,T,H,dv];
+    ds_final [B|N,H,dk,dv] or None.  Returns dq, dk, dv, dbeta, dlog_alpha
+    (None for gate none) and ds0 (gradient w.r.t. the initial state, also
+    when s0 is None, i.e. zeros)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    nseq = B if cu_seqlens is None else len(cu_seqlens) - 1
+    dq = np.zeros_like(q, dtype=np.float64)
+    dk_ = np.zeros_like(k, dtype=np.float64)
+    dv_ = np.zeros_like(v, dtype=np.float64)
+    db = np.zeros_like(beta, dtype=np.float64)
+    dla = None if gate == "none" else np.zeros_like(log_alpha, dtype=np.float64)
+    ds0 = np.zeros((nseq, H, dk, dv))
+    for b, t0, t1, n in _segments(B, T, cu_seqlens):
+        for h in range(H):
+            m0 = np.zeros((dk, dv)) if s0 is None else s0[n, h]
+            la = None if gate == "none" else log_alpha[b, t0:t1, h]
+            dmT = None if ds_final is None else ds_final[n, h]
+            r = gdn_bwd_chain(q[b, t0:t1, h], k[b, t0:t1, h], v[b, t0:t1, h],
+                              beta[b, t0:t1, h], la, m0, do[b, t0:t1, h],
+                              dmT, gate)
+            dq[b, t0:t1, h], dk_[b, t0:t1, h], dv_[b, t0:t1, h] = r[0], r[1], r[2]
+            db[b, t0:t1, h] = r[3]
+            if dla is not None:
+                dla[b, t0:t1, h] = r[4]
+            ds0[n, h] = r[5]
+    return dq, dk_, dv_, db, dla, ds0

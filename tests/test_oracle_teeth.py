@@ -1,0 +1,141 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check
+that the pins catch every one of them.  The copy is made by editing the
+oracle's source text in memory; the oracle module itself is untouched."""
+
+import inspect
+import os
+import types
+
+import numpy as np
+import pytest
+
+import oracle.gdn_oracle as ref_mod
+import pins
+from test_oracle_pins import _read_golden
+
+SRC = inspect.getsource(ref_mod)
+
+
+def _mutant(old, new):
+    assert SRC.count(old) >= 1, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "<oracle_mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+def _golden_err(mod):
+    g = _read_golden("hand_worked_t2.txt")
+    T = len(g["beta"])
+    o, M = mod.gdn_fwd_chain(g["q"].reshape(T, 2), g["k"].reshape(T, 2),
+                             g["v"].reshape(T, 2), g["beta"], g["log_alpha"],
+                             np.zeros((2, 2)), "scalar")
+    return max(np.max(np.abs(o.reshape(-1) - g["o"])),
+               np.max(np.abs(M.reshape(-1) - g["M_final"])))
+
+
+def _forward_pins_pass(mod):
+    c = mod.gdn_fwd_chain
+    ok = _golden_err(mod) < 1e-12
+    for gate in ("scalar", "channel"):
+        ok &= pins.p2_orthonormal_retrieval(c, gate=gate) < 1e-12
+        ok &= pins.p3_gate_product(c, gate=gate) < 1e-12
+        ok &= pins.p6_erasure(c, gate=gate) < 1e-12
+        ok &= pins.p7_gla_limit(c, gate=gate) < 1e-12
+        ok &= pins.p9_single_token(c, gate=gate) < 1e-12
+        ok &= pins.p5_norm_bound(c, gate=gate) <= 1 + 1e-12
+    return bool(ok)
+
+
+FWD_MUTANTS = {
+    "write decayed with the state": (
+        "        M = Mt + np.outer(k[t], e)               # rank-1 delta correction\n",
+        "        M = a[:, None] * (M + np.outer(k[t], e))\n"),
+    "output read before the update": (
+        "        M = Mt + np.outer(k[t], e)               # rank-1 delta correction\n"
+        "        o[t] = M.T @ q[t]                        # read the updated state\n",
+        "        o[t] = Mt.T @ q[t]\n"
+        "        M = Mt + np.outer(k[t], e)\n"),
+    "transposed read": (
+        "        o[t] = M.T @ q[t]                        # read the updated state\n",
+        "        o[t] = (M @ q[t]) if M.shape[0] == M.shape[1] else M.T @ q[t]\n"),
+    "error of the undecayed state": (
+        "        e = beta[t] * (v[t] - Mt.T @ k[t])       # error of the decayed state\n",
+        "        e = beta[t] * (v[t] - M.T @ k[t])\n"),
+    "beta dropped from the error": (
+        "        e = beta[t] * (v[t] - Mt.T @ k[t])       # error of the decayed state\n",
+        "        e = (v[t] - Mt.T @ k[t])\n"),
+    "wrong sign of the correction": (
+        "        M = Mt + np.outer(k[t], e)               # rank-1 delta correction\n",
+        "        M = Mt - np.outer(k[t], e)\n"),
+    "gate exponent sign": (
+        "        return np.full(dk, np.exp(float(log_alpha_t)))\n",
+        "        return np.full(dk, np.exp(-float(log_alpha_t)))\n"),
+}
+
+
+def test_reference_oracle_passes_forward_pins():
+    assert _forward_pins_pass(ref_mod)
+
+
+@pytest.mark.parametrize("name", sorted(FWD_MUTANTS))
+def test_forward_mutant_is_caught(name):
+    mod = _mutant(*FWD_MUTANTS[name])
+    assert not _forward_pins_pass(mod), name
+
+
+def _adjoint_err(mod, gate):
+    r = pins.rng(31)
+    T, dk, dv = 6, 4, 3
+    q = pins.unit(r.standard_normal((1, T, 1, dk)))
+    k = pins.unit(r.standard_normal((1, T, 1, dk)))
+    v = r.standard_normal((1, T, 1, dv))
+    beta = 1.5 * r.random((1, T, 1))
+    la = -0.7 * r.random((1, T, 1)) if gate == "scalar" else -0.7 * r.random((1, T, 1, dk))
+    m0 = r.standard_normal((1, 1, dk, dv))
+    do = r.standard_normal((1, T, 1, dv))
+    dS = r.standard_normal((1, 1, dk, dv))
+    g = mod.gdn_bwd(q, k, v, beta, la, m0, do, dS, gate)
+    vals = [q, k, v, beta, la, m0]
+    worst = 0.0
+    h = 1e-6
+    for j, x in enumerate(vals):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = [y.copy() for y in vals]; xp[j][idx] += h
+            xm = [y.copy() for y in vals]; xm[j][idx] -= h
+            lp = ref_mod.gdn_fwd(*xp, gate=gate)
+            lm = ref_mod.gdn_fwd(*xm, gate=gate)
+            fd[idx] = (np.sum(do * (lp[0] - lm[0])) + np.sum(dS * (lp[1] - lm[1]))) / (2 * h)
+        worst = max(worst, np.max(np.abs(fd - g[j])) / np.max(np.abs(fd)))
+    return worst
+
+
+BWD_MUTANTS = {
+    "dk misses the state-transpose term": (
+        "            dkk[t] = -bt * (G @ (Mt.T @ kt) + Mt @ (G.T @ kt)) + bt * (G @ vt)\n",
+        "            dkk[t] = -bt * (G @ (Mt.T @ kt)) + bt * (G @ vt)\n"),
+    "dbeta uses the undecayed state": (
+        "            db[t] = Gk @ (vt - Mt.T @ kt)\n",
+        "            db[t] = Gk @ (vt - Mprev.T @ kt)\n"),
+    "state adjoint skips the projection": (
+        "            G = a[:, None] * PG\n",
+        "            G = a[:, None] * G\n"),
+    "dq reads the previous state": (
+        "            dq[t] = Mcur @ do[t]\n",
+        "            dq[t] = Mprev @ do[t]\n"),
+    "dlog-alpha misses the gate factor": (
+        "                dla[t] = a * np.sum(PG * Mprev, axis=1)\n",
+        "                dla[t] = np.sum(PG * Mprev, axis=1)\n"),
+}
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_reference_adjoint_passes(gate):
+    assert _adjoint_err(ref_mod, gate) < 1e-7
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_adjoint_mutant_is_caught(name):
+    mod = _mutant(*BWD_MUTANTS[name])
+    gate = "channel" if "gate factor" in name else "scalar"
+    assert _adjoint_err(mod, gate) > 1e-4, name
