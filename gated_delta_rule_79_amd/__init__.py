@@ -1,1 +1,166 @@
-"""libgdn: the gated delta rule on MI355X (gfx950) through a C ABI."""
+"""libgdn: the gated delta rule on AMD MI355X (gfx950), called through its C ABI.
+
+The three entry points mirror ``include/gdn.h``:
+
+  chunk_fwd(q, k, v, beta, log_alpha, s0=None, chunk=64, cu_seqlens=None)
+      -> (o, s_final)
+  chunk_bwd(q, k, v, beta, log_alpha, s0, d_o, ds_final=None, chunk=64,
+            cu_seqlens=None) -> (dq, dk, dv, dbeta, dlog_alpha, ds0)
+  decode_step(q, k, v, beta, log_alpha, state) -> o   (state updated in place)
+
+Tensors are torch CUDA tensors (HIP device memory); torch is used only to
+allocate outputs / workspaces and to name the current stream.  The gate mode
+follows ``log_alpha``: None = no decay (delta rule), one value per
+(token, head) = scalar gate, one value per key channel = per-channel gate.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import GdnError  # noqa: F401
+
+__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "GdnError", "abi_version"]
+
+_DT = {torch.float32: _lib.GDN_F32, torch.bfloat16: _lib.GDN_BF16}
+
+
+def abi_version() -> int:
+    return _lib.load().gdn_abi_version()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libgdn takes contiguous tensors")
+    return t.data_ptr() or None
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _gate_of(log_alpha, token_dims: int) -> int:
+    if log_alpha is None:
+        return _lib.GDN_GATE_NONE
+    return _lib.GDN_GATE_CHANNEL if log_alpha.dim() == token_dims + 1 else _lib.GDN_GATE_SCALAR
+
+
+def _problem(q, v, beta, log_alpha, chunk, cu_seqlens, gate=None):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    p = _lib.GdnProblem()
+    p.B, p.T, p.H, p.dk, p.dv, p.chunk = B, T, H, dk, dv, chunk
+    p.nseq = nseq
+    p.cu_seqlens = None if cu_seqlens is None else cu_seqlens.data_ptr()
+    p.io_dtype = _dtype_code(q)
+    p.gate_dtype = _dtype_code(beta)
+    p.gate = _gate_of(log_alpha, 3) if gate is None else gate
+    return p
+
+
+def _check_cu(cu_seqlens, q):
+    if cu_seqlens is None:
+        return
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must be an int32 tensor on the inputs' device")
+
+
+def chunk_fwd(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
+              cu_seqlens=None, output_final_state: bool = True,
+              workspace: Optional[torch.Tensor] = None):
+    """Chunkwise forward.  Returns (o, s_final or None)."""
+    lib = _lib.load()
+    _check_cu(cu_seqlens, q)
+    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
+    nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+    H, dk, dv = q.shape[2], q.shape[3], v.shape[3]
+    o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    sf = (torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+          if output_final_state else None)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.gdn_chunk_fwd_workspace(ctypes.byref(p), ctypes.byref(need)),
+               "gdn_chunk_fwd_workspace")
+    ws = workspace
+    if ws is None or ws.numel() < need.value:
+        ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    st = lib.gdn_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                           _ptr(log_alpha), _ptr(s0), _ptr(o), _ptr(sf),
+                           _ptr(ws), ws.numel(), _stream(q.device))
+    _lib.check(st, "gdn_chunk_fwd")
+    return o, sf
+
+
+def fwd_workspace_bytes(q, v, beta, log_alpha=None, chunk=64, cu_seqlens=None) -> int:
+    lib = _lib.load()
+    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.gdn_chunk_fwd_workspace(ctypes.byref(p), ctypes.byref(need)),
+               "gdn_chunk_fwd_workspace")
+    return need.value
+
+
+def chunk_bwd(q, k, v, beta, log_alpha, s0, d_o, ds_final=None,
+              chunk: int = 64, cu_seqlens=None, need_ds0: bool = True,
+              workspace: Optional[torch.Tensor] = None):
+    """Chunkwise backward.  Returns (dq, dk, dv, dbeta, dlog_alpha, ds0)."""
+    lib = _lib.load()
+    _check_cu(cu_seqlens, q)
+    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
+    nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+    H, dk, dv = q.shape[2], q.shape[3], v.shape[3]
+    dq = torch.empty_like(q)
+    dk_ = torch.empty_like(k)
+    dv_ = torch.empty_like(v)
+    dbeta = torch.empty(beta.shape, dtype=torch.float32, device=q.device)
+    dla = (None if log_alpha is None else
+           torch.empty(log_alpha.shape, dtype=torch.float32, device=q.device))
+    ds0 = (torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+           if need_ds0 else None)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.gdn_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(need)),
+               "gdn_chunk_bwd_workspace")
+    ws = workspace
+    if ws is None or ws.numel() < need.value:
+        ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    st = lib.gdn_chunk_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                           _ptr(log_alpha), _ptr(s0), _ptr(d_o), _ptr(ds_final),
+                           _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dbeta), _ptr(dla),
+                           _ptr(ds0), _ptr(ws), ws.numel(), _stream(q.device))
+    _lib.check(st, "gdn_chunk_bwd")
+    return dq, dk_, dv_, dbeta, dla, ds0
+
+
+def decode_step(q, k, v, beta, log_alpha, state):
+    """One token per sequence; ``state`` [N, H, dk, dv] fp32 is updated in
+    place.  q, k [N, H, dk]; v [N, H, dv]; beta [N, H]; log_alpha [N, H],
+    [N, H, dk] or None.  Returns o [N, H, dv]."""
+    lib = _lib.load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    p = _lib.GdnProblem()
+    p.B, p.T, p.H, p.dk, p.dv, p.chunk, p.nseq = N, 1, H, dk, dv, 0, 0
+    p.cu_seqlens = None
+    p.io_dtype = _dtype_code(q)
+    p.gate_dtype = _dtype_code(beta)
+    p.gate = _gate_of(log_alpha, 2)
+    if state.dtype != torch.float32:
+        raise TypeError("state must be fp32")
+    o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    st = lib.gdn_decode_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                             _ptr(log_alpha), _ptr(state), _ptr(o),
+                             _stream(q.device))
+    _lib.check(st, "gdn_decode_step")
+    return o

@@ -1,0 +1,256 @@
+// C ABI of libgdn: argument validation, workspace sizing and dispatch.
+// Every check runs on the host before anything is enqueued, so a non-OK
+// status means no work was launched.  No exception crosses the ABI.
+
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <atomic>
+#include <exception>
+
+#include "gdn.h"
+#include "gdn_internal.hpp"
+
+namespace {
+
+std::atomic<int> g_fail_launch{0};
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// A pointer that must be present when its tensor has elements.
+gdn_status need(const void* p, int64_t elems) {
+  if (elems == 0) return GDN_OK;
+  if (p == nullptr) return GDN_ERR_NULL;
+  if (!aligned16(p)) return GDN_ERR_ALIGN;
+  return GDN_OK;
+}
+
+// An optional pointer: NULL is fine, otherwise it must be aligned.
+gdn_status opt(const void* p) {
+  if (p != nullptr && !aligned16(p)) return GDN_ERR_ALIGN;
+  return GDN_OK;
+}
+
+#define GDN_TRY(expr)                 \
+  do {                                \
+    gdn_status _s = (expr);           \
+    if (_s != GDN_OK) return _s;      \
+  } while (0)
+
+bool dk_ok(int dk) { return dk == 16 || dk == 32 || dk == 64 || dk == 128; }
+bool dv_ok(int dv) { return dv >= 16 && dv <= 256 && dv % 16 == 0; }
+bool dtype_ok(int d) { return d == GDN_F32 || d == GDN_BF16; }
+
+// Shared checks of the chunked entry points; fills *out.
+gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out) {
+  if (p == nullptr) return GDN_ERR_NULL;
+  if (!dtype_ok(p->io_dtype) || !dtype_ok(p->gate_dtype)) return GDN_ERR_DTYPE;
+  if (p->gate < GDN_GATE_NONE || p->gate > GDN_GATE_CHANNEL)
+    return GDN_ERR_UNSUPPORTED;
+  if (p->B < 1 || p->H < 1 || p->T < 0 || p->nseq < 0) return GDN_ERR_SHAPE;
+  if (!dk_ok(p->dk) || !dv_ok(p->dv)) return GDN_ERR_UNSUPPORTED;
+  if (p->chunk != 16 && p->chunk != 32 && p->chunk != 64)
+    return GDN_ERR_UNSUPPORTED;
+  if (p->nseq > 0) {
+    if (p->B != 1) return GDN_ERR_SHAPE;
+    if (p->cu_seqlens == nullptr) return GDN_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(p->cu_seqlens) & 3u) != 0)
+      return GDN_ERR_ALIGN;
+  } else if (p->cu_seqlens != nullptr) {
+    return GDN_ERR_SHAPE;
+  }
+  // element counts must stay far inside int64 and the grid limits
+  const int64_t tok = static_cast<int64_t>(p->B) * p->T;
+  if (tok * p->H * 256 > (int64_t(1) << 46)) return GDN_ERR_SHAPE;
+  out->B = p->B;
+  out->T = p->T;
+  out->H = p->H;
+  out->dk = p->dk;
+  out->dv = p->dv;
+  out->chunk = p->chunk;
+  out->varlen = p->nseq > 0;
+  out->nseq = out->varlen ? p->nseq : p->B;
+  out->cu_seqlens = p->cu_seqlens;
+  out->io = p->io_dtype;
+  out->gdt = p->gate_dtype;
+  out->gate = p->gate;
+  const int64_t per_seq = (static_cast<int64_t>(p->T) + p->chunk - 1) / p->chunk;
+  out->nchunks = out->varlen ? per_seq + p->nseq : per_seq * p->B;
+  if (out->nchunks * p->H > (int64_t(1) << 31) - 1) return GDN_ERR_SHAPE;
+  return GDN_OK;
+}
+
+gdn_status check_fwd_pointers(const gdn::Problem& p, const void* q,
+                              const void* k, const void* v, const void* beta,
+                              const void* la, const float* s0, const void* o,
+                              const float* s_final) {
+  const int64_t tok = static_cast<int64_t>(p.B) * p.T * p.H;
+  GDN_TRY(need(q, tok * p.dk));
+  GDN_TRY(need(k, tok * p.dk));
+  GDN_TRY(need(v, tok * p.dv));
+  GDN_TRY(need(beta, tok));
+  if (p.gate != GDN_GATE_NONE) GDN_TRY(need(la, tok));
+  else GDN_TRY(opt(la));
+  GDN_TRY(need(o, tok * p.dv));
+  GDN_TRY(opt(s0));
+  GDN_TRY(opt(s_final));
+  return GDN_OK;
+}
+
+gdn_status launched(hipError_t e) {
+  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_str(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL: required pointer is NULL";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: size out of range or inconsistent";
+    case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unknown dtype code";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: outside the supported sizes or modes";
+    case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: pointer not 16-byte aligned";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP: HIP runtime refused the launch";
+  }
+  return "GDN_ERR_UNKNOWN";
+}
+
+void gdn_test_set_fail_launch(int enable) { g_fail_launch.store(enable != 0); }
+
+gdn_status gdn_chunk_fwd_workspace(const gdn_problem* p, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return GDN_ERR_NULL;
+    gdn::Problem pp;
+    GDN_TRY(check_chunk_problem(p, &pp));
+    *bytes = gdn::fwd_workspace_bytes(pp);
+    return GDN_OK;
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
+                         const void* v, const void* beta,
+                         const void* log_alpha, const float* s0, void* o,
+                         float* s_final, void* ws, size_t ws_bytes,
+                         void* stream) {
+  try {
+    gdn::Problem pp;
+    GDN_TRY(check_chunk_problem(p, &pp));
+    GDN_TRY(check_fwd_pointers(pp, q, k, v, beta, log_alpha, s0, o, s_final));
+    const size_t need_ws = gdn::fwd_workspace_bytes(pp);
+    if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
+      return GDN_ERR_WORKSPACE;
+    GDN_TRY(opt(ws));
+    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o,
+                                    s_final, ws,
+                                    static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return GDN_ERR_NULL;
+    gdn::Problem pp;
+    GDN_TRY(check_chunk_problem(p, &pp));
+    *bytes = gdn::bwd_workspace_bytes(pp);
+    return GDN_OK;
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k,
+                         const void* v, const void* beta,
+                         const void* log_alpha, const float* s0,
+                         const void* d_o, const float* ds_final, void* dq,
+                         void* dk, void* dv, float* dbeta, float* dlog_alpha,
+                         float* ds0, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    gdn::Problem pp;
+    GDN_TRY(check_chunk_problem(p, &pp));
+    const int64_t tok = static_cast<int64_t>(pp.B) * pp.T * pp.H;
+    GDN_TRY(need(q, tok * pp.dk));
+    GDN_TRY(need(k, tok * pp.dk));
+    GDN_TRY(need(v, tok * pp.dv));
+    GDN_TRY(need(beta, tok));
+    GDN_TRY(need(d_o, tok * pp.dv));
+    GDN_TRY(need(dq, tok * pp.dk));
+    GDN_TRY(need(dk, tok * pp.dk));
+    GDN_TRY(need(dv, tok * pp.dv));
+    GDN_TRY(need(dbeta, tok));
+    if (pp.gate != GDN_GATE_NONE) {
+      GDN_TRY(need(log_alpha, tok));
+      GDN_TRY(need(dlog_alpha, tok));
+    } else {
+      GDN_TRY(opt(log_alpha));
+      GDN_TRY(opt(dlog_alpha));
+    }
+    GDN_TRY(opt(s0));
+    GDN_TRY(opt(ds_final));
+    GDN_TRY(opt(ds0));
+    const size_t need_ws = gdn::bwd_workspace_bytes(pp);
+    if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
+      return GDN_ERR_WORKSPACE;
+    GDN_TRY(opt(ws));
+    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    return launched(gdn::launch_bwd(pp, q, k, v, beta, log_alpha, s0, d_o,
+                                    ds_final, dq, dk, dv, dbeta, dlog_alpha,
+                                    ds0, ws, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k,
+                           const void* v, const void* beta,
+                           const void* log_alpha, float* state, void* o,
+                           void* stream) {
+  try {
+    if (p == nullptr) return GDN_ERR_NULL;
+    if (!dtype_ok(p->io_dtype) || !dtype_ok(p->gate_dtype)) return GDN_ERR_DTYPE;
+    if (p->gate < GDN_GATE_NONE || p->gate > GDN_GATE_CHANNEL)
+      return GDN_ERR_UNSUPPORTED;
+    if (p->B < 1 || p->H < 1) return GDN_ERR_SHAPE;
+    if (!dk_ok(p->dk) || !dv_ok(p->dv)) return GDN_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(p->B) * p->H > (int64_t(1) << 31) - 1)
+      return GDN_ERR_SHAPE;
+    gdn::Problem pp{};
+    pp.B = p->B;
+    pp.T = 1;
+    pp.H = p->H;
+    pp.dk = p->dk;
+    pp.dv = p->dv;
+    pp.nseq = p->B;
+    pp.io = p->io_dtype;
+    pp.gdt = p->gate_dtype;
+    pp.gate = p->gate;
+    const int64_t nh = static_cast<int64_t>(p->B) * p->H;
+    GDN_TRY(need(q, nh * p->dk));
+    GDN_TRY(need(k, nh * p->dk));
+    GDN_TRY(need(v, nh * p->dv));
+    GDN_TRY(need(beta, nh));
+    if (pp.gate != GDN_GATE_NONE) GDN_TRY(need(log_alpha, nh));
+    else GDN_TRY(opt(log_alpha));
+    GDN_TRY(need(state, nh * p->dk * p->dv));
+    GDN_TRY(need(o, nh * p->dv));
+    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    return launched(gdn::launch_decode(pp, q, k, v, beta, log_alpha, state, o,
+                                       static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+// Single-token decode of the gated delta rule, state updated in place.
+//
+// "Gated Delta Networks: Improving Mamba2 with Delta Rule" (paper review),
+// "Background": recurrent inference carries a fixed-size matrix state, so a
+// decode step costs O(dk * dv) per head regardless of context length.  The
+// step, in the stored orientation M = S^T ([dk, dv] row-major fp32):
+//     Mt = a (.) M        (a = exp(log alpha): one value, or one per dk row)
+//     u = Mt^T k,  w = Mt^T q,  e = beta (v - u)
+//     o = w + (k . q) e   (= M_new^T q),   M_new = Mt + k e^T
+//
+// The step is a pure stream over the state: 8 bytes of HBM traffic (one fp32
+// read, one fp32 write) per 6 flops, so HBM bandwidth bounds it.  Each
+// workgroup owns one (sequence, head) and a 64-column slab of the state; a
+// thread holds DK/16 rows x 4 columns in registers between the reduction and
+// the write-back, so every state element crosses HBM exactly once each way.
+// Loads are 16-byte and a wave covers four 256-byte row segments.
+
+#include "gdn_device.hpp"
+#include "gdn_internal.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSlab = 64;  // state columns per workgroup
+
+template <int DK, typename IO, typename GT, int GATE>
+__global__ __launch_bounds__(kThreads) void decode_kernel(
+    int H, int dv, const void* __restrict__ q, const void* __restrict__ k,
+    const void* __restrict__ v, const void* __restrict__ beta,
+    const void* __restrict__ la, float* __restrict__ state,
+    void* __restrict__ o) {
+  constexpr int RPT = DK / 16;  // rows per thread
+  const int nh = blockIdx.x;    // n * H + h
+  const int t = threadIdx.x;
+  const int cg = t & 15;        // column group: 4 consecutive columns
+  const int rg = t >> 4;        // row group 0..15: rows rg + 16 j
+  const int col = blockIdx.y * kSlab + cg * 4;
+  const bool active = col < dv;  // dv is a multiple of 16, so all-or-none
+
+  const int64_t vec_off = static_cast<int64_t>(nh) * DK;
+  float* M = state + static_cast<int64_t>(nh) * DK * dv;
+
+  // per-row key, query and decay for the rows this thread owns
+  float kr[RPT], qr[RPT], ar[RPT];
+  float a_scalar = 1.0f;
+  if constexpr (GATE == GDN_GATE_SCALAR) a_scalar = expf(io<GT>::load(la, nh));
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int r = rg + 16 * j;
+    kr[j] = io<IO>::load(k, vec_off + r);
+    qr[j] = io<IO>::load(q, vec_off + r);
+    if constexpr (GATE == GDN_GATE_CHANNEL)
+      ar[j] = expf(io<GT>::load(la, vec_off + r));
+    else
+      ar[j] = a_scalar;
+  }
+
+  // load and decay the state slab; partial reductions over this thread's rows
+  floatx4 m[RPT];
+  floatx4 u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
+  float kq = 0.f;
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int r = rg + 16 * j;
+    if (active) {
+      m[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const floatx4*>(M + static_cast<int64_t>(r) * dv + col));
+    } else {
+      m[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    m[j] *= ar[j];
+    u += m[j] * kr[j];
+    w += m[j] * qr[j];
+    kq += kr[j] * qr[j];
+  }
+
+  // reduce over the 16 row groups: 4 per wave (lanes 16 and 32 apart), then
+  // across the 4 waves through LDS
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    u[c] = wave_sum_xor(u[c], 48);
+    w[c] = wave_sum_xor(w[c], 48);
+  }
+  kq = wave_sum_xor(kq, 48);
+  __shared__ floatx4 su[4][16], sw[4][16];
+  __shared__ float skq[4];
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  if (lane < 16) {
+    su[wave][lane] = u;
+    sw[wave][lane] = w;
+  }
+  if (lane == 0) skq[wave] = kq;
+  __syncthreads();
+  u = su[0][cg] + su[1][cg] + su[2][cg] + su[3][cg];
+  w = sw[0][cg] + sw[1][cg] + sw[2][cg] + sw[3][cg];
+  kq = skq[0] + skq[1] + skq[2] + skq[3];
+
+  if (!active) return;
+  const float b = io<GT>::load(beta, nh);
+  const int64_t vo = static_cast<int64_t>(nh) * dv + col;
+  floatx4 e;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) e[c] = b * (io<IO>::load(v, vo + c) - u[c]);
+
+  if (rg == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) io<IO>::store(o, vo + c, w[c] + kq * e[c]);
+  }
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int r = rg + 16 * j;
+    floatx4 mn = m[j] + kr[j] * e;
+    __builtin_nontemporal_store(
+        mn, reinterpret_cast<floatx4*>(M + static_cast<int64_t>(r) * dv + col));
+  }
+}
+
+template <int DK, typename IO, typename GT>
+hipError_t dispatch_gate(const Problem& p, dim3 grid, const void* q,
+                         const void* k, const void* v, const void* beta,
+                         const void* la, float* state, void* o, hipStream_t s) {
+  switch (p.gate) {
+    case GDN_GATE_NONE:
+      hipLaunchKernelGGL((decode_kernel<DK, IO, GT, GDN_GATE_NONE>), grid,
+                         dim3(kThreads), 0, s, p.H, p.dv, q, k, v, beta, la,
+                         state, o);
+      break;
+    case GDN_GATE_SCALAR:
+      hipLaunchKernelGGL((decode_kernel<DK, IO, GT, GDN_GATE_SCALAR>), grid,
+                         dim3(kThreads), 0, s, p.H, p.dv, q, k, v, beta, la,
+                         state, o);
+      break;
+    default:
+      hipLaunchKernelGGL((decode_kernel<DK, IO, GT, GDN_GATE_CHANNEL>), grid,
+                         dim3(kThreads), 0, s, p.H, p.dv, q, k, v, beta, la,
+                         state, o);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <int DK, typename IO>
+hipError_t dispatch_gdt(const Problem& p, dim3 grid, const void* q,
+                        const void* k, const void* v, const void* beta,
+                        const void* la, float* state, void* o, hipStream_t s) {
+  if (p.gdt == GDN_BF16)
+    return dispatch_gate<DK, IO, bf16_t>(p, grid, q, k, v, beta, la, state, o, s);
+  return dispatch_gate<DK, IO, f32_t>(p, grid, q, k, v, beta, la, state, o, s);
+}
+
+template <int DK>
+hipError_t dispatch_io(const Problem& p, dim3 grid, const void* q,
+                       const void* k, const void* v, const void* beta,
+                       const void* la, float* state, void* o, hipStream_t s) {
+  if (p.io == GDN_BF16)
+    return dispatch_gdt<DK, bf16_t>(p, grid, q, k, v, beta, la, state, o, s);
+  return dispatch_gdt<DK, f32_t>(p, grid, q, k, v, beta, la, state, o, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const Problem& p, const void* q, const void* k,
+                         const void* v, const void* beta, const void* la,
+                         float* state, void* o, hipStream_t s) {
+  const dim3 grid(p.B * p.H, (p.dv + kSlab - 1) / kSlab);
+  switch (p.dk) {
+    case 16: return dispatch_io<16>(p, grid, q, k, v, beta, la, state, o, s);
+    case 32: return dispatch_io<32>(p, grid, q, k, v, beta, la, state, o, s);
+    case 64: return dispatch_io<64>(p, grid, q, k, v, beta, la, state, o, s);
+    default: return dispatch_io<128>(p, grid, q, k, v, beta, la, state, o, s);
+  }
+}
+
+}  // namespace gdn

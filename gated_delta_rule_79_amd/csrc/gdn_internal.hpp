@@ -1,0 +1,45 @@
+// Internal host-side interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// Validated problem, in host-friendly form.
+struct Problem {
+  int B, T, H, dk, dv, chunk;
+  int nseq;                   // number of independent sequences (B or varlen)
+  bool varlen;
+  const int32_t* cu_seqlens;  // device
+  int io;                     // gdn_dtype
+  int gdt;                    // gdn_dtype of beta / log_alpha
+  int gate;                   // gdn_gate
+  // derived
+  int64_t nchunks;            // chunk slots per head (upper bound in varlen)
+};
+
+// Decode launcher (gdn_decode.hip).
+hipError_t launch_decode(const Problem& p, const void* q, const void* k,
+                         const void* v, const void* beta, const void* la,
+                         float* state, void* o, hipStream_t s);
+
+// Forward (gdn_fwd.hip).
+size_t fwd_workspace_bytes(const Problem& p);
+hipError_t launch_fwd(const Problem& p, const void* q, const void* k,
+                      const void* v, const void* beta, const void* la,
+                      const float* s0, void* o, float* s_final, void* ws,
+                      hipStream_t s);
+
+// Backward (gdn_bwd.hip).
+size_t bwd_workspace_bytes(const Problem& p);
+hipError_t launch_bwd(const Problem& p, const void* q, const void* k,
+                      const void* v, const void* beta, const void* la,
+                      const float* s0, const void* d_o, const float* ds_final,
+                      void* dq, void* dk, void* dv, float* dbeta, float* dla,
+                      float* ds0, void* ws, hipStream_t s);
+
+}  // namespace gdn

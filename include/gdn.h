@@ -1,0 +1,176 @@
+/*
+ * libgdn -- the gated delta rule on AMD MI355X (gfx950), C ABI.
+ *
+ * Operation ("Gated Delta Networks: Improving Mamba2 with Delta Rule", paper
+ * review, section "Method"): for every sequence and head, token by token,
+ *
+ *     S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,
+ *
+ * with S_t of shape dv x dk.  The library stores the state transposed,
+ * M = S^T, as a row-major [dk, dv] fp32 matrix per (sequence, head).
+ *   - alpha_t arrives as log alpha_t (finite, normally <= 0).  GDN_GATE_SCALAR
+ *     takes one value per (token, head); GDN_GATE_CHANNEL one value per
+ *     (token, head, key channel), which scales the dk rows of M (the
+ *     Kimi-Delta-style diagonal gate that "Linear Attention Architectures:
+ *     Mechanisms, Trade-offs, and Cross-Layer Routing" names); GDN_GATE_NONE
+ *     is alpha = 1, the plain delta rule ("Key idea": alpha -> 1 recovers it).
+ *   - beta_t is used as given (never clamped); q and k are used as given (the
+ *     caller normalises them); there is no 1/sqrt(dk) scale.
+ *   - The output reads the state after the token's own update.
+ *
+ * Three entry points:
+ *   gdn_chunk_fwd   chunkwise-parallel forward over whole sequences (the WY /
+ *                   UT-transform form named in "Method"), for prefill and
+ *                   training;
+ *   gdn_chunk_bwd   gradients of <dO, o> + <dS_final, S_final>;
+ *   gdn_decode_step one token per sequence, updating the state in place
+ *                   (the O(1)-memory recurrent inference of "Background").
+ *
+ * Conventions shared by all entry points
+ *   Pointers: device pointers owned by the caller (e.g. torch tensors),
+ *     contiguous, 16-byte aligned.  The library keeps no pointer after it
+ *     returns and allocates no device memory: gdn_chunk_fwd / gdn_chunk_bwd
+ *     take a caller-provided workspace of the size the *_workspace query
+ *     returns.  Outputs must not alias inputs, except `state` of decode.
+ *   Layouts (token-major, row-major):
+ *     q, k       [B, T, H, dk]           (varlen: B = 1, T = total tokens)
+ *     v, o, dO   [B, T, H, dv]
+ *     beta       [B, T, H]
+ *     log_alpha  [B, T, H] scalar gate, [B, T, H, dk] channel gate,
+ *                ignored (may be NULL) for GDN_GATE_NONE
+ *     s0, s_final, ds_final, ds0   [nseq, H, dk, dv] fp32
+ *                (nseq = B for dense batches, the varlen sequence count else)
+ *   Dtypes: q, k, v, o, dO, dq, dk, dv use io_dtype (fp32 or bf16); beta
+ *     and log_alpha use gate_dtype; states, dbeta and dlog_alpha are fp32.
+ *     bf16 operands are multiplied on the matrix cores with fp32
+ *     accumulation; the state is always carried in fp32.
+ *   Sizes: dk in {16, 32, 64, 128}; dv a multiple of 16 up to 256; chunk in
+ *     {16, 32, 64}; H >= 1; T >= 0 (T = 0 is a no-op that copies s0 to
+ *     s_final); B >= 1.
+ *   Varlen: nseq > 0 with B == 1 packs nseq sequences; cu_seqlens is a
+ *     DEVICE int32 array [nseq + 1] with cu_seqlens[0] = 0, non-decreasing,
+ *     cu_seqlens[nseq] = T.  Its contents are a precondition (they are not
+ *     read on the host); sequences of length 0 are allowed.  Chunks never
+ *     cross a sequence boundary.
+ *   Streams: all work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) with no implicit synchronisation.  The functions are
+ *     stateless and re-entrant.
+ *   Errors: every argument is validated on the host before anything is
+ *     enqueued, so a non-OK status means nothing was launched.  A failed
+ *     launch returns GDN_ERR_HIP.  Device faults surface at the caller's
+ *     next synchronisation (asynchronous HIP semantics).  No function
+ *     aborts or lets an exception escape.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  GDN_ERR_SHAPE = 2,       /* a size is out of range or inconsistent         */
+  GDN_ERR_DTYPE = 3,       /* unknown dtype code                              */
+  GDN_ERR_UNSUPPORTED = 4, /* valid request outside the supported set        */
+  GDN_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                */
+  GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required      */
+  GDN_ERR_HIP = 7          /* the HIP runtime refused a launch                */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum {
+  GDN_GATE_NONE = 0,       /* alpha = 1: the delta rule without decay          */
+  GDN_GATE_SCALAR = 1,     /* one log alpha per (token, head)                  */
+  GDN_GATE_CHANNEL = 2     /* one log alpha per (token, head, key channel)     */
+} gdn_gate;
+
+/* Problem description.  For decode, T is ignored, B is the number of
+ * sequences N and chunk / nseq / cu_seqlens are ignored. */
+typedef struct {
+  int32_t B, T, H, dk, dv, chunk;
+  int32_t nseq;                 /* 0 = dense [B, T]; > 0 = varlen, B == 1     */
+  const int32_t* cu_seqlens;    /* device [nseq + 1] when nseq > 0, else NULL */
+  int32_t io_dtype;             /* gdn_dtype of q, k, v, o (and grads)        */
+  int32_t gate_dtype;           /* gdn_dtype of beta and log_alpha            */
+  int32_t gate;                 /* gdn_gate                                   */
+} gdn_problem;
+
+/* ABI version of the loaded library (GDN_ABI_VERSION). */
+int gdn_abi_version(void);
+
+/* Static, never NULL, human-readable name of a status. */
+const char* gdn_status_str(gdn_status s);
+
+/* Workspace bytes gdn_chunk_fwd needs for problem *p (written to *bytes).
+ * Returns the same validation status gdn_chunk_fwd would for the sizes. */
+gdn_status gdn_chunk_fwd_workspace(const gdn_problem* p, size_t* bytes);
+
+/* Chunkwise forward ("Method": the WY representation and UT transform keep
+ * the recurrence in matrix-multiply form).  Per chunk of `chunk` tokens it
+ * forms the chunk-local cumulative log-gate, the unit lower-triangular
+ * system (I + tril(diag(beta) K K^T * decay, -1)) and its inverse T, the
+ * WY factors W = T diag(beta * gamma) K and U = T diag(beta) V, then carries
+ * the fp32 state across chunks.
+ *   q, k, v, beta, log_alpha : inputs as in the header comment.
+ *   s0      : initial state [nseq, H, dk, dv] fp32, or NULL for zeros.
+ *   o       : output [B, T, H, dv] in io_dtype.
+ *   s_final : final state [nseq, H, dk, dv] fp32, or NULL to skip it.
+ *   ws      : device workspace of at least gdn_chunk_fwd_workspace bytes
+ *             (256-byte aligned); contents on entry do not matter.
+ */
+gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
+                         const void* v, const void* beta,
+                         const void* log_alpha, const float* s0, void* o,
+                         float* s_final, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Workspace bytes gdn_chunk_bwd needs (see gdn_chunk_fwd_workspace). */
+gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes);
+
+/* Chunkwise backward: gradients of L = <dO, o> + <ds_final, S_final>, the
+ * forward recomputed inside (the pages give no backward; this is the
+ * adjoint of the recurrence above).  Gradients are taken with respect to
+ * log alpha (not alpha) and beta (not a logit).
+ *   d_o      : [B, T, H, dv] io_dtype.   ds_final : fp32 or NULL (zeros).
+ *   dq, dk   : [B, T, H, dk] io_dtype.   dv : [B, T, H, dv] io_dtype.
+ *   dbeta    : [B, T, H] fp32.
+ *   dlog_alpha : fp32, shaped like log_alpha; NULL allowed for GATE_NONE.
+ *   ds0      : [nseq, H, dk, dv] fp32 or NULL to skip.
+ * The result is deterministic (no floating-point atomics). */
+gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k,
+                         const void* v, const void* beta,
+                         const void* log_alpha, const float* s0,
+                         const void* d_o, const float* ds_final, void* dq,
+                         void* dk, void* dv, float* dbeta, float* dlog_alpha,
+                         float* ds0, void* ws, size_t ws_bytes, void* stream);
+
+/* One token per sequence (B = N sequences), state updated in place:
+ *   Mt = a (.) M (a = exp(log alpha), per row for the channel gate),
+ *   e = beta (v - Mt^T k),  M <- Mt + k e^T,  o = M^T q.
+ * Each state element is read once and written once.
+ *   q, k  [N, H, dk]; v [N, H, dv]; beta [N, H]; log_alpha [N, H] or
+ *   [N, H, dk]; state [N, H, dk, dv] fp32 in/out; o [N, H, dv] io_dtype. */
+gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k,
+                           const void* v, const void* beta,
+                           const void* log_alpha, float* state, void* o,
+                           void* stream);
+
+/* Test hook: when set to a non-zero value every entry point returns
+ * GDN_ERR_HIP after validation instead of launching (exercises the launch
+ * failure path on machines without a GPU).  Not for production use. */
+void gdn_test_set_fail_launch(int enable);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

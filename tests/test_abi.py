@@ -1,0 +1,194 @@
+"""The C ABI of libgdn on the CPU: the library loads, exports every function
+include/gdn.h declares, and rejects bad arguments before launching anything.
+
+Every call here either fails validation or runs with the launch-failure test
+hook set, so no kernel is ever launched (fake device pointers are safe)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_79_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+A = 0x10000  # fake, 16-byte aligned "device" addresses (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libgdn.so not built")
+    lib = _lib.load()
+    lib.gdn_test_set_fail_launch(1)
+    yield lib
+    lib.gdn_test_set_fail_launch(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.gdn_abi_version() == 1
+    for s in range(8):
+        txt = lib.gdn_status_str(s).decode()
+        assert txt.startswith("GDN_")
+    assert lib.gdn_status_str(99).decode() == "GDN_ERR_UNKNOWN"
+
+
+def prob(**kw):
+    p = _lib.GdnProblem()
+    d = dict(B=1, T=64, H=2, dk=128, dv=128, chunk=64, nseq=0, cu_seqlens=None,
+             io_dtype=_lib.GDN_BF16, gate_dtype=_lib.GDN_BF16,
+             gate=_lib.GDN_GATE_SCALAR)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(p, k, v)
+    return p
+
+
+def ws_bytes(lib, p):
+    n = ctypes.c_size_t(0)
+    st = lib.gdn_chunk_fwd_workspace(ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+def fwd(lib, p, ws=None, **ptr):
+    d = dict(q=A, k=A, v=A, beta=A, la=A, s0=None, o=A, sf=None)
+    d.update(ptr)
+    st, need = ws_bytes(lib, p)
+    if st != 0:
+        need = 0
+    return lib.gdn_chunk_fwd(ctypes.byref(p), d["q"], d["k"], d["v"], d["beta"],
+                             d["la"], d["s0"], d["o"], d["sf"],
+                             A if ws is None else ws, need, None)
+
+
+def test_valid_call_reaches_launch(lib):
+    # validation passes, the test hook turns the launch into GDN_ERR_HIP
+    assert fwd(lib, prob()) == _lib.GDN_ERR_HIP
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=48), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(dk=256), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(dv=24), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(dv=272), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=128), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=8), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(gate=3), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(io_dtype=2), _lib.GDN_ERR_DTYPE),
+    (dict(gate_dtype=-1), _lib.GDN_ERR_DTYPE),
+    (dict(B=0), _lib.GDN_ERR_SHAPE),
+    (dict(H=0), _lib.GDN_ERR_SHAPE),
+    (dict(T=-1), _lib.GDN_ERR_SHAPE),
+    (dict(nseq=-2), _lib.GDN_ERR_SHAPE),
+    (dict(nseq=3, B=2, cu_seqlens=A), _lib.GDN_ERR_SHAPE),
+    (dict(nseq=3, cu_seqlens=None), _lib.GDN_ERR_NULL),
+    (dict(nseq=0, cu_seqlens=A), _lib.GDN_ERR_SHAPE),
+    (dict(nseq=3, cu_seqlens=A + 2), _lib.GDN_ERR_ALIGN),
+    (dict(T=(1 << 31) - 1, H=1024), _lib.GDN_ERR_SHAPE),
+])
+def test_problem_validation(lib, kw, status):
+    p = prob(**kw)
+    assert fwd(lib, p) == status
+    st, _ = ws_bytes(lib, p)
+    assert st == status
+
+
+def test_null_problem(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_workspace(None, ctypes.byref(n)) == _lib.GDN_ERR_NULL
+    assert lib.gdn_chunk_fwd_workspace(ctypes.byref(prob()), None) == _lib.GDN_ERR_NULL
+    assert lib.gdn_chunk_fwd(None, A, A, A, A, A, None, A, None, A, 0, None) == _lib.GDN_ERR_NULL
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "beta", "la", "o"])
+def test_pointer_checks(lib, name):
+    assert fwd(lib, prob(), **{name: None}) == _lib.GDN_ERR_NULL
+    assert fwd(lib, prob(), **{name: A + 8}) == _lib.GDN_ERR_ALIGN
+
+
+def test_optional_pointers(lib):
+    assert fwd(lib, prob(), s0=A + 4) == _lib.GDN_ERR_ALIGN
+    assert fwd(lib, prob(), sf=A + 4) == _lib.GDN_ERR_ALIGN
+    assert fwd(lib, prob(), s0=A, sf=A) == _lib.GDN_ERR_HIP
+    # gate none: log_alpha may be NULL
+    assert fwd(lib, prob(gate=_lib.GDN_GATE_NONE), la=None) == _lib.GDN_ERR_HIP
+
+
+def test_empty_sequence_needs_no_pointers(lib):
+    p = prob(T=0)
+    st, need = ws_bytes(lib, p)
+    assert st == 0 and need == 0
+    assert lib.gdn_chunk_fwd(ctypes.byref(p), None, None, None, None, None, None,
+                             None, None, None, 0, None) == _lib.GDN_ERR_HIP
+
+
+def test_workspace_checks(lib):
+    p = prob()
+    st, need = ws_bytes(lib, p)
+    assert st == 0 and need > 0
+    assert lib.gdn_chunk_fwd(ctypes.byref(p), A, A, A, A, A, None, A, None, A,
+                             need - 1, None) == _lib.GDN_ERR_WORKSPACE
+    assert lib.gdn_chunk_fwd(ctypes.byref(p), A, A, A, A, A, None, A, None, None,
+                             need, None) == _lib.GDN_ERR_WORKSPACE
+    assert lib.gdn_chunk_fwd(ctypes.byref(p), A, A, A, A, A, None, A, None, A + 4,
+                             need, None) == _lib.GDN_ERR_ALIGN
+
+
+def test_workspace_scales_with_problem(lib):
+    _, a = ws_bytes(lib, prob(T=64))
+    _, b = ws_bytes(lib, prob(T=128))
+    _, c = ws_bytes(lib, prob(T=64, H=4))
+    assert b == 2 * a and c == 2 * a
+    # varlen: one chunk slot per sequence more than the dense bound, plus the map
+    _, d = ws_bytes(lib, prob(T=64, nseq=3, cu_seqlens=A))
+    assert d > a
+
+
+def test_decode_validation(lib):
+    p = prob(B=4, T=0)
+    args = [A, A, A, A, A, A, A, None]
+    assert lib.gdn_decode_step(ctypes.byref(p), *args) == _lib.GDN_ERR_HIP
+    assert lib.gdn_decode_step(None, *args) == _lib.GDN_ERR_NULL
+    assert lib.gdn_decode_step(ctypes.byref(prob(dk=20)), *args) == _lib.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_decode_step(ctypes.byref(prob(B=0)), *args) == _lib.GDN_ERR_SHAPE
+    bad = list(args)
+    bad[5] = None      # state
+    assert lib.gdn_decode_step(ctypes.byref(p), *bad) == _lib.GDN_ERR_NULL
+    bad[5] = A + 2
+    assert lib.gdn_decode_step(ctypes.byref(p), *bad) == _lib.GDN_ERR_ALIGN
+
+
+def test_bwd_validation(lib):
+    p = prob()
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(n)) == 0
+    args = [A] * 6 + [A, None] + [A] * 5 + [None]
+    st = lib.gdn_chunk_bwd(ctypes.byref(p), *args, A, n.value, None)
+    assert st == _lib.GDN_ERR_HIP
+    bad = list(args)
+    bad[6] = None      # d_o
+    assert lib.gdn_chunk_bwd(ctypes.byref(p), *bad, A, n.value, None) == _lib.GDN_ERR_NULL
+    bad = list(args)
+    bad[12] = None     # dlog_alpha with a gate
+    assert lib.gdn_chunk_bwd(ctypes.byref(p), *bad, A, n.value, None) == _lib.GDN_ERR_NULL
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not found"):
+        _lib.load(str(tmp_path / "missing.so"))

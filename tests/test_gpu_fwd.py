@@ -1,0 +1,186 @@
+"""GPU parity of gdn_chunk_fwd against the fp64 oracle (MI355X only).
+
+Sizes span several chunks and 16-wide tiles and include ragged tails
+(T not a multiple of the chunk), every supported chunk size, key sizes,
+both dtypes, all gate modes, initial states and varlen packing with empty
+sequences.  The headline shapes run at full size."""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_79_amd as gdn
+from gated_delta_rule_79_amd import synth
+from gpu_util import TOL, dev, log, np64, oracle_fwd, slice_err, state_err
+
+pytestmark = pytest.mark.gpu
+
+
+def run(inp, **kw):
+    d = dev(inp)
+    o, sf = gdn.chunk_fwd(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0,
+                          chunk=inp.chunk, cu_seqlens=d.cu_seqlens, **kw)
+    torch.cuda.synchronize()
+    return o, sf
+
+
+def check(inp, tol=None, name=""):
+    log(f"[fwd] {name} q={tuple(inp.q.shape)} dtype={inp.q.dtype} gate={inp.gate} "
+        f"C={inp.chunk} seed={inp.seed}")
+    o, sf = run(inp)
+    o_ref, sf_ref = oracle_fwd(inp)
+    tol = tol or TOL[inp.q.dtype]
+    cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
+    eo = slice_err(np64(o), o_ref, cu)
+    es = state_err(np64(sf), sf_ref)
+    log(f"    err o={eo:.3e} s_final={es:.3e} tol={tol}")
+    assert eo < tol and es < tol, (eo, es)
+    return o, sf
+
+
+@pytest.mark.parametrize("gate", ["scalar", "none", "channel"])
+def test_tiny_fp32(gpu_lib, gate):
+    inp = synth.workload("tiny_fp32", gate=gate)
+    check(inp, name="tiny_fp32")
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("gate", ["scalar", "none", "channel"])
+def test_fp32_ragged(gpu_lib, C, gate):
+    inp = synth.make_inputs(2, 100, 3, 32, 48, dtype=torch.float32, gate=gate,
+                            chunk=C, seed=7, s0_std=0.3)
+    check(inp, name="fp32_ragged")
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 32), (128, 128), (128, 256)])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_bf16_shapes(gpu_lib, dk, dv, gate):
+    inp = synth.make_inputs(2, 200, 2, dk, dv, dtype=torch.bfloat16, gate=gate,
+                            chunk=64, seed=11, s0_std=0.05)
+    check(inp, name="bf16_shapes")
+
+
+@pytest.mark.parametrize("C", [16, 32])
+def test_bf16_small_chunks(gpu_lib, C):
+    inp = synth.make_inputs(1, 173, 4, 128, 64, dtype=torch.bfloat16, gate="scalar",
+                            chunk=C, seed=12)
+    check(inp, name="bf16_small_chunks")
+
+
+def test_gate_dtype_fp32_with_bf16_io(gpu_lib):
+    inp = synth.make_inputs(1, 130, 2, 128, 128, dtype=torch.bfloat16,
+                            gate_dtype=torch.float32, gate="scalar", seed=13)
+    check(inp, name="gate_fp32")
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel", "none"])
+def test_varlen(gpu_lib, gate):
+    inp = synth.make_inputs(1, 0, 2, 128, 64, dtype=torch.bfloat16, gate=gate,
+                            seed=14, lengths=[5, 0, 130, 64, 1, 77], s0_std=0.1)
+    check(inp, name="varlen")
+
+
+def test_varlen_fp32_chunk16(gpu_lib):
+    inp = synth.make_inputs(1, 0, 3, 32, 32, dtype=torch.float32, gate="channel",
+                            chunk=16, seed=15, lengths=[17, 0, 0, 33, 2])
+    check(inp, name="varlen_fp32")
+
+
+def test_alpha_to_zero_channel_exact_path(gpu_lib):
+    # log alpha = -60 everywhere: erasure; the per-channel span is far beyond
+    # the factored products' range, so the exact per-element path runs
+    inp = synth.make_inputs(1, 70, 2, 64, 32, dtype=torch.float32, gate="channel",
+                            seed=16, s0_std=1.0)
+    inp.log_alpha.fill_(-60.0)
+    inp.f64["log_alpha"][:] = -60.0
+    check(inp, name="alpha0_channel")
+
+
+def test_alpha_to_zero_scalar(gpu_lib):
+    inp = synth.make_inputs(1, 70, 2, 64, 32, dtype=torch.float32, gate="scalar",
+                            seed=17, s0_std=1.0)
+    inp.log_alpha.fill_(-60.0)
+    inp.f64["log_alpha"][:] = -60.0
+    check(inp, name="alpha0_scalar")
+
+
+def test_beta_up_to_two(gpu_lib):
+    inp = synth.make_inputs(2, 150, 2, 64, 64, dtype=torch.float32, gate="scalar",
+                            seed=18)
+    inp.beta.mul_(2.0)
+    inp.f64["beta"] = inp.beta.double().numpy()
+    check(inp, name="beta_2")
+
+
+def test_gate_none_equals_scalar_zero(gpu_lib):
+    inp = synth.make_inputs(1, 140, 2, 128, 128, dtype=torch.bfloat16, gate="scalar",
+                            seed=19, s0_std=0.02)
+    d = dev(inp)
+    o1, s1 = gdn.chunk_fwd(d.q, d.k, d.v, d.beta, torch.zeros_like(d.log_alpha), d.s0)
+    o2, s2 = gdn.chunk_fwd(d.q, d.k, d.v, d.beta, None, d.s0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_chunk_size_invariance_and_determinism(gpu_lib):
+    inp = synth.make_inputs(1, 250, 2, 64, 64, dtype=torch.float32, gate="channel",
+                            seed=20, s0_std=0.1)
+    outs = []
+    for C in (16, 32, 64):
+        inp.chunk = C
+        outs.append(run(inp))
+    for o, s in outs[1:]:
+        assert slice_err(np64(o), np64(outs[0][0])) < 1e-5
+        assert state_err(np64(s), np64(outs[0][1])) < 1e-5
+    a = run(inp)
+    b = run(inp)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_split_and_resume(gpu_lib):
+    inp = synth.make_inputs(1, 300, 2, 128, 128, dtype=torch.float32, gate="scalar",
+                            seed=21, s0_std=0.1)
+    d = dev(inp)
+    o, s = gdn.chunk_fwd(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0)
+    cut = 110
+    oa, sa = gdn.chunk_fwd(d.q[:, :cut].contiguous(), d.k[:, :cut].contiguous(),
+                           d.v[:, :cut].contiguous(), d.beta[:, :cut].contiguous(),
+                           d.log_alpha[:, :cut].contiguous(), d.s0)
+    ob, sb = gdn.chunk_fwd(d.q[:, cut:].contiguous(), d.k[:, cut:].contiguous(),
+                           d.v[:, cut:].contiguous(), d.beta[:, cut:].contiguous(),
+                           d.log_alpha[:, cut:].contiguous(), sa)
+    torch.cuda.synchronize()
+    assert slice_err(np64(torch.cat([oa, ob], 1)), np64(o)) < 1e-5
+    assert state_err(np64(sb), np64(s)) < 1e-5
+
+
+def test_empty_sequence_copies_state(gpu_lib):
+    inp = synth.make_inputs(2, 0, 2, 64, 32, dtype=torch.bfloat16, seed=22,
+                            s0_std=1.0)
+    o, sf = run(inp)
+    assert o.shape == (2, 0, 2, 32)
+    assert torch.equal(sf.cpu(), inp.s0)
+
+
+def test_headline_full_size(gpu_lib):
+    # T=4096, H=16, d=128, bf16, B=1: every head against the oracle
+    inp = synth.workload("fwd_t4096_h16")
+    check(inp, name="fwd_t4096_h16")
+
+
+def test_layer_b8_sampled(gpu_lib):
+    # B=8, T=2048, H=8, d=128: run all, compare two batch rows in full
+    inp = synth.workload("layer_b8_t2048")
+    log("[fwd] layer_b8_t2048")
+    o, sf = run(inp)
+    f = inp.f64
+    import oracle
+    for b in (0, 7):
+        sl = slice(b, b + 1)
+        o_ref, s_ref = oracle.gdn_fwd(f["q"][sl], f["k"][sl], f["v"][sl],
+                                      f["beta"][sl], f["log_alpha"][sl], None,
+                                      "scalar")
+        eo = slice_err(np64(o[sl]), o_ref)
+        es = state_err(np64(sf[sl]), s_ref)
+        log(f"    batch {b}: err o={eo:.3e} s={es:.3e}")
+        assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
