@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the chunkwise gated-delta-rule forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one gdn_chunk_fwd call (every kernel of the forward) over one batch
+of synthetic inputs already resident in device memory.  Default workload:
+B=1, T=4096, H=16, dk=dv=128, chunk 64, bf16 inputs, fp32 state.  Prints ONE
+JSON line with tokens/s, the roofline position of the dominant kernel
+(per-kernel device time from HIP events recorded by the library on the launch
+stream) and the fp64 CPU oracle timed on this host as a baseline.
+
+Algorithmic work per (token, head), chunk C:
+    flops = 6 dk dv + C (3 dk + 2 dv) + C^2 / 3
+    bytes = (2 dk + 2 dv) s_io + s_beta + s_gate      (+ state once per chain)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def algorithmic(B, T, H, dk, dv, C, s_io, s_gate, gate, nseq, s0, sfinal):
+    th = B * T * H
+    flops = th * (6 * dk * dv + C * (3 * dk + 2 * dv) + C * C / 3.0)
+    gate_bytes = 0 if gate == "none" else (dk if gate == "channel" else 1) * s_gate
+    byts = th * ((2 * dk + 2 * dv) * s_io + s_gate + gate_bytes)
+    byts += nseq * H * dk * dv * 4 * ((1 if s0 else 0) + (1 if sfinal else 0))
+    return flops, byts
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+FWD_SOURCES = ["gated_delta_rule_79_amd/csrc/gdn_fwd.hip",
+               "gated_delta_rule_79_amd/csrc/gdn_chunk_common.hpp",
+               "gated_delta_rule_79_amd/csrc/gdn_device.hpp"]
+
+
+def measured_traffic(workload, kernel, src_hash):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != src_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s):
+    """The fp64 oracle, as it stands, on whole (sequence, head) chains of the
+    same workload until about ``budget_s`` seconds of work; BLAS held to one
+    thread.  Rate is scaled to the whole workload's tokens."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    f = inp.f64
+    B, T, H = f["q"].shape[:3]
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for b in range(B):
+            for h in range(H):
+                la = None if f["log_alpha"] is None else f["log_alpha"][b, :, h]
+                m0 = np.zeros((f["q"].shape[3], f["v"].shape[3]))
+                oracle.gdn_fwd_chain(f["q"][b, :, h], f["k"][b, :, h], f["v"][b, :, h],
+                                     f["beta"][b, :, h], la, m0, inp.gate)
+                done += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    frac = done / float(B * H)
+    return {"value": B * T * frac / dt, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} of {B * H} (sequence, head) chains of T={T} "
+                      f"({dt:.1f} s, 1 thread); tokens/s scaled to the whole workload"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="fwd_t4096_h16")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="extra calls each preceded by a 1 GiB cache-flush write")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the gated delta rule path here runs on a "
+              "single MI355X (heads and sequences shard with no communication; see "
+              "the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_79_amd as gdn
+    from gated_delta_rule_79_amd import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    inp = synth.workload(args.workload)
+    d = inp.to("cuda")
+    B, T, H, dk = inp.q.shape
+    dv = inp.v.shape[-1]
+    C = inp.chunk
+    nseq = B if inp.cu_seqlens is None else inp.cu_seqlens.numel() - 1
+    plan = gdn.FwdPlan(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, chunk=C,
+                       cu_seqlens=d.cu_seqlens)
+
+    for _ in range(args.warmup):
+        plan.run()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back calls
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        plan.run()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # same calls again with the library's per-kernel HIP events
+    gdn.stage_times(True)
+    for _ in range(args.steps):
+        plan.run()
+    torch.cuda.synchronize()
+    st = gdn.stage_times()
+    gdn.stage_times(False)
+    per_kernel = {k: v[0] / v[1] for k, v in st.items()}
+
+    # cold: flush L2 and the 256 MB Infinity Cache before each call
+    cold_ms = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        times = []
+        for _ in range(args.cold_steps):
+            flush.fill_(1)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            plan.run()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        times.sort()
+        cold_ms = times[len(times) // 2]
+        del flush
+
+    s_io = 2 if inp.q.dtype == torch.bfloat16 else 4
+    s_gate = 2 if inp.beta.dtype == torch.bfloat16 else 4
+    flops, byts = algorithmic(B, T, H, dk, dv, C, s_io, s_gate, inp.gate, nseq,
+                              inp.s0 is not None, True)
+    tokens = B * T
+    value = tokens / (ms_per_step * 1e-3)
+
+    dom = max(per_kernel, key=per_kernel.get)
+    dom_ms = per_kernel[dom]
+    kname = {"fwd_prep": "fwd_prep_kernel", "fwd_scan": "fwd_scan_kernel",
+             "chunk_map": "chunk_map_kernel"}[dom]
+    achieved = byts / (dom_ms * 1e-3) / 1e9
+    src_hash = source_hash(FWD_SOURCES)
+    traffic = measured_traffic(args.workload, kname, src_hash)
+    path_ms = sum(per_kernel.values())
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "kernel": kname,
+        "kernel_ms": {k: round(v, 5) for k, v in per_kernel.items()},
+        "alg_bytes_per_launch": int(byts),
+        "alg_flops_per_launch": int(flops),
+        "path_frac_hbm": round(byts / (path_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "path_frac_mfma_bf16": round(flops / (path_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "source_hash": src_hash,
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_budget)
+        cpu["value"] = round(cpu["value"], 1)
+
+    out = {
+        "metric": "tokens/sec gdn_chunk_fwd (T=4096,H=16,d=128 bf16); % MFMA/HBM roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s_io == 2 else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "T": T, "H": H, "dk": dk,
+                   "dv": dv, "chunk": C, "gate": inp.gate, "seed": inp.seed,
+                   "state": "fp32", "parallelism": "single GPU"},
+        "cold_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

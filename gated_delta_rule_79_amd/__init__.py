@@ -24,7 +24,8 @@ import torch
 from . import _lib
 from ._lib import GdnError  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "GdnError", "abi_version"]
+__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "FwdPlan", "GdnError",
+           "abi_version", "stage_times"]
 
 _DT = {torch.float32: _lib.GDN_F32, torch.bfloat16: _lib.GDN_BF16}
 
@@ -101,6 +102,60 @@ def chunk_fwd(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
                            _ptr(ws), ws.numel(), _stream(q.device))
     _lib.check(st, "gdn_chunk_fwd")
     return o, sf
+
+
+class FwdPlan:
+    """A forward call with its outputs and workspace allocated once.
+
+    ``run()`` enqueues gdn_chunk_fwd on the stream that was current when the
+    plan was made, with cached pointers: the input tensors may be refilled in
+    place between runs, and ``o`` / ``s_final`` are overwritten each time.
+    This keeps the host cost of a call to one ctypes call."""
+
+    def __init__(self, q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
+                 cu_seqlens=None, output_final_state: bool = True):
+        lib = _lib.load()
+        _check_cu(cu_seqlens, q)
+        self._keep = (q, k, v, beta, log_alpha, s0, cu_seqlens)
+        self.problem = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
+        nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+        H, dk, dv = q.shape[2], q.shape[3], v.shape[3]
+        self.o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+        self.s_final = (torch.empty((nseq, H, dk, dv), dtype=torch.float32,
+                                    device=q.device) if output_final_state else None)
+        need = ctypes.c_size_t(0)
+        _lib.check(lib.gdn_chunk_fwd_workspace(ctypes.byref(self.problem),
+                                               ctypes.byref(need)),
+                   "gdn_chunk_fwd_workspace")
+        self.workspace = torch.empty(max(need.value, 1), dtype=torch.uint8,
+                                     device=q.device)
+        self._fn = lib.gdn_chunk_fwd
+        self._args = (ctypes.byref(self.problem), _ptr(q), _ptr(k), _ptr(v),
+                      _ptr(beta), _ptr(log_alpha), _ptr(s0), _ptr(self.o),
+                      _ptr(self.s_final), _ptr(self.workspace),
+                      self.workspace.numel(), _stream(q.device))
+
+    def run(self):
+        st = self._fn(*self._args)
+        if st != _lib.GDN_OK:
+            _lib.check(st, "gdn_chunk_fwd")
+        return self.o, self.s_final
+
+
+def stage_times(enable: Optional[bool] = None):
+    """Stage timing hook of the library.  ``stage_times(True)`` starts
+    recording HIP events around every kernel launch, ``stage_times(False)``
+    stops; ``stage_times()`` waits for the recorded events and returns
+    {stage: (total_ms, launches)} for the stages that ran, then clears."""
+    lib = _lib.load()
+    if enable is not None:
+        lib.gdn_profile_enable(1 if enable else 0)
+        return None
+    ms = (ctypes.c_double * _lib.STAGE_COUNT)()
+    cnt = (ctypes.c_int32 * _lib.STAGE_COUNT)()
+    _lib.check(lib.gdn_profile_read(ms, cnt), "gdn_profile_read")
+    return {_lib.STAGES[i]: (ms[i], cnt[i]) for i in range(_lib.STAGE_COUNT)
+            if cnt[i] > 0}
 
 
 def fwd_workspace_bytes(q, v, beta, log_alpha=None, chunk=64, cu_seqlens=None) -> int:

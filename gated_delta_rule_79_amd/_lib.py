@@ -20,8 +20,12 @@ GDN_GATE_NONE, GDN_GATE_SCALAR, GDN_GATE_CHANNEL = 0, 1, 2
 EXPORTED = (
     "gdn_abi_version", "gdn_status_str", "gdn_chunk_fwd_workspace",
     "gdn_chunk_fwd", "gdn_chunk_bwd_workspace", "gdn_chunk_bwd",
-    "gdn_decode_step", "gdn_test_set_fail_launch",
+    "gdn_decode_step", "gdn_test_set_fail_launch", "gdn_profile_enable",
+    "gdn_profile_read",
 )
+STAGE_COUNT = 8
+STAGES = ("chunk_map", "fwd_prep", "fwd_scan", "decode", "bwd_states",
+          "bwd_scan", "bwd_grad", "other")
 
 
 class GdnProblem(ctypes.Structure):
@@ -71,6 +75,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_chunk_bwd.argtypes = [pp] + [vp] * 15 + [sz, vp]
     lib.gdn_decode_step.restype = i32
     lib.gdn_decode_step.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_profile_enable.restype = None
+    lib.gdn_profile_enable.argtypes = [i32]
+    lib.gdn_profile_read.restype = i32
+    lib.gdn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int32)]
     lib.gdn_test_set_fail_launch.restype = None
     lib.gdn_test_set_fail_launch.argtypes = [i32]
     if path is None:

@@ -7,6 +7,8 @@
 
 #include <atomic>
 #include <exception>
+#include <mutex>
+#include <vector>
 
 #include "gdn.h"
 #include "gdn_internal.hpp"
@@ -103,9 +105,112 @@ gdn_status launched(hipError_t e) {
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+// ------------------------------------------------------- stage timing ---
+
+struct ProfRecord {
+  int stage;
+  hipEvent_t begin, end;
+};
+
+struct Profiler {
+  std::mutex mu;
+  std::atomic<bool> on{false};
+  std::vector<ProfRecord> done;
+  std::vector<hipEvent_t> pool;
+  std::vector<std::pair<int, hipEvent_t>> open;  // stage, begin event
+
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+Profiler& prof() {
+  static Profiler* p = new Profiler();  // never destroyed: events outlive exit
+  return *p;
+}
+
 }  // namespace
 
+namespace gdn {
+
+void prof_begin(int stage, hipStream_t s) {
+  Profiler& P = prof();
+  if (!P.on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(P.mu);
+  hipEvent_t e = P.get();
+  if (e == nullptr) return;
+  if (hipEventRecord(e, s) != hipSuccess) {
+    P.pool.push_back(e);
+    return;
+  }
+  P.open.emplace_back(stage, e);
+}
+
+void prof_end(int stage, hipStream_t s) {
+  Profiler& P = prof();
+  if (!P.on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(P.mu);
+  for (size_t i = P.open.size(); i-- > 0;) {
+    if (P.open[i].first != stage) continue;
+    hipEvent_t b = P.open[i].second;
+    P.open.erase(P.open.begin() + static_cast<long>(i));
+    hipEvent_t e = P.get();
+    if (e == nullptr || hipEventRecord(e, s) != hipSuccess) {
+      P.pool.push_back(b);
+      if (e) P.pool.push_back(e);
+      return;
+    }
+    P.done.push_back({stage, b, e});
+    return;
+  }
+}
+
+}  // namespace gdn
+
 extern "C" {
+
+void gdn_profile_enable(int enable) {
+  Profiler& P = prof();
+  std::lock_guard<std::mutex> lk(P.mu);
+  P.on.store(enable != 0);
+}
+
+gdn_status gdn_profile_read(double* total_ms, int32_t* count) {
+  try {
+    if (total_ms == nullptr || count == nullptr) return GDN_ERR_NULL;
+    for (int i = 0; i < GDN_STAGE_COUNT; ++i) {
+      total_ms[i] = 0.0;
+      count[i] = 0;
+    }
+    Profiler& P = prof();
+    std::lock_guard<std::mutex> lk(P.mu);
+    gdn_status st = GDN_OK;
+    for (const ProfRecord& r : P.done) {
+      float ms = 0.f;
+      if (hipEventSynchronize(r.end) != hipSuccess ||
+          hipEventElapsedTime(&ms, r.begin, r.end) != hipSuccess) {
+        st = GDN_ERR_HIP;
+      } else if (r.stage >= 0 && r.stage < GDN_STAGE_COUNT) {
+        total_ms[r.stage] += ms;
+        count[r.stage] += 1;
+      }
+      P.pool.push_back(r.begin);
+      P.pool.push_back(r.end);
+    }
+    P.done.clear();
+    return st;
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
 
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 

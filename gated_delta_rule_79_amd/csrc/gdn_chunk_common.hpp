@@ -85,33 +85,95 @@ template <> struct opstore<f32_t> {
   static constexpr int bytes = 4;
 };
 
+// ------------------------------------------------- operand load/store ---
+
+template <typename OP> using opvec = typename opstore<OP>::vec;
+
+// Accumulator tile stored in the operand type (4 values per lane).
+template <typename OP> struct acc4;
+template <> struct acc4<bf16_t> { using type = bf16x4; };
+template <> struct acc4<f32_t> { using type = floatx4; };
+
+__device__ inline floatx4 to_f4(const bf16x4& x) {
+  return floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+__device__ inline floatx4 to_f4(const floatx4& x) { return x; }
+template <typename OP> __device__ inline typename acc4<OP>::type from_f4(const floatx4& x);
+template <> __device__ inline bf16x4 from_f4<bf16_t>(const floatx4& x) {
+  return bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+}
+template <> __device__ inline floatx4 from_f4<f32_t>(const floatx4& x) { return x; }
+
+template <typename OP>
+__device__ inline opvec<OP> zero_vec() { return frag<OP>::zero(); }
+
+// 8 consecutive elements at element offset `off` of a global array in the
+// operand type (16-byte aligned for bf16, 32-byte for fp32).
+template <typename OP>
+__device__ inline opvec<OP> gload8(const void* base, int64_t off) {
+  return *reinterpret_cast<const opvec<OP>*>(
+      static_cast<const char*>(base) + off * opstore<OP>::bytes);
+}
+
+// Two runs of 4 elements (offsets a and b) joined into one operand vector.
+__device__ inline bf16x8 join44(const uint2& a, const uint2& b) {
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+template <typename OP>
+__device__ inline opvec<OP> gload4x2(const void* base, int64_t a, int64_t b) {
+  const char* p = static_cast<const char*>(base);
+  if constexpr (opstore<OP>::bytes == 2) {
+    return join44(*reinterpret_cast<const uint2*>(p + a * 2),
+                  *reinterpret_cast<const uint2*>(p + b * 2));
+  } else {
+    const floatx4 x = *reinterpret_cast<const floatx4*>(p + a * 4);
+    const floatx4 y = *reinterpret_cast<const floatx4*>(p + b * 4);
+    return floatx8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  }
+}
+
+template <typename OP>
+__device__ inline void to_floats(const opvec<OP>& v, float* out) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) out[s] = (float)v[s];
+}
+
+// Pack two stacked accumulator tiles into one operand fragment (permuted K).
+template <typename OP>
+__device__ inline opvec<OP> pack2(const floatx4& lo, const floatx4& hi) {
+  float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return frag<OP>::from_floats(v);
+}
+
 // -------------------------------------------------------- workspace ---
 // Per chunk-head (slot c of head h, index ch = h * nchunks + c) the forward
-// keeps, in the operand type OP (bf16 or fp32):
+// keeps, in the operand type OP (bf16 for bf16 inputs, fp32 for fp32):
 //   Wn  : -W fragments      [NB][NKD][64 lanes][8]   (W = T diag(b g) K)
-//   Qg  : Q~ fragments      [NB][NKD][64][8]         (Q~ = gamma (.) Q)
 //   Kg  : K~^T fragments    [DK/16][NKC][64][8]      (K~ = K (.) e^{g_C - g})
 //   P   : P fragments       [NB][NKC][64][8]         (masked decayed Q K^T)
-// and in fp32:
 //   U   : U accumulators    [NB][dv/16][64][4]       (U = T diag(b) V)
-//   gam : per-row decay of the state over the chunk, [DK]
+//   Qg  : Q~ fragments      [NB][NKD][64][8]         (per-channel gate only:
+//                                                     Q~ = Q (.) e^{g})
+// and in fp32 the decays  [C] gamma_r = e^{g_r}, then [DK] the per-row decay
+// of the state over the whole chunk.
 struct FwdLayout {
   int C, DK, dv, ob;           // chunk, key dim, value dim, operand bytes
-  int NB, NKD, NKC;            // C/16, ceil(DK/32), ceil(C/32)
-  size_t w, q, k, p, u, g;     // bytes per chunk-head of each buffer
+  int NB, NKD, NKC, NDT;       // C/16, ceil(DK/32), ceil(C/32), DK/16
+  size_t w, k, p, u, q, g;     // bytes per chunk-head of each buffer
   size_t per_ch;               // sum, 256-aligned pieces
-  __host__ __device__ FwdLayout(int C_, int DK_, int dv_, int ob_)
+  __host__ __device__ FwdLayout(int C_, int DK_, int dv_, int ob_, bool chan)
       : C(C_), DK(DK_), dv(dv_), ob(ob_) {
     NB = C / 16;
     NKD = (DK + 31) / 32;
     NKC = (C + 31) / 32;
+    NDT = DK / 16;
     w = al(size_t(NB) * NKD * 512 * ob);
-    q = w;
-    k = al(size_t(DK / 16) * NKC * 512 * ob);
+    k = al(size_t(NDT) * NKC * 512 * ob);
     p = al(size_t(NB) * NKC * 512 * ob);
-    u = al(size_t(C) * dv * 4);
-    g = al(size_t(DK) * 4);
-    per_ch = w + q + k + p + u + g;
+    u = al(size_t(C) * dv * ob);
+    q = chan ? w : 0;
+    g = al(size_t(C + DK) * 4);
+    per_ch = w + k + p + u + q + g;
   }
   __host__ __device__ static size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 };
@@ -119,7 +181,7 @@ struct FwdLayout {
 struct FwdBuffers {
   char* base;     // per-chunk operand area
   size_t per_ch;
-  size_t off_w, off_q, off_k, off_p, off_u, off_g;
+  size_t off_w, off_k, off_p, off_u, off_q, off_g;
   __device__ char* at(int64_t ch, size_t off) const {
     return base + static_cast<size_t>(ch) * per_ch + off;
   }
@@ -130,11 +192,11 @@ inline FwdBuffers make_buffers(char* base, const FwdLayout& L) {
   b.base = base;
   b.per_ch = L.per_ch;
   b.off_w = 0;
-  b.off_q = b.off_w + L.w;
-  b.off_k = b.off_q + L.q;
+  b.off_k = b.off_w + L.w;
   b.off_p = b.off_k + L.k;
   b.off_u = b.off_p + L.p;
-  b.off_g = b.off_u + L.u;
+  b.off_q = b.off_u + L.u;
+  b.off_g = b.off_q + L.q;
   return b;
 }
 

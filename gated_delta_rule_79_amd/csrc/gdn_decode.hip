@@ -122,6 +122,7 @@ template <int DK, typename IO, typename GT>
 hipError_t dispatch_gate(const Problem& p, dim3 grid, const void* q,
                          const void* k, const void* v, const void* beta,
                          const void* la, float* state, void* o, hipStream_t s) {
+  StageScope scope(GDN_STAGE_DECODE, s);
   switch (p.gate) {
     case GDN_GATE_NONE:
       hipLaunchKernelGGL((decode_kernel<DK, IO, GT, GDN_GATE_NONE>), grid,

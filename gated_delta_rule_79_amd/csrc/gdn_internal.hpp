@@ -22,6 +22,18 @@ struct Problem {
   int64_t nchunks;            // chunk slots per head (upper bound in varlen)
 };
 
+// Stage timing (gdn_api.hip): no-ops unless gdn_profile_enable(1).
+void prof_begin(int stage, hipStream_t s);
+void prof_end(int stage, hipStream_t s);
+
+// Brackets one kernel launch with prof_begin / prof_end.
+struct StageScope {
+  int stage;
+  hipStream_t stream;
+  StageScope(int st, hipStream_t s) : stage(st), stream(s) { prof_begin(st, s); }
+  ~StageScope() { prof_end(stage, stream); }
+};
+
 // Decode launcher (gdn_decode.hip).
 hipError_t launch_decode(const Problem& p, const void* q, const void* k,
                          const void* v, const void* beta, const void* la,

@@ -164,6 +164,27 @@ gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k,
                            const void* log_alpha, float* state, void* o,
                            void* stream);
 
+/* Stage timing, for benchmarks and profiling.  While enabled, every kernel
+ * the library enqueues is bracketed by a pair of HIP events recorded on the
+ * same stream.  gdn_profile_read waits for the recorded events, writes the
+ * summed device time (milliseconds) and the number of launches of each stage
+ * into total_ms[GDN_STAGE_COUNT] and count[GDN_STAGE_COUNT], and clears the
+ * record.  Not for use while a stream is being captured into a graph.
+ * Calls that overlap on several host threads are recorded together. */
+#define GDN_STAGE_COUNT 8
+typedef enum {
+  GDN_STAGE_CHUNK_MAP = 0,  /* varlen chunk table                         */
+  GDN_STAGE_FWD_PREP = 1,   /* per-chunk gate, UT transform, W/U/P        */
+  GDN_STAGE_FWD_SCAN = 2,   /* inter-chunk state recurrence and outputs   */
+  GDN_STAGE_DECODE = 3,     /* single-token step                          */
+  GDN_STAGE_BWD_STATES = 4, /* backward: chunk-start states               */
+  GDN_STAGE_BWD_SCAN = 5,   /* backward: reverse state-gradient pass      */
+  GDN_STAGE_BWD_GRAD = 6,   /* backward: per-chunk gradients              */
+  GDN_STAGE_OTHER = 7
+} gdn_stage;
+void gdn_profile_enable(int enable);
+gdn_status gdn_profile_read(double* total_ms, int32_t* count);
+
 /* Test hook: when set to a non-zero value every entry point returns
  * GDN_ERR_HIP after validation instead of launching (exercises the launch
  * failure path on machines without a GPU).  Not for production use. */
