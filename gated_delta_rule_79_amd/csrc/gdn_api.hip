@@ -269,6 +269,7 @@ gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes) {
     if (bytes == nullptr) return GDN_ERR_NULL;
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
+    if (!gdn::bwd_supported(pp)) return GDN_ERR_UNSUPPORTED;
     *bytes = gdn::bwd_workspace_bytes(pp);
     return GDN_OK;
   } catch (...) {
@@ -285,6 +286,7 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k,
   try {
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
+    if (!gdn::bwd_supported(pp)) return GDN_ERR_UNSUPPORTED;
     const int64_t tok = static_cast<int64_t>(pp.B) * pp.T * pp.H;
     GDN_TRY(need(q, tok * pp.dk));
     GDN_TRY(need(k, tok * pp.dk));

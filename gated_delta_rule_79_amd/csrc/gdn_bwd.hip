@@ -1,16 +1,1150 @@
-// Chunkwise backward of the gated delta rule (placeholder until the
-// backward kernels land: reports the request as unsupported).
-#include "gdn_chunk_common.hpp"
+// Chunkwise backward of the gated delta rule.
+//
+// Gradients of L = <dO, o> + <dS_final, S_final> with respect to q, k, v,
+// beta, log alpha and S_0.  The pages ("Gated Delta Networks: Improving
+// Mamba2 with Delta Rule", paper review, "Method") define the forward only;
+// this is the adjoint of the chunk form the forward kernels evaluate.  Per
+// chunk, with M0 the state at the chunk start, dM1 the gradient of the state
+// at the chunk end, and the forward's chunk quantities (T, W = T X with
+// X = diag(b gamma) K, Y = diag(b) V, U = T Y, E = U - W M0, K~, Q~, P, D):
+//
+//   reverse recurrence   dE  = P^T dO + K~ dM1
+//                        dM0 = D dM1 + Q~^T dO - W^T dE
+//   per chunk            dQ~ = dO M0^T     dW = -dE M0^T     dK~ = E dM1^T
+//                        dP  = dO E^T      dY = T^T dE       dX  = T^T dW
+//                        dT  = dE Y^T + dW X^T,   dA = -T^T dT T^T (strict lower)
+//   and then through the decays and K K^T / Q K^T into dq, dk, dbeta and the
+//   per-token gate gradient dg, whose reverse cumulative sum inside the chunk
+//   is d log alpha (the chunk-end decay D feeds the chunk's last row).
+//
+// Kernels, all on the caller's stream:
+//   1. prep (the forward prep with BWD = true): the forward operands plus the
+//      reverse recurrence's fragments K~, -W^T, P^T, Q~^T.
+//   2. forward state pass in STATES mode: the state at every chunk start.
+//   3. reverse state pass (bwd_scan_kernel): dM across chunks, one workgroup
+//      per (sequence, head, 16-column slab of dv); stores dM at every chunk
+//      end and writes dS_0.  As in the forward, a helper wave forms the
+//      chain-free terms P^T dO and Q~^T dO one chunk ahead.
+//   4. per-chunk gradients (bwd_grad_kernel), one workgroup per chunk-head,
+//      value columns in slabs; no atomics, so the result is deterministic.
+
+#include "gdn_fwd_kernels.hpp"
 
 namespace gdn {
 
-size_t bwd_workspace_bytes(const Problem& p) { (void)p; return 0; }
+namespace {
 
-hipError_t launch_bwd(const Problem&, const void*, const void*, const void*,
-                      const void*, const void*, const float*, const void*,
-                      const float*, void*, void*, void*, float*, float*,
-                      float*, void*, hipStream_t) {
-  return hipErrorNotSupported;
+// ------------------------------------------------------ reverse chain ---
+
+template <int C, int DK, typename OP, int GATE>
+struct RevOps {
+  static constexpr int NB = C / 16, NKD = (DK + 31) / 32, NKC = (C + 31) / 32,
+                       NDT = DK / 16;
+  opvec<OP> Kf[NB][NKD];   // K~ rows i, k = dk (permuted)
+  opvec<OP> Wt[NDT][NKC];  // -W^T rows dk, k = tokens (permuted)
+  floatx4 gc[GATE == GDN_GATE_CHANNEL ? NDT : 1];
+};
+
+template <int C, int DK, typename OP, int GATE>
+__device__ __forceinline__ void load_rev(RevOps<C, DK, OP, GATE>& x,
+                                         const FwdBuffers& buf, int64_t ch,
+                                         int lane, int lg) {
+  using X = RevOps<C, DK, OP, GATE>;
+  constexpr int ob = opstore<OP>::bytes;
+  const char* pk = buf.at(ch, buf.off_kf);
+  const char* pw = buf.at(ch, buf.off_wt);
+  const float* pg = reinterpret_cast<const float*>(buf.at(ch, buf.off_g)) + C;
+#pragma unroll
+  for (int rt = 0; rt < X::NB; ++rt)
+#pragma unroll
+    for (int jb = 0; jb < X::NKD; ++jb)
+      x.Kf[rt][jb] = *reinterpret_cast<const opvec<OP>*>(
+          pk + ((size_t(rt) * X::NKD + jb) * 64 + lane) * 8 * ob);
+#pragma unroll
+  for (int a = 0; a < X::NDT; ++a)
+#pragma unroll
+    for (int jb = 0; jb < X::NKC; ++jb)
+      x.Wt[a][jb] = *reinterpret_cast<const opvec<OP>*>(
+          pw + ((size_t(a) * X::NKC + jb) * 64 + lane) * 8 * ob);
+  if constexpr (GATE == GDN_GATE_CHANNEL) {
+#pragma unroll
+    for (int a = 0; a < X::NDT; ++a)
+      x.gc[a] = *reinterpret_cast<const floatx4*>(pg + 16 * a + 4 * lg);
+  } else if constexpr (GATE == GDN_GATE_SCALAR) {
+    const float g = pg[0];
+    x.gc[0] = floatx4{g, g, g, g};
+  } else {
+    x.gc[0] = floatx4{1.f, 1.f, 1.f, 1.f};
+  }
+}
+
+template <int C, int DK, typename OP>
+struct HelpOps {
+  static constexpr int NB = C / 16, NKC = (C + 31) / 32, NDT = DK / 16;
+  opvec<OP> Pt[NB][NKC];   // P^T rows i, k = r (permuted)
+  opvec<OP> Qt[NDT][NKC];  // Q~^T rows dk, k = r (permuted)
+};
+
+template <int C, int DK, typename OP>
+__device__ __forceinline__ void load_help(HelpOps<C, DK, OP>& x,
+                                          const FwdBuffers& buf, int64_t ch,
+                                          int lane) {
+  using X = HelpOps<C, DK, OP>;
+  constexpr int ob = opstore<OP>::bytes;
+  const char* pp = buf.at(ch, buf.off_pt);
+  const char* pq = buf.at(ch, buf.off_qt);
+#pragma unroll
+  for (int it = 0; it < X::NB; ++it)
+#pragma unroll
+    for (int jb = 0; jb < X::NKC; ++jb)
+      if (32 * jb + 31 >= 16 * it)
+        x.Pt[it][jb] = *reinterpret_cast<const opvec<OP>*>(
+            pp + ((size_t(it) * X::NKC + jb) * 64 + lane) * 8 * ob);
+#pragma unroll
+  for (int a = 0; a < X::NDT; ++a)
+#pragma unroll
+    for (int jb = 0; jb < X::NKC; ++jb)
+      x.Qt[a][jb] = *reinterpret_cast<const opvec<OP>*>(
+          pq + ((size_t(a) * X::NKC + jb) * 64 + lane) * 8 * ob);
+}
+
+// Reverse state pass: wave 0 carries dM backwards over the chunks of one
+// (sequence, head, 16-column slab); wave 1 computes R = P^T dO and
+// G = Q~^T dO for the chunk wave 0 takes next and hands them over in LDS.
+template <int C, int DK, typename IO, int GATE>
+__global__ __launch_bounds__(128) void bwd_scan_kernel(
+    ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ d_o,
+    const float* __restrict__ ds_final, float* __restrict__ ds0,
+    FwdBuffers buf, float* __restrict__ dstates) {
+  using OP = IO;
+  using X = RevOps<C, DK, OP, GATE>;
+  using Y = HelpOps<C, DK, OP>;
+  using E = typename io<IO>::storage;
+  constexpr int NB = X::NB, NKD = X::NKD, NKC = X::NKC, NDT = X::NDT;
+  constexpr bool CH = GATE == GDN_GATE_CHANNEL;
+  constexpr bool kPrefetch = io<IO>::bytes == 2;
+
+  __shared__ floatx4 sR[2][NB][64];
+  __shared__ floatx4 sG[2][NDT][64];
+  __shared__ __attribute__((aligned(16))) E sDO[C][16];
+
+  const int w = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int ndvt = dv / 16;
+  const int vt = w % ndvt;
+  const int chain = w / ndvt;
+  const int h = chain % H;
+  const int seq = chain / H;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+  const int col = 16 * vt + l16;
+  const int64_t sbase = (static_cast<int64_t>(seq) * H + h) * DK * dv;
+
+  int cb, ce;
+  seq_chunks(map, seq, &cb, &ce);
+  const int n = ce - cb;
+  const int64_t chl = static_cast<int64_t>(h) * nchunks + ce - 1;  // p = 0
+
+  if (wave == 0) {
+    floatx4 dM[NDT];
+#pragma unroll
+    for (int a = 0; a < NDT; ++a)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        dM[a][s] = ds_final
+            ? ds_final[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] : 0.f;
+
+    auto step = [&](const X& cur, X& nxt, int p) {
+      if (kPrefetch && p + 1 < n) load_rev<C, DK, OP, GATE>(nxt, buf, chl - p - 1, lane, lg);
+      float* st = dstates + (chl - p) * static_cast<int64_t>(DK) * dv;
+#pragma unroll
+      for (int a = 0; a < NDT; ++a)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          st[static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] = dM[a][s];
+      opvec<OP> Mb[NKD];
+#pragma unroll
+      for (int jb = 0; jb < NKD; ++jb) {
+        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+        Mb[jb] = pack2<OP>(dM[2 * jb], 2 * jb + 1 < NDT ? dM[2 * jb + 1] : z);
+      }
+      floatx4 dE[NB];
+#pragma unroll
+      for (int it = 0; it < NB; ++it) {
+        dE[it] = sR[p & 1][it][lane];
+#pragma unroll
+        for (int jb = 0; jb < NKD; ++jb) dE[it] = mma32(cur.Kf[it][jb], Mb[jb], dE[it]);
+      }
+      opvec<OP> Eb[NKC];
+#pragma unroll
+      for (int jb = 0; jb < NKC; ++jb) {
+        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+        Eb[jb] = pack2<OP>(dE[2 * jb], 2 * jb + 1 < NB ? dE[2 * jb + 1] : z);
+      }
+#pragma unroll
+      for (int a = 0; a < NDT; ++a) {
+        dM[a] = dM[a] * cur.gc[CH ? a : 0] + sG[p & 1][a][lane];
+#pragma unroll
+        for (int jb = 0; jb < NKC; ++jb) dM[a] = mma32(cur.Wt[a][jb], Eb[jb], dM[a]);
+      }
+    };
+
+    __syncthreads();  // iteration 0: wave 1 prepares p = 0
+    if constexpr (kPrefetch) {
+      X A, B;
+      if (n > 0) load_rev<C, DK, OP, GATE>(A, buf, chl, lane, lg);
+      for (int j = 1; j <= n; j += 2) {
+        step(A, B, j - 1);
+        __syncthreads();
+        if (j + 1 <= n) {
+          step(B, A, j);
+          __syncthreads();
+        }
+      }
+    } else {
+      for (int j = 1; j <= n; ++j) {
+        X A;
+        load_rev<C, DK, OP, GATE>(A, buf, chl - (j - 1), lane, lg);
+        step(A, A, j - 1);
+        __syncthreads();
+      }
+    }
+    if (ds0) {
+#pragma unroll
+      for (int a = 0; a < NDT; ++a)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          ds0[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] = dM[a][s];
+    }
+  } else {
+    // helper: R = P^T dO and G = Q~^T dO of chunk p into buffer p & 1
+    auto step = [&](const Y& cur, int p) {
+      const ChunkInfo ci = chunk_info(map, ce - 1 - p);
+      constexpr int PPR = 16 * sizeof(E) / 16;  // 16-byte pieces per row
+#pragma unroll
+      for (int u = 0; u < (C * PPR + 63) / 64; ++u) {
+        const int e = lane + 64 * u;
+        const int r = e / PPR, piece = e % PPR;
+        if (e < C * PPR) {
+          uint4 val = make_uint4(0, 0, 0, 0);
+          if (r < ci.len)
+            val = *reinterpret_cast<const uint4*>(static_cast<const char*>(d_o) +
+                (((ci.tok0 + r) * H + h) * dv + 16 * vt) * sizeof(E) + piece * 16);
+          *reinterpret_cast<uint4*>(&sDO[r][piece * (16 / sizeof(E))]) = val;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      opvec<OP> Df[NKC];
+#pragma unroll
+      for (int jb = 0; jb < NKC; ++jb) {
+        float x[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int r = 32 * jb + perm_k(lg, s);
+          x[s] = r < C ? io<IO>::load(&sDO[0][0], r * 16 + l16) : 0.f;
+        }
+        Df[jb] = frag<OP>::from_floats(x);
+      }
+#pragma unroll
+      for (int it = 0; it < NB; ++it) {
+        floatx4 R = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jb = 0; jb < NKC; ++jb)
+          if (32 * jb + 31 >= 16 * it) R = mma32(cur.Pt[it][jb], Df[jb], R);
+        sR[p & 1][it][lane] = R;
+      }
+#pragma unroll
+      for (int a = 0; a < NDT; ++a) {
+        floatx4 G = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jb = 0; jb < NKC; ++jb) G = mma32(cur.Qt[a][jb], Df[jb], G);
+        sG[p & 1][a][lane] = G;
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+    if constexpr (kPrefetch) {
+      Y A, B;
+      if (n > 0) load_help<C, DK, OP>(A, buf, chl, lane);
+      for (int j = 0; j <= n; j += 2) {
+        if (j < n) {
+          if (j + 1 < n) load_help<C, DK, OP>(B, buf, chl - j - 1, lane);
+          step(A, j);
+        }
+        __syncthreads();
+        if (j + 1 <= n) {
+          if (j + 1 < n) {
+            if (j + 2 < n) load_help<C, DK, OP>(A, buf, chl - j - 2, lane);
+            step(B, j + 1);
+          }
+          __syncthreads();
+        }
+      }
+    } else {
+      for (int j = 0; j <= n; ++j) {
+        if (j < n) {
+          Y A;
+          load_help<C, DK, OP>(A, buf, chl - j, lane);
+          step(A, j);
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------- chunk gradients ---
+
+// acc += sum_k A(m0 + row, k) B(k, n0 + col) for the 16x16 tile at (m0, n0);
+// A and B are element readers (LDS), so any transposition is free.
+template <typename OP, int KD, typename FA, typename FB>
+__device__ __forceinline__ floatx4 tmma(FA A, FB B, int m0, int n0, int l16,
+                                        int lg, floatx4 acc) {
+#pragma unroll
+  for (int kb = 0; kb < (KD + 31) / 32; ++kb) {
+    float a[8], b[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int kk = kb * 32 + 8 * lg + s;
+      a[s] = kk < KD ? A(m0 + l16, kk) : 0.f;
+      b[s] = kk < KD ? B(kk, n0 + l16) : 0.f;
+    }
+    acc = mma32(frag<OP>::from_floats(a), frag<OP>::from_floats(b), acc);
+  }
+  return acc;
+}
+
+// Sum of a 16x16 accumulator tile over its 16 columns: lanes with
+// l16 == 0 return the sums of rows 4 lg .. 4 lg + 3.
+__device__ __forceinline__ floatx4 tile_rowsum(floatx4 x) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) x[s] += __shfl_xor(x[s], m, 64);
+  return x;
+}
+
+// Sum of a 16x16 accumulator tile over its 16 rows: lanes with lg == 0
+// return the sum of column l16.
+__device__ __forceinline__ float tile_colsum(const floatx4& x) {
+  float c = x[0] + x[1] + x[2] + x[3];
+  c += __shfl_xor(c, 16, 64);
+  c += __shfl_xor(c, 32, 64);
+  return c;
+}
+
+template <int C, int DK, typename IO, int GATE, int SW>
+struct GradSmem {
+  static constexpr int ib = io<IO>::bytes;
+  static constexpr bool CH = GATE == GDN_GATE_CHANNEL;
+  static constexpr int LDK = DK + 16 / ib;   // K, Q rows (elements)
+  static constexpr int LDC = C + 1;          // fp32 C x C
+  static constexpr int LDS_ = SW + 1;        // fp32 slab rows
+  static constexpr int LDD = DK + 1;         // fp32 C x DK (post phase)
+  static constexpr int NB = C / 16, NDT = DK / 16;
+  static constexpr size_t k_off = 0;
+  static constexpr size_t q_off = k_off + size_t(C) * LDK * ib;
+  static constexpr size_t t_off = q_off + size_t(C) * LDK * ib;
+  static constexpr size_t p_off = t_off + size_t(C) * LDC * 4;
+  static constexpr size_t kk_off = p_off + size_t(C) * LDC * 4;
+  static constexpr size_t g_off = kk_off + size_t(C) * LDC * 4;
+  static constexpr size_t mid_off = g_off + size_t(CH ? C * DK : C) * 4;
+  static constexpr size_t beta_off = mid_off + size_t(CH ? DK : 1) * 4;
+  static constexpr size_t db_off = beta_off + size_t(C) * 4;
+  static constexpr size_t dd_off = db_off + size_t(C) * 4;
+  // tile partial sums: [0, NB*DK) column sums of dK~ (.) K~, then dA row
+  // sums [NB][C], then dX row sums [NDT][C]; the slab phase uses [0, C)
+  static constexpr size_t part_off = dd_off + size_t(DK) * 4;
+  static constexpr size_t part_a = size_t(NB) * DK;
+  static constexpr size_t part_x = part_a + size_t(NB) * C;
+  static constexpr size_t part_n = part_x + size_t(NDT) * C;
+  static constexpr size_t r_off = part_off + part_n * 4;
+  // slab phase: V, dO, Z, E, dE [C][SW+1]; M0, dM1 [DK][SW+1]
+  static constexpr size_t slab_bytes = (5 * size_t(C) + 2 * size_t(DK)) * LDS_ * 4;
+  // post phase: dW, then dT T^T, then the gate gradient, each [C][DK+1]
+  static constexpr size_t post_bytes = size_t(C) * (LDD > LDC ? LDD : LDC) * 4;
+  static constexpr size_t r_bytes = slab_bytes > post_bytes ? slab_bytes : post_bytes;
+  static constexpr size_t total = r_off + r_bytes;
+  static constexpr bool fits = total + 16 <= 160 * 1024;
+};
+
+template <int C, int DK, typename IO, int GATE, int SW>
+__global__ __launch_bounds__(256) void bwd_grad_kernel(
+    ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
+    const void* __restrict__ k, const void* __restrict__ v,
+    const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
+    const void* __restrict__ d_o, const float* __restrict__ states,
+    const float* __restrict__ dstates, void* __restrict__ dq,
+    void* __restrict__ dk, void* __restrict__ dvv, float* __restrict__ dbeta,
+    float* __restrict__ dla) {
+  using OP = IO;
+  using S = GradSmem<C, DK, IO, GATE, SW>;
+  static_assert(S::fits, "gradient LDS budget");
+  constexpr bool CH = GATE == GDN_GATE_CHANNEL;
+  constexpr bool SC = GATE == GDN_GATE_SCALAR;
+  constexpr int ib = S::ib;
+  constexpr int NB = C / 16, NDT = DK / 16;
+  constexpr int LDK = S::LDK, LDC = S::LDC, LS = S::LDS_, LDD = S::LDD;
+  constexpr int VW = 16 / ib;
+  constexpr int VPR = DK / VW;
+  constexpr int NCD = NB * NDT, NU = (NCD + 3) / 4;   // C x DK tiles per wave
+  constexpr int NCC = NB * NB, NUC = (NCC + 3) / 4;   // C x C tiles per wave
+  constexpr int NCS = NB * (SW / 16);                 // C x SW tiles
+
+  __shared__ __attribute__((aligned(16))) char smem[S::total];
+  __shared__ int s_span_bits;
+  char* sK = smem + S::k_off;
+  char* sQ = smem + S::q_off;
+  float* sT = reinterpret_cast<float*>(smem + S::t_off);
+  float* sP = reinterpret_cast<float*>(smem + S::p_off);
+  float* sKK = reinterpret_cast<float*>(smem + S::kk_off);
+  float* sg = reinterpret_cast<float*>(smem + S::g_off);
+  float* smid = reinterpret_cast<float*>(smem + S::mid_off);
+  float* sbeta = reinterpret_cast<float*>(smem + S::beta_off);
+  float* sdb = reinterpret_cast<float*>(smem + S::db_off);
+  float* sdD = reinterpret_cast<float*>(smem + S::dd_off);
+  float* spart = reinterpret_cast<float*>(smem + S::part_off);
+  float* sR = reinterpret_cast<float*>(smem + S::r_off);
+  // slab phase views
+  float* sV = sR;
+  float* sDO = sV + C * LS;
+  float* sZ = sDO + C * LS;
+  float* sE = sZ + C * LS;
+  float* sDE = sE + C * LS;
+  float* sM0 = sDE + C * LS;
+  float* sDM1 = sM0 + DK * LS;
+  // post phase views
+  float* sDW = sR;
+
+  const int L = blockIdx.x;
+  const int c = static_cast<int>(L / H);
+  const int h = L - c * H;
+  const ChunkInfo ci = chunk_info(map, c);
+  if (ci.seq < 0) return;
+  const int len = ci.len;
+  const int64_t tok0 = ci.tok0;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int64_t ch = static_cast<int64_t>(h) * nchunks + c;
+  const float* M0g = states + ch * DK * dv;
+  const float* dM1g = dstates + ch * DK * dv;
+
+  // ---- 0. gates, beta, K and Q rows ----------------------------------------
+  if (tid == 0) s_span_bits = 0;
+  if (tid < C) {
+    sbeta[tid] = tid < len ? load_gate(beta, (tok0 + tid) * H + h, gbf) : 0.f;
+    sdb[tid] = 0.f;
+  }
+  for (int d = tid; d < DK; d += 256) sdD[d] = 0.f;
+  if constexpr (!CH) {
+    if (wave == 0) {
+      float x = 0.f;
+      if constexpr (SC)
+        if (lane < len) x = load_gate(la, (tok0 + lane) * H + h, gbf);
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+      }
+      if (lane < C) sg[lane] = x;
+    }
+  } else {
+    for (int e = tid; e < C * DK; e += 256) {
+      const int r = e / DK, cc = e % DK;
+      sg[e] = r < len ? load_gate(la, ((tok0 + r) * H + h) * DK + cc, gbf) : 0.f;
+    }
+  }
+  for (int e = tid; e < C * VPR; e += 256) {
+    const int r = e / VPR, cv = (e % VPR) * VW;
+    uint4 rk = make_uint4(0, 0, 0, 0), rq = make_uint4(0, 0, 0, 0);
+    if (r < len) {
+      const int64_t off = (((tok0 + r) * H + h) * DK + cv) * ib;
+      rk = *reinterpret_cast<const uint4*>(static_cast<const char*>(k) + off);
+      rq = *reinterpret_cast<const uint4*>(static_cast<const char*>(q) + off);
+    }
+    *reinterpret_cast<uint4*>(sK + (size_t(r) * LDK + cv) * ib) = rk;
+    *reinterpret_cast<uint4*>(sQ + (size_t(r) * LDK + cv) * ib) = rq;
+  }
+  __syncthreads();
+  if constexpr (CH) {
+    for (int cc = tid; cc < DK; cc += 256) {
+      float x = 0.f, mx = -3.0e38f, mn = 3.0e38f;
+      for (int r = 0; r < C; ++r) {
+        x += sg[r * DK + cc];
+        sg[r * DK + cc] = x;
+        mx = fmaxf(mx, x);
+        mn = fminf(mn, x);
+      }
+      smid[cc] = 0.5f * (mx + mn);
+      atomicMax(&s_span_bits, __float_as_int(0.5f * (mx - mn)));
+    }
+  }
+  __syncthreads();
+
+  // element readers of the chunk's matrices
+  auto Kr = [&](int r, int d) { return lds_ld<IO>(sK, size_t(r) * LDK + d); };
+  auto Qr = [&](int r, int d) { return lds_ld<IO>(sQ, size_t(r) * LDK + d); };
+  // decays: gamma_r (per row / per (row, channel)), chunk-end relative decay
+  auto gq = [&](int r, int d) -> float {
+    if constexpr (CH) return expf(sg[r * DK + d]);
+    else if constexpr (SC) return expf(sg[r]);
+    else return 1.f;
+  };
+  auto gk = [&](int r, int d) -> float {
+    if constexpr (CH) return expf(sg[(C - 1) * DK + d] - sg[r * DK + d]);
+    else if constexpr (SC) return expf(sg[C - 1] - sg[r]);
+    else return 1.f;
+  };
+  auto gl = [&](int d) -> float {
+    if constexpr (CH) return expf(sg[(C - 1) * DK + d]);
+    else if constexpr (SC) return expf(sg[C - 1]);
+    else return 1.f;
+  };
+  // factored per-channel decays around the channel's midpoint
+  auto up = [&](int r, int d) -> float {   // e^{g - mid}
+    if constexpr (CH) return expf(sg[r * DK + d] - smid[d]);
+    else return 1.f;
+  };
+  auto dn = [&](int r, int d) -> float {   // e^{mid - g}
+    if constexpr (CH) return expf(smid[d] - sg[r * DK + d]);
+    else return 1.f;
+  };
+  auto dec = [&](int r, int i) -> float {  // scalar pairwise decay, i <= r
+    if constexpr (SC) return expf(sg[r] - sg[i]);
+    else return 1.f;
+  };
+  auto Xr = [&](int r, int d) { return Kr(r, d) * sbeta[r] * gq(r, d); };
+  bool exact = false;
+  if constexpr (CH) exact = __int_as_float(s_span_bits) > kChannelHalfSpan;
+
+  // ---- 1. KK = decayed K K^T (strict lower) and P (lower) ------------------
+  if (!exact) {
+    for (int t = wave; t < NCC; t += 4) {
+      const int mt = t / NB, nt = t % NB;
+      if (nt > mt) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          sKK[(16 * mt + 4 * lg + s) * LDC + 16 * nt + l16] = 0.f;
+          sP[(16 * mt + 4 * lg + s) * LDC + 16 * nt + l16] = 0.f;
+        }
+        continue;
+      }
+      floatx4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+      a = tmma<OP, DK>([&](int r, int d) { return Kr(r, d) * up(r, d); },
+                       [&](int d, int i) { return Kr(i, d) * dn(i, d); },
+                       16 * mt, 16 * nt, l16, lg, a);
+      b = tmma<OP, DK>([&](int r, int d) { return Qr(r, d) * up(r, d); },
+                       [&](int d, int i) { return Kr(i, d) * dn(i, d); },
+                       16 * mt, 16 * nt, l16, lg, b);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int r = 16 * mt + 4 * lg + s, i = 16 * nt + l16;
+        sKK[r * LDC + i] = i < r ? a[s] * dec(r, i) : 0.f;
+        sP[r * LDC + i] = i <= r ? b[s] * dec(r, i) : 0.f;
+      }
+    }
+  } else if constexpr (CH) {
+    for (int e = tid; e < C * C; e += 256) {
+      const int r = e / C, i = e % C;
+      float kv = 0.f, pv = 0.f;
+      if (i <= r) {
+        for (int d = 0; d < DK; ++d) {
+          const float dd = expf(sg[r * DK + d] - sg[i * DK + d]);
+          const float ki = Kr(i, d) * dd;
+          kv += Kr(r, d) * ki;
+          pv += Qr(r, d) * ki;
+        }
+      }
+      sKK[r * LDC + i] = i < r ? kv : 0.f;
+      sP[r * LDC + i] = pv;
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. T = (I + diag(beta) KK)^-1 ---------------------------------------
+  float* sZb = sR;  // 4 x 16 x 16 scratch of the block inverse
+  if (wave == 0) {
+    const int b = lane >> 4, j = lane & 15;
+    if (b < NB) {
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = 0.f;
+        const float br = sbeta[16 * b + r];
+#pragma unroll
+        for (int i = 0; i < r; ++i) s += br * sKK[(16 * b + r) * LDC + 16 * b + i] * x[i];
+        x[r] = (r == j) ? 1.f : (r < j ? 0.f : -s);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sT[(16 * b + r) * LDC + 16 * b + j] = x[r];
+    }
+  } else {
+    for (int e = tid - 64; e < C * C; e += 192) {
+      const int r = e / C, i = e % C;
+      if ((i >> 4) > (r >> 4)) sT[r * LDC + i] = 0.f;
+    }
+  }
+  __syncthreads();
+  for (int b = 1; b < NB; ++b) {
+    if (wave < b) {
+      const int a = wave;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = lane * 4 + u, r = e >> 4, cc = e & 15;
+        const float br = sbeta[16 * b + r];
+        float z = 0.f;
+        for (int jj = a; jj < b; ++jj) {
+#pragma unroll
+          for (int s = 0; s < 16; ++s)
+            z += br * sKK[(16 * b + r) * LDC + 16 * jj + s] * sT[(16 * jj + s) * LDC + 16 * a + cc];
+        }
+        sZb[(a * 16 + r) * 16 + cc] = z;
+      }
+    }
+    __syncthreads();
+    if (wave < b) {
+      const int a = wave;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = lane * 4 + u, r = e >> 4, cc = e & 15;
+        float t = 0.f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+          t += sT[(16 * b + r) * LDC + 16 * b + s] * sZb[(a * 16 + s) * 16 + cc];
+        sT[(16 * b + r) * LDC + 16 * a + cc] = -t;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- 3. value slabs: accumulate everything that contracts over dv -------
+  floatx4 aQ[NU], aW[NU], aK[NU];   // dQ~, -dW, dK~   (C x DK tiles)
+  floatx4 aP[NUC], aT[NUC];         // dP, dE Y^T      (C x C tiles)
+#pragma unroll
+  for (int u = 0; u < NU; ++u) aQ[u] = aW[u] = aK[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < NUC; ++u) aP[u] = aT[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int s0 = 0; s0 < dv; s0 += SW) {
+    // stage V, dO (rows of the chunk) and M0, dM1 (rows dk) for this slab
+    for (int e = tid; e < C * SW; e += 256) {
+      const int r = e / SW, j = e % SW;
+      float vv = 0.f, gg = 0.f;
+      if (r < len) {
+        const int64_t off = ((tok0 + r) * H + h) * dv + s0 + j;
+        vv = io<IO>::load(v, off);
+        gg = io<IO>::load(d_o, off);
+      }
+      sV[r * LS + j] = vv;
+      sDO[r * LS + j] = gg;
+    }
+    for (int e = tid; e < DK * SW; e += 256) {
+      const int d = e / SW, j = e % SW;
+      sM0[d * LS + j] = M0g[static_cast<int64_t>(d) * dv + s0 + j];
+      sDM1[d * LS + j] = dM1g[static_cast<int64_t>(d) * dv + s0 + j];
+    }
+    __syncthreads();
+    // Z = Y - X M0 (Y = diag(b) V),  dE = P^T dO + K~ dM1
+    for (int t = wave; t < 2 * NCS; t += 4) {
+      const int tt = t % NCS, mt = tt / (SW / 16), nt = tt % (SW / 16);
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (t < NCS) {
+        acc = tmma<OP, DK>(Xr, [&](int d, int j) { return sM0[d * LS + j]; },
+                           16 * mt, 16 * nt, l16, lg, acc);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int r = 16 * mt + 4 * lg + s, j = 16 * nt + l16;
+          sZ[r * LS + j] = sbeta[r] * sV[r * LS + j] - acc[s];
+        }
+      } else {
+        acc = tmma<OP, C>([&](int i, int r) { return sP[r * LDC + i]; },
+                          [&](int r, int j) { return sDO[r * LS + j]; },
+                          16 * mt, 16 * nt, l16, lg, acc);
+        acc = tmma<OP, DK>([&](int i, int d) { return Kr(i, d) * gk(i, d); },
+                           [&](int d, int j) { return sDM1[d * LS + j]; },
+                           16 * mt, 16 * nt, l16, lg, acc);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          sDE[(16 * mt + 4 * lg + s) * LS + 16 * nt + l16] = acc[s];
+      }
+    }
+    __syncthreads();
+    // E = T Z;  dY = T^T dE -> dv = b dY and dbeta += rowsum(dY V)
+    for (int t = wave; t < 2 * NCS; t += 4) {
+      const int tt = t % NCS, mt = tt / (SW / 16), nt = tt % (SW / 16);
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (t < NCS) {
+        acc = tmma<OP, C>([&](int r, int i) { return sT[r * LDC + i]; },
+                          [&](int i, int j) { return sZ[i * LS + j]; },
+                          16 * mt, 16 * nt, l16, lg, acc);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          sE[(16 * mt + 4 * lg + s) * LS + 16 * nt + l16] = acc[s];
+      } else {
+        acc = tmma<OP, C>([&](int i, int r) { return sT[r * LDC + i]; },
+                          [&](int r, int j) { return sDE[r * LS + j]; },
+                          16 * mt, 16 * nt, l16, lg, acc);
+        floatx4 pv;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int i = 16 * mt + 4 * lg + s, j = 16 * nt + l16;
+          pv[s] = acc[s] * sV[i * LS + j];
+          if (i < len)
+            io<IO>::store(dvv, ((tok0 + i) * H + h) * dv + s0 + j, sbeta[i] * acc[s]);
+        }
+        pv = tile_rowsum(pv);
+        // one column tile per slab when SW == 16: fixed owner, fixed order
+        if (l16 == 0) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) spart[nt * C + 16 * mt + 4 * lg + s] = pv[s];
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < C) {
+      float acc = sdb[tid];
+      for (int nt = 0; nt < SW / 16; ++nt) acc += spart[nt * C + tid];
+      sdb[tid] = acc;
+    }
+    for (int d = tid; d < DK; d += 256) {
+      float acc = 0.f;
+      for (int j = 0; j < SW; ++j) acc += sM0[d * LS + j] * sDM1[d * LS + j];
+      sdD[d] += acc;
+    }
+    // register accumulators (contractions over the slab's columns)
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int t = wave + 4 * u;
+      if (t >= NCD) continue;
+      const int mt = t / NDT, nt = t % NDT;
+      auto M0t = [&](int j, int d) { return sM0[d * LS + j]; };
+      aQ[u] = tmma<OP, SW>([&](int r, int j) { return sDO[r * LS + j]; }, M0t,
+                           16 * mt, 16 * nt, l16, lg, aQ[u]);
+      aW[u] = tmma<OP, SW>([&](int r, int j) { return sDE[r * LS + j]; }, M0t,
+                           16 * mt, 16 * nt, l16, lg, aW[u]);
+      aK[u] = tmma<OP, SW>([&](int r, int j) { return sE[r * LS + j]; },
+                           [&](int j, int d) { return sDM1[d * LS + j]; },
+                           16 * mt, 16 * nt, l16, lg, aK[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < NUC; ++u) {
+      const int t = wave + 4 * u;
+      if (t >= NCC) continue;
+      const int mt = t / NB, nt = t % NB;
+      aP[u] = tmma<OP, SW>([&](int r, int j) { return sDO[r * LS + j]; },
+                           [&](int j, int i) { return sE[i * LS + j]; },
+                           16 * mt, 16 * nt, l16, lg, aP[u]);
+      aT[u] = tmma<OP, SW>([&](int r, int j) { return sDE[r * LS + j]; },
+                           [&](int j, int i) { return sbeta[i] * sV[i * LS + j]; },
+                           16 * mt, 16 * nt, l16, lg, aT[u]);
+    }
+    __syncthreads();
+  }
+
+  // ---- 4. post: through T, the decays and K K^T / Q K^T --------------------
+  // dq = dQ~ (.) gamma + dq_P ; dk = dK~ (.) e^{g_C - g} + dX (.) b gamma + ...
+  // dg collects the per-(row, channel) gate gradient.
+  floatx4 oq[NU], ok[NU], og[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int t = wave + 4 * u;
+    oq[u] = ok[u] = og[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (t >= NCD) continue;
+    const int mt = t / NDT, nt = t % NDT;
+    floatx4 cs;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r = 16 * mt + 4 * lg + s, d = 16 * nt + l16;
+      const float eq = gq(r, d), ek = gk(r, d);
+      oq[u][s] = aQ[u][s] * eq;
+      ok[u][s] = aK[u][s] * ek;
+      const float kt = aK[u][s] * Kr(r, d) * ek;  // dK~ (.) K~
+      og[u][s] = aQ[u][s] * Qr(r, d) * eq - kt;
+      cs[s] = kt;
+    }
+    // the chunk-end decay e^{g_C} of K~ sends sum_i dK~ (.) K~ to the last row
+    const float colsum = tile_colsum(cs);
+    if (lg == 0) spart[mt * DK + 16 * nt + l16] = colsum;
+  }
+  // dW into LDS (dW = -aW), dP decayed into sP (overwrites P)
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int t = wave + 4 * u;
+    if (t >= NCD) continue;
+    const int mt = t / NDT, nt = t % NDT;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      sDW[(16 * mt + 4 * lg + s) * LDD + 16 * nt + l16] = -aW[u][s];
+  }
+  __syncthreads();  // all P reads of the slab phase are done
+#pragma unroll
+  for (int u = 0; u < NUC; ++u) {
+    const int t = wave + 4 * u;
+    if (t >= NCC) continue;
+    const int mt = t / NB, nt = t % NB;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r = 16 * mt + 4 * lg + s, i = 16 * nt + l16;
+      sP[r * LDC + i] = i <= r ? aP[u][s] * dec(r, i) : 0.f;
+    }
+  }
+  __syncthreads();
+  // dX = T^T dW ;  dq_P, dk_P ;  dT = dE Y^T + dW X^T (kept in registers)
+  floatx4 oX[NU];
+#pragma unroll
+  for (int u = 0; u < NUC; ++u) {
+    const int t = wave + 4 * u;
+    if (t >= NCC) continue;
+    const int mt = t / NB, nt = t % NB;
+    aT[u] = tmma<OP, DK>([&](int r, int d) { return sDW[r * LDD + d]; },
+                         [&](int d, int i) { return Xr(i, d); },
+                         16 * mt, 16 * nt, l16, lg, aT[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int t = wave + 4 * u;
+    oX[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (t >= NCD) continue;
+    const int mt = t / NDT, nt = t % NDT;
+    oX[u] = tmma<OP, C>([&](int i, int r) { return sT[r * LDC + i]; },
+                        [&](int r, int d) { return sDW[r * LDD + d]; },
+                        16 * mt, 16 * nt, l16, lg, oX[u]);
+    // dq_P = (dP o Gamma) K  (channel: factored around the midpoint)
+    floatx4 tq = {0.f, 0.f, 0.f, 0.f};
+    tq = tmma<OP, C>([&](int r, int i) { return sP[r * LDC + i]; },
+                     [&](int i, int d) { return Kr(i, d) * dn(i, d); },
+                     16 * mt, 16 * nt, l16, lg, tq);
+    // dk_P = (dP o Gamma)^T Q
+    floatx4 tk = {0.f, 0.f, 0.f, 0.f};
+    tk = tmma<OP, C>([&](int i, int r) { return sP[r * LDC + i]; },
+                     [&](int r, int d) { return Qr(r, d) * up(r, d); },
+                     16 * mt, 16 * nt, l16, lg, tk);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r = 16 * mt + 4 * lg + s, d = 16 * nt + l16;
+      const float vq = tq[s] * up(r, d), vk = tk[s] * dn(r, d);
+      oq[u][s] += vq;
+      ok[u][s] += vk;
+      og[u][s] += Qr(r, d) * vq - Kr(r, d) * vk;
+    }
+  }
+  __syncthreads();
+  // dT into sP (dP is consumed)
+  float* sDT = sP;
+#pragma unroll
+  for (int u = 0; u < NUC; ++u) {
+    const int t = wave + 4 * u;
+    if (t >= NCC) continue;
+    const int mt = t / NB, nt = t % NB;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sDT[(16 * mt + 4 * lg + s) * LDC + 16 * nt + l16] = aT[u][s];
+  }
+  __syncthreads();
+  // Z2 = dT T^T into the dW bytes (dW is consumed)
+  float* sZ2 = sR;
+#pragma unroll
+  for (int u = 0; u < NUC; ++u) {
+    const int t = wave + 4 * u;
+    if (t >= NCC) continue;
+    const int mt = t / NB, nt = t % NB;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tmma<OP, C>([&](int r, int cc) { return sDT[r * LDC + cc]; },
+                      [&](int cc, int i) { return sT[i * LDC + cc]; },
+                      16 * mt, 16 * nt, l16, lg, acc);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sZ2[(16 * mt + 4 * lg + s) * LDC + 16 * nt + l16] = acc[s];
+  }
+  __syncthreads();
+  // dA = -T^T Z2 (strict lower); dbeta += rowsum(dA (.) KK); b (.) dA (scalar
+  // gate: with the pairwise decay) replaces dT in sP
+  float* sDA = sP;
+#pragma unroll
+  for (int u = 0; u < NUC; ++u) {
+    const int t = wave + 4 * u;
+    if (t >= NCC) continue;
+    const int mt = t / NB, nt = t % NB;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tmma<OP, C>([&](int a, int r) { return sT[r * LDC + a]; },
+                      [&](int r, int b) { return sZ2[r * LDC + b]; },
+                      16 * mt, 16 * nt, l16, lg, acc);
+    aT[u] = acc;
+  }
+  __syncthreads();  // every read of dT is done before dA overwrites it
+#pragma unroll
+  for (int u = 0; u < NUC; ++u) {
+    const int t = wave + 4 * u;
+    if (t >= NCC) continue;
+    const int mt = t / NB, nt = t % NB;
+    floatx4 pb;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int a = 16 * mt + 4 * lg + s, b = 16 * nt + l16;
+      const float da = b < a ? -aT[u][s] : 0.f;
+      pb[s] = da * sKK[a * LDC + b];
+      sDA[a * LDC + b] = b < a ? da * sbeta[a] * dec(a, b) : 0.f;
+    }
+    pb = tile_rowsum(pb);
+    if (l16 == 0) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) spart[S::part_a + nt * C + 16 * mt + 4 * lg + s] = pb[s];
+    }
+  }
+  __syncthreads();
+  // dk_A1 = (b dA o Gamma) K, dk_A2 = (b dA o Gamma)^T K, and the dX terms
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int t = wave + 4 * u;
+    if (t >= NCD) continue;
+    const int mt = t / NDT, nt = t % NDT;
+    floatx4 t1 = {0.f, 0.f, 0.f, 0.f}, t2 = {0.f, 0.f, 0.f, 0.f};
+    t1 = tmma<OP, C>([&](int r, int i) { return sDA[r * LDC + i]; },
+                     [&](int i, int d) { return Kr(i, d) * dn(i, d); },
+                     16 * mt, 16 * nt, l16, lg, t1);
+    t2 = tmma<OP, C>([&](int i, int r) { return sDA[r * LDC + i]; },
+                     [&](int r, int d) { return Kr(r, d) * up(r, d); },
+                     16 * mt, 16 * nt, l16, lg, t2);
+    floatx4 pb;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r = 16 * mt + 4 * lg + s, d = 16 * nt + l16;
+      const float v1 = t1[s] * up(r, d), v2 = t2[s] * dn(r, d);
+      const float kr = Kr(r, d), eq = gq(r, d);
+      ok[u][s] += v1 + v2 + oX[u][s] * sbeta[r] * eq;
+      og[u][s] += kr * (v1 - v2) + oX[u][s] * sbeta[r] * eq * kr;
+      pb[s] = oX[u][s] * kr * eq;
+    }
+    pb = tile_rowsum(pb);
+    if (l16 == 0) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) spart[S::part_x + nt * C + 16 * mt + 4 * lg + s] = pb[s];
+    }
+  }
+  __syncthreads();
+  if (tid < C) {
+    float acc = sdb[tid];
+    for (int nt = 0; nt < NB; ++nt) acc += spart[S::part_a + nt * C + tid];
+    for (int nt = 0; nt < NDT; ++nt) acc += spart[S::part_x + nt * C + tid];
+    if (tid < len) dbeta[(tok0 + tid) * H + h] = acc;
+  }
+  // last row: sum_i dK~ (.) K~ and the chunk-end decay of the state
+  float* sdg = sR;  // [C][DK+1] gate gradient per (row, channel)
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int t = wave + 4 * u;
+    if (t >= NCD) continue;
+    const int mt = t / NDT, nt = t % NDT;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r = 16 * mt + 4 * lg + s, d = 16 * nt + l16;
+      float x = og[u][s];
+      if (r == C - 1) {
+        float cs = 0.f;
+        for (int b = 0; b < NB; ++b) cs += spart[b * DK + d];
+        x += cs + gl(d) * sdD[d];
+      }
+      sdg[r * LDD + d] = x;
+      if (r < len) {
+        const int64_t off = ((tok0 + r) * H + h) * DK + d;
+        io<IO>::store(dq, off, oq[u][s]);
+        io<IO>::store(dk, off, ok[u][s]);
+      }
+    }
+  }
+  __syncthreads();
+  // d log alpha = reverse cumulative sum of dg inside the chunk
+  if constexpr (CH) {
+    for (int d = tid; d < DK; d += 256) {
+      float acc = 0.f;
+      for (int r = C - 1; r >= 0; --r) {
+        acc += sdg[r * LDD + d];
+        if (r < len) dla[((tok0 + r) * H + h) * DK + d] = acc;
+      }
+    }
+  } else if constexpr (SC) {
+    if (tid < C) {
+      float x = 0.f;
+      for (int d = 0; d < DK; ++d) x += sdg[tid * LDD + d];
+      spart[tid] = x;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float acc = 0.f;
+      for (int r = C - 1; r >= 0; --r) {
+        acc += spart[r];
+        if (r < len) dla[(tok0 + r) * H + h] = acc;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ dispatch ---
+
+struct BwdWs {
+  FwdBuffers buf;
+  ChunkMap map;
+  float* states;
+  float* dstates;
+};
+
+inline size_t bwd_states_bytes(const Problem& p) {
+  return FwdLayout::al(size_t(p.nchunks) * p.H * p.dk * p.dv * 4);
+}
+
+constexpr int kSlab = 16;  // value columns per slab of the gradient kernel
+
+template <int C, int DK, typename IO, int GATE>
+hipError_t run_bwd(const Problem& p, const void* q, const void* k,
+                   const void* v, const void* beta, const void* la,
+                   const float* s0, const void* d_o, const float* ds_final,
+                   void* dq, void* dk, void* dv, float* dbeta, float* dla,
+                   float* ds0, char* ws, hipStream_t s) {
+  constexpr int SW = kSlab;
+  if constexpr (!GradSmem<C, DK, IO, GATE, SW>::fits) {
+    return hipErrorNotSupported;
+  } else {
+  const FwdLayout L(C, DK, p.dv, opstore<IO>::bytes, GATE == GDN_GATE_CHANNEL, true);
+  char* map_base = ws;
+  char* ops = ws + chunk_map_bytes(p);
+  const FwdBuffers buf = make_buffers(ops, L);
+  float* states = reinterpret_cast<float*>(ops + size_t(p.nchunks) * p.H * L.per_ch);
+  float* dstates = reinterpret_cast<float*>(reinterpret_cast<char*>(states) + bwd_states_bytes(p));
+  const ChunkMap map = make_chunk_map(p, map_base);
+  const bool gbf = p.gdt == GDN_BF16;
+  hipError_t e;
+  if (p.varlen) {
+    e = launch_chunk_map(p, map_base, s);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t nwork = static_cast<int64_t>(p.nseq) * p.H * (p.dv / 16);
+  const int64_t qb = static_cast<int64_t>(p.B) * p.T * p.H * DK * io<IO>::bytes;
+  const uint32_t q_bytes = qb < (int64_t(1) << 31) ? static_cast<uint32_t>(qb) : 0u;
+  if (p.nchunks > 0) {
+    {
+      StageScope scope(GDN_STAGE_FWD_PREP, s);
+      hipLaunchKernelGGL((fwd_prep_kernel<C, DK, IO, GATE, true>),
+                         dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(256), 0, s,
+                         map, p.H, p.dv, p.nchunks, q, k, v, beta, la, gbf, buf);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    {
+      StageScope scope(GDN_STAGE_BWD_STATES, s);
+      hipLaunchKernelGGL((fwd_scan_kernel<C, DK, IO, GATE, true>),
+                         dim3(static_cast<unsigned>(nwork)), dim3(128), 0, s, map,
+                         p.H, p.dv, p.nchunks, q, q_bytes, s0, static_cast<void*>(nullptr),
+                         static_cast<float*>(nullptr), buf, states);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  {
+    StageScope scope(GDN_STAGE_BWD_SCAN, s);
+    hipLaunchKernelGGL((bwd_scan_kernel<C, DK, IO, GATE>),
+                       dim3(static_cast<unsigned>(nwork)), dim3(128), 0, s, map,
+                       p.H, p.dv, p.nchunks, d_o, ds_final, ds0, buf, dstates);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.nchunks > 0) {
+    StageScope scope(GDN_STAGE_BWD_GRAD, s);
+    hipLaunchKernelGGL((bwd_grad_kernel<C, DK, IO, GATE, SW>),
+                       dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(256), 0, s,
+                       map, p.H, p.dv, p.nchunks, q, k, v, beta, la, gbf, d_o,
+                       states, dstates, dq, dk, dv, dbeta, dla);
+    e = hipGetLastError();
+  }
+  return e;
+  }
+}
+
+template <int C, int DK, typename IO>
+bool fits_gate(int gate) {
+  switch (gate) {
+    case GDN_GATE_NONE: return GradSmem<C, DK, IO, GDN_GATE_NONE, kSlab>::fits;
+    case GDN_GATE_SCALAR: return GradSmem<C, DK, IO, GDN_GATE_SCALAR, kSlab>::fits;
+    default: return GradSmem<C, DK, IO, GDN_GATE_CHANNEL, kSlab>::fits;
+  }
+}
+
+template <int C>
+bool fits_dk(const Problem& p) {
+  const bool bf = p.io == GDN_BF16;
+  switch (p.dk) {
+    case 16: return bf ? fits_gate<C, 16, bf16_t>(p.gate) : fits_gate<C, 16, f32_t>(p.gate);
+    case 32: return bf ? fits_gate<C, 32, bf16_t>(p.gate) : fits_gate<C, 32, f32_t>(p.gate);
+    case 64: return bf ? fits_gate<C, 64, bf16_t>(p.gate) : fits_gate<C, 64, f32_t>(p.gate);
+    default: return bf ? fits_gate<C, 128, bf16_t>(p.gate) : fits_gate<C, 128, f32_t>(p.gate);
+  }
+}
+
+template <int C, int DK, typename IO>
+hipError_t bwd_gate(const Problem& p, const void* q, const void* k,
+                    const void* v, const void* beta, const void* la,
+                    const float* s0, const void* d_o, const float* dsf,
+                    void* dq, void* dk, void* dv, float* db, float* dla,
+                    float* ds0, char* ws, hipStream_t s) {
+  switch (p.gate) {
+    case GDN_GATE_NONE:
+      return run_bwd<C, DK, IO, GDN_GATE_NONE>(p, q, k, v, beta, la, s0, d_o, dsf, dq, dk, dv, db, dla, ds0, ws, s);
+    case GDN_GATE_SCALAR:
+      return run_bwd<C, DK, IO, GDN_GATE_SCALAR>(p, q, k, v, beta, la, s0, d_o, dsf, dq, dk, dv, db, dla, ds0, ws, s);
+    default:
+      return run_bwd<C, DK, IO, GDN_GATE_CHANNEL>(p, q, k, v, beta, la, s0, d_o, dsf, dq, dk, dv, db, dla, ds0, ws, s);
+  }
+}
+
+template <int C, int DK>
+hipError_t bwd_types(const Problem& p, const void* q, const void* k,
+                     const void* v, const void* beta, const void* la,
+                     const float* s0, const void* d_o, const float* dsf,
+                     void* dq, void* dk, void* dv, float* db, float* dla,
+                     float* ds0, char* ws, hipStream_t s) {
+  if (p.io == GDN_BF16)
+    return bwd_gate<C, DK, bf16_t>(p, q, k, v, beta, la, s0, d_o, dsf, dq, dk, dv, db, dla, ds0, ws, s);
+  return bwd_gate<C, DK, f32_t>(p, q, k, v, beta, la, s0, d_o, dsf, dq, dk, dv, db, dla, ds0, ws, s);
+}
+
+template <int C>
+hipError_t bwd_dk(const Problem& p, const void* q, const void* k,
+                  const void* v, const void* beta, const void* la,
+                  const float* s0, const void* d_o, const float* dsf,
+                  void* dq, void* dk, void* dv, float* db, float* dla,
+                  float* ds0, char* ws, hipStream_t s) {
+  switch (p.dk) {
+    case 16: return bwd_types<C, 16>(p, q, k, v, beta, la, s0, d_o, dsf, dq, dk, dv, db, dla, ds0, ws, s);
+    case 32: return bwd_types<C, 32>(p, q, k, v, beta, la, s0, d_o, dsf, dq, dk, dv, db, dla, ds0, ws, s);
+    case 64: return bwd_types<C, 64>(p, q, k, v, beta, la, s0, d_o, dsf, dq, dk, dv, db, dla, ds0, ws, s);
+    default: return bwd_types<C, 128>(p, q, k, v, beta, la, s0, d_o, dsf, dq, dk, dv, db, dla, ds0, ws, s);
+  }
+}
+
+}  // namespace
+
+bool bwd_supported(const Problem& p) {
+  switch (p.chunk) {
+    case 16: return fits_dk<16>(p);
+    case 32: return fits_dk<32>(p);
+    default: return fits_dk<64>(p);
+  }
+}
+
+size_t bwd_workspace_bytes(const Problem& p) {
+  const FwdLayout L(p.chunk, p.dk, p.dv, p.io == GDN_BF16 ? 2 : 4,
+                    p.gate == GDN_GATE_CHANNEL, true);
+  return chunk_map_bytes(p) + size_t(p.nchunks) * p.H * L.per_ch +
+         2 * bwd_states_bytes(p);
+}
+
+hipError_t launch_bwd(const Problem& p, const void* q, const void* k,
+                      const void* v, const void* beta, const void* la,
+                      const float* s0, const void* d_o, const float* ds_final,
+                      void* dq, void* dk, void* dv, float* dbeta, float* dla,
+                      float* ds0, void* ws, hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  switch (p.chunk) {
+    case 16: return bwd_dk<16>(p, q, k, v, beta, la, s0, d_o, ds_final, dq, dk, dv, dbeta, dla, ds0, w, s);
+    case 32: return bwd_dk<32>(p, q, k, v, beta, la, s0, d_o, ds_final, dq, dk, dv, dbeta, dla, ds0, w, s);
+    default: return bwd_dk<64>(p, q, k, v, beta, la, s0, d_o, ds_final, dq, dk, dv, dbeta, dla, ds0, w, s);
+  }
 }
 
 }  // namespace gdn

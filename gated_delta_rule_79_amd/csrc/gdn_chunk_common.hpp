@@ -145,6 +145,30 @@ __device__ inline opvec<OP> pack2(const floatx4& lo, const floatx4& hi) {
   return frag<OP>::from_floats(v);
 }
 
+// ------------------------------------------------------ buffer access ---
+// Raw buffer resources (base, byte size): loads past the end return zero and
+// offsets are 32-bit, so address arithmetic stays in one VGPR.
+constexpr int kBufFlags = 0x00020000;  // dword 3 of a raw gfx9 descriptor
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0,
+                                           static_cast<int>(bytes), kBufFlags);
+}
+
+// Two runs of 4 operand elements at byte offsets a and b of a buffer.
+template <typename OP>
+__device__ inline opvec<OP> bload4x2(__amdgpu_buffer_rsrc_t r, uint32_t a, uint32_t b) {
+  if constexpr (opstore<OP>::bytes == 2) {
+    const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, a, 0, 0));
+    const uint2 y = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, b, 0, 0));
+    return join44(x, y);
+  } else {
+    const floatx4 x = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, a, 0, 0));
+    const floatx4 y = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, b, 0, 0));
+    return floatx8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  }
+}
+
 // -------------------------------------------------------- workspace ---
 // Per chunk-head (slot c of head h, index ch = h * nchunks + c) the forward
 // keeps, in the operand type OP (bf16 for bf16 inputs, fp32 for fp32):
@@ -160,8 +184,11 @@ struct FwdLayout {
   int C, DK, dv, ob;           // chunk, key dim, value dim, operand bytes
   int NB, NKD, NKC, NDT;       // C/16, ceil(DK/32), ceil(C/32), DK/16
   size_t w, k, p, u, q, g;     // bytes per chunk-head of each buffer
+  // backward only: the reverse recurrence's operands (see gdn_bwd.hip)
+  size_t kf, wt, pt, qt;
   size_t per_ch;               // sum, 256-aligned pieces
-  __host__ __device__ FwdLayout(int C_, int DK_, int dv_, int ob_, bool chan)
+  __host__ __device__ FwdLayout(int C_, int DK_, int dv_, int ob_, bool chan,
+                                bool bwd = false)
       : C(C_), DK(DK_), dv(dv_), ob(ob_) {
     NB = C / 16;
     NKD = (DK + 31) / 32;
@@ -173,7 +200,11 @@ struct FwdLayout {
     u = al(size_t(C) * dv * ob);
     q = chan ? w : 0;
     g = al(size_t(C + DK) * 4);
-    per_ch = w + k + p + u + q + g;
+    kf = bwd ? w : 0;
+    wt = bwd ? k : 0;
+    pt = bwd ? p : 0;
+    qt = bwd ? k : 0;
+    per_ch = w + k + p + u + q + g + kf + wt + pt + qt;
   }
   __host__ __device__ static size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 };
@@ -182,6 +213,7 @@ struct FwdBuffers {
   char* base;     // per-chunk operand area
   size_t per_ch;
   size_t off_w, off_k, off_p, off_u, off_q, off_g;
+  size_t off_kf, off_wt, off_pt, off_qt;
   __device__ char* at(int64_t ch, size_t off) const {
     return base + static_cast<size_t>(ch) * per_ch + off;
   }
@@ -197,6 +229,10 @@ inline FwdBuffers make_buffers(char* base, const FwdLayout& L) {
   b.off_u = b.off_p + L.p;
   b.off_q = b.off_u + L.u;
   b.off_g = b.off_q + L.q;
+  b.off_kf = b.off_g + L.g;
+  b.off_wt = b.off_kf + L.kf;
+  b.off_pt = b.off_wt + L.wt;
+  b.off_qt = b.off_pt + L.pt;
   return b;
 }
 

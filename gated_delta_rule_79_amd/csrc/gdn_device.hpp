@@ -44,6 +44,12 @@ __device__ inline float bf16_bits_to_float(uint16_t u) {
   return __uint_as_float(static_cast<uint32_t>(u) << 16);
 }
 
+// beta / log-alpha element i of a gate array stored in bf16 or fp32.
+__device__ inline float load_gate(const void* p, int64_t i, bool bf16) {
+  return bf16 ? bf16_bits_to_float(static_cast<const uint16_t*>(p)[i])
+              : static_cast<const float*>(p)[i];
+}
+
 // ------------------------------------------------------------ reductions ---
 
 __device__ inline float wave_sum_xor(float x, int lane_mask) {

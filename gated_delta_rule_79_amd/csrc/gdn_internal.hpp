@@ -46,7 +46,10 @@ hipError_t launch_fwd(const Problem& p, const void* q, const void* k,
                       const float* s0, void* o, float* s_final, void* ws,
                       hipStream_t s);
 
-// Backward (gdn_bwd.hip).
+// Backward (gdn_bwd.hip).  bwd_supported: whether the per-chunk gradient
+// kernel's LDS plan fits for these sizes (fp32 inputs with the per-channel
+// gate at dk = 128 need chunk <= 32).
+bool bwd_supported(const Problem& p);
 size_t bwd_workspace_bytes(const Problem& p);
 hipError_t launch_bwd(const Problem& p, const void* q, const void* k,
                       const void* v, const void* beta, const void* la,
