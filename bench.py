@@ -50,6 +50,7 @@ def source_hash(files):
 
 
 FWD_SOURCES = ["gated_delta_rule_79_amd/csrc/gdn_fwd.hip",
+               "gated_delta_rule_79_amd/csrc/gdn_fwd_kernels.hpp",
                "gated_delta_rule_79_amd/csrc/gdn_chunk_common.hpp",
                "gated_delta_rule_79_amd/csrc/gdn_device.hpp"]
 
@@ -108,6 +109,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra calls each preceded by a 1 GiB cache-flush write")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 3 device copies of 256 MiB (a kernel of known "
+                         "traffic for scaling memory counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -174,6 +178,14 @@ def main():
         times.sort()
         cold_ms = times[len(times) // 2]
         del flush
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda").fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     s_io = 2 if inp.q.dtype == torch.bfloat16 else 4
     s_gate = 2 if inp.beta.dtype == torch.bfloat16 else 4
