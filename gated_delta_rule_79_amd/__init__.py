@@ -158,6 +158,14 @@ def stage_times(enable: Optional[bool] = None):
             if cnt[i] > 0}
 
 
+def set_segment_chunks(n: int) -> None:
+    """Segment length of the forward state pass, process-wide: 0 automatic
+    (default), n > 0 segments of n chunks, n < 0 never split sequences.  A
+    FwdPlan sizes its workspace when it is built, so build plans after
+    changing this."""
+    _lib.load().gdn_set_segment_chunks(int(n))
+
+
 def fwd_workspace_bytes(q, v, beta, log_alpha=None, chunk=64, cu_seqlens=None) -> int:
     lib = _lib.load()
     p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)

@@ -21,11 +21,11 @@ EXPORTED = (
     "gdn_abi_version", "gdn_status_str", "gdn_chunk_fwd_workspace",
     "gdn_chunk_fwd", "gdn_chunk_bwd_workspace", "gdn_chunk_bwd",
     "gdn_decode_step", "gdn_test_set_fail_launch", "gdn_profile_enable",
-    "gdn_profile_read",
+    "gdn_profile_read", "gdn_set_segment_chunks",
 )
-STAGE_COUNT = 8
+STAGE_COUNT = 10
 STAGES = ("chunk_map", "fwd_prep", "fwd_scan", "decode", "bwd_states",
-          "bwd_scan", "bwd_grad", "other")
+          "bwd_scan", "bwd_grad", "other", "fwd_trans", "fwd_combine")
 
 
 class GdnProblem(ctypes.Structure):
@@ -82,6 +82,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_int32)]
     lib.gdn_test_set_fail_launch.restype = None
     lib.gdn_test_set_fail_launch.argtypes = [i32]
+    lib.gdn_set_segment_chunks.restype = None
+    lib.gdn_set_segment_chunks.argtypes = [i32]
     if path is None:
         _LIB = lib
     return lib

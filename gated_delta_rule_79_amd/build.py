@@ -30,6 +30,9 @@ CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix accumulators in ordinary VGPRs: the kernels scale and convert
+    # them between products, which AGPR accumulators turn into copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE, "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]

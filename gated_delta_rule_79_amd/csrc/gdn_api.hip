@@ -5,7 +5,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <exception>
 #include <mutex>
 #include <vector>
@@ -16,6 +18,7 @@
 namespace {
 
 std::atomic<int> g_fail_launch{0};
+std::atomic<int> g_seg_chunks{0};  // gdn_set_segment_chunks
 
 bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
@@ -81,6 +84,9 @@ gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out) {
   const int64_t per_seq = (static_cast<int64_t>(p->T) + p->chunk - 1) / p->chunk;
   out->nchunks = out->varlen ? per_seq + p->nseq : per_seq * p->B;
   if (out->nchunks * p->H > (int64_t(1) << 31) - 1) return GDN_ERR_SHAPE;
+  out->seg = gdn::plan_segments(*out);
+  out->nsegs = gdn::seg_slots_host(*out);
+  if (out->nsegs * p->H * 32 > (int64_t(1) << 31) - 1) return GDN_ERR_SHAPE;
   return GDN_OK;
 }
 
@@ -172,6 +178,29 @@ void prof_end(int stage, hipStream_t s) {
   }
 }
 
+int plan_segments(const Problem& p) {
+  const int set = g_seg_chunks.load();
+  if (set < 0 || p.nseq == 0) return 0;
+  if (set > 0) return std::min(set, 1 << 20);
+  // automatic: split only when the (sequence, head, 16-column slab) chains
+  // cannot cover the SIMDs, into segments of ~sqrt(n / 2) chunks, which
+  // balances the two per-segment passes against the sequential combine
+  const int64_t chains = static_cast<int64_t>(p.nseq) * p.H * (p.dv / 16);
+  const double n = static_cast<double>(p.nchunks - (p.varlen ? p.nseq : 0)) / p.nseq;
+  if (chains >= 1024 || n < 8.0) return 0;
+  return std::max(2, static_cast<int>(std::ceil(std::sqrt(n / 2.0))));
+}
+
+int64_t seg_slots_host(const Problem& p) {
+  if (p.seg == 0) return p.nseq;
+  if (!p.varlen) {
+    const int64_t nt = (static_cast<int64_t>(p.T) + p.chunk - 1) / p.chunk;
+    return static_cast<int64_t>(p.nseq) * std::max<int64_t>(1, (nt + p.seg - 1) / p.seg);
+  }
+  // sum over sequences of max(1, ceil(n_s / L)) <= nchunks / L + nseq
+  return p.nchunks / p.seg + p.nseq;
+}
+
 }  // namespace gdn
 
 extern "C" {
@@ -229,6 +258,8 @@ const char* gdn_status_str(gdn_status s) {
 }
 
 void gdn_test_set_fail_launch(int enable) { g_fail_launch.store(enable != 0); }
+
+void gdn_set_segment_chunks(int n) { g_seg_chunks.store(n); }
 
 gdn_status gdn_chunk_fwd_workspace(const gdn_problem* p, size_t* bytes) {
   try {

@@ -134,7 +134,9 @@ __global__ __launch_bounds__(128) void bwd_scan_kernel(
   const int chain = w / ndvt;
   const int h = chain % H;
   const int seq = chain / H;
-  const int wave = threadIdx.x >> 6;
+  // wave index in a scalar register: branches on it are scalar branches,
+  // never EXEC masks (matrix instructions ignore EXEC)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
   const int col = 16 * vt + l16;
   const int64_t sbase = (static_cast<int64_t>(seq) * H + h) * DK * dv;
@@ -423,7 +425,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   const int len = ci.len;
   const int64_t tok0 = ci.tok0;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  // wave index in a scalar register: branches on it are scalar branches,
+  // never EXEC masks (matrix instructions ignore EXEC)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int64_t ch = static_cast<int64_t>(h) * nchunks + c;
   const float* M0g = states + ch * DK * dv;
   const float* dM1g = dstates + ch * DK * dv;
@@ -1015,8 +1020,6 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
     if (e != hipSuccess) return e;
   }
   const int64_t nwork = static_cast<int64_t>(p.nseq) * p.H * (p.dv / 16);
-  const int64_t qb = static_cast<int64_t>(p.B) * p.T * p.H * DK * io<IO>::bytes;
-  const uint32_t q_bytes = qb < (int64_t(1) << 31) ? static_cast<uint32_t>(qb) : 0u;
   if (p.nchunks > 0) {
     {
       StageScope scope(GDN_STAGE_FWD_PREP, s);
@@ -1028,10 +1031,15 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
     }
     {
       StageScope scope(GDN_STAGE_BWD_STATES, s);
+      // whole sequences: the recomputation stores every chunk-start state
+      const SegMap whole = make_seg_map(p, map_base, 0);
+      const int64_t ngrp = (p.dv / 16 + kSlabGroup - 1) / kSlabGroup;
       hipLaunchKernelGGL((fwd_scan_kernel<C, DK, IO, GATE, true>),
-                         dim3(static_cast<unsigned>(nwork)), dim3(128), 0, s, map,
-                         p.H, p.dv, p.nchunks, q, q_bytes, s0, static_cast<void*>(nullptr),
-                         static_cast<float*>(nullptr), buf, states);
+                         dim3(static_cast<unsigned>(p.nseq * p.H * ngrp)),
+                         dim3(64 * kStateWaves), 0, s, map,
+                         whole, p.H, p.dv, p.nchunks, q, s0,
+                         static_cast<void*>(nullptr), static_cast<float*>(nullptr),
+                         buf, SegBuffers{}, states);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -2,6 +2,8 @@
 // bookkeeping, the varlen chunk map, workspace layout and fragment helpers.
 #pragma once
 
+#include <algorithm>
+
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -236,10 +238,14 @@ inline FwdBuffers make_buffers(char* base, const FwdLayout& L) {
   return b;
 }
 
-// Host: bytes of the varlen chunk map (table + first-chunk index).
+// Host: bytes of the varlen chunk map (chunk table + first-chunk index, then
+// the segment table + first-segment index when sequences are split).
 inline size_t chunk_map_bytes(const Problem& p) {
   if (!p.varlen) return 0;
-  return FwdLayout::al(size_t(p.nchunks) * 16) + FwdLayout::al(size_t(p.nseq + 1) * 4);
+  size_t b = FwdLayout::al(size_t(p.nchunks) * 16) + FwdLayout::al(size_t(p.nseq + 1) * 4);
+  if (p.seg > 0)
+    b += FwdLayout::al(size_t(p.nsegs) * 16) + FwdLayout::al(size_t(p.nseq + 1) * 4);
+  return b;
 }
 
 // Host: fill a ChunkMap pointing into workspace `map_base`.
@@ -257,9 +263,88 @@ inline ChunkMap make_chunk_map(const Problem& p, char* map_base) {
   return m;
 }
 
+// ----------------------------------------------------------- segments ---
+// The forward state pass splits each sequence into segments of at most L
+// consecutive chunks so that short batches still fill the machine: the
+// state entering segment j is  M_j = Phi_{j-1} M_{j-1} + M0_{j-1},  where
+// Phi is the segment's transition (the product of its per-chunk maps
+// M -> (gamma_c I - K~^T W) M) and M0 the state it produces from zero.
+// L = 0 keeps one segment per sequence (slot = sequence).
+struct SegMap {
+  int L;                 // chunks per segment, 0 = whole sequences
+  int varlen;
+  int nt;                // dense: chunks per sequence
+  int per_seq;           // dense: segments per sequence (>= 1)
+  const int4* tab;       // varlen, L > 0: [nsegs] (seq, c0, c1, j); seq < 0 unused
+  const int32_t* first;  // varlen, L > 0: [nseq + 1] first segment slot
+};
+
+struct SegInfo {
+  int seq;     // < 0: unused slot
+  int j;       // index of the segment within its sequence
+  int c0, c1;  // chunk slots [c0, c1)
+  bool last;   // last segment of its sequence
+};
+
+__device__ inline SegInfo seg_info(const SegMap& s, const ChunkMap& m, int slot) {
+  SegInfo r;
+  if (s.L == 0) {
+    r.seq = slot;
+    r.j = 0;
+    seq_chunks(m, slot, &r.c0, &r.c1);
+    r.last = true;
+  } else if (!s.varlen) {
+    r.seq = slot / s.per_seq;
+    r.j = slot % s.per_seq;
+    r.c0 = r.seq * s.nt + r.j * s.L;
+    r.c1 = min(r.c0 + s.L, (r.seq + 1) * s.nt);
+    r.last = r.j == s.per_seq - 1;
+  } else {
+    const int4 e = s.tab[slot];
+    r.seq = e.x;
+    r.c0 = e.y;
+    r.c1 = e.z;
+    r.j = e.w;
+    r.last = e.x >= 0 && slot + 1 == s.first[e.x + 1];
+  }
+  return r;
+}
+
+// Segment slots of one sequence: [b, e).
+__device__ inline void seq_segs(const SegMap& s, int seq, int* b, int* e) {
+  if (s.L == 0) {
+    *b = seq;
+    *e = seq + 1;
+  } else if (!s.varlen) {
+    *b = seq * s.per_seq;
+    *e = (seq + 1) * s.per_seq;
+  } else {
+    *b = s.first[seq];
+    *e = s.first[seq + 1];
+  }
+}
+
+// Host: a SegMap for segments of L chunks (L = 0 or p.seg) over the map at
+// `map_base`.
+inline SegMap make_seg_map(const Problem& p, char* map_base, int L) {
+  SegMap s{};
+  s.L = L;
+  s.varlen = p.varlen ? 1 : 0;
+  s.nt = (p.T + p.chunk - 1) / p.chunk;
+  s.per_seq = L > 0 ? std::max(1, (s.nt + L - 1) / L) : 1;
+  if (p.varlen && L > 0) {
+    char* b = map_base + FwdLayout::al(size_t(p.nchunks) * 16) +
+              FwdLayout::al(size_t(p.nseq + 1) * 4);
+    s.tab = reinterpret_cast<const int4*>(b);
+    s.first = reinterpret_cast<const int32_t*>(b + FwdLayout::al(size_t(p.nsegs) * 16));
+  }
+  return s;
+}
+
 // Device: build the varlen chunk map (one workgroup).  Lengths are clamped
 // into [0, T] so malformed cu_seqlens cannot send later kernels out of
-// bounds; chunks beyond the slot budget are dropped.
+// bounds; chunks beyond the slot budget are dropped.  With p.seg > 0 it
+// also fills the segment table.
 hipError_t launch_chunk_map(const Problem& p, char* map_base, hipStream_t s);
 
 }  // namespace gdn

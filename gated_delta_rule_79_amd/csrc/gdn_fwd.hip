@@ -36,14 +36,40 @@ namespace gdn {
 
 namespace {
 
+// Exclusive prefix sum over one 256-wide block; returns the thread's offset
+// and adds the block total to *carry (all threads see the same value).
+__device__ int block_excl_scan(int x, int* s_scan, int* carry) {
+  const int tid = threadIdx.x;
+  s_scan[tid] = x;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const int y = tid >= d ? s_scan[tid - d] : 0;
+    __syncthreads();
+    s_scan[tid] += y;
+    __syncthreads();
+  }
+  const int excl = *carry + s_scan[tid] - x;
+  const int total = s_scan[255];
+  __syncthreads();
+  if (tid == 0) *carry += total;
+  __syncthreads();
+  return excl;
+}
+
+// Varlen chunk map and, for L > 0, the segment table: sequence n owns chunk
+// slots [first[n], first[n+1]) and segment slots [sfirst[n], sfirst[n+1]),
+// at least one segment even when it has no chunk.
 __global__ __launch_bounds__(256) void chunk_map_kernel(
     const int32_t* __restrict__ cu, int nseq, int T, int C, int64_t nslots,
-    int4* __restrict__ tab, int32_t* __restrict__ first) {
+    int4* __restrict__ tab, int32_t* __restrict__ first, int L, int64_t nsegs,
+    int4* __restrict__ stab, int32_t* __restrict__ sfirst) {
   const int tid = threadIdx.x;
   for (int64_t i = tid; i < nslots; i += 256) tab[i] = make_int4(-1, 0, 0, 0);
+  if (L > 0)
+    for (int64_t i = tid; i < nsegs; i += 256) stab[i] = make_int4(-1, 0, 0, 0);
   __shared__ int s_scan[256];
-  __shared__ int s_carry;
-  if (tid == 0) s_carry = 0;
+  __shared__ int s_carry[2];
+  if (tid < 2) s_carry[tid] = 0;
   __syncthreads();
   for (int base = 0; base < nseq; base += 256) {
     const int n = base + tid;
@@ -53,38 +79,44 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(
       en = min(max(cu[n + 1], st), T);
       cnt = (en - st + C - 1) / C;
     }
-    s_scan[tid] = cnt;
-    __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {
-      const int y = tid >= d ? s_scan[tid - d] : 0;
-      __syncthreads();
-      s_scan[tid] += y;
-      __syncthreads();
-    }
-    const int excl = s_carry + s_scan[tid] - cnt;
+    const int excl = block_excl_scan(cnt, s_scan, &s_carry[0]);
+    const int c0 = static_cast<int>(min<int64_t>(excl, nslots));
+    const int c1 = static_cast<int>(min<int64_t>(static_cast<int64_t>(excl) + cnt, nslots));
     if (n < nseq) {
-      first[n] = static_cast<int>(min<int64_t>(excl, nslots));
-      for (int j = 0; j < cnt; ++j) {
-        const int64_t slot = static_cast<int64_t>(excl) + j;
-        if (slot < nslots)
-          tab[slot] = make_int4(n, st + j * C, min(C, en - st - j * C), 0);
+      first[n] = c0;
+      for (int j = 0; j < c1 - c0; ++j)
+        tab[c0 + j] = make_int4(n, st + j * C, min(C, en - st - j * C), 0);
+    }
+    if (L > 0) {
+      const int ns = n < nseq ? max(1, (c1 - c0 + L - 1) / L) : 0;
+      const int sx = block_excl_scan(ns, s_scan, &s_carry[1]);
+      if (n < nseq) {
+        sfirst[n] = static_cast<int>(min<int64_t>(sx, nsegs));
+        for (int j = 0; j < ns; ++j) {
+          const int64_t slot = static_cast<int64_t>(sx) + j;
+          if (slot < nsegs)
+            stab[slot] = make_int4(n, c0 + j * L, min(c0 + (j + 1) * L, c1), j);
+        }
       }
     }
-    __syncthreads();
-    if (tid == 0) s_carry += s_scan[255];
-    __syncthreads();
   }
-  if (tid == 0) first[nseq] = static_cast<int>(min<int64_t>(s_carry, nslots));
+  if (tid == 0) {
+    first[nseq] = static_cast<int>(min<int64_t>(s_carry[0], nslots));
+    if (L > 0) sfirst[nseq] = static_cast<int>(min<int64_t>(s_carry[1], nsegs));
+  }
 }
 
 }  // namespace
 
 hipError_t launch_chunk_map(const Problem& p, char* map_base, hipStream_t s) {
-  ChunkMap m = make_chunk_map(p, map_base);
+  const ChunkMap m = make_chunk_map(p, map_base);
+  const SegMap sm = make_seg_map(p, map_base, p.seg);
   StageScope scope(GDN_STAGE_CHUNK_MAP, s);
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, s, p.cu_seqlens,
                      p.nseq, p.T, p.chunk, p.nchunks,
-                     const_cast<int4*>(m.tab), const_cast<int32_t*>(m.first));
+                     const_cast<int4*>(m.tab), const_cast<int32_t*>(m.first),
+                     p.seg, p.nsegs, const_cast<int4*>(sm.tab),
+                     const_cast<int32_t*>(sm.first));
   return hipGetLastError();
 }
 
@@ -93,18 +125,45 @@ hipError_t launch_chunk_map(const Problem& p, char* map_base, hipStream_t s) {
 
 namespace {
 
+// Segment buffers after the per-chunk operands (p.seg > 0).
+SegBuffers make_seg_buffers(const Problem& p, char* base, int ob) {
+  SegBuffers sb{};
+  if (p.seg == 0) return sb;
+  const int NKD = (p.dk + 31) / 32, NDT = p.dk / 16;
+  const size_t n = static_cast<size_t>(p.nsegs) * p.H;
+  const size_t st = FwdLayout::al(size_t(p.dk) * p.dv * 4);
+  sb.trp_bytes = FwdLayout::al(size_t(NDT) * NKD * 512 * ob);
+  sb.trm = reinterpret_cast<float*>(base);
+  sb.trp = base + n * st;
+  sb.ss = reinterpret_cast<float*>(base + n * (st + sb.trp_bytes));
+  return sb;
+}
+
+size_t seg_buffer_bytes(const Problem& p, int ob) {
+  if (p.seg == 0) return 0;
+  const int NKD = (p.dk + 31) / 32, NDT = p.dk / 16;
+  const size_t st = FwdLayout::al(size_t(p.dk) * p.dv * 4);
+  const size_t tp = FwdLayout::al(size_t(NDT) * NKD * 512 * ob);
+  return static_cast<size_t>(p.nsegs) * p.H * (2 * st + tp);
+}
+
 template <int C, int DK, typename IO, int GATE>
 hipError_t run_fwd(const Problem& p, const void* q, const void* k,
                    const void* v, const void* beta, const void* la,
                    const float* s0, void* o, float* s_final, char* ws,
                    hipStream_t s) {
-  const FwdLayout L(C, DK, p.dv, opstore<IO>::bytes, GATE == GDN_GATE_CHANNEL);
+  constexpr int ob = opstore<IO>::bytes;
+  const FwdLayout L(C, DK, p.dv, ob, GATE == GDN_GATE_CHANNEL);
   char* map_base = ws;
   char* ops = ws + chunk_map_bytes(p);
   const FwdBuffers buf = make_buffers(ops, L);
+  const SegBuffers sb = make_seg_buffers(p, ops + size_t(p.nchunks) * p.H * L.per_ch, ob);
   const ChunkMap map = make_chunk_map(p, map_base);
+  const SegMap sm = make_seg_map(p, map_base, p.seg);
+  const int ndvt = p.dv / 16;
+  hipError_t e;
   if (p.varlen) {
-    hipError_t e = launch_chunk_map(p, map_base, s);
+    e = launch_chunk_map(p, map_base, s);
     if (e != hipSuccess) return e;
   }
   if (p.nchunks > 0) {
@@ -113,17 +172,35 @@ hipError_t run_fwd(const Problem& p, const void* q, const void* k,
                        dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(256),
                        0, s, map, p.H, p.dv, p.nchunks, q, k, v, beta, la,
                        p.gdt == GDN_BF16, buf);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t nwork = static_cast<int64_t>(p.nseq) * p.H * (p.dv / 16);
-  // q through a buffer resource when its byte size fits the 32-bit range
-  const int64_t qb = static_cast<int64_t>(p.B) * p.T * p.H * DK * io<IO>::bytes;
-  const uint32_t q_bytes = qb < (int64_t(1) << 31) ? static_cast<uint32_t>(qb) : 0u;
+  if (p.seg > 0 && p.nchunks > 0) {
+    {
+      StageScope scope(GDN_STAGE_FWD_TRANS, s);
+      const int64_t ngrp = (ndvt + DK / 16 + kSlabGroup - 1) / kSlabGroup;
+      hipLaunchKernelGGL((fwd_trans_kernel<C, DK, IO, GATE>),
+                         dim3(static_cast<unsigned>(p.nsegs * p.H * ngrp)),
+                         dim3(64 * kStateWaves), 0, s, map, sm, p.H, p.dv, p.nchunks,
+                         buf, sb);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    {
+      StageScope scope(GDN_STAGE_FWD_COMBINE, s);
+      hipLaunchKernelGGL((fwd_combine_kernel<DK, IO>),
+                         dim3(static_cast<unsigned>(p.nseq * p.H)),
+                         dim3(512), 0, s, map, sm, p.H, p.dv,
+                         s0, sb);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  const int64_t nwork = p.nsegs * p.H * ((ndvt + kSlabGroup - 1) / kSlabGroup);
   StageScope scope(GDN_STAGE_FWD_SCAN, s);
   hipLaunchKernelGGL((fwd_scan_kernel<C, DK, IO, GATE>),
-                     dim3(static_cast<unsigned>(nwork)), dim3(128), 0, s, map,
-                     p.H, p.dv, p.nchunks, q, q_bytes, s0, o, s_final, buf,
+                     dim3(static_cast<unsigned>(nwork)), dim3(64 * kStateWaves), 0, s,
+                     map, sm, p.H, p.dv, p.nchunks, q, s0, o, s_final, buf, sb,
                      static_cast<float*>(nullptr));
   return hipGetLastError();
 }
@@ -171,7 +248,8 @@ hipError_t fwd_dk(const Problem& p, const void* q, const void* k,
 size_t fwd_workspace_bytes(const Problem& p) {
   const FwdLayout L(p.chunk, p.dk, p.dv, p.io == GDN_BF16 ? 2 : 4,
                     p.gate == GDN_GATE_CHANNEL);
-  return chunk_map_bytes(p) + size_t(p.nchunks) * p.H * L.per_ch;
+  return chunk_map_bytes(p) + size_t(p.nchunks) * p.H * L.per_ch +
+         seg_buffer_bytes(p, p.io == GDN_BF16 ? 2 : 4);
 }
 
 hipError_t launch_fwd(const Problem& p, const void* q, const void* k,

@@ -186,7 +186,10 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   const int len = ci.len;
   const int64_t tok0 = ci.tok0;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  // wave index in a scalar register: branches on it are scalar branches,
+  // never EXEC masks (matrix instructions ignore EXEC)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int64_t ch = static_cast<int64_t>(h) * nchunks + c;
 
   // P jobs: fragment (rt, jb) of P for 32 jb <= 16 rt + 15, computed as P^T
@@ -800,305 +803,627 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   }
 }
 
-// --------------------------------------------------------- scan kernel ---
+// Segment buffers of the split state pass (per segment slot and head):
+//   trm : state the segment produces from zero, fp32 accumulator layout
+//         [dv/16][DK/16][64 lanes][4]
+//   trp : the segment's transition Phi (DK x DK) as operand fragments
+//         [DK/16][NKD][64][8] in the operand type (permuted K)
+//   ss  : state entering the segment, same layout as trm (segments j >= 1)
+struct SegBuffers {
+  float* trm;
+  char* trp;
+  float* ss;
+  size_t trp_bytes;  // per (slot, head)
+};
 
-// Per-chunk operands of the state recurrence.
-template <int C, int DK, typename OP, int GATE>
-struct ChainOps {
+// ---------------------------------------------------- state pass kernels ---
+// The state recurrence runs per (segment, head) and 16-column slab of the
+// value dimension.  A workgroup of NW waves owns NW * SPW slabs of one
+// (segment, head); all of them read the same per-chunk operands (W, K~ and,
+// for the outputs, Q and P), so the workgroup copies each chunk's operands
+// once into LDS and every wave reads the fragments it needs from there.  The
+// copies go straight from global memory into LDS (global_load_lds, 16 bytes
+// per lane) into one buffer while the waves compute from the other (bf16;
+// fp32 operands are twice the size and use one buffer).
+
+constexpr int kStateWaves = 4;  // waves per workgroup
+constexpr int kSlabsPerWave = 2;
+constexpr int kSlabGroup = kStateWaves * kSlabsPerWave;  // slabs per workgroup
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Wait until at most N vector memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Copy `bytes` (a multiple of 16) from global `src` to LDS `dst` with all NTH
+// threads: lane l of a wave moves the 16 bytes at wave base + 16 l, and the
+// LDS address of a wave's piece is its base + 16 * lane.
+template <int NTH>
+__device__ __forceinline__ void lds_copy(char* dst, const char* src, int bytes,
+                                         int wave, int lane) {
+  for (int b = wave * 1024; b < bytes; b += NTH * 16)
+    if (b + lane * 16 < bytes)
+      __builtin_amdgcn_global_load_lds(src + b + lane * 16,
+                                       (lds_void_ptr)(dst + b), 16, 0, 0);
+}
+
+// LDS image of one chunk's operands.  Q holds the Q~ fragments (per-channel
+// gate) or the raw q rows of the chunk with their 16-byte pieces permuted
+// within each row (piece c of row r sits at c ^ swz(r)), so that the 16 rows
+// a fragment read touches fall on different banks.
+template <int C, int DK, typename OP, bool OUT, bool RAWQ>
+struct LdsChunk {
+  static constexpr int ob = opstore<OP>::bytes;
   static constexpr int NB = C / 16, NKD = (DK + 31) / 32, NKC = (C + 31) / 32,
                        NDT = DK / 16;
-  opvec<OP> W[NB][NKD];
-  opvec<OP> K[NDT][NKC];
-  typename acc4<OP>::type U[NB];
-  floatx4 gc[GATE == GDN_GATE_CHANNEL ? NDT : 1];
+  static constexpr int W = NB * NKD * 512 * ob;            // -W fragments
+  static constexpr int K = NDT * NKC * 512 * ob;           // K~^T fragments
+  static constexpr int P = OUT ? NB * NKC * 512 * ob : 0;  // P fragments
+  static constexpr int Q = OUT ? (RAWQ ? C * DK * ob : NB * NKD * 512 * ob) : 0;
+  static constexpr int G = (C + DK) * 4;                   // gamma_r, chunk decays
+  static constexpr int U = NB * kSlabGroup * 256 * ob;     // U tiles of the group
+  static constexpr int oW = 0, oK = W, oP = W + K, oQ = W + K + P, oG = W + K + P + Q,
+                       oU = W + K + P + Q + G;
+  static constexpr int BYTES = oU + U;
+  static constexpr int PR = DK * ob / 16;                  // 16-byte pieces per q row
+  __device__ static int swz(int r) { return r & ((PR < 16 ? PR : 16) - 1); }
 };
 
-template <int C, int DK, typename OP, int GATE>
-__device__ __forceinline__ void load_chain(ChainOps<C, DK, OP, GATE>& x,
-                                           const FwdBuffers& buf, int64_t ch,
-                                           int vt, int ndvt, int lane, int lg) {
-  using X = ChainOps<C, DK, OP, GATE>;
-  constexpr int ob = opstore<OP>::bytes;
-  const char* pw = buf.at(ch, buf.off_w);
-  const char* pk = buf.at(ch, buf.off_k);
-  const char* pu = buf.at(ch, buf.off_u);
-  const float* pg = reinterpret_cast<const float*>(buf.at(ch, buf.off_g)) + C;
-#pragma unroll
-  for (int rt = 0; rt < X::NB; ++rt)
-#pragma unroll
-    for (int jb = 0; jb < X::NKD; ++jb)
-      x.W[rt][jb] = *reinterpret_cast<const opvec<OP>*>(
-          pw + ((size_t(rt) * X::NKD + jb) * 64 + lane) * 8 * ob);
-#pragma unroll
-  for (int rt = 0; rt < X::NB; ++rt)
-    x.U[rt] = *reinterpret_cast<const typename acc4<OP>::type*>(
-        pu + ((size_t(rt) * ndvt + vt) * 64 + lane) * 4 * ob);
-#pragma unroll
-  for (int a = 0; a < X::NDT; ++a)
-#pragma unroll
-    for (int jb = 0; jb < X::NKC; ++jb)
-      x.K[a][jb] = *reinterpret_cast<const opvec<OP>*>(
-          pk + ((size_t(a) * X::NKC + jb) * 64 + lane) * 8 * ob);
-  if constexpr (GATE == GDN_GATE_CHANNEL) {
-#pragma unroll
-    for (int a = 0; a < X::NDT; ++a)
-      x.gc[a] = *reinterpret_cast<const floatx4*>(pg + 16 * a + 4 * lg);
-  } else if constexpr (GATE == GDN_GATE_SCALAR) {
-    const float g = pg[0];
-    x.gc[0] = floatx4{g, g, g, g};
-  } else {
-    x.gc[0] = floatx4{1.f, 1.f, 1.f, 1.f};
-  }
-}
-
-// Operands of one chunk's outputs.
-template <int C, int DK, typename OP, int GATE>
-struct OutOps {
-  static constexpr int NB = C / 16, NKD = (DK + 31) / 32, NKC = (C + 31) / 32;
-  opvec<OP> Q[NB][NKD];
-  opvec<OP> P[NB][NKC];
-  floatx4 gr[GATE == GDN_GATE_SCALAR ? NB : 1];
-};
-
-template <int C, int DK, typename OP, int GATE>
-__device__ __forceinline__ void load_out(OutOps<C, DK, OP, GATE>& x,
-                                         const FwdBuffers& buf, int64_t ch,
-                                         const ChunkInfo& ci,
-                                         const void* __restrict__ q,
-                                         __amdgpu_buffer_rsrc_t qr, bool qbuf,
-                                         int H, int h, int lane, int l16, int lg) {
-  using X = OutOps<C, DK, OP, GATE>;
-  constexpr int ob = opstore<OP>::bytes;
-  const char* pp = buf.at(ch, buf.off_p);
-#pragma unroll
-  for (int rt = 0; rt < X::NB; ++rt) {
-    const int r = 16 * rt + l16;
-    // byte offset of q row r (rows past the chunk only feed output rows
-    // that are never stored; past the tensor the buffer returns zero)
-    const uint32_t qrow = static_cast<uint32_t>(((ci.tok0 + r) * H + h) * DK * ob);
-#pragma unroll
-    for (int jb = 0; jb < X::NKD; ++jb) {
-      if constexpr (GATE == GDN_GATE_CHANNEL) {
-        x.Q[rt][jb] = *reinterpret_cast<const opvec<OP>*>(
-            buf.at(ch, buf.off_q) + ((size_t(rt) * X::NKD + jb) * 64 + lane) * 8 * ob);
-      } else {
-        // raw q rows; the scalar decay is applied to the product's rows
-        const int d0 = 32 * jb + 4 * lg;
-        if (d0 >= DK) {
-          x.Q[rt][jb] = zero_vec<OP>();
-        } else if (qbuf) {
-          x.Q[rt][jb] = bload4x2<OP>(qr, qrow + d0 * ob, qrow + (d0 + 16) * ob);
-        } else if (r < ci.len) {
-          const int64_t base = ((ci.tok0 + r) * H + h) * DK;
-          x.Q[rt][jb] = gload4x2<OP>(q, base + d0, base + d0 + 16);
-        } else {
-          x.Q[rt][jb] = zero_vec<OP>();
-        }
+// Issue the copies of chunk slot ch (chunk info ci) into LDS buffer `lds`:
+// [W | K~ | P] (contiguous in the workspace: every piece is a multiple of 256
+// bytes), Q, the decays and the U tiles of the group's slabs [u0, u0 + nu).
+template <int C, int DK, typename OP, int GATE, bool OUT, int NTH>
+__device__ __forceinline__ void copy_chunk(char* lds, const FwdBuffers& buf, int64_t ch,
+                                           const ChunkInfo& ci, const void* q, int H,
+                                           int h, int ndvt, int u0, int nu, int wave,
+                                           int lane) {
+  constexpr bool RAWQ = OUT && GATE != GDN_GATE_CHANNEL;
+  using L = LdsChunk<C, DK, OP, OUT, RAWQ>;
+  constexpr int ob = L::ob;
+  lds_copy<NTH>(lds, buf.at(ch, buf.off_w), L::W + L::K + L::P, wave, lane);
+  if constexpr (OUT) {
+    if constexpr (!RAWQ) {
+      lds_copy<NTH>(lds + L::oQ, buf.at(ch, buf.off_q), L::Q, wave, lane);
+    } else {
+      // piece i of the LDS image: row i / PR, slot i % PR holds the row's
+      // piece slot ^ swz(row); rows past the chunk repeat its last row (they
+      // only feed outputs that are not stored)
+      const char* qb = static_cast<const char*>(q);
+      for (int b = wave * 64; b < C * L::PR; b += NTH) {
+        const int i = b + lane;
+        const int r = i / L::PR, c = (i % L::PR) ^ L::swz(i / L::PR);
+        const int rr = min(r, ci.len - 1);
+        const char* src = qb + (((ci.tok0 + rr) * H + h) * DK) * ob + c * 16;
+        if (i < C * L::PR)
+          __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(lds + L::oQ + b * 16),
+                                           16, 0, 0);
       }
     }
+  }
+  lds_copy<NTH>(lds + L::oG, buf.at(ch, buf.off_g), L::G, wave, lane);
+  if (nu > 0) {
+    const char* pu = buf.at(ch, buf.off_u);
 #pragma unroll
-    for (int jb = 0; jb < X::NKC; ++jb)
-      if (32 * jb <= 16 * rt + 15)
-        x.P[rt][jb] = *reinterpret_cast<const opvec<OP>*>(
-            pp + ((size_t(rt) * X::NKC + jb) * 64 + lane) * 8 * ob);
-    if constexpr (GATE == GDN_GATE_SCALAR)
-      x.gr[rt] = *reinterpret_cast<const floatx4*>(
-          reinterpret_cast<const float*>(buf.at(ch, buf.off_g)) + 16 * rt + 4 * lg);
+    for (int rt = 0; rt < L::NB; ++rt)
+      lds_copy<NTH>(lds + L::oU + rt * kSlabGroup * 256 * ob,
+                    pu + (static_cast<size_t>(rt) * ndvt + u0) * 256 * ob, nu * 256 * ob,
+                    wave, lane);
   }
 }
 
-// State pass.  A workgroup is two waves working on one (sequence, head,
-// 16-column slab of dv):
-//   wave 0 carries the chain  E = U - W M,  M <- gamma_C M + K~^T E  and
-//          hands the bf16 fragments of M (chunk start) and E to wave 1
-//          through a double buffer in LDS;
-//   wave 1 forms the outputs  O = gamma (.) (Q M) + P E  one chunk behind.
-// One barrier per chunk keeps the two waves a chunk apart.  With bf16
-// operands each wave loads the next chunk's operands while it computes the
-// current one.
-//
-// STATES = true (backward recomputation): wave 0 also stores the fp32 state
-// at the start of every chunk into `states` ([chunk-head][DK][dv]) and no
-// outputs are formed.
-template <int C, int DK, typename IO, int GATE, bool STATES = false>
-__global__ __launch_bounds__(128) void fwd_scan_kernel(
-    ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
-    uint32_t q_bytes, const float* __restrict__ s0, void* __restrict__ o,
-    float* __restrict__ s_final, FwdBuffers buf, float* __restrict__ states) {
-  using OP = IO;
-  using X = ChainOps<C, DK, OP, GATE>;
-  using Y = OutOps<C, DK, OP, GATE>;
-  constexpr int NB = X::NB, NKD = X::NKD, NKC = X::NKC, NDT = X::NDT;
+// One chunk of the chain for the wave's slabs, operands in LDS `ops`:
+//   E = U - W M  (U only where has_u),  M <- gamma_c M + K~^T E.
+// Slab s of the wave is slab us[s] of the LDS U tiles.  Returns the operand
+// fragments of M (chunk start) and E in Mb / Eb.  Every slab is computed,
+// also one past the problem's columns (its values are never stored), so the
+// matrix work carries no branches.
+template <int C, int DK, typename OP, int GATE, int SPW, bool OUT, bool RAWQ>
+__device__ __forceinline__ void chain_lds(
+    const char* ops, floatx4 (&M)[SPW][DK / 16],
+    const bool (&has_u)[SPW], const int (&us)[SPW],
+    opvec<OP> (&Mb)[SPW][(DK + 31) / 32], opvec<OP> (&Eb)[SPW][(C + 31) / 32],
+    int lane, int lg) {
+  using L = LdsChunk<C, DK, OP, OUT, RAWQ>;
+  constexpr int NB = L::NB, NKD = L::NKD, NKC = L::NKC, NDT = L::NDT;
   constexpr bool CH = GATE == GDN_GATE_CHANNEL;
-  constexpr bool kPrefetch = io<IO>::bytes == 2;
+  using A4 = typename acc4<OP>::type;
+  const opvec<OP>* sW = reinterpret_cast<const opvec<OP>*>(ops + L::oW);
+  const opvec<OP>* sK = reinterpret_cast<const opvec<OP>*>(ops + L::oK);
+  const A4* sU = reinterpret_cast<const A4*>(ops + L::oU);
+  const float* sg = reinterpret_cast<const float*>(ops + L::oG) + C;
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < SPW; ++s)
+#pragma unroll
+    for (int jb = 0; jb < NKD; ++jb)
+      Mb[s][jb] = pack2<OP>(M[s][2 * jb], 2 * jb + 1 < NDT ? M[s][2 * jb + 1] : z);
+  floatx4 E[SPW][NB];
+#pragma unroll
+  for (int rt = 0; rt < NB; ++rt) {
+    opvec<OP> wf[NKD];
+#pragma unroll
+    for (int jb = 0; jb < NKD; ++jb) wf[jb] = sW[(rt * NKD + jb) * 64 + lane];
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      const floatx4 u = to_f4(sU[(rt * kSlabGroup + us[s]) * 64 + lane]);
+      E[s][rt] = has_u[s] ? u : z;
+#pragma unroll
+      for (int jb = 0; jb < NKD; ++jb) E[s][rt] = mma32(wf[jb], Mb[s][jb], E[s][rt]);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < SPW; ++s)
+#pragma unroll
+    for (int jb = 0; jb < NKC; ++jb)
+      Eb[s][jb] = pack2<OP>(E[s][2 * jb], 2 * jb + 1 < NB ? E[s][2 * jb + 1] : z);
+#pragma unroll
+  for (int a = 0; a < NDT; ++a) {
+    opvec<OP> kf[NKC];
+#pragma unroll
+    for (int jb = 0; jb < NKC; ++jb) kf[jb] = sK[(a * NKC + jb) * 64 + lane];
+    floatx4 gc;
+    if constexpr (CH) gc = *reinterpret_cast<const floatx4*>(sg + 16 * a + 4 * lg);
+    else if constexpr (GATE == GDN_GATE_SCALAR) gc = floatx4{sg[0], sg[0], sg[0], sg[0]};
+    else gc = floatx4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      M[s][a] *= gc;
+#pragma unroll
+      for (int jb = 0; jb < NKC; ++jb) M[s][a] = mma32(kf[jb], Eb[s][jb], M[s][a]);
+    }
+  }
+}
 
-  __shared__ opvec<OP> sMb[2][NKD][64];
-  __shared__ opvec<OP> sEb[2][NKC][64];
-  // output staging: the chunk's [C rows][16 cols] slab in the output dtype
-  __shared__ __attribute__((aligned(16))) typename opstore<OP>::vec sO[C][2];
+// Segment transitions.  Slabs run over the [dv | DK] columns of [M0 | Phi]:
+// the chain over the segment's chunks from M = 0 with U (columns of M0) or
+// from the identity columns without U (columns of Phi; the map from the
+// entering to the leaving state is affine, M_end = Phi M_start + M0).  The
+// last segment of a sequence needs neither.
+template <int C, int DK, typename IO, int GATE>
+__global__ __launch_bounds__(64 * kStateWaves) void fwd_trans_kernel(
+    ChunkMap map, SegMap sm, int H, int dv, int64_t nchunks, FwdBuffers buf,
+    SegBuffers sb) {
+  using OP = IO;
+  constexpr int NW = kStateWaves, SPW = kSlabsPerWave, NTH = 64 * NW;
+  using L = LdsChunk<C, DK, OP, false, false>;
+  constexpr int NKD = L::NKD, NKC = L::NKC, NDT = L::NDT;
+  constexpr bool DB = opstore<OP>::bytes == 2;  // double-buffered
+  __shared__ __attribute__((aligned(16))) char sA[L::BYTES];
+  __shared__ __attribute__((aligned(16))) char sB[DB ? L::BYTES : 16];
 
+  const int ndvt = dv / 16, ncol = ndvt + NDT;
+  const int ngrp = (ncol + kSlabGroup - 1) / kSlabGroup;
+  // head-major: a head's segments (and their maps) stay on one XCD
+  const int nslot = static_cast<int>(gridDim.x) / (ngrp * H);
   const int w = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int grp = w % ngrp;
+  const int slot = (w / ngrp) % nslot;
+  const int h = w / ngrp / nslot;
+  const SegInfo si = seg_info(sm, map, slot);
+  if (si.seq < 0 || si.last) return;  // whole workgroup, before any barrier
+  const int tid = threadIdx.x;
+  // wave index in a scalar register: branches on it are scalar branches,
+  // never EXEC masks (matrix instructions ignore EXEC)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int g0 = grp * kSlabGroup;                  // first column slab of the group
+  const int u0 = g0, nu = max(0, min(kSlabGroup, ndvt - g0));  // its M0 slabs
+  const int vt0 = g0 + wave * SPW;
+  bool own[SPW], phi[SPW], has_u[SPW];
+  int us[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    own[s] = vt0 + s < ncol;
+    phi[s] = vt0 + s >= ndvt;
+    has_u[s] = own[s] && !phi[s];
+    us[s] = wave * SPW + s;
+  }
+
+  floatx4 M[SPW][NDT];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int pc = 16 * (vt0 + s - ndvt) + l16;  // Phi column of this lane
+#pragma unroll
+    for (int a = 0; a < NDT; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        M[s][a][e] = (phi[s] && 16 * a + 4 * lg + e == pc) ? 1.f : 0.f;
+  }
+
+  const int n = si.c1 - si.c0;
+  const int64_t ch0 = static_cast<int64_t>(h) * nchunks + si.c0;
+  const ChunkInfo ci{};
+  opvec<OP> Mb[SPW][NKD], Eb[SPW][NKC];
+  auto copy = [&](char* lds, int j) {
+    copy_chunk<C, DK, OP, GATE, false, NTH>(lds, buf, ch0 + j, ci, nullptr, H, h, ndvt,
+                                            u0, nu, wave, lane);
+  };
+  auto step = [&](const char* lds) {
+    chain_lds<C, DK, OP, GATE, SPW, false, false>(lds, M, has_u, us, Mb, Eb, lane, lg);
+  };
+  if constexpr (DB) {
+    if (n > 0) copy(sA, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int j = 0; j < n; j += 2) {
+      if (j + 1 < n) copy(sB, j + 1);
+      step(sA);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (j + 1 < n) {
+        if (j + 2 < n) copy(sA, j + 2);
+        step(sB);
+        wait_vmcnt<0>();
+        __syncthreads();
+      }
+    }
+  } else {
+    for (int j = 0; j < n; ++j) {
+      if (j > 0) __syncthreads();  // every wave is done with chunk j - 1
+      copy(sA, j);
+      wait_vmcnt<0>();
+      __syncthreads();
+      step(sA);
+    }
+  }
+
+  const size_t sh = static_cast<size_t>(slot) * H + h;
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    if (!own[s]) continue;
+    if (!phi[s]) {
+      floatx4* dst = reinterpret_cast<floatx4*>(sb.trm) + (sh * ndvt + vt0 + s) * NDT * 64;
+#pragma unroll
+      for (int a = 0; a < NDT; ++a) dst[a * 64 + lane] = M[s][a];
+    } else {
+      // lane holds Phi(16a + 4lg + e, pc); operand fragment (a, jb) lane L'
+      // slot t stands for Phi(16a + L'%16, 32jb + perm_k(L'/16, t))
+      using E = typename io<IO>::storage;
+      E* dst = reinterpret_cast<E*>(sb.trp + sh * sb.trp_bytes);
+      const int cp = vt0 + s - ndvt, jb = cp >> 1, half = cp & 1;
+      const int t = (l16 & 3) + 4 * half;
+#pragma unroll
+      for (int a = 0; a < NDT; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int Lp = 4 * lg + e + 16 * (l16 >> 2);
+          const size_t off = ((static_cast<size_t>(a) * NKD + jb) * 64 + Lp) * 8;
+          io<IO>::store(dst, off + t, M[s][a][e]);
+          if (DK == 16) io<IO>::store(dst, off + t + 4, 0.f);  // K slots past DK
+        }
+    }
+  }
+}
+
+// Q fragment (row tile rt, K block jb) of raw q rows staged in LDS: lane
+// holds row 16 rt + l%16, the runs of 4 columns at 32 jb + 4 (l/16) and 16
+// further (zero past DK).
+template <int C, int DK, typename OP>
+__device__ __forceinline__ opvec<OP> q_frag_raw(const char* sq, int rt, int jb, int l16, int lg) {
+  using L = LdsChunk<C, DK, OP, true, true>;
+  const int r = 16 * rt + l16;
+  const int d0 = 32 * jb + 4 * lg;
+  const char* row = sq + r * L::PR * 16;
+  if constexpr (opstore<OP>::bytes == 2) {
+    const int c0 = d0 >> 3, in = (d0 & 7) * 2;
+    const u32x2 x = *reinterpret_cast<const u32x2*>(row + ((c0 ^ L::swz(r)) * 16) + in);
+    u32x2 y = {0u, 0u};
+    if (d0 + 16 < DK)
+      y = *reinterpret_cast<const u32x2*>(row + (((c0 + 2) ^ L::swz(r)) * 16) + in);
+    return __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], y[0], y[1]});
+  } else {
+    const int c0 = d0 >> 2;
+    const floatx4 x = *reinterpret_cast<const floatx4*>(row + ((c0 ^ L::swz(r)) * 16));
+    floatx4 y = {0.f, 0.f, 0.f, 0.f};
+    if (d0 + 16 < DK) y = *reinterpret_cast<const floatx4*>(row + (((c0 + 4) ^ L::swz(r)) * 16));
+    return floatx8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  }
+}
+
+// State pass over one segment with the outputs.  Each wave carries the fp32
+// state of its slabs from the segment's entering state (s0, or the combine
+// result) and per chunk forms
+//   E = U - W M,   M <- gamma_C M + K~^T E,
+//   O^T = M^T Q~^T + E^T P^T   (Q~ = gamma (.) Q for the scalar gate),
+// the outputs transposed so that each lane ends up with 4 consecutive
+// columns of one token row (one 8-byte store in bf16).  The operands of the
+// transposed products are the same register fragments with the roles of A
+// and B swapped.  A chunk's stores are issued at the start of the next one,
+// so that the wait for the next chunk's copies never waits on them.
+//
+// STATES = true (backward recomputation): no outputs; every chunk-start
+// state is stored in fp32 into `states` ([chunk-head][DK][dv]).
+template <int C, int DK, typename IO, int GATE, bool STATES = false>
+__global__ __launch_bounds__(64 * kStateWaves) void fwd_scan_kernel(
+    ChunkMap map, SegMap sm, int H, int dv, int64_t nchunks,
+    const void* __restrict__ q, const float* __restrict__ s0,
+    void* __restrict__ o, float* __restrict__ s_final, FwdBuffers buf,
+    SegBuffers sb, float* __restrict__ states) {
+  using OP = IO;
+  constexpr bool OUT = !STATES;
+  constexpr bool RAWQ = OUT && GATE != GDN_GATE_CHANNEL;
+  constexpr int NW = kStateWaves, SPW = kSlabsPerWave, NTH = 64 * NW;
+  using L = LdsChunk<C, DK, OP, OUT, RAWQ>;
+  constexpr int NB = L::NB, NKD = L::NKD, NKC = L::NKC, NDT = L::NDT;
+  constexpr bool DB = opstore<OP>::bytes == 2;  // double-buffered
+  using E = typename io<IO>::storage;
+  __shared__ __attribute__((aligned(16))) char sA[L::BYTES];
+  __shared__ __attribute__((aligned(16))) char sB[DB ? L::BYTES : 16];
+
   const int ndvt = dv / 16;
-  const int vt = w % ndvt;
-  const int chain = w / ndvt;
-  const int h = chain % H;
-  const int seq = chain / H;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
-  const int col = 16 * vt + l16;
+  const int ngrp = (ndvt + kSlabGroup - 1) / kSlabGroup;
+  const int nslot = static_cast<int>(gridDim.x) / (ngrp * H);
+  const int w = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int grp = w % ngrp;
+  const int slot = (w / ngrp) % nslot;
+  const int h = w / ngrp / nslot;
+  const SegInfo si = seg_info(sm, map, slot);
+  if (si.seq < 0) return;  // whole workgroup, before any barrier
+  const int seq = si.seq;
+  const int tid = threadIdx.x;
+  // wave index in a scalar register: branches on it are scalar branches,
+  // never EXEC masks (matrix instructions ignore EXEC)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int g0 = grp * kSlabGroup;
+  const int nu = max(0, min(kSlabGroup, ndvt - g0));
+  const int vt0 = g0 + wave * SPW;
+  const int nown = max(0, min(SPW, ndvt - vt0));  // slabs of this wave
+  bool own[SPW], has_u[SPW];
+  int us[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    own[s] = s < nown;
+    has_u[s] = true;
+    us[s] = wave * SPW + s;
+  }
   const int64_t sbase = (static_cast<int64_t>(seq) * H + h) * DK * dv;
 
-  int cb, ce;
-  seq_chunks(map, seq, &cb, &ce);
-  const int n = ce - cb;
-  const int64_t ch0 = static_cast<int64_t>(h) * nchunks + cb;
+  floatx4 M[SPW][NDT];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int col = 16 * (vt0 + s) + l16;
+    if (si.j == 0) {
+#pragma unroll
+      for (int a = 0; a < NDT; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          M[s][a][e] = (s0 && own[s])
+              ? s0[sbase + static_cast<int64_t>(16 * a + 4 * lg + e) * dv + col] : 0.f;
+    } else {
+      const size_t sh = static_cast<size_t>(slot) * H + h;
+      const floatx4* src = reinterpret_cast<const floatx4*>(sb.ss) + (sh * ndvt + vt0 + s) * NDT * 64;
+#pragma unroll
+      for (int a = 0; a < NDT; ++a) M[s][a] = own[s] ? src[a * 64 + lane] : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
 
-  if (wave == 0) {
-    floatx4 M[NDT];
+  const int n = si.c1 - si.c0;
+  const int64_t ch0 = static_cast<int64_t>(h) * nchunks + si.c0;
+
+  // outputs of the previous chunk, held for their stores
+  using O4 = typename acc4<OP>::type;
+  O4 Ov[SPW][NB];
+  int64_t o_tok0 = 0;
+  int o_len = 0;
+  auto store_out = [&]() {
+    if constexpr (OUT) {
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        const int r = 16 * rt + l16;
+        if (r >= o_len) continue;
+        E* dst = static_cast<E*>(o) + ((o_tok0 + r) * H + h) * dv + 16 * vt0 + 4 * lg;
+#pragma unroll
+        for (int s = 0; s < SPW; ++s)
+          if (own[s]) *reinterpret_cast<O4*>(dst + 16 * s) = Ov[s][rt];
+      }
+    }
+  };
+
+  auto copy = [&](char* lds, int j) {
+    const ChunkInfo ci = OUT ? chunk_info(map, si.c0 + j) : ChunkInfo{};
+    copy_chunk<C, DK, OP, GATE, OUT, NTH>(lds, buf, ch0 + j, ci, q, H, h, ndvt, g0, nu,
+                                          wave, lane);
+  };
+  auto step = [&](const char* ops, int j) {
+    if constexpr (STATES) {
+      float* stp = states + (ch0 + j) * static_cast<int64_t>(DK) * dv;
+#pragma unroll
+      for (int s = 0; s < SPW; ++s) {
+        if (!own[s]) continue;
+        const int col = 16 * (vt0 + s) + l16;
+#pragma unroll
+        for (int a = 0; a < NDT; ++a)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            stp[static_cast<int64_t>(16 * a + 4 * lg + e) * dv + col] = M[s][a][e];
+      }
+    }
+    opvec<OP> Mb[SPW][NKD], Eb[SPW][NKC];
+    chain_lds<C, DK, OP, GATE, SPW, OUT, RAWQ>(ops, M, has_u, us, Mb, Eb, lane, lg);
+    if constexpr (OUT) {
+      const ChunkInfo ci = chunk_info(map, si.c0 + j);
+      const opvec<OP>* sQ = reinterpret_cast<const opvec<OP>*>(ops + L::oQ);
+      const opvec<OP>* sP = reinterpret_cast<const opvec<OP>*>(ops + L::oP);
+      const float* sg = reinterpret_cast<const float*>(ops + L::oG);
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        opvec<OP> qf[NKD], pf[NKC];
+#pragma unroll
+        for (int jb = 0; jb < NKD; ++jb) {
+          if constexpr (RAWQ) qf[jb] = q_frag_raw<C, DK, OP>(ops + L::oQ, rt, jb, l16, lg);
+          else qf[jb] = sQ[(rt * NKD + jb) * 64 + lane];
+        }
+#pragma unroll
+        for (int jb = 0; jb < NKC; ++jb)
+          if (32 * jb <= 16 * rt + 15) pf[jb] = sP[(rt * NKC + jb) * 64 + lane];
+        const float gr = GATE == GDN_GATE_SCALAR ? sg[16 * rt + l16] : 1.f;
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) {
+          floatx4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int jb = 0; jb < NKD; ++jb) O = mma32(Mb[s][jb], qf[jb], O);
+          if constexpr (GATE == GDN_GATE_SCALAR) O *= gr;
+#pragma unroll
+          for (int jb = 0; jb < NKC; ++jb)
+            if (32 * jb <= 16 * rt + 15) O = mma32(Eb[s][jb], pf[jb], O);
+          Ov[s][rt] = from_f4<OP>(O);
+        }
+      }
+      o_tok0 = ci.tok0;
+      o_len = ci.len;
+    }
+  };
+
+  if constexpr (DB) {
+    if (n > 0) copy(sA, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int j = 0; j < n; j += 2) {
+      store_out();
+      if (j + 1 < n) copy(sB, j + 1);
+      step(sA, j);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (j + 1 < n) {
+        store_out();
+        if (j + 2 < n) copy(sA, j + 2);
+        step(sB, j + 1);
+        wait_vmcnt<0>();
+        __syncthreads();
+      }
+    }
+  } else {
+    for (int j = 0; j < n; ++j) {
+      store_out();
+      if (j > 0) __syncthreads();  // every wave is done with chunk j - 1
+      copy(sA, j);
+      wait_vmcnt<0>();
+      __syncthreads();
+      step(sA, j);
+    }
+  }
+  store_out();
+  if (s_final && si.last) {
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      if (!own[s]) continue;
+      const int col = 16 * (vt0 + s) + l16;
+#pragma unroll
+      for (int a = 0; a < NDT; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s_final[sbase + static_cast<int64_t>(16 * a + 4 * lg + e) * dv + col] = M[s][a][e];
+    }
+  }
+}
+
+// Sequential combine over the segments of each sequence:
+//   M_{j+1} = Phi_j M_j + M0_j,  M_0 = s0.
+// One workgroup of 8 waves per (sequence, head); wave w owns the 16-column
+// slabs w and w + 8 of dv.  All threads stage Phi_j in LDS (the next one is
+// loaded into registers while the current one is applied).
+template <int DK, typename IO>
+__global__ __launch_bounds__(512) void fwd_combine_kernel(
+    ChunkMap map, SegMap sm, int H, int dv, const float* __restrict__ s0,
+    SegBuffers sb) {
+  using OP = IO;
+  constexpr int NKD = (DK + 31) / 32, NDT = DK / 16;
+  constexpr int NF = NDT * NKD * 64;               // fragments of Phi
+  constexpr int RP = NF / 512 > 0 ? NF / 512 : 1;  // per thread
+  constexpr int NS = 2;                            // slabs per wave
+  __shared__ opvec<OP> sPhi[NF];
+  (void)map;
+
+  const int ndvt = dv / 16;
+  // wave index in a scalar register: branches on it are scalar branches,
+  // never EXEC masks (matrix instructions ignore EXEC)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+  // head-major and XCD-aware, like the transition kernel that wrote the
+  // segment maps, so a head's maps are read from the L2 they were written to
+  const int nseq = static_cast<int>(gridDim.x) / H;
+  const int wg = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int seq = wg % nseq, h = wg / nseq;
+  int sb0, se0;
+  seq_segs(sm, seq, &sb0, &se0);
+  const int nseg = se0 - sb0;
+  if (nseg <= 1) return;
+  const int64_t sbase = (static_cast<int64_t>(seq) * H + h) * DK * dv;
+
+  floatx4 M[NS][NDT];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int vt = wave + 8 * u;
+    const int col = 16 * vt + l16;
 #pragma unroll
     for (int a = 0; a < NDT; ++a)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        M[a][s] = s0 ? s0[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] : 0.f;
+        M[u][a][s] = (s0 && vt < ndvt)
+            ? s0[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] : 0.f;
+  }
 
-    auto step = [&](const X& cur, X& nxt, int j) {
-      if (kPrefetch && j + 1 < n)
-        load_chain<C, DK, OP, GATE>(nxt, buf, ch0 + j + 1, vt, ndvt, lane, lg);
-      if constexpr (STATES) {
-        float* st = states + (ch0 + j) * static_cast<int64_t>(DK) * dv;
+  opvec<OP> pr[RP];
+  floatx4 m0r[NS][NDT];
+  auto fetch = [&](int slot) {
+    const size_t sh = static_cast<size_t>(slot) * H + h;
+    const opvec<OP>* src = reinterpret_cast<const opvec<OP>*>(sb.trp + sh * sb.trp_bytes);
 #pragma unroll
-        for (int a = 0; a < NDT; ++a)
+    for (int r = 0; r < RP; ++r) {
+      const int i = threadIdx.x + r * 512;
+      if (i < NF) pr[r] = src[i];
+    }
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            st[static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] = M[a][s];
+    for (int u = 0; u < NS; ++u) {
+      const int vt = wave + 8 * u;
+      if (vt < ndvt) {
+        const floatx4* m0 = reinterpret_cast<const floatx4*>(sb.trm) + (sh * ndvt + vt) * NDT * 64;
+#pragma unroll
+        for (int a = 0; a < NDT; ++a) m0r[u][a] = m0[a * 64 + lane];
       }
+    }
+  };
+
+  fetch(sb0);
+  for (int j = 0; j + 1 < nseg; ++j) {
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      const int i = threadIdx.x + r * 512;
+      if (i < NF) sPhi[i] = pr[r];
+    }
+    floatx4 acc[NS][NDT];
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+#pragma unroll
+      for (int a = 0; a < NDT; ++a) acc[u][a] = m0r[u][a];
+    __syncthreads();
+    if (j + 2 < nseg) fetch(sb0 + j + 1);
+    const size_t sh = static_cast<size_t>(sb0 + j + 1) * H + h;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int vt = wave + 8 * u;
+      if (vt >= ndvt) continue;
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
       opvec<OP> Mb[NKD];
 #pragma unroll
-      for (int jb = 0; jb < NKD; ++jb) {
-        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-        Mb[jb] = pack2<OP>(M[2 * jb], 2 * jb + 1 < NDT ? M[2 * jb + 1] : z);
-        sMb[j & 1][jb][lane] = Mb[jb];
-      }
-      floatx4 E[NB];
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        E[rt] = to_f4(cur.U[rt]);
-#pragma unroll
-        for (int jb = 0; jb < NKD; ++jb) E[rt] = mma32(cur.W[rt][jb], Mb[jb], E[rt]);
-      }
-      opvec<OP> Eb[NKC];
-#pragma unroll
-      for (int jb = 0; jb < NKC; ++jb) {
-        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-        Eb[jb] = pack2<OP>(E[2 * jb], 2 * jb + 1 < NB ? E[2 * jb + 1] : z);
-        sEb[j & 1][jb][lane] = Eb[jb];
-      }
+      for (int jb = 0; jb < NKD; ++jb)
+        Mb[jb] = pack2<OP>(M[u][2 * jb], 2 * jb + 1 < NDT ? M[u][2 * jb + 1] : z);
 #pragma unroll
       for (int a = 0; a < NDT; ++a) {
-        M[a] *= cur.gc[CH ? a : 0];
 #pragma unroll
-        for (int jb = 0; jb < NKC; ++jb) M[a] = mma32(cur.K[a][jb], Eb[jb], M[a]);
+        for (int jb = 0; jb < NKD; ++jb)
+          acc[u][a] = mma32(sPhi[(a * NKD + jb) * 64 + lane], Mb[jb], acc[u][a]);
+        M[u][a] = acc[u][a];
       }
-    };
-
-    if constexpr (kPrefetch) {
-      X A, B;
-      if (n > 0) load_chain<C, DK, OP, GATE>(A, buf, ch0, vt, ndvt, lane, lg);
-      for (int j = 0; j <= n; j += 2) {
-        if (j < n) step(A, B, j);
-        __syncthreads();
-        if (j + 1 <= n) {
-          if (j + 1 < n) step(B, A, j + 1);
-          __syncthreads();
-        }
-      }
-    } else {
-      for (int j = 0; j <= n; ++j) {
-        if (j < n) {
-          X A;
-          load_chain<C, DK, OP, GATE>(A, buf, ch0 + j, vt, ndvt, lane, lg);
-          step(A, A, j);
-        }
-        __syncthreads();
-      }
-    }
-    if (s_final) {
+      floatx4* dst = reinterpret_cast<floatx4*>(sb.ss) + (sh * ndvt + vt) * NDT * 64;
 #pragma unroll
-      for (int a = 0; a < NDT; ++a)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          s_final[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] = M[a][s];
-    }
-  } else {
-    const bool qbuf = q_bytes > 0;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q, q_bytes);
-    auto step = [&](const Y& cur, int jj) {
-      if constexpr (STATES) return;
-      const ChunkInfo ci = chunk_info(map, cb + jj);
-      opvec<OP> Mb[NKD], Eb[NKC];
-#pragma unroll
-      for (int jb = 0; jb < NKD; ++jb) Mb[jb] = sMb[jj & 1][jb][lane];
-#pragma unroll
-      for (int jb = 0; jb < NKC; ++jb) Eb[jb] = sEb[jj & 1][jb][lane];
-      // O tile rt lands in LDS as rows of the output dtype; each lane then
-      // writes whole 16-byte pieces of one row
-      using E = typename io<IO>::storage;
-      E* so = reinterpret_cast<E*>(&sO[0][0]);
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        floatx4 O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int jb = 0; jb < NKD; ++jb) O = mma32(cur.Q[rt][jb], Mb[jb], O);
-        if constexpr (GATE == GDN_GATE_SCALAR) O *= cur.gr[rt];
-#pragma unroll
-        for (int jb = 0; jb < NKC; ++jb)
-          if (32 * jb <= 16 * rt + 15) O = mma32(cur.P[rt][jb], Eb[jb], O);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) io<IO>::store(so, (16 * rt + 4 * lg + s) * 16 + l16, O[s]);
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes
-      __builtin_amdgcn_wave_barrier();
-      constexpr int PPR = 16 * sizeof(E) / 16;  // 16-byte pieces per row
-#pragma unroll
-      for (int u = 0; u < (C * PPR + 63) / 64; ++u) {
-        const int e = lane + 64 * u;
-        const int r = e / PPR, piece = e % PPR;
-        if (e < C * PPR && r < ci.len) {
-          const uint4 val = *reinterpret_cast<const uint4*>(so + r * 16 + piece * (16 / sizeof(E)));
-          *reinterpret_cast<uint4*>(static_cast<char*>(o) +
-              (((ci.tok0 + r) * H + h) * dv + 16 * vt) * sizeof(E) + piece * 16) = val;
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    };
-    auto load = [&](Y& x, int jj) {
-      if constexpr (STATES) return;
-      const ChunkInfo ci = chunk_info(map, cb + jj);
-      load_out<C, DK, OP, GATE>(x, buf, ch0 + jj, ci, q, qr, qbuf, H, h, lane, l16, lg);
-    };
-
-    if constexpr (kPrefetch) {
-      Y A, B;
-      if (n > 0) load(A, 0);
-      __syncthreads();
-      for (int j = 1; j <= n; j += 2) {
-        if (j < n) load(B, j);
-        step(A, j - 1);
-        __syncthreads();
-        if (j + 1 <= n) {
-          if (j + 1 < n) load(A, j + 1);
-          step(B, j);
-          __syncthreads();
-        }
-      }
-    } else {
-      __syncthreads();
-      for (int j = 1; j <= n; ++j) {
-        Y A;
-        load(A, j - 1);
-        step(A, j - 1);
-        __syncthreads();
-      }
+      for (int a = 0; a < NDT; ++a) dst[a * 64 + lane] = M[u][a];
     }
   }
 }

@@ -20,7 +20,17 @@ struct Problem {
   int gate;                   // gdn_gate
   // derived
   int64_t nchunks;            // chunk slots per head (upper bound in varlen)
+  int seg;                    // chunks per segment of the forward state pass
+                              // (0: one segment per sequence)
+  int64_t nsegs;              // segment slots (upper bound in varlen)
 };
+
+// Segment length the forward state pass uses for this problem (0 = whole
+// sequences), from the sizes and the process-wide setting of
+// gdn_set_segment_chunks (gdn_api.hip).
+int plan_segments(const Problem& p);
+// Segment slots for p.seg (upper bound in varlen).
+int64_t seg_slots_host(const Problem& p);
 
 // Stage timing (gdn_api.hip): no-ops unless gdn_profile_enable(1).
 void prof_begin(int stage, hipStream_t s);

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
   GDN_OK = 0,
@@ -171,19 +171,34 @@ gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k,
  * into total_ms[GDN_STAGE_COUNT] and count[GDN_STAGE_COUNT], and clears the
  * record.  Not for use while a stream is being captured into a graph.
  * Calls that overlap on several host threads are recorded together. */
-#define GDN_STAGE_COUNT 8
+#define GDN_STAGE_COUNT 10
 typedef enum {
   GDN_STAGE_CHUNK_MAP = 0,  /* varlen chunk table                         */
   GDN_STAGE_FWD_PREP = 1,   /* per-chunk gate, UT transform, W/U/P        */
-  GDN_STAGE_FWD_SCAN = 2,   /* inter-chunk state recurrence and outputs   */
+  GDN_STAGE_FWD_SCAN = 2,   /* state recurrence and outputs per segment   */
   GDN_STAGE_DECODE = 3,     /* single-token step                          */
   GDN_STAGE_BWD_STATES = 4, /* backward: chunk-start states               */
   GDN_STAGE_BWD_SCAN = 5,   /* backward: reverse state-gradient pass      */
   GDN_STAGE_BWD_GRAD = 6,   /* backward: per-chunk gradients              */
-  GDN_STAGE_OTHER = 7
+  GDN_STAGE_OTHER = 7,
+  GDN_STAGE_FWD_TRANS = 8,  /* forward: per-segment state maps [M0 | Phi] */
+  GDN_STAGE_FWD_COMBINE = 9 /* forward: states entering each segment      */
 } gdn_stage;
 void gdn_profile_enable(int enable);
 gdn_status gdn_profile_read(double* total_ms, int32_t* count);
+
+/* Segment length of the forward state pass, process-wide.  The forward
+ * carries the state across the chunks of a sequence; when there are few
+ * (sequence, head) pairs it splits each sequence into segments of n chunks,
+ * computes every segment's affine state map in parallel, combines them in a
+ * short sequential pass and then runs the segments in parallel from their
+ * entering states (mathematically the same recurrence, rounded differently).
+ *   n = 0  : automatic (default): split only when the pairs cannot fill
+ *            the GPU, with segments of about sqrt(chunks / 2) chunks;
+ *   n > 0  : segments of n chunks (values above 2^20 are clamped);
+ *   n < 0  : never split.
+ * Changes the workspace size: query gdn_chunk_fwd_workspace after setting. */
+void gdn_set_segment_chunks(int n);
 
 /* Test hook: when set to a non-zero value every entry point returns
  * GDN_ERR_HIP after validation instead of launching (exercises the launch

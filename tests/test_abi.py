@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
     for s in range(8):
         txt = lib.gdn_status_str(s).decode()
         assert txt.startswith("GDN_")
@@ -158,6 +158,47 @@ def test_workspace_scales_with_problem(lib):
     # varlen: one chunk slot per sequence more than the dense bound, plus the map
     _, d = ws_bytes(lib, prob(T=64, nseq=3, cu_seqlens=A))
     assert d > a
+
+
+def seg_bytes(nsegs, H, dk, dv, ob):
+    al = lambda x: (x + 255) // 256 * 256
+    return nsegs * H * (2 * al(dk * dv * 4) + al((dk // 16) * ((dk + 31) // 32) * 512 * ob))
+
+
+def test_workspace_of_segmented_state_pass(lib):
+    try:
+        lib.gdn_set_segment_chunks(-1)
+        _, off = ws_bytes(lib, prob(T=640))
+        _, off_big = ws_bytes(lib, prob(T=4096, H=16))
+        lib.gdn_set_segment_chunks(3)           # 10 chunks -> 4 segments
+        _, seg3 = ws_bytes(lib, prob(T=640))
+        assert seg3 - off == seg_bytes(4, 2, 128, 128, 2)
+        _, seg3f = ws_bytes(lib, prob(T=640, io_dtype=_lib.GDN_F32))
+        lib.gdn_set_segment_chunks(-1)
+        _, offf = ws_bytes(lib, prob(T=640, io_dtype=_lib.GDN_F32))
+        assert seg3f - offf == seg_bytes(4, 2, 128, 128, 4)
+        # automatic: 16 heads x 8 slabs cannot fill the GPU, 64 chunks ->
+        # segments of ceil(sqrt(32)) = 6 chunks, 11 per sequence
+        lib.gdn_set_segment_chunks(0)
+        _, auto = ws_bytes(lib, prob(T=4096, H=16))
+        assert auto - off_big == seg_bytes(11, 16, 128, 128, 2)
+        # enough (sequence, head, slab) chains: no split
+        _, a = ws_bytes(lib, prob(B=8, T=4096, H=16))
+        lib.gdn_set_segment_chunks(-1)
+        _, b = ws_bytes(lib, prob(B=8, T=4096, H=16))
+        assert a == b
+        # varlen with a forced split: segment table + buffers for at most
+        # nchunks / L + nseq slots
+        lib.gdn_set_segment_chunks(2)
+        _, v2 = ws_bytes(lib, prob(T=640, nseq=3, cu_seqlens=A))
+        lib.gdn_set_segment_chunks(-1)
+        _, v0 = ws_bytes(lib, prob(T=640, nseq=3, cu_seqlens=A))
+        nch = 10 + 3
+        slots = nch // 2 + 3
+        al = lambda x: (x + 255) // 256 * 256
+        assert v2 - v0 == seg_bytes(slots, 2, 128, 128, 2) + al(slots * 16) + al(4 * 4)
+    finally:
+        lib.gdn_set_segment_chunks(0)
 
 
 def test_decode_validation(lib):

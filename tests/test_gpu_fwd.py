@@ -184,3 +184,79 @@ def test_layer_b8_sampled(gpu_lib):
         es = state_err(np64(sf[sl]), s_ref)
         log(f"    batch {b}: err o={eo:.3e} s={es:.3e}")
         assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
+
+
+# ---------------------------------------------------- segmented state pass ---
+# The state pass can split each sequence into segments of L chunks: segment
+# maps [M0 | Phi] in parallel, a sequential combine, then the segments from
+# their entering states.  Forced segment lengths cover one-chunk segments,
+# ragged last segments, single-segment sequences, empty sequences in varlen
+# batches and every dtype / gate / key size.
+
+@pytest.fixture
+def seg_chunks(gpu_lib):
+    yield gdn.set_segment_chunks
+    gdn.set_segment_chunks(0)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 5])
+@pytest.mark.parametrize("gate", ["scalar", "none", "channel"])
+def test_segmented_fp32(seg_chunks, L, gate):
+    inp = synth.make_inputs(2, 150, 3, 32, 48, dtype=torch.float32, gate=gate,
+                            chunk=16, seed=41, s0_std=0.3)
+    seg_chunks(L)
+    check(inp, name=f"segmented_fp32 L={L}")
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_segmented_fp32_dk128(seg_chunks, C):
+    inp = synth.make_inputs(1, 333, 2, 128, 64, dtype=torch.float32, gate="channel",
+                            chunk=C, seed=42, s0_std=0.1)
+    seg_chunks(2)
+    check(inp, name=f"segmented_fp32_dk128 C={C}")
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 32), (128, 128), (128, 256)])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_segmented_bf16(seg_chunks, dk, dv, gate):
+    inp = synth.make_inputs(1, 700, 2, dk, dv, dtype=torch.bfloat16, gate=gate,
+                            chunk=64, seed=43, s0_std=0.05)
+    seg_chunks(3)
+    check(inp, name="segmented_bf16")
+
+
+@pytest.mark.parametrize("gate", ["scalar", "none", "channel"])
+def test_segmented_varlen(seg_chunks, gate):
+    inp = synth.make_inputs(1, 0, 2, 128, 64, dtype=torch.bfloat16, gate=gate,
+                            seed=44, lengths=[5, 0, 300, 64, 1, 177, 129, 0],
+                            s0_std=0.1)
+    seg_chunks(2)
+    check(inp, name="segmented_varlen")
+
+
+def test_segmented_varlen_fp32_no_s0(seg_chunks):
+    inp = synth.make_inputs(1, 0, 3, 64, 32, dtype=torch.float32, gate="scalar",
+                            chunk=16, seed=45, lengths=[40, 0, 97, 16, 33])
+    seg_chunks(1)
+    check(inp, name="segmented_varlen_fp32")
+
+
+def test_segmented_deterministic_and_unsplit_agree(seg_chunks):
+    inp = synth.make_inputs(1, 1000, 2, 128, 128, dtype=torch.float32, gate="scalar",
+                            seed=46, s0_std=0.1)
+    seg_chunks(-1)
+    o0, s0 = run(inp)
+    seg_chunks(4)
+    o1, s1 = run(inp)
+    o2, s2 = run(inp)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert slice_err(np64(o1), np64(o0)) < 1e-5
+    assert state_err(np64(s1), np64(s0)) < 1e-5
+
+
+def test_segmented_empty_batch_keeps_state(seg_chunks):
+    inp = synth.make_inputs(2, 0, 2, 64, 32, dtype=torch.bfloat16, seed=47,
+                            s0_std=1.0)
+    seg_chunks(2)
+    o, sf = run(inp)
+    assert torch.equal(sf.cpu(), inp.s0)
