@@ -1033,7 +1033,7 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
       StageScope scope(GDN_STAGE_BWD_STATES, s);
       // whole sequences: the recomputation stores every chunk-start state
       const SegMap whole = make_seg_map(p, map_base, 0);
-      const int64_t ngrp = (p.dv / 16 + kSlabGroup - 1) / kSlabGroup;
+      const int64_t ngrp = (p.dv / 16 + kScanGroup - 1) / kScanGroup;
       hipLaunchKernelGGL((fwd_scan_kernel<C, DK, IO, GATE, true>),
                          dim3(static_cast<unsigned>(p.nseq * p.H * ngrp)),
                          dim3(64 * kStateWaves), 0, s, map,

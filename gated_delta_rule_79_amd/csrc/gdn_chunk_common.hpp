@@ -27,6 +27,17 @@ struct ChunkInfo {
   int len;       // tokens in the chunk, 1..C
 };
 
+// Read-only table entry through the constant address space: with a uniform
+// index this is a scalar load, which leaves the vector memory counter (and
+// so the waits on in-flight copies) alone.
+__device__ inline int ld_table(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)(p))[i];
+}
+__device__ inline int4 ld_table(const int4* p, int64_t i) {
+  const int32_t* q = reinterpret_cast<const int32_t*>(p) + 4 * i;
+  return make_int4(ld_table(q, 0), ld_table(q, 1), ld_table(q, 2), ld_table(q, 3));
+}
+
 __device__ inline ChunkInfo chunk_info(const ChunkMap& m, int c) {
   ChunkInfo r;
   if (!m.varlen) {
@@ -35,7 +46,7 @@ __device__ inline ChunkInfo chunk_info(const ChunkMap& m, int c) {
     r.tok0 = static_cast<int64_t>(b) * m.T + static_cast<int64_t>(j) * m.C;
     r.len = min(m.C, m.T - j * m.C);
   } else {
-    const int4 e = m.tab[c];
+    const int4 e = ld_table(m.tab, c);
     r.seq = e.x;
     r.tok0 = e.y;
     r.len = e.z;
@@ -50,8 +61,8 @@ __device__ inline void seq_chunks(const ChunkMap& m, int seq, int* c_begin,
     *c_begin = seq * m.nt;
     *c_end = (seq + 1) * m.nt;
   } else {
-    *c_begin = m.first[seq];
-    *c_end = m.first[seq + 1];
+    *c_begin = ld_table(m.first, seq);
+    *c_end = ld_table(m.first, seq + 1);
   }
 }
 
@@ -300,12 +311,12 @@ __device__ inline SegInfo seg_info(const SegMap& s, const ChunkMap& m, int slot)
     r.c1 = min(r.c0 + s.L, (r.seq + 1) * s.nt);
     r.last = r.j == s.per_seq - 1;
   } else {
-    const int4 e = s.tab[slot];
+    const int4 e = ld_table(s.tab, slot);
     r.seq = e.x;
     r.c0 = e.y;
     r.c1 = e.z;
     r.j = e.w;
-    r.last = e.x >= 0 && slot + 1 == s.first[e.x + 1];
+    r.last = e.x >= 0 && slot + 1 == ld_table(s.first, e.x + 1);
   }
   return r;
 }
@@ -319,8 +330,8 @@ __device__ inline void seq_segs(const SegMap& s, int seq, int* b, int* e) {
     *b = seq * s.per_seq;
     *e = (seq + 1) * s.per_seq;
   } else {
-    *b = s.first[seq];
-    *e = s.first[seq + 1];
+    *b = ld_table(s.first, seq);
+    *e = ld_table(s.first, seq + 1);
   }
 }
 

@@ -178,7 +178,7 @@ hipError_t run_fwd(const Problem& p, const void* q, const void* k,
   if (p.seg > 0 && p.nchunks > 0) {
     {
       StageScope scope(GDN_STAGE_FWD_TRANS, s);
-      const int64_t ngrp = (ndvt + DK / 16 + kSlabGroup - 1) / kSlabGroup;
+      const int64_t ngrp = (ndvt + DK / 16 + kTransGroup - 1) / kTransGroup;
       hipLaunchKernelGGL((fwd_trans_kernel<C, DK, IO, GATE>),
                          dim3(static_cast<unsigned>(p.nsegs * p.H * ngrp)),
                          dim3(64 * kStateWaves), 0, s, map, sm, p.H, p.dv, p.nchunks,
@@ -189,14 +189,14 @@ hipError_t run_fwd(const Problem& p, const void* q, const void* k,
     {
       StageScope scope(GDN_STAGE_FWD_COMBINE, s);
       hipLaunchKernelGGL((fwd_combine_kernel<DK, IO>),
-                         dim3(static_cast<unsigned>(p.nseq * p.H)),
-                         dim3(512), 0, s, map, sm, p.H, p.dv,
+                         dim3(static_cast<unsigned>(p.nseq * p.H * ndvt)),
+                         dim3(64 * ((DK + 31) / 32)), 0, s, map, sm, p.H, p.dv,
                          s0, sb);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
-  const int64_t nwork = p.nsegs * p.H * ((ndvt + kSlabGroup - 1) / kSlabGroup);
+  const int64_t nwork = p.nsegs * p.H * ((ndvt + kScanGroup - 1) / kScanGroup);
   StageScope scope(GDN_STAGE_FWD_SCAN, s);
   hipLaunchKernelGGL((fwd_scan_kernel<C, DK, IO, GATE>),
                      dim3(static_cast<unsigned>(nwork)), dim3(64 * kStateWaves), 0, s,

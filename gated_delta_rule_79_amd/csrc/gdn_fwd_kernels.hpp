@@ -826,9 +826,11 @@ struct SegBuffers {
 // per lane) into one buffer while the waves compute from the other (bf16;
 // fp32 operands are twice the size and use one buffer).
 
-constexpr int kStateWaves = 4;  // waves per workgroup
-constexpr int kSlabsPerWave = 2;
-constexpr int kSlabGroup = kStateWaves * kSlabsPerWave;  // slabs per workgroup
+constexpr int kStateWaves = 8;  // waves per workgroup (two per SIMD)
+constexpr int kScanSlabs = 1;   // slabs per wave, scan: 8 slabs per workgroup
+constexpr int kTransSlabs = 2;  // slabs per wave, transitions: [M0 | Phi] of 128 + 128
+constexpr int kScanGroup = kStateWaves * kScanSlabs;
+constexpr int kTransGroup = kStateWaves * kTransSlabs;
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
@@ -839,23 +841,31 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Copy `bytes` (a multiple of 16) from global `src` to LDS `dst` with all NTH
-// threads: lane l of a wave moves the 16 bytes at wave base + 16 l, and the
-// LDS address of a wave's piece is its base + 16 * lane.
-template <int NTH>
-__device__ __forceinline__ void lds_copy(char* dst, const char* src, int bytes,
-                                         int wave, int lane) {
-  for (int b = wave * 1024; b < bytes; b += NTH * 16)
-    if (b + lane * 16 < bytes)
-      __builtin_amdgcn_global_load_lds(src + b + lane * 16,
-                                       (lds_void_ptr)(dst + b), 16, 0, 0);
+// Copy MAXB bytes (a multiple of 16; only the first `bytes` when given) from
+// global `src` to LDS `dst` with all NTH threads: lane l of a wave moves the
+// 16 bytes at the wave's base + 16 l, and the LDS address of a wave's piece
+// is its base + 16 * lane.  The uniform base stays in scalar registers and
+// each lane adds a 32-bit offset.
+template <int NTH, int MAXB>
+__device__ __forceinline__ void lds_copy(char* dst, const char* src, int wave, int lane,
+                                         int bytes = MAXB) {
+  constexpr int STEP = NTH * 16;
+#pragma unroll
+  for (int it = 0; it < (MAXB + STEP - 1) / STEP; ++it) {
+    const int b = it * STEP + wave * 1024;  // uniform
+    if (MAXB % STEP == 0 || b < MAXB) {
+      const uint32_t off = static_cast<uint32_t>(lane * 16);
+      if (bytes == MAXB || b + static_cast<int>(off) < bytes)
+        __builtin_amdgcn_global_load_lds(src + b + off, (lds_void_ptr)(dst + b), 16, 0, 0);
+    }
+  }
 }
 
 // LDS image of one chunk's operands.  Q holds the Q~ fragments (per-channel
 // gate) or the raw q rows of the chunk with their 16-byte pieces permuted
 // within each row (piece c of row r sits at c ^ swz(r)), so that the 16 rows
 // a fragment read touches fall on different banks.
-template <int C, int DK, typename OP, bool OUT, bool RAWQ>
+template <int C, int DK, typename OP, bool OUT, bool RAWQ, int GS>
 struct LdsChunk {
   static constexpr int ob = opstore<OP>::bytes;
   static constexpr int NB = C / 16, NKD = (DK + 31) / 32, NKC = (C + 31) / 32,
@@ -865,7 +875,7 @@ struct LdsChunk {
   static constexpr int P = OUT ? NB * NKC * 512 * ob : 0;  // P fragments
   static constexpr int Q = OUT ? (RAWQ ? C * DK * ob : NB * NKD * 512 * ob) : 0;
   static constexpr int G = (C + DK) * 4;                   // gamma_r, chunk decays
-  static constexpr int U = NB * kSlabGroup * 256 * ob;     // U tiles of the group
+  static constexpr int U = NB * GS * 256 * ob;             // U tiles of the group
   static constexpr int oW = 0, oK = W, oP = W + K, oQ = W + K + P, oG = W + K + P + Q,
                        oU = W + K + P + Q + G;
   static constexpr int BYTES = oU + U;
@@ -873,45 +883,71 @@ struct LdsChunk {
   __device__ static int swz(int r) { return r & ((PR < 16 ? PR : 16) - 1); }
 };
 
+// Per-lane byte offsets, within a chunk's q rows, of the raw-q pieces a lane
+// copies (row i / PR, piece (i % PR) ^ swz(row)) for a full chunk.
+template <int C, int DK, typename OP, int NTH>
+struct QPieces {
+  static constexpr int PR = DK * opstore<OP>::bytes / 16;
+  static constexpr int NIT = (C * PR + NTH - 1) / NTH;
+  uint32_t off[NIT];
+  __device__ __forceinline__ int piece(int it, int wave, int lane) const {
+    return it * NTH + wave * 64 + lane;
+  }
+  __device__ __forceinline__ static uint32_t offset(int r, int i, int H) {
+    const int c = (i % PR) ^ (r & ((PR < 16 ? PR : 16) - 1));
+    return static_cast<uint32_t>(r) * static_cast<uint32_t>(H * DK * opstore<OP>::bytes) +
+           static_cast<uint32_t>(c * 16);
+  }
+  __device__ __forceinline__ void init(int H, int wave, int lane) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int i = piece(it, wave, lane);
+      off[it] = offset(i / PR, i, H);
+    }
+  }
+};
+
 // Issue the copies of chunk slot ch (chunk info ci) into LDS buffer `lds`:
 // [W | K~ | P] (contiguous in the workspace: every piece is a multiple of 256
 // bytes), Q, the decays and the U tiles of the group's slabs [u0, u0 + nu).
-template <int C, int DK, typename OP, int GATE, bool OUT, int NTH>
+template <int C, int DK, typename OP, int GATE, bool OUT, int NTH, int GS>
 __device__ __forceinline__ void copy_chunk(char* lds, const FwdBuffers& buf, int64_t ch,
-                                           const ChunkInfo& ci, const void* q, int H,
+                                           const ChunkInfo& ci, const void* q,
+                                           const QPieces<C, DK, OP, NTH>& qp, int H,
                                            int h, int ndvt, int u0, int nu, int wave,
                                            int lane) {
   constexpr bool RAWQ = OUT && GATE != GDN_GATE_CHANNEL;
-  using L = LdsChunk<C, DK, OP, OUT, RAWQ>;
+  using L = LdsChunk<C, DK, OP, OUT, RAWQ, GS>;
+  using QP = QPieces<C, DK, OP, NTH>;
   constexpr int ob = L::ob;
-  lds_copy<NTH>(lds, buf.at(ch, buf.off_w), L::W + L::K + L::P, wave, lane);
+  lds_copy<NTH, L::W + L::K + L::P>(lds, buf.at(ch, buf.off_w), wave, lane);
   if constexpr (OUT) {
     if constexpr (!RAWQ) {
-      lds_copy<NTH>(lds + L::oQ, buf.at(ch, buf.off_q), L::Q, wave, lane);
+      lds_copy<NTH, L::Q>(lds + L::oQ, buf.at(ch, buf.off_q), wave, lane);
     } else {
-      // piece i of the LDS image: row i / PR, slot i % PR holds the row's
-      // piece slot ^ swz(row); rows past the chunk repeat its last row (they
-      // only feed outputs that are not stored)
-      const char* qb = static_cast<const char*>(q);
-      for (int b = wave * 64; b < C * L::PR; b += NTH) {
+      // rows past the chunk repeat its last row (they only feed outputs that
+      // are not stored)
+      const char* qb = static_cast<const char*>(q) + (ci.tok0 * H + h) * DK * ob;
+      const bool full = ci.len == C;
+#pragma unroll
+      for (int it = 0; it < QP::NIT; ++it) {
+        const int b = it * NTH + wave * 64;  // uniform
+        if (!((C * QP::PR) % NTH == 0 || b < C * QP::PR)) continue;
         const int i = b + lane;
-        const int r = i / L::PR, c = (i % L::PR) ^ L::swz(i / L::PR);
-        const int rr = min(r, ci.len - 1);
-        const char* src = qb + (((ci.tok0 + rr) * H + h) * DK) * ob + c * 16;
-        if (i < C * L::PR)
-          __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(lds + L::oQ + b * 16),
-                                           16, 0, 0);
+        const uint32_t off = full ? qp.off[it] : QP::offset(min(i / QP::PR, ci.len - 1), i, H);
+        __builtin_amdgcn_global_load_lds(qb + off, (lds_void_ptr)(lds + L::oQ + b * 16),
+                                         16, 0, 0);
       }
     }
   }
-  lds_copy<NTH>(lds + L::oG, buf.at(ch, buf.off_g), L::G, wave, lane);
+  lds_copy<NTH, L::G>(lds + L::oG, buf.at(ch, buf.off_g), wave, lane);
   if (nu > 0) {
     const char* pu = buf.at(ch, buf.off_u);
 #pragma unroll
     for (int rt = 0; rt < L::NB; ++rt)
-      lds_copy<NTH>(lds + L::oU + rt * kSlabGroup * 256 * ob,
-                    pu + (static_cast<size_t>(rt) * ndvt + u0) * 256 * ob, nu * 256 * ob,
-                    wave, lane);
+      lds_copy<NTH, GS * 256 * ob>(lds + L::oU + rt * GS * 256 * ob,
+                                           pu + (static_cast<size_t>(rt) * ndvt + u0) * 256 * ob,
+                                           wave, lane, nu * 256 * ob);
   }
 }
 
@@ -921,13 +957,13 @@ __device__ __forceinline__ void copy_chunk(char* lds, const FwdBuffers& buf, int
 // fragments of M (chunk start) and E in Mb / Eb.  Every slab is computed,
 // also one past the problem's columns (its values are never stored), so the
 // matrix work carries no branches.
-template <int C, int DK, typename OP, int GATE, int SPW, bool OUT, bool RAWQ>
+template <int C, int DK, typename OP, int GATE, int SPW, bool OUT, bool RAWQ, int GS>
 __device__ __forceinline__ void chain_lds(
     const char* ops, floatx4 (&M)[SPW][DK / 16],
     const bool (&has_u)[SPW], const int (&us)[SPW],
     opvec<OP> (&Mb)[SPW][(DK + 31) / 32], opvec<OP> (&Eb)[SPW][(C + 31) / 32],
     int lane, int lg) {
-  using L = LdsChunk<C, DK, OP, OUT, RAWQ>;
+  using L = LdsChunk<C, DK, OP, OUT, RAWQ, GS>;
   constexpr int NB = L::NB, NKD = L::NKD, NKC = L::NKC, NDT = L::NDT;
   constexpr bool CH = GATE == GDN_GATE_CHANNEL;
   using A4 = typename acc4<OP>::type;
@@ -949,7 +985,7 @@ __device__ __forceinline__ void chain_lds(
     for (int jb = 0; jb < NKD; ++jb) wf[jb] = sW[(rt * NKD + jb) * 64 + lane];
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
-      const floatx4 u = to_f4(sU[(rt * kSlabGroup + us[s]) * 64 + lane]);
+      const floatx4 u = to_f4(sU[(rt * GS + us[s]) * 64 + lane]);
       E[s][rt] = has_u[s] ? u : z;
 #pragma unroll
       for (int jb = 0; jb < NKD; ++jb) E[s][rt] = mma32(wf[jb], Mb[s][jb], E[s][rt]);
@@ -984,19 +1020,20 @@ __device__ __forceinline__ void chain_lds(
 // entering to the leaving state is affine, M_end = Phi M_start + M0).  The
 // last segment of a sequence needs neither.
 template <int C, int DK, typename IO, int GATE>
-__global__ __launch_bounds__(64 * kStateWaves) void fwd_trans_kernel(
+__global__ __launch_bounds__(64 * kStateWaves)
+void fwd_trans_kernel(
     ChunkMap map, SegMap sm, int H, int dv, int64_t nchunks, FwdBuffers buf,
     SegBuffers sb) {
   using OP = IO;
-  constexpr int NW = kStateWaves, SPW = kSlabsPerWave, NTH = 64 * NW;
-  using L = LdsChunk<C, DK, OP, false, false>;
+  constexpr int NW = kStateWaves, SPW = kTransSlabs, NTH = 64 * NW, GS = kTransGroup;
+  using L = LdsChunk<C, DK, OP, false, false, GS>;
   constexpr int NKD = L::NKD, NKC = L::NKC, NDT = L::NDT;
   constexpr bool DB = opstore<OP>::bytes == 2;  // double-buffered
   __shared__ __attribute__((aligned(16))) char sA[L::BYTES];
   __shared__ __attribute__((aligned(16))) char sB[DB ? L::BYTES : 16];
 
   const int ndvt = dv / 16, ncol = ndvt + NDT;
-  const int ngrp = (ncol + kSlabGroup - 1) / kSlabGroup;
+  const int ngrp = (ncol + GS - 1) / GS;
   // head-major: a head's segments (and their maps) stay on one XCD
   const int nslot = static_cast<int>(gridDim.x) / (ngrp * H);
   const int w = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -1010,8 +1047,8 @@ __global__ __launch_bounds__(64 * kStateWaves) void fwd_trans_kernel(
   // never EXEC masks (matrix instructions ignore EXEC)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int g0 = grp * kSlabGroup;                  // first column slab of the group
-  const int u0 = g0, nu = max(0, min(kSlabGroup, ndvt - g0));  // its M0 slabs
+  const int g0 = grp * GS;                                // first column slab of the group
+  const int u0 = g0, nu = max(0, min(GS, ndvt - g0));      // its M0 slabs
   const int vt0 = g0 + wave * SPW;
   bool own[SPW], phi[SPW], has_u[SPW];
   int us[SPW];
@@ -1038,12 +1075,13 @@ __global__ __launch_bounds__(64 * kStateWaves) void fwd_trans_kernel(
   const int64_t ch0 = static_cast<int64_t>(h) * nchunks + si.c0;
   const ChunkInfo ci{};
   opvec<OP> Mb[SPW][NKD], Eb[SPW][NKC];
+  QPieces<C, DK, OP, NTH> qp;  // unused without outputs
   auto copy = [&](char* lds, int j) {
-    copy_chunk<C, DK, OP, GATE, false, NTH>(lds, buf, ch0 + j, ci, nullptr, H, h, ndvt,
-                                            u0, nu, wave, lane);
+    copy_chunk<C, DK, OP, GATE, false, NTH, GS>(lds, buf, ch0 + j, ci, nullptr, qp, H, h,
+                                                ndvt, u0, nu, wave, lane);
   };
   auto step = [&](const char* lds) {
-    chain_lds<C, DK, OP, GATE, SPW, false, false>(lds, M, has_u, us, Mb, Eb, lane, lg);
+    chain_lds<C, DK, OP, GATE, SPW, false, false, GS>(lds, M, has_u, us, Mb, Eb, lane, lg);
   };
   if constexpr (DB) {
     if (n > 0) copy(sA, 0);
@@ -1104,7 +1142,7 @@ __global__ __launch_bounds__(64 * kStateWaves) void fwd_trans_kernel(
 // further (zero past DK).
 template <int C, int DK, typename OP>
 __device__ __forceinline__ opvec<OP> q_frag_raw(const char* sq, int rt, int jb, int l16, int lg) {
-  using L = LdsChunk<C, DK, OP, true, true>;
+  using L = LdsChunk<C, DK, OP, true, true, kScanGroup>;
   const int r = 16 * rt + l16;
   const int d0 = 32 * jb + 4 * lg;
   const char* row = sq + r * L::PR * 16;
@@ -1138,7 +1176,8 @@ __device__ __forceinline__ opvec<OP> q_frag_raw(const char* sq, int rt, int jb, 
 // STATES = true (backward recomputation): no outputs; every chunk-start
 // state is stored in fp32 into `states` ([chunk-head][DK][dv]).
 template <int C, int DK, typename IO, int GATE, bool STATES = false>
-__global__ __launch_bounds__(64 * kStateWaves) void fwd_scan_kernel(
+__global__ __launch_bounds__(64 * kStateWaves)
+void fwd_scan_kernel(
     ChunkMap map, SegMap sm, int H, int dv, int64_t nchunks,
     const void* __restrict__ q, const float* __restrict__ s0,
     void* __restrict__ o, float* __restrict__ s_final, FwdBuffers buf,
@@ -1146,8 +1185,8 @@ __global__ __launch_bounds__(64 * kStateWaves) void fwd_scan_kernel(
   using OP = IO;
   constexpr bool OUT = !STATES;
   constexpr bool RAWQ = OUT && GATE != GDN_GATE_CHANNEL;
-  constexpr int NW = kStateWaves, SPW = kSlabsPerWave, NTH = 64 * NW;
-  using L = LdsChunk<C, DK, OP, OUT, RAWQ>;
+  constexpr int NW = kStateWaves, SPW = kScanSlabs, NTH = 64 * NW, GS = kScanGroup;
+  using L = LdsChunk<C, DK, OP, OUT, RAWQ, GS>;
   constexpr int NB = L::NB, NKD = L::NKD, NKC = L::NKC, NDT = L::NDT;
   constexpr bool DB = opstore<OP>::bytes == 2;  // double-buffered
   using E = typename io<IO>::storage;
@@ -1155,7 +1194,7 @@ __global__ __launch_bounds__(64 * kStateWaves) void fwd_scan_kernel(
   __shared__ __attribute__((aligned(16))) char sB[DB ? L::BYTES : 16];
 
   const int ndvt = dv / 16;
-  const int ngrp = (ndvt + kSlabGroup - 1) / kSlabGroup;
+  const int ngrp = (ndvt + GS - 1) / GS;
   const int nslot = static_cast<int>(gridDim.x) / (ngrp * H);
   const int w = xcd_swizzle(blockIdx.x, gridDim.x);
   const int grp = w % ngrp;
@@ -1169,8 +1208,8 @@ __global__ __launch_bounds__(64 * kStateWaves) void fwd_scan_kernel(
   // never EXEC masks (matrix instructions ignore EXEC)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int g0 = grp * kSlabGroup;
-  const int nu = max(0, min(kSlabGroup, ndvt - g0));
+  const int g0 = grp * GS;
+  const int nu = max(0, min(GS, ndvt - g0));
   const int vt0 = g0 + wave * SPW;
   const int nown = max(0, min(SPW, ndvt - vt0));  // slabs of this wave
   bool own[SPW], has_u[SPW];
@@ -1210,24 +1249,29 @@ __global__ __launch_bounds__(64 * kStateWaves) void fwd_scan_kernel(
   O4 Ov[SPW][NB];
   int64_t o_tok0 = 0;
   int o_len = 0;
+  // lane part of an output address: row l16 of a row tile, columns 4 lg ..
+  const uint32_t o_lane = static_cast<uint32_t>((l16 * H * dv + 16 * vt0 + 4 * lg) * sizeof(E));
   auto store_out = [&]() {
     if constexpr (OUT) {
+      char* ob = static_cast<char*>(o) + (o_tok0 * H + h) * dv * static_cast<int64_t>(sizeof(E));
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
         const int r = 16 * rt + l16;
         if (r >= o_len) continue;
-        E* dst = static_cast<E*>(o) + ((o_tok0 + r) * H + h) * dv + 16 * vt0 + 4 * lg;
+        char* dst = ob + static_cast<int64_t>(16 * rt) * H * dv * sizeof(E) + o_lane;
 #pragma unroll
         for (int s = 0; s < SPW; ++s)
-          if (own[s]) *reinterpret_cast<O4*>(dst + 16 * s) = Ov[s][rt];
+          if (own[s]) *reinterpret_cast<O4*>(dst + 16 * s * sizeof(E)) = Ov[s][rt];
       }
     }
   };
 
+  QPieces<C, DK, OP, NTH> qp;
+  if constexpr (RAWQ) qp.init(H, wave, lane);
   auto copy = [&](char* lds, int j) {
     const ChunkInfo ci = OUT ? chunk_info(map, si.c0 + j) : ChunkInfo{};
-    copy_chunk<C, DK, OP, GATE, OUT, NTH>(lds, buf, ch0 + j, ci, q, H, h, ndvt, g0, nu,
-                                          wave, lane);
+    copy_chunk<C, DK, OP, GATE, OUT, NTH, GS>(lds, buf, ch0 + j, ci, q, qp, H, h, ndvt, g0,
+                                              nu, wave, lane);
   };
   auto step = [&](const char* ops, int j) {
     if constexpr (STATES) {
@@ -1244,7 +1288,7 @@ __global__ __launch_bounds__(64 * kStateWaves) void fwd_scan_kernel(
       }
     }
     opvec<OP> Mb[SPW][NKD], Eb[SPW][NKC];
-    chain_lds<C, DK, OP, GATE, SPW, OUT, RAWQ>(ops, M, has_u, us, Mb, Eb, lane, lg);
+    chain_lds<C, DK, OP, GATE, SPW, OUT, RAWQ, GS>(ops, M, has_u, us, Mb, Eb, lane, lg);
     if constexpr (OUT) {
       const ChunkInfo ci = chunk_info(map, si.c0 + j);
       const opvec<OP>* sQ = reinterpret_cast<const opvec<OP>*>(ops + L::oQ);
@@ -1324,106 +1368,98 @@ __global__ __launch_bounds__(64 * kStateWaves) void fwd_scan_kernel(
 
 // Sequential combine over the segments of each sequence:
 //   M_{j+1} = Phi_j M_j + M0_j,  M_0 = s0.
-// One workgroup of 8 waves per (sequence, head); wave w owns the 16-column
-// slabs w and w + 8 of dv.  All threads stage Phi_j in LDS (the next one is
-// loaded into registers while the current one is applied).
+// One workgroup per (sequence, head, 16-column slab).  Wave w computes the
+// row tiles 2w, 2w+1 of the slab, which together are the w-th 32-row K block
+// of the next product: after each step every wave publishes that block's
+// operand fragment in LDS and reads the others'.  Phi_j's rows and M0_j's
+// tiles do not depend on the recurrence and are loaded D steps ahead.
 template <int DK, typename IO>
-__global__ __launch_bounds__(512) void fwd_combine_kernel(
+__global__ __launch_bounds__(64 * ((DK + 31) / 32)) void fwd_combine_kernel(
     ChunkMap map, SegMap sm, int H, int dv, const float* __restrict__ s0,
     SegBuffers sb) {
   using OP = IO;
   constexpr int NKD = (DK + 31) / 32, NDT = DK / 16;
-  constexpr int NF = NDT * NKD * 64;               // fragments of Phi
-  constexpr int RP = NF / 512 > 0 ? NF / 512 : 1;  // per thread
-  constexpr int NS = 2;                            // slabs per wave
-  __shared__ opvec<OP> sPhi[NF];
+  constexpr int NT = NDT >= 2 ? 2 : 1;                 // row tiles per wave
+  constexpr int D = opstore<OP>::bytes == 2 ? 4 : 2;   // steps loaded ahead
+  __shared__ opvec<OP> sMb[2][NKD][64];
   (void)map;
 
   const int ndvt = dv / 16;
+  const int nseq = static_cast<int>(gridDim.x) / (H * ndvt);
+  // head-major and XCD-aware, like the transition kernel that wrote the
+  // segment maps, so a head's maps are read from the L2 they were written to
+  const int wg = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int vt = wg % ndvt;
+  const int seq = (wg / ndvt) % nseq;
+  const int h = wg / ndvt / nseq;
+  int sb0, se0;
+  seq_segs(sm, seq, &sb0, &se0);
+  const int nsteps = se0 - sb0 - 1;
+  if (nsteps <= 0) return;  // whole workgroup, before any barrier
   // wave index in a scalar register: branches on it are scalar branches,
   // never EXEC masks (matrix instructions ignore EXEC)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
-  // head-major and XCD-aware, like the transition kernel that wrote the
-  // segment maps, so a head's maps are read from the L2 they were written to
-  const int nseq = static_cast<int>(gridDim.x) / H;
-  const int wg = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int seq = wg % nseq, h = wg / nseq;
-  int sb0, se0;
-  seq_segs(sm, seq, &sb0, &se0);
-  const int nseg = se0 - sb0;
-  if (nseg <= 1) return;
+  const int t0 = NT * wave;
+  const int col = 16 * vt + l16;
   const int64_t sbase = (static_cast<int64_t>(seq) * H + h) * DK * dv;
 
-  floatx4 M[NS][NDT];
+  floatx4 M[NT];
 #pragma unroll
-  for (int u = 0; u < NS; ++u) {
-    const int vt = wave + 8 * u;
-    const int col = 16 * vt + l16;
+  for (int u = 0; u < NT; ++u)
 #pragma unroll
-    for (int a = 0; a < NDT; ++a)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        M[u][a][s] = (s0 && vt < ndvt)
-            ? s0[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] : 0.f;
-  }
+    for (int e = 0; e < 4; ++e)
+      M[u][e] = s0 ? s0[sbase + static_cast<int64_t>(16 * (t0 + u) + 4 * lg + e) * dv + col] : 0.f;
 
-  opvec<OP> pr[RP];
-  floatx4 m0r[NS][NDT];
-  auto fetch = [&](int slot) {
-    const size_t sh = static_cast<size_t>(slot) * H + h;
-    const opvec<OP>* src = reinterpret_cast<const opvec<OP>*>(sb.trp + sh * sb.trp_bytes);
+  struct Ahead {
+    opvec<OP> phi[NT][NKD];
+    floatx4 m0[NT];
+  };
+  Ahead ah[D];
+  auto fetch = [&](Ahead& a, int j) {
+    const size_t sh = static_cast<size_t>(sb0 + j) * H + h;
+    const opvec<OP>* phi = reinterpret_cast<const opvec<OP>*>(sb.trp + sh * sb.trp_bytes);
 #pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      const int i = threadIdx.x + r * 512;
-      if (i < NF) pr[r] = src[i];
-    }
+    for (int u = 0; u < NT; ++u)
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int vt = wave + 8 * u;
-      if (vt < ndvt) {
-        const floatx4* m0 = reinterpret_cast<const floatx4*>(sb.trm) + (sh * ndvt + vt) * NDT * 64;
+      for (int jb = 0; jb < NKD; ++jb) a.phi[u][jb] = phi[((t0 + u) * NKD + jb) * 64 + lane];
+    const floatx4* m0 = reinterpret_cast<const floatx4*>(sb.trm) + (sh * ndvt + vt) * NDT * 64;
 #pragma unroll
-        for (int a = 0; a < NDT; ++a) m0r[u][a] = m0[a * 64 + lane];
-      }
-    }
+    for (int u = 0; u < NT; ++u) a.m0[u] = m0[(t0 + u) * 64 + lane];
+  };
+  auto publish = [&](int b) {
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+    sMb[b][wave][lane] = pack2<OP>(M[0], NT > 1 ? M[NT - 1] : z);
   };
 
-  fetch(sb0);
-  for (int j = 0; j + 1 < nseg; ++j) {
-    __syncthreads();
 #pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      const int i = threadIdx.x + r * 512;
-      if (i < NF) sPhi[i] = pr[r];
-    }
-    floatx4 acc[NS][NDT];
+  for (int d = 0; d < D; ++d)
+    if (d < nsteps) fetch(ah[d], d);
+  publish(0);
+  __syncthreads();
+  for (int j = 0; j < nsteps; j += D) {
 #pragma unroll
-    for (int u = 0; u < NS; ++u)
+    for (int d = 0; d < D; ++d) {
+      const int jj = j + d;
+      if (jj < nsteps) {
+        opvec<OP> Mb[NKD];
 #pragma unroll
-      for (int a = 0; a < NDT; ++a) acc[u][a] = m0r[u][a];
-    __syncthreads();
-    if (j + 2 < nseg) fetch(sb0 + j + 1);
-    const size_t sh = static_cast<size_t>(sb0 + j + 1) * H + h;
+        for (int jb = 0; jb < NKD; ++jb) Mb[jb] = sMb[jj & 1][jb][lane];
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int vt = wave + 8 * u;
-      if (vt >= ndvt) continue;
-      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-      opvec<OP> Mb[NKD];
+        for (int u = 0; u < NT; ++u) {
+          floatx4 acc = ah[d].m0[u];
 #pragma unroll
-      for (int jb = 0; jb < NKD; ++jb)
-        Mb[jb] = pack2<OP>(M[u][2 * jb], 2 * jb + 1 < NDT ? M[u][2 * jb + 1] : z);
+          for (int jb = 0; jb < NKD; ++jb) acc = mma32(ah[d].phi[u][jb], Mb[jb], acc);
+          M[u] = acc;
+        }
+        if (jj + D < nsteps) fetch(ah[d], jj + D);
+        const size_t sh = static_cast<size_t>(sb0 + jj + 1) * H + h;
+        floatx4* dst = reinterpret_cast<floatx4*>(sb.ss) + (sh * ndvt + vt) * NDT * 64;
 #pragma unroll
-      for (int a = 0; a < NDT; ++a) {
-#pragma unroll
-        for (int jb = 0; jb < NKD; ++jb)
-          acc[u][a] = mma32(sPhi[(a * NKD + jb) * 64 + lane], Mb[jb], acc[u][a]);
-        M[u][a] = acc[u][a];
+        for (int u = 0; u < NT; ++u) dst[(t0 + u) * 64 + lane] = M[u];
+        publish((jj + 1) & 1);
+        __syncthreads();
       }
-      floatx4* dst = reinterpret_cast<floatx4*>(sb.ss) + (sh * ndvt + vt) * NDT * 64;
-#pragma unroll
-      for (int a = 0; a < NDT; ++a) dst[a * 64 + lane] = M[u][a];
     }
   }
 }
