@@ -196,7 +196,8 @@ def main():
 
     dom = max(per_kernel, key=per_kernel.get)
     dom_ms = per_kernel[dom]
-    kname = {"fwd_prep": "fwd_prep_kernel", "fwd_scan": "fwd_scan_kernel",
+    prep_kernel = "fwd_prep_kernel" if inp.gate == "channel" else "fwd_prep_sg_kernel"
+    kname = {"fwd_prep": prep_kernel, "fwd_scan": "fwd_scan_kernel",
              "fwd_trans": "fwd_trans_kernel", "fwd_combine": "fwd_combine_kernel",
              "chunk_map": "chunk_map_kernel"}[dom]
     achieved = byts / (dom_ms * 1e-3) / 1e9

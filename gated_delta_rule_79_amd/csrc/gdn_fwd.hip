@@ -168,10 +168,16 @@ hipError_t run_fwd(const Problem& p, const void* q, const void* k,
   }
   if (p.nchunks > 0) {
     StageScope scope(GDN_STAGE_FWD_PREP, s);
-    hipLaunchKernelGGL((fwd_prep_kernel<C, DK, IO, GATE>),
-                       dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(256),
-                       0, s, map, p.H, p.dv, p.nchunks, q, k, v, beta, la,
-                       p.gdt == GDN_BF16, buf);
+    if constexpr (GATE == GDN_GATE_CHANNEL)
+      hipLaunchKernelGGL((fwd_prep_kernel<C, DK, IO, GATE>),
+                         dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(256),
+                         0, s, map, p.H, p.dv, p.nchunks, q, k, v, beta, la,
+                         p.gdt == GDN_BF16, buf);
+    else
+      hipLaunchKernelGGL((fwd_prep_sg_kernel<C, DK, IO, GATE>),
+                         dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(256),
+                         0, s, map, p.H, p.dv, p.nchunks, q, k, v, beta, la,
+                         p.gdt == GDN_BF16, buf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

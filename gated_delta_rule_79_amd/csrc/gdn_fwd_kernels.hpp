@@ -803,6 +803,407 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   }
 }
 
+// ---------------------------------------- prep for per-token gates ---
+// Prep of one (chunk, head) for the scalar gate or no gate, with the same
+// outputs as fwd_prep_kernel, organised around the matrix cores:
+//   - K and V rows are staged in LDS once as 16-byte pieces; the operands
+//     that contract over tokens (X^T = (diag(b gamma) K)^T, K~^T and
+//     Y = diag(b) V) are gathered from their columns, the A and P tiles use
+//     row fragments;
+//   - T = (I + A)^-1 has its 16 x 16 diagonal blocks solved by substitution
+//     (one wave, all blocks at once) and the blocks below filled diagonal by
+//     diagonal on fp32 MFMA:  T_ba = -T_bb sum_{a <= j < b} A_bj T_ja;
+//   - W^T = X^T T^T and U = T Y on the matrix cores in the operand type;
+//   - decays as exp2 of base-2 cumulative log gates.
+template <int C, int DK, typename IO>
+struct PrepSgSmem {
+  static constexpr int ib = io<IO>::bytes;
+  static constexpr int LDKB = DK * ib + 16;        // K row pitch (bytes)
+  static constexpr int VCOLS = 128;                // V columns staged at a time
+  static constexpr int LDVB = VCOLS * ib + 16;     // V row pitch
+  static constexpr int LDC = C + 4;                // fp32 C x C matrices
+  static constexpr int LDZ = 17;                   // 16 x 16 scratch tiles
+  static constexpr size_t k_off = 0;
+  static constexpr size_t v_off = k_off + size_t(C) * LDKB;
+  static constexpr size_t a_off = v_off + size_t(C) * LDVB;
+  static constexpr size_t t_off = a_off + size_t(C) * LDC * 4;
+  static constexpr size_t z_off = t_off + size_t(C) * LDC * 4;
+  static constexpr size_t beta_off = z_off + size_t(4) * 16 * LDZ * 4;
+  static constexpr size_t g_off = beta_off + size_t(C) * 4;
+  static constexpr size_t xs_off = g_off + size_t(C) * 4;
+  static constexpr size_t ks_off = xs_off + size_t(C) * 4;
+  static constexpr size_t total = ks_off + size_t(C) * 4;
+  static_assert(total <= 160 * 1024, "prep LDS budget");
+};
+
+template <int C, int DK, typename IO, int GATE>
+__global__ __launch_bounds__(256) void fwd_prep_sg_kernel(
+    ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
+    const void* __restrict__ k, const void* __restrict__ v,
+    const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
+    FwdBuffers buf) {
+  static_assert(GATE != GDN_GATE_CHANNEL, "per-token gates only");
+  using OP = IO;
+  using S = PrepSgSmem<C, DK, IO>;
+  constexpr int ib = S::ib;
+  constexpr int ob = opstore<OP>::bytes;
+  constexpr int NB = C / 16, NKD = (DK + 31) / 32, NKC = (C + 31) / 32, NDT = DK / 16;
+  constexpr int LDC = S::LDC, LDZ = S::LDZ, LDKB = S::LDKB, LDVB = S::LDVB;
+  constexpr float kLog2e = 1.4426950408889634f;
+  (void)NDT;
+
+  __shared__ __attribute__((aligned(16))) char smem[S::total];
+  char* sK = smem + S::k_off;
+  char* sV = smem + S::v_off;
+  float* sA = reinterpret_cast<float*>(smem + S::a_off);
+  float* sT = reinterpret_cast<float*>(smem + S::t_off);
+  float* sZ = reinterpret_cast<float*>(smem + S::z_off);
+  float* sbeta = reinterpret_cast<float*>(smem + S::beta_off);
+  float* sg2 = reinterpret_cast<float*>(smem + S::g_off);
+  float* sxs = reinterpret_cast<float*>(smem + S::xs_off);
+  float* sks = reinterpret_cast<float*>(smem + S::ks_off);
+
+  const int L = blockIdx.x;
+  const int c = static_cast<int>(L / H);
+  const int h = L - c * H;
+  const ChunkInfo ci = chunk_info(map, c);
+  if (ci.seq < 0) return;
+  const int len = ci.len;
+  const int64_t tok0 = ci.tok0;
+  const int tid = threadIdx.x;
+  // wave index in a scalar register: branches on it are scalar branches,
+  // never EXEC masks (matrix instructions ignore EXEC)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int64_t ch = static_cast<int64_t>(h) * nchunks + c;
+
+  // jobs: the NT2 lower tiles of A (diagonal included), then the P
+  // fragments (rt, jb) with 32 jb <= 16 rt + 15; their q rows are
+  // requested first
+  constexpr int NT2 = NB * (NB + 1) / 2;
+  constexpr int NPF = NB == 1 ? 1 : (NB == 2 ? 2 : 6);
+  constexpr int JOBS = NT2 + NPF;
+  constexpr int MAXJ = (JOBS + 3) / 4;
+  auto p_job = [&](int job, int* rt, int* jb) {
+    int f = job - NT2;
+    for (*rt = 0; *rt < NB; ++*rt) {
+      const int nj = (16 * *rt + 15) / 32 + 1;
+      if (f < nj) { *jb = f; return; }
+      f -= nj;
+    }
+  };
+  opvec<OP> qpre[MAXJ][NKD];
+#pragma unroll
+  for (int u = 0; u < MAXJ; ++u) {
+    const int job = wave + 4 * u;
+    if (job >= NT2 && job < JOBS) {
+      int rt = 0, jb = 0;
+      p_job(job, &rt, &jb);
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb)
+        qpre[u][kb] = row_frag<IO, DK>(q, tok0, H, h, 16 * rt + l16, len, kb * 32 + lg * 8);
+    }
+  }
+
+  // ---- 0. K rows and the first V columns into LDS; beta and base-2
+  //      cumulative log gate.  Every load is issued before any store.
+  constexpr int KP = DK * ib / 16;             // 16-byte pieces per K row
+  constexpr int VPM = S::VCOLS * ib / 16;      // pieces per staged V row
+  constexpr int NKL = (C * KP + 255) / 256;    // K pieces per thread
+  constexpr int NVL = (C * VPM + 255) / 256;   // V pieces per thread (max)
+  auto stage_v = [&](int c0) {
+    // columns [c0, c0 + VCOLS) of V; pieces past dv or the chunk are zero
+    const int VP = min(S::VCOLS, dv - c0) * ib / 16;
+    uint4 raw[NVL];
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / VPM, pc = e % VPM;
+      raw[u] = make_uint4(0, 0, 0, 0);
+      if (e < C * VPM && r < len && pc < VP)
+        raw[u] = *reinterpret_cast<const uint4*>(
+            static_cast<const char*>(v) +
+            (((tok0 + r) * H + h) * static_cast<int64_t>(dv) + c0) * ib + pc * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+      const int e = tid + 256 * u;
+      if (e < C * VPM) *reinterpret_cast<uint4*>(sV + (e / VPM) * LDVB + (e % VPM) * 16) = raw[u];
+    }
+  };
+  {
+    uint4 raw[NKL];
+#pragma unroll
+    for (int u = 0; u < NKL; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / KP, pc = e % KP;
+      raw[u] = make_uint4(0, 0, 0, 0);
+      if (e < C * KP && r < len)
+        raw[u] = *reinterpret_cast<const uint4*>(
+            static_cast<const char*>(k) + ((tok0 + r) * H + h) * DK * ib + pc * 16);
+    }
+    stage_v(0);
+#pragma unroll
+    for (int u = 0; u < NKL; ++u) {
+      const int e = tid + 256 * u;
+      if (e < C * KP) *reinterpret_cast<uint4*>(sK + (e / KP) * LDKB + (e % KP) * 16) = raw[u];
+    }
+  }
+  if (wave == 0) {
+    float x = 0.f, b = 0.f;
+    if (lane < len) {
+      b = load_gate(beta, (tok0 + lane) * H + h, gbf);
+      if constexpr (GATE == GDN_GATE_SCALAR) x = load_gate(la, (tok0 + lane) * H + h, gbf) * kLog2e;
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    const float gend = __shfl(x, C - 1, 64);
+    if (lane < C) {
+      sbeta[lane] = b;
+      sg2[lane] = x;
+      if constexpr (GATE == GDN_GATE_SCALAR) {
+        sxs[lane] = b * __builtin_amdgcn_exp2f(x);
+        sks[lane] = __builtin_amdgcn_exp2f(gend - x);
+      } else {
+        sxs[lane] = b;
+        sks[lane] = 1.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 1. A tiles (LDS, fp32) and P fragments (workspace) ---------------
+  char* dP = buf.at(ch, buf.off_p);
+#pragma unroll
+  for (int u = 0; u < MAXJ; ++u) {
+    const int job = wave + 4 * u;
+    if (job >= JOBS) continue;
+    if (job < NT2) {
+      int t = job, rt = 0;
+      while (t > rt) { t -= rt + 1; ++rt; }
+      const int it = t;
+      const int ra = 16 * rt + l16, rb = 16 * it + l16;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb) {
+        // K slots past DK (DK = 16) hold zero; the product itself is never
+        // behind a per-lane condition
+        const int k0 = kb * 32 + lg * 8;
+        opvec<OP> af = zero_vec<OP>(), bf = zero_vec<OP>();
+        if (k0 < DK) {
+          af = *reinterpret_cast<const opvec<OP>*>(sK + ra * LDKB + k0 * ib);
+          bf = *reinterpret_cast<const opvec<OP>*>(sK + rb * LDKB + k0 * ib);
+        }
+        acc = mma32(af, bf, acc);
+      }
+      const int i = 16 * it + l16;
+      const float gi = sg2[i];
+      const floatx4 br = *reinterpret_cast<const floatx4*>(sbeta + 16 * rt + 4 * lg);
+      const floatx4 gr = *reinterpret_cast<const floatx4*>(sg2 + 16 * rt + 4 * lg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * lg + e;
+        float val = acc[e] * br[e];
+        if constexpr (GATE == GDN_GATE_SCALAR) val *= __builtin_amdgcn_exp2f(gr[e] - gi);
+        sA[r * LDC + i] = i < r ? val : 0.f;
+      }
+    } else {
+      int rt = 0, jb = 0;
+      p_job(job, &rt, &jb);
+      const int r = 16 * rt + l16;
+      const float grr = sg2[r];
+      float out[8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int it = 2 * jb + half;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        const floatx4 gi4 = it < NB ? *reinterpret_cast<const floatx4*>(sg2 + 16 * it + 4 * lg)
+                                    : floatx4{0.f, 0.f, 0.f, 0.f};
+        if (it <= rt && it < NB) {
+          const int ri = 16 * it + l16;
+#pragma unroll
+          for (int kb = 0; kb < NKD; ++kb) {
+            const int k0 = kb * 32 + lg * 8;
+            opvec<OP> kf = zero_vec<OP>();
+            if (k0 < DK) kf = *reinterpret_cast<const opvec<OP>*>(sK + ri * LDKB + k0 * ib);
+            acc = mma32(kf, qpre[u][kb], acc);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * it + 4 * lg + e;
+          float val = acc[e];
+          if constexpr (GATE == GDN_GATE_SCALAR) val *= __builtin_amdgcn_exp2f(grr - gi4[e]);
+          out[4 * half + e] = (it <= rt && it < NB && i <= r) ? val : 0.f;
+        }
+      }
+      *reinterpret_cast<opvec<OP>*>(dP + ((size_t(rt) * NKC + jb) * 64 + lane) * 8 * ob) =
+          frag<OP>::from_floats(out);
+    }
+  }
+  // strictly upper blocks of T are zero; decays for the state pass
+  for (int e = tid; e < C * C; e += 256) {
+    const int r = e / C, i = e % C;
+    if ((i >> 4) > (r >> 4)) sT[r * LDC + i] = 0.f;
+  }
+  {
+    float* gam = reinterpret_cast<float*>(buf.at(ch, buf.off_g));
+    if (tid < C) gam[tid] = GATE == GDN_GATE_SCALAR ? __builtin_amdgcn_exp2f(sg2[tid]) : 1.f;
+    for (int d = tid; d < DK; d += 256)
+      gam[C + d] = GATE == GDN_GATE_SCALAR ? __builtin_amdgcn_exp2f(sg2[C - 1]) : 1.f;
+  }
+  __syncthreads();
+
+  // ---- 2. diagonal blocks of T: lane 16 b + j solves column j of block b
+  if (wave == 0) {
+    const int b = lane >> 4, j = lane & 15;
+    if (b < NB) {
+      float x[16];
+      const float* Ab = sA + (16 * b) * LDC + 16 * b;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < r; ++i) s += Ab[r * LDC + i] * x[i];
+        x[r] = (r == j) ? 1.f : (r < j ? 0.f : -s);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sT[(16 * b + r) * LDC + 16 * b + j] = x[r];
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. blocks below the diagonal, one diagonal d = b - a at a time ---
+  for (int d = 1; d < NB; ++d) {
+    const int a = wave, b = wave + d;
+    if (b < NB) {
+      floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 16 * a; k0 < 16 * b; k0 += 4)
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * b + l16) * LDC + k0 + lg],
+                                                 sT[(k0 + lg) * LDC + 16 * a + l16], z, 0, 0, 0);
+      float* zw = sZ + wave * 16 * LDZ;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zw[(4 * lg + e) * LDZ + l16] = z[e];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes
+      __builtin_amdgcn_wave_barrier();
+      floatx4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4)
+        t = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[(16 * b + l16) * LDC + 16 * b + k0 + lg],
+                                                 zw[(k0 + lg) * LDZ + l16], t, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sT[(16 * b + 4 * lg + e) * LDC + 16 * a + l16] = -t[e];
+    }
+    __syncthreads();
+  }
+
+  // ---- 4. T fragments: row r of tile rt, tokens 32 kb + perm_k ---------
+  opvec<OP> tf[NB][NKC];
+#pragma unroll
+  for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb) {
+      if (32 * kb > 16 * rt + 15) continue;  // T is lower triangular
+      const float* row = sT + (16 * rt + l16) * LDC + 32 * kb + 4 * lg;
+      float x[8];
+      const floatx4 lo = *reinterpret_cast<const floatx4*>(row);
+      floatx4 hi = {0.f, 0.f, 0.f, 0.f};
+      if (32 * kb + 16 < C) hi = *reinterpret_cast<const floatx4*>(row + 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { x[e] = lo[e]; x[4 + e] = hi[e]; }
+      tf[rt][kb] = frag<OP>::from_floats(x);
+    }
+
+  // ---- 5. K~^T fragments and -W fragments: wave w owns dk block w -------
+  // (token order perm_k in both, so one gather of K's columns serves both)
+  for (int jb = wave; jb < NKD; jb += 4) {
+    opvec<OP> xf[2][NKC];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int a = 2 * jb + half;
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb) {
+        float kt[8], xt[8];
+        const int dk = 16 * a + l16;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int i = 32 * kb + perm_k(lg, s);
+          float x = 0.f;
+          if (16 * a < DK && i < C) x = lds_ld<IO>(sK + i * LDKB, dk);
+          kt[s] = i < C ? x * sks[i] : 0.f;
+          xt[s] = i < C ? x * sxs[i] : 0.f;
+        }
+        xf[half][kb] = frag<OP>::from_floats(xt);
+        if (16 * a < DK)
+          *reinterpret_cast<opvec<OP>*>(
+              buf.at(ch, buf.off_k) + ((size_t(a) * NKC + kb) * 64 + lane) * 8 * ob) =
+              frag<OP>::from_floats(kt);
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+      floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb) {
+        if (32 * kb > 16 * rt + 15) continue;
+        acc0 = mma32(xf[0][kb], tf[rt][kb], acc0);
+        if (32 * jb + 16 < DK) acc1 = mma32(xf[1][kb], tf[rt][kb], acc1);
+      }
+      float out[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        out[e] = -acc0[e];
+        out[4 + e] = -acc1[e];
+      }
+      *reinterpret_cast<opvec<OP>*>(
+          buf.at(ch, buf.off_w) + ((size_t(rt) * NKD + jb) * 64 + lane) * 8 * ob) =
+          frag<OP>::from_floats(out);
+    }
+  }
+
+  // ---- 6. U = T Y, Y = diag(b) V: wave w takes value tiles w, w + 4, ..
+  //      of each VCOLS-column pass --------------------------------------
+  for (int c0 = 0; c0 < dv; c0 += S::VCOLS) {
+    if (c0 > 0) {
+      __syncthreads();  // every wave is done with the previous columns
+      stage_v(c0);
+      __syncthreads();
+    }
+    char* U = buf.at(ch, buf.off_u);
+    const int ndvt = dv / 16;
+    const int nvt = min(S::VCOLS, dv - c0) / 16;
+    for (int vl = wave; vl < nvt; vl += 4) {
+      const int vt = c0 / 16 + vl;
+      opvec<OP> yf[NKC];
+      const int col = 16 * vl + l16;
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb) {
+        float y[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int i = 32 * kb + perm_k(lg, s);
+          y[s] = i < C ? lds_ld<IO>(sV + i * LDVB, col) * sbeta[i] : 0.f;
+        }
+        yf[kb] = frag<OP>::from_floats(y);
+      }
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKC; ++kb) {
+          if (32 * kb > 16 * rt + 15) continue;
+          acc = mma32(tf[rt][kb], yf[kb], acc);
+        }
+        *reinterpret_cast<typename acc4<OP>::type*>(
+            U + ((size_t(rt) * ndvt + vt) * 64 + lane) * 4 * ob) = from_f4<OP>(acc);
+      }
+    }
+  }
+}
+
 // Segment buffers of the split state pass (per segment slot and head):
 //   trm : state the segment produces from zero, fp32 accumulator layout
 //         [dv/16][DK/16][64 lanes][4]
