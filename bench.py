@@ -10,6 +10,11 @@ JSON line with tokens/s, the roofline position of the dominant kernel
 (per-kernel device time from HIP events recorded by the library on the launch
 stream) and the fp64 CPU oracle timed on this host as a baseline.
 
+Other entry points (same JSON shape, their own metric string):
+    --mode bwd      gdn_chunk_bwd alone      (default workload varlen_16k_dv256)
+    --mode fwdbwd   forward + backward       (tokens / (t_fwd + t_bwd))
+    --mode decode   gdn_decode_step in place (default workload decode_n256_h32)
+
 Algorithmic work per (token, head), chunk C:
     flops = 6 dk dv + C (3 dk + 2 dv) + C^2 / 3
     bytes = (2 dk + 2 dv) s_io + s_beta + s_gate      (+ state once per chain)
@@ -68,6 +73,217 @@ def measured_traffic(workload, kernel, src_hash):
     return d.get("bytes_per_launch")
 
 
+def bwd_algorithmic(B, T, H, dk, dv, C, s_io, s_gate, gate, nseq):
+    """Backward: flops = 2 x forward (matmul-backward convention, recompute not
+    counted); bytes = read q, k, v, dO, beta, log-alpha, write dq, dk, dv and
+    fp32 dbeta, dlog-alpha."""
+    f_flops, _ = algorithmic(B, T, H, dk, dv, C, s_io, s_gate, gate, nseq, False, False)
+    th = B * T * H
+    gl = 0 if gate == "none" else (dk if gate == "channel" else 1)
+    byts = th * ((2 * dk + 2 * dv) * s_io + dv * s_io + s_gate + gl * s_gate)  # reads
+    byts += th * ((2 * dk + dv) * s_io + 4 + gl * 4)                          # writes
+    return 2 * f_flops, byts
+
+
+def decode_bytes(N, H, dk, dv, s_io):
+    """Per step: fp32 state read and written once, q, k, v read, o written, and
+    beta, log-alpha (fp32 or bf16; counted as 8 bytes)."""
+    return N * H * (8 * dk * dv + (2 * dk + 2 * dv) * s_io + 8)
+
+
+def cpu_baseline_bwd(inp, budget_s):
+    """The oracle's adjoint on whole (sequence, head) chains, one thread, until
+    about budget_s seconds; rate scaled to the whole workload's tokens."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    f = inp.f64
+    T_all = f["q"].shape[1]
+    H = f["q"].shape[2]
+    cu = (np.array([0, T_all]) if inp.cu_seqlens is None else inp.cu_seqlens.numpy())
+    units = [(s, h) for s in range(len(cu) - 1) for h in range(H)]
+    done_tok = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for s, h in units:
+            a, b = int(cu[s]), int(cu[s + 1])
+            sl = lambda x: None if x is None else x[0, a:b, h]
+            m0 = np.zeros((f["q"].shape[3], f["v"].shape[3]))
+            oracle.gdn_bwd_chain(sl(f["q"]), sl(f["k"]), sl(f["v"]), sl(f["beta"]),
+                                 sl(f["log_alpha"]), m0, sl(f["do"]), None, inp.gate)
+            done_tok += b - a
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    frac = done_tok / float(T_all * H)
+    return {"value": T_all * frac / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_tok} of {T_all * H} token-heads of the backward as whole "
+                      f"(sequence, head) chains ({dt:.1f} s, 1 thread); tokens/s scaled "
+                      "to the whole workload"}
+
+
+def cpu_baseline_decode(inp, budget_s):
+    """The oracle's decode step on (sequence, head) rows, one thread, until
+    about budget_s seconds; rate scaled to the whole batch (tokens/s)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    f = inp.f64
+    N, _, H, dk = f["q"].shape
+    rows = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for n in range(N):
+            la = None if f["log_alpha"] is None else f["log_alpha"][n:n + 1, 0]
+            oracle.gdn_decode(f["q"][n:n + 1, 0], f["k"][n:n + 1, 0], f["v"][n:n + 1, 0],
+                              f["beta"][n:n + 1, 0], la, f["s0"][n:n + 1], inp.gate)
+            rows += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    steps_per_s = (rows / N) / dt
+    return {"value": N * steps_per_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {N} sequences x {H} heads of one decode step "
+                      f"({dt:.1f} s, 1 thread); tokens/s scaled to the whole batch"}
+
+
+def time_calls(fn, steps, warmup, cold_steps=0):
+    """Median-free K-call timing with events on the current stream, plus an
+    optional cold median (1 GiB write before each call)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        fn()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    cold = None
+    if cold_steps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        times = []
+        for _ in range(cold_steps):
+            flush.fill_(1)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        times.sort()
+        cold = times[len(times) // 2]
+        del flush
+    return ms, cold
+
+
+def stage_pass(fn, steps):
+    import torch
+    import gated_delta_rule_79_amd as gdn
+    gdn.stage_times(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    st = gdn.stage_times()
+    gdn.stage_times(False)
+    return {k: v[0] / v[1] for k, v in st.items()}
+
+
+def main_other(args):
+    """bwd, fwdbwd and decode modes."""
+    import torch
+    import gated_delta_rule_79_amd as gdn
+    from gated_delta_rule_79_amd import synth
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    wl = args.workload or ("decode_n256_h32" if args.mode == "decode" else "varlen_16k_dv256")
+    inp = synth.workload(wl, with_do=args.mode != "decode")
+    d = inp.to("cuda")
+    B, T, H, dk = inp.q.shape
+    dv = inp.v.shape[-1]
+    C = inp.chunk
+    s_io = 2 if inp.q.dtype == torch.bfloat16 else 4
+    s_gate = 2 if inp.beta.dtype == torch.bfloat16 else 4
+    nseq = B if inp.cu_seqlens is None else inp.cu_seqlens.numel() - 1
+    cfg = {"workload": wl, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": C,
+           "gate": inp.gate, "seed": inp.seed, "state": "fp32", "parallelism": "single GPU"}
+    out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if s_io == 2 else "f32",
+           "data": "synthetic", "config": cfg}
+    if args.mode == "decode":
+        q, k, v = d.q[:, 0], d.k[:, 0], d.v[:, 0]
+        beta = d.beta[:, 0]
+        la = None if d.log_alpha is None else d.log_alpha[:, 0]
+        state = d.s0.clone()
+        fn = lambda: gdn.decode_step(q, k, v, beta, la, state)
+        ms, cold = time_calls(fn, args.steps, args.warmup, args.cold_steps)
+        per = stage_pass(fn, args.steps)
+        kms = per.get("decode", ms)
+        byts = decode_bytes(B, H, dk, dv, s_io)
+        gbs = byts / (kms * 1e-3) / 1e9
+        out.update({"metric": "tokens/sec gdn_decode_step (N=%d,H=%d,d=%d); %% HBM" % (B, H, dk),
+                    "value": round(B / (ms * 1e-3), 1), "unit": "tokens/s",
+                    "ms_per_step": round(ms, 5),
+                    "cold_ms_per_step": None if cold is None else round(cold, 5),
+                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                 "traffic": None, "kernel": "decode_kernel",
+                                 "kernel_ms": {k2: round(v2, 5) for k2, v2 in per.items()},
+                                 "alg_bytes_per_launch": int(byts)}})
+        cpu = None if args.no_cpu_baseline else cpu_baseline_decode(inp, args.cpu_budget)
+    else:
+        plan = gdn.FwdPlan(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, chunk=C,
+                           cu_seqlens=d.cu_seqlens)
+        bwd = lambda: gdn.chunk_bwd(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, d.do,
+                                    d.ds_final, chunk=C, cu_seqlens=d.cu_seqlens,
+                                    need_ds0=d.s0 is not None)
+        ms_b, cold_b = time_calls(bwd, args.steps, args.warmup, args.cold_steps)
+        per = stage_pass(bwd, args.steps)
+        bflops, bbytes = bwd_algorithmic(B, T, H, dk, dv, C, s_io, s_gate, inp.gate, nseq)
+        tokens = B * T
+        rf = {"bound": "mfma", "achieved": round(bflops / (ms_b * 1e-3) / 1e12, 2),
+              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+              "frac": round(bflops / (ms_b * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+              "traffic": None, "kernel": "gdn_chunk_bwd (all stages)",
+              "kernel_ms": {k2: round(v2, 5) for k2, v2 in per.items()},
+              "alg_flops_per_launch": int(bflops), "alg_bytes_per_launch": int(bbytes),
+              "path_frac_hbm": round(bbytes / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if args.mode == "bwd":
+            out.update({"metric": "tokens/sec gdn_chunk_bwd (%s); %% MFMA/HBM roofline" % wl,
+                        "value": round(tokens / (ms_b * 1e-3), 1), "unit": "tokens/s",
+                        "ms_per_step": round(ms_b, 5),
+                        "cold_ms_per_step": None if cold_b is None else round(cold_b, 5),
+                        "roofline": rf})
+        else:
+            ms_f, cold_f = time_calls(plan.run, args.steps, args.warmup, args.cold_steps)
+            fflops, fbytes = algorithmic(B, T, H, dk, dv, C, s_io, s_gate, inp.gate, nseq,
+                                         inp.s0 is not None, True)
+            ms = ms_f + ms_b
+            rf.update({"kernel": "gdn_chunk_fwd + gdn_chunk_bwd", "fwd_ms": round(ms_f, 5),
+                       "bwd_ms": round(ms_b, 5),
+                       "achieved": round((fflops + bflops) / (ms * 1e-3) / 1e12, 2),
+                       "frac": round((fflops + bflops) / (ms * 1e-3) / 1e12 /
+                                     MFMA_BF16_PEAK_TFLOPS, 4),
+                       "alg_flops_per_launch": int(fflops + bflops),
+                       "alg_bytes_per_launch": int(fbytes + bbytes),
+                       "path_frac_hbm": round((fbytes + bbytes) / (ms * 1e-3) / 1e9 /
+                                              HBM_PEAK_GBS, 4)})
+            out.update({"metric": "tokens/sec gdn_chunk_fwd+bwd (%s); %% MFMA/HBM roofline" % wl,
+                        "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s",
+                        "ms_per_step": round(ms, 5), "cold_ms_per_step": None,
+                        "roofline": rf})
+        cpu = None if args.no_cpu_baseline else cpu_baseline_bwd(inp, args.cpu_budget)
+    if cpu is not None:
+        cpu["value"] = round(cpu["value"], 1)
+    out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(inp, budget_s):
     """The fp64 oracle, as it stands, on whole (sequence, head) chains of the
     same workload until about ``budget_s`` seconds of work; BLAS held to one
@@ -104,7 +320,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="fwd_t4096_h16")
+    ap.add_argument("--workload", default=None,
+                    help="synthetic workload (default: fwd_t4096_h16 for the forward)")
+    ap.add_argument("--mode", default="fwd", choices=("fwd", "bwd", "fwdbwd", "decode"))
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20,
@@ -120,6 +338,12 @@ def main():
               "single MI355X (heads and sequences shard with no communication; see "
               "the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.mode != "fwd":
+        main_other(args)
+        return
+    if args.workload is None:
+        args.workload = "fwd_t4096_h16"
 
     import torch
     import gated_delta_rule_79_amd as gdn

@@ -182,12 +182,13 @@ int plan_segments(const Problem& p) {
   const int set = g_seg_chunks.load();
   if (set < 0 || p.nseq == 0) return 0;
   if (set > 0) return std::min(set, 1 << 20);
-  // automatic: split only when the (sequence, head, 16-column slab) chains
-  // cannot cover the SIMDs, into segments of ~sqrt(n / 2) chunks, which
+  // automatic: a state-pass workgroup takes one (sequence, head) and 8 value
+  // slabs and walks its chunks in order.  Split when those workgroups cannot
+  // fill the CUs twice over, into segments of ~sqrt(n / 2) chunks, which
   // balances the two per-segment passes against the sequential combine
-  const int64_t chains = static_cast<int64_t>(p.nseq) * p.H * (p.dv / 16);
+  const int64_t groups = static_cast<int64_t>(p.nseq) * p.H * ((p.dv / 16 + 7) / 8);
   const double n = static_cast<double>(p.nchunks - (p.varlen ? p.nseq : 0)) / p.nseq;
-  if (chains >= 1024 || n < 8.0) return 0;
+  if (groups >= 512 || n < 8.0) return 0;
   return std::max(2, static_cast<int>(std::ceil(std::sqrt(n / 2.0))));
 }
 

@@ -315,6 +315,33 @@ __device__ __forceinline__ floatx4 tmma(FA A, FB B, int m0, int n0, int l16,
   return acc;
 }
 
+// 16x16 tile product over a 16-column value slab whose operands both keep
+// the contraction index contiguous in fp32 LDS: A(m, j) = A[m * ld + j],
+// B(j, n) = bs(n) * B[n * ld + j] (ld even).  Lanes of K groups 0 and 1 read
+// their 8 columns as 8-byte pieces, groups 2 and 3 carry the zero half of
+// the 32-wide K block; the product itself is unconditional.
+template <typename OP>
+__device__ __forceinline__ floatx4 slab_mma(const float* A, const float* B, int ld,
+                                            float bs, int l16, int lg, floatx4 acc) {
+  float a[8], b[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) a[s] = b[s] = 0.f;
+  if (lg < 2) {
+    const float* pa = A + l16 * ld + 8 * lg;
+    const float* pb = B + l16 * ld + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float2 x = *reinterpret_cast<const float2*>(pa + 2 * s);
+      const float2 y = *reinterpret_cast<const float2*>(pb + 2 * s);
+      a[2 * s] = x.x;
+      a[2 * s + 1] = x.y;
+      b[2 * s] = y.x * bs;
+      b[2 * s + 1] = y.y * bs;
+    }
+  }
+  return mma32(frag<OP>::from_floats(a), frag<OP>::from_floats(b), acc);
+}
+
 // Sum of a 16x16 accumulator tile over its 16 columns: lanes with
 // l16 == 0 return the sums of rows 4 lg .. 4 lg + 3.
 __device__ __forceinline__ floatx4 tile_rowsum(floatx4 x) {
@@ -340,7 +367,10 @@ struct GradSmem {
   static constexpr bool CH = GATE == GDN_GATE_CHANNEL;
   static constexpr int LDK = DK + 16 / ib;   // K, Q rows (elements)
   static constexpr int LDC = C + 1;          // fp32 C x C
-  static constexpr int LDS_ = SW + 1;        // fp32 slab rows
+  // fp32 slab rows: an even pitch lets the products over the slab's columns
+  // read 8-byte pieces (conflict-free at 18); the per-channel gate keeps the
+  // odd pitch, its LDS budget has no room for the extra column
+  static constexpr int LDS_ = CH ? SW + 1 : SW + 2;
   static constexpr int LDD = DK + 1;         // fp32 C x DK (post phase)
   static constexpr int NB = C / 16, NDT = DK / 16;
   static constexpr size_t k_off = 0;
@@ -631,21 +661,47 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 
   for (int s0 = 0; s0 < dv; s0 += SW) {
     // stage V, dO (rows of the chunk) and M0, dM1 (rows dk) for this slab
-    for (int e = tid; e < C * SW; e += 256) {
-      const int r = e / SW, j = e % SW;
-      float vv = 0.f, gg = 0.f;
-      if (r < len) {
-        const int64_t off = ((tok0 + r) * H + h) * dv + s0 + j;
-        vv = io<IO>::load(v, off);
-        gg = io<IO>::load(d_o, off);
+    {
+      // every load of the slab is issued before its LDS stores
+      constexpr int NVE = (C * SW + 255) / 256, NME = (DK * SW + 255) / 256;
+      float vv[NVE], gg[NVE], mm[NME], dd[NME];
+#pragma unroll
+      for (int u = 0; u < NVE; ++u) {
+        const int e = tid + 256 * u;
+        const int r = e / SW, j = e % SW;
+        vv[u] = gg[u] = 0.f;
+        if (e < C * SW && r < len) {
+          const int64_t off = ((tok0 + r) * H + h) * dv + s0 + j;
+          vv[u] = io<IO>::load(v, off);
+          gg[u] = io<IO>::load(d_o, off);
+        }
       }
-      sV[r * LS + j] = vv;
-      sDO[r * LS + j] = gg;
-    }
-    for (int e = tid; e < DK * SW; e += 256) {
-      const int d = e / SW, j = e % SW;
-      sM0[d * LS + j] = M0g[static_cast<int64_t>(d) * dv + s0 + j];
-      sDM1[d * LS + j] = dM1g[static_cast<int64_t>(d) * dv + s0 + j];
+#pragma unroll
+      for (int u = 0; u < NME; ++u) {
+        const int e = tid + 256 * u;
+        const int d = e / SW, j = e % SW;
+        mm[u] = dd[u] = 0.f;
+        if (e < DK * SW) {
+          mm[u] = M0g[static_cast<int64_t>(d) * dv + s0 + j];
+          dd[u] = dM1g[static_cast<int64_t>(d) * dv + s0 + j];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NVE; ++u) {
+        const int e = tid + 256 * u;
+        if (e < C * SW) {
+          sV[(e / SW) * LS + e % SW] = vv[u];
+          sDO[(e / SW) * LS + e % SW] = gg[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NME; ++u) {
+        const int e = tid + 256 * u;
+        if (e < DK * SW) {
+          sM0[(e / SW) * LS + e % SW] = mm[u];
+          sDM1[(e / SW) * LS + e % SW] = dd[u];
+        }
+      }
     }
     __syncthreads();
     // Z = Y - X M0 (Y = diag(b) V),  dE = P^T dO + K~ dM1
@@ -721,26 +777,38 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       const int t = wave + 4 * u;
       if (t >= NCD) continue;
       const int mt = t / NDT, nt = t % NDT;
-      auto M0t = [&](int j, int d) { return sM0[d * LS + j]; };
-      aQ[u] = tmma<OP, SW>([&](int r, int j) { return sDO[r * LS + j]; }, M0t,
-                           16 * mt, 16 * nt, l16, lg, aQ[u]);
-      aW[u] = tmma<OP, SW>([&](int r, int j) { return sDE[r * LS + j]; }, M0t,
-                           16 * mt, 16 * nt, l16, lg, aW[u]);
-      aK[u] = tmma<OP, SW>([&](int r, int j) { return sE[r * LS + j]; },
-                           [&](int j, int d) { return sDM1[d * LS + j]; },
-                           16 * mt, 16 * nt, l16, lg, aK[u]);
+      if constexpr (LS % 2 == 0 && SW == 16) {
+        aQ[u] = slab_mma<OP>(sDO + 16 * mt * LS, sM0 + 16 * nt * LS, LS, 1.f, l16, lg, aQ[u]);
+        aW[u] = slab_mma<OP>(sDE + 16 * mt * LS, sM0 + 16 * nt * LS, LS, 1.f, l16, lg, aW[u]);
+        aK[u] = slab_mma<OP>(sE + 16 * mt * LS, sDM1 + 16 * nt * LS, LS, 1.f, l16, lg, aK[u]);
+      } else {
+        auto M0t = [&](int j, int d) { return sM0[d * LS + j]; };
+        aQ[u] = tmma<OP, SW>([&](int r, int j) { return sDO[r * LS + j]; }, M0t,
+                             16 * mt, 16 * nt, l16, lg, aQ[u]);
+        aW[u] = tmma<OP, SW>([&](int r, int j) { return sDE[r * LS + j]; }, M0t,
+                             16 * mt, 16 * nt, l16, lg, aW[u]);
+        aK[u] = tmma<OP, SW>([&](int r, int j) { return sE[r * LS + j]; },
+                             [&](int j, int d) { return sDM1[d * LS + j]; },
+                             16 * mt, 16 * nt, l16, lg, aK[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < NUC; ++u) {
       const int t = wave + 4 * u;
       if (t >= NCC) continue;
       const int mt = t / NB, nt = t % NB;
-      aP[u] = tmma<OP, SW>([&](int r, int j) { return sDO[r * LS + j]; },
-                           [&](int j, int i) { return sE[i * LS + j]; },
-                           16 * mt, 16 * nt, l16, lg, aP[u]);
-      aT[u] = tmma<OP, SW>([&](int r, int j) { return sDE[r * LS + j]; },
-                           [&](int j, int i) { return sbeta[i] * sV[i * LS + j]; },
-                           16 * mt, 16 * nt, l16, lg, aT[u]);
+      if constexpr (LS % 2 == 0 && SW == 16) {
+        aP[u] = slab_mma<OP>(sDO + 16 * mt * LS, sE + 16 * nt * LS, LS, 1.f, l16, lg, aP[u]);
+        aT[u] = slab_mma<OP>(sDE + 16 * mt * LS, sV + 16 * nt * LS, LS,
+                             sbeta[16 * nt + l16], l16, lg, aT[u]);
+      } else {
+        aP[u] = tmma<OP, SW>([&](int r, int j) { return sDO[r * LS + j]; },
+                             [&](int j, int i) { return sE[i * LS + j]; },
+                             16 * mt, 16 * nt, l16, lg, aP[u]);
+        aT[u] = tmma<OP, SW>([&](int r, int j) { return sDE[r * LS + j]; },
+                             [&](int j, int i) { return sbeta[i] * sV[i * LS + j]; },
+                             16 * mt, 16 * nt, l16, lg, aT[u]);
+      }
     }
     __syncthreads();
   }

@@ -182,11 +182,15 @@ def test_workspace_of_segmented_state_pass(lib):
         lib.gdn_set_segment_chunks(0)
         _, auto = ws_bytes(lib, prob(T=4096, H=16))
         assert auto - off_big == seg_bytes(11, 16, 128, 128, 2)
-        # enough (sequence, head, slab) chains: no split
-        _, a = ws_bytes(lib, prob(B=8, T=4096, H=16))
+        # enough (sequence, head) workgroups (32 x 16 = 512): no split
+        _, a = ws_bytes(lib, prob(B=32, T=4096, H=16))
         lib.gdn_set_segment_chunks(-1)
-        _, b = ws_bytes(lib, prob(B=8, T=4096, H=16))
+        _, b = ws_bytes(lib, prob(B=32, T=4096, H=16))
         assert a == b
+        # 8 x 16 = 128 workgroups of 64 chunks: split into 11 segments each
+        lib.gdn_set_segment_chunks(0)
+        _, a = ws_bytes(lib, prob(B=8, T=4096, H=16))
+        assert a - b // 4 == seg_bytes(8 * 11, 16, 128, 128, 2)
         # varlen with a forced split: segment table + buffers for at most
         # nchunks / L + nseq slots
         lib.gdn_set_segment_chunks(2)
