@@ -278,10 +278,24 @@ def main_other(args):
                         "ms_per_step": round(ms, 5), "cold_ms_per_step": None,
                         "roofline": rf})
         cpu = None if args.no_cpu_baseline else cpu_baseline_bwd(inp, args.cpu_budget)
+    if args.copy_calibration:
+        copy_calibration()
     if cpu is not None:
         cpu["value"] = round(cpu["value"], 1)
     out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
+
+
+def copy_calibration():
+    """Three device copies of 256 MiB: a kernel of known traffic for scaling
+    memory counters."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda").fill_(3)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(inp, budget_s):
@@ -404,12 +418,7 @@ def main():
         del flush
 
     if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda").fill_(3)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration()
 
     s_io = 2 if inp.q.dtype == torch.bfloat16 else 4
     s_gate = 2 if inp.beta.dtype == torch.bfloat16 else 4
