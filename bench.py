@@ -47,10 +47,15 @@ def algorithmic(B, T, H, dk, dv, C, s_io, s_gate, gate, nseq, s0, sfinal):
 
 
 def source_hash(files):
+    """Hash of the kernel sources with // comments and blank lines removed,
+    so a counter summary stays valid across comment-only edits."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -58,6 +63,8 @@ FWD_SOURCES = ["gated_delta_rule_79_amd/csrc/gdn_fwd.hip",
                "gated_delta_rule_79_amd/csrc/gdn_fwd_kernels.hpp",
                "gated_delta_rule_79_amd/csrc/gdn_chunk_common.hpp",
                "gated_delta_rule_79_amd/csrc/gdn_device.hpp"]
+DECODE_SOURCES = ["gated_delta_rule_79_amd/csrc/gdn_decode.hip",
+                  "gated_delta_rule_79_amd/csrc/gdn_device.hpp"]
 
 
 def measured_traffic(workload, kernel, src_hash):
@@ -232,7 +239,9 @@ def main_other(args):
                     "cold_ms_per_step": None if cold is None else round(cold, 5),
                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                 "traffic": None, "kernel": "decode_kernel",
+                                 "traffic": measured_traffic(
+                                     wl, "decode_kernel", source_hash(DECODE_SOURCES)),
+                                 "kernel": "decode_kernel",
                                  "kernel_ms": {k2: round(v2, 5) for k2, v2 in per.items()},
                                  "alg_bytes_per_launch": int(byts)}})
         cpu = None if args.no_cpu_baseline else cpu_baseline_decode(inp, args.cpu_budget)

@@ -14,19 +14,31 @@
 //
 // (the per-channel gate moves every exp(g_r - g_i) inside the k-sums).
 //
-// Two kernels:
+// Kernels, in launch order:
 //   prep (one workgroup per chunk and head, all in parallel): cumulative gate,
 //     K K^T and Q K^T on the matrix cores, the unit lower-triangular inverse T
-//     in LDS (16x16 diagonal blocks by column substitution, then block rows),
-//     W and U products; writes every operand the state pass needs already in
-//     MFMA fragment order.
-//   scan (one wave per sequence, head and 16-column slab of dv): carries the
-//     fp32 state slab in registers across the chunks of the sequence.  Each
-//     chunk is E = U - W M, O = Q~ M + P E, M <- gamma_c M + K~^T E.  The
-//     state and E accumulators are fed straight back as MFMA operands in a
-//     permuted K order (see perm_k), so the sequential chain never goes
-//     through LDS.  dv columns are independent, so slabs need no
-//     communication.
+//     (16x16 diagonal blocks by column substitution, off-diagonal blocks by
+//     block rows on fp32 MFMA), W and U products; writes every operand the
+//     state pass needs already in MFMA fragment order.
+//   The state pass carries M across the chunks of each sequence.  Over one
+//   chunk M -> (gamma_c I - K~^T W) M + K~^T U is affine in M, so so is the
+//   map over a run of chunks (a segment): M_end = Phi M_start + M0.  When the
+//   (sequence, head) chains alone cannot fill the GPU, the chains are cut
+//   into segments and the pass runs in three launches:
+//   trans   (per segment, head and group of 16-column tiles): M0 from a zero
+//           state with U, and Phi by running the identity's columns through
+//           the same chain without U.
+//   combine (per sequence, head and dv tile): M_{j+1} = Phi_j M_j + M0_j
+//           over the segments, the entering state of each segment.
+//   scan    (per segment, head and group of eight 16-column dv tiles, one
+//           wave per tile): E = U - W M, O = Q~ M + P E, M <- gamma_c M
+//           + K~^T E from the segment's entering state; writes O and the
+//           final state.  Unsplit chains run the scan alone from S0.
+//   The state tile and E accumulators are fed straight back as MFMA operands
+//   in a permuted K order (see perm_k), so the sequential chain never goes
+//   through LDS; the per-chunk operands are staged into LDS by direct
+//   global-to-LDS loads, double-buffered one chunk ahead.  dv columns are
+//   independent, so tiles need no communication.
 
 #include "gdn_fwd_kernels.hpp"
 
