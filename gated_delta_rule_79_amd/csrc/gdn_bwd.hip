@@ -1104,7 +1104,7 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
       const int64_t ngrp = (p.dv / 16 + kScanGroup - 1) / kScanGroup;
       hipLaunchKernelGGL((fwd_scan_kernel<C, DK, IO, GATE, true>),
                          dim3(static_cast<unsigned>(p.nseq * p.H * ngrp)),
-                         dim3(64 * kStateWaves), 0, s, map,
+                         dim3(64 * kScanWaves), 0, s, map,
                          whole, p.H, p.dv, p.nchunks, q, s0,
                          static_cast<void*>(nullptr), static_cast<float*>(nullptr),
                          buf, SegBuffers{}, states);

@@ -199,7 +199,7 @@ hipError_t run_fwd(const Problem& p, const void* q, const void* k,
       const int64_t ngrp = (ndvt + DK / 16 + kTransGroup - 1) / kTransGroup;
       hipLaunchKernelGGL((fwd_trans_kernel<C, DK, IO, GATE>),
                          dim3(static_cast<unsigned>(p.nsegs * p.H * ngrp)),
-                         dim3(64 * kStateWaves), 0, s, map, sm, p.H, p.dv, p.nchunks,
+                         dim3(64 * kTransWaves), 0, s, map, sm, p.H, p.dv, p.nchunks,
                          buf, sb);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -217,7 +217,7 @@ hipError_t run_fwd(const Problem& p, const void* q, const void* k,
   const int64_t nwork = p.nsegs * p.H * ((ndvt + kScanGroup - 1) / kScanGroup);
   StageScope scope(GDN_STAGE_FWD_SCAN, s);
   hipLaunchKernelGGL((fwd_scan_kernel<C, DK, IO, GATE>),
-                     dim3(static_cast<unsigned>(nwork)), dim3(64 * kStateWaves), 0, s,
+                     dim3(static_cast<unsigned>(nwork)), dim3(64 * kScanWaves), 0, s,
                      map, sm, p.H, p.dv, p.nchunks, q, s0, o, s_final, buf, sb,
                      static_cast<float*>(nullptr));
   return hipGetLastError();

@@ -1227,11 +1227,12 @@ struct SegBuffers {
 // per lane) into one buffer while the waves compute from the other (bf16;
 // fp32 operands are twice the size and use one buffer).
 
-constexpr int kStateWaves = 8;  // waves per workgroup (two per SIMD)
-constexpr int kScanSlabs = 1;   // slabs per wave, scan: 8 slabs per workgroup
-constexpr int kTransSlabs = 2;  // slabs per wave, transitions: [M0 | Phi] of 128 + 128
-constexpr int kScanGroup = kStateWaves * kScanSlabs;
-constexpr int kTransGroup = kStateWaves * kTransSlabs;
+constexpr int kScanWaves = 8;   // scan: waves per workgroup (two per SIMD)
+constexpr int kScanSlabs = 1;   // scan: slabs per wave, 8 slabs per workgroup
+constexpr int kTransWaves = 8;  // transitions: waves per workgroup
+constexpr int kTransSlabs = 2;  // transitions: slabs per wave, [M0 | Phi] of 128 + 128
+constexpr int kScanGroup = kScanWaves * kScanSlabs;
+constexpr int kTransGroup = kTransWaves * kTransSlabs;
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
@@ -1251,12 +1252,14 @@ template <int NTH, int MAXB>
 __device__ __forceinline__ void lds_copy(char* dst, const char* src, int wave, int lane,
                                          int bytes = MAXB) {
   constexpr int STEP = NTH * 16;
+  // a region that is not whole 1 KiB wave pieces needs the per-lane bound
+  constexpr bool WHOLE = MAXB % 1024 == 0;
 #pragma unroll
   for (int it = 0; it < (MAXB + STEP - 1) / STEP; ++it) {
     const int b = it * STEP + wave * 1024;  // uniform
     if (MAXB % STEP == 0 || b < MAXB) {
       const uint32_t off = static_cast<uint32_t>(lane * 16);
-      if (bytes == MAXB || b + static_cast<int>(off) < bytes)
+      if ((WHOLE && bytes == MAXB) || b + static_cast<int>(off) < bytes)
         __builtin_amdgcn_global_load_lds(src + b + off, (lds_void_ptr)(dst + b), 16, 0, 0);
     }
   }
@@ -1335,6 +1338,7 @@ __device__ __forceinline__ void copy_chunk(char* lds, const FwdBuffers& buf, int
         const int b = it * NTH + wave * 64;  // uniform
         if (!((C * QP::PR) % NTH == 0 || b < C * QP::PR)) continue;
         const int i = b + lane;
+        if ((C * QP::PR) % 64 != 0 && i >= C * QP::PR) continue;  // past the rows
         const uint32_t off = full ? qp.off[it] : QP::offset(min(i / QP::PR, ci.len - 1), i, H);
         __builtin_amdgcn_global_load_lds(qb + off, (lds_void_ptr)(lds + L::oQ + b * 16),
                                          16, 0, 0);
@@ -1421,12 +1425,12 @@ __device__ __forceinline__ void chain_lds(
 // entering to the leaving state is affine, M_end = Phi M_start + M0).  The
 // last segment of a sequence needs neither.
 template <int C, int DK, typename IO, int GATE>
-__global__ __launch_bounds__(64 * kStateWaves)
+__global__ __launch_bounds__(64 * kTransWaves)
 void fwd_trans_kernel(
     ChunkMap map, SegMap sm, int H, int dv, int64_t nchunks, FwdBuffers buf,
     SegBuffers sb) {
   using OP = IO;
-  constexpr int NW = kStateWaves, SPW = kTransSlabs, NTH = 64 * NW, GS = kTransGroup;
+  constexpr int NW = kTransWaves, SPW = kTransSlabs, NTH = 64 * NW, GS = kTransGroup;
   using L = LdsChunk<C, DK, OP, false, false, GS>;
   constexpr int NKD = L::NKD, NKC = L::NKC, NDT = L::NDT;
   constexpr bool DB = opstore<OP>::bytes == 2;  // double-buffered
@@ -1577,7 +1581,7 @@ __device__ __forceinline__ opvec<OP> q_frag_raw(const char* sq, int rt, int jb, 
 // STATES = true (backward recomputation): no outputs; every chunk-start
 // state is stored in fp32 into `states` ([chunk-head][DK][dv]).
 template <int C, int DK, typename IO, int GATE, bool STATES = false>
-__global__ __launch_bounds__(64 * kStateWaves)
+__global__ __launch_bounds__(64 * kScanWaves)
 void fwd_scan_kernel(
     ChunkMap map, SegMap sm, int H, int dv, int64_t nchunks,
     const void* __restrict__ q, const float* __restrict__ s0,
@@ -1586,7 +1590,7 @@ void fwd_scan_kernel(
   using OP = IO;
   constexpr bool OUT = !STATES;
   constexpr bool RAWQ = OUT && GATE != GDN_GATE_CHANNEL;
-  constexpr int NW = kStateWaves, SPW = kScanSlabs, NTH = 64 * NW, GS = kScanGroup;
+  constexpr int NW = kScanWaves, SPW = kScanSlabs, NTH = 64 * NW, GS = kScanGroup;
   using L = LdsChunk<C, DK, OP, OUT, RAWQ, GS>;
   constexpr int NB = L::NB, NKD = L::NKD, NKC = L::NKC, NDT = L::NDT;
   constexpr bool DB = opstore<OP>::bytes == 2;  // double-buffered
