@@ -183,13 +183,20 @@ int plan_segments(const Problem& p) {
   if (set < 0 || p.nseq == 0) return 0;
   if (set > 0) return std::min(set, 1 << 20);
   // automatic: a state-pass workgroup takes one (sequence, head) and 8 value
-  // slabs and walks its chunks in order.  Split when those workgroups cannot
-  // fill the CUs twice over, into segments of ~sqrt(n / 2) chunks, which
-  // balances the two per-segment passes against the sequential combine
+  // slabs and walks its chunks in order, so with few (sequence, head) pairs
+  // most CUs idle.  Segments of L chunks give groups * n / L workgroups;
+  // take L so that they about fill the 256 CUs once, but not below
+  // ~sqrt(n / 2.56) chunks (each segment costs a step of the sequential
+  // combine and its own transition columns).  No split when the pairs alone
+  // fill the CUs or the chains are short.
+  constexpr double kCUs = 256.0;
   const int64_t groups = static_cast<int64_t>(p.nseq) * p.H * ((p.dv / 16 + 7) / 8);
   const double n = static_cast<double>(p.nchunks - (p.varlen ? p.nseq : 0)) / p.nseq;
-  if (groups >= 512 || n < 8.0) return 0;
-  return std::max(2, static_cast<int>(std::ceil(std::sqrt(n / 2.0))));
+  if (n < 8.0) return 0;
+  const int fill = static_cast<int>(std::ceil(n * static_cast<double>(groups) / kCUs));
+  const int lo = std::max(2, static_cast<int>(std::ceil(std::sqrt(n / 2.56))));
+  const int L = std::max(fill, lo);
+  return L >= n ? 0 : L;
 }
 
 int64_t seg_slots_host(const Problem& p) {

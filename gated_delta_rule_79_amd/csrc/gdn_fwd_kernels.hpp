@@ -815,6 +815,8 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
 //     diagonal on fp32 MFMA:  T_ba = -T_bb sum_{a <= j < b} A_bj T_ja;
 //   - W^T = X^T T^T and U = T Y on the matrix cores in the operand type;
 //   - decays as exp2 of base-2 cumulative log gates.
+constexpr int kPrepWaves = 8;  // waves of the per-token-gate prep
+
 template <int C, int DK, typename IO>
 struct PrepSgSmem {
   static constexpr int ib = io<IO>::bytes;
@@ -837,7 +839,7 @@ struct PrepSgSmem {
 };
 
 template <int C, int DK, typename IO, int GATE>
-__global__ __launch_bounds__(256) void fwd_prep_sg_kernel(
+__global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
@@ -883,7 +885,8 @@ __global__ __launch_bounds__(256) void fwd_prep_sg_kernel(
   constexpr int NT2 = NB * (NB + 1) / 2;
   constexpr int NPF = NB == 1 ? 1 : (NB == 2 ? 2 : 6);
   constexpr int JOBS = NT2 + NPF;
-  constexpr int MAXJ = (JOBS + 3) / 4;
+  constexpr int PW = kPrepWaves, NT = 64 * PW;
+  constexpr int MAXJ = (JOBS + PW - 1) / PW;
   auto p_job = [&](int job, int* rt, int* jb) {
     int f = job - NT2;
     for (*rt = 0; *rt < NB; ++*rt) {
@@ -895,7 +898,7 @@ __global__ __launch_bounds__(256) void fwd_prep_sg_kernel(
   opvec<OP> qpre[MAXJ][NKD];
 #pragma unroll
   for (int u = 0; u < MAXJ; ++u) {
-    const int job = wave + 4 * u;
+    const int job = wave + PW * u;
     if (job >= NT2 && job < JOBS) {
       int rt = 0, jb = 0;
       p_job(job, &rt, &jb);
@@ -909,15 +912,15 @@ __global__ __launch_bounds__(256) void fwd_prep_sg_kernel(
   //      cumulative log gate.  Every load is issued before any store.
   constexpr int KP = DK * ib / 16;             // 16-byte pieces per K row
   constexpr int VPM = S::VCOLS * ib / 16;      // pieces per staged V row
-  constexpr int NKL = (C * KP + 255) / 256;    // K pieces per thread
-  constexpr int NVL = (C * VPM + 255) / 256;   // V pieces per thread (max)
+  constexpr int NKL = (C * KP + NT - 1) / NT;   // K pieces per thread
+  constexpr int NVL = (C * VPM + NT - 1) / NT;  // V pieces per thread (max)
   auto stage_v = [&](int c0) {
     // columns [c0, c0 + VCOLS) of V; pieces past dv or the chunk are zero
     const int VP = min(S::VCOLS, dv - c0) * ib / 16;
     uint4 raw[NVL];
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + NT * u;
       const int r = e / VPM, pc = e % VPM;
       raw[u] = make_uint4(0, 0, 0, 0);
       if (e < C * VPM && r < len && pc < VP)
@@ -927,7 +930,7 @@ __global__ __launch_bounds__(256) void fwd_prep_sg_kernel(
     }
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + NT * u;
       if (e < C * VPM) *reinterpret_cast<uint4*>(sV + (e / VPM) * LDVB + (e % VPM) * 16) = raw[u];
     }
   };
@@ -935,7 +938,7 @@ __global__ __launch_bounds__(256) void fwd_prep_sg_kernel(
     uint4 raw[NKL];
 #pragma unroll
     for (int u = 0; u < NKL; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + NT * u;
       const int r = e / KP, pc = e % KP;
       raw[u] = make_uint4(0, 0, 0, 0);
       if (e < C * KP && r < len)
@@ -945,7 +948,7 @@ __global__ __launch_bounds__(256) void fwd_prep_sg_kernel(
     stage_v(0);
 #pragma unroll
     for (int u = 0; u < NKL; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + NT * u;
       if (e < C * KP) *reinterpret_cast<uint4*>(sK + (e / KP) * LDKB + (e % KP) * 16) = raw[u];
     }
   }
@@ -979,7 +982,7 @@ __global__ __launch_bounds__(256) void fwd_prep_sg_kernel(
   char* dP = buf.at(ch, buf.off_p);
 #pragma unroll
   for (int u = 0; u < MAXJ; ++u) {
-    const int job = wave + 4 * u;
+    const int job = wave + PW * u;
     if (job >= JOBS) continue;
     if (job < NT2) {
       int t = job, rt = 0;
@@ -1045,14 +1048,14 @@ __global__ __launch_bounds__(256) void fwd_prep_sg_kernel(
     }
   }
   // strictly upper blocks of T are zero; decays for the state pass
-  for (int e = tid; e < C * C; e += 256) {
+  for (int e = tid; e < C * C; e += NT) {
     const int r = e / C, i = e % C;
     if ((i >> 4) > (r >> 4)) sT[r * LDC + i] = 0.f;
   }
   {
     float* gam = reinterpret_cast<float*>(buf.at(ch, buf.off_g));
     if (tid < C) gam[tid] = GATE == GDN_GATE_SCALAR ? __builtin_amdgcn_exp2f(sg2[tid]) : 1.f;
-    for (int d = tid; d < DK; d += 256)
+    for (int d = tid; d < DK; d += NT)
       gam[C + d] = GATE == GDN_GATE_SCALAR ? __builtin_amdgcn_exp2f(sg2[C - 1]) : 1.f;
   }
   __syncthreads();
@@ -1117,54 +1120,49 @@ __global__ __launch_bounds__(256) void fwd_prep_sg_kernel(
       tf[rt][kb] = frag<OP>::from_floats(x);
     }
 
-  // ---- 5. K~^T fragments and -W fragments: wave w owns dk block w -------
-  // (token order perm_k in both, so one gather of K's columns serves both)
-  for (int jb = wave; jb < NKD; jb += 4) {
-    opvec<OP> xf[2][NKC];
+  // ---- 5. K~^T fragments and -W fragments: job (jb, half) takes key tile
+  //      a = 2 jb + half, the K~^T fragments of that tile and half of the
+  //      -W fragments of key block jb (token order perm_k in both, so one
+  //      gather of K's columns serves both)
+  for (int job = wave; job < 2 * NKD; job += PW) {
+    const int jb = job >> 1, half = job & 1, a = 2 * jb + half;
+    opvec<OP> xf[NKC];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int a = 2 * jb + half;
+    for (int kb = 0; kb < NKC; ++kb) {
+      float kt[8], xt[8];
+      const int dk = 16 * a + l16;
 #pragma unroll
-      for (int kb = 0; kb < NKC; ++kb) {
-        float kt[8], xt[8];
-        const int dk = 16 * a + l16;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int i = 32 * kb + perm_k(lg, s);
-          float x = 0.f;
-          if (16 * a < DK && i < C) x = lds_ld<IO>(sK + i * LDKB, dk);
-          kt[s] = i < C ? x * sks[i] : 0.f;
-          xt[s] = i < C ? x * sxs[i] : 0.f;
-        }
-        xf[half][kb] = frag<OP>::from_floats(xt);
-        if (16 * a < DK)
-          *reinterpret_cast<opvec<OP>*>(
-              buf.at(ch, buf.off_k) + ((size_t(a) * NKC + kb) * 64 + lane) * 8 * ob) =
-              frag<OP>::from_floats(kt);
+      for (int s = 0; s < 8; ++s) {
+        const int i = 32 * kb + perm_k(lg, s);
+        float x = 0.f;
+        if (16 * a < DK && i < C) x = lds_ld<IO>(sK + i * LDKB, dk);
+        kt[s] = i < C ? x * sks[i] : 0.f;
+        xt[s] = i < C ? x * sxs[i] : 0.f;
       }
+      xf[kb] = frag<OP>::from_floats(xt);
+      if (16 * a < DK)
+        *reinterpret_cast<opvec<OP>*>(
+            buf.at(ch, buf.off_k) + ((size_t(a) * NKC + kb) * 64 + lane) * 8 * ob) =
+            frag<OP>::from_floats(kt);
     }
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt) {
-      floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (16 * a < DK) {
 #pragma unroll
-      for (int kb = 0; kb < NKC; ++kb) {
-        if (32 * kb > 16 * rt + 15) continue;
-        acc0 = mma32(xf[0][kb], tf[rt][kb], acc0);
-        if (32 * jb + 16 < DK) acc1 = mma32(xf[1][kb], tf[rt][kb], acc1);
+        for (int kb = 0; kb < NKC; ++kb) {
+          if (32 * kb > 16 * rt + 15) continue;
+          acc = mma32(xf[kb], tf[rt][kb], acc);
+        }
       }
-      float out[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        out[e] = -acc0[e];
-        out[4 + e] = -acc1[e];
-      }
-      *reinterpret_cast<opvec<OP>*>(
-          buf.at(ch, buf.off_w) + ((size_t(rt) * NKD + jb) * 64 + lane) * 8 * ob) =
-          frag<OP>::from_floats(out);
+      // slots 4 half .. +3 of the lane's fragment (zero past DK)
+      *reinterpret_cast<typename acc4<OP>::type*>(
+          buf.at(ch, buf.off_w) + ((size_t(rt) * NKD + jb) * 64 + lane) * 8 * ob + half * 4 * ob) =
+          from_f4<OP>(-acc);
     }
   }
 
-  // ---- 6. U = T Y, Y = diag(b) V: wave w takes value tiles w, w + 4, ..
+  // ---- 6. U = T Y, Y = diag(b) V: wave w takes value tiles w, w + PW, ..
   //      of each VCOLS-column pass --------------------------------------
   for (int c0 = 0; c0 < dv; c0 += S::VCOLS) {
     if (c0 > 0) {
@@ -1174,8 +1172,9 @@ __global__ __launch_bounds__(256) void fwd_prep_sg_kernel(
     }
     char* U = buf.at(ch, buf.off_u);
     const int ndvt = dv / 16;
-    const int nvt = min(S::VCOLS, dv - c0) / 16;
-    for (int vl = wave; vl < nvt; vl += 4) {
+    // in a scalar register, so the loop below never runs under an EXEC mask
+    const int nvt = __builtin_amdgcn_readfirstlane(min(S::VCOLS, dv - c0) / 16);
+    for (int vl = wave; vl < nvt; vl += PW) {
       const int vt = c0 / 16 + vl;
       opvec<OP> yf[NKC];
       const int col = 16 * vl + l16;

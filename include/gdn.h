@@ -193,9 +193,11 @@ gdn_status gdn_profile_read(double* total_ms, int32_t* count);
  * computes every segment's affine state map in parallel, combines them in a
  * short sequential pass and then runs the segments in parallel from their
  * entering states (mathematically the same recurrence, rounded differently).
- *   n = 0  : automatic (default): split only when the (sequence, head)
- *            pairs cannot fill the GPU twice over, with segments of about
- *            sqrt(chunks / 2) chunks;
+ *   n = 0  : automatic (default): segments long enough that the segment
+ *            workgroups about fill the GPU's 256 CUs once, and at least
+ *            sqrt(chunks / 2.56) chunks; no split when the (sequence, head)
+ *            pairs already fill the CUs or a sequence has fewer than 8
+ *            chunks;
  *   n > 0  : segments of n chunks (values above 2^20 are clamped);
  *   n < 0  : never split.
  * Changes the workspace size: query gdn_chunk_fwd_workspace after setting. */

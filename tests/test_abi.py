@@ -177,20 +177,34 @@ def test_workspace_of_segmented_state_pass(lib):
         lib.gdn_set_segment_chunks(-1)
         _, offf = ws_bytes(lib, prob(T=640, io_dtype=_lib.GDN_F32))
         assert seg3f - offf == seg_bytes(4, 2, 128, 128, 4)
-        # automatic: 16 heads x 8 slabs cannot fill the GPU, 64 chunks ->
-        # segments of ceil(sqrt(32)) = 6 chunks, 11 per sequence
+        # automatic: 16 (sequence, head) workgroups of 64 chunks; filling 256
+        # CUs takes segments of 64 * 16 / 256 = 4 chunks, raised to the floor
+        # ceil(sqrt(64 / 2.56)) = 5: 13 segments per sequence
         lib.gdn_set_segment_chunks(0)
         _, auto = ws_bytes(lib, prob(T=4096, H=16))
-        assert auto - off_big == seg_bytes(11, 16, 128, 128, 2)
-        # enough (sequence, head) workgroups (32 x 16 = 512): no split
-        _, a = ws_bytes(lib, prob(B=32, T=4096, H=16))
+        assert auto - off_big == seg_bytes(13, 16, 128, 128, 2)
+        # enough (sequence, head) workgroups (16 x 16 = 256): no split
+        _, a = ws_bytes(lib, prob(B=16, T=4096, H=16))
         lib.gdn_set_segment_chunks(-1)
-        _, b = ws_bytes(lib, prob(B=32, T=4096, H=16))
+        _, b = ws_bytes(lib, prob(B=16, T=4096, H=16))
         assert a == b
-        # 8 x 16 = 128 workgroups of 64 chunks: split into 11 segments each
+        # 8 x 16 = 128 workgroups of 64 chunks: segments of 64 * 128 / 256 =
+        # 32 chunks, 2 per sequence
         lib.gdn_set_segment_chunks(0)
         _, a = ws_bytes(lib, prob(B=8, T=4096, H=16))
-        assert a - b // 4 == seg_bytes(8 * 11, 16, 128, 128, 2)
+        assert a - b // 2 == seg_bytes(8 * 2, 16, 128, 128, 2)
+        # long chains: 16 workgroups of 1024 chunks -> 64-chunk segments
+        _, a = ws_bytes(lib, prob(T=65536, H=16))
+        lib.gdn_set_segment_chunks(-1)
+        _, b = ws_bytes(lib, prob(T=65536, H=16))
+        lib.gdn_set_segment_chunks(0)
+        assert a - b == seg_bytes(16, 16, 128, 128, 2)
+        # short chains (fewer than 8 chunks) are never split
+        _, a = ws_bytes(lib, prob(T=448, H=16))
+        lib.gdn_set_segment_chunks(-1)
+        _, b = ws_bytes(lib, prob(T=448, H=16))
+        lib.gdn_set_segment_chunks(0)
+        assert a == b
         # varlen with a forced split: segment table + buffers for at most
         # nchunks / L + nseq slots
         lib.gdn_set_segment_chunks(2)
