@@ -1836,34 +1836,38 @@ __global__ __launch_bounds__(64 * ((DK + 31) / 32)) void fwd_combine_kernel(
     sMb[b][wave][lane] = pack2<OP>(M[0], NT > 1 ? M[NT - 1] : z);
   };
 
+  // The step count is padded to a multiple of D and every step fetches and
+  // stores unconditionally, so the body is straight-line code and the
+  // compiler's waits let D steps of loads stay in flight.  Padded steps
+  // re-read the last segment's map and write to the sequence's first slot,
+  // which holds no entering state (the first segment starts from s0).
+  const int npad = (nsteps + D - 1) / D * D;
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < nsteps) fetch(ah[d], d);
+  for (int d = 0; d < D; ++d) fetch(ah[d], min(d, nsteps - 1));
   publish(0);
   __syncthreads();
-  for (int j = 0; j < nsteps; j += D) {
+  for (int j = 0; j < npad; j += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int jj = j + d;
-      if (jj < nsteps) {
-        opvec<OP> Mb[NKD];
+      opvec<OP> Mb[NKD];
 #pragma unroll
-        for (int jb = 0; jb < NKD; ++jb) Mb[jb] = sMb[jj & 1][jb][lane];
+      for (int jb = 0; jb < NKD; ++jb) Mb[jb] = sMb[jj & 1][jb][lane];
 #pragma unroll
-        for (int u = 0; u < NT; ++u) {
-          floatx4 acc = ah[d].m0[u];
+      for (int u = 0; u < NT; ++u) {
+        floatx4 acc = ah[d].m0[u];
 #pragma unroll
-          for (int jb = 0; jb < NKD; ++jb) acc = mma32(ah[d].phi[u][jb], Mb[jb], acc);
-          M[u] = acc;
-        }
-        if (jj + D < nsteps) fetch(ah[d], jj + D);
-        const size_t sh = static_cast<size_t>(sb0 + jj + 1) * H + h;
-        floatx4* dst = reinterpret_cast<floatx4*>(sb.ss) + (sh * ndvt + vt) * NDT * 64;
-#pragma unroll
-        for (int u = 0; u < NT; ++u) dst[(t0 + u) * 64 + lane] = M[u];
-        publish((jj + 1) & 1);
-        __syncthreads();
+        for (int jb = 0; jb < NKD; ++jb) acc = mma32(ah[d].phi[u][jb], Mb[jb], acc);
+        M[u] = acc;
       }
+      fetch(ah[d], min(jj + D, nsteps - 1));
+      const int slot = jj < nsteps ? sb0 + jj + 1 : sb0;
+      const size_t sh = static_cast<size_t>(slot) * H + h;
+      floatx4* dst = reinterpret_cast<floatx4*>(sb.ss) + (sh * ndvt + vt) * NDT * 64;
+#pragma unroll
+      for (int u = 0; u < NT; ++u) dst[(t0 + u) * 64 + lane] = M[u];
+      publish((jj + 1) & 1);
+      __syncthreads();
     }
   }
 }
