@@ -12,6 +12,8 @@ Sources (cited by page title and section):
   * "Linear Attention Architectures: Mechanisms, Trade-offs, and Cross-Layer
     Routing" (abstract) -- names the per-channel (Kimi-Delta-style) gate
     without defining it.
+  * the GDN review's "Future work" and closing section -- name Householder-
+    product transitions (several delta steps per token) without a formula.
 
 Parity status per function is listed in ``gdn_oracle.__doc__``.
 """
@@ -25,5 +27,6 @@ from .gdn_oracle import (  # noqa: F401
     gdn_chunked_bruteforce,
     gdn_sgd_form,
     delta_rule_ungated,
+    deltaproduct_fwd,
     normwise_rel_err,
 )

@@ -29,6 +29,10 @@ Readings where the pages are silent (each is listed in the design notes):
     all-equal-channels case equals the scalar gate.
   * the backward is the gradient of <dO, o> + <dS_final, S_final> with respect
     to q, k, v, beta, log alpha and S_0 (the pages give no backward).
+  * Householder-product transitions (only named by the pages): nh delta
+    steps per token after a single decay, output after the last step (see
+    deltaproduct_fwd).  Parity with an external definition is UNPINNED; the
+    pins fix its reductions and reflection properties.
 
 Parity pins (tests/test_oracle_pins.py): chunked brute-force form, orthonormal
 retrieval, beta = 0 gate product, DeltaNet limit, norm bound, alpha -> 0
@@ -143,6 +147,52 @@ def gdn_fwd(q, k, v, beta, log_alpha, s0=None, gate: str = "scalar",
             o[b, t0:t1, h], sf[n, h] = gdn_fwd_chain(
                 q[b, t0:t1, h], k[b, t0:t1, h], v[b, t0:t1, h],
                 beta[b, t0:t1, h], la, m0, gate)
+    return o, sf
+
+
+# --------------------------------------------------------------------------
+# Householder-product transitions (several delta steps per token)
+# --------------------------------------------------------------------------
+
+def deltaproduct_fwd(q, k, v, beta, log_alpha, s0=None, gate: str = "scalar",
+                     cu_seqlens=None):
+    """Products of generalised Householder transitions per token ("Gated Delta
+    Networks: Improving Mamba2 with Delta Rule", paper review, "Future work"
+    and the closing section: Householder-product transitions can be grafted
+    onto the gated delta rule).  The pages give no formula; the reading taken
+    is the plainest one: token t carries nh (key, value, beta) triples, the
+    state is decayed once by alpha_t and then takes the nh delta-rule steps
+    in order,
+
+        M <- a_t M;   for j = 1..nh:  e = beta_tj (v_tj - M^T k_tj),
+                                      M <- M + k_tj e^T
+        o_t = M^T q_t  (after the last step),
+
+    so that S_t = S_{t-1} alpha_t H_t1 ... H_tnh + writes with
+    H_tj = I - beta_tj k_tj k_tj^T.  nh = 1 is :func:`gdn_fwd`.
+
+    Shapes: q [B,T,H,dk]; k [B,T,nh,H,dk]; v [B,T,nh,H,dv]; beta [B,T,nh,H];
+    log_alpha [B,T,H] (scalar gate) or None (gate none); s0 as in gdn_fwd;
+    cu_seqlens counts tokens.  Returns o [B,T,H,dv], s_final."""
+    assert gate in ("none", "scalar")
+    B, T, H, dk = q.shape
+    nh = k.shape[2]
+    dv = v.shape[-1]
+    nseq = B if cu_seqlens is None else len(cu_seqlens) - 1
+    o = np.zeros((B, T, H, dv))
+    sf = np.zeros((nseq, H, dk, dv))
+    for b, t0, t1, n in _segments(B, T, cu_seqlens):
+        for h in range(H):
+            M = np.zeros((dk, dv)) if s0 is None else np.array(s0[n, h], dtype=np.float64)
+            for t in range(t0, t1):
+                a = 1.0 if gate == "none" else float(np.exp(log_alpha[b, t, h]))
+                M = a * M                                   # one decay per token
+                for j in range(nh):
+                    kj = k[b, t, j, h]
+                    e = beta[b, t, j, h] * (v[b, t, j, h] - M.T @ kj)
+                    M = M + np.outer(kj, e)                 # delta step j
+                o[b, t, h] = M.T @ q[b, t, h]
+            sf[n, h] = M
     return o, sf
 
 

@@ -164,3 +164,76 @@ def p5_norm_bound(chain, dk=8, dv=6, T=40, beta_max=2.0, zero_v=False,
         worst = max(worst, np.linalg.norm(Mn) / bound)
         M = Mn
     return worst
+
+
+# ------------------------------------------------ Householder products ---
+# Checks of ``dp_fwd`` (signature of oracle.deltaproduct_fwd) for the
+# Householder-product reading: nh delta steps per token after one decay.
+
+def _dp_problem(r, T, H, nh, dk, dv):
+    q = unit(r.standard_normal((1, T, H, dk)))
+    k = unit(r.standard_normal((1, T, nh, H, dk)))
+    v = r.standard_normal((1, T, nh, H, dv))
+    beta = r.random((1, T, nh, H))
+    la = -r.random((1, T, H))
+    s0 = r.standard_normal((1, H, dk, dv))
+    return q, k, v, beta, la, s0
+
+
+def dp_single_step_is_gdn(dp_fwd, gdn_fwd, seed=7):
+    """nh = 1 is the gated delta rule itself."""
+    r = rng(seed)
+    q, k, v, beta, la, s0 = _dp_problem(r, 9, 2, 1, 6, 5)
+    o1, s1 = dp_fwd(q, k, v, beta, la, s0, "scalar")
+    o2, s2 = gdn_fwd(q, k[:, :, 0], v[:, :, 0], beta[:, :, 0], la, s0, "scalar")
+    return max(np.max(np.abs(o1 - o2)), np.max(np.abs(s1 - s2)))
+
+
+def dp_reflections(dp_fwd, seed=8):
+    """beta = 2 with unit keys and no write makes every factor a reflection:
+    the Frobenius norm of the state is preserved, and the same key twice in
+    one token cancels (H H = I).  Returns the worst deviation."""
+    r = rng(seed)
+    dk, dv, T = 5, 4, 6
+    q, k, v, beta, la, s0 = _dp_problem(r, T, 1, 3, dk, dv)
+    v[:] = 0.0
+    beta[:] = 2.0
+    _, s = dp_fwd(q, k, v, beta, None, s0, "none")
+    worst = abs(np.linalg.norm(s[0, 0]) - np.linalg.norm(s0[0, 0]))
+    k2 = np.repeat(k[:, :, :1], 2, axis=2)           # k_t1 = k_t2
+    _, s = dp_fwd(q, k2, v[:, :, :2], beta[:, :, :2], None, s0, "none")
+    return max(worst, np.max(np.abs(s - s0)))
+
+
+def dp_two_step_closed_form(dp_fwd, seed=9):
+    """One token, nh = 2, written with explicit Householder matrices:
+    M_1 = H_2 (H_1 a M_0 + b_1 k_1 v_1^T) + b_2 k_2 v_2^T, H_j = I - b_j k_j k_j^T,
+    o = M_1^T q.  Returns the worst deviation."""
+    r = rng(seed)
+    dk, dv = 4, 3
+    q, k, v, beta, la, s0 = _dp_problem(r, 1, 1, 2, dk, dv)
+    a = np.exp(la[0, 0, 0])
+    k1, k2 = k[0, 0, 0, 0], k[0, 0, 1, 0]
+    v1, v2 = v[0, 0, 0, 0], v[0, 0, 1, 0]
+    b1, b2 = beta[0, 0, 0, 0], beta[0, 0, 1, 0]
+    H1 = np.eye(dk) - b1 * np.outer(k1, k1)
+    H2 = np.eye(dk) - b2 * np.outer(k2, k2)
+    M = H2 @ (H1 @ (a * s0[0, 0]) + b1 * np.outer(k1, v1)) + b2 * np.outer(k2, v2)
+    o, s = dp_fwd(q, k, v, beta, la, s0, "scalar")
+    return max(np.max(np.abs(s[0, 0] - M)), np.max(np.abs(o[0, 0, 0] - M.T @ q[0, 0, 0])))
+
+
+def dp_gate_once_per_token(dp_fwd, gdn_fwd, seed=10):
+    """With beta = 0 on one of the two steps the token is a single gated
+    delta step: the decay is applied once, before the steps.  Returns the
+    worst deviation over both choices of the silent step."""
+    r = rng(seed)
+    q, k, v, beta, la, s0 = _dp_problem(r, 7, 2, 2, 5, 4)
+    worst = 0.0
+    for live in (0, 1):
+        b = beta.copy()
+        b[:, :, 1 - live] = 0.0
+        o1, s1 = dp_fwd(q, k, v, b, la, s0, "scalar")
+        o2, s2 = gdn_fwd(q, k[:, :, live], v[:, :, live], b[:, :, live], la, s0, "scalar")
+        worst = max(worst, np.max(np.abs(o1 - o2)), np.max(np.abs(s1 - s2)))
+    return worst

@@ -264,3 +264,21 @@ def test_p12_adjoint_checkpoint_segments():
     g2 = oracle.gdn_bwd_chain(*a, ckpt=4)
     for x, y in zip(g1, g2):
         assert np.max(np.abs(x - y)) < 1e-12
+
+
+# ------------------------------------------- Householder-product transitions ---
+
+def test_dp_single_step_is_gdn():
+    assert pins.dp_single_step_is_gdn(oracle.deltaproduct_fwd, oracle.gdn_fwd) < 1e-14
+
+
+def test_dp_reflections():
+    assert pins.dp_reflections(oracle.deltaproduct_fwd) < 1e-12
+
+
+def test_dp_two_step_closed_form():
+    assert pins.dp_two_step_closed_form(oracle.deltaproduct_fwd) < 1e-13
+
+
+def test_dp_gate_once_per_token():
+    assert pins.dp_gate_once_per_token(oracle.deltaproduct_fwd, oracle.gdn_fwd) < 1e-13

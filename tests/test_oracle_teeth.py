@@ -139,3 +139,46 @@ def test_adjoint_mutant_is_caught(name):
     mod = _mutant(*BWD_MUTANTS[name])
     gate = "channel" if "gate factor" in name else "scalar"
     assert _adjoint_err(mod, gate) > 1e-4, name
+
+
+# ------------------------------------------- Householder-product transitions ---
+
+def _dp_pins_pass(mod):
+    f = mod.deltaproduct_fwd
+    return bool(pins.dp_single_step_is_gdn(f, mod.gdn_fwd) < 1e-14
+                and pins.dp_reflections(f) < 1e-12
+                and pins.dp_two_step_closed_form(f) < 1e-13
+                and pins.dp_gate_once_per_token(f, mod.gdn_fwd) < 1e-13)
+
+
+DP_MUTANTS = {
+    "decay at every step": (
+        "                M = a * M                                   # one decay per token\n"
+        "                for j in range(nh):\n",
+        "                for j in range(nh):\n"
+        "                    M = a * M\n"),
+    "steps in reverse order": (
+        "                    kj = k[b, t, j, h]\n"
+        "                    e = beta[b, t, j, h] * (v[b, t, j, h] - M.T @ kj)\n",
+        "                    kj = k[b, t, nh - 1 - j, h]\n"
+        "                    e = beta[b, t, nh - 1 - j, h] * (v[b, t, nh - 1 - j, h] - M.T @ kj)\n"),
+    "output after the first step": (
+        "                    M = M + np.outer(kj, e)                 # delta step j\n"
+        "                o[b, t, h] = M.T @ q[b, t, h]\n",
+        "                    M = M + np.outer(kj, e)                 # delta step j\n"
+        "                    if j == 0:\n"
+        "                        o[b, t, h] = M.T @ q[b, t, h]\n"),
+    "error of the state before the decay": (
+        "                    e = beta[b, t, j, h] * (v[b, t, j, h] - M.T @ kj)\n",
+        "                    e = beta[b, t, j, h] * (v[b, t, j, h] - (M / (a if j == 0 else 1.0)).T @ kj)\n"),
+}
+
+
+def test_reference_oracle_passes_dp_pins():
+    assert _dp_pins_pass(ref_mod)
+
+
+@pytest.mark.parametrize("name", sorted(DP_MUTANTS))
+def test_dp_mutant_is_caught(name):
+    mod = _mutant(*DP_MUTANTS[name])
+    assert not _dp_pins_pass(mod), name
