@@ -104,6 +104,31 @@ def chunk_fwd(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
     return o, sf
 
 
+def chunk_fwd_product(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
+                      cu_seqlens=None, output_final_state: bool = True):
+    """Householder-product forward (gdn_chunk_fwd_product): k [B,T,nh,H,dk],
+    v [B,T,nh,H,dv], beta [B,T,nh,H], q [B,T,H,dk], log_alpha [B,T,H] or None.
+    Returns (o [B,T,H,dv], s_final or None)."""
+    lib = _lib.load()
+    _check_cu(cu_seqlens, q)
+    nh = k.shape[2]
+    H, dk, dv = q.shape[2], q.shape[3], v.shape[-1]
+    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
+    nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+    o = torch.empty(q.shape[:3] + (dv,), dtype=q.dtype, device=q.device)
+    sf = (torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+          if output_final_state else None)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.gdn_chunk_fwd_product_workspace(ctypes.byref(p), nh, ctypes.byref(need)),
+               "gdn_chunk_fwd_product_workspace")
+    ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    st = lib.gdn_chunk_fwd_product(ctypes.byref(p), nh, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                   _ptr(log_alpha), _ptr(s0), _ptr(o), _ptr(sf),
+                                   _ptr(ws), ws.numel(), _stream(q.device))
+    _lib.check(st, "gdn_chunk_fwd_product")
+    return o, sf
+
+
 class FwdPlan:
     """A forward call with its outputs and workspace allocated once.
 

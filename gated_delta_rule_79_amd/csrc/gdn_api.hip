@@ -48,8 +48,9 @@ bool dk_ok(int dk) { return dk == 16 || dk == 32 || dk == 64 || dk == 128; }
 bool dv_ok(int dv) { return dv >= 16 && dv <= 256 && dv % 16 == 0; }
 bool dtype_ok(int d) { return d == GDN_F32 || d == GDN_BF16; }
 
-// Shared checks of the chunked entry points; fills *out.
-gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out) {
+// Shared checks of the chunked entry points; fills *out.  lnh > 0: each
+// token takes 2^lnh delta steps (k, v, beta per step), out->T counts steps.
+gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out, int lnh = 0) {
   if (p == nullptr) return GDN_ERR_NULL;
   if (!dtype_ok(p->io_dtype) || !dtype_ok(p->gate_dtype)) return GDN_ERR_DTYPE;
   if (p->gate < GDN_GATE_NONE || p->gate > GDN_GATE_CHANNEL)
@@ -67,10 +68,12 @@ gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out) {
     return GDN_ERR_SHAPE;
   }
   // element counts must stay far inside int64 and the grid limits
-  const int64_t tok = static_cast<int64_t>(p->B) * p->T;
+  const int64_t tok = (static_cast<int64_t>(p->B) * p->T) << lnh;
   if (tok * p->H * 256 > (int64_t(1) << 46)) return GDN_ERR_SHAPE;
+  if ((static_cast<int64_t>(p->T) << lnh) > (int64_t(1) << 30)) return GDN_ERR_SHAPE;
   out->B = p->B;
-  out->T = p->T;
+  out->T = p->T << lnh;
+  out->lnh = lnh;
   out->H = p->H;
   out->dk = p->dk;
   out->dv = p->dv;
@@ -81,7 +84,7 @@ gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out) {
   out->io = p->io_dtype;
   out->gdt = p->gate_dtype;
   out->gate = p->gate;
-  const int64_t per_seq = (static_cast<int64_t>(p->T) + p->chunk - 1) / p->chunk;
+  const int64_t per_seq = (static_cast<int64_t>(out->T) + p->chunk - 1) / p->chunk;
   out->nchunks = out->varlen ? per_seq + p->nseq : per_seq * p->B;
   if (out->nchunks * p->H > (int64_t(1) << 31) - 1) return GDN_ERR_SHAPE;
   out->seg = gdn::plan_segments(*out);
@@ -94,14 +97,15 @@ gdn_status check_fwd_pointers(const gdn::Problem& p, const void* q,
                               const void* k, const void* v, const void* beta,
                               const void* la, const float* s0, const void* o,
                               const float* s_final) {
-  const int64_t tok = static_cast<int64_t>(p.B) * p.T * p.H;
-  GDN_TRY(need(q, tok * p.dk));
+  const int64_t tok = static_cast<int64_t>(p.B) * p.T * p.H;  // steps
+  const int64_t tq = tok >> p.lnh;                             // tokens
+  GDN_TRY(need(q, tq * p.dk));
   GDN_TRY(need(k, tok * p.dk));
   GDN_TRY(need(v, tok * p.dv));
   GDN_TRY(need(beta, tok));
-  if (p.gate != GDN_GATE_NONE) GDN_TRY(need(la, tok));
+  if (p.gate != GDN_GATE_NONE) GDN_TRY(need(la, tq));
   else GDN_TRY(opt(la));
-  GDN_TRY(need(o, tok * p.dv));
+  GDN_TRY(need(o, tq * p.dv));
   GDN_TRY(opt(s0));
   GDN_TRY(opt(s_final));
   return GDN_OK;
@@ -289,6 +293,50 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
   try {
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
+    GDN_TRY(check_fwd_pointers(pp, q, k, v, beta, log_alpha, s0, o, s_final));
+    const size_t need_ws = gdn::fwd_workspace_bytes(pp);
+    if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
+      return GDN_ERR_WORKSPACE;
+    GDN_TRY(opt(ws));
+    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o,
+                                    s_final, ws,
+                                    static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+// Householder-product transitions: nh in {1, 2, 4} delta steps per token,
+// per-token gates only.
+static gdn_status check_product(const gdn_problem* p, int32_t nh, gdn::Problem* out) {
+  if (p == nullptr) return GDN_ERR_NULL;
+  if (nh != 1 && nh != 2 && nh != 4) return GDN_ERR_UNSUPPORTED;
+  if (p->gate == GDN_GATE_CHANNEL) return GDN_ERR_UNSUPPORTED;
+  return check_chunk_problem(p, out, nh == 1 ? 0 : (nh == 2 ? 1 : 2));
+}
+
+gdn_status gdn_chunk_fwd_product_workspace(const gdn_problem* p, int32_t nh,
+                                           size_t* bytes) {
+  try {
+    if (bytes == nullptr) return GDN_ERR_NULL;
+    gdn::Problem pp;
+    GDN_TRY(check_product(p, nh, &pp));
+    *bytes = gdn::fwd_workspace_bytes(pp);
+    return GDN_OK;
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+gdn_status gdn_chunk_fwd_product(const gdn_problem* p, int32_t nh, const void* q,
+                                 const void* k, const void* v, const void* beta,
+                                 const void* log_alpha, const float* s0, void* o,
+                                 float* s_final, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  try {
+    gdn::Problem pp;
+    GDN_TRY(check_product(p, nh, &pp));
     GDN_TRY(check_fwd_pointers(pp, q, k, v, beta, log_alpha, s0, o, s_final));
     const size_t need_ws = gdn::fwd_workspace_bytes(pp);
     if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))

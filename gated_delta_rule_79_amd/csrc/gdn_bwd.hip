@@ -1107,7 +1107,7 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
                          dim3(64 * kScanWaves), 0, s, map,
                          whole, p.H, p.dv, p.nchunks, q, s0,
                          static_cast<void*>(nullptr), static_cast<float*>(nullptr),
-                         buf, SegBuffers{}, states);
+                         buf, SegBuffers{}, states, 0);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

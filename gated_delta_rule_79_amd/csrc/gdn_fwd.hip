@@ -71,10 +71,11 @@ __device__ int block_excl_scan(int x, int* s_scan, int* carry) {
 // Varlen chunk map and, for L > 0, the segment table: sequence n owns chunk
 // slots [first[n], first[n+1]) and segment slots [sfirst[n], sfirst[n+1]),
 // at least one segment even when it has no chunk.
+// cu counts tokens; with 2^lnh delta steps per token the table counts steps.
 __global__ __launch_bounds__(256) void chunk_map_kernel(
     const int32_t* __restrict__ cu, int nseq, int T, int C, int64_t nslots,
     int4* __restrict__ tab, int32_t* __restrict__ first, int L, int64_t nsegs,
-    int4* __restrict__ stab, int32_t* __restrict__ sfirst) {
+    int4* __restrict__ stab, int32_t* __restrict__ sfirst, int lnh) {
   const int tid = threadIdx.x;
   for (int64_t i = tid; i < nslots; i += 256) tab[i] = make_int4(-1, 0, 0, 0);
   if (L > 0)
@@ -87,8 +88,11 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(
     const int n = base + tid;
     int cnt = 0, st = 0, en = 0;
     if (n < nseq) {
-      st = min(max(cu[n], 0), T);
-      en = min(max(cu[n + 1], st), T);
+      const int tt = T >> lnh;  // tokens
+      st = min(max(cu[n], 0), tt);
+      en = min(max(cu[n + 1], st), tt);
+      st <<= lnh;
+      en <<= lnh;
       cnt = (en - st + C - 1) / C;
     }
     const int excl = block_excl_scan(cnt, s_scan, &s_carry[0]);
@@ -128,7 +132,7 @@ hipError_t launch_chunk_map(const Problem& p, char* map_base, hipStream_t s) {
                      p.nseq, p.T, p.chunk, p.nchunks,
                      const_cast<int4*>(m.tab), const_cast<int32_t*>(m.first),
                      p.seg, p.nsegs, const_cast<int4*>(sm.tab),
-                     const_cast<int32_t*>(sm.first));
+                     const_cast<int32_t*>(sm.first), p.lnh);
   return hipGetLastError();
 }
 
@@ -189,7 +193,7 @@ hipError_t run_fwd(const Problem& p, const void* q, const void* k,
       hipLaunchKernelGGL((fwd_prep_sg_kernel<C, DK, IO, GATE>),
                          dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(64 * kPrepWaves),
                          0, s, map, p.H, p.dv, p.nchunks, q, k, v, beta, la,
-                         p.gdt == GDN_BF16, buf);
+                         p.gdt == GDN_BF16, buf, p.lnh);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -219,7 +223,7 @@ hipError_t run_fwd(const Problem& p, const void* q, const void* k,
   hipLaunchKernelGGL((fwd_scan_kernel<C, DK, IO, GATE>),
                      dim3(static_cast<unsigned>(nwork)), dim3(64 * kScanWaves), 0, s,
                      map, sm, p.H, p.dv, p.nchunks, q, s0, o, s_final, buf, sb,
-                     static_cast<float*>(nullptr));
+                     static_cast<float*>(nullptr), p.lnh);
   return hipGetLastError();
 }
 

@@ -838,12 +838,15 @@ struct PrepSgSmem {
   static_assert(total <= 160 * 1024, "prep LDS budget");
 };
 
+// lnh > 0 (Householder products, 2^lnh delta steps per token): rows are
+// steps; q and log alpha are per token, the gate acts on a token's first
+// step and q on its last (the other steps' outputs are never stored).
 template <int C, int DK, typename IO, int GATE>
 __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
-    FwdBuffers buf) {
+    FwdBuffers buf, int lnh) {
   static_assert(GATE != GDN_GATE_CHANNEL, "per-token gates only");
   using OP = IO;
   using S = PrepSgSmem<C, DK, IO>;
@@ -895,6 +898,13 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
       f -= nj;
     }
   };
+  const int nhm = (1 << lnh) - 1;
+  // q row of step r: the token's q on its last step, zero elsewhere
+  auto q_row_frag = [&](int r, int k0) -> opvec<OP> {
+    const int64_t t = tok0 + r;
+    if (r >= len || k0 >= DK || (t & nhm) != nhm) return zero_vec<OP>();
+    return gload8<IO>(q, ((t >> lnh) * H + h) * DK + k0);
+  };
   opvec<OP> qpre[MAXJ][NKD];
 #pragma unroll
   for (int u = 0; u < MAXJ; ++u) {
@@ -904,7 +914,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
       p_job(job, &rt, &jb);
 #pragma unroll
       for (int kb = 0; kb < NKD; ++kb)
-        qpre[u][kb] = row_frag<IO, DK>(q, tok0, H, h, 16 * rt + l16, len, kb * 32 + lg * 8);
+        qpre[u][kb] = q_row_frag(16 * rt + l16, kb * 32 + lg * 8);
     }
   }
 
@@ -956,7 +966,9 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
     float x = 0.f, b = 0.f;
     if (lane < len) {
       b = load_gate(beta, (tok0 + lane) * H + h, gbf);
-      if constexpr (GATE == GDN_GATE_SCALAR) x = load_gate(la, (tok0 + lane) * H + h, gbf) * kLog2e;
+      if constexpr (GATE == GDN_GATE_SCALAR)
+        if (((tok0 + lane) & nhm) == 0)  // the decay acts on a token's first step
+          x = load_gate(la, ((tok0 + lane) >> lnh) * H + h, gbf) * kLog2e;
     }
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -1296,16 +1308,18 @@ struct QPieces {
   __device__ __forceinline__ int piece(int it, int wave, int lane) const {
     return it * NTH + wave * 64 + lane;
   }
-  __device__ __forceinline__ static uint32_t offset(int r, int i, int H) {
+  // LDS row r holds the q row of step r, the row of token r >> lnh of the
+  // chunk (chunks start on a token boundary)
+  __device__ __forceinline__ static uint32_t offset(int r, int i, int H, int lnh) {
     const int c = (i % PR) ^ (r & ((PR < 16 ? PR : 16) - 1));
-    return static_cast<uint32_t>(r) * static_cast<uint32_t>(H * DK * opstore<OP>::bytes) +
+    return static_cast<uint32_t>(r >> lnh) * static_cast<uint32_t>(H * DK * opstore<OP>::bytes) +
            static_cast<uint32_t>(c * 16);
   }
-  __device__ __forceinline__ void init(int H, int wave, int lane) {
+  __device__ __forceinline__ void init(int H, int lnh, int wave, int lane) {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int i = piece(it, wave, lane);
-      off[it] = offset(i / PR, i, H);
+      off[it] = offset(i / PR, i, H, lnh);
     }
   }
 };
@@ -1318,7 +1332,7 @@ __device__ __forceinline__ void copy_chunk(char* lds, const FwdBuffers& buf, int
                                            const ChunkInfo& ci, const void* q,
                                            const QPieces<C, DK, OP, NTH>& qp, int H,
                                            int h, int ndvt, int u0, int nu, int wave,
-                                           int lane) {
+                                           int lane, int lnh = 0) {
   constexpr bool RAWQ = OUT && GATE != GDN_GATE_CHANNEL;
   using L = LdsChunk<C, DK, OP, OUT, RAWQ, GS>;
   using QP = QPieces<C, DK, OP, NTH>;
@@ -1330,7 +1344,7 @@ __device__ __forceinline__ void copy_chunk(char* lds, const FwdBuffers& buf, int
     } else {
       // rows past the chunk repeat its last row (they only feed outputs that
       // are not stored)
-      const char* qb = static_cast<const char*>(q) + (ci.tok0 * H + h) * DK * ob;
+      const char* qb = static_cast<const char*>(q) + ((ci.tok0 >> lnh) * H + h) * DK * ob;
       const bool full = ci.len == C;
 #pragma unroll
       for (int it = 0; it < QP::NIT; ++it) {
@@ -1338,7 +1352,8 @@ __device__ __forceinline__ void copy_chunk(char* lds, const FwdBuffers& buf, int
         if (!((C * QP::PR) % NTH == 0 || b < C * QP::PR)) continue;
         const int i = b + lane;
         if ((C * QP::PR) % 64 != 0 && i >= C * QP::PR) continue;  // past the rows
-        const uint32_t off = full ? qp.off[it] : QP::offset(min(i / QP::PR, ci.len - 1), i, H);
+        const uint32_t off =
+            full ? qp.off[it] : QP::offset(min(i / QP::PR, ci.len - 1), i, H, lnh);
         __builtin_amdgcn_global_load_lds(qb + off, (lds_void_ptr)(lds + L::oQ + b * 16),
                                          16, 0, 0);
       }
@@ -1585,7 +1600,7 @@ void fwd_scan_kernel(
     ChunkMap map, SegMap sm, int H, int dv, int64_t nchunks,
     const void* __restrict__ q, const float* __restrict__ s0,
     void* __restrict__ o, float* __restrict__ s_final, FwdBuffers buf,
-    SegBuffers sb, float* __restrict__ states) {
+    SegBuffers sb, float* __restrict__ states, int lnh) {
   using OP = IO;
   constexpr bool OUT = !STATES;
   constexpr bool RAWQ = OUT && GATE != GDN_GATE_CHANNEL;
@@ -1653,16 +1668,22 @@ void fwd_scan_kernel(
   O4 Ov[SPW][NB];
   int64_t o_tok0 = 0;
   int o_len = 0;
-  // lane part of an output address: row l16 of a row tile, columns 4 lg ..
-  const uint32_t o_lane = static_cast<uint32_t>((l16 * H * dv + 16 * vt0 + 4 * lg) * sizeof(E));
+  // lane part of an output address: row l16 of a row tile, columns 4 lg ..;
+  // with 2^lnh steps per token only a token's last step is an output row,
+  // stored at the token's row
+  const int nhm = (1 << lnh) - 1;
+  const bool o_row = (l16 & nhm) == nhm;
+  const uint32_t o_lane =
+      static_cast<uint32_t>(((l16 >> lnh) * H * dv + 16 * vt0 + 4 * lg) * sizeof(E));
   auto store_out = [&]() {
     if constexpr (OUT) {
-      char* ob = static_cast<char*>(o) + (o_tok0 * H + h) * dv * static_cast<int64_t>(sizeof(E));
+      char* ob = static_cast<char*>(o) +
+                 ((o_tok0 >> lnh) * H + h) * dv * static_cast<int64_t>(sizeof(E));
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
         const int r = 16 * rt + l16;
-        if (r >= o_len) continue;
-        char* dst = ob + static_cast<int64_t>(16 * rt) * H * dv * sizeof(E) + o_lane;
+        if (r >= o_len || !o_row) continue;
+        char* dst = ob + static_cast<int64_t>((16 * rt) >> lnh) * H * dv * sizeof(E) + o_lane;
 #pragma unroll
         for (int s = 0; s < SPW; ++s)
           if (own[s]) *reinterpret_cast<O4*>(dst + 16 * s * sizeof(E)) = Ov[s][rt];
@@ -1671,11 +1692,11 @@ void fwd_scan_kernel(
   };
 
   QPieces<C, DK, OP, NTH> qp;
-  if constexpr (RAWQ) qp.init(H, wave, lane);
+  if constexpr (RAWQ) qp.init(H, lnh, wave, lane);
   auto copy = [&](char* lds, int j) {
     const ChunkInfo ci = OUT ? chunk_info(map, si.c0 + j) : ChunkInfo{};
     copy_chunk<C, DK, OP, GATE, OUT, NTH, GS>(lds, buf, ch0 + j, ci, q, qp, H, h, ndvt, g0,
-                                              nu, wave, lane);
+                                              nu, wave, lane, lnh);
   };
   auto step = [&](const char* ops, int j) {
     if constexpr (STATES) {

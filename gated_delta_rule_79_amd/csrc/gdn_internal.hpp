@@ -18,6 +18,9 @@ struct Problem {
   int io;                     // gdn_dtype
   int gdt;                    // gdn_dtype of beta / log_alpha
   int gate;                   // gdn_gate
+  int lnh;                    // log2 of the delta steps per token (Householder
+                              // products); T counts steps, q / o / log alpha
+                              // / cu_seqlens count tokens.  0 otherwise.
   // derived
   int64_t nchunks;            // chunk slots per head (upper bound in varlen)
   int seg;                    // chunks per segment of the forward state pass

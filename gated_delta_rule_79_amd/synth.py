@@ -26,7 +26,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Inputs", "make_inputs", "varlen_lengths", "WORKLOADS", "workload"]
+__all__ = ["Inputs", "make_inputs", "make_product_inputs", "varlen_lengths",
+           "WORKLOADS", "workload"]
 
 
 @dataclass
@@ -141,6 +142,47 @@ def make_inputs(B: int, T: int, H: int, dk: int, dv: int, *,
         t = getattr(inp, name)
         f[name] = None if t is None else t.double().numpy()
     inp.f64 = f
+    return inp
+
+
+def make_product_inputs(B: int, T: int, H: int, dk: int, dv: int, nh: int, *,
+                        dtype: torch.dtype = torch.bfloat16,
+                        gate: str = "scalar",
+                        chunk: int = 64,
+                        seed: int = 0,
+                        s0_std: Optional[float] = None,
+                        lengths=None) -> Inputs:
+    """Draw one problem with nh (key, value, beta) triples per token, the
+    inputs of the Householder-product forward: k [B,T,nh,H,dk],
+    v [B,T,nh,H,dv], beta [B,T,nh,H]; q [B,T,H,dk] and log alpha [B,T,H]
+    per token.  Same distributions as make_inputs."""
+    assert gate in ("none", "scalar")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cu = None
+    nseq = B
+    if lengths is not None:
+        assert B == 1
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        T = int(cu[-1])
+        nseq = len(lengths)
+    q = _l2norm(rng.standard_normal((B, T, H, dk)))
+    k = _l2norm(rng.standard_normal((B, T, nh, H, dk)))
+    v = rng.standard_normal((B, T, nh, H, dv))
+    beta = _sigmoid(rng.standard_normal((B, T, nh, H)))
+    la = -_softplus(rng.standard_normal((B, T, H)) - 2.0)
+    s0 = None
+    if s0_std is not None:
+        s0 = rng.standard_normal((nseq, H, dk, dv)) * s0_std
+    inp = Inputs(
+        q=_round(q, dtype), k=_round(k, dtype), v=_round(v, dtype),
+        beta=_round(beta, dtype),
+        log_alpha=None if gate == "none" else _round(la, dtype),
+        s0=None if s0 is None else _round(s0, torch.float32),
+        do=None, cu_seqlens=None if cu is None else torch.from_numpy(cu),
+        ds_final=None, gate=gate, chunk=chunk, seed=seed)
+    inp.f64 = {name: (None if getattr(inp, name) is None
+                      else getattr(inp, name).double().numpy())
+               for name in ("q", "k", "v", "beta", "log_alpha", "s0")}
     return inp
 
 

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
   GDN_OK = 0,
@@ -132,6 +132,31 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
                          const void* log_alpha, const float* s0, void* o,
                          float* s_final, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* Householder-product transitions (the GDN review's "Future work" and its
+ * closing section name products of Householder matrices as a way to graft
+ * stronger state tracking onto the gated delta rule).  Each token carries
+ * nh (key, value, beta) triples; the state is decayed once by the token's
+ * alpha and then takes the nh delta-rule steps in order, and the output is
+ * read after the last step:
+ *   S_t = S_{t-1} alpha_t H_t1 ... H_tnh + writes,  H_tj = I - beta_tj k_tj k_tj^T.
+ * The chunked forward runs over the nh * T steps (chunk counts steps).
+ *   nh        : 1, 2 or 4 (1 is gdn_chunk_fwd itself).
+ *   k, v      : [B, T, nh, H, dk] and [B, T, nh, H, dv] in io_dtype.
+ *   beta      : [B, T, nh, H] in gate_dtype.
+ *   q         : [B, T, H, dk]; log_alpha [B, T, H] (scalar gate) or NULL
+ *               (gate none); the per-channel gate is GDN_ERR_UNSUPPORTED.
+ *   o         : [B, T, H, dv]; s0 / s_final as in gdn_chunk_fwd.
+ *   p->T and cu_seqlens count tokens, not steps.
+ * Errors: GDN_ERR_UNSUPPORTED for another nh or the per-channel gate, the
+ * rest as gdn_chunk_fwd. */
+gdn_status gdn_chunk_fwd_product_workspace(const gdn_problem* p, int32_t nh,
+                                           size_t* bytes);
+gdn_status gdn_chunk_fwd_product(const gdn_problem* p, int32_t nh, const void* q,
+                                 const void* k, const void* v, const void* beta,
+                                 const void* log_alpha, const float* s0, void* o,
+                                 float* s_final, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* Workspace bytes gdn_chunk_bwd needs (see gdn_chunk_fwd_workspace). */
 gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes);

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
     for s in range(8):
         txt = lib.gdn_status_str(s).decode()
         assert txt.startswith("GDN_")
@@ -251,3 +251,27 @@ def test_bwd_validation(lib):
 def test_python_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         _lib.load(str(tmp_path / "missing.so"))
+
+
+def test_product_workspace_and_rejections(lib):
+    """Householder-product forward: nh steps per token run as nh * T steps,
+    so its workspace is the forward's for nh * T; other nh and the
+    per-channel gate are rejected before any launch."""
+    n = ctypes.c_size_t(0)
+    for nh in (1, 2, 4):
+        st = lib.gdn_chunk_fwd_product_workspace(ctypes.byref(prob(T=100)), nh,
+                                                 ctypes.byref(n))
+        assert st == _lib.GDN_OK
+        st2, ref = ws_bytes(lib, prob(T=100 * nh))
+        assert st2 == _lib.GDN_OK and n.value == ref
+    for nh in (0, 3, 8, -1):
+        assert lib.gdn_chunk_fwd_product_workspace(
+            ctypes.byref(prob(T=100)), nh, ctypes.byref(n)) == _lib.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_chunk_fwd_product_workspace(
+        ctypes.byref(prob(T=100, gate=_lib.GDN_GATE_CHANNEL)), 2,
+        ctypes.byref(n)) == _lib.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_chunk_fwd_product_workspace(None, 2, ctypes.byref(n)) == _lib.GDN_ERR_NULL
+    # null pointers are rejected before any launch
+    st = lib.gdn_chunk_fwd_product(ctypes.byref(prob(T=100)), 2, None, A, A, A, A,
+                                   None, A, None, A, 1 << 30, None)
+    assert st == _lib.GDN_ERR_NULL
