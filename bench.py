@@ -200,6 +200,95 @@ def stage_pass(fn, steps):
     return {k: v[0] / v[1] for k, v in st.items()}
 
 
+def product_algorithmic(B, T, H, dk, dv, C, nh, s_io):
+    """Householder-product forward: nh steps per token.  Flops: per step the
+    state products (4 dk dv) and the intra-chunk terms of the forward count,
+    per token the output read 2 dk dv; bytes: q, o per token, k, v, beta
+    per step, the gate per token and the fp32 final state."""
+    th, sh = B * T * H, B * T * nh * H
+    flops = sh * (4 * dk * dv + C * (3 * dk + 2 * dv) + C * C / 3.0) + th * 2 * dk * dv
+    byts = (th * (dk + dv) * s_io + sh * (dk + dv) * s_io + sh * s_io + th * s_io
+            + B * H * dk * dv * 4)
+    return flops, byts
+
+
+def cpu_baseline_product(inp, budget_s):
+    """The fp64 oracle of the Householder-product forward on whole sequences
+    of the workload (all heads of a sequence per call) until about
+    ``budget_s`` seconds; one BLAS thread.  Scaled to the workload's tokens."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    f = inp.f64
+    B, T, H = f["q"].shape[:3]
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for h in range(H):
+            sl = slice(h, h + 1)
+            la = None if f["log_alpha"] is None else f["log_alpha"][:1, :, sl]
+            oracle.deltaproduct_fwd(f["q"][:1, :, sl], f["k"][:1, :, :, sl], f["v"][:1, :, :, sl],
+                                    f["beta"][:1, :, :, sl], la, None, inp.gate)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    frac = done / float(B * H)
+    return {"value": B * T * frac / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {B * H} (sequence, head) chains of T={T} tokens with "
+                      f"{inp.k.shape[2]} steps each ({dt:.1f} s, 1 thread); tokens/s scaled "
+                      "to the whole workload"}
+
+
+def main_product(args):
+    """Householder-product forward (gdn_chunk_fwd_product) on B1 T4096 H16
+    d128 bf16 with nh steps per token."""
+    import torch
+    import gated_delta_rule_79_amd as gdn
+    from gated_delta_rule_79_amd import synth
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    B, T, H, dk, dv, C, nh = 1, 4096, 16, 128, 128, 64, args.nh
+    wl = f"product_t{T}_h{H}_nh{nh}"
+    inp = synth.make_product_inputs(B, T, H, dk, dv, nh, dtype=torch.bfloat16,
+                                    gate="scalar", chunk=C, seed=1006)
+    d = inp.to("cuda")
+    fn = lambda: gdn.chunk_fwd_product(d.q, d.k, d.v, d.beta, d.log_alpha, None, chunk=C)
+    ms, cold = time_calls(fn, args.steps, args.warmup, args.cold_steps)
+    per = stage_pass(fn, args.steps)
+    flops, byts = product_algorithmic(B, T, H, dk, dv, C, nh, 2)
+    dom = max(per, key=per.get)
+    kernel = {"fwd_prep": "fwd_prep_sg_kernel", "fwd_scan": "fwd_scan_kernel",
+              "fwd_trans": "fwd_trans_kernel", "fwd_combine": "fwd_combine_kernel",
+              "chunk_map": "chunk_map_kernel"}.get(dom, dom)
+    out = {
+        "metric": f"tokens/sec gdn_chunk_fwd_product (T={T},H={H},d={dk},nh={nh} bf16); "
+                  "% HBM roofline",
+        "value": round(B * T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "cold_ms_per_step": None if cold is None else round(cold, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": C,
+                   "nh": nh, "gate": "scalar", "state": "fp32", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm",
+                     "achieved": round(byts / (per[dom] * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(byts / (per[dom] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": kernel,
+                     "kernel_ms": {k: round(v, 5) for k, v in per.items()},
+                     "alg_bytes_per_launch": int(byts), "alg_flops_per_launch": int(flops),
+                     "path_frac_hbm": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "path_frac_mfma_bf16": round(flops / (ms * 1e-3) / 1e12 /
+                                                  MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+    cpu = None if args.no_cpu_baseline else cpu_baseline_product(inp, args.cpu_budget)
+    if cpu is not None:
+        cpu["value"] = round(cpu["value"], 1)
+    out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
 def main_other(args):
     """bwd, fwdbwd and decode modes."""
     import torch
@@ -345,7 +434,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None,
                     help="synthetic workload (default: fwd_t4096_h16 for the forward)")
-    ap.add_argument("--mode", default="fwd", choices=("fwd", "bwd", "fwdbwd", "decode"))
+    ap.add_argument("--mode", default="fwd",
+                    choices=("fwd", "bwd", "fwdbwd", "decode", "product"))
+    ap.add_argument("--nh", type=int, default=2,
+                    help="delta steps per token for --mode product")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20,
@@ -362,6 +454,9 @@ def main():
               "the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.mode == "product":
+        main_product(args)
+        return
     if args.mode != "fwd":
         main_other(args)
         return
