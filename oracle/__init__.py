@@ -28,5 +28,7 @@ from .gdn_oracle import (  # noqa: F401
     gdn_sgd_form,
     delta_rule_ungated,
     deltaproduct_fwd,
+    gdn_fwd_qknorm,
+    l2_normalize,
     normwise_rel_err,
 )

@@ -151,6 +151,28 @@ def gdn_fwd(q, k, v, beta, log_alpha, s0=None, gate: str = "scalar",
 
 
 # --------------------------------------------------------------------------
+# L2-normalised q and k ("Method": the block normalises q and k)
+# --------------------------------------------------------------------------
+
+def l2_normalize(x):
+    """x / ||x|| over the last axis, each (token, head) row separately; an
+    all-zero row stays zero."""
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+
+def gdn_fwd_qknorm(q, k, v, beta, log_alpha, s0=None, gate: str = "scalar",
+                   cu_seqlens=None):
+    """The forward with q and k L2-normalised per (token, head) first ("Gated
+    Delta Networks: Improving Mamba2 with Delta Rule", "Method": in the block
+    design q and k go through an L2 normalisation for training stability,
+    v does not).  Same shapes and returns as :func:`gdn_fwd`."""
+    return gdn_fwd(l2_normalize(q), l2_normalize(k), v, beta, log_alpha, s0,
+                   gate, cu_seqlens=cu_seqlens)
+
+
+# --------------------------------------------------------------------------
 # Householder-product transitions (several delta steps per token)
 # --------------------------------------------------------------------------
 

@@ -282,3 +282,32 @@ def test_dp_two_step_closed_form():
 
 def test_dp_gate_once_per_token():
     assert pins.dp_gate_once_per_token(oracle.deltaproduct_fwd, oracle.gdn_fwd) < 1e-13
+
+
+# ------------------------------------------------ normalised q and k ---
+
+def test_l2_normalize_rows_are_unit_and_parallel():
+    r = pins.rng(21)
+    x = r.standard_normal((3, 5, 2, 7)) * r.random((3, 5, 2, 1)) * 10
+    y = oracle.l2_normalize(x)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), 1.0, atol=1e-15)
+    # y is a positive multiple of x: cosine 1 row by row
+    cos = np.sum(x * y, axis=-1) / np.linalg.norm(x, axis=-1)
+    np.testing.assert_allclose(cos, 1.0, atol=1e-15)
+    z = np.zeros((2, 3))
+    assert np.all(oracle.l2_normalize(z) == 0)
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_qknorm_is_scale_invariant(gate):
+    """Positive per-row scales of q and k do not change the outputs, and
+    already-unit rows give the plain forward."""
+    r = pins.rng(22)
+    q, k, v, beta, la, m0 = _rand_problem(r, 1, 9, 2, 6, 4, gate)
+    o1, s1 = oracle.gdn_fwd(q, k, v, beta, la, m0, gate)
+    o2, s2 = oracle.gdn_fwd_qknorm(q, k, v, beta, la, m0, gate)
+    sq = np.exp(r.standard_normal(q.shape[:-1] + (1,)))
+    sk = np.exp(r.standard_normal(k.shape[:-1] + (1,)))
+    o3, s3 = oracle.gdn_fwd_qknorm(q * sq, k * sk, v, beta, la, m0, gate)
+    for a, b in ((o1, o2), (s1, s2), (o1, o3), (s1, s3)):
+        assert np.max(np.abs(a - b)) < 1e-12
