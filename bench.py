@@ -14,6 +14,9 @@ Other entry points (same JSON shape, their own metric string):
     --mode bwd      gdn_chunk_bwd alone      (default workload varlen_16k_dv256)
     --mode fwdbwd   forward + backward       (tokens / (t_fwd + t_bwd))
     --mode decode   gdn_decode_step in place (default workload decode_n256_h32)
+    --mode product  gdn_chunk_fwd_product (Householder products, --nh steps)
+    --qk-l2norm     (forward) gdn_chunk_fwd_qknorm on q, k rows that are not
+                    unit vectors (log-uniform row scales in [0.05, 20])
 
 Algorithmic work per (token, head), chunk C:
     flops = 6 dk dv + C (3 dk + 2 dv) + C^2 / 3
@@ -396,10 +399,11 @@ def copy_calibration():
     del src, dst
 
 
-def cpu_baseline(inp, budget_s):
+def cpu_baseline(inp, budget_s, qknorm=False):
     """The fp64 oracle, as it stands, on whole (sequence, head) chains of the
     same workload until about ``budget_s`` seconds of work; BLAS held to one
-    thread.  Rate is scaled to the whole workload's tokens."""
+    thread.  Rate is scaled to the whole workload's tokens.  qknorm: q and k
+    rows go through the oracle's L2 normalisation first (timed)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     import oracle
@@ -412,8 +416,11 @@ def cpu_baseline(inp, budget_s):
             for h in range(H):
                 la = None if f["log_alpha"] is None else f["log_alpha"][b, :, h]
                 m0 = np.zeros((f["q"].shape[3], f["v"].shape[3]))
-                oracle.gdn_fwd_chain(f["q"][b, :, h], f["k"][b, :, h], f["v"][b, :, h],
-                                     f["beta"][b, :, h], la, m0, inp.gate)
+                qc, kc = f["q"][b, :, h], f["k"][b, :, h]
+                if qknorm:
+                    qc, kc = oracle.l2_normalize(qc), oracle.l2_normalize(kc)
+                oracle.gdn_fwd_chain(qc, kc, f["v"][b, :, h], f["beta"][b, :, h], la, m0,
+                                     inp.gate)
                 done += 1
                 if time.perf_counter() - t0 > budget_s:
                     break
@@ -438,6 +445,8 @@ def main():
                     choices=("fwd", "bwd", "fwdbwd", "decode", "product"))
     ap.add_argument("--nh", type=int, default=2,
                     help="delta steps per token for --mode product")
+    ap.add_argument("--qk-l2norm", action="store_true",
+                    help="forward with q and k L2-normalised inside the kernels")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20,
@@ -470,14 +479,15 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    inp = synth.workload(args.workload)
+    qkn = args.qk_l2norm
+    inp = synth.workload(args.workload, **({"raw_qk": (0.05, 20.0, 0.0)} if qkn else {}))
     d = inp.to("cuda")
     B, T, H, dk = inp.q.shape
     dv = inp.v.shape[-1]
     C = inp.chunk
     nseq = B if inp.cu_seqlens is None else inp.cu_seqlens.numel() - 1
     plan = gdn.FwdPlan(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, chunk=C,
-                       cu_seqlens=d.cu_seqlens)
+                       cu_seqlens=d.cu_seqlens, qk_l2norm=qkn)
 
     for _ in range(args.warmup):
         plan.run()
@@ -539,7 +549,7 @@ def main():
              "chunk_map": "chunk_map_kernel"}[dom]
     achieved = byts / (dom_ms * 1e-3) / 1e9
     src_hash = source_hash(FWD_SOURCES)
-    traffic = measured_traffic(args.workload, kname, src_hash)
+    traffic = None if qkn else measured_traffic(args.workload, kname, src_hash)
     path_ms = sum(per_kernel.values())
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -555,11 +565,13 @@ def main():
     }
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_budget)
+        cpu = cpu_baseline(inp, args.cpu_budget, qknorm=qkn)
         cpu["value"] = round(cpu["value"], 1)
 
     out = {
-        "metric": "tokens/sec gdn_chunk_fwd (T=4096,H=16,d=128 bf16); % MFMA/HBM roofline",
+        "metric": ("tokens/sec gdn_chunk_fwd_qknorm (T=4096,H=16,d=128 bf16); % HBM roofline"
+                   if qkn else
+                   "tokens/sec gdn_chunk_fwd (T=4096,H=16,d=128 bf16); % MFMA/HBM roofline"),
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -571,7 +583,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if s_io == 2 else "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "T": T, "H": H, "dk": dk,
+        "config": {"workload": args.workload + ("_qknorm" if qkn else ""), "B": B, "T": T,
+                   "H": H, "dk": dk,
                    "dv": dv, "chunk": C, "gate": inp.gate, "seed": inp.seed,
                    "state": "fp32", "parallelism": "single GPU"},
         "cold_ms_per_step": None if cold_ms is None else round(cold_ms, 5),

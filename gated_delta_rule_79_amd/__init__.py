@@ -81,8 +81,9 @@ def _check_cu(cu_seqlens, q):
 
 def chunk_fwd(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
               cu_seqlens=None, output_final_state: bool = True,
-              workspace: Optional[torch.Tensor] = None):
-    """Chunkwise forward.  Returns (o, s_final or None)."""
+              workspace: Optional[torch.Tensor] = None, qk_l2norm: bool = False):
+    """Chunkwise forward.  Returns (o, s_final or None).  qk_l2norm: q and k
+    rows are L2-normalised inside the kernels (gdn_chunk_fwd_qknorm)."""
     lib = _lib.load()
     _check_cu(cu_seqlens, q)
     p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
@@ -97,10 +98,12 @@ def chunk_fwd(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
     ws = workspace
     if ws is None or ws.numel() < need.value:
         ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
-    st = lib.gdn_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
-                           _ptr(log_alpha), _ptr(s0), _ptr(o), _ptr(sf),
-                           _ptr(ws), ws.numel(), _stream(q.device))
-    _lib.check(st, "gdn_chunk_fwd")
+    fn, name = ((lib.gdn_chunk_fwd_qknorm, "gdn_chunk_fwd_qknorm") if qk_l2norm
+                else (lib.gdn_chunk_fwd, "gdn_chunk_fwd"))
+    st = fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+            _ptr(log_alpha), _ptr(s0), _ptr(o), _ptr(sf),
+            _ptr(ws), ws.numel(), _stream(q.device))
+    _lib.check(st, name)
     return o, sf
 
 
@@ -138,7 +141,8 @@ class FwdPlan:
     This keeps the host cost of a call to one ctypes call."""
 
     def __init__(self, q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
-                 cu_seqlens=None, output_final_state: bool = True):
+                 cu_seqlens=None, output_final_state: bool = True,
+                 qk_l2norm: bool = False):
         lib = _lib.load()
         _check_cu(cu_seqlens, q)
         self._keep = (q, k, v, beta, log_alpha, s0, cu_seqlens)
@@ -154,7 +158,8 @@ class FwdPlan:
                    "gdn_chunk_fwd_workspace")
         self.workspace = torch.empty(max(need.value, 1), dtype=torch.uint8,
                                      device=q.device)
-        self._fn = lib.gdn_chunk_fwd
+        self._name = "gdn_chunk_fwd_qknorm" if qk_l2norm else "gdn_chunk_fwd"
+        self._fn = getattr(lib, self._name)
         self._args = (ctypes.byref(self.problem), _ptr(q), _ptr(k), _ptr(v),
                       _ptr(beta), _ptr(log_alpha), _ptr(s0), _ptr(self.o),
                       _ptr(self.s_final), _ptr(self.workspace),
@@ -163,7 +168,7 @@ class FwdPlan:
     def run(self):
         st = self._fn(*self._args)
         if st != _lib.GDN_OK:
-            _lib.check(st, "gdn_chunk_fwd")
+            _lib.check(st, self._name)
         return self.o, self.s_final
 
 

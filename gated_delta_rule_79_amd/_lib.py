@@ -23,6 +23,7 @@ EXPORTED = (
     "gdn_decode_step", "gdn_test_set_fail_launch", "gdn_profile_enable",
     "gdn_profile_read", "gdn_set_segment_chunks",
     "gdn_chunk_fwd_product_workspace", "gdn_chunk_fwd_product",
+    "gdn_chunk_fwd_qknorm",
 )
 STAGE_COUNT = 10
 STAGES = ("chunk_map", "fwd_prep", "fwd_scan", "decode", "bwd_states",
@@ -89,6 +90,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_chunk_fwd_product_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
     lib.gdn_chunk_fwd_product.restype = i32
     lib.gdn_chunk_fwd_product.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_chunk_fwd_qknorm.restype = i32
+    lib.gdn_chunk_fwd_qknorm.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     if path is None:
         _LIB = lib
     return lib

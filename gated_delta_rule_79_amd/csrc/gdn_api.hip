@@ -74,6 +74,7 @@ gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out, int lnh 
   out->B = p->B;
   out->T = p->T << lnh;
   out->lnh = lnh;
+  out->qknorm = false;
   out->H = p->H;
   out->dk = p->dk;
   out->dv = p->dv;
@@ -299,6 +300,32 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
       return GDN_ERR_WORKSPACE;
     GDN_TRY(opt(ws));
     if (g_fail_launch.load()) return GDN_ERR_HIP;
+    return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o,
+                                    s_final, ws,
+                                    static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+// q and k rows L2-normalised inside the forward; per-token gates only.
+gdn_status gdn_chunk_fwd_qknorm(const gdn_problem* p, const void* q, const void* k,
+                                const void* v, const void* beta,
+                                const void* log_alpha, const float* s0, void* o,
+                                float* s_final, void* ws, size_t ws_bytes,
+                                void* stream) {
+  try {
+    if (p == nullptr) return GDN_ERR_NULL;
+    if (p->gate == GDN_GATE_CHANNEL) return GDN_ERR_UNSUPPORTED;
+    gdn::Problem pp;
+    GDN_TRY(check_chunk_problem(p, &pp));
+    GDN_TRY(check_fwd_pointers(pp, q, k, v, beta, log_alpha, s0, o, s_final));
+    const size_t need_ws = gdn::fwd_workspace_bytes(pp);
+    if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
+      return GDN_ERR_WORKSPACE;
+    GDN_TRY(opt(ws));
+    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    pp.qknorm = true;
     return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o,
                                     s_final, ws,
                                     static_cast<hipStream_t>(stream)));

@@ -125,6 +125,25 @@ __device__ inline void unpack16(const uint4& raw, float* x) {
   }
 }
 
+// Encode floats as 16 bytes of the input dtype (8 bf16, rounded to nearest
+// even, or 4 fp32); the inverse of unpack16.
+template <typename IO>
+__device__ inline uint4 pack16(const float* x) {
+  if constexpr (io<IO>::bytes == 2) {
+    uint32_t w[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[2 * s]));
+      const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[2 * s + 1]));
+      w[s] = lo | (hi << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                      __float_as_uint(x[3]));
+  }
+}
+
 template <typename IO>
 __device__ inline void lds_st(char* base, size_t idx, float x) {
   if constexpr (io<IO>::bytes == 2)
@@ -834,19 +853,25 @@ struct PrepSgSmem {
   static constexpr size_t g_off = beta_off + size_t(C) * 4;
   static constexpr size_t xs_off = g_off + size_t(C) * 4;
   static constexpr size_t ks_off = xs_off + size_t(C) * 4;
-  static constexpr size_t total = ks_off + size_t(C) * 4;
+  static constexpr size_t qn_off = ks_off + size_t(C) * 4;   // 1 / |q_r|
+  static constexpr size_t total = qn_off + size_t(C) * 4;
   static_assert(total <= 160 * 1024, "prep LDS budget");
 };
 
 // lnh > 0 (Householder products, 2^lnh delta steps per token): rows are
 // steps; q and log alpha are per token, the gate acts on a token's first
 // step and q on its last (the other steps' outputs are never stored).
+// qkn: q and k rows are used divided by their L2 norms (an all-zero row stays
+// zero).  K rows are normalised as they enter LDS (then rounded to the input
+// dtype); q rows keep their values and the factor 1 / |q_r| goes to the P
+// rows (in fp32, after the product) and into gamma_r for the scan, whose
+// state term multiplies the raw q product by gamma_r.
 template <int C, int DK, typename IO, int GATE>
 __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
-    FwdBuffers buf, int lnh) {
+    FwdBuffers buf, int lnh, bool qkn) {
   static_assert(GATE != GDN_GATE_CHANNEL, "per-token gates only");
   using OP = IO;
   using S = PrepSgSmem<C, DK, IO>;
@@ -867,6 +892,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
   float* sg2 = reinterpret_cast<float*>(smem + S::g_off);
   float* sxs = reinterpret_cast<float*>(smem + S::xs_off);
   float* sks = reinterpret_cast<float*>(smem + S::ks_off);
+  float* sqn = reinterpret_cast<float*>(smem + S::qn_off);
 
   const int L = blockIdx.x;
   const int c = static_cast<int>(L / H);
@@ -956,10 +982,51 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
             static_cast<const char*>(k) + ((tok0 + r) * H + h) * DK * ib + pc * 16);
     }
     stage_v(0);
+    if (qkn) {
+      // the KP pieces of a row sit in KP aligned consecutive lanes
+      static_assert(KP <= 64 && (KP & (KP - 1)) == 0, "K row pieces per wave");
+#pragma unroll
+      for (int u = 0; u < NKL; ++u) {
+        float x[16 / ib];
+        unpack16<IO>(raw[u], x);
+        float ss = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < 16 / ib; ++s2) ss += x[s2] * x[s2];
+#pragma unroll
+        for (int m = 1; m < KP; m <<= 1) ss += __shfl_xor(ss, m, 64);
+        const float sc = ss > 0.f ? rsqrtf(ss) : 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < 16 / ib; ++s2) x[s2] *= sc;
+        raw[u] = pack16<IO>(x);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < NKL; ++u) {
       const int e = tid + NT * u;
       if (e < C * KP) *reinterpret_cast<uint4*>(sK + (e / KP) * LDKB + (e % KP) * 16) = raw[u];
+    }
+  }
+  if (qkn) {
+    // 1 / |q_r| of every row from the P jobs' q rows (row tile rt has the
+    // job jb = 0); a row's lanes l16, l16 + 16, .. hold its 32-slot pieces
+#pragma unroll
+    for (int u = 0; u < MAXJ; ++u) {
+      const int job = wave + PW * u;
+      if (job < NT2 || job >= JOBS) continue;
+      int rt = 0, jb = 0;
+      p_job(job, &rt, &jb);
+      if (jb != 0) continue;
+      float ss = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb) {
+        float x[8];
+        to_floats<OP>(qpre[u][kb], x);
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) ss += x[s2] * x[s2];
+      }
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      if (lg == 0) sqn[16 * rt + l16] = ss > 0.f ? rsqrtf(ss) : 0.f;
     }
   }
   if (wave == 0) {
@@ -1030,6 +1097,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
       p_job(job, &rt, &jb);
       const int r = 16 * rt + l16;
       const float grr = sg2[r];
+      const float qs = qkn ? sqn[r] : 1.f;
       float out[8];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -1050,7 +1118,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * it + 4 * lg + e;
-          float val = acc[e];
+          float val = acc[e] * qs;
           if constexpr (GATE == GDN_GATE_SCALAR) val *= __builtin_amdgcn_exp2f(grr - gi4[e]);
           out[4 * half + e] = (it <= rt && it < NB && i <= r) ? val : 0.f;
         }
@@ -1066,7 +1134,9 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
   }
   {
     float* gam = reinterpret_cast<float*>(buf.at(ch, buf.off_g));
-    if (tid < C) gam[tid] = GATE == GDN_GATE_SCALAR ? __builtin_amdgcn_exp2f(sg2[tid]) : 1.f;
+    if (tid < C)
+      gam[tid] = (GATE == GDN_GATE_SCALAR ? __builtin_amdgcn_exp2f(sg2[tid]) : 1.f) *
+                 (qkn ? sqn[tid] : 1.f);
     for (int d = tid; d < DK; d += NT)
       gam[C + d] = GATE == GDN_GATE_SCALAR ? __builtin_amdgcn_exp2f(sg2[C - 1]) : 1.f;
   }
@@ -1730,13 +1800,14 @@ void fwd_scan_kernel(
 #pragma unroll
         for (int jb = 0; jb < NKC; ++jb)
           if (32 * jb <= 16 * rt + 15) pf[jb] = sP[(rt * NKC + jb) * 64 + lane];
-        const float gr = GATE == GDN_GATE_SCALAR ? sg[16 * rt + l16] : 1.f;
+        // gamma_r (the decay, times 1 / |q_r| when q is normalised)
+        const float gr = RAWQ ? sg[16 * rt + l16] : 1.f;
 #pragma unroll
         for (int s = 0; s < SPW; ++s) {
           floatx4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int jb = 0; jb < NKD; ++jb) O = mma32(Mb[s][jb], qf[jb], O);
-          if constexpr (GATE == GDN_GATE_SCALAR) O *= gr;
+          if constexpr (RAWQ) O *= gr;
 #pragma unroll
           for (int jb = 0; jb < NKC; ++jb)
             if (32 * jb <= 16 * rt + 15) O = mma32(Eb[s][jb], pf[jb], O);

@@ -21,6 +21,7 @@ struct Problem {
   int lnh;                    // log2 of the delta steps per token (Householder
                               // products); T counts steps, q / o / log alpha
                               // / cu_seqlens count tokens.  0 otherwise.
+  bool qknorm;                // forward only: q and k rows L2-normalised
   // derived
   int64_t nchunks;            // chunk slots per head (upper bound in varlen)
   int seg;                    // chunks per segment of the forward state pass

@@ -15,7 +15,12 @@ not; alpha is a Mamba2-style decay in (0,1), beta a writing strength):
     log alpha = -softplus(N(-2, 1))     (per head, or per channel)
     S0    ~ N(0, std^2) when requested
 Draw order from one numpy PCG64 stream: lengths -> q -> k -> v -> beta
-logits -> alpha logits -> S0 -> dO.
+logits -> alpha logits -> S0 -> dO -> dS.
+
+Inputs for the forward that normalises q and k itself (``raw_qk``): the
+unit rows above are multiplied by log-uniform row scales in [lo, hi] (q's,
+then k's, drawn after everything else), and a fraction of the rows is set
+to zero (q's, then k's uniform draws).
 """
 
 from __future__ import annotations
@@ -98,9 +103,12 @@ def make_inputs(B: int, T: int, H: int, dk: int, dv: int, *,
                 with_do: bool = False,
                 with_ds: bool = False,
                 lengths=None,
-                varlen: Optional[tuple] = None) -> Inputs:
+                varlen: Optional[tuple] = None,
+                raw_qk: Optional[tuple] = None) -> Inputs:
     """Draw one problem.  ``lengths`` (explicit list) or ``varlen`` =
-    (total, lo, hi) packs sequences into B = 1 with ``cu_seqlens``."""
+    (total, lo, hi) packs sequences into B = 1 with ``cu_seqlens``.
+    ``raw_qk`` = (lo, hi, zero_frac): q and k rows not normalised (see the
+    module docstring)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     if gate_dtype is None:
         gate_dtype = dtype
@@ -124,6 +132,12 @@ def make_inputs(B: int, T: int, H: int, dk: int, dv: int, *,
         s0 = rng.standard_normal((nseq, H, dk, dv)) * s0_std
     do = rng.standard_normal((B, T, H, dv)) if with_do else None
     ds = rng.standard_normal((nseq, H, dk, dv)) if with_ds else None
+    if raw_qk is not None:
+        lo, hi, zf = raw_qk
+        q = q * np.exp(rng.uniform(np.log(lo), np.log(hi), (B, T, H, 1)))
+        k = k * np.exp(rng.uniform(np.log(lo), np.log(hi), (B, T, H, 1)))
+        q = np.where(rng.uniform(size=(B, T, H, 1)) < zf, 0.0, q)
+        k = np.where(rng.uniform(size=(B, T, H, 1)) < zf, 0.0, k)
 
     inp = Inputs(
         q=_round(q, dtype), k=_round(k, dtype), v=_round(v, dtype),

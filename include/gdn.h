@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
   GDN_OK = 0,
@@ -132,6 +132,21 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
                          const void* log_alpha, const float* s0, void* o,
                          float* s_final, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* The forward with q and k normalised inside ("Gated Delta Networks:
+ * Improving Mamba2 with Delta Rule", "Method": the block design passes q and
+ * k through an L2 normalisation per token and head; v is left as it is).
+ * Computes gdn_chunk_fwd on q_t / |q_t| and k_t / |k_t| (norms over dk, in
+ * fp32, per token and head; an all-zero row stays zero) without writing the
+ * normalised tensors: k rows are normalised as the chunk is staged, the q
+ * factor is applied to the fp32 products.  Arguments, layouts, workspace
+ * (gdn_chunk_fwd_workspace) and errors as gdn_chunk_fwd; the per-channel
+ * gate is GDN_ERR_UNSUPPORTED. */
+gdn_status gdn_chunk_fwd_qknorm(const gdn_problem* p, const void* q, const void* k,
+                                const void* v, const void* beta,
+                                const void* log_alpha, const float* s0, void* o,
+                                float* s_final, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /* Householder-product transitions (the GDN review's "Future work" and its
  * closing section name products of Householder matrices as a way to graft

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
     for s in range(8):
         txt = lib.gdn_status_str(s).decode()
         assert txt.startswith("GDN_")
@@ -275,3 +275,20 @@ def test_product_workspace_and_rejections(lib):
     st = lib.gdn_chunk_fwd_product(ctypes.byref(prob(T=100)), 2, None, A, A, A, A,
                                    None, A, None, A, 1 << 30, None)
     assert st == _lib.GDN_ERR_NULL
+
+
+def test_qknorm_rejections(lib):
+    """The forward that normalises q and k itself: the per-channel gate is
+    rejected, null pointers and a short workspace are caught before any
+    launch."""
+    st = lib.gdn_chunk_fwd_qknorm(ctypes.byref(prob(T=100, gate=_lib.GDN_GATE_CHANNEL)),
+                                  A, A, A, A, A, None, A, None, A, 1 << 30, None)
+    assert st == _lib.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_chunk_fwd_qknorm(None, A, A, A, A, A, None, A, None, A, 1 << 30,
+                                    None) == _lib.GDN_ERR_NULL
+    st = lib.gdn_chunk_fwd_qknorm(ctypes.byref(prob(T=100)), None, A, A, A, A,
+                                  None, A, None, A, 1 << 30, None)
+    assert st == _lib.GDN_ERR_NULL
+    st = lib.gdn_chunk_fwd_qknorm(ctypes.byref(prob(T=100)), A, A, A, A, A,
+                                  None, A, None, A, 1, None)
+    assert st == _lib.GDN_ERR_WORKSPACE
