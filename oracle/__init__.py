@@ -14,6 +14,9 @@ Sources (cited by page title and section):
     without defining it.
   * the GDN review's "Future work" and closing section -- name Householder-
     product transitions (several delta steps per token) without a formula.
+  * "TreeWY: Speculative Verification for Gated DeltaNet Hybrids" (summary in
+    the list of related papers) -- draft-tree verification with one
+    triangular solve and a commit of the accepted state only.
 
 Parity status per function is listed in ``gdn_oracle.__doc__``.
 """
@@ -30,5 +33,9 @@ from .gdn_oracle import (  # noqa: F401
     deltaproduct_fwd,
     gdn_fwd_qknorm,
     l2_normalize,
+    tree_fwd,
+    tree_commit,
+    tree_path,
+    tree_wy_bruteforce,
     normwise_rel_err,
 )

@@ -34,6 +34,13 @@ Readings where the pages are silent (each is listed in the design notes):
     deltaproduct_fwd).  Parity with an external definition is UNPINNED; the
     pins fix its reductions and reflection properties.
 
+  * draft trees (TreeWY, only summarised by the pages): a node continues
+    its parent's state with one step on its own token; the verification
+    returns every node's output, the commit rebuilds the accepted node's
+    state from its root path (tree_fwd, tree_commit).  Pinned by reductions
+    to the chain (a path tree is a sequence, a star tree is independent
+    single steps, every root path is a sequence) and by the tree WY form.
+
 Parity pins (tests/test_oracle_pins.py): chunked brute-force form, orthonormal
 retrieval, beta = 0 gate product, DeltaNet limit, norm bound, alpha -> 0
 erasure, gated-linear-attention limit, SGD reading, T = 1 closed form,
@@ -234,6 +241,136 @@ def gdn_decode(q, k, v, beta, log_alpha, state, gate: str = "scalar"):
             o[n, h] = oo[0]
             new[n, h] = mm
     return o, new
+
+
+# --------------------------------------------------------------------------
+# draft trees: verification and commit ("TreeWY: Speculative Verification for
+# Gated DeltaNet Hybrids")
+# --------------------------------------------------------------------------
+
+def _tree_parent(parent):
+    """Parent array of one tree: node i's parent is an earlier node or -1
+    (the committed state)."""
+    p = np.asarray(parent, dtype=np.int64)
+    assert p.ndim == 1 and np.all((p >= -1) & (p < np.arange(len(p)))), \
+        "every parent precedes its child"
+    return p
+
+
+def _trees(B: int, n: int, parent, cu_seqlens):
+    """Yield (b, start, end, tree index, parent array) for B dense trees of n
+    nodes (parent [B, n]) or trees packed by cu_seqlens (parent [total])."""
+    for b, t0, t1, m in _segments(B, n, cu_seqlens):
+        par = parent[b] if cu_seqlens is None else parent[t0:t1]
+        yield b, t0, t1, m, _tree_parent(par)
+
+
+def tree_fwd(q, k, v, beta, log_alpha, parent, s0=None, gate: str = "scalar",
+             cu_seqlens=None):
+    """Every node of draft trees hanging off a committed state.  Node i takes
+    one step of the recurrence on its own token from the state of its parent
+    (the committed state when parent[i] = -1) and reads its output from the
+    result, so each node sees exactly the tokens on its root path.
+    q,k [B,n,H,dk]; v [B,n,H,dv]; beta [B,n,H]; log_alpha as in gdn_fwd;
+    parent [B,n] int (indices inside the tree), or with cu_seqlens (trees
+    packed into B = 1) parent [total] with each tree counting from 0;
+    s0 [N,H,dk,dv] committed states (zeros if None).
+    Returns (o [B,n,H,dv], states [B,n,H,dk,dv]: the state after each node)."""
+    assert gate in GATES
+    B, n, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, n, H, dv))
+    st = np.zeros((B, n, H, dk, dv))
+    for b, t0, t1, m, par in _trees(B, n, parent, cu_seqlens):
+        for h in range(H):
+            m0 = np.zeros((dk, dv)) if s0 is None else s0[m, h]
+            for i in range(t1 - t0):
+                t = t0 + i
+                prev = m0 if par[i] < 0 else st[b, t0 + par[i], h]
+                la = None if gate == "none" else log_alpha[b, t:t + 1, h]
+                oo, mm = gdn_fwd_chain(q[b, t:t + 1, h], k[b, t:t + 1, h],
+                                       v[b, t:t + 1, h], beta[b, t:t + 1, h],
+                                       la, prev, gate)
+                o[b, t, h], st[b, t, h] = oo[0], mm
+    return o, st
+
+
+def tree_path(parent, node):
+    """Nodes from the root down to ``node`` (empty for node = -1)."""
+    par = _tree_parent(parent)
+    path = []
+    while node >= 0:
+        path.append(int(node))
+        node = par[node]
+    return path[::-1]
+
+
+def tree_commit(k, v, beta, log_alpha, parent, accepted, s0=None,
+                gate: str = "scalar", cu_seqlens=None):
+    """New committed state of every tree after accepting node accepted[m]:
+    the tokens on that node's root path, in order, run through the plain
+    recurrence from the committed state; accepted = -1 keeps it.  Shapes as
+    in tree_fwd; accepted [N].  Returns the states [N,H,dk,dv]."""
+    assert gate in GATES
+    B, n, H, dk = k.shape
+    dv = v.shape[-1]
+    N = B if cu_seqlens is None else len(cu_seqlens) - 1
+    out = np.zeros((N, H, dk, dv))
+    for b, t0, t1, m, par in _trees(B, n, parent, cu_seqlens):
+        idx = [t0 + i for i in tree_path(par, int(accepted[m]))]
+        for h in range(H):
+            m0 = np.zeros((dk, dv)) if s0 is None else s0[m, h]
+            if not idx:
+                out[m, h] = m0
+                continue
+            la = None if gate == "none" else log_alpha[b, idx, h]
+            _, out[m, h] = gdn_fwd_chain(np.zeros((len(idx), dk)), k[b, idx, h],
+                                         v[b, idx, h], beta[b, idx, h], la, m0, gate)
+    return out
+
+
+def tree_wy_bruteforce(q, k, v, beta, log_alpha, parent, m0, gate: str):
+    """The tree-structured WY form of one (tree, head), with an explicit
+    dense inverse: the chunk equations of gdn_chunked_bruteforce with "i
+    before r" replaced by "i is an ancestor of r" and the cumulative log gate
+    summed along root paths,
+        g_r = log alpha_r + g_parent(r),   gamma = exp(g),
+        A_ri = beta_r exp(g_r - g_i) k_r.k_i   (i a strict ancestor of r),
+        T = (I + A)^-1,  U = T diag(beta) V,  W = T diag(beta*gamma) K,
+        E = U - W M0,    O = diag(gamma) Q M0 + (Q K^T o Gamma) E
+    with Gamma_ri = exp(g_r - g_i) for i an ancestor of r or r itself and 0
+    elsewhere: one triangular system verifies every node.  Returns O."""
+    par = _tree_parent(parent)
+    n, dk = k.shape
+    anc = np.zeros((n, n), dtype=bool)
+    for r in range(n):
+        a = par[r]
+        while a >= 0:
+            anc[r, a] = True
+            a = par[a]
+    g = np.zeros((n, dk))
+    for r in range(n):
+        if gate == "scalar":
+            own = np.full(dk, float(log_alpha[r]))
+        elif gate == "channel":
+            own = np.asarray(log_alpha[r], dtype=np.float64)
+        else:
+            own = np.zeros(dk)
+        g[r] = own + (g[par[r]] if par[r] >= 0 else 0.0)
+    A = np.zeros((n, n))
+    P = np.zeros((n, n))
+    for r in range(n):
+        for i in range(n):
+            if anc[r, i] or i == r:
+                d = np.exp(g[r] - g[i])
+                P[r, i] = np.sum(q[r] * k[i] * d)
+                if i != r:
+                    A[r, i] = beta[r] * np.sum(k[r] * k[i] * d)
+    Tm = np.linalg.inv(np.eye(n) + A)
+    U = Tm @ (beta[:, None] * v)
+    W = Tm @ (beta[:, None] * k * np.exp(g))
+    E = U - W @ m0
+    return (q * np.exp(g)) @ m0 + P @ E
 
 
 # --------------------------------------------------------------------------

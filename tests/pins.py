@@ -237,3 +237,116 @@ def dp_gate_once_per_token(dp_fwd, gdn_fwd, seed=10):
         o2, s2 = gdn_fwd(q, k[:, :, live], v[:, :, live], b[:, :, live], la, s0, "scalar")
         worst = max(worst, np.max(np.abs(o1 - o2)), np.max(np.abs(s1 - s2)))
     return worst
+
+
+# ------------------------------------------------------------- draft trees ---
+# Checks of oracle.tree_fwd / tree_commit / tree_wy_bruteforce (draft-tree
+# verification): a node continues its parent's state with one step on its own
+# token.  Each check reduces a tree to sequences of the pinned recurrence.
+
+def _tree_problem(r, B, n, H, dk, dv, gate):
+    q = unit(r.standard_normal((B, n, H, dk)))
+    k = unit(r.standard_normal((B, n, H, dk)))
+    v = r.standard_normal((B, n, H, dv))
+    beta = r.random((B, n, H))
+    if gate == "channel":
+        la = -r.random((B, n, H, dk))
+    elif gate == "scalar":
+        la = -r.random((B, n, H))
+    else:
+        la = None
+    s0 = r.standard_normal((B, H, dk, dv))
+    return q, k, v, beta, la, s0
+
+
+def random_tree(r, n):
+    """Parents drawn uniformly from the earlier nodes and the root (-1)."""
+    return np.array([int(r.integers(-1, i)) for i in range(n)], dtype=np.int64)
+
+
+def _sel(la, b, idx, h):
+    return None if la is None else la[b, idx, h][None, :, None]
+
+
+def tree_chain_is_sequence(tree_fwd, gdn_fwd, gate, seed=21):
+    """parent[i] = i - 1: the tree is one sequence."""
+    r = rng(seed)
+    q, k, v, beta, la, s0 = _tree_problem(r, 2, 9, 2, 5, 4, gate)
+    par = np.tile(np.arange(9) - 1, (2, 1))
+    o1, st = tree_fwd(q, k, v, beta, la, par, s0, gate)
+    o2, sf = gdn_fwd(q, k, v, beta, la, s0, gate)
+    return max(np.max(np.abs(o1 - o2)), np.max(np.abs(st[:, -1] - sf)))
+
+
+def tree_star_is_single_steps(tree_fwd, gdn_decode, gate, seed=22):
+    """All parents -1: every node is one decode step from the committed
+    state."""
+    r = rng(seed)
+    n = 7
+    q, k, v, beta, la, s0 = _tree_problem(r, 1, n, 2, 5, 4, gate)
+    o1, st = tree_fwd(q, k, v, beta, la, np.full((1, n), -1), s0, gate)
+    worst = 0.0
+    for i in range(n):
+        lai = None if la is None else la[:, i]
+        o2, s2 = gdn_decode(q[:, i], k[:, i], v[:, i], beta[:, i], lai, s0, gate)
+        worst = max(worst, np.max(np.abs(o1[:, i] - o2)), np.max(np.abs(st[:, i] - s2)))
+    return worst
+
+
+def tree_paths_are_sequences(tree_fwd, gdn_fwd, gate, seed=23):
+    """Every node's output and state are those of the sequence of tokens on
+    its root path."""
+    r = rng(seed)
+    n = 12
+    q, k, v, beta, la, s0 = _tree_problem(r, 1, n, 2, 5, 4, gate)
+    par = random_tree(r, n)
+    o1, st = tree_fwd(q, k, v, beta, la, par[None], s0, gate)
+    worst = 0.0
+    for node in range(n):
+        path, a = [], node
+        while a >= 0:
+            path.append(a)
+            a = par[a]
+        path = path[::-1]
+        for h in range(2):
+            lap = None if la is None else la[0, path, h][None, :, None]
+            o2, s2 = gdn_fwd(q[0, path, h][None, :, None], k[0, path, h][None, :, None],
+                             v[0, path, h][None, :, None], beta[0, path, h][None, :, None],
+                             lap, s0[:, h:h + 1], gate)
+            worst = max(worst, np.max(np.abs(o1[0, node, h] - o2[0, -1, 0])),
+                        np.max(np.abs(st[0, node, h] - s2[0, 0])))
+    return worst
+
+
+def tree_commit_is_node_state(tree_commit, tree_fwd, gate, seed=24):
+    """The commit of node a equals the verification's state after a (the
+    two are computed along different routes); a = -1 keeps the committed
+    state.  Trees packed by cu_seqlens."""
+    r = rng(seed)
+    lens = [6, 1, 9, 4]
+    n = sum(lens)
+    q, k, v, beta, la, _ = _tree_problem(r, 1, n, 2, 5, 4, gate)
+    s0 = r.standard_normal((len(lens), 2, 5, 4))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    par = np.concatenate([random_tree(r, L) for L in lens])
+    acc = np.array([3, -1, 8, 2])
+    _, st = tree_fwd(q, k, v, beta, la, par, s0, gate, cu_seqlens=cu)
+    new = tree_commit(k, v, beta, la, par, acc, s0, gate, cu_seqlens=cu)
+    worst = 0.0
+    for m, a in enumerate(acc):
+        ref = s0[m] if a < 0 else st[0, cu[m] + a]
+        worst = max(worst, np.max(np.abs(new[m] - ref)))
+    return worst
+
+
+def tree_wy_matches_recurrence(tree_wy, tree_fwd, gate, seed=25):
+    """The tree WY form (one triangular solve over ancestors) gives every
+    node's output."""
+    r = rng(seed)
+    n = 14
+    q, k, v, beta, la, s0 = _tree_problem(r, 1, n, 1, 6, 3, gate)
+    par = random_tree(r, n)
+    o1, _ = tree_fwd(q, k, v, beta, la, par[None], s0, gate)
+    lah = None if la is None else la[0, :, 0]
+    o2 = tree_wy(q[0, :, 0], k[0, :, 0], v[0, :, 0], beta[0, :, 0], lah, par, s0[0, 0], gate)
+    return np.max(np.abs(o1[0, :, 0] - o2))

@@ -311,3 +311,43 @@ def test_qknorm_is_scale_invariant(gate):
     o3, s3 = oracle.gdn_fwd_qknorm(q * sq, k * sk, v, beta, la, m0, gate)
     for a, b in ((o1, o2), (s1, s2), (o1, o3), (s1, s3)):
         assert np.max(np.abs(a - b)) < 1e-12
+
+
+# ------------------------------------------------------------- draft trees ---
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_tree_reductions_to_sequences(gate):
+    assert pins.tree_chain_is_sequence(oracle.tree_fwd, oracle.gdn_fwd, gate) < 1e-13
+    assert pins.tree_star_is_single_steps(oracle.tree_fwd, oracle.gdn_decode, gate) < 1e-13
+    assert pins.tree_paths_are_sequences(oracle.tree_fwd, oracle.gdn_fwd, gate) < 1e-13
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_tree_commit_and_wy_form(gate):
+    assert pins.tree_commit_is_node_state(oracle.tree_commit, oracle.tree_fwd, gate) < 1e-13
+    assert pins.tree_wy_matches_recurrence(oracle.tree_wy_bruteforce, oracle.tree_fwd,
+                                           gate) < 1e-12
+
+
+def test_tree_relabelling():
+    """Another topological numbering of the same tree permutes the outputs."""
+    r = pins.rng(26)
+    n = 10
+    q, k, v, beta, la, s0 = pins._tree_problem(r, 1, n, 2, 4, 3, "scalar")
+    par = pins.random_tree(r, n)
+    # children of the root first, then by depth (a breadth-first numbering)
+    depth = np.zeros(n, dtype=int)
+    for i in range(n):
+        depth[i] = 0 if par[i] < 0 else depth[par[i]] + 1
+    perm = np.argsort(depth, kind="stable")        # new node j is old perm[j]
+    inv = np.argsort(perm)
+    par2 = np.array([-1 if par[perm[j]] < 0 else inv[par[perm[j]]] for j in range(n)])
+    o1, _ = oracle.tree_fwd(q, k, v, beta, la, par[None], s0, "scalar")
+    o2, _ = oracle.tree_fwd(q[:, perm], k[:, perm], v[:, perm], beta[:, perm], la[:, perm],
+                            par2[None], s0, "scalar")
+    assert np.max(np.abs(o2 - o1[:, perm])) < 1e-14
+
+
+def test_tree_rejects_parent_after_child():
+    with pytest.raises(AssertionError):
+        oracle.tree_path([-1, 2, 0], 1)

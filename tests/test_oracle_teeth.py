@@ -182,3 +182,44 @@ def test_reference_oracle_passes_dp_pins():
 def test_dp_mutant_is_caught(name):
     mod = _mutant(*DP_MUTANTS[name])
     assert not _dp_pins_pass(mod), name
+
+
+# ------------------------------------------------------------- draft trees ---
+
+def _tree_pins_pass(mod):
+    worst = 0.0
+    for gate in ("scalar", "channel"):
+        worst = max(worst,
+                    pins.tree_chain_is_sequence(mod.tree_fwd, mod.gdn_fwd, gate),
+                    pins.tree_star_is_single_steps(mod.tree_fwd, mod.gdn_decode, gate),
+                    pins.tree_paths_are_sequences(mod.tree_fwd, mod.gdn_fwd, gate),
+                    pins.tree_commit_is_node_state(mod.tree_commit, mod.tree_fwd, gate),
+                    pins.tree_wy_matches_recurrence(mod.tree_wy_bruteforce, mod.tree_fwd,
+                                                    gate))
+    return worst < 1e-12
+
+
+TREE_MUTANTS = {
+    "node continues the previous node": (
+        "                prev = m0 if par[i] < 0 else st[b, t0 + par[i], h]\n",
+        "                prev = m0 if i == 0 else st[b, t - 1, h]\n"),
+    "commit walks the path leaf first": (
+        "    return path[::-1]\n",
+        "    return path\n"),
+    "WY mask over every earlier node": (
+        "            if anc[r, i] or i == r:\n",
+        "            if i <= r:\n"),
+    "path gate summed over earlier nodes": (
+        "        g[r] = own + (g[par[r]] if par[r] >= 0 else 0.0)\n",
+        "        g[r] = own + (g[r - 1] if r > 0 else 0.0)\n"),
+}
+
+
+def test_reference_oracle_passes_tree_pins():
+    assert _tree_pins_pass(ref_mod)
+
+
+@pytest.mark.parametrize("name", sorted(TREE_MUTANTS))
+def test_tree_mutant_is_caught(name):
+    mod = _mutant(*TREE_MUTANTS[name])
+    assert not _tree_pins_pass(mod), name
