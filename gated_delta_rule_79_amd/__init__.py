@@ -24,7 +24,8 @@ import torch
 from . import _lib
 from ._lib import GdnError  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "FwdPlan", "GdnError",
+__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "chunk_fwd_product", "tree_verify",
+           "tree_commit", "FwdPlan", "GdnError", "set_segment_chunks",
            "abi_version", "stage_times"]
 
 _DT = {torch.float32: _lib.GDN_F32, torch.bfloat16: _lib.GDN_BF16}
@@ -130,6 +131,53 @@ def chunk_fwd_product(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
                                    _ptr(ws), ws.numel(), _stream(q.device))
     _lib.check(st, "gdn_chunk_fwd_product")
     return o, sf
+
+
+def _check_tree_index(t, name, q):
+    if t.dtype != torch.int32 or t.device != q.device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor on the inputs' device")
+
+
+def tree_verify(q, k, v, beta, log_alpha, parent, state=None, chunk: int = 64,
+                cu_seqlens=None, workspace: Optional[torch.Tensor] = None):
+    """Outputs of every node of draft trees (gdn_tree_verify).  q, k [B,n,H,dk],
+    v [B,n,H,dv], beta [B,n,H], log_alpha [B,n,H] or None; parent int32
+    [B,n] (or [total] with cu_seqlens), parents inside each tree, -1 = the
+    committed state; state [ntrees,H,dk,dv] fp32 (read only) or None.
+    Returns o [B,n,H,dv]."""
+    lib = _lib.load()
+    _check_cu(cu_seqlens, q)
+    _check_tree_index(parent, "parent", q)
+    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
+    o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.gdn_tree_verify_workspace(ctypes.byref(p), ctypes.byref(need)),
+               "gdn_tree_verify_workspace")
+    ws = workspace
+    if ws is None or ws.numel() < need.value:
+        ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    st = lib.gdn_tree_verify(ctypes.byref(p), _ptr(parent), _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(beta), _ptr(log_alpha), _ptr(state), _ptr(o),
+                             _ptr(ws), ws.numel(), _stream(q.device))
+    _lib.check(st, "gdn_tree_verify")
+    return o
+
+
+def tree_commit(k, v, beta, log_alpha, parent, accepted, state, chunk: int = 64,
+                cu_seqlens=None):
+    """In place: state[m] becomes the state of node accepted[m] of tree m
+    (gdn_tree_commit); accepted[m] = -1 keeps it.  Shapes as tree_verify;
+    accepted int32 [ntrees].  Returns state."""
+    lib = _lib.load()
+    _check_cu(cu_seqlens, k)
+    _check_tree_index(parent, "parent", k)
+    _check_tree_index(accepted, "accepted", k)
+    p = _problem(k, v, beta, log_alpha, chunk, cu_seqlens)
+    st = lib.gdn_tree_commit(ctypes.byref(p), _ptr(parent), _ptr(accepted), _ptr(k),
+                             _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(state),
+                             _stream(k.device))
+    _lib.check(st, "gdn_tree_commit")
+    return state
 
 
 class FwdPlan:

@@ -23,11 +23,12 @@ EXPORTED = (
     "gdn_decode_step", "gdn_test_set_fail_launch", "gdn_profile_enable",
     "gdn_profile_read", "gdn_set_segment_chunks",
     "gdn_chunk_fwd_product_workspace", "gdn_chunk_fwd_product",
-    "gdn_chunk_fwd_qknorm",
+    "gdn_chunk_fwd_qknorm", "gdn_tree_verify_workspace", "gdn_tree_verify",
+    "gdn_tree_commit",
 )
-STAGE_COUNT = 10
+STAGE_COUNT = 11
 STAGES = ("chunk_map", "fwd_prep", "fwd_scan", "decode", "bwd_states",
-          "bwd_scan", "bwd_grad", "other", "fwd_trans", "fwd_combine")
+          "bwd_scan", "bwd_grad", "other", "fwd_trans", "fwd_combine", "tree_commit")
 
 
 class GdnProblem(ctypes.Structure):
@@ -92,6 +93,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_chunk_fwd_product.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_chunk_fwd_qknorm.restype = i32
     lib.gdn_chunk_fwd_qknorm.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_tree_verify_workspace.restype = i32
+    lib.gdn_tree_verify_workspace.argtypes = [pp, ctypes.POINTER(sz)]
+    lib.gdn_tree_verify.restype = i32
+    lib.gdn_tree_verify.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_tree_commit.restype = i32
+    lib.gdn_tree_commit.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
     if path is None:
         _LIB = lib
     return lib

@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_fwd.hip", "gdn_bwd.hip"]
+SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_fwd.hip", "gdn_bwd.hip", "gdn_tree.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

@@ -75,6 +75,7 @@ gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out, int lnh 
   out->T = p->T << lnh;
   out->lnh = lnh;
   out->qknorm = false;
+  out->parent = nullptr;
   out->H = p->H;
   out->dk = p->dk;
   out->dv = p->dv;
@@ -329,6 +330,79 @@ gdn_status gdn_chunk_fwd_qknorm(const gdn_problem* p, const void* q, const void*
     return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o,
                                     s_final, ws,
                                     static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+// Draft trees: one tree per chunk, no segment split, per-token gates only.
+static gdn_status check_tree(const gdn_problem* p, gdn::Problem* out) {
+  if (p == nullptr) return GDN_ERR_NULL;
+  if (p->gate == GDN_GATE_CHANNEL) return GDN_ERR_UNSUPPORTED;
+  GDN_TRY(check_chunk_problem(p, out));
+  if (!out->varlen && p->T > p->chunk) return GDN_ERR_SHAPE;
+  out->seg = 0;
+  out->nsegs = out->nseq;
+  return GDN_OK;
+}
+
+gdn_status gdn_tree_verify_workspace(const gdn_problem* p, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return GDN_ERR_NULL;
+    gdn::Problem pp;
+    GDN_TRY(check_tree(p, &pp));
+    *bytes = gdn::fwd_workspace_bytes(pp);
+    return GDN_OK;
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+gdn_status gdn_tree_verify(const gdn_problem* p, const int32_t* parent, const void* q,
+                           const void* k, const void* v, const void* beta,
+                           const void* log_alpha, const float* state, void* o,
+                           void* ws, size_t ws_bytes, void* stream) {
+  try {
+    gdn::Problem pp;
+    GDN_TRY(check_tree(p, &pp));
+    GDN_TRY(check_fwd_pointers(pp, q, k, v, beta, log_alpha, state, o, nullptr));
+    GDN_TRY(need(parent, static_cast<int64_t>(pp.B) * pp.T));
+    if ((reinterpret_cast<uintptr_t>(parent) & 3u) != 0) return GDN_ERR_ALIGN;
+    const size_t need_ws = gdn::fwd_workspace_bytes(pp);
+    if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
+      return GDN_ERR_WORKSPACE;
+    GDN_TRY(opt(ws));
+    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    pp.parent = parent;
+    return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, state, o, nullptr, ws,
+                                    static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+gdn_status gdn_tree_commit(const gdn_problem* p, const int32_t* parent,
+                           const int32_t* accepted, const void* k, const void* v,
+                           const void* beta, const void* log_alpha, float* state,
+                           void* stream) {
+  try {
+    gdn::Problem pp;
+    GDN_TRY(check_tree(p, &pp));
+    const int64_t tok = static_cast<int64_t>(pp.B) * pp.T * pp.H;
+    GDN_TRY(need(k, tok * pp.dk));
+    GDN_TRY(need(v, tok * pp.dv));
+    GDN_TRY(need(beta, tok));
+    if (pp.gate != GDN_GATE_NONE) GDN_TRY(need(log_alpha, tok));
+    else GDN_TRY(opt(log_alpha));
+    GDN_TRY(need(parent, static_cast<int64_t>(pp.B) * pp.T));
+    GDN_TRY(need(accepted, pp.nseq));
+    GDN_TRY(need(state, static_cast<int64_t>(pp.nseq) * pp.H * pp.dk * pp.dv));
+    if ((reinterpret_cast<uintptr_t>(parent) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(accepted) & 3u) != 0)
+      return GDN_ERR_ALIGN;
+    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    return launched(gdn::launch_tree_commit(pp, parent, accepted, k, v, beta, log_alpha,
+                                            state, static_cast<hipStream_t>(stream)));
   } catch (...) {
     return GDN_ERR_HIP;
   }

@@ -854,7 +854,8 @@ struct PrepSgSmem {
   static constexpr size_t xs_off = g_off + size_t(C) * 4;
   static constexpr size_t ks_off = xs_off + size_t(C) * 4;
   static constexpr size_t qn_off = ks_off + size_t(C) * 4;   // 1 / |q_r|
-  static constexpr size_t total = qn_off + size_t(C) * 4;
+  static constexpr size_t anc_off = qn_off + size_t(C) * 4;  // tree ancestor sets
+  static constexpr size_t total = anc_off + size_t(C) * 8;
   static_assert(total <= 160 * 1024, "prep LDS budget");
 };
 
@@ -866,12 +867,20 @@ struct PrepSgSmem {
 // dtype); q rows keep their values and the factor 1 / |q_r| goes to the P
 // rows (in fp32, after the product) and into gamma_r for the scan, whose
 // state term multiplies the raw q product by gamma_r.
+// parent != nullptr (draft trees, one tree per chunk): row r continues the
+// state of row parent[tok0 + r] (-1: the chunk's entering state) instead of
+// row r - 1.  The cumulative log gate is summed along root paths and the A
+// and P entries are kept only where i is an ancestor of r (P: or r itself);
+// everything else is the chunk form unchanged, since an entry of
+// T = (I + A)^-1 only ever chains ancestors.  The state carried past the
+// chunk is not meaningful for a tree: its decays are set to zero.  Parent
+// entries outside [-1, r) are read as -1.
 template <int C, int DK, typename IO, int GATE>
 __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
-    FwdBuffers buf, int lnh, bool qkn) {
+    FwdBuffers buf, int lnh, bool qkn, const int32_t* __restrict__ parent) {
   static_assert(GATE != GDN_GATE_CHANNEL, "per-token gates only");
   using OP = IO;
   using S = PrepSgSmem<C, DK, IO>;
@@ -893,6 +902,8 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
   float* sxs = reinterpret_cast<float*>(smem + S::xs_off);
   float* sks = reinterpret_cast<float*>(smem + S::ks_off);
   float* sqn = reinterpret_cast<float*>(smem + S::qn_off);
+  uint64_t* sanc = reinterpret_cast<uint64_t*>(smem + S::anc_off);
+  const bool tree = parent != nullptr;
 
   const int L = blockIdx.x;
   const int c = static_cast<int>(L / H);
@@ -1037,10 +1048,36 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
         if (((tok0 + lane) & nhm) == 0)  // the decay acts on a token's first step
           x = load_gate(la, ((tok0 + lane) >> lnh) * H + h, gbf) * kLog2e;
     }
+    if (!tree) {
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float y = __shfl_up(x, d, 64);
-      if (lane >= d) x += y;
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+      }
+    } else {
+      // pointer jumping over parents: after round j, x sums the log gates of
+      // the 2^j nearest nodes of the root path (the row itself included),
+      // anc holds the 2^j nearest strict ancestors and nx the next node up
+      int nx = -1;
+      if (lane < len) {
+        nx = parent[tok0 + lane];
+        if (nx < -1 || nx >= lane) nx = -1;
+      }
+      uint64_t anc = nx >= 0 ? (uint64_t(1) << nx) : 0;
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {  // 2^6 = 64 >= any path in a chunk
+        const int src = nx >= 0 ? nx : lane;
+        const float xs = __shfl(x, src, 64);
+        const uint32_t alo = __shfl(static_cast<uint32_t>(anc), src, 64);
+        const uint32_t ahi = __shfl(static_cast<uint32_t>(anc >> 32), src, 64);
+        const int ns = __shfl(nx, src, 64);
+        if (nx >= 0) {
+          x += xs;
+          anc |= (static_cast<uint64_t>(ahi) << 32) | alo;
+          nx = ns;
+        }
+      }
+      if (lane < C) sanc[lane] = anc;
     }
     const float gend = __shfl(x, C - 1, 64);
     if (lane < C) {
@@ -1048,10 +1085,10 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
       sg2[lane] = x;
       if constexpr (GATE == GDN_GATE_SCALAR) {
         sxs[lane] = b * __builtin_amdgcn_exp2f(x);
-        sks[lane] = __builtin_amdgcn_exp2f(gend - x);
+        sks[lane] = tree ? 0.f : __builtin_amdgcn_exp2f(gend - x);
       } else {
         sxs[lane] = b;
-        sks[lane] = 1.f;
+        sks[lane] = tree ? 0.f : 1.f;
       }
     }
   }
@@ -1090,7 +1127,8 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
         const int r = 16 * rt + 4 * lg + e;
         float val = acc[e] * br[e];
         if constexpr (GATE == GDN_GATE_SCALAR) val *= __builtin_amdgcn_exp2f(gr[e] - gi);
-        sA[r * LDC + i] = i < r ? val : 0.f;
+        const bool keep = i < r && (!tree || ((sanc[r] >> i) & 1));
+        sA[r * LDC + i] = keep ? val : 0.f;
       }
     } else {
       int rt = 0, jb = 0;
@@ -1098,6 +1136,8 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
       const int r = 16 * rt + l16;
       const float grr = sg2[r];
       const float qs = qkn ? sqn[r] : 1.f;
+      // columns kept in row r: all i <= r, or the ancestors of r and r itself
+      const uint64_t keep = tree ? (sanc[r] | (uint64_t(1) << r)) : ~uint64_t(0);
       float out[8];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -1120,7 +1160,8 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
           const int i = 16 * it + 4 * lg + e;
           float val = acc[e] * qs;
           if constexpr (GATE == GDN_GATE_SCALAR) val *= __builtin_amdgcn_exp2f(grr - gi4[e]);
-          out[4 * half + e] = (it <= rt && it < NB && i <= r) ? val : 0.f;
+          out[4 * half + e] =
+              (it <= rt && it < NB && i <= r && ((keep >> i) & 1)) ? val : 0.f;
         }
       }
       *reinterpret_cast<opvec<OP>*>(dP + ((size_t(rt) * NKC + jb) * 64 + lane) * 8 * ob) =
@@ -1138,7 +1179,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
       gam[tid] = (GATE == GDN_GATE_SCALAR ? __builtin_amdgcn_exp2f(sg2[tid]) : 1.f) *
                  (qkn ? sqn[tid] : 1.f);
     for (int d = tid; d < DK; d += NT)
-      gam[C + d] = GATE == GDN_GATE_SCALAR ? __builtin_amdgcn_exp2f(sg2[C - 1]) : 1.f;
+      gam[C + d] = tree ? 0.f : (GATE == GDN_GATE_SCALAR ? __builtin_amdgcn_exp2f(sg2[C - 1]) : 1.f);
   }
   __syncthreads();
 

@@ -22,6 +22,8 @@ struct Problem {
                               // products); T counts steps, q / o / log alpha
                               // / cu_seqlens count tokens.  0 otherwise.
   bool qknorm;                // forward only: q and k rows L2-normalised
+  const int32_t* parent;      // forward only: draft trees, one per chunk
+                              // (device, node parents inside each tree)
   // derived
   int64_t nchunks;            // chunk slots per head (upper bound in varlen)
   int seg;                    // chunks per segment of the forward state pass
@@ -52,6 +54,12 @@ struct StageScope {
 hipError_t launch_decode(const Problem& p, const void* q, const void* k,
                          const void* v, const void* beta, const void* la,
                          float* state, void* o, hipStream_t s);
+
+// Draft-tree commit (gdn_tree.hip).
+hipError_t launch_tree_commit(const Problem& p, const int32_t* parent,
+                              const int32_t* accepted, const void* k, const void* v,
+                              const void* beta, const void* la, float* state,
+                              hipStream_t s);
 
 // Forward (gdn_fwd.hip).
 size_t fwd_workspace_bytes(const Problem& p);

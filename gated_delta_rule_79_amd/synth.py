@@ -31,7 +31,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Inputs", "make_inputs", "make_product_inputs", "varlen_lengths",
+__all__ = ["Inputs", "make_inputs", "make_product_inputs", "make_tree_inputs",
+           "random_parents", "varlen_lengths",
            "WORKLOADS", "workload"]
 
 
@@ -198,6 +199,46 @@ def make_product_inputs(B: int, T: int, H: int, dk: int, dv: int, nh: int, *,
                       else getattr(inp, name).double().numpy())
                for name in ("q", "k", "v", "beta", "log_alpha", "s0")}
     return inp
+
+
+def random_parents(rng: np.random.Generator, n: int) -> np.ndarray:
+    """A random recursive tree of n nodes: node i's parent is uniform over
+    the earlier nodes and the root (-1)."""
+    return np.array([int(rng.integers(-1, i)) for i in range(n)], dtype=np.int32)
+
+
+def make_tree_inputs(B: int, n: int, H: int, dk: int, dv: int, *,
+                     dtype: torch.dtype = torch.bfloat16,
+                     gate: str = "scalar",
+                     chunk: int = 64,
+                     seed: int = 0,
+                     s0_std: Optional[float] = 0.02,
+                     lengths=None,
+                     shape: str = "random"):
+    """Draw B draft trees of n nodes (or trees of the given ``lengths``
+    packed with cu_seqlens), one token per node, with the distributions of
+    make_inputs and the committed states ~ N(0, s0_std^2).  ``shape``:
+    "random" (random recursive trees), "chain" (parent i - 1) or "star"
+    (every parent -1).  The tensors are make_inputs' draws; the parents and
+    one accepted node per tree (uniform over its nodes, -1 for an empty
+    tree) come from a second PCG64 stream seeded seed + 7919.  Returns (Inputs, parent int32 tensor [B, n] or
+    [total], accepted int32 tensor [ntrees])."""
+    inp = make_inputs(B, n, H, dk, dv, dtype=dtype, gate=gate, chunk=chunk, seed=seed,
+                      s0_std=s0_std, lengths=lengths)
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    sizes = [n] * B if lengths is None else list(lengths)
+    par, acc = [], []
+    for L in sizes:
+        if shape == "chain":
+            par.append(np.arange(L, dtype=np.int32) - 1)
+        elif shape == "star":
+            par.append(np.full(L, -1, dtype=np.int32))
+        else:
+            par.append(random_parents(rng, L))
+        acc.append(int(rng.integers(0, L)) if L > 0 else -1)
+    parent = (np.stack(par) if lengths is None else np.concatenate(par + [np.zeros(0, np.int32)]))
+    return (inp, torch.from_numpy(parent.astype(np.int32)),
+            torch.tensor(acc, dtype=torch.int32))
 
 
 # Named workloads.  Sizes follow the configurations the method is measured on.

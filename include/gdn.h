@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum {
   GDN_OK = 0,
@@ -173,6 +173,48 @@ gdn_status gdn_chunk_fwd_product(const gdn_problem* p, int32_t nh, const void* q
                                  float* s_final, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* Draft-tree verification for speculative decoding ("TreeWY: Speculative
+ * Verification for Gated DeltaNet Hybrids": the gated delta rule as a
+ * tree-structured WY transform, every draft node verified by one triangular
+ * solve, only the accepted state rebuilt on commit).  Each tree hangs off a
+ * committed state; node i carries one token and continues the state of its
+ * parent (parent[i] in [-1, i), -1 = the committed state) with one step of
+ * the recurrence, and o_i is read from the node's state.  No per-node state
+ * is stored: one chunk per tree runs the chunk form with "earlier token"
+ * replaced by "ancestor" (path-summed log gates, A and QK^T kept on
+ * ancestors only).
+ *   p        : B trees of T nodes (dense) or nseq trees packed by
+ *              cu_seqlens (B == 1); every tree has at most `chunk` nodes
+ *              (dense: T <= chunk, else GDN_ERR_SHAPE; varlen: the caller's
+ *              promise, nodes past the chunk get unspecified outputs);
+ *              gate none or scalar (per-channel: GDN_ERR_UNSUPPORTED).
+ *   parent   : device int32, [B, T] or [total nodes], indices inside each
+ *              tree; entries outside [-1, i) are read as -1.
+ *   q, k, v, beta, log_alpha : per node, layouts as in gdn_chunk_fwd.
+ *   state    : committed states [ntrees, H, dk, dv] fp32 (read only), or
+ *              NULL for zeros.
+ *   o        : [B, T, H, dv] in io_dtype.
+ *   ws       : at least gdn_tree_verify_workspace bytes.
+ * Errors as gdn_chunk_fwd, plus GDN_ERR_NULL for a NULL parent. */
+gdn_status gdn_tree_verify_workspace(const gdn_problem* p, size_t* bytes);
+gdn_status gdn_tree_verify(const gdn_problem* p, const int32_t* parent, const void* q,
+                           const void* k, const void* v, const void* beta,
+                           const void* log_alpha, const float* state, void* o,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Commit after a verification: state[m] becomes the state of node
+ * accepted[m] of tree m, rebuilt from the committed state along that node's
+ * root path (in place; one read and one write of the state).  accepted[m] =
+ * -1, or any index outside [0, min(tree size, 64)), leaves state[m] as it is.
+ *   p, parent, k, v, beta, log_alpha : as in gdn_tree_verify (q is not
+ *              needed); trees of up to 64 nodes.
+ *   accepted : device int32 [ntrees].
+ *   state    : [ntrees, H, dk, dv] fp32, in/out. */
+gdn_status gdn_tree_commit(const gdn_problem* p, const int32_t* parent,
+                           const int32_t* accepted, const void* k, const void* v,
+                           const void* beta, const void* log_alpha, float* state,
+                           void* stream);
+
 /* Workspace bytes gdn_chunk_bwd needs (see gdn_chunk_fwd_workspace). */
 gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes);
 
@@ -211,7 +253,7 @@ gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k,
  * into total_ms[GDN_STAGE_COUNT] and count[GDN_STAGE_COUNT], and clears the
  * record.  Not for use while a stream is being captured into a graph.
  * Calls that overlap on several host threads are recorded together. */
-#define GDN_STAGE_COUNT 10
+#define GDN_STAGE_COUNT 11
 typedef enum {
   GDN_STAGE_CHUNK_MAP = 0,  /* varlen chunk table                         */
   GDN_STAGE_FWD_PREP = 1,   /* per-chunk gate, UT transform, W/U/P        */
@@ -222,7 +264,8 @@ typedef enum {
   GDN_STAGE_BWD_GRAD = 6,   /* backward: per-chunk gradients              */
   GDN_STAGE_OTHER = 7,
   GDN_STAGE_FWD_TRANS = 8,  /* forward: per-segment state maps [M0 | Phi] */
-  GDN_STAGE_FWD_COMBINE = 9 /* forward: states entering each segment      */
+  GDN_STAGE_FWD_COMBINE = 9, /* forward: states entering each segment     */
+  GDN_STAGE_TREE_COMMIT = 10 /* draft trees: accepted state rebuilt       */
 } gdn_stage;
 void gdn_profile_enable(int enable);
 gdn_status gdn_profile_read(double* total_ms, int32_t* count);

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 4
+    assert lib.gdn_abi_version() == 5
     for s in range(8):
         txt = lib.gdn_status_str(s).decode()
         assert txt.startswith("GDN_")
@@ -292,3 +292,31 @@ def test_qknorm_rejections(lib):
     st = lib.gdn_chunk_fwd_qknorm(ctypes.byref(prob(T=100)), A, A, A, A, A,
                                   None, A, None, A, 1, None)
     assert st == _lib.GDN_ERR_WORKSPACE
+
+
+def test_tree_rejections_before_launch(lib):
+    """Draft trees: more nodes than the chunk (dense), the per-channel gate,
+    null or misaligned parent / accepted arrays are rejected before any
+    launch; the verification workspace is the forward's for the same sizes."""
+    n = ctypes.c_size_t(0)
+    st = lib.gdn_tree_verify_workspace(ctypes.byref(prob(T=16, chunk=16)), ctypes.byref(n))
+    st2, ref = ws_bytes(lib, prob(T=16, chunk=16))
+    assert st == _lib.GDN_OK and st2 == _lib.GDN_OK and n.value == ref
+    assert lib.gdn_tree_verify_workspace(ctypes.byref(prob(T=40, chunk=32)),
+                                         ctypes.byref(n)) == _lib.GDN_ERR_SHAPE
+    assert lib.gdn_tree_verify_workspace(
+        ctypes.byref(prob(T=16, chunk=16, gate=_lib.GDN_GATE_CHANNEL)),
+        ctypes.byref(n)) == _lib.GDN_ERR_UNSUPPORTED
+    p = prob(T=16, chunk=16)
+    assert lib.gdn_tree_verify(ctypes.byref(p), None, A, A, A, A, A, None, A, A, 1 << 30,
+                               None) == _lib.GDN_ERR_NULL
+    assert lib.gdn_tree_verify(ctypes.byref(p), A + 2, A, A, A, A, A, None, A, A, 1 << 30,
+                               None) == _lib.GDN_ERR_ALIGN
+    assert lib.gdn_tree_verify(ctypes.byref(p), A, A, A, A, A, A, None, A, A, 1,
+                               None) == _lib.GDN_ERR_WORKSPACE
+    assert lib.gdn_tree_commit(ctypes.byref(p), A, None, A, A, A, A, A,
+                               None) == _lib.GDN_ERR_NULL
+    assert lib.gdn_tree_commit(ctypes.byref(p), A, A, A, A, A, A, None,
+                               None) == _lib.GDN_ERR_NULL
+    assert lib.gdn_tree_commit(ctypes.byref(prob(T=40, chunk=32)), A, A, A, A, A, A, A,
+                               None) == _lib.GDN_ERR_SHAPE
