@@ -15,6 +15,7 @@ Other entry points (same JSON shape, their own metric string):
     --mode fwdbwd   forward + backward       (tokens / (t_fwd + t_bwd))
     --mode decode   gdn_decode_step in place (default workload decode_n256_h32)
     --mode product  gdn_chunk_fwd_product (Householder products, --nh steps)
+    --mode tree     gdn_tree_verify + gdn_tree_commit (one speculative round)
     --qk-l2norm     (forward) gdn_chunk_fwd_qknorm on q, k rows that are not
                     unit vectors (log-uniform row scales in [0.05, 20])
 
@@ -292,6 +293,126 @@ def main_product(args):
     print(json.dumps(out), flush=True)
 
 
+def tree_depths(parent, n):
+    """Root-path length of every node of dense trees parent [B, n]."""
+    B = parent.shape[0]
+    depth = [[0] * n for _ in range(B)]
+    for b in range(B):
+        for i in range(n):
+            p = int(parent[b, i])
+            depth[b][i] = 1 + (depth[b][p] if p >= 0 else 0)
+    return depth
+
+
+def tree_algorithmic(N, n, H, dk, dv, s_io, s_gate, path_nodes):
+    """One speculative round over N trees of n nodes: verification reads the
+    committed state once and every node's q, k, v, beta, log alpha and writes
+    its output; the commit reads and writes the state once and reads k, v,
+    beta, log alpha of the accepted paths' nodes.  Flops: the chunk form per
+    node (the forward's count at chunk n) and 6 dk dv per committed step."""
+    state = N * H * dk * dv * 4
+    nodes = N * n * H
+    v_bytes = state + nodes * ((2 * dk + 2 * dv) * s_io + 2 * s_gate)
+    c_bytes = 2 * state + path_nodes * H * ((dk + dv) * s_io + 2 * s_gate)
+    v_flops = nodes * (6 * dk * dv + n * (3 * dk + 2 * dv) + n * n / 3.0)
+    c_flops = path_nodes * H * 6 * dk * dv
+    return v_bytes, c_bytes, v_flops, c_flops
+
+
+def cpu_baseline_tree(inp, parent, accepted, budget_s):
+    """The fp64 oracle's verification and commit on whole trees (all heads)
+    until about ``budget_s`` seconds; one BLAS thread.  Scaled to the
+    workload's nodes."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    f = inp.f64
+    N, n = f["q"].shape[:2]
+    par, acc = parent.numpy(), accepted.numpy()
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for m in range(N):
+            sl = slice(m, m + 1)
+            la = None if f["log_alpha"] is None else f["log_alpha"][sl]
+            oracle.tree_fwd(f["q"][sl], f["k"][sl], f["v"][sl], f["beta"][sl], la,
+                            par[sl], f["s0"][sl], inp.gate)
+            oracle.tree_commit(f["k"][sl], f["v"][sl], f["beta"][sl], la, par[sl], acc[sl],
+                               f["s0"][sl], inp.gate)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": done * n / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {N} trees of {n} nodes, all heads, verification and "
+                      f"commit ({dt:.1f} s, 1 thread)"}
+
+
+def main_tree(args):
+    """Speculative round on draft trees: gdn_tree_verify then gdn_tree_commit
+    on 256 trees of 16 nodes, H32, d128, bf16 (the decode batch with a
+    16-node draft tree per sequence)."""
+    import torch
+    import gated_delta_rule_79_amd as gdn
+    from gated_delta_rule_79_amd import synth
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    N, n, H, dk, dv = 256, 16, 32, 128, 128
+    wl = f"tree_n{N}_h{H}_w{n}"
+    inp, parent, accepted = synth.make_tree_inputs(N, n, H, dk, dv, dtype=torch.bfloat16,
+                                                   gate="scalar", chunk=n, seed=1007,
+                                                   s0_std=0.02)
+    d = inp.to("cuda")
+    par, acc = parent.cuda(), accepted.cuda()
+    state = d.s0.clone()
+    ws = torch.empty(max(1, gdn.tree_verify_workspace(d.q, d.v, d.beta, d.log_alpha, chunk=n)),
+                     dtype=torch.uint8, device="cuda")
+
+    def fn():
+        gdn.tree_verify(d.q, d.k, d.v, d.beta, d.log_alpha, par, state, chunk=n, workspace=ws)
+        gdn.tree_commit(d.k, d.v, d.beta, d.log_alpha, par, acc, state, chunk=n)
+
+    ms, cold = time_calls(fn, args.steps, args.warmup, args.cold_steps)
+    per = stage_pass(fn, args.steps)
+    depth = tree_depths(parent, n)
+    path_nodes = sum(depth[m][int(accepted[m])] for m in range(N))
+    vb, cb, vf, cf = tree_algorithmic(N, n, H, dk, dv, 2, 2, path_nodes)
+    names = {"fwd_prep": "fwd_prep_sg_kernel", "fwd_scan": "fwd_scan_kernel",
+             "tree_commit": "tree_commit_kernel"}
+    # the kernels' own algorithmic bytes: the commit's state stream; the
+    # scan reads the state, q and writes o; the prep reads k, v, beta, alpha
+    own = {"tree_commit": cb,
+           "fwd_scan": N * H * dk * dv * 4 + N * n * H * (dk + dv) * 2,
+           "fwd_prep": N * n * H * ((dk + dv) * 2 + 4)}
+    dom = max(per, key=per.get)
+    ach = own[dom] / (per[dom] * 1e-3) / 1e9
+    out = {
+        "metric": f"nodes/sec gdn_tree_verify + gdn_tree_commit (N={N},n={n},H={H},d={dk} "
+                  "bf16); % HBM roofline",
+        "value": round(N * n / (ms * 1e-3), 1), "unit": "nodes/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "cold_ms_per_step": None if cold is None else round(cold, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl, "trees": N, "nodes": n, "H": H, "dk": dk, "dv": dv,
+                   "chunk": n, "gate": "scalar", "accepted_path_nodes": path_nodes,
+                   "state": "fp32", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": names.get(dom, dom),
+                     "kernel_ms": {k: round(v, 5) for k, v in per.items()},
+                     "alg_bytes_per_launch": int(own[dom]),
+                     "alg_bytes_per_step": int(vb + cb), "alg_flops_per_step": int(vf + cf),
+                     "path_frac_hbm": round((vb + cb) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    cpu = None if args.no_cpu_baseline else cpu_baseline_tree(inp, parent, accepted,
+                                                              args.cpu_budget)
+    if cpu is not None:
+        cpu["value"] = round(cpu["value"], 1)
+    out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
 def main_other(args):
     """bwd, fwdbwd and decode modes."""
     import torch
@@ -442,7 +563,7 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="synthetic workload (default: fwd_t4096_h16 for the forward)")
     ap.add_argument("--mode", default="fwd",
-                    choices=("fwd", "bwd", "fwdbwd", "decode", "product"))
+                    choices=("fwd", "bwd", "fwdbwd", "decode", "product", "tree"))
     ap.add_argument("--nh", type=int, default=2,
                     help="delta steps per token for --mode product")
     ap.add_argument("--qk-l2norm", action="store_true",
@@ -465,6 +586,9 @@ def main():
 
     if args.mode == "product":
         main_product(args)
+        return
+    if args.mode == "tree":
+        main_tree(args)
         return
     if args.mode != "fwd":
         main_other(args)

@@ -138,6 +138,17 @@ def _check_tree_index(t, name, q):
         raise ValueError(f"{name} must be a contiguous int32 tensor on the inputs' device")
 
 
+def tree_verify_workspace(q, v, beta, log_alpha=None, chunk: int = 64,
+                          cu_seqlens=None) -> int:
+    """Workspace bytes of tree_verify for these inputs."""
+    lib = _lib.load()
+    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.gdn_tree_verify_workspace(ctypes.byref(p), ctypes.byref(need)),
+               "gdn_tree_verify_workspace")
+    return need.value
+
+
 def tree_verify(q, k, v, beta, log_alpha, parent, state=None, chunk: int = 64,
                 cu_seqlens=None, workspace: Optional[torch.Tensor] = None):
     """Outputs of every node of draft trees (gdn_tree_verify).  q, k [B,n,H,dk],
