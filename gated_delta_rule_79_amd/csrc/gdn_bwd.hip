@@ -315,6 +315,35 @@ __device__ __forceinline__ floatx4 tmma(FA A, FB B, int m0, int n0, int l16,
   return acc;
 }
 
+// acc += A B for the 16x16 tile at (m0, n0) with both operands stored with
+// the contraction index contiguous in the input dtype: A(m, k) = A[m][k],
+// B(k, n) = B[n][k], rows ld elements apart (16-byte aligned).  Each lane's
+// 8 K-slots are one 16-byte LDS read; slots past KD are zero.
+template <typename IO, int KD>
+__device__ __forceinline__ floatx4 rows_mma(const char* A, const char* B, int ld, int m0,
+                                            int n0, int l16, int lg, floatx4 acc) {
+#pragma unroll
+  for (int kb = 0; kb < (KD + 31) / 32; ++kb) {
+    const int k0 = kb * 32 + 8 * lg;
+    opvec<IO> a = zero_vec<IO>(), b = zero_vec<IO>();
+    if (k0 < KD) {
+      a = lds_vec8<IO>(A, size_t(m0 + l16) * ld + k0);
+      b = lds_vec8<IO>(B, size_t(n0 + l16) * ld + k0);
+    }
+    acc = mma32(a, b, acc);
+  }
+  return acc;
+}
+
+// Operand fragment of a 16-row block of a [rows][16] bf16 slab: lanes of K
+// groups 0 and 1 take 8 consecutive columns of row l16 (one 16-byte LDS
+// read), groups 2 and 3 the zero half of the 32-wide K block.
+__device__ __forceinline__ opvec<bf16_t> slab_row16(const __bf16* base, int l16, int lg) {
+  opvec<bf16_t> x = zero_vec<bf16_t>();
+  if (lg < 2) x = *reinterpret_cast<const opvec<bf16_t>*>(base + l16 * 16 + 8 * lg);
+  return x;
+}
+
 // 16x16 tile product over a 16-column value slab whose operands both keep
 // the contraction index contiguous in fp32 LDS: A(m, j) = A[m * ld + j],
 // B(j, n) = bs(n) * B[n * ld + j] (ld even).  Lanes of K groups 0 and 1 read
@@ -383,15 +412,26 @@ struct GradSmem {
   static constexpr size_t beta_off = mid_off + size_t(CH ? DK : 1) * 4;
   static constexpr size_t db_off = beta_off + size_t(C) * 4;
   static constexpr size_t dd_off = db_off + size_t(C) * 4;
+  // per-row decays gamma_r and e^{g_C - g_r} (per-token gates)
+  static constexpr size_t eq_off = dd_off + size_t(DK) * 4;
+  static constexpr size_t ek_off = eq_off + size_t(CH ? 0 : C) * 4;
   // tile partial sums: [0, NB*DK) column sums of dK~ (.) K~, then dA row
   // sums [NB][C], then dX row sums [NDT][C]; the slab phase uses [0, C)
-  static constexpr size_t part_off = dd_off + size_t(DK) * 4;
+  static constexpr size_t part_off = ek_off + size_t(CH ? 0 : C) * 4;
   static constexpr size_t part_a = size_t(NB) * DK;
   static constexpr size_t part_x = part_a + size_t(NB) * C;
   static constexpr size_t part_n = part_x + size_t(NDT) * C;
-  static constexpr size_t r_off = part_off + part_n * 4;
+  static constexpr size_t r_off = (part_off + part_n * 4 + 15) / 16 * 16;  // 16-byte rows
   // slab phase: V, dO, Z, E, dE [C][SW+1]; M0, dM1 [DK][SW+1]
-  static constexpr size_t slab_bytes = (5 * size_t(C) + 2 * size_t(DK)) * LDS_ * 4;
+  // per-token gates also keep M0 and dM1 transposed in the input dtype
+  // ([SW][LDK]), so that K M0 and K dM1 read both operands as 16-byte rows
+  static constexpr size_t slabt_bytes = CH ? 0 : 2 * size_t(SW) * LDK * ib;
+  // bf16 inputs with per-token gates also keep dO, diag(b) V, E, dE ([C][SW])
+  // and M0, dM1 ([DK][SW]) as bf16 rows for the contractions over the slab
+  static constexpr bool BROWS = !CH && ib == 2 && SW == 16;
+  static constexpr size_t slabb_bytes = BROWS ? (4 * size_t(C) + 2 * size_t(DK)) * SW * 2 : 0;
+  static constexpr size_t slab_bytes =
+      (5 * size_t(C) + 2 * size_t(DK)) * LDS_ * 4 + slabt_bytes + slabb_bytes;
   // post phase: dW, then dT T^T, then the gate gradient, each [C][DK+1]
   static constexpr size_t post_bytes = size_t(C) * (LDD > LDC ? LDD : LDC) * 4;
   static constexpr size_t r_bytes = slab_bytes > post_bytes ? slab_bytes : post_bytes;
@@ -434,6 +474,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   float* sbeta = reinterpret_cast<float*>(smem + S::beta_off);
   float* sdb = reinterpret_cast<float*>(smem + S::db_off);
   float* sdD = reinterpret_cast<float*>(smem + S::dd_off);
+  float* seq = reinterpret_cast<float*>(smem + S::eq_off);
+  float* sek = reinterpret_cast<float*>(smem + S::ek_off);
   float* spart = reinterpret_cast<float*>(smem + S::part_off);
   float* sR = reinterpret_cast<float*>(smem + S::r_off);
   // slab phase views
@@ -444,6 +486,15 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   float* sDE = sE + C * LS;
   float* sM0 = sDE + C * LS;
   float* sDM1 = sM0 + DK * LS;
+  char* sM0t = reinterpret_cast<char*>(sDM1 + DK * LS);    // [SW][LDK], !CH
+  char* sDM1t = sM0t + size_t(SW) * LDK * ib;
+  // bf16 slab rows (S::BROWS)
+  __bf16* sDOb = reinterpret_cast<__bf16*>(sDM1t + size_t(SW) * LDK * ib);
+  __bf16* sYb = sDOb + C * SW;
+  __bf16* sEb = sYb + C * SW;
+  __bf16* sDEb = sEb + C * SW;
+  __bf16* sM0b = sDEb + C * SW;
+  __bf16* sDM1b = sM0b + DK * SW;
   // post phase views
   float* sDW = sR;
 
@@ -512,6 +563,11 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       smid[cc] = 0.5f * (mx + mn);
       atomicMax(&s_span_bits, __float_as_int(0.5f * (mx - mn)));
     }
+  } else if constexpr (SC) {
+    if (tid < C) {
+      seq[tid] = expf(sg[tid]);
+      sek[tid] = expf(sg[C - 1] - sg[tid]);
+    }
   }
   __syncthreads();
 
@@ -521,12 +577,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   // decays: gamma_r (per row / per (row, channel)), chunk-end relative decay
   auto gq = [&](int r, int d) -> float {
     if constexpr (CH) return expf(sg[r * DK + d]);
-    else if constexpr (SC) return expf(sg[r]);
+    else if constexpr (SC) return seq[r];
     else return 1.f;
   };
   auto gk = [&](int r, int d) -> float {
     if constexpr (CH) return expf(sg[(C - 1) * DK + d] - sg[r * DK + d]);
-    else if constexpr (SC) return expf(sg[C - 1] - sg[r]);
+    else if constexpr (SC) return sek[r];
     else return 1.f;
   };
   auto gl = [&](int d) -> float {
@@ -692,6 +748,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
         if (e < C * SW) {
           sV[(e / SW) * LS + e % SW] = vv[u];
           sDO[(e / SW) * LS + e % SW] = gg[u];
+          if constexpr (S::BROWS) {
+            sDOb[e] = static_cast<__bf16>(gg[u]);
+            sYb[e] = static_cast<__bf16>(sbeta[e / SW] * vv[u]);
+          }
         }
       }
 #pragma unroll
@@ -699,7 +759,15 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
         const int e = tid + 256 * u;
         if (e < DK * SW) {
           sM0[(e / SW) * LS + e % SW] = mm[u];
+          if constexpr (S::BROWS) {
+            sM0b[e] = static_cast<__bf16>(mm[u]);
+            sDM1b[e] = static_cast<__bf16>(dd[u]);
+          }
           sDM1[(e / SW) * LS + e % SW] = dd[u];
+          if constexpr (!CH) {
+            lds_st<IO>(sM0t, size_t(e % SW) * LDK + e / SW, mm[u]);
+            lds_st<IO>(sDM1t, size_t(e % SW) * LDK + e / SW, dd[u]);
+          }
         }
       }
     }
@@ -709,23 +777,46 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       const int tt = t % NCS, mt = tt / (SW / 16), nt = tt % (SW / 16);
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
       if (t < NCS) {
-        acc = tmma<OP, DK>(Xr, [&](int d, int j) { return sM0[d * LS + j]; },
-                           16 * mt, 16 * nt, l16, lg, acc);
+        if constexpr (!CH) {
+          // X M0 = diag(b gamma) (K M0): the row scale goes on the result
+          acc = rows_mma<IO, DK>(sK, sM0t, LDK, 16 * mt, 16 * nt, l16, lg, acc);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int r = 16 * mt + 4 * lg + s, j = 16 * nt + l16;
-          sZ[r * LS + j] = sbeta[r] * sV[r * LS + j] - acc[s];
+          for (int s = 0; s < 4; ++s) {
+            const int r = 16 * mt + 4 * lg + s, j = 16 * nt + l16;
+            sZ[r * LS + j] = sbeta[r] * (sV[r * LS + j] - gq(r, 0) * acc[s]);
+          }
+        } else {
+          acc = tmma<OP, DK>(Xr, [&](int d, int j) { return sM0[d * LS + j]; },
+                             16 * mt, 16 * nt, l16, lg, acc);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int r = 16 * mt + 4 * lg + s, j = 16 * nt + l16;
+            sZ[r * LS + j] = sbeta[r] * sV[r * LS + j] - acc[s];
+          }
         }
       } else {
         acc = tmma<OP, C>([&](int i, int r) { return sP[r * LDC + i]; },
                           [&](int r, int j) { return sDO[r * LS + j]; },
                           16 * mt, 16 * nt, l16, lg, acc);
-        acc = tmma<OP, DK>([&](int i, int d) { return Kr(i, d) * gk(i, d); },
-                           [&](int d, int j) { return sDM1[d * LS + j]; },
-                           16 * mt, 16 * nt, l16, lg, acc);
+        if constexpr (!CH) {
+          // K~ dM1 = diag(e^{g_C - g}) (K dM1)
+          floatx4 a2 = {0.f, 0.f, 0.f, 0.f};
+          a2 = rows_mma<IO, DK>(sK, sDM1t, LDK, 16 * mt, 16 * nt, l16, lg, a2);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc[s] += gk(16 * mt + 4 * lg + s, 0) * a2[s];
+        } else {
+          acc = tmma<OP, DK>([&](int i, int d) { return Kr(i, d) * gk(i, d); },
+                             [&](int d, int j) { return sDM1[d * LS + j]; },
+                             16 * mt, 16 * nt, l16, lg, acc);
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           sDE[(16 * mt + 4 * lg + s) * LS + 16 * nt + l16] = acc[s];
+        if constexpr (S::BROWS) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            sDEb[(16 * mt + 4 * lg + s) * SW + 16 * nt + l16] = static_cast<__bf16>(acc[s]);
+        }
       }
     }
     __syncthreads();
@@ -740,6 +831,11 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           sE[(16 * mt + 4 * lg + s) * LS + 16 * nt + l16] = acc[s];
+        if constexpr (S::BROWS) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            sEb[(16 * mt + 4 * lg + s) * SW + 16 * nt + l16] = static_cast<__bf16>(acc[s]);
+        }
       } else {
         acc = tmma<OP, C>([&](int i, int r) { return sT[r * LDC + i]; },
                           [&](int r, int j) { return sDE[r * LS + j]; },
@@ -777,7 +873,16 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       const int t = wave + 4 * u;
       if (t >= NCD) continue;
       const int mt = t / NDT, nt = t % NDT;
-      if constexpr (LS % 2 == 0 && SW == 16) {
+      if constexpr (S::BROWS) {
+        const opvec<OP> fdo = slab_row16(sDOb + 16 * mt * SW, l16, lg);
+        const opvec<OP> fde = slab_row16(sDEb + 16 * mt * SW, l16, lg);
+        const opvec<OP> fe = slab_row16(sEb + 16 * mt * SW, l16, lg);
+        const opvec<OP> fm = slab_row16(sM0b + 16 * nt * SW, l16, lg);
+        const opvec<OP> fd = slab_row16(sDM1b + 16 * nt * SW, l16, lg);
+        aQ[u] = mma32(fdo, fm, aQ[u]);
+        aW[u] = mma32(fde, fm, aW[u]);
+        aK[u] = mma32(fe, fd, aK[u]);
+      } else if constexpr (LS % 2 == 0 && SW == 16) {
         aQ[u] = slab_mma<OP>(sDO + 16 * mt * LS, sM0 + 16 * nt * LS, LS, 1.f, l16, lg, aQ[u]);
         aW[u] = slab_mma<OP>(sDE + 16 * mt * LS, sM0 + 16 * nt * LS, LS, 1.f, l16, lg, aW[u]);
         aK[u] = slab_mma<OP>(sE + 16 * mt * LS, sDM1 + 16 * nt * LS, LS, 1.f, l16, lg, aK[u]);
@@ -797,7 +902,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       const int t = wave + 4 * u;
       if (t >= NCC) continue;
       const int mt = t / NB, nt = t % NB;
-      if constexpr (LS % 2 == 0 && SW == 16) {
+      if constexpr (S::BROWS) {
+        aP[u] = mma32(slab_row16(sDOb + 16 * mt * SW, l16, lg),
+                      slab_row16(sEb + 16 * nt * SW, l16, lg), aP[u]);
+        aT[u] = mma32(slab_row16(sDEb + 16 * mt * SW, l16, lg),
+                      slab_row16(sYb + 16 * nt * SW, l16, lg), aT[u]);
+      } else if constexpr (LS % 2 == 0 && SW == 16) {
         aP[u] = slab_mma<OP>(sDO + 16 * mt * LS, sE + 16 * nt * LS, LS, 1.f, l16, lg, aP[u]);
         aT[u] = slab_mma<OP>(sDE + 16 * mt * LS, sV + 16 * nt * LS, LS,
                              sbeta[16 * nt + l16], l16, lg, aT[u]);
