@@ -715,33 +715,37 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 #pragma unroll
   for (int u = 0; u < NUC; ++u) aP[u] = aT[u] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // slab loads in registers: the next slab's are issued as soon as the
+  // current one is in LDS, so they travel while the slab is processed
+  constexpr int NVE = (C * SW + 255) / 256, NME = (DK * SW + 255) / 256;
+  float vv[NVE], gg[NVE], mm[NME], dd[NME];
+  auto load_slab = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < NVE; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / SW, j = e % SW;
+      vv[u] = gg[u] = 0.f;
+      if (e < C * SW && r < len) {
+        const int64_t off = ((tok0 + r) * H + h) * dv + s0 + j;
+        vv[u] = io<IO>::load(v, off);
+        gg[u] = io<IO>::load(d_o, off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NME; ++u) {
+      const int e = tid + 256 * u;
+      const int d = e / SW, j = e % SW;
+      mm[u] = dd[u] = 0.f;
+      if (e < DK * SW) {
+        mm[u] = M0g[static_cast<int64_t>(d) * dv + s0 + j];
+        dd[u] = dM1g[static_cast<int64_t>(d) * dv + s0 + j];
+      }
+    }
+  };
+  load_slab(0);
   for (int s0 = 0; s0 < dv; s0 += SW) {
     // stage V, dO (rows of the chunk) and M0, dM1 (rows dk) for this slab
     {
-      // every load of the slab is issued before its LDS stores
-      constexpr int NVE = (C * SW + 255) / 256, NME = (DK * SW + 255) / 256;
-      float vv[NVE], gg[NVE], mm[NME], dd[NME];
-#pragma unroll
-      for (int u = 0; u < NVE; ++u) {
-        const int e = tid + 256 * u;
-        const int r = e / SW, j = e % SW;
-        vv[u] = gg[u] = 0.f;
-        if (e < C * SW && r < len) {
-          const int64_t off = ((tok0 + r) * H + h) * dv + s0 + j;
-          vv[u] = io<IO>::load(v, off);
-          gg[u] = io<IO>::load(d_o, off);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NME; ++u) {
-        const int e = tid + 256 * u;
-        const int d = e / SW, j = e % SW;
-        mm[u] = dd[u] = 0.f;
-        if (e < DK * SW) {
-          mm[u] = M0g[static_cast<int64_t>(d) * dv + s0 + j];
-          dd[u] = dM1g[static_cast<int64_t>(d) * dv + s0 + j];
-        }
-      }
 #pragma unroll
       for (int u = 0; u < NVE; ++u) {
         const int e = tid + 256 * u;
@@ -771,6 +775,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
         }
       }
     }
+    if (s0 + SW < dv) load_slab(s0 + SW);
     __syncthreads();
     // Z = Y - X M0 (Y = diag(b) V),  dE = P^T dO + K~ dM1
     for (int t = wave; t < 2 * NCS; t += 4) {
