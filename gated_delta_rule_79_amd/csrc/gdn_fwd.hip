@@ -191,7 +191,7 @@ hipError_t run_fwd(const Problem& p, const void* q, const void* k,
                          p.gdt == GDN_BF16, buf);
     else
       hipLaunchKernelGGL((fwd_prep_sg_kernel<C, DK, IO, GATE>),
-                         dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(64 * kPrepWaves),
+                         dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(64 * prep_waves(C)),
                          0, s, map, p.H, p.dv, p.nchunks, q, k, v, beta, la,
                          p.gdt == GDN_BF16, buf, p.lnh, p.qknorm, p.parent);
     e = hipGetLastError();

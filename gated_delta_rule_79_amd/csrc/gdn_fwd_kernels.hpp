@@ -834,7 +834,9 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
 //     diagonal on fp32 MFMA:  T_ba = -T_bb sum_{a <= j < b} A_bj T_ja;
 //   - W^T = X^T T^T and U = T Y on the matrix cores in the operand type;
 //   - decays as exp2 of base-2 cumulative log gates.
-constexpr int kPrepWaves = 8;  // waves of the per-token-gate prep
+// waves of the per-token-gate prep: a 16- or 32-token chunk has too few
+// tiles for eight waves, and smaller workgroups keep more chunks in flight
+constexpr int prep_waves(int C) { return C == 16 ? 2 : (C == 32 ? 4 : 8); }
 
 template <int C, int DK, typename IO>
 struct PrepSgSmem {
@@ -876,7 +878,7 @@ struct PrepSgSmem {
 // chunk is not meaningful for a tree: its decays are set to zero.  Parent
 // entries outside [-1, r) are read as -1.
 template <int C, int DK, typename IO, int GATE>
-__global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
+__global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
@@ -925,7 +927,8 @@ __global__ __launch_bounds__(64 * kPrepWaves) void fwd_prep_sg_kernel(
   constexpr int NT2 = NB * (NB + 1) / 2;
   constexpr int NPF = NB == 1 ? 1 : (NB == 2 ? 2 : 6);
   constexpr int JOBS = NT2 + NPF;
-  constexpr int PW = kPrepWaves, NT = 64 * PW;
+  constexpr int PW = prep_waves(C), NT = 64 * PW;
+  static_assert(PW >= C / 16 - 1 && NT >= C, "prep waves per chunk size");
   constexpr int MAXJ = (JOBS + PW - 1) / PW;
   auto p_job = [&](int job, int* rt, int* jb) {
     int f = job - NT2;
