@@ -16,6 +16,7 @@ Other entry points (same JSON shape, their own metric string):
     --mode decode   gdn_decode_step in place (default workload decode_n256_h32)
     --mode product  gdn_chunk_fwd_product (Householder products, --nh steps)
     --mode tree     gdn_tree_verify + gdn_tree_commit (one speculative round)
+    --mode decode_product  gdn_decode_step_product (--nh steps per token)
     --qk-l2norm     (forward) gdn_chunk_fwd_qknorm on q, k rows that are not
                     unit vectors (log-uniform row scales in [0.05, 20])
 
@@ -413,6 +414,49 @@ def main_tree(args):
     print(json.dumps(out), flush=True)
 
 
+def main_decode_product(args):
+    """Decode step with nh delta steps per token (gdn_decode_step_product) on
+    the decode batch: N256 H32 d128 bf16, state fp32 in place."""
+    import torch
+    import gated_delta_rule_79_amd as gdn
+    from gated_delta_rule_79_amd import synth
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    N, H, dk, dv, nh = 256, 32, 128, 128, args.nh
+    wl = f"decode_product_n{N}_h{H}_nh{nh}"
+    inp = synth.make_product_inputs(N, 1, H, dk, dv, nh, dtype=torch.bfloat16,
+                                    gate="scalar", chunk=16, seed=1008, s0_std=0.02)
+    d = inp.to("cuda")
+    q, k, v = d.q[:, 0].contiguous(), d.k[:, 0].contiguous(), d.v[:, 0].contiguous()
+    beta, la = d.beta[:, 0].contiguous(), d.log_alpha[:, 0].contiguous()
+    state = d.s0.clone()
+    fn = lambda: gdn.decode_step_product(q, k, v, beta, la, state)
+    ms, cold = time_calls(fn, args.steps, args.warmup, args.cold_steps)
+    per = stage_pass(fn, args.steps)
+    kms = per.get("decode", ms)
+    # state read + written (fp32), q, o, and per step k, v, beta; the gate
+    byts = N * H * (8 * dk * dv + (dk + dv) * 2 + nh * ((dk + dv) * 2 + 2) + 2)
+    gbs = byts / (kms * 1e-3) / 1e9
+    out = {
+        "metric": f"tokens/sec gdn_decode_step_product (N={N},H={H},d={dk},nh={nh}); % HBM",
+        "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "cold_ms_per_step": None if cold is None else round(cold, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl, "N": N, "H": H, "dk": dk, "dv": dv, "nh": nh,
+                   "gate": "scalar", "state": "fp32", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_product_kernel",
+                     "kernel_ms": {k2: round(v2, 5) for k2, v2 in per.items()},
+                     "alg_bytes_per_launch": int(byts)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main_other(args):
     """bwd, fwdbwd and decode modes."""
     import torch
@@ -563,7 +607,8 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="synthetic workload (default: fwd_t4096_h16 for the forward)")
     ap.add_argument("--mode", default="fwd",
-                    choices=("fwd", "bwd", "fwdbwd", "decode", "product", "tree"))
+                    choices=("fwd", "bwd", "fwdbwd", "decode", "product", "tree",
+                             "decode_product"))
     ap.add_argument("--nh", type=int, default=2,
                     help="delta steps per token for --mode product")
     ap.add_argument("--qk-l2norm", action="store_true",
@@ -589,6 +634,9 @@ def main():
         return
     if args.mode == "tree":
         main_tree(args)
+        return
+    if args.mode == "decode_product":
+        main_decode_product(args)
         return
     if args.mode != "fwd":
         main_other(args)

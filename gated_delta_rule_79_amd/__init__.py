@@ -24,7 +24,8 @@ import torch
 from . import _lib
 from ._lib import GdnError  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "chunk_fwd_product", "tree_verify",
+__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "decode_step_product",
+           "chunk_fwd_product", "tree_verify",
            "tree_commit", "FwdPlan", "GdnError", "set_segment_chunks",
            "abi_version", "stage_times"]
 
@@ -136,6 +137,30 @@ def chunk_fwd_product(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
 def _check_tree_index(t, name, q):
     if t.dtype != torch.int32 or t.device != q.device or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous int32 tensor on the inputs' device")
+
+
+def decode_step_product(q, k, v, beta, log_alpha, state):
+    """One token per sequence with nh delta steps (gdn_decode_step_product):
+    q [N, H, dk], k [N, nh, H, dk], v [N, nh, H, dv], beta [N, nh, H],
+    log_alpha [N, H] or None; ``state`` [N, H, dk, dv] fp32 is updated in
+    place.  Returns o [N, H, dv]."""
+    lib = _lib.load()
+    N, H, dk = q.shape
+    nh, dv = k.shape[1], v.shape[-1]
+    p = _lib.GdnProblem()
+    p.B, p.T, p.H, p.dk, p.dv, p.chunk, p.nseq = N, 1, H, dk, dv, 0, 0
+    p.cu_seqlens = None
+    p.io_dtype = _dtype_code(q)
+    p.gate_dtype = _dtype_code(beta)
+    p.gate = _gate_of(log_alpha, 2)
+    if state.dtype != torch.float32:
+        raise TypeError("state must be fp32")
+    o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    st = lib.gdn_decode_step_product(ctypes.byref(p), nh, _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(beta), _ptr(log_alpha), _ptr(state), _ptr(o),
+                                     _stream(q.device))
+    _lib.check(st, "gdn_decode_step_product")
+    return o
 
 
 def tree_verify_workspace(q, v, beta, log_alpha=None, chunk: int = 64,

@@ -24,7 +24,7 @@ EXPORTED = (
     "gdn_profile_read", "gdn_set_segment_chunks",
     "gdn_chunk_fwd_product_workspace", "gdn_chunk_fwd_product",
     "gdn_chunk_fwd_qknorm", "gdn_tree_verify_workspace", "gdn_tree_verify",
-    "gdn_tree_commit",
+    "gdn_tree_commit", "gdn_decode_step_product",
 )
 STAGE_COUNT = 11
 STAGES = ("chunk_map", "fwd_prep", "fwd_scan", "decode", "bwd_states",
@@ -97,6 +97,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_tree_verify_workspace.argtypes = [pp, ctypes.POINTER(sz)]
     lib.gdn_tree_verify.restype = i32
     lib.gdn_tree_verify.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_decode_step_product.restype = i32
+    lib.gdn_decode_step_product.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_tree_commit.restype = i32
     lib.gdn_tree_commit.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
     if path is None:

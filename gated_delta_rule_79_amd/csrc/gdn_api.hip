@@ -548,4 +548,43 @@ gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k,
   }
 }
 
+gdn_status gdn_decode_step_product(const gdn_problem* p, int32_t nh, const void* q,
+                                   const void* k, const void* v, const void* beta,
+                                   const void* log_alpha, float* state, void* o,
+                                   void* stream) {
+  try {
+    if (p == nullptr) return GDN_ERR_NULL;
+    if (!dtype_ok(p->io_dtype) || !dtype_ok(p->gate_dtype)) return GDN_ERR_DTYPE;
+    if (p->gate != GDN_GATE_NONE && p->gate != GDN_GATE_SCALAR) return GDN_ERR_UNSUPPORTED;
+    if (nh != 1 && nh != 2 && nh != 4) return GDN_ERR_UNSUPPORTED;
+    if (p->B < 1 || p->H < 1) return GDN_ERR_SHAPE;
+    if (!dk_ok(p->dk) || !dv_ok(p->dv)) return GDN_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(p->B) * p->H > (int64_t(1) << 31) - 1) return GDN_ERR_SHAPE;
+    gdn::Problem pp{};
+    pp.B = p->B;
+    pp.T = 1;
+    pp.H = p->H;
+    pp.dk = p->dk;
+    pp.dv = p->dv;
+    pp.nseq = p->B;
+    pp.io = p->io_dtype;
+    pp.gdt = p->gate_dtype;
+    pp.gate = p->gate;
+    const int64_t nhd = static_cast<int64_t>(p->B) * p->H;
+    GDN_TRY(need(q, nhd * p->dk));
+    GDN_TRY(need(k, nhd * nh * p->dk));
+    GDN_TRY(need(v, nhd * nh * p->dv));
+    GDN_TRY(need(beta, nhd * nh));
+    if (pp.gate != GDN_GATE_NONE) GDN_TRY(need(log_alpha, nhd));
+    else GDN_TRY(opt(log_alpha));
+    GDN_TRY(need(state, nhd * p->dk * p->dv));
+    GDN_TRY(need(o, nhd * p->dv));
+    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    return launched(gdn::launch_decode_product(pp, nh, q, k, v, beta, log_alpha, state, o,
+                                               static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
 }  // extern "C"

@@ -118,6 +118,114 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   }
 }
 
+// Decode with Householder-product transitions: nh (k, v, beta) triples per
+// token, one decay, nh delta steps in order, the output read after the last.
+// One wave per (sequence, head, 64-column slab): lane (rg, cg) keeps rows
+// rg, rg + 4, .. (DK / 4 of them) of columns 4 cg .. 4 cg + 3 in registers,
+// each step's k-projection is reduced over the four row groups with two
+// shuffles, so the nh steps need no LDS and no barrier and the state still
+// crosses HBM once each way.
+template <int DK, typename IO, typename GT, int GATE>
+__global__ __launch_bounds__(64) void decode_product_kernel(
+    int H, int dv, int nh, const void* __restrict__ q, const void* __restrict__ k,
+    const void* __restrict__ v, const void* __restrict__ beta,
+    const void* __restrict__ la, float* __restrict__ state, void* __restrict__ o) {
+  constexpr int RPT = DK / 4;
+  const int nhd = blockIdx.x;  // n * H + h
+  const int n = nhd / H, h = nhd - n * H;
+  const int lane = threadIdx.x;
+  const int cg = lane & 15, rg = lane >> 4;
+  const int col = blockIdx.y * kSlab + cg * 4;
+  const bool active = col < dv;  // dv is a multiple of 16: whole lane groups
+  float* M = state + static_cast<int64_t>(nhd) * DK * dv;
+  floatx4 mm[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j)
+    mm[j] = active ? __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(
+                         M + static_cast<int64_t>(rg + 4 * j) * dv + col))
+                   : floatx4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (GATE == GDN_GATE_SCALAR) {
+    const float a = expf(io<GT>::load(la, nhd));
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) mm[j] *= a;
+  }
+  for (int st = 0; st < nh; ++st) {
+    const int64_t sh = (static_cast<int64_t>(n) * nh + st) * H + h;  // [N, nh, H]
+    float kr[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) kr[j] = io<IO>::load(k, sh * DK + rg + 4 * j);
+    const float b = io<GT>::load(beta, sh);
+    floatx4 vv = {0.f, 0.f, 0.f, 0.f};
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) vv[c] = io<IO>::load(v, sh * dv + col + c);
+    }
+    floatx4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) u += mm[j] * kr[j];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u[c] += __shfl_xor(u[c], 16, 64);
+      u[c] += __shfl_xor(u[c], 32, 64);
+    }
+    const floatx4 e = b * (vv - u);
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) mm[j] += kr[j] * e;
+  }
+  // o = M^T q after the last step
+  floatx4 w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < RPT; ++j)
+    w += mm[j] * io<IO>::load(q, static_cast<int64_t>(nhd) * DK + rg + 4 * j);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    w[c] += __shfl_xor(w[c], 16, 64);
+    w[c] += __shfl_xor(w[c], 32, 64);
+  }
+  if (!active) return;
+  if (rg == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) io<IO>::store(o, static_cast<int64_t>(nhd) * dv + col + c, w[c]);
+  }
+#pragma unroll
+  for (int j = 0; j < RPT; ++j)
+    __builtin_nontemporal_store(
+        mm[j], reinterpret_cast<floatx4*>(M + static_cast<int64_t>(rg + 4 * j) * dv + col));
+}
+
+template <int DK, typename IO, typename GT>
+hipError_t dispatch_product(const Problem& p, int nh, const void* q, const void* k,
+                            const void* v, const void* beta, const void* la,
+                            float* state, void* o, hipStream_t s) {
+  StageScope scope(GDN_STAGE_DECODE, s);
+  const dim3 grid(static_cast<unsigned>(p.B * p.H), (p.dv + kSlab - 1) / kSlab);
+  if (p.gate == GDN_GATE_SCALAR)
+    hipLaunchKernelGGL((decode_product_kernel<DK, IO, GT, GDN_GATE_SCALAR>), grid, dim3(64),
+                       0, s, p.H, p.dv, nh, q, k, v, beta, la, state, o);
+  else
+    hipLaunchKernelGGL((decode_product_kernel<DK, IO, GT, GDN_GATE_NONE>), grid, dim3(64),
+                       0, s, p.H, p.dv, nh, q, k, v, beta, la, state, o);
+  return hipGetLastError();
+}
+
+template <int DK, typename IO>
+hipError_t product_gdt(const Problem& p, int nh, const void* q, const void* k,
+                       const void* v, const void* beta, const void* la, float* state,
+                       void* o, hipStream_t s) {
+  if (p.gdt == GDN_BF16)
+    return dispatch_product<DK, IO, bf16_t>(p, nh, q, k, v, beta, la, state, o, s);
+  return dispatch_product<DK, IO, f32_t>(p, nh, q, k, v, beta, la, state, o, s);
+}
+
+template <int DK>
+hipError_t product_io(const Problem& p, int nh, const void* q, const void* k,
+                      const void* v, const void* beta, const void* la, float* state,
+                      void* o, hipStream_t s) {
+  if (p.io == GDN_BF16)
+    return product_gdt<DK, bf16_t>(p, nh, q, k, v, beta, la, state, o, s);
+  return product_gdt<DK, f32_t>(p, nh, q, k, v, beta, la, state, o, s);
+}
+
 template <int DK, typename IO, typename GT>
 hipError_t dispatch_gate(const Problem& p, dim3 grid, const void* q,
                          const void* k, const void* v, const void* beta,
@@ -162,6 +270,17 @@ hipError_t dispatch_io(const Problem& p, dim3 grid, const void* q,
 }
 
 }  // namespace
+
+hipError_t launch_decode_product(const Problem& p, int nh, const void* q, const void* k,
+                                 const void* v, const void* beta, const void* la,
+                                 float* state, void* o, hipStream_t s) {
+  switch (p.dk) {
+    case 16: return product_io<16>(p, nh, q, k, v, beta, la, state, o, s);
+    case 32: return product_io<32>(p, nh, q, k, v, beta, la, state, o, s);
+    case 64: return product_io<64>(p, nh, q, k, v, beta, la, state, o, s);
+    default: return product_io<128>(p, nh, q, k, v, beta, la, state, o, s);
+  }
+}
 
 hipError_t launch_decode(const Problem& p, const void* q, const void* k,
                          const void* v, const void* beta, const void* la,

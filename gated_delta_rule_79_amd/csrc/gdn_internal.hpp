@@ -55,6 +55,11 @@ hipError_t launch_decode(const Problem& p, const void* q, const void* k,
                          const void* v, const void* beta, const void* la,
                          float* state, void* o, hipStream_t s);
 
+// Decode with Householder-product transitions (gdn_decode.hip).
+hipError_t launch_decode_product(const Problem& p, int nh, const void* q, const void* k,
+                                 const void* v, const void* beta, const void* la,
+                                 float* state, void* o, hipStream_t s);
+
 // Draft-tree commit (gdn_tree.hip).
 hipError_t launch_tree_commit(const Problem& p, const int32_t* parent,
                               const int32_t* accepted, const void* k, const void* v,

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum {
   GDN_OK = 0,
@@ -245,6 +245,22 @@ gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k,
                            const void* v, const void* beta,
                            const void* log_alpha, float* state, void* o,
                            void* stream);
+
+/* Decode step with Householder-product transitions (the serving side of
+ * gdn_chunk_fwd_product; same reading of the GDN review's "Future work"):
+ * per (sequence, head) the state is decayed once by alpha, takes the nh
+ * delta-rule steps of the token in order, and o = S q is read after the
+ * last one; the state is updated in place.
+ *   nh        : 1, 2 or 4 (else GDN_ERR_UNSUPPORTED).
+ *   q [N, H, dk]; k [N, nh, H, dk]; v [N, nh, H, dv]; beta [N, nh, H];
+ *   log_alpha [N, H] (scalar gate) or NULL (gate none); the per-channel
+ *   gate is GDN_ERR_UNSUPPORTED.  state [N, H, dk, dv] fp32 in/out;
+ *   o [N, H, dv] in io_dtype.  p->B = N; T, chunk and varlen fields are
+ *   ignored. */
+gdn_status gdn_decode_step_product(const gdn_problem* p, int32_t nh, const void* q,
+                                   const void* k, const void* v, const void* beta,
+                                   const void* log_alpha, float* state, void* o,
+                                   void* stream);
 
 /* Stage timing, for benchmarks and profiling.  While enabled, every kernel
  * the library enqueues is bracketed by a pair of HIP events recorded on the

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 5
+    assert lib.gdn_abi_version() == 6
     for s in range(8):
         txt = lib.gdn_status_str(s).decode()
         assert txt.startswith("GDN_")
@@ -320,3 +320,19 @@ def test_tree_rejections_before_launch(lib):
                                None) == _lib.GDN_ERR_NULL
     assert lib.gdn_tree_commit(ctypes.byref(prob(T=40, chunk=32)), A, A, A, A, A, A, A,
                                None) == _lib.GDN_ERR_SHAPE
+
+
+def test_decode_product_rejections(lib):
+    """Product decode: nh outside {1, 2, 4} and the per-channel gate are
+    rejected, null pointers caught, before any launch."""
+    p = prob(B=4, T=1)
+    for nh in (0, 3, 8):
+        assert lib.gdn_decode_step_product(ctypes.byref(p), nh, A, A, A, A, A, A, A,
+                                           None) == _lib.GDN_ERR_UNSUPPORTED
+    pc = prob(B=4, T=1, gate=_lib.GDN_GATE_CHANNEL)
+    assert lib.gdn_decode_step_product(ctypes.byref(pc), 2, A, A, A, A, A, A, A,
+                                       None) == _lib.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_decode_step_product(ctypes.byref(p), 2, None, A, A, A, A, A, A,
+                                       None) == _lib.GDN_ERR_NULL
+    assert lib.gdn_decode_step_product(ctypes.byref(p), 2, A, A, A, A, A, None, A,
+                                       None) == _lib.GDN_ERR_NULL

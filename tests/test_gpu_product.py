@@ -94,3 +94,67 @@ def test_product_rejects(gpu_lib):
     with pytest.raises(_lib.GdnError) as e:
         gdn.chunk_fwd_product(d.q, d.k, d.v, d.beta, d.log_alpha)
     assert e.value.status == _lib.GDN_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------ decode step ---
+
+def _decode_inputs(N, H, dk, dv, nh, dtype, gate, seed, beta_scale=1.0):
+    inp = synth.make_product_inputs(N, 1, H, dk, dv, nh, dtype=dtype, gate=gate,
+                                    chunk=16, seed=seed, s0_std=0.3)
+    if beta_scale != 1.0:       # beta in (0, beta_scale): negative eigenvalues
+        inp.beta = (inp.beta.double() * beta_scale).to(inp.beta.dtype)
+        inp.f64["beta"] = inp.beta.double().numpy()
+    return inp
+
+
+@pytest.mark.parametrize("nh", [1, 2, 4])
+@pytest.mark.parametrize("gate", ["scalar", "none"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_product_decode(gpu_lib, nh, gate, dtype):
+    inp = _decode_inputs(5, 3, 128, 96, nh, dtype, gate, seed=65, beta_scale=2.0)
+    log(f"[product decode] nh={nh} gate={gate} dtype={dtype}")
+    d = dev(inp)
+    state = d.s0.clone()
+    la = None if d.log_alpha is None else d.log_alpha[:, 0].contiguous()
+    o = gdn.decode_step_product(d.q[:, 0].contiguous(), d.k[:, 0].contiguous(),
+                                d.v[:, 0].contiguous(), d.beta[:, 0].contiguous(), la, state)
+    torch.cuda.synchronize()
+    f = inp.f64
+    o_ref, s_ref = oracle.deltaproduct_fwd(f["q"], f["k"], f["v"], f["beta"], f["log_alpha"],
+                                           f["s0"], gate)
+    eo = np.max(np.abs(np64(o) - o_ref[:, 0])) / np.max(np.abs(o_ref))
+    es = state_err(np64(state), s_ref)
+    log(f"    err o={eo:.3e} state={es:.3e}")
+    # the step runs in fp32 on the stored values: only the output's rounding
+    # to the input dtype separates it from the oracle
+    assert eo < (1e-5 if dtype == torch.float32 else 1e-2) and es < 1e-5, (eo, es)
+
+
+def test_product_decode_steps_equal_the_chunked_forward(gpu_lib):
+    # T decode steps from S0 give the chunked forward's outputs and state
+    T, nh = 23, 2
+    inp = synth.make_product_inputs(2, T, 2, 64, 64, nh, dtype=torch.float32,
+                                    gate="scalar", chunk=16, seed=66, s0_std=0.2)
+    d = dev(inp)
+    o_ref, s_ref = gdn.chunk_fwd_product(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, chunk=16)
+    state = d.s0.clone()
+    outs = []
+    for t in range(T):
+        outs.append(gdn.decode_step_product(
+            d.q[:, t].contiguous(), d.k[:, t].contiguous(), d.v[:, t].contiguous(),
+            d.beta[:, t].contiguous(), d.log_alpha[:, t].contiguous(), state))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=1)
+    e = max(slice_err(np64(o), np64(o_ref)), state_err(np64(state), np64(s_ref)))
+    log(f"[product decode] {T} steps vs chunked forward: {e:.3e}")
+    assert e < 1e-4
+
+
+@pytest.mark.parametrize("nh", [2, 4])
+def test_product_forward_beta_up_to_two(gpu_lib, nh):
+    # beta in (0, 2): each factor I - beta k k^T may have a negative eigenvalue
+    inp = synth.make_product_inputs(1, 130, 2, 64, 64, nh, dtype=torch.float32,
+                                    gate="scalar", chunk=64, seed=67, s0_std=0.2)
+    inp.beta = inp.beta * 2.0
+    inp.f64["beta"] = inp.beta.double().numpy()
+    check(inp, name="beta in (0, 2)")
