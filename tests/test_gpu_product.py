@@ -158,3 +158,33 @@ def test_product_forward_beta_up_to_two(gpu_lib, nh):
     inp.beta = inp.beta * 2.0
     inp.f64["beta"] = inp.beta.double().numpy()
     check(inp, name="beta in (0, 2)")
+
+
+def test_product_headline_size(gpu_lib):
+    # the benchmark's workload: T=4096, H=16, d=128, 2 steps per token, bf16;
+    # every head against the oracle
+    inp = synth.make_product_inputs(1, 4096, 16, 128, 128, 2, dtype=torch.bfloat16,
+                                    gate="scalar", chunk=64, seed=1006)
+    check(inp, name="t4096_h16_nh2")
+
+
+def test_product_decode_batch_sampled(gpu_lib):
+    # the benchmark's decode batch (N256 H32 d128, 2 steps), sampled sequences
+    inp = synth.make_product_inputs(256, 1, 32, 128, 128, 2, dtype=torch.bfloat16,
+                                    gate="scalar", chunk=16, seed=1008, s0_std=0.02)
+    d = dev(inp)
+    state = d.s0.clone()
+    o = gdn.decode_step_product(d.q[:, 0].contiguous(), d.k[:, 0].contiguous(),
+                                d.v[:, 0].contiguous(), d.beta[:, 0].contiguous(),
+                                d.log_alpha[:, 0].contiguous(), state)
+    torch.cuda.synchronize()
+    f = inp.f64
+    for n in (0, 1, 100, 255):
+        sl = slice(n, n + 1)
+        o_ref, s_ref = oracle.deltaproduct_fwd(f["q"][sl], f["k"][sl], f["v"][sl],
+                                               f["beta"][sl], f["log_alpha"][sl], f["s0"][sl],
+                                               "scalar")
+        eo = np.max(np.abs(np64(o[sl]) - o_ref[:, 0])) / np.max(np.abs(o_ref))
+        es = state_err(np64(state[sl]), s_ref)
+        log(f"[product decode] batch seq {n}: err o={eo:.3e} state={es:.3e}")
+        assert eo < 1e-2 and es < 1e-5
