@@ -1213,16 +1213,35 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
       if (e != hipSuccess) return e;
     }
     {
+      // the forward's state pass, storing every chunk-start state: split
+      // into segments like the forward (per-segment maps, their chain,
+      // then every segment from its entering state) when the plan says so
       StageScope scope(GDN_STAGE_BWD_STATES, s);
-      // whole sequences: the recomputation stores every chunk-start state
-      const SegMap whole = make_seg_map(p, map_base, 0);
-      const int64_t ngrp = (p.dv / 16 + kScanGroup - 1) / kScanGroup;
+      const SegMap sm = make_seg_map(p, map_base, p.seg);
+      const SegBuffers sb = make_seg_buffers(
+          p, reinterpret_cast<char*>(dstates) + bwd_states_bytes(p), opstore<IO>::bytes);
+      const int ndvt = p.dv / 16;
+      if (p.seg > 0) {
+        const int64_t tgrp = (ndvt + DK / 16 + kTransGroup - 1) / kTransGroup;
+        hipLaunchKernelGGL((fwd_trans_kernel<C, DK, IO, GATE>),
+                           dim3(static_cast<unsigned>(p.nsegs * p.H * tgrp)),
+                           dim3(64 * kTransWaves), 0, s, map, sm, p.H, p.dv, p.nchunks,
+                           buf, sb);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((fwd_combine_kernel<DK, IO>),
+                           dim3(static_cast<unsigned>(p.nseq * p.H * ndvt)),
+                           dim3(64 * ((DK + 31) / 32)), 0, s, map, sm, p.H, p.dv, s0, sb);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      const int64_t ngrp = (ndvt + kScanGroup - 1) / kScanGroup;
       hipLaunchKernelGGL((fwd_scan_kernel<C, DK, IO, GATE, true>),
-                         dim3(static_cast<unsigned>(p.nseq * p.H * ngrp)),
+                         dim3(static_cast<unsigned>(p.nsegs * p.H * ngrp)),
                          dim3(64 * kScanWaves), 0, s, map,
-                         whole, p.H, p.dv, p.nchunks, q, s0,
+                         sm, p.H, p.dv, p.nchunks, q, s0,
                          static_cast<void*>(nullptr), static_cast<float*>(nullptr),
-                         buf, SegBuffers{}, states, 0);
+                         buf, sb, states, 0);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -1319,10 +1338,10 @@ bool bwd_supported(const Problem& p) {
 }
 
 size_t bwd_workspace_bytes(const Problem& p) {
-  const FwdLayout L(p.chunk, p.dk, p.dv, p.io == GDN_BF16 ? 2 : 4,
-                    p.gate == GDN_GATE_CHANNEL, true);
+  const int ob = p.io == GDN_BF16 ? 2 : 4;
+  const FwdLayout L(p.chunk, p.dk, p.dv, ob, p.gate == GDN_GATE_CHANNEL, true);
   return chunk_map_bytes(p) + size_t(p.nchunks) * p.H * L.per_ch +
-         2 * bwd_states_bytes(p);
+         2 * bwd_states_bytes(p) + seg_buffer_bytes(p, ob);
 }
 
 hipError_t launch_bwd(const Problem& p, const void* q, const void* k,

@@ -141,28 +141,6 @@ hipError_t launch_chunk_map(const Problem& p, char* map_base, hipStream_t s) {
 
 namespace {
 
-// Segment buffers after the per-chunk operands (p.seg > 0).
-SegBuffers make_seg_buffers(const Problem& p, char* base, int ob) {
-  SegBuffers sb{};
-  if (p.seg == 0) return sb;
-  const int NKD = (p.dk + 31) / 32, NDT = p.dk / 16;
-  const size_t n = static_cast<size_t>(p.nsegs) * p.H;
-  const size_t st = FwdLayout::al(size_t(p.dk) * p.dv * 4);
-  sb.trp_bytes = FwdLayout::al(size_t(NDT) * NKD * 512 * ob);
-  sb.trm = reinterpret_cast<float*>(base);
-  sb.trp = base + n * st;
-  sb.ss = reinterpret_cast<float*>(base + n * (st + sb.trp_bytes));
-  return sb;
-}
-
-size_t seg_buffer_bytes(const Problem& p, int ob) {
-  if (p.seg == 0) return 0;
-  const int NKD = (p.dk + 31) / 32, NDT = p.dk / 16;
-  const size_t st = FwdLayout::al(size_t(p.dk) * p.dv * 4);
-  const size_t tp = FwdLayout::al(size_t(NDT) * NKD * 512 * ob);
-  return static_cast<size_t>(p.nsegs) * p.H * (2 * st + tp);
-}
-
 template <int C, int DK, typename IO, int GATE>
 hipError_t run_fwd(const Problem& p, const void* q, const void* k,
                    const void* v, const void* beta, const void* la,

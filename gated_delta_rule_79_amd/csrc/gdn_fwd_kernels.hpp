@@ -1342,6 +1342,28 @@ struct SegBuffers {
   size_t trp_bytes;  // per (slot, head)
 };
 
+// Host: segment buffers at `base` (p.seg > 0; empty otherwise) and their size.
+inline SegBuffers make_seg_buffers(const Problem& p, char* base, int ob) {
+  SegBuffers sb{};
+  if (p.seg == 0) return sb;
+  const int NKD = (p.dk + 31) / 32, NDT = p.dk / 16;
+  const size_t n = static_cast<size_t>(p.nsegs) * p.H;
+  const size_t st = FwdLayout::al(size_t(p.dk) * p.dv * 4);
+  sb.trp_bytes = FwdLayout::al(size_t(NDT) * NKD * 512 * ob);
+  sb.trm = reinterpret_cast<float*>(base);
+  sb.trp = base + n * st;
+  sb.ss = reinterpret_cast<float*>(base + n * (st + sb.trp_bytes));
+  return sb;
+}
+
+inline size_t seg_buffer_bytes(const Problem& p, int ob) {
+  if (p.seg == 0) return 0;
+  const int NKD = (p.dk + 31) / 32, NDT = p.dk / 16;
+  const size_t st = FwdLayout::al(size_t(p.dk) * p.dv * 4);
+  const size_t tp = FwdLayout::al(size_t(NDT) * NKD * 512 * ob);
+  return static_cast<size_t>(p.nsegs) * p.H * (2 * st + tp);
+}
+
 // ---------------------------------------------------- state pass kernels ---
 // The state recurrence runs per (segment, head) and 16-column slab of the
 // value dimension.  A workgroup of NW waves owns NW * SPW slabs of one

@@ -147,3 +147,28 @@ def test_varlen_training_batch_sampled(gpu_lib):
                 e = slice_err(xa, ya, cu)
                 log(f"    head {h} {nm} err={e:.2e}")
                 assert e < TOL[torch.bfloat16], (name, h, nm, e)
+
+
+@pytest.fixture
+def seg_chunks(gpu_lib):
+    yield gdn.set_segment_chunks
+    gdn.set_segment_chunks(0)
+
+
+@pytest.mark.parametrize("L", [1, 3])
+@pytest.mark.parametrize("gate", ["scalar", "none", "channel"])
+def test_segmented_state_recompute(seg_chunks, L, gate):
+    # the chunk-start states recomputed by the split state pass (per-segment
+    # maps, their chain, every segment from its entering state)
+    inp = synth.make_inputs(2, 300, 2, 64, 32, dtype=torch.float32, gate=gate, chunk=32,
+                            seed=41, s0_std=0.2, with_do=True, with_ds=True)
+    seg_chunks(L)
+    check(inp, name=f"segmented L={L}")
+
+
+def test_segmented_state_recompute_varlen_bf16(seg_chunks):
+    inp = synth.make_inputs(1, 0, 2, 128, 128, dtype=torch.bfloat16, gate="scalar",
+                            chunk=64, seed=42, s0_std=0.05, with_do=True, with_ds=True,
+                            lengths=[130, 0, 700, 64, 1])
+    seg_chunks(2)
+    check(inp, name="segmented varlen")
