@@ -186,6 +186,47 @@ def test_layer_b8_sampled(gpu_lib):
         assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
 
 
+def test_long_context_sampled(gpu_lib):
+    # B=1, T=65536, H=16, d=128, initial state, final state: all heads run
+    # (64-chunk segments), two heads compared with the oracle over the whole
+    # sequence
+    inp = synth.workload("long_t65536")
+    log("[fwd] long_t65536")
+    o, sf = run(inp)
+    f = inp.f64
+    import oracle
+    for h in (0, 9):
+        hs = slice(h, h + 1)
+        o_ref, s_ref = oracle.gdn_fwd(f["q"][:, :, hs], f["k"][:, :, hs], f["v"][:, :, hs],
+                                      f["beta"][:, :, hs], f["log_alpha"][:, :, hs],
+                                      f["s0"][:, hs], "scalar")
+        eo = slice_err(np64(o[:, :, hs]), o_ref)
+        es = state_err(np64(sf[:, hs]), s_ref)
+        log(f"    head {h}: err o={eo:.3e} s={es:.3e}")
+        assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("name", ["varlen_16k_dv256", "varlen_16k_dv256_channel"])
+def test_varlen_training_forward_sampled(gpu_lib, name):
+    # 16384 packed tokens, H=16, dk=128, dv=256: all heads run, two heads of
+    # every sequence compared with the oracle
+    inp = synth.workload(name)
+    log(f"[fwd] {name} lengths={np.diff(inp.cu_seqlens.numpy()).tolist()}")
+    o, sf = run(inp)
+    f = inp.f64
+    cu = inp.cu_seqlens.numpy()
+    import oracle
+    for h in (3, 14):
+        hs = slice(h, h + 1)
+        sub = lambda x: None if x is None else x[:, :, hs]
+        o_ref, s_ref = oracle.gdn_fwd(sub(f["q"]), sub(f["k"]), sub(f["v"]), sub(f["beta"]),
+                                      sub(f["log_alpha"]), None, inp.gate, cu_seqlens=cu)
+        eo = slice_err(np64(o[:, :, hs]), o_ref, cu)
+        es = state_err(np64(sf[:, hs]), s_ref)
+        log(f"    head {h}: err o={eo:.3e} s={es:.3e}")
+        assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
+
+
 # ---------------------------------------------------- segmented state pass ---
 # The state pass can split each sequence into segments of L chunks: segment
 # maps [M0 | Phi] in parallel, a sequential combine, then the segments from
