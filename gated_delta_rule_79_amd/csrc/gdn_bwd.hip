@@ -109,13 +109,22 @@ __device__ __forceinline__ void load_help(HelpOps<C, DK, OP>& x,
 }
 
 // Reverse state pass: wave 0 carries dM backwards over the chunks of one
-// (sequence, head, 16-column slab); wave 1 computes R = P^T dO and
+// (segment, head, 16-column slab); wave 1 computes R = P^T dO and
 // G = Q~^T dO for the chunk wave 0 takes next and hands them over in LDS.
-template <int C, int DK, typename IO, int GATE>
+// Over a segment the reverse map is affine, dM_start = Phi^T dM_end + b,
+// with Phi the forward transition of the segment.  Two modes:
+//   ZERO (segment maps): start from dM_end = 0, store nothing per chunk and
+//     write dM_start = b into `seg_out` (segments j >= 1 only);
+//   otherwise: start from dS_final (last segment of a sequence) or from
+//     `seg_in` (the gradient entering the segment from the right), store dM
+//     at every chunk end and write dS_0 from the first segment.
+// One segment per sequence (sm.L = 0) is the plain reverse pass.
+template <int C, int DK, typename IO, int GATE, bool ZERO = false>
 __global__ __launch_bounds__(128) void bwd_scan_kernel(
-    ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ d_o,
+    ChunkMap map, SegMap sm, int H, int dv, int64_t nchunks, const void* __restrict__ d_o,
     const float* __restrict__ ds_final, float* __restrict__ ds0,
-    FwdBuffers buf, float* __restrict__ dstates) {
+    FwdBuffers buf, float* __restrict__ dstates, const float* __restrict__ seg_in,
+    float* __restrict__ seg_out) {
   using OP = IO;
   using X = RevOps<C, DK, OP, GATE>;
   using Y = HelpOps<C, DK, OP>;
@@ -133,36 +142,51 @@ __global__ __launch_bounds__(128) void bwd_scan_kernel(
   const int vt = w % ndvt;
   const int chain = w / ndvt;
   const int h = chain % H;
-  const int seq = chain / H;
+  const int slot = chain / H;
+  const SegInfo si = seg_info(sm, map, slot);
+  if (si.seq < 0 || (ZERO && si.j == 0)) return;  // whole workgroup, before any barrier
+  const int seq = si.seq;
   // wave index in a scalar register: branches on it are scalar branches,
   // never EXEC masks (matrix instructions ignore EXEC)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
   const int col = 16 * vt + l16;
   const int64_t sbase = (static_cast<int64_t>(seq) * H + h) * DK * dv;
+  // segment buffers, accumulator layout [slot][H][dv/16][DK/16][64]
+  const size_t sl = (static_cast<size_t>(slot) * H + h) * ndvt + vt;
 
-  int cb, ce;
-  seq_chunks(map, seq, &cb, &ce);
-  const int n = ce - cb;
+  const int ce = si.c1;
+  const int n = si.c1 - si.c0;
   const int64_t chl = static_cast<int64_t>(h) * nchunks + ce - 1;  // p = 0
 
   if (wave == 0) {
     floatx4 dM[NDT];
+    if (ZERO) {
 #pragma unroll
-    for (int a = 0; a < NDT; ++a)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        dM[a][s] = ds_final
-            ? ds_final[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] : 0.f;
-
-    auto step = [&](const X& cur, X& nxt, int p) {
-      if (kPrefetch && p + 1 < n) load_rev<C, DK, OP, GATE>(nxt, buf, chl - p - 1, lane, lg);
-      float* st = dstates + (chl - p) * static_cast<int64_t>(DK) * dv;
+      for (int a = 0; a < NDT; ++a) dM[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+    } else if (si.last) {
 #pragma unroll
       for (int a = 0; a < NDT; ++a)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          st[static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] = dM[a][s];
+          dM[a][s] = ds_final
+              ? ds_final[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] : 0.f;
+    } else {
+      const floatx4* src = reinterpret_cast<const floatx4*>(seg_in) + sl * NDT * 64;
+#pragma unroll
+      for (int a = 0; a < NDT; ++a) dM[a] = src[a * 64 + lane];
+    }
+
+    auto step = [&](const X& cur, X& nxt, int p) {
+      if (kPrefetch && p + 1 < n) load_rev<C, DK, OP, GATE>(nxt, buf, chl - p - 1, lane, lg);
+      if constexpr (!ZERO) {
+        float* st = dstates + (chl - p) * static_cast<int64_t>(DK) * dv;
+#pragma unroll
+        for (int a = 0; a < NDT; ++a)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            st[static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] = dM[a][s];
+      }
       opvec<OP> Mb[NKD];
 #pragma unroll
       for (int jb = 0; jb < NKD; ++jb) {
@@ -210,7 +234,11 @@ __global__ __launch_bounds__(128) void bwd_scan_kernel(
         __syncthreads();
       }
     }
-    if (ds0) {
+    if (ZERO) {
+      floatx4* dst = reinterpret_cast<floatx4*>(seg_out) + sl * NDT * 64;
+#pragma unroll
+      for (int a = 0; a < NDT; ++a) dst[a * 64 + lane] = dM[a];
+    } else if (ds0 && si.j == 0) {
 #pragma unroll
       for (int a = 0; a < NDT; ++a)
 #pragma unroll
@@ -290,6 +318,88 @@ __global__ __launch_bounds__(128) void bwd_scan_kernel(
         }
         __syncthreads();
       }
+    }
+  }
+}
+
+// Reverse chain over the segments of one (sequence, head, 16-column slab):
+// the gradient entering segment j from the right is g_j (g_last = dS_final),
+// and g_{j-1} = Phi_j^T g_j + b_j with b_j the segment's ZERO-mode result.
+// Phi_j is stored as operand fragments of its rows (the forward transition
+// pass); its transpose's fragments are read back through LDS.  One wave.
+template <int DK, typename IO>
+__global__ __launch_bounds__(64) void bwd_combine_kernel(
+    ChunkMap map, SegMap sm, int H, int dv, const float* __restrict__ ds_final,
+    SegBuffers sb, const float* __restrict__ seg_b, float* __restrict__ seg_g) {
+  using OP = IO;
+  using E = typename io<IO>::storage;
+  constexpr int NKD = (DK + 31) / 32, NDT = DK / 16, LP = DK + 16 / sizeof(E);
+  __shared__ __attribute__((aligned(16))) E sPhi[DK * LP];
+  (void)map;
+  const int ndvt = dv / 16;
+  const int nseq = static_cast<int>(gridDim.x) / (H * ndvt);
+  const int wg = blockIdx.x;
+  const int vt = wg % ndvt;
+  const int seq = (wg / ndvt) % nseq;
+  const int h = wg / ndvt / nseq;
+  int sb0, se0;
+  seq_segs(sm, seq, &sb0, &se0);
+  if (se0 - sb0 <= 1) return;
+  const int lane = threadIdx.x, l16 = lane & 15, lg = lane >> 4;
+  const int col = 16 * vt + l16;
+  const int64_t sbase = (static_cast<int64_t>(seq) * H + h) * DK * dv;
+
+  floatx4 g[NDT];
+#pragma unroll
+  for (int a = 0; a < NDT; ++a)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      g[a][s] = ds_final ? ds_final[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col]
+                         : 0.f;
+  for (int j = se0 - 1; j > sb0; --j) {
+    const size_t sh = static_cast<size_t>(j) * H + h;
+    // Phi_j rows into LDS, element (r, c) at r * LP + c
+    const opvec<OP>* phi = reinterpret_cast<const opvec<OP>*>(sb.trp + sh * sb.trp_bytes);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int a = 0; a < NDT; ++a)
+#pragma unroll
+      for (int jb = 0; jb < NKD; ++jb) {
+        float x[8];
+        to_floats<OP>(phi[(a * NKD + jb) * 64 + lane], x);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int c = 32 * jb + perm_k(lg, s);
+          if (c < DK) lds_st<IO>(reinterpret_cast<char*>(sPhi), size_t(16 * a + l16) * LP + c, x[s]);
+        }
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes
+    __builtin_amdgcn_wave_barrier();
+    opvec<OP> gb[NKD];
+#pragma unroll
+    for (int jb = 0; jb < NKD; ++jb) {
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      gb[jb] = pack2<OP>(g[2 * jb], 2 * jb + 1 < NDT ? g[2 * jb + 1] : z);
+    }
+    const floatx4* bj = reinterpret_cast<const floatx4*>(seg_b) + (sh * ndvt + vt) * NDT * 64;
+    floatx4* out = reinterpret_cast<floatx4*>(seg_g) + ((sh - H) * ndvt + vt) * NDT * 64;
+#pragma unroll
+    for (int a = 0; a < NDT; ++a) {
+      floatx4 acc = bj[a * 64 + lane];
+#pragma unroll
+      for (int jb = 0; jb < NKD; ++jb) {
+        // rows 16 a .. of Phi^T: Phi's columns, k = Phi's rows (permuted)
+        float x[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int r = 32 * jb + perm_k(lg, s);
+          x[s] = r < DK ? lds_ld<IO>(reinterpret_cast<const char*>(sPhi),
+                                     size_t(r) * LP + 16 * a + l16) : 0.f;
+        }
+        acc = mma32(frag<OP>::from_floats(x), gb[jb], acc);
+      }
+      g[a] = acc;
+      out[a * 64 + lane] = acc;  // entering gradient of segment j - 1
     }
   }
 }
@@ -1202,7 +1312,16 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
     e = launch_chunk_map(p, map_base, s);
     if (e != hipSuccess) return e;
   }
-  const int64_t nwork = static_cast<int64_t>(p.nseq) * p.H * (p.dv / 16);
+  const SegMap sm = make_seg_map(p, map_base, p.seg);
+  // the reverse pass has one workgroup per (chain, 16-column slab) already;
+  // it is split into segments only while those leave the CUs short of work
+  // (splitting adds a pass over all but the first segment)
+  constexpr int64_t kRevSplitBelow = 512;
+  const bool rseg = p.seg > 0 && static_cast<int64_t>(p.nseq) * p.H * (p.dv / 16) < kRevSplitBelow;
+  const SegMap rsm = rseg ? sm : make_seg_map(p, map_base, 0);
+  const int64_t nwork = (rseg ? p.nsegs : p.nseq) * p.H * (p.dv / 16);
+  const SegBuffers sb = make_seg_buffers(
+      p, reinterpret_cast<char*>(dstates) + bwd_states_bytes(p), opstore<IO>::bytes);
   if (p.nchunks > 0) {
     {
       StageScope scope(GDN_STAGE_FWD_PREP, s);
@@ -1217,16 +1336,13 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
       // into segments like the forward (per-segment maps, their chain,
       // then every segment from its entering state) when the plan says so
       StageScope scope(GDN_STAGE_BWD_STATES, s);
-      const SegMap sm = make_seg_map(p, map_base, p.seg);
-      const SegBuffers sb = make_seg_buffers(
-          p, reinterpret_cast<char*>(dstates) + bwd_states_bytes(p), opstore<IO>::bytes);
       const int ndvt = p.dv / 16;
       if (p.seg > 0) {
         const int64_t tgrp = (ndvt + DK / 16 + kTransGroup - 1) / kTransGroup;
         hipLaunchKernelGGL((fwd_trans_kernel<C, DK, IO, GATE>),
                            dim3(static_cast<unsigned>(p.nsegs * p.H * tgrp)),
                            dim3(64 * kTransWaves), 0, s, map, sm, p.H, p.dv, p.nchunks,
-                           buf, sb);
+                           buf, sb, rseg);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((fwd_combine_kernel<DK, IO>),
@@ -1247,10 +1363,29 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
     }
   }
   {
+    // split like the state recomputation: each segment's reverse map from a
+    // zero gradient (its M0 buffer is free again), the chain over segments
+    // through the transposed transitions (into the entering-state buffer),
+    // then every segment from its entering gradient
     StageScope scope(GDN_STAGE_BWD_SCAN, s);
+    if (rseg && p.nchunks > 0) {
+      hipLaunchKernelGGL((bwd_scan_kernel<C, DK, IO, GATE, true>),
+                         dim3(static_cast<unsigned>(nwork)), dim3(128), 0, s, map, rsm,
+                         p.H, p.dv, p.nchunks, d_o, ds_final, ds0, buf, dstates,
+                         static_cast<const float*>(nullptr), sb.trm);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((bwd_combine_kernel<DK, IO>),
+                         dim3(static_cast<unsigned>(p.nseq * p.H * (p.dv / 16))), dim3(64),
+                         0, s, map, rsm, p.H, p.dv, ds_final, sb,
+                         static_cast<const float*>(sb.trm), sb.ss);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((bwd_scan_kernel<C, DK, IO, GATE>),
-                       dim3(static_cast<unsigned>(nwork)), dim3(128), 0, s, map,
-                       p.H, p.dv, p.nchunks, d_o, ds_final, ds0, buf, dstates);
+                       dim3(static_cast<unsigned>(nwork)), dim3(128), 0, s, map, rsm,
+                       p.H, p.dv, p.nchunks, d_o, ds_final, ds0, buf, dstates,
+                       static_cast<const float*>(sb.ss), static_cast<float*>(nullptr));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -182,7 +182,7 @@ hipError_t run_fwd(const Problem& p, const void* q, const void* k,
       hipLaunchKernelGGL((fwd_trans_kernel<C, DK, IO, GATE>),
                          dim3(static_cast<unsigned>(p.nsegs * p.H * ngrp)),
                          dim3(64 * kTransWaves), 0, s, map, sm, p.H, p.dv, p.nchunks,
-                         buf, sb);
+                         buf, sb, false);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -1573,12 +1573,13 @@ __device__ __forceinline__ void chain_lds(
 // the chain over the segment's chunks from M = 0 with U (columns of M0) or
 // from the identity columns without U (columns of Phi; the map from the
 // entering to the leaving state is affine, M_end = Phi M_start + M0).  The
-// last segment of a sequence needs neither.
+// forward's chain never needs the last segment of a sequence; the backward's
+// reverse chain needs every segment's Phi but the first's (with_last).
 template <int C, int DK, typename IO, int GATE>
 __global__ __launch_bounds__(64 * kTransWaves)
 void fwd_trans_kernel(
     ChunkMap map, SegMap sm, int H, int dv, int64_t nchunks, FwdBuffers buf,
-    SegBuffers sb) {
+    SegBuffers sb, bool with_last) {
   using OP = IO;
   constexpr int NW = kTransWaves, SPW = kTransSlabs, NTH = 64 * NW, GS = kTransGroup;
   using L = LdsChunk<C, DK, OP, false, false, GS>;
@@ -1596,7 +1597,7 @@ void fwd_trans_kernel(
   const int slot = (w / ngrp) % nslot;
   const int h = w / ngrp / nslot;
   const SegInfo si = seg_info(sm, map, slot);
-  if (si.seq < 0 || si.last) return;  // whole workgroup, before any barrier
+  if (si.seq < 0 || (si.last && !with_last)) return;  // whole workgroup, before any barrier
   const int tid = threadIdx.x;
   // wave index in a scalar register: branches on it are scalar branches,
   // never EXEC masks (matrix instructions ignore EXEC)
