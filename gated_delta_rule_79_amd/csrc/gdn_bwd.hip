@@ -675,8 +675,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     }
   } else if constexpr (SC) {
     if (tid < C) {
-      seq[tid] = expf(sg[tid]);
-      sek[tid] = expf(sg[C - 1] - sg[tid]);
+      seq[tid] = fast_exp(sg[tid]);
+      sek[tid] = fast_exp(sg[C - 1] - sg[tid]);
     }
   }
   __syncthreads();
@@ -686,31 +686,31 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   auto Qr = [&](int r, int d) { return lds_ld<IO>(sQ, size_t(r) * LDK + d); };
   // decays: gamma_r (per row / per (row, channel)), chunk-end relative decay
   auto gq = [&](int r, int d) -> float {
-    if constexpr (CH) return expf(sg[r * DK + d]);
+    if constexpr (CH) return fast_exp(sg[r * DK + d]);
     else if constexpr (SC) return seq[r];
     else return 1.f;
   };
   auto gk = [&](int r, int d) -> float {
-    if constexpr (CH) return expf(sg[(C - 1) * DK + d] - sg[r * DK + d]);
+    if constexpr (CH) return fast_exp(sg[(C - 1) * DK + d] - sg[r * DK + d]);
     else if constexpr (SC) return sek[r];
     else return 1.f;
   };
   auto gl = [&](int d) -> float {
-    if constexpr (CH) return expf(sg[(C - 1) * DK + d]);
-    else if constexpr (SC) return expf(sg[C - 1]);
+    if constexpr (CH) return fast_exp(sg[(C - 1) * DK + d]);
+    else if constexpr (SC) return fast_exp(sg[C - 1]);
     else return 1.f;
   };
   // factored per-channel decays around the channel's midpoint
   auto up = [&](int r, int d) -> float {   // e^{g - mid}
-    if constexpr (CH) return expf(sg[r * DK + d] - smid[d]);
+    if constexpr (CH) return fast_exp(sg[r * DK + d] - smid[d]);
     else return 1.f;
   };
   auto dn = [&](int r, int d) -> float {   // e^{mid - g}
-    if constexpr (CH) return expf(smid[d] - sg[r * DK + d]);
+    if constexpr (CH) return fast_exp(smid[d] - sg[r * DK + d]);
     else return 1.f;
   };
   auto dec = [&](int r, int i) -> float {  // scalar pairwise decay, i <= r
-    if constexpr (SC) return expf(sg[r] - sg[i]);
+    if constexpr (SC) return fast_exp(sg[r] - sg[i]);
     else return 1.f;
   };
   auto Xr = [&](int r, int d) { return Kr(r, d) * sbeta[r] * gq(r, d); };
@@ -749,7 +749,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       float kv = 0.f, pv = 0.f;
       if (i <= r) {
         for (int d = 0; d < DK; ++d) {
-          const float dd = expf(sg[r * DK + d] - sg[i * DK + d]);
+          const float dd = fast_exp(sg[r * DK + d] - sg[i * DK + d]);
           const float ki = Kr(i, d) * dd;
           kv += Kr(r, d) * ki;
           pv += Qr(r, d) * ki;

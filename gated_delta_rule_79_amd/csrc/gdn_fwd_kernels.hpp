@@ -163,6 +163,12 @@ __host__ __device__ constexpr int num_pt_frags(int NB, int NKC) {
   return n;
 }
 
+// e^x as one hardware base-2 exponential of x log2(e): relative error about
+// 1e-7 for |x| <= 88, zero far below (the decays here are bounded so).
+__device__ inline float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
 template <int C, int DK, typename IO, int GATE, bool BWD = false>
 __global__ __launch_bounds__(256) void fwd_prep_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
@@ -286,8 +292,8 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   }
   if (tid < C) {
     if constexpr (GATE == GDN_GATE_SCALAR) {
-      sxs[tid] = sbeta[tid] * expf(sg[tid]);
-      sks[tid] = expf(sg[C - 1] - sg[tid]);
+      sxs[tid] = sbeta[tid] * fast_exp(sg[tid]);
+      sks[tid] = fast_exp(sg[C - 1] - sg[tid]);
     } else {
       sxs[tid] = sbeta[tid];
       sks[tid] = 1.f;
@@ -326,8 +332,8 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
             for (int s = 0; s < 8; ++s) {
               const int kk = k0 + s;
               if (kk < DK) {
-                x[s] *= expf(sg[ra * DK + kk] - smid[kk]);
-                y[s] *= expf(smid[kk] - sg[rb * DK + kk]);
+                x[s] *= fast_exp(sg[ra * DK + kk] - smid[kk]);
+                y[s] *= fast_exp(smid[kk] - sg[rb * DK + kk]);
               }
             }
             af = frag<OP>::from_floats(x);
@@ -342,7 +348,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
           float val = 0.f;
           if (i < r) {
             val = acc[s] * sbeta[r];
-            if constexpr (GATE == GDN_GATE_SCALAR) val *= expf(sg[r] - sg[i]);
+            if constexpr (GATE == GDN_GATE_SCALAR) val *= fast_exp(sg[r] - sg[i]);
           }
           sA[r * LDC + i] = val;
         }
@@ -378,8 +384,8 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
                 for (int s = 0; s < 8; ++s) {
                   const int kk = k0 + s;
                   if (kk < DK) {
-                    x[s] *= expf(sg[rr * DK + kk] - smid[kk]);
-                    y[s] *= expf(smid[kk] - sg[ri * DK + kk]);
+                    x[s] *= fast_exp(sg[rr * DK + kk] - smid[kk]);
+                    y[s] *= fast_exp(smid[kk] - sg[ri * DK + kk]);
                   }
                 }
                 af = frag<OP>::from_floats(x);
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
             float val = 0.f;
             if (rt >= it && rt < NB && i <= r) {
               val = acc[s];
-              if constexpr (GATE == GDN_GATE_SCALAR) val *= expf(sg[r] - sg[i]);
+              if constexpr (GATE == GDN_GATE_SCALAR) val *= fast_exp(sg[r] - sg[i]);
             }
             out[4 * half + s] = val;
           }
@@ -421,7 +427,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
               const int kk = kb * 32 + lg * 8 + s;
-              if (kk < DK) x[s] *= expf(sg[r * DK + kk] - smid[kk]);
+              if (kk < DK) x[s] *= fast_exp(sg[r * DK + kk] - smid[kk]);
             }
             qf[kb] = frag<OP>::from_floats(x);
           }
@@ -444,7 +450,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
                   const int kk = k0 + s;
-                  if (kk < DK) x[s] *= expf(smid[kk] - sg[ri * DK + kk]);
+                  if (kk < DK) x[s] *= fast_exp(smid[kk] - sg[ri * DK + kk]);
                 }
                 kf = frag<OP>::from_floats(x);
               }
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
             float val = 0.f;
             if (it <= rt && i <= r) {
               val = acc[s];
-              if constexpr (GATE == GDN_GATE_SCALAR) val *= expf(sg[r] - sg[i]);
+              if constexpr (GATE == GDN_GATE_SCALAR) val *= fast_exp(sg[r] - sg[i]);
             }
             out[4 * half + s] = val;
           }
@@ -474,7 +480,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
       float pv = 0.f, av = 0.f;
       if (i <= r && r < len) {
         for (int kk = 0; kk < DK; ++kk) {
-          const float d = expf(sg[r * DK + kk] - sg[i * DK + kk]);
+          const float d = fast_exp(sg[r * DK + kk] - sg[i * DK + kk]);
           const float ki = lds_ld<IO>(sKt, size_t(kk) * LDT + i) * d;
           pv += io<IO>::load(q, ((tok0 + r) * H + h) * DK + kk) * ki;
           av += lds_ld<IO>(sKt, size_t(kk) * LDT + r) * ki;
@@ -556,7 +562,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
       for (int s = 0; s < 8; ++s) {
         const int i = 32 * jb + perm_k(g, s);
         if (i < C) {
-          if constexpr (CH) vals[s] *= expf(sg[(C - 1) * DK + dk] - sg[i * DK + dk]);
+          if constexpr (CH) vals[s] *= fast_exp(sg[(C - 1) * DK + dk] - sg[i * DK + dk]);
           else vals[s] *= sks[i];
         }
       }
@@ -576,7 +582,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
           const int dk = 32 * jb + perm_k(g, s);
           float x = 0.f;
           if (dk < DK && r < len)
-            x = io<IO>::load(q, ((tok0 + r) * H + h) * DK + dk) * expf(sg[r * DK + dk]);
+            x = io<IO>::load(q, ((tok0 + r) * H + h) * DK + dk) * fast_exp(sg[r * DK + dk]);
           vals[s] = x;
         }
         *reinterpret_cast<opvec<OP>*>(dq + (size_t(fr) * 64 + ln) * 8 * ob) =
@@ -599,7 +605,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
           float x = 0.f;
           if (dk < DK) {
             x = lds_ld<IO>(sK, size_t(i) * LDK + dk);
-            if constexpr (CH) x *= expf(sg[(C - 1) * DK + dk] - sg[i * DK + dk]);
+            if constexpr (CH) x *= fast_exp(sg[(C - 1) * DK + dk] - sg[i * DK + dk]);
             else x *= sks[i];
           }
           vals[s] = x;
@@ -620,8 +626,8 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
           float x = 0.f;
           if (r < len) {
             x = io<IO>::load(q, ((tok0 + r) * H + h) * DK + dk);
-            if constexpr (CH) x *= expf(sg[r * DK + dk]);
-            else if constexpr (GATE == GDN_GATE_SCALAR) x *= expf(sg[r]);
+            if constexpr (CH) x *= fast_exp(sg[r * DK + dk]);
+            else if constexpr (GATE == GDN_GATE_SCALAR) x *= fast_exp(sg[r]);
           }
           vals[s] = x;
         }
@@ -632,13 +638,13 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
     float* gam = reinterpret_cast<float*>(buf.at(ch, buf.off_g));
     if (t3 < C) {
       float x = 1.f;
-      if constexpr (GATE == GDN_GATE_SCALAR) x = expf(sg[t3]);
+      if constexpr (GATE == GDN_GATE_SCALAR) x = fast_exp(sg[t3]);
       gam[t3] = x;
     }
     for (int d = t3; d < DK; d += 192) {
       float x = 1.f;
-      if constexpr (GATE == GDN_GATE_SCALAR) x = expf(sg[C - 1]);
-      if constexpr (CH) x = expf(sg[(C - 1) * DK + d]);
+      if constexpr (GATE == GDN_GATE_SCALAR) x = fast_exp(sg[C - 1]);
+      if constexpr (CH) x = fast_exp(sg[(C - 1) * DK + d]);
       gam[C + d] = x;
     }
   }
@@ -708,7 +714,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
               av[s] *= xs[s];
-              if constexpr (CH) av[s] *= expf(sg[(i0 + s) * DK + dk]);
+              if constexpr (CH) av[s] *= fast_exp(sg[(i0 + s) * DK + dk]);
             }
           } else {
 #pragma unroll
@@ -754,7 +760,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
 #pragma unroll
               for (int s = 0; s < 8; ++s) {
                 xv[s] *= xs[s];
-                if constexpr (CH) xv[s] *= expf(sg[(i0 + s) * DK + dk]);
+                if constexpr (CH) xv[s] *= fast_exp(sg[(i0 + s) * DK + dk]);
               }
             } else {
 #pragma unroll
