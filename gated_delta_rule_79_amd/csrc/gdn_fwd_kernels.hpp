@@ -39,7 +39,12 @@ struct PrepSmem {
   static constexpr size_t a_bytes = size_t(C) * LDC * 4;
   static constexpr size_t v_bytes = 64 * size_t(LDV) * ib;
   static constexpr size_t p_off = a_off + (a_bytes > v_bytes ? a_bytes : v_bytes);
-  static constexpr size_t total = p_off + (CH ? size_t(C) * LDC * 4 : 0);
+  // per-channel gate, bf16 inputs: the decay factors e^{g - mid} and
+  // e^{mid - g} of every (row, channel) as bf16 rows [C][LDE], formed once
+  static constexpr bool EF = CH && ib == 2;
+  static constexpr int LDE = DK + 8;
+  static constexpr size_t eu_off = p_off + (CH ? size_t(C) * LDC * 4 : 0);
+  static constexpr size_t total = eu_off + (EF ? 2 * size_t(C) * LDE * 2 : 0);
   static_assert(total <= 160 * 1024, "prep LDS budget");
 };
 
@@ -202,6 +207,26 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   float* sA = reinterpret_cast<float*>(smem + S::a_off);
   char* sVt = smem + S::a_off;
   float* sP = reinterpret_cast<float*>(smem + S::p_off);
+  __bf16* sEu = reinterpret_cast<__bf16*>(smem + S::eu_off);
+  __bf16* sEd = sEu + C * S::LDE;
+  // x[0..7] (channels k0 .. k0 + 7 of row r) times e^{g - mid} (up) or
+  // e^{mid - g}: from the factor rows when they exist, else evaluated here
+  auto chan = [&](float* x, bool up, int r, int k0) {
+    if (k0 >= DK) return;  // DK is a multiple of 16: all 8 or none
+    if constexpr (S::EF) {
+      float e[8];
+      to_floats<bf16_t>(*reinterpret_cast<const opvec<bf16_t>*>(
+                            (up ? sEu : sEd) + r * S::LDE + k0), e);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) x[s] *= e[s];
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float gm = sg[r * DK + k0 + s] - smid[k0 + s];
+        x[s] *= fast_exp(up ? gm : -gm);
+      }
+    }
+  };
 
   const int L = blockIdx.x;
   const int c = static_cast<int>(L / H);
@@ -258,21 +283,55 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
       }
       if (lane < C) sg[lane] = x;
     }
-  } else {
-    for (int e = tid; e < C * DK; e += 256) {
-      const int r = e / DK, col = e % DK;
-      sg[e] = r < len ? load_gate(la, ((tok0 + r) * H + h) * DK + col, gbf) : 0.f;
+  }
+  // K rows, and the per-channel log gates, as 16-byte pieces: every load is
+  // issued before the first LDS store, so the loads travel together
+  constexpr int NKP = (C * VPR + 255) / 256;
+  uint4 kraw[NKP];
+#pragma unroll
+  for (int u = 0; u < NKP; ++u) {
+    const int e = tid + 256 * u;
+    const int r = e / VPR, cv = (e % VPR) * VW;
+    kraw[u] = make_uint4(0, 0, 0, 0);
+    if (e < C * VPR && r < len)
+      kraw[u] = *reinterpret_cast<const uint4*>(
+          static_cast<const char*>(k) + (((tok0 + r) * H + h) * DK + cv) * ib);
+  }
+  if constexpr (CH) {
+    constexpr int NGP = (C * DK / 4 + 255) / 256;  // pieces per thread (fp32 gates)
+    const int per = gbf ? 8 : 4;                    // gate elements per piece
+    const int np = C * DK / per;
+    uint4 graw[NGP];
+#pragma unroll
+    for (int u = 0; u < NGP; ++u) {
+      const int e = tid + 256 * u;
+      const int r = (e * per) / DK, col = (e * per) % DK;
+      graw[u] = make_uint4(0, 0, 0, 0);
+      if (e < np && r < len)
+        graw[u] = *reinterpret_cast<const uint4*>(
+            static_cast<const char*>(la) + (((tok0 + r) * H + h) * DK + col) * (gbf ? 2 : 4));
+    }
+#pragma unroll
+    for (int u = 0; u < NGP; ++u) {
+      const int e = tid + 256 * u;
+      if (e < np) {
+        float x[8];
+        if (gbf) unpack16<bf16_t>(graw[u], x);
+        else unpack16<f32_t>(graw[u], x);
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2)
+          if (s2 < per) sg[e * per + s2] = x[s2];
+      }
     }
   }
-  for (int e = tid; e < C * VPR; e += 256) {
+#pragma unroll
+  for (int u = 0; u < NKP; ++u) {
+    const int e = tid + 256 * u;
+    if (e >= C * VPR) continue;
     const int r = e / VPR, cv = (e % VPR) * VW;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (r < len)
-      raw = *reinterpret_cast<const uint4*>(
-          static_cast<const char*>(k) + (((tok0 + r) * H + h) * DK + cv) * ib);
-    *reinterpret_cast<uint4*>(sK + (size_t(r) * LDK + cv) * ib) = raw;
+    *reinterpret_cast<uint4*>(sK + (size_t(r) * LDK + cv) * ib) = kraw[u];
     float x[8];
-    unpack16<IO>(raw, x);
+    unpack16<IO>(kraw[u], x);
 #pragma unroll
     for (int s = 0; s < VW; ++s) lds_st<IO>(sKt, size_t(cv + s) * LDT + r, x[s]);
   }
@@ -304,6 +363,17 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   // ---- 2. A = decayed beta K K^T (LDS) and P fragments (workspace) --------
   bool exact = false;
   if constexpr (CH) exact = __int_as_float(s_span_bits) > kChannelHalfSpan;
+  if constexpr (S::EF) {
+    if (!exact) {  // the same for the whole workgroup
+      for (int e = tid; e < C * DK; e += 256) {
+        const int r = e / DK, d = e % DK;
+        const float gm = sg[e] - smid[d];
+        sEu[r * S::LDE + d] = static_cast<__bf16>(fast_exp(gm));
+        sEd[r * S::LDE + d] = static_cast<__bf16>(fast_exp(-gm));
+      }
+      __syncthreads();
+    }
+  }
   char* dP = buf.at(ch, buf.off_p);
   if (!exact) {
 #pragma unroll
@@ -328,14 +398,8 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
             float x[8], y[8];
             to_floats<OP>(af, x);
             to_floats<OP>(bf, y);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-              const int kk = k0 + s;
-              if (kk < DK) {
-                x[s] *= fast_exp(sg[ra * DK + kk] - smid[kk]);
-                y[s] *= fast_exp(smid[kk] - sg[rb * DK + kk]);
-              }
-            }
+            chan(x, true, ra, k0);
+            chan(y, false, rb, k0);
             af = frag<OP>::from_floats(x);
             bf = frag<OP>::from_floats(y);
           }
@@ -380,14 +444,8 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
                 float x[8], y[8];
                 to_floats<OP>(af, x);
                 to_floats<OP>(bf, y);
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                  const int kk = k0 + s;
-                  if (kk < DK) {
-                    x[s] *= fast_exp(sg[rr * DK + kk] - smid[kk]);
-                    y[s] *= fast_exp(smid[kk] - sg[ri * DK + kk]);
-                  }
-                }
+                chan(x, true, rr, k0);
+                chan(y, false, ri, k0);
                 af = frag<OP>::from_floats(x);
                 bf = frag<OP>::from_floats(y);
               }
@@ -424,11 +482,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
           if constexpr (CH) {
             float x[8];
             to_floats<OP>(qf[kb], x);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-              const int kk = kb * 32 + lg * 8 + s;
-              if (kk < DK) x[s] *= fast_exp(sg[r * DK + kk] - smid[kk]);
-            }
+            chan(x, true, r, kb * 32 + lg * 8);
             qf[kb] = frag<OP>::from_floats(x);
           }
         }
@@ -447,11 +501,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
               if constexpr (CH) {
                 float x[8];
                 to_floats<OP>(kf, x);
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                  const int kk = k0 + s;
-                  if (kk < DK) x[s] *= fast_exp(smid[kk] - sg[ri * DK + kk]);
-                }
+                chan(x, false, ri, k0);
                 kf = frag<OP>::from_floats(x);
               }
               acc = mma32(kf, qf[kb], acc);
