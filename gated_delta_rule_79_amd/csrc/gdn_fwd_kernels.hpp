@@ -832,19 +832,35 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
     char* U = buf.at(ch, buf.off_u);
     const int ndt = dv / 16;
     constexpr int SV = 64 / VW;  // 16-byte vectors per slab row
+    // the next slab's V pieces are loaded while the current one is used
+    constexpr int NVS = (C * SV + 255) / 256;
+    uint4 vraw[NVS];
+    auto load_v = [&](int slab) {
+      const int ncol = min(64, dv - slab);
+#pragma unroll
+      for (int u = 0; u < NVS; ++u) {
+        const int e = tid + 256 * u;
+        const int i = e / SV, cv = (e % SV) * VW;
+        vraw[u] = make_uint4(0, 0, 0, 0);
+        if (e < C * SV && i < len && cv < ncol)
+          vraw[u] = *reinterpret_cast<const uint4*>(
+              static_cast<const char*>(v) + (((tok0 + i) * H + h) * dv + slab + cv) * ib);
+      }
+    };
+    load_v(0);
     for (int slab = 0; slab < dv; slab += 64) {
       const int ncol = min(64, dv - slab);
-      for (int e = tid; e < C * SV; e += 256) {
+#pragma unroll
+      for (int u = 0; u < NVS; ++u) {
+        const int e = tid + 256 * u;
+        if (e >= C * SV) continue;
         const int i = e / SV, cv = (e % SV) * VW;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (i < len && cv < ncol)
-          raw = *reinterpret_cast<const uint4*>(
-              static_cast<const char*>(v) + (((tok0 + i) * H + h) * dv + slab + cv) * ib);
         float x[8];
-        unpack16<IO>(raw, x);
+        unpack16<IO>(vraw[u], x);
 #pragma unroll
         for (int s = 0; s < VW; ++s) lds_st<IO>(sVt, size_t(cv + s) * LDV + i, x[s]);
       }
+      if (slab + 64 < dv) load_v(slab + 64);
       __syncthreads();
       const int nvt = ncol / 16;
       for (int job = wave; job < NB * nvt; job += 4) {
