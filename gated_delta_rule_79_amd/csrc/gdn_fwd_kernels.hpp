@@ -112,6 +112,22 @@ __device__ inline opvec<IO> row_frag(const void* x, int64_t tok0, int H, int h,
   return gload8<IO>(x, ((tok0 + r) * H + h) * DK + k0);
 }
 
+// 4 consecutive elements of an input tensor in global memory as floats
+// (one 8-byte load in bf16, one 16-byte load in fp32; index a multiple of 4).
+template <typename IO>
+__device__ inline void gload4(const void* base, int64_t idx, float* out) {
+  if constexpr (io<IO>::bytes == 2) {
+    const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const char*>(base) + idx * 2);
+    out[0] = __uint_as_float(raw.x << 16);
+    out[1] = __uint_as_float(raw.x & 0xffff0000u);
+    out[2] = __uint_as_float(raw.y << 16);
+    out[3] = __uint_as_float(raw.y & 0xffff0000u);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const char*>(base) + idx * 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  }
+}
+
 // Decode 16 bytes of the input dtype into floats (8 bf16 or 4 fp32).
 template <typename IO>
 __device__ inline void unpack16(const uint4& raw, float* x) {
@@ -621,19 +637,37 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
     }
     if constexpr (CH) {
       char* dq = buf.at(ch, buf.off_q);
-      for (int e = t3; e < NB * NKD * 64; e += 192) {
+      // slots 0..3 and 4..7 of a lane are channels 32 jb + 4 g .. + 3 and
+      // 16 further on: two 4-element loads, all issued before any use
+      constexpr int NQF = NB * NKD * 64, NQI = (NQF + 191) / 192;
+      float qv[NQI][8];
+#pragma unroll
+      for (int u = 0; u < NQI; ++u) {
+        const int e = t3 + 192 * u;
         const int ln = e & 63, fr = e >> 6;
         const int rt = fr / NKD, jb = fr % NKD;
-        const int m = ln & 15, g = ln >> 4;
-        const int r = 16 * rt + m;
+        const int r = 16 * rt + (ln & 15), dk0 = 32 * jb + 4 * (ln >> 4);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qv[u][s] = 0.f;
+        if (e < NQF && r < len && dk0 < DK) {
+          const int64_t base = ((tok0 + r) * H + h) * DK;
+          gload4<IO>(q, base + dk0, qv[u]);
+          if (dk0 + 16 < DK) gload4<IO>(q, base + dk0 + 16, qv[u] + 4);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NQI; ++u) {
+        const int e = t3 + 192 * u;
+        if (e >= NQF) continue;
+        const int ln = e & 63, fr = e >> 6;
+        const int rt = fr / NKD, jb = fr % NKD;
+        const int g = ln >> 4;
+        const int r = 16 * rt + (ln & 15);
         float vals[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           const int dk = 32 * jb + perm_k(g, s);
-          float x = 0.f;
-          if (dk < DK && r < len)
-            x = io<IO>::load(q, ((tok0 + r) * H + h) * DK + dk) * fast_exp(sg[r * DK + dk]);
-          vals[s] = x;
+          vals[s] = dk < DK ? qv[u][s] * fast_exp(sg[r * DK + dk]) : 0.f;
         }
         *reinterpret_cast<opvec<OP>*>(dq + (size_t(fr) * 64 + ln) * 8 * ob) =
             frag<OP>::from_floats(vals);
