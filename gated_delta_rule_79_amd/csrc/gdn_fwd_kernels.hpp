@@ -734,35 +734,27 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   }
   __syncthreads();
 
-  // ---- 4. off-diagonal blocks of T, block row by block row ----------------
-  for (int b = 1; b < NB; ++b) {
-    if (wave < b) {
-      const int a = wave;
+  // ---- 4. blocks below the diagonal, one diagonal d = b - a at a time, on
+  //      fp32 MFMA:  T_ba = -T_bb sum_{a <= j < b} A_bj T_ja
+  for (int d = 1; d < NB; ++d) {
+    const int a = wave, b = wave + d;  // wave-uniform: never under an EXEC mask
+    if (b < NB) {
+      floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 16 * a; k0 < 16 * b; k0 += 4)
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * b + l16) * LDC + k0 + lg],
+                                                 sT[(k0 + lg) * LDC + 16 * a + l16], z, 0, 0, 0);
+      float* zw = sZ + wave * 256;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = lane * 4 + u, r = e >> 4, cc = e & 15;
-        float z = 0.f;
-        for (int jj = a; jj < b; ++jj) {
+      for (int e = 0; e < 4; ++e) zw[(4 * lg + e) * 16 + l16] = z[e];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes
+      __builtin_amdgcn_wave_barrier();
+      floatx4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < 16; ++s)
-            z += sA[(16 * b + r) * LDC + 16 * jj + s] *
-                 sT[(16 * jj + s) * LDC + 16 * a + cc];
-        }
-        sZ[(a * 16 + r) * 16 + cc] = z;
-      }
-    }
-    __syncthreads();
-    if (wave < b) {
-      const int a = wave;
+      for (int k0 = 0; k0 < 16; k0 += 4)
+        t = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[(16 * b + l16) * LDC + 16 * b + k0 + lg],
+                                                 zw[(k0 + lg) * 16 + l16], t, 0, 0, 0);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = lane * 4 + u, r = e >> 4, cc = e & 15;
-        float t = 0.f;
-#pragma unroll
-        for (int s = 0; s < 16; ++s)
-          t += sT[(16 * b + r) * LDC + 16 * b + s] * sZ[(a * 16 + s) * 16 + cc];
-        sT[(16 * b + r) * LDC + 16 * a + cc] = -t;
-      }
+      for (int e = 0; e < 4; ++e) sT[(16 * b + 4 * lg + e) * LDC + 16 * a + l16] = -t[e];
     }
     __syncthreads();
   }
