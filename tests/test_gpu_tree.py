@@ -148,17 +148,17 @@ def test_commit_varlen(gpu_lib):
 
 
 def test_verify_commit_verify(gpu_lib):
-    # one speculative round and the next: verify, accept a node, commit,
+    # one speculative step and the next: verify, accept a node, commit,
     # verify a new tree from the committed state
     inp, par, acc = synth.make_tree_inputs(4, 32, 2, 128, 128, dtype=torch.bfloat16,
                                            gate="scalar", chunk=32, seed=90, s0_std=0.05)
-    verify(inp, par, name="round 1")
-    st = commit(inp, par, acc, name="round 1")
+    verify(inp, par, name="first verify")
+    st = commit(inp, par, acc, name="first commit")
     nxt, par2, _ = synth.make_tree_inputs(4, 32, 2, 128, 128, dtype=torch.bfloat16,
                                           gate="scalar", chunk=32, seed=91, s0_std=0.05)
     nxt.s0 = st.cpu()
     nxt.f64["s0"] = nxt.s0.double().numpy()
-    verify(nxt, par2, name="round 2")
+    verify(nxt, par2, name="second verify")
 
 
 def test_decode_sized_batch_sampled(gpu_lib):
