@@ -115,6 +115,20 @@ def test_no_initial_state_no_final_grad(gpu_lib):
     check(inp, "no_s0")
 
 
+@pytest.mark.parametrize("gate", ["scalar", "none"])
+def test_empty_sequences(gpu_lib, gate):
+    # T = 0: no step of the recurrence, so S_final = S0 and the gradient of
+    # <dS_final, S_final> w.r.t. S0 is dS_final itself; without dS_final it is 0
+    for with_ds in (True, False):
+        inp = synth.make_inputs(2, 0, 2, 64, 32, dtype=torch.bfloat16, gate=gate,
+                                seed=38, s0_std=0.1, with_do=True, with_ds=with_ds)
+        log(f"[bwd] empty gate={gate} with_ds={with_ds}")
+        dq, dk, dv, db, dla, ds0 = run_bwd(inp)
+        assert dq.shape == (2, 0, 2, 64) and dv.shape == (2, 0, 2, 32) and db.numel() == 0
+        want = inp.ds_final if with_ds else torch.zeros(2, 2, 64, 32)
+        assert torch.equal(ds0.cpu(), want)
+
+
 def test_deterministic(gpu_lib):
     inp = synth.make_inputs(1, 200, 2, 128, 128, dtype=torch.bfloat16, gate="channel",
                             seed=37, s0_std=0.05, with_do=True, with_ds=True)
