@@ -188,3 +188,16 @@ def test_product_decode_batch_sampled(gpu_lib):
         es = state_err(np64(state[sl]), s_ref)
         log(f"[product decode] batch seq {n}: err o={eo:.3e} state={es:.3e}")
         assert eo < 1e-2 and es < 1e-5
+
+
+@pytest.mark.parametrize("nh", [2, 4])
+def test_product_empty_sequences_copy_state(gpu_lib, nh):
+    # T = 0: no transition, the final state is the initial one bit for bit
+    inp = synth.make_product_inputs(2, 0, 2, 64, 32, nh, dtype=torch.bfloat16, seed=1010,
+                                    s0_std=1.0)
+    log(f"[product] empty nh={nh}")
+    d = inp.to("cuda")
+    o, sf = gdn.chunk_fwd_product(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 2, 32)
+    assert torch.equal(sf.cpu(), inp.s0)

@@ -142,3 +142,14 @@ def test_qknorm_plan_and_channel_gate_rejected(gpu_lib):
     with pytest.raises(_lib.GdnError) as ei:
         gdn.chunk_fwd(dc.q, dc.k, dc.v, dc.beta, dc.log_alpha, qk_l2norm=True)
     assert ei.value.status == _lib.GDN_ERR_UNSUPPORTED
+
+
+def test_qknorm_empty_sequences_copy_state(gpu_lib):
+    inp = synth.make_inputs(2, 0, 2, 64, 32, dtype=torch.bfloat16, seed=1011, s0_std=1.0,
+                            raw_qk=(0.1, 10.0, 0.0))
+    log("[qknorm] empty")
+    d = inp.to("cuda")
+    o, sf = gdn.chunk_fwd(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, qk_l2norm=True)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 2, 32)
+    assert torch.equal(sf.cpu(), inp.s0)
