@@ -26,7 +26,7 @@ from ._lib import GdnError  # noqa: F401
 
 __all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "decode_step_product",
            "chunk_fwd_product", "tree_verify",
-           "tree_commit", "FwdPlan", "GdnError", "set_segment_chunks",
+           "tree_commit", "FwdPlan", "GdnError",
            "abi_version", "stage_times"]
 
 _DT = {torch.float32: _lib.GDN_F32, torch.bfloat16: _lib.GDN_BF16}
@@ -60,7 +60,7 @@ def _gate_of(log_alpha, token_dims: int) -> int:
     return _lib.GDN_GATE_CHANNEL if log_alpha.dim() == token_dims + 1 else _lib.GDN_GATE_SCALAR
 
 
-def _problem(q, v, beta, log_alpha, chunk, cu_seqlens, gate=None):
+def _problem(q, v, beta, log_alpha, chunk, cu_seqlens, gate=None, seg_chunks=0):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -71,6 +71,7 @@ def _problem(q, v, beta, log_alpha, chunk, cu_seqlens, gate=None):
     p.io_dtype = _dtype_code(q)
     p.gate_dtype = _dtype_code(beta)
     p.gate = _gate_of(log_alpha, 3) if gate is None else gate
+    p.seg_chunks = int(seg_chunks)
     return p
 
 
@@ -83,12 +84,15 @@ def _check_cu(cu_seqlens, q):
 
 def chunk_fwd(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
               cu_seqlens=None, output_final_state: bool = True,
-              workspace: Optional[torch.Tensor] = None, qk_l2norm: bool = False):
+              workspace: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+              seg_chunks: int = 0):
     """Chunkwise forward.  Returns (o, s_final or None).  qk_l2norm: q and k
-    rows are L2-normalised inside the kernels (gdn_chunk_fwd_qknorm)."""
+    rows are L2-normalised inside the kernels (gdn_chunk_fwd_qknorm).
+    seg_chunks: state-pass segment length (0 automatic, > 0 chunks per
+    segment, < 0 never split)."""
     lib = _lib.load()
     _check_cu(cu_seqlens, q)
-    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
+    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens, seg_chunks=seg_chunks)
     nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
     H, dk, dv = q.shape[2], q.shape[3], v.shape[3]
     o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
@@ -110,7 +114,8 @@ def chunk_fwd(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
 
 
 def chunk_fwd_product(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
-                      cu_seqlens=None, output_final_state: bool = True):
+                      cu_seqlens=None, output_final_state: bool = True,
+                      seg_chunks: int = 0):
     """Householder-product forward (gdn_chunk_fwd_product): k [B,T,nh,H,dk],
     v [B,T,nh,H,dv], beta [B,T,nh,H], q [B,T,H,dk], log_alpha [B,T,H] or None.
     Returns (o [B,T,H,dv], s_final or None)."""
@@ -118,7 +123,7 @@ def chunk_fwd_product(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
     _check_cu(cu_seqlens, q)
     nh = k.shape[2]
     H, dk, dv = q.shape[2], q.shape[3], v.shape[-1]
-    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
+    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens, seg_chunks=seg_chunks)
     nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
     o = torch.empty(q.shape[:3] + (dv,), dtype=q.dtype, device=q.device)
     sf = (torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
@@ -226,11 +231,12 @@ class FwdPlan:
 
     def __init__(self, q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
                  cu_seqlens=None, output_final_state: bool = True,
-                 qk_l2norm: bool = False):
+                 qk_l2norm: bool = False, seg_chunks: int = 0):
         lib = _lib.load()
         _check_cu(cu_seqlens, q)
         self._keep = (q, k, v, beta, log_alpha, s0, cu_seqlens)
-        self.problem = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
+        self.problem = _problem(q, v, beta, log_alpha, chunk, cu_seqlens,
+                                seg_chunks=seg_chunks)
         nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
         H, dk, dv = q.shape[2], q.shape[3], v.shape[3]
         self.o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
@@ -272,17 +278,10 @@ def stage_times(enable: Optional[bool] = None):
             if cnt[i] > 0}
 
 
-def set_segment_chunks(n: int) -> None:
-    """Segment length of the forward state pass, process-wide: 0 automatic
-    (default), n > 0 segments of n chunks, n < 0 never split sequences.  A
-    FwdPlan sizes its workspace when it is built, so build plans after
-    changing this."""
-    _lib.load().gdn_set_segment_chunks(int(n))
-
-
-def fwd_workspace_bytes(q, v, beta, log_alpha=None, chunk=64, cu_seqlens=None) -> int:
+def fwd_workspace_bytes(q, v, beta, log_alpha=None, chunk=64, cu_seqlens=None,
+                        seg_chunks: int = 0) -> int:
     lib = _lib.load()
-    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
+    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens, seg_chunks=seg_chunks)
     need = ctypes.c_size_t(0)
     _lib.check(lib.gdn_chunk_fwd_workspace(ctypes.byref(p), ctypes.byref(need)),
                "gdn_chunk_fwd_workspace")
@@ -291,11 +290,12 @@ def fwd_workspace_bytes(q, v, beta, log_alpha=None, chunk=64, cu_seqlens=None) -
 
 def chunk_bwd(q, k, v, beta, log_alpha, s0, d_o, ds_final=None,
               chunk: int = 64, cu_seqlens=None, need_ds0: bool = True,
-              workspace: Optional[torch.Tensor] = None):
-    """Chunkwise backward.  Returns (dq, dk, dv, dbeta, dlog_alpha, ds0)."""
+              workspace: Optional[torch.Tensor] = None, seg_chunks: int = 0):
+    """Chunkwise backward.  Returns (dq, dk, dv, dbeta, dlog_alpha, ds0).
+    seg_chunks as in chunk_fwd (the state recompute's segments)."""
     lib = _lib.load()
     _check_cu(cu_seqlens, q)
-    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens)
+    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens, seg_chunks=seg_chunks)
     nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
     H, dk, dv = q.shape[2], q.shape[3], v.shape[3]
     dq = torch.empty_like(q)

@@ -21,7 +21,7 @@ EXPORTED = (
     "gdn_abi_version", "gdn_status_str", "gdn_chunk_fwd_workspace",
     "gdn_chunk_fwd", "gdn_chunk_bwd_workspace", "gdn_chunk_bwd",
     "gdn_decode_step", "gdn_test_set_fail_launch", "gdn_profile_enable",
-    "gdn_profile_read", "gdn_set_segment_chunks",
+    "gdn_profile_read",
     "gdn_chunk_fwd_product_workspace", "gdn_chunk_fwd_product",
     "gdn_chunk_fwd_qknorm", "gdn_tree_verify_workspace", "gdn_tree_verify",
     "gdn_tree_commit", "gdn_decode_step_product",
@@ -38,7 +38,7 @@ class GdnProblem(ctypes.Structure):
         ("nseq", ctypes.c_int32),
         ("cu_seqlens", ctypes.c_void_p),
         ("io_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
-        ("gate", ctypes.c_int32),
+        ("gate", ctypes.c_int32), ("seg_chunks", ctypes.c_int32),
     ]
 
 
@@ -85,8 +85,6 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_int32)]
     lib.gdn_test_set_fail_launch.restype = None
     lib.gdn_test_set_fail_launch.argtypes = [i32]
-    lib.gdn_set_segment_chunks.restype = None
-    lib.gdn_set_segment_chunks.argtypes = [i32]
     lib.gdn_chunk_fwd_product_workspace.restype = i32
     lib.gdn_chunk_fwd_product_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
     lib.gdn_chunk_fwd_product.restype = i32

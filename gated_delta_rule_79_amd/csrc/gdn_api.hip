@@ -17,8 +17,7 @@
 
 namespace {
 
-std::atomic<int> g_fail_launch{0};
-std::atomic<int> g_seg_chunks{0};  // gdn_set_segment_chunks
+std::atomic<int> g_fail_launch{0};  // gdn_test_set_fail_launch
 
 bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
@@ -83,6 +82,7 @@ gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out, int lnh 
   out->varlen = p->nseq > 0;
   out->nseq = out->varlen ? p->nseq : p->B;
   out->cu_seqlens = p->cu_seqlens;
+  out->seg_req = p->seg_chunks;
   out->io = p->io_dtype;
   out->gdt = p->gate_dtype;
   out->gate = p->gate;
@@ -185,7 +185,7 @@ void prof_end(int stage, hipStream_t s) {
 }
 
 int plan_segments(const Problem& p) {
-  const int set = g_seg_chunks.load();
+  const int set = p.seg_req;
   if (set < 0 || p.nseq == 0) return 0;
   if (set > 0) return std::min(set, 1 << 20);
   // automatic: a state-pass workgroup takes one (sequence, head) and 8 value
@@ -272,8 +272,6 @@ const char* gdn_status_str(gdn_status s) {
 }
 
 void gdn_test_set_fail_launch(int enable) { g_fail_launch.store(enable != 0); }
-
-void gdn_set_segment_chunks(int n) { g_seg_chunks.store(n); }
 
 gdn_status gdn_chunk_fwd_workspace(const gdn_problem* p, size_t* bytes) {
   try {

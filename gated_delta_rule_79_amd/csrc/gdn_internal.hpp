@@ -15,6 +15,8 @@ struct Problem {
   int nseq;                   // number of independent sequences (B or varlen)
   bool varlen;
   const int32_t* cu_seqlens;  // device
+  int seg_req;                // gdn_problem::seg_chunks (0 automatic,
+                              // > 0 chunks per segment, < 0 never split)
   int io;                     // gdn_dtype
   int gdt;                    // gdn_dtype of beta / log_alpha
   int gate;                   // gdn_gate
@@ -32,8 +34,7 @@ struct Problem {
 };
 
 // Segment length the forward state pass uses for this problem (0 = whole
-// sequences), from the sizes and the process-wide setting of
-// gdn_set_segment_chunks (gdn_api.hip).
+// sequences), from the sizes and the requested seg_req (gdn_api.hip).
 int plan_segments(const Problem& p);
 // Segment slots for p.seg (upper bound in varlen).
 int64_t seg_slots_host(const Problem& p);

@@ -54,8 +54,12 @@
  *     read on the host); sequences of length 0 are allowed.  Chunks never
  *     cross a sequence boundary.
  *   Streams: all work is enqueued on `stream` (a hipStream_t; NULL = the null
- *     stream) with no implicit synchronisation.  The functions are
- *     stateless and re-entrant.
+ *     stream) with no implicit synchronisation.  The compute functions keep
+ *     no state between calls: everything a call depends on is in its
+ *     arguments, so they are re-entrant and may run concurrently on several
+ *     streams (with separate workspaces).  The only process-wide settings
+ *     are the two diagnostic hooks at the end of this header (stage timing
+ *     and the launch-failure test hook), which change no result.
  *   Errors: every argument is validated on the host before anything is
  *     enqueued, so a non-OK status means nothing was launched.  A failed
  *     launch returns GDN_ERR_HIP.  Device faults surface at the caller's
@@ -72,7 +76,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum {
   GDN_OK = 0,
@@ -94,7 +98,23 @@ typedef enum {
 } gdn_gate;
 
 /* Problem description.  For decode, T is ignored, B is the number of
- * sequences N and chunk / nseq / cu_seqlens are ignored. */
+ * sequences N and chunk / nseq / cu_seqlens / seg_chunks are ignored.
+ *
+ * seg_chunks: segment length of the state pass of the chunked forward (and
+ * of the backward's state recompute).  The state is carried across the
+ * chunks of each sequence; when there are few (sequence, head) pairs the
+ * sequences are cut into segments of seg_chunks chunks, every segment's
+ * affine state map is computed in parallel, the maps are chained in a short
+ * sequential pass and the segments then run in parallel from their entering
+ * states (the same recurrence, rounded differently).
+ *   0  : automatic: segments long enough that the segment workgroups about
+ *        fill the GPU's 256 compute units once and at least
+ *        sqrt(chunks / 2.56) chunks; no split when the (sequence, head)
+ *        pairs already fill the GPU or a sequence has fewer than 8 chunks;
+ *   >0 : segments of seg_chunks chunks (values above 2^20 are clamped);
+ *   <0 : never split.
+ * It changes the workspace size: query the *_workspace function with the
+ * same problem.  Draft trees ignore it (one chunk per tree). */
 typedef struct {
   int32_t B, T, H, dk, dv, chunk;
   int32_t nseq;                 /* 0 = dense [B, T]; > 0 = varlen, B == 1     */
@@ -102,6 +122,7 @@ typedef struct {
   int32_t io_dtype;             /* gdn_dtype of q, k, v, o (and grads)        */
   int32_t gate_dtype;           /* gdn_dtype of beta and log_alpha            */
   int32_t gate;                 /* gdn_gate                                   */
+  int32_t seg_chunks;           /* state-pass segment length, 0 = automatic   */
 } gdn_problem;
 
 /* ABI version of the loaded library (GDN_ABI_VERSION). */
@@ -285,22 +306,6 @@ typedef enum {
 } gdn_stage;
 void gdn_profile_enable(int enable);
 gdn_status gdn_profile_read(double* total_ms, int32_t* count);
-
-/* Segment length of the forward state pass, process-wide.  The forward
- * carries the state across the chunks of a sequence; when there are few
- * (sequence, head) pairs it splits each sequence into segments of n chunks,
- * computes every segment's affine state map in parallel, combines them in a
- * short sequential pass and then runs the segments in parallel from their
- * entering states (mathematically the same recurrence, rounded differently).
- *   n = 0  : automatic (default): segments long enough that the segment
- *            workgroups about fill the GPU's 256 CUs once, and at least
- *            sqrt(chunks / 2.56) chunks; no split when the (sequence, head)
- *            pairs already fill the CUs or a sequence has fewer than 8
- *            chunks;
- *   n > 0  : segments of n chunks (values above 2^20 are clamped);
- *   n < 0  : never split.
- * Changes the workspace size: query gdn_chunk_fwd_workspace after setting. */
-void gdn_set_segment_chunks(int n);
 
 /* Test hook: when set to a non-zero value every entry point returns
  * GDN_ERR_HIP after validation instead of launching (exercises the launch

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 6
+    assert lib.gdn_abi_version() == 7
     for s in range(8):
         txt = lib.gdn_status_str(s).decode()
         assert txt.startswith("GDN_")
@@ -166,57 +166,64 @@ def seg_bytes(nsegs, H, dk, dv, ob):
 
 
 def test_workspace_of_segmented_state_pass(lib):
-    try:
-        lib.gdn_set_segment_chunks(-1)
-        _, off = ws_bytes(lib, prob(T=640))
-        _, off_big = ws_bytes(lib, prob(T=4096, H=16))
-        lib.gdn_set_segment_chunks(3)           # 10 chunks -> 4 segments
-        _, seg3 = ws_bytes(lib, prob(T=640))
-        assert seg3 - off == seg_bytes(4, 2, 128, 128, 2)
-        _, seg3f = ws_bytes(lib, prob(T=640, io_dtype=_lib.GDN_F32))
-        lib.gdn_set_segment_chunks(-1)
-        _, offf = ws_bytes(lib, prob(T=640, io_dtype=_lib.GDN_F32))
-        assert seg3f - offf == seg_bytes(4, 2, 128, 128, 4)
-        # automatic: 16 (sequence, head) workgroups of 64 chunks; filling 256
-        # CUs takes segments of 64 * 16 / 256 = 4 chunks, raised to the floor
-        # ceil(sqrt(64 / 2.56)) = 5: 13 segments per sequence
-        lib.gdn_set_segment_chunks(0)
-        _, auto = ws_bytes(lib, prob(T=4096, H=16))
-        assert auto - off_big == seg_bytes(13, 16, 128, 128, 2)
-        # enough (sequence, head) workgroups (16 x 16 = 256): no split
-        _, a = ws_bytes(lib, prob(B=16, T=4096, H=16))
-        lib.gdn_set_segment_chunks(-1)
-        _, b = ws_bytes(lib, prob(B=16, T=4096, H=16))
-        assert a == b
-        # 8 x 16 = 128 workgroups of 64 chunks: segments of 64 * 128 / 256 =
-        # 32 chunks, 2 per sequence
-        lib.gdn_set_segment_chunks(0)
-        _, a = ws_bytes(lib, prob(B=8, T=4096, H=16))
-        assert a - b // 2 == seg_bytes(8 * 2, 16, 128, 128, 2)
-        # long chains: 16 workgroups of 1024 chunks -> 64-chunk segments
-        _, a = ws_bytes(lib, prob(T=65536, H=16))
-        lib.gdn_set_segment_chunks(-1)
-        _, b = ws_bytes(lib, prob(T=65536, H=16))
-        lib.gdn_set_segment_chunks(0)
-        assert a - b == seg_bytes(16, 16, 128, 128, 2)
-        # short chains (fewer than 8 chunks) are never split
-        _, a = ws_bytes(lib, prob(T=448, H=16))
-        lib.gdn_set_segment_chunks(-1)
-        _, b = ws_bytes(lib, prob(T=448, H=16))
-        lib.gdn_set_segment_chunks(0)
-        assert a == b
-        # varlen with a forced split: segment table + buffers for at most
-        # nchunks / L + nseq slots
-        lib.gdn_set_segment_chunks(2)
-        _, v2 = ws_bytes(lib, prob(T=640, nseq=3, cu_seqlens=A))
-        lib.gdn_set_segment_chunks(-1)
-        _, v0 = ws_bytes(lib, prob(T=640, nseq=3, cu_seqlens=A))
-        nch = 10 + 3
-        slots = nch // 2 + 3
-        al = lambda x: (x + 255) // 256 * 256
-        assert v2 - v0 == seg_bytes(slots, 2, 128, 128, 2) + al(slots * 16) + al(4 * 4)
-    finally:
-        lib.gdn_set_segment_chunks(0)
+    # the segment length is a field of the problem (seg_chunks): 0 automatic,
+    # > 0 chunks per segment, < 0 never split
+    _, off = ws_bytes(lib, prob(T=640, seg_chunks=-1))
+    _, off_big = ws_bytes(lib, prob(T=4096, H=16, seg_chunks=-1))
+    _, seg3 = ws_bytes(lib, prob(T=640, seg_chunks=3))      # 10 chunks -> 4 segments
+    assert seg3 - off == seg_bytes(4, 2, 128, 128, 2)
+    _, seg3f = ws_bytes(lib, prob(T=640, io_dtype=_lib.GDN_F32, seg_chunks=3))
+    _, offf = ws_bytes(lib, prob(T=640, io_dtype=_lib.GDN_F32, seg_chunks=-1))
+    assert seg3f - offf == seg_bytes(4, 2, 128, 128, 4)
+    # automatic: 16 (sequence, head) workgroups of 64 chunks; filling 256
+    # CUs takes segments of 64 * 16 / 256 = 4 chunks, raised to the floor
+    # ceil(sqrt(64 / 2.56)) = 5: 13 segments per sequence
+    _, auto = ws_bytes(lib, prob(T=4096, H=16))
+    assert auto - off_big == seg_bytes(13, 16, 128, 128, 2)
+    # enough (sequence, head) workgroups (16 x 16 = 256): no split
+    _, a = ws_bytes(lib, prob(B=16, T=4096, H=16))
+    _, b = ws_bytes(lib, prob(B=16, T=4096, H=16, seg_chunks=-1))
+    assert a == b
+    # 8 x 16 = 128 workgroups of 64 chunks: segments of 64 * 128 / 256 =
+    # 32 chunks, 2 per sequence
+    _, a = ws_bytes(lib, prob(B=8, T=4096, H=16))
+    assert a - b // 2 == seg_bytes(8 * 2, 16, 128, 128, 2)
+    # long chains: 16 workgroups of 1024 chunks -> 64-chunk segments
+    _, a = ws_bytes(lib, prob(T=65536, H=16))
+    _, b = ws_bytes(lib, prob(T=65536, H=16, seg_chunks=-1))
+    assert a - b == seg_bytes(16, 16, 128, 128, 2)
+    # short chains (fewer than 8 chunks) are never split
+    _, a = ws_bytes(lib, prob(T=448, H=16))
+    _, b = ws_bytes(lib, prob(T=448, H=16, seg_chunks=-1))
+    assert a == b
+    # varlen with a forced split: segment table + buffers for at most
+    # nchunks / L + nseq slots
+    _, v2 = ws_bytes(lib, prob(T=640, nseq=3, cu_seqlens=A, seg_chunks=2))
+    _, v0 = ws_bytes(lib, prob(T=640, nseq=3, cu_seqlens=A, seg_chunks=-1))
+    nch = 10 + 3
+    slots = nch // 2 + 3
+    al = lambda x: (x + 255) // 256 * 256
+    assert v2 - v0 == seg_bytes(slots, 2, 128, 128, 2) + al(slots * 16) + al(4 * 4)
+    # huge requests are clamped, not rejected
+    st, big = ws_bytes(lib, prob(T=640, seg_chunks=2 ** 30))
+    assert st == 0 and big == off + seg_bytes(1, 2, 128, 128, 2)
+
+
+def test_segment_length_is_per_call(lib):
+    # two problems that differ only in seg_chunks, queried in any order, keep
+    # their own workspace sizes: nothing is remembered between calls
+    pa, pb = prob(T=4096, H=16), prob(T=4096, H=16, seg_chunks=2)
+    sizes = [ws_bytes(lib, x)[1] for x in (pa, pb, pa, pb, pa)]
+    assert sizes[0] == sizes[2] == sizes[4] and sizes[1] == sizes[3]
+    assert sizes[0] != sizes[1]
+    # and a call with a workspace sized for one setting is checked against
+    # its own setting
+    assert fwd(lib, pb, ws=A) == 7               # reaches the (failing) launch
+    pb2 = prob(T=4096, H=16, seg_chunks=2)
+    need = ws_bytes(lib, pb2)[1]
+    st = lib.gdn_chunk_fwd(ctypes.byref(pb2), A, A, A, A, A, None, A, None, A,
+                           sizes[0] if sizes[0] < need else need - 256, None)
+    assert st == 6                               # GDN_ERR_WORKSPACE
 
 
 def test_decode_validation(lib):

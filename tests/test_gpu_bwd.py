@@ -11,15 +11,15 @@ import torch
 import gated_delta_rule_79_amd as gdn
 import oracle
 from gated_delta_rule_79_amd import synth
-from gpu_util import TOL, log, np64, slice_err, state_err
+from gpu_util import TOL, bwd_errors_per_head, log, np64, slice_err, state_err
 
 pytestmark = pytest.mark.gpu
 
 
-def run_bwd(inp, need_ds0=True):
+def run_bwd(inp, need_ds0=True, **kw):
     d = inp.to("cuda")
     g = gdn.chunk_bwd(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, d.do, d.ds_final,
-                      chunk=inp.chunk, cu_seqlens=d.cu_seqlens, need_ds0=need_ds0)
+                      chunk=inp.chunk, cu_seqlens=d.cu_seqlens, need_ds0=need_ds0, **kw)
     torch.cuda.synchronize()
     return g
 
@@ -31,10 +31,10 @@ def ref_bwd(inp):
                           f["do"], f["ds_final"], inp.gate, cu_seqlens=cu)
 
 
-def check(inp, name="", tol=None):
+def check(inp, name="", tol=None, **kw):
     log(f"[bwd] {name} q={tuple(inp.q.shape)} {inp.q.dtype} gate={inp.gate} "
-        f"C={inp.chunk} seed={inp.seed}")
-    got = run_bwd(inp)
+        f"C={inp.chunk} seed={inp.seed} {kw}")
+    got = run_bwd(inp, **kw)
     ref = ref_bwd(inp)
     tol = tol or TOL[inp.q.dtype]
     cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
@@ -138,51 +138,56 @@ def test_deterministic(gpu_lib):
         assert torch.equal(x, y)
 
 
-def test_varlen_training_batch_sampled(gpu_lib):
-    # 16384 packed tokens, H=16, dk=128, dv=256, both gate modes: all heads run,
-    # two heads of every sequence are compared with the oracle
-    for name in ("varlen_16k_dv256", "varlen_16k_dv256_channel"):
-        inp = synth.workload(name)
-        log(f"[bwd] {name} lengths={np.diff(inp.cu_seqlens.numpy()).tolist()}")
-        got = run_bwd(inp, need_ds0=False)
-        f = inp.f64
-        cu = inp.cu_seqlens.numpy()
-        for h in (0, 11):
-            hs = slice(h, h + 1)
-            sub = lambda x: None if x is None else x[:, :, hs]
-            ref = oracle.gdn_bwd(sub(f["q"]), sub(f["k"]), sub(f["v"]), sub(f["beta"]),
-                                 sub(f["log_alpha"]), None, sub(f["do"]), None, inp.gate,
-                                 cu_seqlens=cu)
-            for nm, x, y in zip(("dq", "dk", "dv", "dbeta", "dlog_alpha"), got[:5], ref[:5]):
-                xa = np64(x)[:, :, hs]
-                ya = y
-                if ya.ndim == 3:
-                    xa, ya = xa[..., None], ya[..., None]
-                e = slice_err(xa, ya, cu)
-                log(f"    head {h} {nm} err={e:.2e}")
-                assert e < TOL[torch.bfloat16], (name, h, nm, e)
+@pytest.mark.parametrize("name", ["varlen_16k_dv256", "varlen_16k_dv256_channel"])
+def test_varlen_training_batch_all_heads(gpu_lib, name):
+    # 16384 packed tokens, H=16, dk=128, dv=256: every head of every sequence
+    inp = synth.workload(name)
+    log(f"[bwd] {name} lengths={np.diff(inp.cu_seqlens.numpy()).tolist()}")
+    got = run_bwd(inp, need_ds0=False)
+    for h, errs in bwd_errors_per_head(inp, got):
+        log(f"    head {h} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        for k, v in errs.items():
+            assert v < TOL[torch.bfloat16], (name, h, k, v)
 
 
-@pytest.fixture
-def seg_chunks(gpu_lib):
-    yield gdn.set_segment_chunks
-    gdn.set_segment_chunks(0)
+def test_long_context_two_heads(gpu_lib):
+    # T=65536 (1024 chunks per chain, the split reverse pass) with an initial
+    # state and a final-state gradient: both heads compared in full
+    inp = synth.make_inputs(1, 65536, 2, 128, 128, dtype=torch.bfloat16, gate="scalar",
+                            seed=1014, s0_std=0.02, with_do=True, with_ds=True)
+    log("[bwd] T=65536 H=2")
+    got = run_bwd(inp)
+    for h, errs in bwd_errors_per_head(inp, got):
+        log(f"    head {h} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        for k, v in errs.items():
+            assert v < TOL[torch.bfloat16], (h, k, v)
+
+
+@pytest.mark.parametrize("side", [0.95, 1.05])
+@pytest.mark.parametrize("C", [32, 64])
+def test_channel_gate_near_factored_limit(gpu_lib, side, C):
+    # the per-channel backward's factored products near their e^+-80 limit
+    # (see the forward test of the same name)
+    inp = synth.make_inputs(1, 3 * C + 13, 2, 128, 64, dtype=torch.bfloat16,
+                            gate="channel", chunk=C, seed=60 + C, s0_std=0.1,
+                            with_do=True, with_ds=True)
+    inp.log_alpha[..., [0, 5, 77, 127]] = -side * 160.0 / (C - 1)
+    inp.f64["log_alpha"] = inp.log_alpha.double().numpy()
+    check(inp, f"channel_near_limit C={C} side={side}")
 
 
 @pytest.mark.parametrize("L", [1, 3])
 @pytest.mark.parametrize("gate", ["scalar", "none", "channel"])
-def test_segmented_state_recompute(seg_chunks, L, gate):
+def test_segmented_state_recompute(gpu_lib, L, gate):
     # the chunk-start states recomputed by the split state pass (per-segment
     # maps, their chain, every segment from its entering state)
     inp = synth.make_inputs(2, 300, 2, 64, 32, dtype=torch.float32, gate=gate, chunk=32,
                             seed=41, s0_std=0.2, with_do=True, with_ds=True)
-    seg_chunks(L)
-    check(inp, name=f"segmented L={L}")
+    check(inp, name=f"segmented L={L}", seg_chunks=L)
 
 
-def test_segmented_state_recompute_varlen_bf16(seg_chunks):
+def test_segmented_state_recompute_varlen_bf16(gpu_lib):
     inp = synth.make_inputs(1, 0, 2, 128, 128, dtype=torch.bfloat16, gate="scalar",
                             chunk=64, seed=42, s0_std=0.05, with_do=True, with_ds=True,
                             lengths=[130, 0, 700, 64, 1])
-    seg_chunks(2)
-    check(inp, name="segmented varlen")
+    check(inp, name="segmented varlen", seg_chunks=2)

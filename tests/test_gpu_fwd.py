@@ -11,7 +11,9 @@ import torch
 
 import gated_delta_rule_79_amd as gdn
 from gated_delta_rule_79_amd import synth
-from gpu_util import TOL, dev, log, np64, oracle_fwd, slice_err, state_err
+import oracle
+from gpu_util import (TOL, dev, fwd_errors_per_head, log, np64, oracle_fwd,
+                      par_map, slice_err, state_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,10 +26,10 @@ def run(inp, **kw):
     return o, sf
 
 
-def check(inp, tol=None, name=""):
+def check(inp, tol=None, name="", **kw):
     log(f"[fwd] {name} q={tuple(inp.q.shape)} dtype={inp.q.dtype} gate={inp.gate} "
-        f"C={inp.chunk} seed={inp.seed}")
-    o, sf = run(inp)
+        f"C={inp.chunk} seed={inp.seed} {kw}")
+    o, sf = run(inp, **kw)
     o_ref, sf_ref = oracle_fwd(inp)
     tol = tol or TOL[inp.q.dtype]
     cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
@@ -168,63 +170,80 @@ def test_headline_full_size(gpu_lib):
     check(inp, name="fwd_t4096_h16")
 
 
-def test_layer_b8_sampled(gpu_lib):
-    # B=8, T=2048, H=8, d=128: run all, compare two batch rows in full
+def _check_heads(inp, o, sf, name, tol=None, heads=None):
+    tol = tol or TOL[inp.q.dtype]
+    for h, eo, es, er in fwd_errors_per_head(inp, o, sf, heads=heads):
+        log(f"    {name} head {h}: err o={eo:.3e} s={es:.3e} (worst token row {er:.2e})")
+        assert eo < tol and es < tol, (name, h, eo, es)
+
+
+def test_layer_b8_all_rows(gpu_lib):
+    # B=8, T=2048, H=8, d=128: every batch row and head against the oracle
     inp = synth.workload("layer_b8_t2048")
     log("[fwd] layer_b8_t2048")
     o, sf = run(inp)
     f = inp.f64
-    import oracle
-    for b in (0, 7):
+    xo, xs = np64(o), np64(sf)
+
+    def job(b):
         sl = slice(b, b + 1)
-        o_ref, s_ref = oracle.gdn_fwd(f["q"][sl], f["k"][sl], f["v"][sl],
-                                      f["beta"][sl], f["log_alpha"][sl], None,
-                                      "scalar")
-        eo = slice_err(np64(o[sl]), o_ref)
-        es = state_err(np64(sf[sl]), s_ref)
+        o_ref, s_ref = oracle.gdn_fwd(f["q"][sl], f["k"][sl], f["v"][sl], f["beta"][sl],
+                                      f["log_alpha"][sl], None, "scalar")
+        return b, slice_err(xo[sl], o_ref), state_err(xs[sl], s_ref)
+
+    for b, eo, es in par_map(job, range(8)):
         log(f"    batch {b}: err o={eo:.3e} s={es:.3e}")
-        assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
+        assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16], (b, eo, es)
 
 
-def test_long_context_sampled(gpu_lib):
-    # B=1, T=65536, H=16, d=128, initial state, final state: all heads run
-    # (64-chunk segments), two heads compared with the oracle over the whole
-    # sequence
+def test_long_context_all_heads(gpu_lib):
+    # B=1, T=65536, H=16, d=128, initial and final state (64-chunk segments):
+    # every head compared with the oracle over the whole sequence
     inp = synth.workload("long_t65536")
     log("[fwd] long_t65536")
     o, sf = run(inp)
-    f = inp.f64
-    import oracle
-    for h in (0, 9):
-        hs = slice(h, h + 1)
-        o_ref, s_ref = oracle.gdn_fwd(f["q"][:, :, hs], f["k"][:, :, hs], f["v"][:, :, hs],
-                                      f["beta"][:, :, hs], f["log_alpha"][:, :, hs],
-                                      f["s0"][:, hs], "scalar")
-        eo = slice_err(np64(o[:, :, hs]), o_ref)
-        es = state_err(np64(sf[:, hs]), s_ref)
-        log(f"    head {h}: err o={eo:.3e} s={es:.3e}")
-        assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
+    _check_heads(inp, o, sf, "long_t65536")
+
+
+def test_gate_none_long_context(gpu_lib):
+    # alpha = 1 (the plain delta rule) over 65536 tokens with an initial
+    # state: nothing decays the rounding of the segment transitions away
+    inp = synth.workload("long_t65536", gate="none")
+    log("[fwd] long_t65536 gate=none")
+    o, sf = run(inp)
+    _check_heads(inp, o, sf, "long_t65536_none")
 
 
 @pytest.mark.parametrize("name", ["varlen_16k_dv256", "varlen_16k_dv256_channel"])
-def test_varlen_training_forward_sampled(gpu_lib, name):
-    # 16384 packed tokens, H=16, dk=128, dv=256: all heads run, two heads of
-    # every sequence compared with the oracle
+def test_varlen_training_forward_all_heads(gpu_lib, name):
+    # 16384 packed tokens, H=16, dk=128, dv=256: every head of every sequence
     inp = synth.workload(name)
     log(f"[fwd] {name} lengths={np.diff(inp.cu_seqlens.numpy()).tolist()}")
     o, sf = run(inp)
-    f = inp.f64
-    cu = inp.cu_seqlens.numpy()
-    import oracle
-    for h in (3, 14):
-        hs = slice(h, h + 1)
-        sub = lambda x: None if x is None else x[:, :, hs]
-        o_ref, s_ref = oracle.gdn_fwd(sub(f["q"]), sub(f["k"]), sub(f["v"]), sub(f["beta"]),
-                                      sub(f["log_alpha"]), None, inp.gate, cu_seqlens=cu)
-        eo = slice_err(np64(o[:, :, hs]), o_ref, cu)
-        es = state_err(np64(sf[:, hs]), s_ref)
-        log(f"    head {h}: err o={eo:.3e} s={es:.3e}")
-        assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
+    _check_heads(inp, o, sf, name)
+
+
+def _channel_threshold(C):
+    # per-token log alpha at which a chunk's per-channel log-gate half-span
+    # (C - 1) |log alpha| / 2 reaches the factored products' limit of 80
+    return 160.0 / (C - 1)
+
+
+@pytest.mark.parametrize("side", [0.95, 1.05])
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_channel_gate_near_factored_limit(gpu_lib, side, C, dtype):
+    # a few key channels decay at a constant rate whose half-span inside a
+    # chunk sits just below (factored products, factors near e^+-76) or just
+    # above (exact per-element path) the switch; the others follow the usual
+    # distribution
+    inp = synth.make_inputs(1, 3 * C + 13, 2, 128, 64, dtype=dtype, gate="channel",
+                            chunk=C, seed=50 + C, s0_std=0.1)
+    la = -side * _channel_threshold(C)
+    chans = [0, 5, 77, 127]
+    inp.log_alpha[..., chans] = la
+    inp.f64["log_alpha"] = inp.log_alpha.double().numpy()
+    check(inp, name=f"channel_near_limit C={C} log_alpha={la:.3f}")
 
 
 # ---------------------------------------------------- segmented state pass ---
@@ -234,70 +253,56 @@ def test_varlen_training_forward_sampled(gpu_lib, name):
 # ragged last segments, single-segment sequences, empty sequences in varlen
 # batches and every dtype / gate / key size.
 
-@pytest.fixture
-def seg_chunks(gpu_lib):
-    yield gdn.set_segment_chunks
-    gdn.set_segment_chunks(0)
-
-
 @pytest.mark.parametrize("L", [1, 2, 3, 5])
 @pytest.mark.parametrize("gate", ["scalar", "none", "channel"])
-def test_segmented_fp32(seg_chunks, L, gate):
+def test_segmented_fp32(gpu_lib, L, gate):
     inp = synth.make_inputs(2, 150, 3, 32, 48, dtype=torch.float32, gate=gate,
                             chunk=16, seed=41, s0_std=0.3)
-    seg_chunks(L)
-    check(inp, name=f"segmented_fp32 L={L}")
+    check(inp, name=f"segmented_fp32 L={L}", seg_chunks=L)
 
 
 @pytest.mark.parametrize("C", [16, 32, 64])
-def test_segmented_fp32_dk128(seg_chunks, C):
+def test_segmented_fp32_dk128(gpu_lib, C):
     inp = synth.make_inputs(1, 333, 2, 128, 64, dtype=torch.float32, gate="channel",
                             chunk=C, seed=42, s0_std=0.1)
-    seg_chunks(2)
-    check(inp, name=f"segmented_fp32_dk128 C={C}")
+    check(inp, name=f"segmented_fp32_dk128 C={C}", seg_chunks=2)
 
 
 @pytest.mark.parametrize("dk,dv", [(16, 16), (64, 32), (128, 128), (128, 256)])
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
-def test_segmented_bf16(seg_chunks, dk, dv, gate):
+def test_segmented_bf16(gpu_lib, dk, dv, gate):
     inp = synth.make_inputs(1, 700, 2, dk, dv, dtype=torch.bfloat16, gate=gate,
                             chunk=64, seed=43, s0_std=0.05)
-    seg_chunks(3)
-    check(inp, name="segmented_bf16")
+    check(inp, name="segmented_bf16", seg_chunks=3)
 
 
 @pytest.mark.parametrize("gate", ["scalar", "none", "channel"])
-def test_segmented_varlen(seg_chunks, gate):
+def test_segmented_varlen(gpu_lib, gate):
     inp = synth.make_inputs(1, 0, 2, 128, 64, dtype=torch.bfloat16, gate=gate,
                             seed=44, lengths=[5, 0, 300, 64, 1, 177, 129, 0],
                             s0_std=0.1)
-    seg_chunks(2)
-    check(inp, name="segmented_varlen")
+    check(inp, name="segmented_varlen", seg_chunks=2)
 
 
-def test_segmented_varlen_fp32_no_s0(seg_chunks):
+def test_segmented_varlen_fp32_no_s0(gpu_lib):
     inp = synth.make_inputs(1, 0, 3, 64, 32, dtype=torch.float32, gate="scalar",
                             chunk=16, seed=45, lengths=[40, 0, 97, 16, 33])
-    seg_chunks(1)
-    check(inp, name="segmented_varlen_fp32")
+    check(inp, name="segmented_varlen_fp32", seg_chunks=1)
 
 
-def test_segmented_deterministic_and_unsplit_agree(seg_chunks):
+def test_segmented_deterministic_and_unsplit_agree(gpu_lib):
     inp = synth.make_inputs(1, 1000, 2, 128, 128, dtype=torch.float32, gate="scalar",
                             seed=46, s0_std=0.1)
-    seg_chunks(-1)
-    o0, s0 = run(inp)
-    seg_chunks(4)
-    o1, s1 = run(inp)
-    o2, s2 = run(inp)
+    o0, s0 = run(inp, seg_chunks=-1)
+    o1, s1 = run(inp, seg_chunks=4)
+    o2, s2 = run(inp, seg_chunks=4)
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     assert slice_err(np64(o1), np64(o0)) < 1e-5
     assert state_err(np64(s1), np64(s0)) < 1e-5
 
 
-def test_segmented_empty_batch_keeps_state(seg_chunks):
+def test_segmented_empty_batch_keeps_state(gpu_lib):
     inp = synth.make_inputs(2, 0, 2, 64, 32, dtype=torch.bfloat16, seed=47,
                             s0_std=1.0)
-    seg_chunks(2)
-    o, sf = run(inp)
+    o, sf = run(inp, seg_chunks=2)
     assert torch.equal(sf.cpu(), inp.s0)

@@ -16,13 +16,13 @@ from gpu_util import TOL, dev, log, np64, slice_err, state_err
 pytestmark = pytest.mark.gpu
 
 
-def check(inp, name=""):
+def check(inp, name="", **kw):
     nh = inp.k.shape[2]
     log(f"[product] {name} q={tuple(inp.q.shape)} nh={nh} dtype={inp.q.dtype} "
         f"gate={inp.gate} C={inp.chunk} seed={inp.seed}")
     d = dev(inp)
     o, sf = gdn.chunk_fwd_product(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0,
-                                  chunk=inp.chunk, cu_seqlens=d.cu_seqlens)
+                                  chunk=inp.chunk, cu_seqlens=d.cu_seqlens, **kw)
     torch.cuda.synchronize()
     f = inp.f64
     cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
@@ -35,12 +35,6 @@ def check(inp, name=""):
     log(f"    err o={eo:.3e} s_final={es:.3e} tol={tol}")
     assert eo < tol and es < tol, (eo, es)
     return o, sf
-
-
-@pytest.fixture
-def seg_chunks(gpu_lib):
-    yield gdn.set_segment_chunks
-    gdn.set_segment_chunks(0)
 
 
 @pytest.mark.parametrize("nh", [1, 2, 4])
@@ -69,11 +63,10 @@ def test_product_varlen(gpu_lib, nh):
 
 
 @pytest.mark.parametrize("L", [1, 3])
-def test_product_segmented(seg_chunks, L):
+def test_product_segmented(gpu_lib, L):
     inp = synth.make_product_inputs(1, 300, 2, 128, 64, 2, dtype=torch.bfloat16,
                                     gate="scalar", chunk=64, seed=64, s0_std=0.05)
-    seg_chunks(L)
-    check(inp, name=f"segmented L={L}")
+    check(inp, name=f"segmented L={L}", seg_chunks=L)
 
 
 def test_product_nh1_equals_chunk_fwd(gpu_lib):

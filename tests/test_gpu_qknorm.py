@@ -22,12 +22,12 @@ pytestmark = pytest.mark.gpu
 RAW = (0.05, 20.0, 0.1)
 
 
-def check(inp, name=""):
+def check(inp, name="", **kw):
     log(f"[qknorm] {name} q={tuple(inp.q.shape)} v={tuple(inp.v.shape)} "
         f"dtype={inp.q.dtype} gate={inp.gate} C={inp.chunk} seed={inp.seed}")
     d = dev(inp)
     o, sf = gdn.chunk_fwd(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, chunk=inp.chunk,
-                          cu_seqlens=d.cu_seqlens, qk_l2norm=True)
+                          cu_seqlens=d.cu_seqlens, qk_l2norm=True, **kw)
     torch.cuda.synchronize()
     f = inp.f64
     cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
@@ -40,12 +40,6 @@ def check(inp, name=""):
     log(f"    err o={eo:.3e} s_final={es:.3e} tol={tol}")
     assert eo < tol and es < tol, (eo, es)
     return o, sf
-
-
-@pytest.fixture
-def seg_chunks(gpu_lib):
-    yield gdn.set_segment_chunks
-    gdn.set_segment_chunks(0)
 
 
 @pytest.mark.parametrize("gate", ["scalar", "none"])
@@ -79,11 +73,10 @@ def test_qknorm_varlen(gpu_lib):
 
 
 @pytest.mark.parametrize("L", [1, 3])
-def test_qknorm_segmented(seg_chunks, L):
+def test_qknorm_segmented(gpu_lib, L):
     inp = synth.make_inputs(1, 600, 2, 128, 64, dtype=torch.bfloat16, gate="scalar",
                             chunk=64, seed=75, s0_std=0.05, raw_qk=RAW)
-    seg_chunks(L)
-    check(inp, name=f"segmented L={L}")
+    check(inp, name=f"segmented L={L}", seg_chunks=L)
 
 
 def test_qknorm_headline_full_size(gpu_lib):
