@@ -24,7 +24,7 @@ import torch
 from . import _lib
 from ._lib import GdnError  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "decode_step_product",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "decode_step", "decode_step_product",
            "chunk_fwd_product", "tree_verify",
            "tree_commit", "FwdPlan", "GdnError",
            "abi_version", "stage_times"]
@@ -111,6 +111,28 @@ def chunk_fwd(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
             _ptr(ws), ws.numel(), _stream(q.device))
     _lib.check(st, name)
     return o, sf
+
+
+def chunk_fwd_noalloc(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
+                      cu_seqlens=None, o=None, s_final=None, seg_chunks: int = 0):
+    """gdn_chunk_fwd_noalloc: the forward with the library's static scratch
+    buffer as its workspace (no workspace argument).  ``o`` / ``s_final`` may
+    be preallocated outputs (then nothing at all is allocated here);
+    otherwise they are created.  Returns (o, s_final)."""
+    lib = _lib.load()
+    _check_cu(cu_seqlens, q)
+    p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens, seg_chunks=seg_chunks)
+    nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+    H, dk, dv = q.shape[2], q.shape[3], v.shape[3]
+    if o is None:
+        o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    if s_final is None:
+        s_final = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+    st = lib.gdn_chunk_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                   _ptr(log_alpha), _ptr(s0), _ptr(o), _ptr(s_final),
+                                   _stream(q.device))
+    _lib.check(st, "gdn_chunk_fwd_noalloc")
+    return o, s_final
 
 
 def chunk_fwd_product(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,

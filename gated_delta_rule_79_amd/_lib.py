@@ -14,6 +14,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 # status codes (include/gdn.h)
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE = 0, 1, 2, 3
 GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 4, 5, 6, 7
+GDN_ERR_SCRATCH = 8
+NOALLOC_SCRATCH_BYTES = 256 << 20  # GDN_NOALLOC_SCRATCH_BYTES
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATE_NONE, GDN_GATE_SCALAR, GDN_GATE_CHANNEL = 0, 1, 2
 
@@ -24,7 +26,7 @@ EXPORTED = (
     "gdn_profile_read",
     "gdn_chunk_fwd_product_workspace", "gdn_chunk_fwd_product",
     "gdn_chunk_fwd_qknorm", "gdn_tree_verify_workspace", "gdn_tree_verify",
-    "gdn_tree_commit", "gdn_decode_step_product",
+    "gdn_tree_commit", "gdn_decode_step_product", "gdn_chunk_fwd_noalloc",
 )
 STAGE_COUNT = 11
 STAGES = ("chunk_map", "fwd_prep", "fwd_scan", "decode", "bwd_states",
@@ -97,6 +99,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_tree_verify.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_decode_step_product.restype = i32
     lib.gdn_decode_step_product.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_chunk_fwd_noalloc.restype = i32
+    lib.gdn_chunk_fwd_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_tree_commit.restype = i32
     lib.gdn_tree_commit.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
     if path is None:

@@ -267,6 +267,9 @@ const char* gdn_status_str(gdn_status s) {
     case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: pointer not 16-byte aligned";
     case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: HIP runtime refused the launch";
+    case GDN_ERR_SCRATCH:
+      return "GDN_ERR_SCRATCH: problem needs more workspace than the library's static "
+             "scratch buffer holds (GDN_NOALLOC_SCRATCH_BYTES)";
   }
   return "GDN_ERR_UNKNOWN";
 }
@@ -302,6 +305,72 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
     return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o,
                                     s_final, ws,
                                     static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+// ---------------------------------------------- forward without a workspace ---
+// The workspace lives in a file-scope device array of fixed size: every GPU
+// the library runs on holds its own copy until the process ends.  Host code
+// never uses the array's name as an address (on the host it is only a
+// stand-in for the symbol): the device address is looked up once per device
+// with hipGetSymbolAddress, with that device current, and kept here.
+
+}  // extern "C"
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on first use).
+hipError_t scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* p, const void* q, const void* k,
+                                 const void* v, const void* beta,
+                                 const void* log_alpha, const float* s0, void* o,
+                                 float* s_final, void* stream) {
+  try {
+    gdn::Problem pp;
+    GDN_TRY(check_chunk_problem(p, &pp));
+    GDN_TRY(check_fwd_pointers(pp, q, k, v, beta, log_alpha, s0, o, s_final));
+    if (gdn::fwd_workspace_bytes(pp) > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_SCRATCH;
+    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    if ((st != nullptr ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev)) != hipSuccess)
+      return GDN_ERR_HIP;
+    void* ws = nullptr;
+    if (scratch_on(dev, &ws) != hipSuccess) return GDN_ERR_HIP;
+    return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o, s_final, ws, st));
   } catch (...) {
     return GDN_ERR_HIP;
   }

@@ -86,7 +86,9 @@ typedef enum {
   GDN_ERR_UNSUPPORTED = 4, /* valid request outside the supported set        */
   GDN_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                */
   GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required      */
-  GDN_ERR_HIP = 7          /* the HIP runtime refused a launch                */
+  GDN_ERR_HIP = 7,         /* the HIP runtime refused a launch                */
+  GDN_ERR_SCRATCH = 8      /* gdn_chunk_fwd_noalloc: the problem needs more
+                              workspace than the static scratch buffer holds */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -153,6 +155,31 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
                          const void* log_alpha, const float* s0, void* o,
                          float* s_final, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* The forward without a workspace argument, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid allocation.  Computes exactly what
+ * gdn_chunk_fwd computes (the same kernels, bit-identical results) but takes
+ * its workspace from a static device array of GDN_NOALLOC_SCRATCH_BYTES
+ * inside the library instead of from the caller.
+ *   - Each GPU the library runs on holds its own copy of the array from the
+ *     first call on that device until the process ends; the first call on a
+ *     device looks up the array's address (no allocation call is made,
+ *     then or ever).
+ *   - Problems whose gdn_chunk_fwd_workspace exceeds the array are refused
+ *     with GDN_ERR_SCRATCH before anything is enqueued (B=1, T=4096, H=16,
+ *     d=128, bf16 needs 89.25 MiB; B=8, T=2048, H=8 needs 153.5 MiB).
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     behind; nothing in it needs to start at any value.  Calls that overlap
+ *     in time on one GPU (several streams, several host threads) race on
+ *     the array and give undefined results: serialise them.
+ * Arguments, layouts and the other errors as gdn_chunk_fwd; `stream`
+ * decides the device. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* p, const void* q, const void* k,
+                                 const void* v, const void* beta,
+                                 const void* log_alpha, const float* s0, void* o,
+                                 float* s_final, void* stream);
 
 /* The forward with q and k normalised inside ("Gated Delta Networks:
  * Improving Mamba2 with Delta Rule", "Method": the block design passes q and

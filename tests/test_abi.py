@@ -343,3 +343,26 @@ def test_decode_product_rejections(lib):
                                        None) == _lib.GDN_ERR_NULL
     assert lib.gdn_decode_step_product(ctypes.byref(p), 2, A, A, A, A, A, None, A,
                                        None) == _lib.GDN_ERR_NULL
+
+
+def test_noalloc_validation_before_launch(lib):
+    # gdn_chunk_fwd_noalloc: same validation as gdn_chunk_fwd, then a size
+    # check against the static scratch buffer, all before any device call
+    def call(p, **ptr):
+        d = dict(q=A, k=A, v=A, beta=A, la=A, s0=None, o=A, sf=None)
+        d.update(ptr)
+        return lib.gdn_chunk_fwd_noalloc(ctypes.byref(p), d["q"], d["k"], d["v"],
+                                         d["beta"], d["la"], d["s0"], d["o"], d["sf"],
+                                         None)
+    assert call(prob(T=4096, H=16)) == 7                 # valid: reaches the launch hook
+    assert call(prob(T=4096, H=16), q=None) == 1
+    assert call(prob(T=4096, H=16), o=A + 8) == 5
+    assert call(prob(dk=48)) == 4
+    # workspace sizes around the limit
+    limit = _lib.NOALLOC_SCRATCH_BYTES
+    fits = prob(B=8, T=2048, H=8)
+    big = prob(B=4, T=4096, H=16)
+    assert ws_bytes(lib, fits)[1] <= limit < ws_bytes(lib, big)[1]
+    assert call(fits) == 7
+    assert call(big) == 8                                # GDN_ERR_SCRATCH
+    assert "scratch" in lib.gdn_status_str(8).decode()
