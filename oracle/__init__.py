@@ -17,6 +17,10 @@ Sources (cited by page title and section):
   * "TreeWY: Speculative Verification for Gated DeltaNet Hybrids" (summary in
     the list of related papers) -- draft-tree verification with one
     triangular solve and a commit of the accepted state only.
+  * "Linear Attention Architectures: Mechanisms, Trade-offs, and Cross-Layer
+    Routing" (abstract) and its related-paper entry "Gated DeltaNet-2:
+    Decoupling Erase and Write in Linear Attention" -- name Gated
+    DeltaNet-2's separate erase and write control without a formula.
 
 Parity status per function is listed in ``gdn_oracle.__doc__``.
 """
@@ -38,4 +42,8 @@ from .gdn_oracle import (  # noqa: F401
     tree_path,
     tree_wy_bruteforce,
     normwise_rel_err,
+    gdn2_fwd,
+    gdn2_fwd_chain,
+    gdn2_decode,
+    gdn2_chunked_bruteforce,
 )

@@ -41,12 +41,19 @@ Readings where the pages are silent (each is listed in the design notes):
     to the chain (a path tree is a sequence, a star tree is independent
     single steps, every root path is a sequence) and by the tree WY form.
 
+  * Gated DeltaNet-2 (only named by the pages, as decoupling erase and
+    write): the strength of the erase factor and of the write get separate
+    values (gdn2_fwd).  Parity with an external definition is UNPINNED; the
+    pins fix its reductions (to the gated delta rule, to gated linear
+    attention, to pure erasure) and its overwrite property.
+
 Parity pins (tests/test_oracle_pins.py): chunked brute-force form, orthonormal
 retrieval, beta = 0 gate product, DeltaNet limit, norm bound, alpha -> 0
 erasure, gated-linear-attention limit, SGD reading, T = 1 closed form,
 equal-channel reduction, boundary semantics, finite differences for the
 adjoint, plus a hand-worked golden example.  Nothing here is "parity
-unpinned" except the per-channel gate's match to an external definition.
+unpinned" except the matches of the per-channel gate, the Householder
+products, the draft trees and Gated DeltaNet-2 to external definitions.
 """
 
 from __future__ import annotations
@@ -447,6 +454,123 @@ def gdn_chunked_bruteforce(q, k, v, beta, log_alpha, m0, gate: str, C: int):
         Tm = np.linalg.inv(np.eye(c) + A)
         U = Tm @ (bt[:, None] * V)
         W = Tm @ (bt[:, None] * K * np.exp(g))
+        E = U - W @ M
+        o[s:e_] = (Q * np.exp(g)) @ M + P @ E
+        M = np.exp(g[-1])[:, None] * M + (K * np.exp(g[-1][None, :] - g)).T @ E
+    return o, M
+
+
+# --------------------------------------------------------------------------
+# Gated DeltaNet-2: decoupled erase and write strengths ("Linear Attention
+# Architectures: Mechanisms, Trade-offs, and Cross-Layer Routing", abstract,
+# and the related-paper entry "Gated DeltaNet-2: Decoupling Erase and Write
+# in Linear Attention"; the pages name the method and say it generalises
+# Gated DeltaNet and Kimi Delta Attention, but print no formula)
+# --------------------------------------------------------------------------
+
+def gdn2_fwd_chain(q, k, v, erase, write, log_alpha, m0, gate: str):
+    """One (sequence, head) of the reading taken here: the gated delta rule's
+    single strength beta_t does two jobs, erasing the old value stored under
+    k_t (the factor I - beta k k^T) and writing the new one (beta v k^T); the
+    decoupled rule gives each job its own strength,
+
+        S_t = S_{t-1} D_t (I - erase_t k_t k_t^T) + write_t v_t k_t^T,
+
+    D_t = alpha_t (scalar gate) or Diag(alpha_t) (per-channel gate), so that
+    erase = write is Gated DeltaNet (scalar gate) or the per-channel
+    (Kimi-Delta-style) reading, and erase = 0 is gated linear attention.
+    Stored orientation M = S^T: Mt = D M, e = write v - erase Mt^T k,
+    M = Mt + k e^T, o = M^T q.  Shapes as gdn_fwd_chain; erase, write [T].
+    Parity with any external definition of Gated DeltaNet-2 is UNPINNED."""
+    T, dk = k.shape
+    dv = v.shape[1]
+    M = np.array(m0, dtype=np.float64, copy=True)
+    o = np.zeros((T, dv))
+    for t in range(T):
+        a = _gate_rows(None if log_alpha is None else log_alpha[t], gate, dk)
+        Mt = a[:, None] * M                              # decay first
+        e = write[t] * v[t] - erase[t] * (Mt.T @ k[t])   # write minus erased value
+        M = Mt + np.outer(k[t], e)
+        o[t] = M.T @ q[t]
+    return o, M
+
+
+def gdn2_fwd(q, k, v, erase, write, log_alpha, s0=None, gate: str = "scalar",
+             cu_seqlens=None):
+    """Whole batch of :func:`gdn2_fwd_chain`; shapes and returns as
+    :func:`gdn_fwd` with erase and write [B,T,H] in place of beta."""
+    assert gate in GATES
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    nseq = B if cu_seqlens is None else len(cu_seqlens) - 1
+    o = np.zeros((B, T, H, dv))
+    sf = np.zeros((nseq, H, dk, dv))
+    for b, t0, t1, n in _segments(B, T, cu_seqlens):
+        for h in range(H):
+            m0 = np.zeros((dk, dv)) if s0 is None else s0[n, h]
+            la = None if gate == "none" else log_alpha[b, t0:t1, h]
+            o[b, t0:t1, h], sf[n, h] = gdn2_fwd_chain(
+                q[b, t0:t1, h], k[b, t0:t1, h], v[b, t0:t1, h], erase[b, t0:t1, h],
+                write[b, t0:t1, h], la, m0, gate)
+    return o, sf
+
+
+def gdn2_decode(q, k, v, erase, write, log_alpha, state, gate: str = "scalar"):
+    """One token per (sequence, head) of the decoupled rule: q,k [N,H,dk],
+    v [N,H,dv], erase, write [N,H], log_alpha [N,H] / [N,H,dk] / None,
+    state [N,H,dk,dv].  Returns (o [N,H,dv], new state)."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((N, H, dv))
+    new = np.array(state, dtype=np.float64, copy=True)
+    for n in range(N):
+        for h in range(H):
+            la = None if gate == "none" else log_alpha[n, h][None]
+            oo, mm = gdn2_fwd_chain(q[n, h][None], k[n, h][None], v[n, h][None],
+                                    erase[n, h][None], write[n, h][None], la,
+                                    state[n, h], gate)
+            o[n, h] = oo[0]
+            new[n, h] = mm
+    return o, new
+
+
+def gdn2_chunked_bruteforce(q, k, v, erase, write, log_alpha, m0, gate: str, C: int):
+    """Chunkwise form of one chain of the decoupled rule with an explicit
+    dense inverse.  Unrolling e_r = write_r v_r - erase_r Mt_r^T k_r over a
+    chunk gives (I + A) E = diag(write) V - diag(erase * gamma) K M0 with
+    A_ri = erase_r exp(g_r - g_i) k_r.k_i (i < r): the erase strength enters
+    A and W, the write strength only U:
+        T = (I + A)^-1,  U = T diag(write) V,  W = T diag(erase*gamma) K,
+        E = U - W M0,    O = diag(gamma) Q M0 + (Q K^T o Gamma) E,
+        M_c = gamma_c M0 + (K o exp(g_c - g))^T E
+    (per-channel gate: the decays move inside the key sums as in
+    gdn_chunked_bruteforce).  Checks the equations, not the GPU."""
+    T, dk = k.shape
+    dv = v.shape[1]
+    M = np.array(m0, dtype=np.float64, copy=True)
+    o = np.zeros((T, dv))
+    for s in range(0, T, C):
+        e_ = min(T, s + C)
+        c = e_ - s
+        K, Q, V = k[s:e_], q[s:e_], v[s:e_]
+        er, wr = erase[s:e_], write[s:e_]
+        if gate == "none":
+            g = np.zeros((c, dk))
+        elif gate == "scalar":
+            g = np.repeat(np.cumsum(log_alpha[s:e_])[:, None], dk, axis=1)
+        else:
+            g = np.cumsum(log_alpha[s:e_], axis=0)
+        A = np.zeros((c, c))
+        P = np.zeros((c, c))
+        for r in range(c):
+            for i in range(r + 1):
+                d = np.exp(g[r] - g[i])
+                P[r, i] = np.sum(Q[r] * K[i] * d)
+                if i < r:
+                    A[r, i] = er[r] * np.sum(K[r] * K[i] * d)
+        Tm = np.linalg.inv(np.eye(c) + A)
+        U = Tm @ (wr[:, None] * V)
+        W = Tm @ (er[:, None] * K * np.exp(g))
         E = U - W @ M
         o[s:e_] = (Q * np.exp(g)) @ M + P @ E
         M = np.exp(g[-1])[:, None] * M + (K * np.exp(g[-1][None, :] - g)).T @ E

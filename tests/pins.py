@@ -350,3 +350,106 @@ def tree_wy_matches_recurrence(tree_wy, tree_fwd, gate, seed=25):
     lah = None if la is None else la[0, :, 0]
     o2 = tree_wy(q[0, :, 0], k[0, :, 0], v[0, :, 0], beta[0, :, 0], lah, par, s0[0, 0], gate)
     return np.max(np.abs(o1[0, :, 0] - o2))
+
+
+# ------------------------------------------------ Gated DeltaNet-2 ---
+# Checks of the decoupled erase/write reading, written against a callable
+# with the signature of oracle.gdn2_fwd_chain(q, k, v, erase, write,
+# log_alpha, m0, gate).  Everything compared against is fixed without the
+# decoupled oracle: the pinned gated delta rule, explicit sums and explicit
+# matrix products.
+
+def _g2_problem(r, T, dk, dv, gate, s0_std=0.5):
+    q = unit(r.standard_normal((T, dk)))
+    k = unit(r.standard_normal((T, dk)))
+    v = r.standard_normal((T, dv))
+    er = 1.0 / (1.0 + np.exp(-r.standard_normal(T)))
+    wr = 1.0 / (1.0 + np.exp(-r.standard_normal(T)))
+    if gate == "none":
+        la = None
+    elif gate == "scalar":
+        la = -np.logaddexp(0.0, r.standard_normal(T) - 2.0)
+    else:
+        la = -np.logaddexp(0.0, r.standard_normal((T, dk)) - 2.0)
+    m0 = r.standard_normal((dk, dv)) * s0_std
+    return q, k, v, er, wr, la, m0
+
+
+def _decay_rows(la, t, gate, dk):
+    """Per-row decay of token t (vector of dk)."""
+    if gate == "none":
+        return np.ones(dk)
+    if gate == "scalar":
+        return np.full(dk, np.exp(la[t]))
+    return np.exp(la[t])
+
+
+def g2_equal_strengths_is_gdn(g2, gdn_chain, gate, T=23, dk=8, dv=5, seed=31):
+    """erase = write = beta: the gated delta rule (per-channel gate: the
+    per-channel reading), i.e. the pinned gdn_fwd_chain."""
+    r = rng(seed)
+    q, k, v, er, _, la, m0 = _g2_problem(r, T, dk, dv, gate)
+    o1, m1 = g2(q, k, v, er, er, la, m0, gate)
+    o2, m2 = gdn_chain(q, k, v, er, la, m0, gate)
+    return max(np.max(np.abs(o1 - o2)), np.max(np.abs(m1 - m2)))
+
+
+def g2_no_erase_is_linear_attention(g2, gate, T=17, dk=7, dv=4, seed=32):
+    """erase = 0: nothing is erased, every token only adds write_s v_s k_s^T
+    to the decayed state, so o_t is the gated-linear-attention sum
+        o_t = (D_t..D_1 M0)^T q_t + sum_{s<=t} write_s (q_t . (d_ts * k_s)) v_s
+    with d_ts the product of the decays of tokens s+1..t (per channel),
+    for any keys."""
+    r = rng(seed)
+    q, k, v, _, wr, la, m0 = _g2_problem(r, T, dk, dv, gate)
+    o, m = g2(q, k, v, np.zeros(T), wr, la, m0, gate)
+    worst = 0.0
+    for t in range(T):
+        dec0 = np.ones(dk)
+        for u in range(t + 1):
+            dec0 = dec0 * _decay_rows(la, u, gate, dk)
+        want = (dec0[:, None] * m0).T @ q[t]
+        for s in range(t + 1):
+            d = np.ones(dk)
+            for u in range(s + 1, t + 1):
+                d = d * _decay_rows(la, u, gate, dk)
+            want = want + wr[s] * np.dot(q[t], d * k[s]) * v[s]
+        worst = max(worst, np.max(np.abs(o[t] - want)))
+    return worst
+
+
+def g2_no_write_is_erasure(g2, gate, T=11, dk=6, dv=4, seed=33):
+    """write = 0: the state only decays and is projected away from each key,
+    M_t = (I - erase_t k_t k_t^T) D_t M_{t-1} as explicit dk x dk matrices,
+    and o_t = M_t^T q_t."""
+    r = rng(seed)
+    q, k, v, er, _, la, m0 = _g2_problem(r, T, dk, dv, gate)
+    o, m = g2(q, k, v, er, np.zeros(T), la, m0, gate)
+    M = m0.copy()
+    worst = 0.0
+    for t in range(T):
+        Pm = np.eye(dk) - er[t] * np.outer(k[t], k[t])
+        M = Pm @ np.diag(_decay_rows(la, t, gate, dk)) @ M
+        worst = max(worst, np.max(np.abs(o[t] - M.T @ q[t])))
+    return max(worst, np.max(np.abs(m - M)))
+
+
+def g2_full_erase_stores_write(g2, gate, T=13, dk=8, dv=5, seed=34):
+    """erase = 1 with unit keys: the old value under k_t is removed entirely
+    and write_t v_t stored in its place, whatever the history and gate:
+    M_t^T k_t = write_t v_t (read with q_t = k_t)."""
+    r = rng(seed)
+    q, k, v, _, wr, la, m0 = _g2_problem(r, T, dk, dv, gate, s0_std=1.0)
+    o, _ = g2(q, k, v, np.ones(T), wr * 3.0, la, m0, gate)
+    o2, _ = g2(k, k, v, np.ones(T), wr * 3.0, la, m0, gate)
+    return max(np.max(np.abs(o2[t] - 3.0 * wr[t] * v[t])) for t in range(T))
+
+
+def g2_chunked_equals_recurrence(g2, g2_chunked, gate, C, T=37, dk=8, dv=5, seed=35):
+    """The decoupled chunk equations (erase in A and W, write in U) give the
+    recurrence's outputs and final state for any chunk size."""
+    r = rng(seed + C)
+    q, k, v, er, wr, la, m0 = _g2_problem(r, T, dk, dv, gate)
+    o1, m1 = g2(q, k, v, er, wr, la, m0, gate)
+    o2, m2 = g2_chunked(q, k, v, er, wr, la, m0, gate, C)
+    return max(np.max(np.abs(o1 - o2)), np.max(np.abs(m1 - m2)))

@@ -351,3 +351,57 @@ def test_tree_relabelling():
 def test_tree_rejects_parent_after_child():
     with pytest.raises(AssertionError):
         oracle.tree_path([-1, 2, 0], 1)
+
+
+# ------------------------------------------------ Gated DeltaNet-2 ---
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_g2_equal_strengths_is_gdn(gate):
+    assert pins.g2_equal_strengths_is_gdn(oracle.gdn2_fwd_chain, oracle.gdn_fwd_chain,
+                                          gate) < 1e-13
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_g2_no_erase_is_linear_attention(gate):
+    assert pins.g2_no_erase_is_linear_attention(oracle.gdn2_fwd_chain, gate) < 1e-12
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_g2_no_write_is_erasure(gate):
+    assert pins.g2_no_write_is_erasure(oracle.gdn2_fwd_chain, gate) < 1e-12
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_g2_full_erase_stores_write(gate):
+    assert pins.g2_full_erase_stores_write(oracle.gdn2_fwd_chain, gate) < 1e-12
+
+
+@pytest.mark.parametrize("C", [1, 4, 16])
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_g2_chunked_form(gate, C):
+    assert pins.g2_chunked_equals_recurrence(oracle.gdn2_fwd_chain,
+                                             oracle.gdn2_chunked_bruteforce, gate, C) < 1e-11
+
+
+def test_g2_batch_and_decode_wrap_the_chain():
+    r = pins.rng(36)
+    B, T, H, dk, dv = 2, 9, 3, 6, 4
+    q = pins.unit(r.standard_normal((B, T, H, dk)))
+    k = pins.unit(r.standard_normal((B, T, H, dk)))
+    v = r.standard_normal((B, T, H, dv))
+    er, wr = r.random((B, T, H)), r.random((B, T, H)) * 2
+    la = -r.random((B, T, H, dk))
+    s0 = r.standard_normal((B, H, dk, dv))
+    o, sf = oracle.gdn2_fwd(q, k, v, er, wr, la, s0, "channel")
+    for b in range(B):
+        for h in range(H):
+            oc, mc = oracle.gdn2_fwd_chain(q[b, :, h], k[b, :, h], v[b, :, h], er[b, :, h],
+                                           wr[b, :, h], la[b, :, h], s0[b, h], "channel")
+            assert np.max(np.abs(o[b, :, h] - oc)) < 1e-14
+            assert np.max(np.abs(sf[b, h] - mc)) < 1e-14
+    # decode of the next token continues the forward
+    od, st = oracle.gdn2_decode(q[:, 0], k[:, 0], v[:, 0], er[:, 0], wr[:, 0], la[:, 0],
+                                s0, "channel")
+    o1, s1 = oracle.gdn2_fwd(q[:, :1], k[:, :1], v[:, :1], er[:, :1], wr[:, :1], la[:, :1],
+                             s0, "channel")
+    assert np.max(np.abs(od - o1[:, 0])) < 1e-14 and np.max(np.abs(st - s1)) < 1e-14

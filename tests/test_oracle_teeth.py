@@ -223,3 +223,41 @@ def test_reference_oracle_passes_tree_pins():
 def test_tree_mutant_is_caught(name):
     mod = _mutant(*TREE_MUTANTS[name])
     assert not _tree_pins_pass(mod), name
+
+
+# ------------------------------------------------ Gated DeltaNet-2 ---
+
+def _g2_pins_pass(mod):
+    ok = True
+    for gate in ("none", "scalar", "channel"):
+        ok &= pins.g2_equal_strengths_is_gdn(mod.gdn2_fwd_chain, ref_mod.gdn_fwd_chain,
+                                             gate) < 1e-13
+        ok &= pins.g2_no_erase_is_linear_attention(mod.gdn2_fwd_chain, gate) < 1e-12
+        ok &= pins.g2_no_write_is_erasure(mod.gdn2_fwd_chain, gate) < 1e-12
+        ok &= pins.g2_full_erase_stores_write(mod.gdn2_fwd_chain, gate) < 1e-12
+    return bool(ok)
+
+
+G2_LINE = ("        e = write[t] * v[t] - erase[t] * (Mt.T @ k[t])"
+           "   # write minus erased value\n")
+G2_MUTANTS = {
+    "erase and write swapped": (G2_LINE, "        e = erase[t] * v[t] - write[t] * (Mt.T @ k[t])\n"),
+    "write strength used for both": (G2_LINE, "        e = write[t] * (v[t] - Mt.T @ k[t])\n"),
+    "erase strength used for both": (G2_LINE, "        e = erase[t] * (v[t] - Mt.T @ k[t])\n"),
+    "erase of the undecayed state": (G2_LINE,
+                                     "        e = write[t] * v[t] - erase[t] * (M.T @ k[t])\n"),
+    "write decayed with the state": (
+        "        e = write[t] * v[t] - erase[t] * (Mt.T @ k[t])   # write minus erased value\n"
+        "        M = Mt + np.outer(k[t], e)\n",
+        "        e = write[t] * v[t] - erase[t] * (Mt.T @ k[t])\n"
+        "        M = Mt + np.outer(k[t], e - write[t] * v[t] + write[t] * a[0] * v[t])\n"),
+}
+
+
+def test_reference_oracle_passes_g2_pins():
+    assert _g2_pins_pass(ref_mod)
+
+
+@pytest.mark.parametrize("name", sorted(G2_MUTANTS))
+def test_g2_mutant_is_caught(name):
+    assert not _g2_pins_pass(_mutant(*G2_MUTANTS[name]))
