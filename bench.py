@@ -4,11 +4,14 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one gdn_chunk_fwd call (every kernel of the forward) over one batch
-of synthetic inputs already resident in device memory.  Default workload:
-B=1, T=4096, H=16, dk=dv=128, chunk 64, bf16 inputs, fp32 state.  Prints ONE
-JSON line with tokens/s, the roofline position of the dominant kernel
-(per-kernel device time from HIP events recorded by the library on the launch
-stream) and the fp64 CPU oracle timed on this host as a baseline.
+of synthetic inputs already resident in device memory, with L2 and the
+Infinity Cache evicted before it (median of K such calls; back-to-back
+"warm" calls are reported beside it).  Default workload: B=1, T=4096, H=16,
+dk=dv=128, chunk 64, bf16 inputs, fp32 state.  Prints ONE JSON line with
+tokens/s, the roofline position of the forward call (its algorithmic bytes
+over the summed per-kernel device time from HIP events recorded by the
+library on the launch stream) and the fp64 CPU oracle timed on this host's
+cores as a baseline.
 
 Other entry points (same JSON shape, their own metric string):
     --mode bwd      gdn_chunk_bwd alone      (default workload varlen_16k_dv256)
@@ -103,61 +106,112 @@ def decode_bytes(N, H, dk, dv, s_io):
     return N * H * (8 * dk * dv + (2 * dk + 2 * dv) * s_io + 8)
 
 
-def cpu_baseline_bwd(inp, budget_s):
-    """The oracle's adjoint on whole (sequence, head) chains, one thread, until
-    about budget_s seconds; rate scaled to the whole workload's tokens."""
-    import numpy as np
+def host_cpu(max_workers=16):
+    """Worker processes the CPU baseline may use (the cores this process may
+    run on, at most ``max_workers``: the host's share for one GPU) and the
+    CPU model string."""
+    P = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return max(1, min(P, max_workers)), model
+
+
+_ORACLE_JOB = None
+
+
+def _oracle_unit(u):
     from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t = time.perf_counter()
+        _ORACLE_JOB(u)
+        return time.perf_counter() - t
+
+
+def cpu_oracle_rate(job, units, work_per_unit, budget_s, what, unit="tokens/s"):
+    """The oracle as it stands, run as ``job(u)`` over independent units
+    (whole (sequence, head) chains, decode rows, trees) by P forked worker
+    processes with one BLAS thread each; rounds over all units repeat until
+    about ``budget_s`` seconds of wall clock.  Timed: the compute only (the
+    pool is started and warmed first).  Call before the GPU is touched, so
+    the workers hold no GPU state.  Returns the cpu_baseline record."""
+    global _ORACLE_JOB
+    import multiprocessing as mp
+    units = list(units)
+    P, model = host_cpu()
+    P = min(P, len(units))
+    _ORACLE_JOB = job
+    try:
+        with mp.get_context("fork").Pool(P) as pool:
+            pool.map(_oracle_unit, units[:P], chunksize=1)        # warm the workers
+            rounds, work, serial = 0, 0.0, 0.0
+            t0 = time.perf_counter()
+            while True:
+                per = pool.map(_oracle_unit, units, chunksize=1)
+                rounds += 1
+                serial += sum(per)
+                work += sum(work_per_unit(u) for u in units)
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            dt = time.perf_counter() - t0
+    finally:
+        _ORACLE_JOB = None
+    return {"value": work / dt, "unit": unit, "cores": P, "kind": "oracle",
+            "cpu_model": model,
+            "single_worker_value": work / serial,
+            "sample": f"{what}: {len(units)} units x {rounds} round(s) in {dt:.1f} s on "
+                      f"{P} worker processes (one thread each) of {model}"}
+
+
+def _chains(inp):
+    """(batch row, first token, end token, state index) of every sequence."""
+    B, T = inp.q.shape[:2]
+    if inp.cu_seqlens is None:
+        return [(b, 0, T, b) for b in range(B)]
+    cu = inp.cu_seqlens.numpy()
+    return [(0, int(cu[n]), int(cu[n + 1]), n) for n in range(len(cu) - 1)]
+
+
+def cpu_baseline_bwd(inp, budget_s):
+    """The oracle's adjoint on whole (sequence, head) chains of the workload
+    (P workers); tokens/s of the whole workload."""
+    import numpy as np
     import oracle
     f = inp.f64
-    T_all = f["q"].shape[1]
-    H = f["q"].shape[2]
-    cu = (np.array([0, T_all]) if inp.cu_seqlens is None else inp.cu_seqlens.numpy())
-    units = [(s, h) for s in range(len(cu) - 1) for h in range(H)]
-    done_tok = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        for s, h in units:
-            a, b = int(cu[s]), int(cu[s + 1])
-            sl = lambda x: None if x is None else x[0, a:b, h]
-            m0 = np.zeros((f["q"].shape[3], f["v"].shape[3]))
-            oracle.gdn_bwd_chain(sl(f["q"]), sl(f["k"]), sl(f["v"]), sl(f["beta"]),
-                                 sl(f["log_alpha"]), m0, sl(f["do"]), None, inp.gate)
-            done_tok += b - a
-            if time.perf_counter() - t0 > budget_s:
-                break
-    dt = time.perf_counter() - t0
-    frac = done_tok / float(T_all * H)
-    return {"value": T_all * frac / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done_tok} of {T_all * H} token-heads of the backward as whole "
-                      f"(sequence, head) chains ({dt:.1f} s, 1 thread); tokens/s scaled "
-                      "to the whole workload"}
+    H, dk, dv = f["q"].shape[2], f["q"].shape[3], f["v"].shape[3]
+    units = [(c, h) for c in _chains(inp) for h in range(H)]
 
+    def job(u):
+        (b, a, e, n), h = u
+        sl = lambda x: None if x is None else x[b, a:e, h]
+        m0 = np.zeros((dk, dv)) if f["s0"] is None else f["s0"][n, h]
+        dm = None if f["ds_final"] is None else f["ds_final"][n, h]
+        oracle.gdn_bwd_chain(sl(f["q"]), sl(f["k"]), sl(f["v"]), sl(f["beta"]),
+                             sl(f["log_alpha"]), m0, sl(f["do"]), dm, inp.gate)
+
+    return cpu_oracle_rate(job, units, lambda u: (u[0][2] - u[0][1]) / H, budget_s,
+                           "oracle adjoint (backward) over every (sequence, head) chain")
 
 def cpu_baseline_decode(inp, budget_s):
-    """The oracle's decode step on (sequence, head) rows, one thread, until
-    about budget_s seconds; rate scaled to the whole batch (tokens/s)."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
+    """The oracle's decode step on every sequence (all heads per unit), P
+    workers; tokens/s of the whole batch (one token per sequence)."""
     import oracle
     f = inp.f64
-    N, _, H, dk = f["q"].shape
-    rows = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        for n in range(N):
-            la = None if f["log_alpha"] is None else f["log_alpha"][n:n + 1, 0]
-            oracle.gdn_decode(f["q"][n:n + 1, 0], f["k"][n:n + 1, 0], f["v"][n:n + 1, 0],
-                              f["beta"][n:n + 1, 0], la, f["s0"][n:n + 1], inp.gate)
-            rows += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-    dt = time.perf_counter() - t0
-    steps_per_s = (rows / N) / dt
-    return {"value": N * steps_per_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} of {N} sequences x {H} heads of one decode step "
-                      f"({dt:.1f} s, 1 thread); tokens/s scaled to the whole batch"}
+    N = f["q"].shape[0]
 
+    def job(n):
+        la = None if f["log_alpha"] is None else f["log_alpha"][n:n + 1, 0]
+        oracle.gdn_decode(f["q"][n:n + 1, 0], f["k"][n:n + 1, 0], f["v"][n:n + 1, 0],
+                          f["beta"][n:n + 1, 0], la, f["s0"][n:n + 1], inp.gate)
+
+    return cpu_oracle_rate(job, range(N), lambda n: 1.0, budget_s,
+                           "oracle decode step, one unit per sequence (all heads)")
 
 def time_calls(fn, steps, warmup, cold_steps=0):
     """Median-free K-call timing with events on the current stream, plus an
@@ -218,31 +272,23 @@ def product_algorithmic(B, T, H, dk, dv, C, nh, s_io):
 
 
 def cpu_baseline_product(inp, budget_s):
-    """The fp64 oracle of the Householder-product forward on whole sequences
-    of the workload (all heads of a sequence per call) until about
-    ``budget_s`` seconds; one BLAS thread.  Scaled to the workload's tokens."""
-    from threadpoolctl import threadpool_limits
+    """The fp64 oracle of the Householder-product forward on every
+    (sequence, head) chain, P workers; tokens/s of the whole workload."""
     import oracle
     f = inp.f64
     B, T, H = f["q"].shape[:3]
-    done = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        for h in range(H):
-            sl = slice(h, h + 1)
-            la = None if f["log_alpha"] is None else f["log_alpha"][:1, :, sl]
-            oracle.deltaproduct_fwd(f["q"][:1, :, sl], f["k"][:1, :, :, sl], f["v"][:1, :, :, sl],
-                                    f["beta"][:1, :, :, sl], la, None, inp.gate)
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-    dt = time.perf_counter() - t0
-    frac = done / float(B * H)
-    return {"value": B * T * frac / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {B * H} (sequence, head) chains of T={T} tokens with "
-                      f"{inp.k.shape[2]} steps each ({dt:.1f} s, 1 thread); tokens/s scaled "
-                      "to the whole workload"}
+    units = [(b, h) for b in range(B) for h in range(H)]
 
+    def job(u):
+        b, h = u
+        bs, sl = slice(b, b + 1), slice(h, h + 1)
+        la = None if f["log_alpha"] is None else f["log_alpha"][bs, :, sl]
+        oracle.deltaproduct_fwd(f["q"][bs, :, sl], f["k"][bs, :, :, sl], f["v"][bs, :, :, sl],
+                                f["beta"][bs, :, :, sl], la, None, inp.gate)
+
+    return cpu_oracle_rate(job, units, lambda u: T / H, budget_s,
+                           f"oracle Householder-product forward ({inp.k.shape[2]} steps per "
+                           "token) over every (sequence, head) chain")
 
 def main_product(args):
     """Householder-product forward (gdn_chunk_fwd_product) on B1 T4096 H16
@@ -250,13 +296,14 @@ def main_product(args):
     import torch
     import gated_delta_rule_79_amd as gdn
     from gated_delta_rule_79_amd import synth
-    if not torch.cuda.is_available():
+    if torch.cuda.device_count() < 1:   # counts devices without initialising HIP
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     B, T, H, dk, dv, C, nh = 1, 4096, 16, 128, 128, 64, args.nh
     wl = f"product_t{T}_h{H}_nh{nh}"
     inp = synth.make_product_inputs(B, T, H, dk, dv, nh, dtype=torch.bfloat16,
                                     gate="scalar", chunk=C, seed=1006)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_product(inp, args.cpu_budget)
     d = inp.to("cuda")
     fn = lambda: gdn.chunk_fwd_product(d.q, d.k, d.v, d.beta, d.log_alpha, None, chunk=C)
     ms, cold = time_calls(fn, args.steps, args.warmup, args.cold_steps)
@@ -287,7 +334,6 @@ def main_product(args):
                      "path_frac_mfma_bf16": round(flops / (ms * 1e-3) / 1e12 /
                                                   MFMA_BF16_PEAK_TFLOPS, 4)},
     }
-    cpu = None if args.no_cpu_baseline else cpu_baseline_product(inp, args.cpu_budget)
     if cpu is not None:
         cpu["value"] = round(cpu["value"], 1)
     out["cpu_baseline"] = cpu
@@ -321,32 +367,24 @@ def tree_algorithmic(N, n, H, dk, dv, s_io, s_gate, path_nodes):
 
 
 def cpu_baseline_tree(inp, parent, accepted, budget_s):
-    """The fp64 oracle's verification and commit on whole trees (all heads)
-    until about ``budget_s`` seconds; one BLAS thread.  Scaled to the
-    workload's nodes."""
-    from threadpoolctl import threadpool_limits
+    """The fp64 oracle's verification and commit on every tree (all heads per
+    unit), P workers; nodes/s."""
     import oracle
     f = inp.f64
     N, n = f["q"].shape[:2]
     par, acc = parent.numpy(), accepted.numpy()
-    done = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        for m in range(N):
-            sl = slice(m, m + 1)
-            la = None if f["log_alpha"] is None else f["log_alpha"][sl]
-            oracle.tree_fwd(f["q"][sl], f["k"][sl], f["v"][sl], f["beta"][sl], la,
-                            par[sl], f["s0"][sl], inp.gate)
-            oracle.tree_commit(f["k"][sl], f["v"][sl], f["beta"][sl], la, par[sl], acc[sl],
-                               f["s0"][sl], inp.gate)
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-    dt = time.perf_counter() - t0
-    return {"value": done * n / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {N} trees of {n} nodes, all heads, verification and "
-                      f"commit ({dt:.1f} s, 1 thread)"}
 
+    def job(m):
+        sl = slice(m, m + 1)
+        la = None if f["log_alpha"] is None else f["log_alpha"][sl]
+        oracle.tree_fwd(f["q"][sl], f["k"][sl], f["v"][sl], f["beta"][sl], la,
+                        par[sl], f["s0"][sl], inp.gate)
+        oracle.tree_commit(f["k"][sl], f["v"][sl], f["beta"][sl], la, par[sl], acc[sl],
+                           f["s0"][sl], inp.gate)
+
+    return cpu_oracle_rate(job, range(N), lambda m: float(n), budget_s,
+                           f"oracle verification and commit of every tree of {n} nodes",
+                           unit="nodes/s")
 
 def main_tree(args):
     """Speculative round on draft trees: gdn_tree_verify then gdn_tree_commit
@@ -355,7 +393,7 @@ def main_tree(args):
     import torch
     import gated_delta_rule_79_amd as gdn
     from gated_delta_rule_79_amd import synth
-    if not torch.cuda.is_available():
+    if torch.cuda.device_count() < 1:   # counts devices without initialising HIP
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     N, n, H, dk, dv = 256, 16, 32, 128, 128
@@ -363,6 +401,8 @@ def main_tree(args):
     inp, parent, accepted = synth.make_tree_inputs(N, n, H, dk, dv, dtype=torch.bfloat16,
                                                    gate="scalar", chunk=n, seed=1007,
                                                    s0_std=0.02)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_tree(inp, parent, accepted,
+                                                              args.cpu_budget)
     d = inp.to("cuda")
     par, acc = parent.cuda(), accepted.cuda()
     state = d.s0.clone()
@@ -406,8 +446,6 @@ def main_tree(args):
                      "alg_bytes_per_step": int(vb + cb), "alg_flops_per_step": int(vf + cf),
                      "path_frac_hbm": round((vb + cb) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
-    cpu = None if args.no_cpu_baseline else cpu_baseline_tree(inp, parent, accepted,
-                                                              args.cpu_budget)
     if cpu is not None:
         cpu["value"] = round(cpu["value"], 1)
     out["cpu_baseline"] = cpu
@@ -420,7 +458,7 @@ def main_decode_product(args):
     import torch
     import gated_delta_rule_79_amd as gdn
     from gated_delta_rule_79_amd import synth
-    if not torch.cuda.is_available():
+    if torch.cuda.device_count() < 1:   # counts devices without initialising HIP
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     N, H, dk, dv, nh = 256, 32, 128, 128, args.nh
@@ -462,11 +500,15 @@ def main_other(args):
     import torch
     import gated_delta_rule_79_amd as gdn
     from gated_delta_rule_79_amd import synth
-    if not torch.cuda.is_available():
+    if torch.cuda.device_count() < 1:   # counts devices without initialising HIP
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     wl = args.workload or ("decode_n256_h32" if args.mode == "decode" else "varlen_16k_dv256")
     inp = synth.workload(wl, with_do=args.mode != "decode")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = (cpu_baseline_decode(inp, args.cpu_budget) if args.mode == "decode"
+               else cpu_baseline_bwd(inp, args.cpu_budget))
     d = inp.to("cuda")
     B, T, H, dk = inp.q.shape
     dv = inp.v.shape[-1]
@@ -490,6 +532,7 @@ def main_other(args):
         kms = per.get("decode", ms)
         byts = decode_bytes(B, H, dk, dv, s_io)
         gbs = byts / (kms * 1e-3) / 1e9
+        copy_gbs = copy_bandwidth()
         out.update({"metric": "tokens/sec gdn_decode_step (N=%d,H=%d,d=%d); %% HBM" % (B, H, dk),
                     "value": round(B / (ms * 1e-3), 1), "unit": "tokens/s",
                     "ms_per_step": round(ms, 5),
@@ -500,8 +543,9 @@ def main_other(args):
                                      wl, "decode_kernel", source_hash(DECODE_SOURCES)),
                                  "kernel": "decode_kernel",
                                  "kernel_ms": {k2: round(v2, 5) for k2, v2 in per.items()},
-                                 "alg_bytes_per_launch": int(byts)}})
-        cpu = None if args.no_cpu_baseline else cpu_baseline_decode(inp, args.cpu_budget)
+                                 "alg_bytes_per_launch": int(byts),
+                                 "copy_GBps_measured": round(copy_gbs, 1),
+                                 "frac_of_copy": round(gbs / copy_gbs, 4)}})
     else:
         plan = gdn.FwdPlan(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, chunk=C,
                            cu_seqlens=d.cu_seqlens)
@@ -543,7 +587,6 @@ def main_other(args):
                         "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s",
                         "ms_per_step": round(ms, 5), "cold_ms_per_step": None,
                         "roofline": rf})
-        cpu = None if args.no_cpu_baseline else cpu_baseline_bwd(inp, args.cpu_budget)
     if args.copy_calibration:
         copy_calibration()
     if cpu is not None:
@@ -552,52 +595,77 @@ def main_other(args):
     print(json.dumps(out), flush=True)
 
 
-def copy_calibration():
-    """Three device copies of 256 MiB: a kernel of known traffic for scaling
-    memory counters."""
+def cache_evictor(nbytes=1 << 30):
+    """A function that reads a 1 GiB device buffer: it evicts the inputs and
+    the workspace of the previous call from L2 (4 MB per XCD) and the 256 MB
+    Infinity Cache, leaving clean lines (a write would leave 256 MB of dirty
+    lines whose write-back the next call would pay for)."""
     import torch
-    src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda").fill_(3)
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+
+    def evict():
+        buf.max()
+    return evict
+
+
+def copy_calibration():
+    """Device copies of known traffic for scaling memory counters: three of
+    256 MiB (inside the 256 MB Infinity Cache) and three of 1 GiB (beyond
+    it)."""
+    import torch
+    for n in (1 << 28, 1 << 30):
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=10):
+    """GB/s of the runtime's device-to-device copy of ``nbytes`` (read +
+    written bytes over the median duration): the practical streaming
+    ceiling of this GPU, measured in the same process."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
     dst = torch.empty_like(src)
-    for _ in range(3):
+    dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
         dst.copy_(src)
-    torch.cuda.synchronize()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    times.sort()
     del src, dst
+    return 2 * nbytes / (times[len(times) // 2] * 1e-3) / 1e9
 
 
 def cpu_baseline(inp, budget_s, qknorm=False):
-    """The fp64 oracle, as it stands, on whole (sequence, head) chains of the
-    same workload until about ``budget_s`` seconds of work; BLAS held to one
-    thread.  Rate is scaled to the whole workload's tokens.  qknorm: q and k
-    rows go through the oracle's L2 normalisation first (timed)."""
+    """The fp64 oracle, as it stands, on every (sequence, head) chain of the
+    workload, P workers; tokens/s of the whole workload.  qknorm: q and k rows
+    go through the oracle's L2 normalisation first (timed)."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
     import oracle
     f = inp.f64
-    B, T, H = f["q"].shape[:3]
-    done = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        for b in range(B):
-            for h in range(H):
-                la = None if f["log_alpha"] is None else f["log_alpha"][b, :, h]
-                m0 = np.zeros((f["q"].shape[3], f["v"].shape[3]))
-                qc, kc = f["q"][b, :, h], f["k"][b, :, h]
-                if qknorm:
-                    qc, kc = oracle.l2_normalize(qc), oracle.l2_normalize(kc)
-                oracle.gdn_fwd_chain(qc, kc, f["v"][b, :, h], f["beta"][b, :, h], la, m0,
-                                     inp.gate)
-                done += 1
-                if time.perf_counter() - t0 > budget_s:
-                    break
-            if time.perf_counter() - t0 > budget_s:
-                break
-    dt = time.perf_counter() - t0
-    frac = done / float(B * H)
-    return {"value": B * T * frac / dt, "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{done} of {B * H} (sequence, head) chains of T={T} "
-                      f"({dt:.1f} s, 1 thread); tokens/s scaled to the whole workload"}
+    H, dk, dv = f["q"].shape[2], f["q"].shape[3], f["v"].shape[3]
+    units = [(c, h) for c in _chains(inp) for h in range(H)]
 
+    def job(u):
+        (b, a, e, n), h = u
+        la = None if f["log_alpha"] is None else f["log_alpha"][b, a:e, h]
+        m0 = np.zeros((dk, dv)) if f["s0"] is None else f["s0"][n, h]
+        qc, kc = f["q"][b, a:e, h], f["k"][b, a:e, h]
+        if qknorm:
+            qc, kc = oracle.l2_normalize(qc), oracle.l2_normalize(kc)
+        oracle.gdn_fwd_chain(qc, kc, f["v"][b, a:e, h], f["beta"][b, a:e, h], la, m0,
+                             inp.gate)
+
+    return cpu_oracle_rate(job, units, lambda u: (u[0][2] - u[0][1]) / H, budget_s,
+                           "oracle token recurrence over every (sequence, head) chain")
 
 def main():
     ap = argparse.ArgumentParser()
@@ -613,12 +681,14 @@ def main():
                     help="delta steps per token for --mode product")
     ap.add_argument("--qk-l2norm", action="store_true",
                     help="forward with q and k L2-normalised inside the kernels")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="(forward) override the workload's batch size B")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra calls each preceded by a 1 GiB cache-flush write")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run 3 device copies of 256 MiB (a kernel of known "
+                    help="also run device copies of 256 MiB and 1 GiB (kernels of known "
                          "traffic for scaling memory counters)")
     args = ap.parse_args()
 
@@ -643,65 +713,83 @@ def main():
         return
     if args.workload is None:
         args.workload = "fwd_t4096_h16"
+    main_fwd(args)
 
+
+def main_fwd(args):
+    """The headline: gdn_chunk_fwd on B=1, T=4096, H=16, dk=dv=128, chunk 64,
+    bf16 inputs, fp32 state (``--batch`` overrides B for the batch sweep).
+
+    Timed region: K steps, each a 1 GiB read that evicts L2 and the 256 MB
+    Infinity Cache (outside the events) followed by one forward call
+    bracketed by HIP events on the call's stream; ``value`` is tokens over
+    the median call.  The same K steps then run again with the library's
+    per-kernel HIP events (kept out of the timed region: an event between
+    kernels costs a few microseconds).  Back-to-back (warm) calls are timed
+    last and reported as extra keys."""
     import torch
     import gated_delta_rule_79_amd as gdn
     from gated_delta_rule_79_amd import synth
 
-    if not torch.cuda.is_available():
+    if torch.cuda.device_count() < 1:   # counts devices without initialising HIP
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     qkn = args.qk_l2norm
-    inp = synth.workload(args.workload, **({"raw_qk": (0.05, 20.0, 0.0)} if qkn else {}))
-    d = inp.to("cuda")
+    over = {"raw_qk": (0.05, 20.0, 0.0)} if qkn else {}
+    if args.batch:
+        over["B"] = args.batch
+    inp = synth.workload(args.workload, **over)
     B, T, H, dk = inp.q.shape
     dv = inp.v.shape[-1]
     C = inp.chunk
     nseq = B if inp.cu_seqlens is None else inp.cu_seqlens.numel() - 1
+    wl = args.workload + (f"_b{B}" if args.batch else "") + ("_qknorm" if qkn else "")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_budget, qknorm=qkn)
+        cpu["value"] = round(cpu["value"], 1)
+        cpu["single_worker_value"] = round(cpu["single_worker_value"], 1)
+
+    d = inp.to("cuda")
     plan = gdn.FwdPlan(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, chunk=C,
                        cu_seqlens=d.cu_seqlens, qk_l2norm=qkn)
-
+    evict = cache_evictor()
     for _ in range(args.warmup):
+        evict()
         plan.run()
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back calls
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(args.steps):
-        plan.run()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-
-    # same calls again with the library's per-kernel HIP events
-    gdn.stage_times(True)
-    for _ in range(args.steps):
-        plan.run()
-    torch.cuda.synchronize()
-    st = gdn.stage_times()
-    gdn.stage_times(False)
-    per_kernel = {k: v[0] / v[1] for k, v in st.items()}
-
-    # cold: flush L2 and the 256 MB Infinity Cache before each call
-    cold_ms = None
-    if args.cold_steps > 0:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        times = []
-        for _ in range(args.cold_steps):
-            flush.fill_(1)
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
+    def cold_region(stages):
+        """K steps: evict the caches, then one call between two events."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        if stages:
+            gdn.stage_times(True)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for a, b in ev:
+            evict()
             a.record()
             plan.run()
             b.record()
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b))
-        times.sort()
-        cold_ms = times[len(times) // 2]
-        del flush
+        torch.cuda.synchronize()
+        t = time.perf_counter() - t
+        st = None
+        if stages:
+            st = gdn.stage_times()
+            gdn.stage_times(False)
+        return sorted(a.elapsed_time(b) for a, b in ev), t, st
+
+    # the timed region, then the same steps again with the library's HIP
+    # events around every kernel (the per-kernel durations)
+    times, t_host, _ = cold_region(False)
+    cold_ms = times[len(times) // 2]
+    _, _, st = cold_region(True)
+    per_kernel = {k: v[0] / v[1] for k, v in st.items()}
+
+    # warm: back-to-back calls, inputs and workspace resident in the caches
+    warm_ms, _ = time_calls(plan.run, args.steps, 0)
+    del evict
 
     if args.copy_calibration:
         copy_calibration()
@@ -711,55 +799,59 @@ def main():
     flops, byts = algorithmic(B, T, H, dk, dv, C, s_io, s_gate, inp.gate, nseq,
                               inp.s0 is not None, True)
     tokens = B * T
-    value = tokens / (ms_per_step * 1e-3)
-
-    dom = max(per_kernel, key=per_kernel.get)
-    dom_ms = per_kernel[dom]
-    prep_kernel = "fwd_prep_kernel" if inp.gate == "channel" else "fwd_prep_sg_kernel"
-    kname = {"fwd_prep": prep_kernel, "fwd_scan": "fwd_scan_kernel",
-             "fwd_trans": "fwd_trans_kernel", "fwd_combine": "fwd_combine_kernel",
-             "chunk_map": "chunk_map_kernel"}[dom]
-    achieved = byts / (dom_ms * 1e-3) / 1e9
-    src_hash = source_hash(FWD_SOURCES)
-    traffic = None if qkn else measured_traffic(args.workload, kname, src_hash)
     path_ms = sum(per_kernel.values())
+    prep_kernel = "fwd_prep_kernel" if inp.gate == "channel" else "fwd_prep_sg_kernel"
+    names = {"fwd_prep": prep_kernel, "fwd_scan": "fwd_scan_kernel",
+             "fwd_trans": "fwd_trans_kernel", "fwd_combine": "fwd_combine_kernel",
+             "chunk_map": "chunk_map_kernel"}
+    dom = max(per_kernel, key=per_kernel.get)
+    src_hash = source_hash(FWD_SOURCES)
+    traffic = None if qkn else measured_traffic(wl, "fwd_call", src_hash)
+    achieved = byts / (cold_ms * 1e-3) / 1e9
     roofline = {
+        # the forward call as one unit: its algorithmic bytes over the median
+        # call duration of the timed region (the per-kernel durations below
+        # come from the second pass, where the events between kernels add a
+        # few microseconds each)
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
-        "kernel": kname,
-        "kernel_ms": {k: round(v, 5) for k, v in per_kernel.items()},
+        "kernel": "gdn_chunk_fwd (" + " + ".join(names.get(k, k) for k in per_kernel) + ")",
+        "kernel_ms": {names.get(k, k): round(v, 5) for k, v in per_kernel.items()},
+        "call_kernel_ms": round(path_ms, 5),
         "alg_bytes_per_launch": int(byts),
         "alg_flops_per_launch": int(flops),
-        "path_frac_hbm": round(byts / (path_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "path_frac_mfma_bf16": round(flops / (path_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "frac_mfma_bf16": round(flops / (cold_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "dominant_kernel": names.get(dom, dom),
+        "dominant_kernel_frac_if_alone": round(byts / (per_kernel[dom] * 1e-3) / 1e9 /
+                                               HBM_PEAK_GBS, 4),
         "source_hash": src_hash,
     }
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_budget, qknorm=qkn)
-        cpu["value"] = round(cpu["value"], 1)
-
     out = {
         "metric": ("tokens/sec gdn_chunk_fwd_qknorm (T=4096,H=16,d=128 bf16); % HBM roofline"
                    if qkn else
                    "tokens/sec gdn_chunk_fwd (T=4096,H=16,d=128 bf16); % MFMA/HBM roofline"),
-        "value": round(value, 1),
+        "value": round(tokens / (cold_ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(cold_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if s_io == 2 else "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload + ("_qknorm" if qkn else ""), "B": B, "T": T,
-                   "H": H, "dk": dk,
-                   "dv": dv, "chunk": C, "gate": inp.gate, "seed": inp.seed,
-                   "state": "fp32", "parallelism": "single GPU"},
-        "cold_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
+        "config": {"workload": wl, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": C,
+                   "gate": inp.gate, "seed": inp.seed, "state": "fp32",
+                   "timing": "median of K calls, each after a 1 GiB read that evicts L2 "
+                             "and the Infinity Cache",
+                   "parallelism": "single GPU"},
+        "p10_ms": round(times[len(times) // 10], 5),
+        "p90_ms": round(times[(len(times) * 9) // 10], 5),
+        "warm_ms_per_step": round(warm_ms, 5),
+        "warm_value": round(tokens / (warm_ms * 1e-3), 1),
+        "timed_region_host_s": round(t_host, 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

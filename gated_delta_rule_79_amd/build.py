@@ -1,6 +1,6 @@
 """Build libgdn.so in-tree with hipcc for gfx950.
 
-    python -m gated_delta_rule_79_amd.build [-v] [-j N]
+    python -m gated_delta_rule_79_amd.build [-v] [-j N] [-i]
 
 Every HIP source under csrc/ is compiled to an object under _build/ and the
 objects are linked into gated_delta_rule_79_amd/libgdn.so (written to a
@@ -45,8 +45,22 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _stale(src: str, obj: str) -> bool:
+    """An object is stale when it is missing or older than its source or any
+    header under csrc/ or include/."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [os.path.join(CSRC, src)]
+    for d in (CSRC, INCLUDE):
+        deps += [os.path.join(d, f) for f in os.listdir(d) if f.endswith((".h", ".hpp"))]
+    return any(os.path.getmtime(x) > t for x in deps)
+
+
+def _compile(src: str, verbose: bool, incremental: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if incremental and not _stale(src, obj):
+        return obj
     cmd = [_hipcc(), *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -60,11 +74,14 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None,
+          incremental: bool = False) -> str:
+    """Compile every source (incremental: only those whose object is stale)
+    and link the library."""
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 8)
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, verbose, incremental), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs,
            "-o", tmp]
@@ -81,8 +98,10 @@ def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("-v", "--verbose", action="store_true")
     ap.add_argument("-j", "--jobs", type=int, default=None)
+    ap.add_argument("-i", "--incremental", action="store_true",
+                    help="recompile only sources whose object is stale")
     a = ap.parse_args()
-    print(build(a.verbose, a.jobs))
+    print(build(a.verbose, a.jobs, a.incremental))
 
 
 if __name__ == "__main__":
