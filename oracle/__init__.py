@@ -46,4 +46,8 @@ from .gdn_oracle import (  # noqa: F401
     gdn2_fwd_chain,
     gdn2_decode,
     gdn2_chunked_bruteforce,
+    short_conv,
+    silu,
+    conv_prologue,
+    gdn_fwd_conv,
 )

@@ -34,6 +34,13 @@ Readings where the pages are silent (each is listed in the design notes):
     deltaproduct_fwd).  Parity with an external definition is UNPINNED; the
     pins fix its reductions and reflection properties.
 
+  * short convolution + SiLU in front of q, k, v (the block design of
+    "Method"; the pages give neither the width nor the tap layout): a
+    causal depthwise convolution of caller-given width and taps, no bias,
+    zero history at every sequence start (short_conv, conv_prologue,
+    gdn_fwd_conv).  Pinned by numpy's own convolution, causality, sequence
+    isolation and SiLU identities.
+
   * draft trees (TreeWY, only summarised by the pages): a node continues
     its parent's state with one step on its own token; the verification
     returns every node's output, the commit rebuilds the accepted node's
@@ -184,6 +191,57 @@ def gdn_fwd_qknorm(q, k, v, beta, log_alpha, s0=None, gate: str = "scalar",
     v does not).  Same shapes and returns as :func:`gdn_fwd`."""
     return gdn_fwd(l2_normalize(q), l2_normalize(k), v, beta, log_alpha, s0,
                    gate, cu_seqlens=cu_seqlens)
+
+
+# --------------------------------------------------------------------------
+# short causal convolution and SiLU in front of the recurrence ("Method":
+# in the block design q and k pass through a projection, a short convolution
+# and SiLU before the L2 normalisation; v takes the same path without it)
+# --------------------------------------------------------------------------
+
+def short_conv(x, taps, cu_seqlens=None):
+    """Causal depthwise convolution over time, channel by channel:
+
+        y[b, t, h, c] = sum_{j=0}^{W-1} taps[h, c, j] * x[b, t - j, h, c]
+
+    tap j weighs the input j tokens back; inputs before the start of the
+    sequence (dense row or packed varlen sequence) read as zero, so packed
+    sequences never see each other.  x [B,T,H,D], taps [H,D,W]."""
+    x = np.asarray(x, dtype=np.float64)
+    taps = np.asarray(taps, dtype=np.float64)
+    B, T, H, D = x.shape
+    W = taps.shape[-1]
+    y = np.zeros_like(x)
+    for b, t0, t1, _ in _segments(B, T, cu_seqlens):
+        for t in range(t0, t1):
+            for j in range(W):
+                if t - j >= t0:
+                    y[b, t] += taps[:, :, j] * x[b, t - j]
+    return y
+
+
+def silu(x):
+    """x * sigmoid(x)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def conv_prologue(x, taps, normalize, cu_seqlens=None):
+    """The path of one projection: short convolution, SiLU, and for q and k
+    the L2 normalisation per (token, head)."""
+    y = silu(short_conv(x, taps, cu_seqlens))
+    return l2_normalize(y) if normalize else y
+
+
+def gdn_fwd_conv(xq, xk, xv, wq, wk, wv, beta, log_alpha, s0=None,
+                 gate: str = "scalar", cu_seqlens=None):
+    """The forward on the block's q, k, v paths: q = l2(silu(conv(xq))),
+    k = l2(silu(conv(xk))), v = silu(conv(xv)), then :func:`gdn_fwd`.
+    xq, xk [B,T,H,dk], xv [B,T,H,dv]; wq, wk [H,dk,W], wv [H,dv,W]."""
+    return gdn_fwd(conv_prologue(xq, wq, True, cu_seqlens),
+                   conv_prologue(xk, wk, True, cu_seqlens),
+                   conv_prologue(xv, wv, False, cu_seqlens),
+                   beta, log_alpha, s0, gate, cu_seqlens=cu_seqlens)
 
 
 # --------------------------------------------------------------------------

@@ -453,3 +453,66 @@ def g2_chunked_equals_recurrence(g2, g2_chunked, gate, C, T=37, dk=8, dv=5, seed
     o1, m1 = g2(q, k, v, er, wr, la, m0, gate)
     o2, m2 = g2_chunked(q, k, v, er, wr, la, m0, gate, C)
     return max(np.max(np.abs(o1 - o2)), np.max(np.abs(m1 - m2)))
+
+
+# ------------------------------------ short convolution + SiLU prologue ---
+# Checks written against callables with the signatures of
+# oracle.short_conv(x, taps, cu_seqlens) and oracle.silu(x); references are
+# numpy's own convolution and closed forms.
+
+def conv_equals_numpy_convolve(conv, seed=41, B=2, T=19, H=2, D=3, W=4):
+    """Each channel of each row is numpy's full convolution of the inputs
+    with the taps, cut to the first T outputs (y[t] = sum_j w[j] x[t-j])."""
+    r = rng(seed)
+    x = r.standard_normal((B, T, H, D))
+    w = r.standard_normal((H, D, W))
+    y = conv(x, w, None)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            for c in range(D):
+                ref = np.convolve(x[b, :, h, c], w[h, c])[:T]
+                worst = max(worst, np.max(np.abs(y[b, :, h, c] - ref)))
+    return worst
+
+
+def conv_impulse_response(conv, T=12, W=4, t0=5, seed=42):
+    """A unit impulse at token t0 returns the taps at t0 .. t0 + W - 1 and
+    zero elsewhere (nothing before t0: causal)."""
+    r = rng(seed)
+    w = r.standard_normal((1, 2, W))
+    x = np.zeros((1, T, 1, 2))
+    x[0, t0, 0, 1] = 1.0
+    y = conv(x, w, None)
+    want = np.zeros((T,))
+    want[t0:t0 + W] = w[0, 1, :min(W, T - t0)]
+    return max(np.max(np.abs(y[0, :, 0, 1] - want)), np.max(np.abs(y[0, :, 0, 0])))
+
+
+def conv_isolates_sequences(conv, seed=43, W=4):
+    """Packed sequences never see each other: the packed result equals the
+    sequences run alone (each with zero history)."""
+    r = rng(seed)
+    lens = [5, 0, 1, 9, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = r.standard_normal((1, int(cu[-1]), 2, 3))
+    w = r.standard_normal((2, 3, W))
+    y = conv(x, w, cu)
+    worst = 0.0
+    for n in range(len(lens)):
+        a, e = int(cu[n]), int(cu[n + 1])
+        if e > a:
+            worst = max(worst, np.max(np.abs(y[:, a:e] - conv(x[:, a:e], w, None))))
+    return worst
+
+
+def silu_identities(silu):
+    """silu(0) = 0; silu(x) - silu(-x) = x; silu(1) = 1 / (1 + e^-1);
+    silu(40) = 40 and silu(-40) = 0 to within 1e-15 of 40."""
+    x = np.linspace(-6, 6, 25)
+    one = silu(np.array([0.0, 1.0, 40.0, -40.0]))
+    return max(abs(one[0]),
+               np.max(np.abs(silu(x) - silu(-x) - x)),
+               abs(one[1] - 1.0 / (1.0 + np.exp(-1.0))),
+               abs(one[2] - 40.0) / 40.0,
+               abs(one[3]))

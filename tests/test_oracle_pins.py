@@ -405,3 +405,62 @@ def test_g2_batch_and_decode_wrap_the_chain():
     o1, s1 = oracle.gdn2_fwd(q[:, :1], k[:, :1], v[:, :1], er[:, :1], wr[:, :1], la[:, :1],
                              s0, "channel")
     assert np.max(np.abs(od - o1[:, 0])) < 1e-14 and np.max(np.abs(st - s1)) < 1e-14
+
+
+# ------------------------------------ short convolution + SiLU prologue ---
+
+def test_conv_equals_numpy_convolve():
+    assert pins.conv_equals_numpy_convolve(oracle.short_conv) < 1e-13
+
+
+@pytest.mark.parametrize("W,t0", [(1, 0), (3, 4), (4, 10), (4, 0)])
+def test_conv_impulse_response(W, t0):
+    assert pins.conv_impulse_response(oracle.short_conv, W=W, t0=t0) < 1e-15
+
+
+def test_conv_isolates_sequences():
+    assert pins.conv_isolates_sequences(oracle.short_conv) < 1e-15
+
+
+def test_silu_identities():
+    assert pins.silu_identities(oracle.silu) < 1e-12
+
+
+def test_conv_prologue_paths():
+    # q and k rows come out unit (or zero), v rows are not normalised; with
+    # width-1 unit taps the convolution is the identity
+    r = pins.rng(44)
+    x = r.standard_normal((1, 7, 2, 5))
+    w1 = np.ones((2, 5, 1))
+    qk = oracle.conv_prologue(x, w1, True)
+    n = np.linalg.norm(qk, axis=-1)
+    assert np.max(np.abs(n - 1.0)) < 1e-14
+    vv = oracle.conv_prologue(x, w1, False)
+    assert np.max(np.abs(vv - x / (1 + np.exp(-x)))) < 1e-15
+    z = oracle.conv_prologue(x, np.zeros((2, 5, 3)), True)
+    assert np.all(z == 0.0)
+
+
+def test_conv_forward_composes_the_paths():
+    # the block forward is the pinned forward on the three prologue outputs,
+    # each built here from numpy's convolution
+    r = pins.rng(45)
+    B, T, H, dk, dv, W = 1, 20, 2, 6, 4, 4
+    xq, xk = r.standard_normal((B, T, H, dk)), r.standard_normal((B, T, H, dk))
+    xv = r.standard_normal((B, T, H, dv))
+    wq, wk = r.standard_normal((H, dk, W)), r.standard_normal((H, dk, W))
+    wv = r.standard_normal((H, dv, W))
+    beta, la = r.random((B, T, H)), -r.random((B, T, H))
+
+    def path(x, w, norm):
+        y = np.zeros_like(x)
+        for h in range(x.shape[2]):
+            for c in range(x.shape[3]):
+                y[0, :, h, c] = np.convolve(x[0, :, h, c], w[h, c])[:T]
+        y = y / (1.0 + np.exp(-y))
+        return pins.unit(y) if norm else y
+
+    o, s = oracle.gdn_fwd_conv(xq, xk, xv, wq, wk, wv, beta, la, None, "scalar")
+    o2, s2 = oracle.gdn_fwd(path(xq, wq, True), path(xk, wk, True), path(xv, wv, False),
+                            beta, la, None, "scalar")
+    assert np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(s - s2)) < 1e-12

@@ -261,3 +261,39 @@ def test_reference_oracle_passes_g2_pins():
 @pytest.mark.parametrize("name", sorted(G2_MUTANTS))
 def test_g2_mutant_is_caught(name):
     assert not _g2_pins_pass(_mutant(*G2_MUTANTS[name]))
+
+
+# ------------------------------------ short convolution + SiLU prologue ---
+
+def _conv_pins_pass(mod):
+    ok = pins.conv_equals_numpy_convolve(mod.short_conv) < 1e-13
+    for W, t0 in ((1, 0), (3, 4), (4, 10)):
+        ok &= pins.conv_impulse_response(mod.short_conv, W=W, t0=t0) < 1e-15
+    ok &= pins.conv_isolates_sequences(mod.short_conv) < 1e-15
+    ok &= pins.silu_identities(mod.silu) < 1e-12
+    return bool(ok)
+
+
+CONV_MUTANTS = {
+    "taps applied forward in time": (
+        "                    y[b, t] += taps[:, :, j] * x[b, t - j]\n",
+        "                    y[b, t] += taps[:, :, W - 1 - j] * x[b, t - j]\n"),
+    "history leaks across sequences": (
+        "                if t - j >= t0:\n",
+        "                if t - j >= 0:\n"),
+    "current token skipped": (
+        "                    y[b, t] += taps[:, :, j] * x[b, t - j]\n",
+        "                    y[b, t] += taps[:, :, j] * x[b, t - j - 1] if t - j - 1 >= t0 else 0.0\n"),
+    "sigmoid instead of SiLU": (
+        "    return x / (1.0 + np.exp(-x))\n",
+        "    return 1.0 / (1.0 + np.exp(-x))\n"),
+}
+
+
+def test_reference_oracle_passes_conv_pins():
+    assert _conv_pins_pass(ref_mod)
+
+
+@pytest.mark.parametrize("name", sorted(CONV_MUTANTS))
+def test_conv_mutant_is_caught(name):
+    assert not _conv_pins_pass(_mutant(*CONV_MUTANTS[name]))
