@@ -24,7 +24,9 @@ import torch
 from . import _lib
 from ._lib import GdnError  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "decode_step", "decode_step_product",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_conv", "gdn2_chunk_fwd",
+           "gdn2_decode_step",
+           "chunk_bwd", "decode_step", "decode_step_product",
            "chunk_fwd_product", "tree_verify",
            "tree_commit", "FwdPlan", "GdnError",
            "abi_version", "stage_times"]
@@ -99,8 +101,8 @@ def chunk_fwd(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
     sf = (torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
           if output_final_state else None)
     need = ctypes.c_size_t(0)
-    _lib.check(lib.gdn_chunk_fwd_workspace(ctypes.byref(p), ctypes.byref(need)),
-               "gdn_chunk_fwd_workspace")
+    wsq = lib.gdn_chunk_fwd_qknorm_workspace if qk_l2norm else lib.gdn_chunk_fwd_workspace
+    _lib.check(wsq(ctypes.byref(p), ctypes.byref(need)), "workspace query")
     ws = workspace
     if ws is None or ws.numel() < need.value:
         ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
@@ -133,6 +135,88 @@ def chunk_fwd_noalloc(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
                                    _stream(q.device))
     _lib.check(st, "gdn_chunk_fwd_noalloc")
     return o, s_final
+
+
+def chunk_fwd_conv(xq, xk, xv, wq, wk, wv, beta, log_alpha=None, s0=None, chunk: int = 64,
+                   cu_seqlens=None, output_final_state: bool = True, seg_chunks: int = 0):
+    """The forward behind the block's q, k, v paths (gdn_chunk_fwd_conv):
+    xq, xk [B,T,H,dk], xv [B,T,H,dv] projections; wq, wk [H,dk,W], wv
+    [H,dv,W] fp32 convolution taps (W in 1..8).  q = l2(silu(conv(xq))),
+    k = l2(silu(conv(xk))), v = silu(conv(xv)), then the forward.
+    Returns (o, s_final or None)."""
+    lib = _lib.load()
+    _check_cu(cu_seqlens, xq)
+    width = wq.shape[-1]
+    for w in (wq, wk, wv):
+        if w.dtype != torch.float32 or w.shape[-1] != width:
+            raise ValueError("taps must be fp32 with one width")
+    p = _problem(xq, xv, beta, log_alpha, chunk, cu_seqlens, seg_chunks=seg_chunks)
+    nseq = xq.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+    H, dk, dv = xq.shape[2], xq.shape[3], xv.shape[3]
+    o = torch.empty(xv.shape, dtype=xq.dtype, device=xq.device)
+    sf = (torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=xq.device)
+          if output_final_state else None)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.gdn_chunk_fwd_conv_workspace(ctypes.byref(p), width, ctypes.byref(need)),
+               "gdn_chunk_fwd_conv_workspace")
+    ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=xq.device)
+    st = lib.gdn_chunk_fwd_conv(ctypes.byref(p), width, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq),
+                                _ptr(wk), _ptr(wv), _ptr(beta), _ptr(log_alpha), _ptr(s0),
+                                _ptr(o), _ptr(sf), _ptr(ws), ws.numel(), _stream(xq.device))
+    _lib.check(st, "gdn_chunk_fwd_conv")
+    return o, sf
+
+
+def gdn2_chunk_fwd(q, k, v, erase, write, log_alpha=None, s0=None, chunk: int = 64,
+                   cu_seqlens=None, output_final_state: bool = True,
+                   workspace: Optional[torch.Tensor] = None, seg_chunks: int = 0):
+    """Gated DeltaNet-2 forward (gdn2_chunk_fwd): separate erase and write
+    strengths [B,T,H] in place of beta.  Returns (o, s_final or None)."""
+    lib = _lib.load()
+    _check_cu(cu_seqlens, q)
+    if write.shape != erase.shape or write.dtype != erase.dtype:
+        raise ValueError("erase and write must have the same shape and dtype")
+    p = _problem(q, v, erase, log_alpha, chunk, cu_seqlens, seg_chunks=seg_chunks)
+    nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+    H, dk, dv = q.shape[2], q.shape[3], v.shape[3]
+    o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    sf = (torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+          if output_final_state else None)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.gdn_chunk_fwd_workspace(ctypes.byref(p), ctypes.byref(need)),
+               "gdn_chunk_fwd_workspace")
+    ws = workspace
+    if ws is None or ws.numel() < need.value:
+        ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    st = lib.gdn2_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(erase),
+                            _ptr(write), _ptr(log_alpha), _ptr(s0), _ptr(o), _ptr(sf),
+                            _ptr(ws), ws.numel(), _stream(q.device))
+    _lib.check(st, "gdn2_chunk_fwd")
+    return o, sf
+
+
+def gdn2_decode_step(q, k, v, erase, write, log_alpha, state):
+    """Gated DeltaNet-2 decode step (gdn2_decode_step); ``state`` is updated
+    in place.  erase, write [N, H].  Returns o [N, H, dv]."""
+    lib = _lib.load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if write.shape != erase.shape or write.dtype != erase.dtype:
+        raise ValueError("erase and write must have the same shape and dtype")
+    p = _lib.GdnProblem()
+    p.B, p.T, p.H, p.dk, p.dv, p.chunk, p.nseq = N, 1, H, dk, dv, 0, 0
+    p.cu_seqlens = None
+    p.io_dtype = _dtype_code(q)
+    p.gate_dtype = _dtype_code(erase)
+    p.gate = _gate_of(log_alpha, 2)
+    if state.dtype != torch.float32:
+        raise TypeError("state must be fp32")
+    o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    st = lib.gdn2_decode_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(erase),
+                              _ptr(write), _ptr(log_alpha), _ptr(state), _ptr(o),
+                              _stream(q.device))
+    _lib.check(st, "gdn2_decode_step")
+    return o
 
 
 def chunk_fwd_product(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
@@ -265,9 +349,8 @@ class FwdPlan:
         self.s_final = (torch.empty((nseq, H, dk, dv), dtype=torch.float32,
                                     device=q.device) if output_final_state else None)
         need = ctypes.c_size_t(0)
-        _lib.check(lib.gdn_chunk_fwd_workspace(ctypes.byref(self.problem),
-                                               ctypes.byref(need)),
-                   "gdn_chunk_fwd_workspace")
+        wsq = lib.gdn_chunk_fwd_qknorm_workspace if qk_l2norm else lib.gdn_chunk_fwd_workspace
+        _lib.check(wsq(ctypes.byref(self.problem), ctypes.byref(need)), "workspace query")
         self.workspace = torch.empty(max(need.value, 1), dtype=torch.uint8,
                                      device=q.device)
         self._name = "gdn_chunk_fwd_qknorm" if qk_l2norm else "gdn_chunk_fwd"

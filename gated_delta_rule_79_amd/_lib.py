@@ -27,10 +27,13 @@ EXPORTED = (
     "gdn_chunk_fwd_product_workspace", "gdn_chunk_fwd_product",
     "gdn_chunk_fwd_qknorm", "gdn_tree_verify_workspace", "gdn_tree_verify",
     "gdn_tree_commit", "gdn_decode_step_product", "gdn_chunk_fwd_noalloc",
+    "gdn2_chunk_fwd", "gdn2_decode_step", "gdn_chunk_fwd_qknorm_workspace",
+    "gdn_chunk_fwd_conv_workspace", "gdn_chunk_fwd_conv",
 )
-STAGE_COUNT = 11
+STAGE_COUNT = 12
 STAGES = ("chunk_map", "fwd_prep", "fwd_scan", "decode", "bwd_states",
-          "bwd_scan", "bwd_grad", "other", "fwd_trans", "fwd_combine", "tree_commit")
+          "bwd_scan", "bwd_grad", "other", "fwd_trans", "fwd_combine", "tree_commit",
+          "prologue")
 
 
 class GdnProblem(ctypes.Structure):
@@ -101,6 +104,16 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_decode_step_product.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_chunk_fwd_noalloc.restype = i32
     lib.gdn_chunk_fwd_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn2_chunk_fwd.restype = i32
+    lib.gdn2_chunk_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn2_decode_step.restype = i32
+    lib.gdn2_decode_step.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_chunk_fwd_qknorm_workspace.restype = i32
+    lib.gdn_chunk_fwd_qknorm_workspace.argtypes = [pp, ctypes.POINTER(sz)]
+    lib.gdn_chunk_fwd_conv_workspace.restype = i32
+    lib.gdn_chunk_fwd_conv_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
+    lib.gdn_chunk_fwd_conv.restype = i32
+    lib.gdn_chunk_fwd_conv.argtypes = [pp, i32] + [vp] * 12 + [sz, vp]
     lib.gdn_tree_commit.restype = i32
     lib.gdn_tree_commit.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
     if path is None:

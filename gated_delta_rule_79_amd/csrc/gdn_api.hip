@@ -75,6 +75,7 @@ gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out, int lnh 
   out->lnh = lnh;
   out->qknorm = false;
   out->parent = nullptr;
+  out->beta_w = nullptr;
   out->H = p->H;
   out->dk = p->dk;
   out->dv = p->dv;
@@ -376,27 +377,119 @@ gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* p, const void* q, const void
   }
 }
 
-// q and k rows L2-normalised inside the forward; per-token gates only.
+}  // extern "C"
+
+namespace {
+
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Bytes of one [B * T, H, D] tensor in the problem's io dtype, 256-aligned.
+size_t rows_bytes(const gdn::Problem& p, int D) {
+  return al256(static_cast<size_t>(p.B) * p.T * p.H * D * (p.io == GDN_BF16 ? 2 : 4));
+}
+
+// The normalising forward: per-token gates normalise inside the forward's
+// kernels; the per-channel gate takes normalised q, k rows from a prologue.
+size_t qknorm_workspace_bytes(const gdn::Problem& p) {
+  const size_t pro = p.gate == GDN_GATE_CHANNEL ? 2 * rows_bytes(p, p.dk) : 0;
+  return pro + gdn::fwd_workspace_bytes(p);
+}
+
+size_t conv_workspace_bytes(const gdn::Problem& p) {
+  return 2 * rows_bytes(p, p.dk) + rows_bytes(p, p.dv) + gdn::fwd_workspace_bytes(p);
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd_qknorm_workspace(const gdn_problem* p, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return GDN_ERR_NULL;
+    gdn::Problem pp;
+    GDN_TRY(check_chunk_problem(p, &pp));
+    *bytes = qknorm_workspace_bytes(pp);
+    return GDN_OK;
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+// q and k rows L2-normalised inside the forward.
 gdn_status gdn_chunk_fwd_qknorm(const gdn_problem* p, const void* q, const void* k,
                                 const void* v, const void* beta,
                                 const void* log_alpha, const float* s0, void* o,
                                 float* s_final, void* ws, size_t ws_bytes,
                                 void* stream) {
   try {
-    if (p == nullptr) return GDN_ERR_NULL;
-    if (p->gate == GDN_GATE_CHANNEL) return GDN_ERR_UNSUPPORTED;
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
     GDN_TRY(check_fwd_pointers(pp, q, k, v, beta, log_alpha, s0, o, s_final));
-    const size_t need_ws = gdn::fwd_workspace_bytes(pp);
+    const size_t need_ws = qknorm_workspace_bytes(pp);
     if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
       return GDN_ERR_WORKSPACE;
     GDN_TRY(opt(ws));
     if (g_fail_launch.load()) return GDN_ERR_HIP;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (pp.gate == GDN_GATE_CHANNEL) {
+      char* w = static_cast<char*>(ws);
+      char* qn = w;
+      char* kn = w + rows_bytes(pp, pp.dk);
+      char* fw = kn + rows_bytes(pp, pp.dk);
+      hipError_t e = gdn::launch_prologue(pp, pp.dk, 0, q, nullptr, true, qn, st);
+      if (e == hipSuccess) e = gdn::launch_prologue(pp, pp.dk, 0, k, nullptr, true, kn, st);
+      if (e != hipSuccess) return GDN_ERR_HIP;
+      return launched(gdn::launch_fwd(pp, qn, kn, v, beta, log_alpha, s0, o, s_final, fw, st));
+    }
     pp.qknorm = true;
-    return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o,
-                                    s_final, ws,
-                                    static_cast<hipStream_t>(stream)));
+    return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o, s_final, ws, st));
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+gdn_status gdn_chunk_fwd_conv_workspace(const gdn_problem* p, int32_t width, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return GDN_ERR_NULL;
+    if (width < 1 || width > 8) return GDN_ERR_UNSUPPORTED;
+    gdn::Problem pp;
+    GDN_TRY(check_chunk_problem(p, &pp));
+    *bytes = conv_workspace_bytes(pp);
+    return GDN_OK;
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+// Short convolution + SiLU on q, k, v (q and k then L2-normalised), then the
+// forward.
+gdn_status gdn_chunk_fwd_conv(const gdn_problem* p, int32_t width, const void* xq,
+                              const void* xk, const void* xv, const float* wq,
+                              const float* wk, const float* wv, const void* beta,
+                              const void* log_alpha, const float* s0, void* o,
+                              float* s_final, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (width < 1 || width > 8) return GDN_ERR_UNSUPPORTED;
+    gdn::Problem pp;
+    GDN_TRY(check_chunk_problem(p, &pp));
+    GDN_TRY(check_fwd_pointers(pp, xq, xk, xv, beta, log_alpha, s0, o, s_final));
+    GDN_TRY(need(wq, static_cast<int64_t>(pp.H) * pp.dk * width));
+    GDN_TRY(need(wk, static_cast<int64_t>(pp.H) * pp.dk * width));
+    GDN_TRY(need(wv, static_cast<int64_t>(pp.H) * pp.dv * width));
+    const size_t need_ws = conv_workspace_bytes(pp);
+    if (ws == nullptr || ws_bytes < need_ws) return GDN_ERR_WORKSPACE;
+    GDN_TRY(opt(ws));
+    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* qn = static_cast<char*>(ws);
+    char* kn = qn + rows_bytes(pp, pp.dk);
+    char* vn = kn + rows_bytes(pp, pp.dk);
+    char* fw = vn + rows_bytes(pp, pp.dv);
+    hipError_t e = gdn::launch_prologue(pp, pp.dk, width, xq, wq, true, qn, st);
+    if (e == hipSuccess) e = gdn::launch_prologue(pp, pp.dk, width, xk, wk, true, kn, st);
+    if (e == hipSuccess) e = gdn::launch_prologue(pp, pp.dv, width, xv, wv, false, vn, st);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+    return launched(gdn::launch_fwd(pp, qn, kn, vn, beta, log_alpha, s0, o, s_final, fw, st));
   } catch (...) {
     return GDN_ERR_HIP;
   }
@@ -575,40 +668,97 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k,
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared validation of the decode entry points; fills *pp.
+gdn_status check_decode(const gdn_problem* p, const void* q, const void* k, const void* v,
+                        const void* beta, const void* log_alpha, const float* state,
+                        const void* o, gdn::Problem* pp) {
+  if (p == nullptr) return GDN_ERR_NULL;
+  if (!dtype_ok(p->io_dtype) || !dtype_ok(p->gate_dtype)) return GDN_ERR_DTYPE;
+  if (p->gate < GDN_GATE_NONE || p->gate > GDN_GATE_CHANNEL)
+    return GDN_ERR_UNSUPPORTED;
+  if (p->B < 1 || p->H < 1) return GDN_ERR_SHAPE;
+  if (!dk_ok(p->dk) || !dv_ok(p->dv)) return GDN_ERR_UNSUPPORTED;
+  // one workgroup per (sequence, head, 64-column slab): within the grid limit
+  if (static_cast<int64_t>(p->B) * p->H * ((p->dv + 63) / 64) > (int64_t(1) << 31) - 1)
+    return GDN_ERR_SHAPE;
+  *pp = gdn::Problem{};
+  pp->B = p->B;
+  pp->T = 1;
+  pp->H = p->H;
+  pp->dk = p->dk;
+  pp->dv = p->dv;
+  pp->nseq = p->B;
+  pp->io = p->io_dtype;
+  pp->gdt = p->gate_dtype;
+  pp->gate = p->gate;
+  const int64_t nh = static_cast<int64_t>(p->B) * p->H;
+  GDN_TRY(need(q, nh * p->dk));
+  GDN_TRY(need(k, nh * p->dk));
+  GDN_TRY(need(v, nh * p->dv));
+  GDN_TRY(need(beta, nh));
+  if (pp->gate != GDN_GATE_NONE) GDN_TRY(need(log_alpha, nh));
+  else GDN_TRY(opt(log_alpha));
+  GDN_TRY(need(state, nh * p->dk * p->dv));
+  GDN_TRY(need(o, nh * p->dv));
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k,
                            const void* v, const void* beta,
                            const void* log_alpha, float* state, void* o,
                            void* stream) {
   try {
-    if (p == nullptr) return GDN_ERR_NULL;
-    if (!dtype_ok(p->io_dtype) || !dtype_ok(p->gate_dtype)) return GDN_ERR_DTYPE;
-    if (p->gate < GDN_GATE_NONE || p->gate > GDN_GATE_CHANNEL)
-      return GDN_ERR_UNSUPPORTED;
-    if (p->B < 1 || p->H < 1) return GDN_ERR_SHAPE;
-    if (!dk_ok(p->dk) || !dv_ok(p->dv)) return GDN_ERR_UNSUPPORTED;
-    if (static_cast<int64_t>(p->B) * p->H > (int64_t(1) << 31) - 1)
-      return GDN_ERR_SHAPE;
-    gdn::Problem pp{};
-    pp.B = p->B;
-    pp.T = 1;
-    pp.H = p->H;
-    pp.dk = p->dk;
-    pp.dv = p->dv;
-    pp.nseq = p->B;
-    pp.io = p->io_dtype;
-    pp.gdt = p->gate_dtype;
-    pp.gate = p->gate;
-    const int64_t nh = static_cast<int64_t>(p->B) * p->H;
-    GDN_TRY(need(q, nh * p->dk));
-    GDN_TRY(need(k, nh * p->dk));
-    GDN_TRY(need(v, nh * p->dv));
-    GDN_TRY(need(beta, nh));
-    if (pp.gate != GDN_GATE_NONE) GDN_TRY(need(log_alpha, nh));
-    else GDN_TRY(opt(log_alpha));
-    GDN_TRY(need(state, nh * p->dk * p->dv));
-    GDN_TRY(need(o, nh * p->dv));
+    gdn::Problem pp;
+    GDN_TRY(check_decode(p, q, k, v, beta, log_alpha, state, o, &pp));
     if (g_fail_launch.load()) return GDN_ERR_HIP;
     return launched(gdn::launch_decode(pp, q, k, v, beta, log_alpha, state, o,
+                                       static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+// Gated DeltaNet-2: separate erase and write strengths.
+gdn_status gdn2_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
+                          const void* v, const void* erase, const void* write,
+                          const void* log_alpha, const float* s0, void* o,
+                          float* s_final, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    gdn::Problem pp;
+    GDN_TRY(check_chunk_problem(p, &pp));
+    GDN_TRY(check_fwd_pointers(pp, q, k, v, erase, log_alpha, s0, o, s_final));
+    GDN_TRY(need(write, static_cast<int64_t>(pp.B) * pp.T * pp.H));
+    const size_t need_ws = gdn::fwd_workspace_bytes(pp);
+    if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
+      return GDN_ERR_WORKSPACE;
+    GDN_TRY(opt(ws));
+    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    pp.beta_w = write;
+    return launched(gdn::launch_fwd(pp, q, k, v, erase, log_alpha, s0, o, s_final, ws,
+                                    static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_ERR_HIP;
+  }
+}
+
+gdn_status gdn2_decode_step(const gdn_problem* p, const void* q, const void* k,
+                            const void* v, const void* erase, const void* write,
+                            const void* log_alpha, float* state, void* o, void* stream) {
+  try {
+    gdn::Problem pp;
+    GDN_TRY(check_decode(p, q, k, v, erase, log_alpha, state, o, &pp));
+    GDN_TRY(need(write, static_cast<int64_t>(pp.B) * pp.H));
+    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    pp.beta_w = write;
+    return launched(gdn::launch_decode(pp, q, k, v, erase, log_alpha, state, o,
                                        static_cast<hipStream_t>(stream)));
   } catch (...) {
     return GDN_ERR_HIP;
@@ -626,7 +776,8 @@ gdn_status gdn_decode_step_product(const gdn_problem* p, int32_t nh, const void*
     if (nh != 1 && nh != 2 && nh != 4) return GDN_ERR_UNSUPPORTED;
     if (p->B < 1 || p->H < 1) return GDN_ERR_SHAPE;
     if (!dk_ok(p->dk) || !dv_ok(p->dv)) return GDN_ERR_UNSUPPORTED;
-    if (static_cast<int64_t>(p->B) * p->H > (int64_t(1) << 31) - 1) return GDN_ERR_SHAPE;
+    if (static_cast<int64_t>(p->B) * p->H * ((p->dv + 63) / 64) > (int64_t(1) << 31) - 1)
+      return GDN_ERR_SHAPE;
     gdn::Problem pp{};
     pp.B = p->B;
     pp.T = 1;

@@ -1327,7 +1327,7 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
       StageScope scope(GDN_STAGE_FWD_PREP, s);
       hipLaunchKernelGGL((fwd_prep_kernel<C, DK, IO, GATE, true>),
                          dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(256), 0, s,
-                         map, p.H, p.dv, p.nchunks, q, k, v, beta, la, gbf, buf);
+                         map, p.H, p.dv, p.nchunks, q, k, v, beta, la, gbf, buf, nullptr);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -25,18 +25,24 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSlab = 64;  // state columns per workgroup
 
+// beta_w: write strength of the decoupled erase / write rule (then beta is
+// the erase strength, e = beta_w v - beta Mt^T k); nullptr: beta does both.
 template <int DK, typename IO, typename GT, int GATE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     int H, int dv, const void* __restrict__ q, const void* __restrict__ k,
     const void* __restrict__ v, const void* __restrict__ beta,
     const void* __restrict__ la, float* __restrict__ state,
-    void* __restrict__ o) {
+    void* __restrict__ o, const void* __restrict__ beta_w) {
   constexpr int RPT = DK / 16;  // rows per thread
-  const int nh = blockIdx.x;    // n * H + h
+  // the slabs of one head are consecutive workgroups, so the two halves of
+  // every state row are streamed at about the same time
+  const int nslab = (dv + kSlab - 1) / kSlab;
+  const int nh = blockIdx.x / nslab;  // n * H + h
+  const int slab = blockIdx.x - nh * nslab;
   const int t = threadIdx.x;
   const int cg = t & 15;        // column group: 4 consecutive columns
   const int rg = t >> 4;        // row group 0..15: rows rg + 16 j
-  const int col = blockIdx.y * kSlab + cg * 4;
+  const int col = slab * kSlab + cg * 4;
   const bool active = col < dv;  // dv is a multiple of 16, so all-or-none
 
   const int64_t vec_off = static_cast<int64_t>(nh) * DK;
@@ -102,8 +108,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   const float b = io<GT>::load(beta, nh);
   const int64_t vo = static_cast<int64_t>(nh) * dv + col;
   floatx4 e;
+  if (beta_w == nullptr) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) e[c] = b * (io<IO>::load(v, vo + c) - u[c]);
+    for (int c = 0; c < 4; ++c) e[c] = b * (io<IO>::load(v, vo + c) - u[c]);
+  } else {
+    const float bw = io<GT>::load(beta_w, nh);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) e[c] = bw * io<IO>::load(v, vo + c) - b * u[c];
+  }
 
   if (rg == 0) {
 #pragma unroll
@@ -131,11 +143,13 @@ __global__ __launch_bounds__(64) void decode_product_kernel(
     const void* __restrict__ v, const void* __restrict__ beta,
     const void* __restrict__ la, float* __restrict__ state, void* __restrict__ o) {
   constexpr int RPT = DK / 4;
-  const int nhd = blockIdx.x;  // n * H + h
+  const int nslab = (dv + kSlab - 1) / kSlab;
+  const int nhd = blockIdx.x / nslab;  // n * H + h
+  const int slab = blockIdx.x - nhd * nslab;
   const int n = nhd / H, h = nhd - n * H;
   const int lane = threadIdx.x;
   const int cg = lane & 15, rg = lane >> 4;
-  const int col = blockIdx.y * kSlab + cg * 4;
+  const int col = slab * kSlab + cg * 4;
   const bool active = col < dv;  // dv is a multiple of 16: whole lane groups
   float* M = state + static_cast<int64_t>(nhd) * DK * dv;
   floatx4 mm[RPT];
@@ -198,7 +212,7 @@ hipError_t dispatch_product(const Problem& p, int nh, const void* q, const void*
                             const void* v, const void* beta, const void* la,
                             float* state, void* o, hipStream_t s) {
   StageScope scope(GDN_STAGE_DECODE, s);
-  const dim3 grid(static_cast<unsigned>(p.B * p.H), (p.dv + kSlab - 1) / kSlab);
+  const dim3 grid(static_cast<unsigned>(int64_t(p.B) * p.H * ((p.dv + kSlab - 1) / kSlab)));
   if (p.gate == GDN_GATE_SCALAR)
     hipLaunchKernelGGL((decode_product_kernel<DK, IO, GT, GDN_GATE_SCALAR>), grid, dim3(64),
                        0, s, p.H, p.dv, nh, q, k, v, beta, la, state, o);
@@ -235,17 +249,17 @@ hipError_t dispatch_gate(const Problem& p, dim3 grid, const void* q,
     case GDN_GATE_NONE:
       hipLaunchKernelGGL((decode_kernel<DK, IO, GT, GDN_GATE_NONE>), grid,
                          dim3(kThreads), 0, s, p.H, p.dv, q, k, v, beta, la,
-                         state, o);
+                         state, o, p.beta_w);
       break;
     case GDN_GATE_SCALAR:
       hipLaunchKernelGGL((decode_kernel<DK, IO, GT, GDN_GATE_SCALAR>), grid,
                          dim3(kThreads), 0, s, p.H, p.dv, q, k, v, beta, la,
-                         state, o);
+                         state, o, p.beta_w);
       break;
     default:
       hipLaunchKernelGGL((decode_kernel<DK, IO, GT, GDN_GATE_CHANNEL>), grid,
                          dim3(kThreads), 0, s, p.H, p.dv, q, k, v, beta, la,
-                         state, o);
+                         state, o, p.beta_w);
       break;
   }
   return hipGetLastError();
@@ -285,7 +299,7 @@ hipError_t launch_decode_product(const Problem& p, int nh, const void* q, const 
 hipError_t launch_decode(const Problem& p, const void* q, const void* k,
                          const void* v, const void* beta, const void* la,
                          float* state, void* o, hipStream_t s) {
-  const dim3 grid(p.B * p.H, (p.dv + kSlab - 1) / kSlab);
+  const dim3 grid(static_cast<unsigned>(int64_t(p.B) * p.H * ((p.dv + kSlab - 1) / kSlab)));
   switch (p.dk) {
     case 16: return dispatch_io<16>(p, grid, q, k, v, beta, la, state, o, s);
     case 32: return dispatch_io<32>(p, grid, q, k, v, beta, la, state, o, s);

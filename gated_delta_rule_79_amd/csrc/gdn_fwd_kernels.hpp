@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
-    FwdBuffers buf) {
+    FwdBuffers buf, const void* __restrict__ beta_w = nullptr) {
   using OP = IO;  // bf16 inputs multiply on bf16 MFMA, fp32 on fp32 MFMA
   using S = PrepSmem<C, DK, IO, GATE, BWD>;
   constexpr bool CH = GATE == GDN_GATE_CHANNEL;
@@ -287,6 +287,10 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   // ---- 1. beta, cumulative log-gate, K and K^T ----------------------------
   if (tid == 0) s_span_bits = 0;
   if (tid < C) sbeta[tid] = tid < len ? load_gate(beta, (tok0 + tid) * H + h, gbf) : 0.f;
+  // decoupled erase / write: beta (erase) scales A and W, the write strength
+  // U; it replaces beta in LDS once A and W's scales are formed (step 3)
+  float bw = 0.f;
+  if (beta_w != nullptr && tid < len) bw = load_gate(beta_w, (tok0 + tid) * H + h, gbf);
   if constexpr (!CH) {
     if (wave == 0) {
       float x = 0.f;
@@ -588,6 +592,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
     }
   }
   __syncthreads();
+  if (beta_w != nullptr && tid < C) sbeta[tid] = bw;  // last read of beta was A's
 
   // ---- 3. diagonal blocks of T (wave 0) beside the T-free outputs ---------
   if (wave == 0) {
@@ -980,7 +985,8 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
-    FwdBuffers buf, int lnh, bool qkn, const int32_t* __restrict__ parent) {
+    FwdBuffers buf, int lnh, bool qkn, const int32_t* __restrict__ parent,
+    const void* __restrict__ beta_w) {
   static_assert(GATE != GDN_GATE_CHANNEL, "per-token gates only");
   using OP = IO;
   using S = PrepSgSmem<C, DK, IO>;
@@ -1141,10 +1147,12 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
       if (lg == 0) sqn[16 * rt + l16] = ss > 0.f ? rsqrtf(ss) : 0.f;
     }
   }
+  float bw = 0.f;  // decoupled erase / write: the write strength (U only)
   if (wave == 0) {
     float x = 0.f, b = 0.f;
     if (lane < len) {
       b = load_gate(beta, (tok0 + lane) * H + h, gbf);
+      if (beta_w != nullptr) bw = load_gate(beta_w, (tok0 + lane) * H + h, gbf);
       if constexpr (GATE == GDN_GATE_SCALAR)
         if (((tok0 + lane) & nhm) == 0)  // the decay acts on a token's first step
           x = load_gate(la, ((tok0 + lane) >> lnh) * H + h, gbf) * kLog2e;
@@ -1285,6 +1293,8 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
   __syncthreads();
 
   // ---- 2. diagonal blocks of T: lane 16 b + j solves column j of block b
+  // (beta's last reader was A in step 1: U takes the write strength)
+  if (wave == 0 && beta_w != nullptr && lane < C) sbeta[lane] = bw;
   if (wave == 0) {
     const int b = lane >> 4, j = lane & 15;
     if (b < NB) {

@@ -26,6 +26,10 @@ struct Problem {
   bool qknorm;                // forward only: q and k rows L2-normalised
   const int32_t* parent;      // forward only: draft trees, one per chunk
                               // (device, node parents inside each tree)
+  const void* beta_w;         // forward and decode: write strength of the
+                              // decoupled erase/write rule (gate_dtype, like
+                              // beta, which is then the erase strength);
+                              // nullptr: beta does both
   // derived
   int64_t nchunks;            // chunk slots per head (upper bound in varlen)
   int seg;                    // chunks per segment of the forward state pass
@@ -66,6 +70,12 @@ hipError_t launch_tree_commit(const Problem& p, const int32_t* parent,
                               const int32_t* accepted, const void* k, const void* v,
                               const void* beta, const void* la, float* state,
                               hipStream_t s);
+
+// q, k, v prologue (gdn_prologue.hip): y = silu(conv(x)) with taps [H, D, W]
+// (taps == nullptr: y = x), rows L2-normalised when `normalize`; x, y
+// [B * T, H, D] in p.io.
+hipError_t launch_prologue(const Problem& p, int D, int W, const void* x, const float* taps,
+                           bool normalize, void* y, hipStream_t s);
 
 // Forward (gdn_fwd.hip).
 size_t fwd_workspace_bytes(const Problem& p);

@@ -35,7 +35,10 @@ __global__ __launch_bounds__(64) void tree_commit_kernel(
     const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
     float* __restrict__ state) {
   constexpr int RPT = DK / 4;  // rows per lane
-  const int mh = blockIdx.x;   // tree * H + head
+  // the column slabs of one (tree, head) are consecutive workgroups
+  const int nslab = (dv + kCommitCols - 1) / kCommitCols;
+  const int mh = blockIdx.x / nslab;  // tree * H + head
+  const int slab = blockIdx.x - mh * nslab;
   const int m = mh / H, h = mh - m * H;
   const int lane = threadIdx.x;
   const int64_t t0 = cu ? static_cast<int64_t>(cu[m]) : static_cast<int64_t>(m) * n;
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(64) void tree_commit_kernel(
       (uint64_t(1) << a);
 
   const int cg = lane & 15, rg = lane >> 4;
-  const int col = blockIdx.y * kCommitCols + cg * 4;
+  const int col = slab * kCommitCols + cg * 4;
   const bool active = col < dv;  // dv is a multiple of 16: whole lane groups
   float* M = state + static_cast<int64_t>(mh) * DK * dv;
   floatx4 mm[RPT];
@@ -146,7 +149,8 @@ hipError_t launch_tree_commit(const Problem& p, const int32_t* parent,
                               hipStream_t s) {
   if (p.nseq == 0) return hipSuccess;
   StageScope scope(GDN_STAGE_TREE_COMMIT, s);
-  const dim3 grid(static_cast<unsigned>(p.nseq * p.H), (p.dv + kCommitCols - 1) / kCommitCols);
+  const dim3 grid(static_cast<unsigned>(int64_t(p.nseq) * p.H *
+                                        ((p.dv + kCommitCols - 1) / kCommitCols)));
   switch (p.dk) {
     case 16: return commit_io<16>(p, grid, parent, accepted, k, v, beta, la, state, s);
     case 32: return commit_io<32>(p, grid, parent, accepted, k, v, beta, la, state, s);

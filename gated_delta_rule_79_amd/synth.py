@@ -31,7 +31,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Inputs", "make_inputs", "make_product_inputs", "make_tree_inputs",
+__all__ = ["Inputs", "make_inputs", "make_gdn2_inputs", "make_product_inputs",
+           "make_tree_inputs",
            "random_parents", "varlen_lengths",
            "WORKLOADS", "workload"]
 
@@ -51,6 +52,7 @@ class Inputs:
     chunk: int
     seed: int
     f64: dict = field(default_factory=dict)
+    write: Optional[torch.Tensor] = None   # decoupled rule: write strength
 
     def to(self, device):
         """Copy every tensor to ``device`` (fp64 views stay on the host)."""
@@ -157,6 +159,20 @@ def make_inputs(B: int, T: int, H: int, dk: int, dv: int, *,
         t = getattr(inp, name)
         f[name] = None if t is None else t.double().numpy()
     inp.f64 = f
+    return inp
+
+
+def make_gdn2_inputs(*args, seed: int = 0, **kw) -> Inputs:
+    """make_inputs' problem for the decoupled erase / write rule: ``beta``
+    serves as the erase strength and ``write`` (same shape and dtype) is drawn
+    from the same distribution, sigmoid(N(0, 1)), from a second PCG64 stream
+    seeded seed + 4099.  The pages give no distribution for either strength;
+    beta's is reused for both."""
+    inp = make_inputs(*args, seed=seed, **kw)
+    rng = np.random.Generator(np.random.PCG64(seed + 4099))
+    w = _sigmoid(rng.standard_normal(tuple(inp.beta.shape)))
+    inp.write = _round(w, inp.beta.dtype)
+    inp.f64["write"] = inp.write.double().numpy()
     return inp
 
 

@@ -185,16 +185,43 @@ gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* p, const void* q, const void
  * Improving Mamba2 with Delta Rule", "Method": the block design passes q and
  * k through an L2 normalisation per token and head; v is left as it is).
  * Computes gdn_chunk_fwd on q_t / |q_t| and k_t / |k_t| (norms over dk, in
- * fp32, per token and head; an all-zero row stays zero) without writing the
- * normalised tensors: k rows are normalised as the chunk is staged, the q
- * factor is applied to the fp32 products.  Arguments, layouts, workspace
- * (gdn_chunk_fwd_workspace) and errors as gdn_chunk_fwd; the per-channel
- * gate is GDN_ERR_UNSUPPORTED. */
+ * fp32, per token and head; an all-zero row stays zero).  With the scalar
+ * gate or no gate nothing normalised is written: k rows are normalised as
+ * the chunk is staged, the q factor is applied to the fp32 products.  With
+ * the per-channel gate a prologue pass first writes the normalised q and k
+ * rows (input dtype) into the workspace.  Workspace:
+ * gdn_chunk_fwd_qknorm_workspace (equal to gdn_chunk_fwd_workspace for the
+ * scalar gate and no gate).  Arguments, layouts and errors as
+ * gdn_chunk_fwd. */
+gdn_status gdn_chunk_fwd_qknorm_workspace(const gdn_problem* p, size_t* bytes);
 gdn_status gdn_chunk_fwd_qknorm(const gdn_problem* p, const void* q, const void* k,
                                 const void* v, const void* beta,
                                 const void* log_alpha, const float* s0, void* o,
                                 float* s_final, void* ws, size_t ws_bytes,
                                 void* stream);
+
+/* The forward behind the block's q, k, v paths ("Gated Delta Networks:
+ * Improving Mamba2 with Delta Rule", "Method": q and k pass through a short
+ * convolution, SiLU and an L2 normalisation, v through the same without the
+ * normalisation).  The caller's projections xq, xk, xv go through
+ *   y[t, h, c] = silu(sum_{j < width} taps[h, c, j] x[t - j, h, c])
+ * (causal and depthwise; tap j weighs the input j tokens back; no history
+ * before a sequence's first token, so packed sequences never see each
+ * other; no bias), q and k rows are then L2-normalised, and gdn_chunk_fwd
+ * runs on the results, which a prologue pass writes into the workspace in
+ * the input dtype.
+ *   width       : taps per channel, 1 .. 8 (else GDN_ERR_UNSUPPORTED).
+ *   xq, xk      : [B, T, H, dk] io_dtype;  xv : [B, T, H, dv] io_dtype.
+ *   wq, wk      : [H, dk, width] fp32;     wv : [H, dv, width] fp32.
+ *   beta, log_alpha, s0, o, s_final : as in gdn_chunk_fwd (every gate).
+ *   ws          : at least gdn_chunk_fwd_conv_workspace bytes.
+ * Errors as gdn_chunk_fwd. */
+gdn_status gdn_chunk_fwd_conv_workspace(const gdn_problem* p, int32_t width, size_t* bytes);
+gdn_status gdn_chunk_fwd_conv(const gdn_problem* p, int32_t width, const void* xq,
+                              const void* xk, const void* xv, const float* wq,
+                              const float* wk, const float* wv, const void* beta,
+                              const void* log_alpha, const float* s0, void* o,
+                              float* s_final, void* ws, size_t ws_bytes, void* stream);
 
 /* Householder-product transitions (the GDN review's "Future work" and its
  * closing section name products of Householder matrices as a way to graft
@@ -220,6 +247,32 @@ gdn_status gdn_chunk_fwd_product(const gdn_problem* p, int32_t nh, const void* q
                                  const void* log_alpha, const float* s0, void* o,
                                  float* s_final, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/* Gated DeltaNet-2 with decoupled erase and write strengths.  "Linear
+ * Attention Architectures: Mechanisms, Trade-offs, and Cross-Layer
+ * Routing" (abstract, and its related-paper entry "Gated DeltaNet-2:
+ * Decoupling Erase and Write in Linear Attention") names the method and its
+ * separate erase and write control but prints no formula.  Reading taken:
+ * the single strength beta_t of the gated delta rule splits into an erase
+ * strength e_t and a write strength w_t,
+ *     S_t = S_{t-1} D_t (I - e_t k_t k_t^T) + w_t v_t k_t^T,
+ * with D_t the scalar or per-channel gate as in gdn_chunk_fwd; e = w gives
+ * gdn_chunk_fwd, e = 0 gated linear attention.  (In the chunk form e scales
+ * the rows of A and W, w those of U.)
+ *   erase, write : [B, T, H] in gate_dtype, used as given (never clamped).
+ * Everything else (problem, layouts, workspace = gdn_chunk_fwd_workspace,
+ * errors) as gdn_chunk_fwd. */
+gdn_status gdn2_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
+                          const void* v, const void* erase, const void* write,
+                          const void* log_alpha, const float* s0, void* o,
+                          float* s_final, void* ws, size_t ws_bytes, void* stream);
+
+/* One decode step of the same rule, state in place: Mt = a (.) M,
+ * e = w v - e_t Mt^T k, M <- Mt + k e^T, o = M^T q.  erase, write [N, H];
+ * the rest as gdn_decode_step. */
+gdn_status gdn2_decode_step(const gdn_problem* p, const void* q, const void* k,
+                            const void* v, const void* erase, const void* write,
+                            const void* log_alpha, float* state, void* o, void* stream);
 
 /* Draft-tree verification for speculative decoding ("TreeWY: Speculative
  * Verification for Gated DeltaNet Hybrids": the gated delta rule as a
@@ -317,7 +370,7 @@ gdn_status gdn_decode_step_product(const gdn_problem* p, int32_t nh, const void*
  * into total_ms[GDN_STAGE_COUNT] and count[GDN_STAGE_COUNT], and clears the
  * record.  Not for use while a stream is being captured into a graph.
  * Calls that overlap on several host threads are recorded together. */
-#define GDN_STAGE_COUNT 11
+#define GDN_STAGE_COUNT 12
 typedef enum {
   GDN_STAGE_CHUNK_MAP = 0,  /* varlen chunk table                         */
   GDN_STAGE_FWD_PREP = 1,   /* per-chunk gate, UT transform, W/U/P        */
@@ -329,7 +382,8 @@ typedef enum {
   GDN_STAGE_OTHER = 7,
   GDN_STAGE_FWD_TRANS = 8,  /* forward: per-segment state maps [M0 | Phi] */
   GDN_STAGE_FWD_COMBINE = 9, /* forward: states entering each segment     */
-  GDN_STAGE_TREE_COMMIT = 10 /* draft trees: accepted state rebuilt       */
+  GDN_STAGE_TREE_COMMIT = 10, /* draft trees: accepted state rebuilt      */
+  GDN_STAGE_PROLOGUE = 11   /* q, k, v paths: convolution, SiLU, L2 norm  */
 } gdn_stage;
 void gdn_profile_enable(int enable);
 gdn_status gdn_profile_read(double* total_ms, int32_t* count);

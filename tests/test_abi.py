@@ -31,7 +31,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gdn2?_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -285,12 +285,25 @@ def test_product_workspace_and_rejections(lib):
 
 
 def test_qknorm_rejections(lib):
-    """The forward that normalises q and k itself: the per-channel gate is
-    rejected, null pointers and a short workspace are caught before any
-    launch."""
-    st = lib.gdn_chunk_fwd_qknorm(ctypes.byref(prob(T=100, gate=_lib.GDN_GATE_CHANNEL)),
-                                  A, A, A, A, A, None, A, None, A, 1 << 30, None)
-    assert st == _lib.GDN_ERR_UNSUPPORTED
+    """The forward that normalises q and k itself: null pointers and a short
+    workspace are caught before any launch; the per-channel gate needs room
+    for the normalised rows on top of the forward's workspace."""
+    pc = prob(T=100, gate=_lib.GDN_GATE_CHANNEL)
+    n_fwd, n_qkn = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_workspace(ctypes.byref(pc), ctypes.byref(n_fwd)) == 0
+    assert lib.gdn_chunk_fwd_qknorm_workspace(ctypes.byref(pc), ctypes.byref(n_qkn)) == 0
+    rows = (100 * 2 * 128 * 2 + 255) // 256 * 256
+    assert n_qkn.value == n_fwd.value + 2 * rows
+    st = lib.gdn_chunk_fwd_qknorm(ctypes.byref(pc), A, A, A, A, A, None, A, None, A,
+                                  n_qkn.value - 1, None)
+    assert st == _lib.GDN_ERR_WORKSPACE
+    st = lib.gdn_chunk_fwd_qknorm(ctypes.byref(pc), A, A, A, A, A, None, A, None, A,
+                                  n_qkn.value, None)
+    assert st == _lib.GDN_ERR_HIP          # valid: reaches the launch hook
+    ps = prob(T=100)
+    assert lib.gdn_chunk_fwd_qknorm_workspace(ctypes.byref(ps), ctypes.byref(n_qkn)) == 0
+    assert lib.gdn_chunk_fwd_workspace(ctypes.byref(ps), ctypes.byref(n_fwd)) == 0
+    assert n_qkn.value == n_fwd.value
     assert lib.gdn_chunk_fwd_qknorm(None, A, A, A, A, A, None, A, None, A, 1 << 30,
                                     None) == _lib.GDN_ERR_NULL
     st = lib.gdn_chunk_fwd_qknorm(ctypes.byref(prob(T=100)), None, A, A, A, A,
@@ -366,3 +379,53 @@ def test_noalloc_validation_before_launch(lib):
     assert call(fits) == 7
     assert call(big) == 8                                # GDN_ERR_SCRATCH
     assert "scratch" in lib.gdn_status_str(8).decode()
+
+
+def test_gdn2_validation_before_launch(lib):
+    # gdn2_chunk_fwd / gdn2_decode_step: the forward's and decode's checks
+    # plus the write strength (required whenever the problem has tokens)
+    p = prob(T=200)
+    _, need = ws_bytes(lib, p)
+
+    def fwd2(p, write=A, erase=A, ws=A, n=None):
+        return lib.gdn2_chunk_fwd(ctypes.byref(p), A, A, A, erase, write, A, None, A, None,
+                                  ws, need if n is None else n, None)
+    assert fwd2(p) == 7                       # valid: reaches the launch hook
+    assert fwd2(p, write=None) == 1
+    assert fwd2(p, write=A + 4) == 5
+    assert fwd2(p, erase=None) == 1
+    assert fwd2(p, n=need - 256) == 6
+    assert fwd2(prob(T=0), write=None, erase=None) == 7   # nothing to read
+    d = prob(B=4, H=2, dk=64, dv=32)
+
+    def dec2(write=A, state=A):
+        return lib.gdn2_decode_step(ctypes.byref(d), A, A, A, A, write, A, state, A, None)
+    assert dec2() == 7
+    assert dec2(write=None) == 1
+    assert dec2(state=None) == 1
+    assert lib.gdn2_decode_step(None, A, A, A, A, A, A, A, A, None) == 1
+
+
+def test_conv_forward_validation(lib):
+    """gdn_chunk_fwd_conv: width 1..8, taps required, workspace = three
+    prologue tensors on top of the forward's."""
+    p = prob(T=100, dv=64)
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_conv_workspace(ctypes.byref(p), 0, ctypes.byref(n)) == 4
+    assert lib.gdn_chunk_fwd_conv_workspace(ctypes.byref(p), 9, ctypes.byref(n)) == 4
+    assert lib.gdn_chunk_fwd_conv_workspace(ctypes.byref(p), 4, ctypes.byref(n)) == 0
+    f = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_workspace(ctypes.byref(p), ctypes.byref(f)) == 0
+    al = lambda x: (x + 255) // 256 * 256
+    assert n.value == f.value + 2 * al(100 * 2 * 128 * 2) + al(100 * 2 * 64 * 2)
+
+    def call(width=4, wq=A, wk=A, wv=A, xq=A, nbytes=None):
+        return lib.gdn_chunk_fwd_conv(ctypes.byref(p), width, xq, A, A, wq, wk, wv, A, A,
+                                      None, A, None, A, n.value if nbytes is None else nbytes,
+                                      None)
+    assert call() == 7
+    assert call(width=9) == 4
+    assert call(wv=None) == 1
+    assert call(wq=A + 4) == 5
+    assert call(xq=None) == 1
+    assert call(nbytes=n.value - 1) == 6

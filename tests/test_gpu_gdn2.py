@@ -1,0 +1,164 @@
+"""GPU parity of the decoupled erase / write rule (Gated DeltaNet-2 as read
+from "Linear Attention Architectures: Mechanisms, Trade-offs, and
+Cross-Layer Routing"): gdn2_chunk_fwd and gdn2_decode_step against the fp64
+oracle's gdn2_fwd / gdn2_decode, whose reductions are pinned on the CPU.
+
+Sizes span several chunks with ragged tails for every chunk size, every
+gate and both dtypes; varlen batches with empty sequences; the split state
+pass; the headline shape at full size with every head compared."""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_79_amd as gdn
+import oracle
+from gated_delta_rule_79_amd import synth
+from gpu_util import TOL, log, np64, par_map, slice_err, state_err
+
+pytestmark = pytest.mark.gpu
+
+
+def run(inp, **kw):
+    d = inp.to("cuda")
+    o, sf = gdn.gdn2_chunk_fwd(d.q, d.k, d.v, d.beta, d.write, d.log_alpha, d.s0,
+                               chunk=inp.chunk, cu_seqlens=d.cu_seqlens, **kw)
+    torch.cuda.synchronize()
+    return o, sf
+
+
+def ref(inp):
+    f = inp.f64
+    cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
+    return oracle.gdn2_fwd(f["q"], f["k"], f["v"], f["beta"], f["write"], f["log_alpha"],
+                           f["s0"], inp.gate, cu_seqlens=cu)
+
+
+def check(inp, name, **kw):
+    log(f"[gdn2] {name} q={tuple(inp.q.shape)} {inp.q.dtype} gate={inp.gate} "
+        f"C={inp.chunk} seed={inp.seed} {kw}")
+    o, sf = run(inp, **kw)
+    o_ref, s_ref = ref(inp)
+    cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
+    eo, es = slice_err(np64(o), o_ref, cu), state_err(np64(sf), s_ref)
+    tol = TOL[inp.q.dtype]
+    log(f"    err o={eo:.3e} s_final={es:.3e} tol={tol}")
+    assert eo < tol and es < tol, (eo, es)
+    return o, sf
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("gate", ["scalar", "none", "channel"])
+def test_fp32_ragged(gpu_lib, C, gate):
+    inp = synth.make_gdn2_inputs(2, 100, 3, 32, 48, dtype=torch.float32, gate=gate,
+                                 chunk=C, seed=91, s0_std=0.3)
+    check(inp, "fp32_ragged")
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 32), (128, 128), (128, 256)])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_bf16_shapes(gpu_lib, dk, dv, gate):
+    inp = synth.make_gdn2_inputs(2, 200, 2, dk, dv, dtype=torch.bfloat16, gate=gate,
+                                 chunk=64, seed=92, s0_std=0.05)
+    check(inp, "bf16_shapes")
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel", "none"])
+def test_varlen_and_segments(gpu_lib, gate):
+    inp = synth.make_gdn2_inputs(1, 0, 2, 128, 64, dtype=torch.bfloat16, gate=gate,
+                                 seed=93, lengths=[5, 0, 300, 64, 1, 177], s0_std=0.1)
+    check(inp, "varlen")
+    check(inp, "varlen, 2-chunk segments", seg_chunks=2)
+
+
+def test_strengths_beyond_one(gpu_lib):
+    # erase up to 2 (negative-eigenvalue factor) and write up to 3
+    inp = synth.make_gdn2_inputs(1, 150, 2, 64, 64, dtype=torch.float32, gate="scalar",
+                                 seed=94, s0_std=0.2)
+    inp.beta.mul_(2.0)
+    inp.write.mul_(3.0)
+    inp.f64["beta"], inp.f64["write"] = inp.beta.double().numpy(), inp.write.double().numpy()
+    check(inp, "erase<=2 write<=3")
+
+
+def test_no_erase_is_gated_linear_attention(gpu_lib):
+    inp = synth.make_gdn2_inputs(1, 130, 2, 64, 32, dtype=torch.float32, gate="channel",
+                                 seed=95, s0_std=0.2)
+    inp.beta.zero_()
+    inp.f64["beta"][:] = 0.0
+    check(inp, "erase=0")
+
+
+def test_equal_strengths_is_the_gated_delta_rule(gpu_lib):
+    # erase = write: the same kernels and values as gdn_chunk_fwd, bit for bit
+    for gate in ("scalar", "channel", "none"):
+        inp = synth.make_inputs(1, 200, 2, 128, 128, dtype=torch.bfloat16, gate=gate,
+                                seed=96, s0_std=0.05)
+        d = inp.to("cuda")
+        o1, s1 = gdn.chunk_fwd(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0)
+        o2, s2 = gdn.gdn2_chunk_fwd(d.q, d.k, d.v, d.beta, d.beta.clone(), d.log_alpha, d.s0)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(s1, s2), gate
+
+
+def test_headline_shape_all_heads(gpu_lib):
+    # T=4096, H=16, d=128, bf16, B=1 (split state pass): every head
+    inp = synth.make_gdn2_inputs(1, 4096, 16, 128, 128, dtype=torch.bfloat16, chunk=64,
+                                 seed=97)
+    log("[gdn2] t4096_h16")
+    o, sf = run(inp)
+    f = inp.f64
+    xo, xs = np64(o), np64(sf)
+
+    def job(h):
+        hs = slice(h, h + 1)
+        o_ref, s_ref = oracle.gdn2_fwd(f["q"][:, :, hs], f["k"][:, :, hs], f["v"][:, :, hs],
+                                       f["beta"][:, :, hs], f["write"][:, :, hs],
+                                       f["log_alpha"][:, :, hs], None, "scalar")
+        return h, slice_err(xo[:, :, hs], o_ref), state_err(xs[:, hs], s_ref)
+
+    for h, eo, es in par_map(job, range(16)):
+        log(f"    head {h}: err o={eo:.3e} s={es:.3e}")
+        assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16], (h, eo, es)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("gate", ["scalar", "none", "channel"])
+def test_decode(gpu_lib, dtype, gate):
+    inp = synth.make_gdn2_inputs(5, 1, 3, 64, 48, dtype=dtype, gate=gate, seed=98,
+                                 s0_std=0.5)
+    d = inp.to("cuda")
+    la = None if d.log_alpha is None else d.log_alpha[:, 0].contiguous()
+    state = d.s0.clone()
+    o = gdn.gdn2_decode_step(d.q[:, 0].contiguous(), d.k[:, 0].contiguous(),
+                             d.v[:, 0].contiguous(), d.beta[:, 0].contiguous(),
+                             d.write[:, 0].contiguous(), la, state)
+    torch.cuda.synchronize()
+    f = inp.f64
+    o_ref, s_ref = oracle.gdn2_decode(f["q"][:, 0], f["k"][:, 0], f["v"][:, 0], f["beta"][:, 0],
+                                      f["write"][:, 0],
+                                      None if f["log_alpha"] is None else f["log_alpha"][:, 0],
+                                      f["s0"], gate)
+    eo = np.max(np.abs(np64(o) - o_ref)) / np.max(np.abs(o_ref))
+    es = state_err(np64(state), s_ref)
+    log(f"[gdn2] decode {dtype} {gate}: err o={eo:.3e} state={es:.3e}")
+    tol = TOL[dtype]
+    assert eo < tol and es < 1e-4
+
+
+def test_decode_after_forward(gpu_lib):
+    # a prefill of T tokens, then one decode step = the forward over T + 1
+    inp = synth.make_gdn2_inputs(2, 97, 2, 128, 64, dtype=torch.float32, gate="scalar",
+                                 seed=99, s0_std=0.1)
+    d = inp.to("cuda")
+    T = 96
+    sl = lambda x: x[:, :T].contiguous()
+    _, st = gdn.gdn2_chunk_fwd(sl(d.q), sl(d.k), sl(d.v), sl(d.beta), sl(d.write),
+                               sl(d.log_alpha), d.s0)
+    o_dec = gdn.gdn2_decode_step(d.q[:, T].contiguous(), d.k[:, T].contiguous(),
+                                 d.v[:, T].contiguous(), d.beta[:, T].contiguous(),
+                                 d.write[:, T].contiguous(), d.log_alpha[:, T].contiguous(), st)
+    o_all, s_all = gdn.gdn2_chunk_fwd(d.q, d.k, d.v, d.beta, d.write, d.log_alpha, d.s0)
+    torch.cuda.synchronize()
+    assert slice_err(np64(o_dec)[:, None], np64(o_all[:, T:T + 1])) < 1e-5
+    assert state_err(np64(st), np64(s_all)) < 1e-5

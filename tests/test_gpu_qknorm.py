@@ -15,7 +15,7 @@ import torch
 import gated_delta_rule_79_amd as gdn
 import oracle
 from gated_delta_rule_79_amd import _lib, synth
-from gpu_util import TOL, dev, log, np64, slice_err, state_err
+from gpu_util import TOL, dev, log, np64, par_map, slice_err, state_err
 
 pytestmark = pytest.mark.gpu
 
@@ -120,7 +120,7 @@ def test_qknorm_scale_invariance(gpu_lib):
     assert e < 2e-3
 
 
-def test_qknorm_plan_and_channel_gate_rejected(gpu_lib):
+def test_qknorm_plan_matches_call(gpu_lib):
     inp = synth.make_inputs(1, 100, 2, 64, 64, dtype=torch.bfloat16, gate="scalar",
                             chunk=64, seed=79, raw_qk=RAW)
     d = dev(inp)
@@ -129,12 +129,50 @@ def test_qknorm_plan_and_channel_gate_rejected(gpu_lib):
     o2, _ = gdn.chunk_fwd(d.q, d.k, d.v, d.beta, d.log_alpha, qk_l2norm=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+    # the per-channel gate: normalised rows from the prologue pass
     ch = synth.make_inputs(1, 40, 2, 64, 64, dtype=torch.float32, gate="channel",
-                           chunk=64, seed=80)
+                           chunk=64, seed=80, raw_qk=RAW)
     dc = dev(ch)
-    with pytest.raises(_lib.GdnError) as ei:
-        gdn.chunk_fwd(dc.q, dc.k, dc.v, dc.beta, dc.log_alpha, qk_l2norm=True)
-    assert ei.value.status == _lib.GDN_ERR_UNSUPPORTED
+    plan = gdn.FwdPlan(dc.q, dc.k, dc.v, dc.beta, dc.log_alpha, qk_l2norm=True)
+    o1, _ = plan.run()
+    o2, _ = gdn.chunk_fwd(dc.q, dc.k, dc.v, dc.beta, dc.log_alpha, qk_l2norm=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_qknorm_channel_gate(gpu_lib, C, dtype):
+    inp = synth.make_inputs(2, 150, 2, 128, 64, dtype=dtype, gate="channel", chunk=C,
+                            seed=81, s0_std=0.1, raw_qk=RAW)
+    check(inp, name="channel")
+
+
+def test_qknorm_channel_gate_varlen_full_size(gpu_lib):
+    # the per-channel training batch's shapes (16384 packed tokens, H16,
+    # dk128, dv256) with rows that are not unit vectors
+    inp = synth.make_inputs(1, 16384, 16, 128, 256, dtype=torch.bfloat16, gate="channel",
+                            chunk=64, seed=82, varlen=(16384, 512, 8192), raw_qk=RAW)
+    log(f"[qknorm] channel varlen lengths={np.diff(inp.cu_seqlens.numpy()).tolist()}")
+    d = dev(inp)
+    o, sf = gdn.chunk_fwd(d.q, d.k, d.v, d.beta, d.log_alpha, None, chunk=64,
+                          cu_seqlens=d.cu_seqlens, qk_l2norm=True)
+    torch.cuda.synchronize()
+    f = inp.f64
+    cu = inp.cu_seqlens.numpy()
+    xo, xs = np64(o), np64(sf)
+
+    def job(h):
+        hs = slice(h, h + 1)
+        o_ref, s_ref = oracle.gdn_fwd_qknorm(f["q"][:, :, hs], f["k"][:, :, hs],
+                                             f["v"][:, :, hs], f["beta"][:, :, hs],
+                                             f["log_alpha"][:, :, hs], None, "channel",
+                                             cu_seqlens=cu)
+        return h, slice_err(xo[:, :, hs], o_ref, cu), state_err(xs[:, hs], s_ref)
+
+    for h, eo, es in par_map(job, range(16)):
+        log(f"    head {h}: err o={eo:.3e} s={es:.3e}")
+        assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16], (h, eo, es)
 
 
 def test_qknorm_empty_sequences_copy_state(gpu_lib):
