@@ -84,21 +84,30 @@ def _check_cu(cu_seqlens, q):
         raise ValueError("cu_seqlens must be an int32 tensor on the inputs' device")
 
 
+def _out(t, shape, dtype, device):
+    """A caller's preallocated output, checked, or a new tensor."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"output must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    return t
+
+
 def chunk_fwd(q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
               cu_seqlens=None, output_final_state: bool = True,
               workspace: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
-              seg_chunks: int = 0):
+              seg_chunks: int = 0, o=None, s_final=None):
     """Chunkwise forward.  Returns (o, s_final or None).  qk_l2norm: q and k
     rows are L2-normalised inside the kernels (gdn_chunk_fwd_qknorm).
     seg_chunks: state-pass segment length (0 automatic, > 0 chunks per
-    segment, < 0 never split)."""
+    segment, < 0 never split).  o / s_final: optional preallocated outputs."""
     lib = _lib.load()
     _check_cu(cu_seqlens, q)
     p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens, seg_chunks=seg_chunks)
     nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
     H, dk, dv = q.shape[2], q.shape[3], v.shape[3]
-    o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
-    sf = (torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+    o = _out(o, v.shape, q.dtype, q.device)
+    sf = (_out(s_final, (nseq, H, dk, dv), torch.float32, q.device)
           if output_final_state else None)
     need = ctypes.c_size_t(0)
     wsq = lib.gdn_chunk_fwd_qknorm_workspace if qk_l2norm else lib.gdn_chunk_fwd_workspace
@@ -395,21 +404,25 @@ def fwd_workspace_bytes(q, v, beta, log_alpha=None, chunk=64, cu_seqlens=None,
 
 def chunk_bwd(q, k, v, beta, log_alpha, s0, d_o, ds_final=None,
               chunk: int = 64, cu_seqlens=None, need_ds0: bool = True,
-              workspace: Optional[torch.Tensor] = None, seg_chunks: int = 0):
+              workspace: Optional[torch.Tensor] = None, seg_chunks: int = 0,
+              out=None):
     """Chunkwise backward.  Returns (dq, dk, dv, dbeta, dlog_alpha, ds0).
-    seg_chunks as in chunk_fwd (the state recompute's segments)."""
+    seg_chunks as in chunk_fwd (the state recompute's segments).  out:
+    optional preallocated (dq, dk, dv, dbeta, dlog_alpha, ds0), entries may
+    be None."""
     lib = _lib.load()
     _check_cu(cu_seqlens, q)
     p = _problem(q, v, beta, log_alpha, chunk, cu_seqlens, seg_chunks=seg_chunks)
     nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
     H, dk, dv = q.shape[2], q.shape[3], v.shape[3]
-    dq = torch.empty_like(q)
-    dk_ = torch.empty_like(k)
-    dv_ = torch.empty_like(v)
-    dbeta = torch.empty(beta.shape, dtype=torch.float32, device=q.device)
+    out = (None,) * 6 if out is None else tuple(out)
+    dq = _out(out[0], q.shape, q.dtype, q.device)
+    dk_ = _out(out[1], k.shape, k.dtype, k.device)
+    dv_ = _out(out[2], v.shape, v.dtype, v.device)
+    dbeta = _out(out[3], beta.shape, torch.float32, q.device)
     dla = (None if log_alpha is None else
-           torch.empty(log_alpha.shape, dtype=torch.float32, device=q.device))
-    ds0 = (torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+           _out(out[4], log_alpha.shape, torch.float32, q.device))
+    ds0 = (_out(out[5], (nseq, H, dk, dv), torch.float32, q.device)
            if need_ds0 else None)
     need = ctypes.c_size_t(0)
     _lib.check(lib.gdn_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(need)),

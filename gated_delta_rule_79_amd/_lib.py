@@ -9,7 +9,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+# the in-tree library; GDN_LIBRARY names another build of it (for example
+# the host-sanitized one the C-ABI tests also run against)
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 
 # status codes (include/gdn.h)
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE = 0, 1, 2, 3

@@ -1,10 +1,16 @@
 """Build libgdn.so in-tree with hipcc for gfx950.
 
-    python -m gated_delta_rule_79_amd.build [-v] [-j N] [-i]
+    python -m gated_delta_rule_79_amd.build [-v] [-j N] [-i] [--sanitize]
 
 Every HIP source under csrc/ is compiled to an object under _build/ and the
 objects are linked into gated_delta_rule_79_amd/libgdn.so (written to a
 temporary name first, then renamed, so a half-built library is never seen).
+
+--sanitize builds a second library, _build/asan/libgdn_asan.so, whose host
+code (argument validation, workspace sizing, dispatch) carries
+AddressSanitizer and UndefinedBehaviorSanitizer; the device code is the
+same.  tests/test_abi_sanitized.py runs the C-ABI tests against it on the
+CPU.
 """
 
 from __future__ import annotations
@@ -22,6 +28,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libgdn_asan.so")
+# sanitizers on the host side only (each flag behind -Xarch_host)
+SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+       "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
 
 SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_fwd.hip", "gdn_bwd.hip", "gdn_tree.hip",
            "gdn_prologue.hip"]
@@ -58,11 +69,12 @@ def _stale(src: str, obj: str) -> bool:
     return any(os.path.getmtime(x) > t for x in deps)
 
 
-def _compile(src: str, verbose: bool, incremental: bool = False) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, verbose: bool, incremental: bool = False, sanitize: bool = False) -> str:
+    obj = os.path.join(ASAN_DIR if sanitize else BUILD, os.path.splitext(src)[0] + ".o")
     if incremental and not _stale(src, obj):
         return obj
-    cmd = [_hipcc(), *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *CFLAGS, *(SAN if sanitize else []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -76,23 +88,25 @@ def _compile(src: str, verbose: bool, incremental: bool = False) -> str:
 
 
 def build(verbose: bool = False, jobs: int | None = None,
-          incremental: bool = False) -> str:
+          incremental: bool = False, sanitize: bool = False) -> str:
     """Compile every source (incremental: only those whose object is stale)
-    and link the library."""
-    os.makedirs(BUILD, exist_ok=True)
+    and link the library (sanitize: the host-sanitized variant)."""
+    os.makedirs(ASAN_DIR if sanitize else BUILD, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 8)
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, incremental), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, incremental, sanitize), SOURCES))
+    lib = ASAN_LIB if sanitize else LIB
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs,
+           *(["-fsanitize=address,undefined", "-shared-libsan"] if sanitize else []),
            "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def main() -> None:
@@ -101,8 +115,10 @@ def main() -> None:
     ap.add_argument("-j", "--jobs", type=int, default=None)
     ap.add_argument("-i", "--incremental", action="store_true",
                     help="recompile only sources whose object is stale")
+    ap.add_argument("--sanitize", action="store_true",
+                    help="build the host-sanitized variant _build/asan/libgdn_asan.so")
     a = ap.parse_args()
-    print(build(a.verbose, a.jobs, a.incremental))
+    print(build(a.verbose, a.jobs, a.incremental, a.sanitize))
 
 
 if __name__ == "__main__":

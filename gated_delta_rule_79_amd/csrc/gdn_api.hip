@@ -258,7 +258,7 @@ gdn_status gdn_profile_read(double* total_ms, int32_t* count) {
 
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
-const char* gdn_status_str(gdn_status s) {
+const char* gdn_status_str(int s) {
   switch (s) {
     case GDN_OK: return "GDN_OK";
     case GDN_ERR_NULL: return "GDN_ERR_NULL: required pointer is NULL";

@@ -549,8 +549,8 @@ struct GradSmem {
   static constexpr bool fits = total + 16 <= 160 * 1024;
 };
 
-template <int C, int DK, typename IO, int GATE, int SW>
-__global__ __launch_bounds__(256) void bwd_grad_kernel(
+template <int C, int DK, typename IO, int GATE, int SW, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
@@ -568,8 +568,9 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   constexpr int LDK = S::LDK, LDC = S::LDC, LS = S::LDS_, LDD = S::LDD;
   constexpr int VW = 16 / ib;
   constexpr int VPR = DK / VW;
-  constexpr int NCD = NB * NDT, NU = (NCD + 3) / 4;   // C x DK tiles per wave
-  constexpr int NCC = NB * NB, NUC = (NCC + 3) / 4;   // C x C tiles per wave
+  constexpr int NT = 64 * NW;                         // threads
+  constexpr int NCD = NB * NDT, NU = (NCD + NW - 1) / NW;   // C x DK tiles per wave
+  constexpr int NCC = NB * NB, NUC = (NCC + NW - 1) / NW;   // C x C tiles per wave
   constexpr int NCS = NB * (SW / 16);                 // C x SW tiles
 
   __shared__ __attribute__((aligned(16))) char smem[S::total];
@@ -630,7 +631,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     sbeta[tid] = tid < len ? load_gate(beta, (tok0 + tid) * H + h, gbf) : 0.f;
     sdb[tid] = 0.f;
   }
-  for (int d = tid; d < DK; d += 256) sdD[d] = 0.f;
+  for (int d = tid; d < DK; d += NT) sdD[d] = 0.f;
   if constexpr (!CH) {
     if (wave == 0) {
       float x = 0.f;
@@ -644,12 +645,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       if (lane < C) sg[lane] = x;
     }
   } else {
-    for (int e = tid; e < C * DK; e += 256) {
+    for (int e = tid; e < C * DK; e += NT) {
       const int r = e / DK, cc = e % DK;
       sg[e] = r < len ? load_gate(la, ((tok0 + r) * H + h) * DK + cc, gbf) : 0.f;
     }
   }
-  for (int e = tid; e < C * VPR; e += 256) {
+  for (int e = tid; e < C * VPR; e += NT) {
     const int r = e / VPR, cv = (e % VPR) * VW;
     uint4 rk = make_uint4(0, 0, 0, 0), rq = make_uint4(0, 0, 0, 0);
     if (r < len) {
@@ -662,7 +663,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   }
   __syncthreads();
   if constexpr (CH) {
-    for (int cc = tid; cc < DK; cc += 256) {
+    for (int cc = tid; cc < DK; cc += NT) {
       float x = 0.f, mx = -3.0e38f, mn = 3.0e38f;
       for (int r = 0; r < C; ++r) {
         x += sg[r * DK + cc];
@@ -719,7 +720,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 
   // ---- 1. KK = decayed K K^T (strict lower) and P (lower) ------------------
   if (!exact) {
-    for (int t = wave; t < NCC; t += 4) {
+    for (int t = wave; t < NCC; t += NW) {
       const int mt = t / NB, nt = t % NB;
       if (nt > mt) {
 #pragma unroll
@@ -744,7 +745,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       }
     }
   } else if constexpr (CH) {
-    for (int e = tid; e < C * C; e += 256) {
+    for (int e = tid; e < C * C; e += NT) {
       const int r = e / C, i = e % C;
       float kv = 0.f, pv = 0.f;
       if (i <= r) {
@@ -779,7 +780,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       for (int r = 0; r < 16; ++r) sT[(16 * b + r) * LDC + 16 * b + j] = x[r];
     }
   } else {
-    for (int e = tid - 64; e < C * C; e += 192) {
+    for (int e = tid - 64; e < C * C; e += NT - 64) {
       const int r = e / C, i = e % C;
       if ((i >> 4) > (r >> 4)) sT[r * LDC + i] = 0.f;
     }
@@ -827,12 +828,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 
   // slab loads in registers: the next slab's are issued as soon as the
   // current one is in LDS, so they travel while the slab is processed
-  constexpr int NVE = (C * SW + 255) / 256, NME = (DK * SW + 255) / 256;
+  constexpr int NVE = (C * SW + NT - 1) / NT, NME = (DK * SW + NT - 1) / NT;
   float vv[NVE], gg[NVE], mm[NME], dd[NME];
   auto load_slab = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < NVE; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + NT * u;
       const int r = e / SW, j = e % SW;
       vv[u] = gg[u] = 0.f;
       if (e < C * SW && r < len) {
@@ -843,7 +844,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     }
 #pragma unroll
     for (int u = 0; u < NME; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + NT * u;
       const int d = e / SW, j = e % SW;
       mm[u] = dd[u] = 0.f;
       if (e < DK * SW) {
@@ -858,7 +859,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     {
 #pragma unroll
       for (int u = 0; u < NVE; ++u) {
-        const int e = tid + 256 * u;
+        const int e = tid + NT * u;
         if (e < C * SW) {
           sV[(e / SW) * LS + e % SW] = vv[u];
           sDO[(e / SW) * LS + e % SW] = gg[u];
@@ -870,7 +871,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       }
 #pragma unroll
       for (int u = 0; u < NME; ++u) {
-        const int e = tid + 256 * u;
+        const int e = tid + NT * u;
         if (e < DK * SW) {
           sM0[(e / SW) * LS + e % SW] = mm[u];
           if constexpr (S::BROWS) {
@@ -888,7 +889,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     if (s0 + SW < dv) load_slab(s0 + SW);
     __syncthreads();
     // Z = Y - X M0 (Y = diag(b) V),  dE = P^T dO + K~ dM1
-    for (int t = wave; t < 2 * NCS; t += 4) {
+    for (int t = wave; t < 2 * NCS; t += NW) {
       const int tt = t % NCS, mt = tt / (SW / 16), nt = tt % (SW / 16);
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
       if (t < NCS) {
@@ -936,7 +937,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     }
     __syncthreads();
     // E = T Z;  dY = T^T dE -> dv = b dY and dbeta += rowsum(dY V)
-    for (int t = wave; t < 2 * NCS; t += 4) {
+    for (int t = wave; t < 2 * NCS; t += NW) {
       const int tt = t % NCS, mt = tt / (SW / 16), nt = tt % (SW / 16);
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
       if (t < NCS) {
@@ -977,7 +978,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       for (int nt = 0; nt < SW / 16; ++nt) acc += spart[nt * C + tid];
       sdb[tid] = acc;
     }
-    for (int d = tid; d < DK; d += 256) {
+    for (int d = tid; d < DK; d += NT) {
       float acc = 0.f;
       for (int j = 0; j < SW; ++j) acc += sM0[d * LS + j] * sDM1[d * LS + j];
       sdD[d] += acc;
@@ -985,7 +986,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     // register accumulators (contractions over the slab's columns)
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int t = wave + 4 * u;
+      const int t = wave + NW * u;
       if (t >= NCD) continue;
       const int mt = t / NDT, nt = t % NDT;
       if constexpr (S::BROWS) {
@@ -1014,7 +1015,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     }
 #pragma unroll
     for (int u = 0; u < NUC; ++u) {
-      const int t = wave + 4 * u;
+      const int t = wave + NW * u;
       if (t >= NCC) continue;
       const int mt = t / NB, nt = t % NB;
       if constexpr (S::BROWS) {
@@ -1044,7 +1045,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   floatx4 oq[NU], ok[NU], og[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int t = wave + 4 * u;
+    const int t = wave + NW * u;
     oq[u] = ok[u] = og[u] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (t >= NCD) continue;
     const int mt = t / NDT, nt = t % NDT;
@@ -1066,7 +1067,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   // dW into LDS (dW = -aW), dP decayed into sP (overwrites P)
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int t = wave + 4 * u;
+    const int t = wave + NW * u;
     if (t >= NCD) continue;
     const int mt = t / NDT, nt = t % NDT;
 #pragma unroll
@@ -1076,7 +1077,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   __syncthreads();  // all P reads of the slab phase are done
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
-    const int t = wave + 4 * u;
+    const int t = wave + NW * u;
     if (t >= NCC) continue;
     const int mt = t / NB, nt = t % NB;
 #pragma unroll
@@ -1090,7 +1091,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   floatx4 oX[NU];
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
-    const int t = wave + 4 * u;
+    const int t = wave + NW * u;
     if (t >= NCC) continue;
     const int mt = t / NB, nt = t % NB;
     aT[u] = tmma<OP, DK>([&](int r, int d) { return sDW[r * LDD + d]; },
@@ -1099,7 +1100,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   }
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int t = wave + 4 * u;
+    const int t = wave + NW * u;
     oX[u] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (t >= NCD) continue;
     const int mt = t / NDT, nt = t % NDT;
@@ -1130,7 +1131,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   float* sDT = sP;
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
-    const int t = wave + 4 * u;
+    const int t = wave + NW * u;
     if (t >= NCC) continue;
     const int mt = t / NB, nt = t % NB;
 #pragma unroll
@@ -1141,7 +1142,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   float* sZ2 = sR;
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
-    const int t = wave + 4 * u;
+    const int t = wave + NW * u;
     if (t >= NCC) continue;
     const int mt = t / NB, nt = t % NB;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1157,7 +1158,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   float* sDA = sP;
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
-    const int t = wave + 4 * u;
+    const int t = wave + NW * u;
     if (t >= NCC) continue;
     const int mt = t / NB, nt = t % NB;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1169,7 +1170,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   __syncthreads();  // every read of dT is done before dA overwrites it
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
-    const int t = wave + 4 * u;
+    const int t = wave + NW * u;
     if (t >= NCC) continue;
     const int mt = t / NB, nt = t % NB;
     floatx4 pb;
@@ -1190,7 +1191,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   // dk_A1 = (b dA o Gamma) K, dk_A2 = (b dA o Gamma)^T K, and the dX terms
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int t = wave + 4 * u;
+    const int t = wave + NW * u;
     if (t >= NCD) continue;
     const int mt = t / NDT, nt = t % NDT;
     floatx4 t1 = {0.f, 0.f, 0.f, 0.f}, t2 = {0.f, 0.f, 0.f, 0.f};
@@ -1227,7 +1228,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   float* sdg = sR;  // [C][DK+1] gate gradient per (row, channel)
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int t = wave + 4 * u;
+    const int t = wave + NW * u;
     if (t >= NCD) continue;
     const int mt = t / NDT, nt = t % NDT;
 #pragma unroll
@@ -1250,7 +1251,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   __syncthreads();
   // d log alpha = reverse cumulative sum of dg inside the chunk
   if constexpr (CH) {
-    for (int d = tid; d < DK; d += 256) {
+    for (int d = tid; d < DK; d += NT) {
       float acc = 0.f;
       for (int r = C - 1; r >= 0; --r) {
         acc += sdg[r * LDD + d];
@@ -1288,6 +1289,11 @@ inline size_t bwd_states_bytes(const Problem& p) {
 }
 
 constexpr int kSlab = 16;  // value columns per slab of the gradient kernel
+// waves of the gradient kernel (its LDS plan allows one workgroup per CU).
+// Eight waves were measured against four on the 16k varlen batch: the same
+// time with the scalar gate (2.50 against 2.52 ms) and slower with the
+// per-channel gate (8.4 against 8.0 ms), whose accumulators then spill.
+constexpr int kGradWaves = 4;
 
 template <int C, int DK, typename IO, int GATE>
 hipError_t run_bwd(const Problem& p, const void* q, const void* k,
@@ -1391,8 +1397,8 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
   }
   if (p.nchunks > 0) {
     StageScope scope(GDN_STAGE_BWD_GRAD, s);
-    hipLaunchKernelGGL((bwd_grad_kernel<C, DK, IO, GATE, SW>),
-                       dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(256), 0, s,
+    hipLaunchKernelGGL((bwd_grad_kernel<C, DK, IO, GATE, SW, kGradWaves>),
+                       dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(64 * kGradWaves), 0, s,
                        map, p.H, p.dv, p.nchunks, q, k, v, beta, la, gbf, d_o,
                        states, dstates, dq, dk, dv, dbeta, dla);
     e = hipGetLastError();

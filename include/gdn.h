@@ -130,8 +130,10 @@ typedef struct {
 /* ABI version of the loaded library (GDN_ABI_VERSION). */
 int gdn_abi_version(void);
 
-/* Static, never NULL, human-readable name of a status. */
-const char* gdn_status_str(gdn_status s);
+/* Static, never NULL, human-readable name of a status.  Takes the status as
+ * an int so that any value is defined behaviour ("GDN_ERR_UNKNOWN" for values
+ * outside gdn_status). */
+const char* gdn_status_str(int status);
 
 /* Workspace bytes gdn_chunk_fwd needs for problem *p (written to *bytes).
  * Returns the same validation status gdn_chunk_fwd would for the sizes. */

@@ -174,3 +174,34 @@ def bwd_errors_per_head(inp, got, heads=None):
         return h, errs
 
     return par_map(job, heads)
+
+
+# ---- canary-padded outputs: every kernel write outside its output is caught
+
+CANARY_BYTES = 4096
+CANARY = 0x5A
+
+
+class Padded:
+    """An output tensor inside a larger byte buffer whose CANARY_BYTES before
+    and after hold a fixed byte pattern; check() asserts they are intact."""
+
+    def __init__(self, shape, dtype, device="cuda"):
+        n = 1
+        for x in shape:
+            n *= int(x)
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        self.raw = torch.full((CANARY_BYTES * 2 + nbytes,), CANARY, dtype=torch.uint8,
+                              device=device)
+        self.nbytes = nbytes
+        self.t = self.raw[CANARY_BYTES:CANARY_BYTES + nbytes].view(dtype).view(*shape)
+
+    def check(self, what=""):
+        head = self.raw[:CANARY_BYTES]
+        tail = self.raw[CANARY_BYTES + self.nbytes:]
+        bad = int((head != CANARY).sum()) + int((tail != CANARY).sum())
+        assert bad == 0, f"{what}: {bad} canary bytes overwritten around the output"
+
+
+def padded_like(shape, dtype):
+    return Padded(shape, dtype)

@@ -11,16 +11,29 @@ import torch
 import gated_delta_rule_79_amd as gdn
 import oracle
 from gated_delta_rule_79_amd import synth
-from gpu_util import TOL, bwd_errors_per_head, log, np64, slice_err, state_err
+from gpu_util import TOL, Padded, bwd_errors_per_head, log, np64, slice_err, state_err
 
 pytestmark = pytest.mark.gpu
 
 
 def run_bwd(inp, need_ds0=True, **kw):
+    # every gradient inside a canary-padded buffer: a write past either end
+    # fails
     d = inp.to("cuda")
+    nseq = inp.q.shape[0] if inp.cu_seqlens is None else inp.cu_seqlens.numel() - 1
+    H, dk, dv = inp.q.shape[2], inp.q.shape[3], inp.v.shape[3]
+    pads = [Padded(tuple(inp.q.shape), inp.q.dtype), Padded(tuple(inp.k.shape), inp.k.dtype),
+            Padded(tuple(inp.v.shape), inp.v.dtype),
+            Padded(tuple(inp.beta.shape), torch.float32),
+            None if inp.log_alpha is None else Padded(tuple(inp.log_alpha.shape), torch.float32),
+            Padded((nseq, H, dk, dv), torch.float32) if need_ds0 else None]
     g = gdn.chunk_bwd(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, d.do, d.ds_final,
-                      chunk=inp.chunk, cu_seqlens=d.cu_seqlens, need_ds0=need_ds0, **kw)
+                      chunk=inp.chunk, cu_seqlens=d.cu_seqlens, need_ds0=need_ds0,
+                      out=[None if x is None else x.t for x in pads], **kw)
     torch.cuda.synchronize()
+    for nm, x in zip(("dq", "dk", "dv", "dbeta", "dlog_alpha", "ds0"), pads):
+        if x is not None:
+            x.check(nm)
     return g
 
 

@@ -12,17 +12,25 @@ import torch
 import gated_delta_rule_79_amd as gdn
 from gated_delta_rule_79_amd import synth
 import oracle
-from gpu_util import (TOL, dev, fwd_errors_per_head, log, np64, oracle_fwd,
+from gpu_util import (TOL, Padded, dev, fwd_errors_per_head, log, np64, oracle_fwd,
                       par_map, slice_err, state_err)
 
 pytestmark = pytest.mark.gpu
 
 
 def run(inp, **kw):
+    # outputs inside canary-padded buffers: a write past either end fails
     d = dev(inp)
+    nseq = inp.q.shape[0] if inp.cu_seqlens is None else inp.cu_seqlens.numel() - 1
+    H, dk, dv = inp.q.shape[2], inp.q.shape[3], inp.v.shape[3]
+    po = Padded(tuple(inp.v.shape), inp.q.dtype)
+    ps = Padded((nseq, H, dk, dv), torch.float32)
     o, sf = gdn.chunk_fwd(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0,
-                          chunk=inp.chunk, cu_seqlens=d.cu_seqlens, **kw)
+                          chunk=inp.chunk, cu_seqlens=d.cu_seqlens, o=po.t, s_final=ps.t,
+                          **kw)
     torch.cuda.synchronize()
+    po.check("o")
+    ps.check("s_final")
     return o, sf
 
 
