@@ -540,8 +540,17 @@ struct GradSmem {
   // and M0, dM1 ([DK][SW]) as bf16 rows for the contractions over the slab
   static constexpr bool BROWS = !CH && ib == 2 && SW == 16;
   static constexpr size_t slabb_bytes = BROWS ? (4 * size_t(C) + 2 * size_t(DK)) * SW * 2 : 0;
+  // bf16 inputs, per-token gates, 64-token chunks, 32-column slabs: the
+  // slab lives only as bf16 rows, each operand in the layout its products
+  // read as 16-byte fragments (contraction index contiguous): V, dO, E, dE
+  // [C][PR]; M0, dM1 [DK][PD]; M0^T, dM1^T [SW][PT]; dO^T, Z^T, dE^T [SW][PC]
+  static constexpr bool FAST = !CH && ib == 2 && C == 64 && SW == 32;
+  static constexpr int PR = SW + 8, PD = SW, PT = DK + 8, PC = C + 8;
+  static constexpr size_t fast_bytes =
+      (4 * size_t(C) * PR + 2 * size_t(DK) * PD + 2 * size_t(SW) * PT + 3 * size_t(SW) * PC) * 2;
   static constexpr size_t slab_bytes =
-      (5 * size_t(C) + 2 * size_t(DK)) * LDS_ * 4 + slabt_bytes + slabb_bytes;
+      FAST ? fast_bytes
+           : (5 * size_t(C) + 2 * size_t(DK)) * LDS_ * 4 + slabt_bytes + slabb_bytes;
   // post phase: dW, then dT T^T, then the gate gradient, each [C][DK+1]
   static constexpr size_t post_bytes = size_t(C) * (LDD > LDC ? LDD : LDC) * 4;
   static constexpr size_t r_bytes = slab_bytes > post_bytes ? slab_bytes : post_bytes;
@@ -826,6 +835,211 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
 #pragma unroll
   for (int u = 0; u < NUC; ++u) aP[u] = aT[u] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  if constexpr (S::FAST) {
+    // Wave w owns row tile w (C = 64 = 16 NW) of every product.  Per slab:
+    // stage (16-byte global loads, the next slab's issued before this one is
+    // processed), A: Z = diag(b) (V - diag(gamma) K M0) and dE = P^T dO
+    // + diag(e^{g_C - g}) K dM1, B: E = T Z and dY = T^T dE (dv, dbeta),
+    // C: the contractions over the slab's columns.  All operands are read as
+    // 16-byte fragments except T, T^T and P^T, built from the fp32 matrices.
+    static_assert(NB == NW, "one row tile per wave");
+    constexpr int PR = S::PR, PD = S::PD, PT = S::PT, PC = S::PC;
+    constexpr int NKDF = (DK + 31) / 32;
+    constexpr int VP = SW / 8, NVP = (C * VP + NT - 1) / NT;   // bf16 pieces
+    constexpr int MP = SW / 4, NMP = (DK * MP + NT - 1) / NT;  // fp32 pieces
+    __bf16* fV = reinterpret_cast<__bf16*>(sR);
+    __bf16* fDO = fV + C * PR;
+    __bf16* fE = fDO + C * PR;
+    __bf16* fDE = fE + C * PR;
+    __bf16* fM0 = fDE + C * PR;
+    __bf16* fDM1 = fM0 + DK * PD;
+    __bf16* fM0t = fDM1 + DK * PD;
+    __bf16* fDM1t = fM0t + SW * PT;
+    __bf16* fDOt = fDM1t + SW * PT;
+    __bf16* fZt = fDOt + SW * PC;
+    __bf16* fDEt = fZt + SW * PC;
+    auto fr = [](const __bf16* base, int idx) {
+      return lds_vec8<IO>(reinterpret_cast<const char*>(base), size_t(idx));
+    };
+    uint4 rv[NVP], rg[NVP], rm[NMP], rd[NMP];
+    float ddacc[NMP];
+#pragma unroll
+    for (int u = 0; u < NMP; ++u) ddacc[u] = 0.f;
+    auto load = [&](int s0) {
+#pragma unroll
+      for (int u = 0; u < NVP; ++u) {
+        const int e = tid + NT * u, r = e / VP, col = s0 + 8 * (e % VP);
+        rv[u] = rg[u] = make_uint4(0, 0, 0, 0);
+        if (e < C * VP && r < len && col < dv) {
+          const int64_t off = (((tok0 + r) * H + h) * dv + col) * 2;
+          rv[u] = *reinterpret_cast<const uint4*>(static_cast<const char*>(v) + off);
+          rg[u] = *reinterpret_cast<const uint4*>(static_cast<const char*>(d_o) + off);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NMP; ++u) {
+        const int e = tid + NT * u, d = e / MP, col = s0 + 4 * (e % MP);
+        rm[u] = rd[u] = make_uint4(0, 0, 0, 0);
+        if (e < DK * MP && col < dv) {
+          rm[u] = *reinterpret_cast<const uint4*>(M0g + static_cast<int64_t>(d) * dv + col);
+          rd[u] = *reinterpret_cast<const uint4*>(dM1g + static_cast<int64_t>(d) * dv + col);
+        }
+      }
+    };
+    auto stage = [&]() {
+#pragma unroll
+      for (int u = 0; u < NVP; ++u) {
+        const int e = tid + NT * u;
+        if (e >= C * VP) continue;
+        const int r = e / VP, j0 = 8 * (e % VP);
+        *reinterpret_cast<uint4*>(fV + r * PR + j0) = rv[u];
+        *reinterpret_cast<uint4*>(fDO + r * PR + j0) = rg[u];
+        const __bf16* g = reinterpret_cast<const __bf16*>(&rg[u]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) fDOt[(j0 + q) * PC + r] = g[q];
+      }
+#pragma unroll
+      for (int u = 0; u < NMP; ++u) {
+        const int e = tid + NT * u;
+        if (e >= DK * MP) continue;
+        const int d = e / MP, j0 = 4 * (e % MP);
+        const float* m = reinterpret_cast<const float*>(&rm[u]);
+        const float* dm = reinterpret_cast<const float*>(&rd[u]);
+        bf16x4 mb, db;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          ddacc[u] += m[q] * dm[q];
+          mb[q] = static_cast<__bf16>(m[q]);
+          db[q] = static_cast<__bf16>(dm[q]);
+          fM0t[(j0 + q) * PT + d] = mb[q];
+          fDM1t[(j0 + q) * PT + d] = db[q];
+        }
+        *reinterpret_cast<bf16x4*>(fM0 + d * PD + j0) = mb;
+        *reinterpret_cast<bf16x4*>(fDM1 + d * PD + j0) = db;
+      }
+    };
+    const int r0 = 16 * wave;
+    floatx4 dbacc = {0.f, 0.f, 0.f, 0.f};
+    load(0);
+    for (int s0 = 0; s0 < dv; s0 += SW) {
+      stage();
+      if (s0 + SW < dv) load(s0 + SW);
+      __syncthreads();
+      // A. Z (into Z^T) and dE (rows and dE^T)
+      opvec<OP> kf[NKDF], pt[2];
+#pragma unroll
+      for (int kb = 0; kb < NKDF; ++kb) {
+        const int k0 = 32 * kb + 8 * lg;
+        kf[kb] = k0 < DK ? lds_vec8<IO>(sK, size_t(r0 + l16) * LDK + k0) : zero_vec<OP>();
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float a[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a[q] = sP[(32 * kb + 8 * lg + q) * LDC + r0 + l16];
+        pt[kb] = frag<OP>::from_floats(a);
+      }
+#pragma unroll
+      for (int nt = 0; nt < SW / 16; ++nt) {
+        const int j = 16 * nt + l16;
+        floatx4 xm = {0.f, 0.f, 0.f, 0.f}, a1 = xm, a2 = xm;
+#pragma unroll
+        for (int kb = 0; kb < NKDF; ++kb) {
+          const int k0 = 32 * kb + 8 * lg;
+          xm = mma32(kf[kb], k0 < DK ? fr(fM0t, j * PT + k0) : zero_vec<OP>(), xm);
+          a2 = mma32(kf[kb], k0 < DK ? fr(fDM1t, j * PT + k0) : zero_vec<OP>(), a2);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) a1 = mma32(pt[kb], fr(fDOt, j * PC + 32 * kb + 8 * lg), a1);
+        bf16x4 zb, eb;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = r0 + 4 * lg + q;
+          const float vr = static_cast<float>(fV[r * PR + j]);
+          zb[q] = static_cast<__bf16>(sbeta[r] * (vr - gq(r, 0) * xm[q]));
+          eb[q] = static_cast<__bf16>(a1[q] + gk(r, 0) * a2[q]);
+          fDE[r * PR + j] = eb[q];
+        }
+        *reinterpret_cast<bf16x4*>(fZt + j * PC + r0 + 4 * lg) = zb;
+        *reinterpret_cast<bf16x4*>(fDEt + j * PC + r0 + 4 * lg) = eb;
+      }
+      __syncthreads();
+      // B. E = T Z (rows) and dY = T^T dE: dv = b dY, dbeta += rowsum(dY V)
+      opvec<OP> tf[2], ttf[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float a[8], b[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int i = 32 * kb + 8 * lg + q;
+          a[q] = sT[(r0 + l16) * LDC + i];
+          b[q] = sT[i * LDC + r0 + l16];
+        }
+        tf[kb] = frag<OP>::from_floats(a);
+        ttf[kb] = frag<OP>::from_floats(b);
+      }
+#pragma unroll
+      for (int nt = 0; nt < SW / 16; ++nt) {
+        const int j = 16 * nt + l16;
+        floatx4 ee = {0.f, 0.f, 0.f, 0.f}, yy = ee;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          ee = mma32(tf[kb], fr(fZt, j * PC + 32 * kb + 8 * lg), ee);
+          yy = mma32(ttf[kb], fr(fDEt, j * PC + 32 * kb + 8 * lg), yy);
+        }
+        floatx4 pv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = r0 + 4 * lg + q;
+          fE[i * PR + j] = static_cast<__bf16>(ee[q]);
+          pv[q] = yy[q] * static_cast<float>(fV[i * PR + j]);
+          if (i < len && s0 + j < dv)
+            io<IO>::store(dvv, ((tok0 + i) * H + h) * dv + s0 + j, sbeta[i] * yy[q]);
+        }
+        dbacc += tile_rowsum(pv);
+      }
+      __syncthreads();
+      // C. contractions over the slab's 32 columns (one K block)
+      const opvec<OP> fdo = fr(fDO, (r0 + l16) * PR + 8 * lg);
+      const opvec<OP> fde = fr(fDE, (r0 + l16) * PR + 8 * lg);
+      const opvec<OP> fe = fr(fE, (r0 + l16) * PR + 8 * lg);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const opvec<OP> fm = fr(fM0, (16 * u + l16) * PD + 8 * lg);
+        const opvec<OP> fd = fr(fDM1, (16 * u + l16) * PD + 8 * lg);
+        aQ[u] = mma32(fdo, fm, aQ[u]);
+        aW[u] = mma32(fde, fm, aW[u]);
+        aK[u] = mma32(fe, fd, aK[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < NUC; ++u) {
+        aP[u] = mma32(fdo, fr(fE, (16 * u + l16) * PR + 8 * lg), aP[u]);
+        aT[u] = mma32(fde, fr(fV, (16 * u + l16) * PR + 8 * lg), aT[u]);
+      }
+      __syncthreads();
+    }
+    // Y = diag(b) V: the scale of aT's columns
+#pragma unroll
+    for (int u = 0; u < NUC; ++u) {
+      const float bi = sbeta[16 * u + l16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) aT[u][q] *= bi;
+    }
+    if (l16 == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sdb[r0 + 4 * lg + q] = dbacc[q];
+    }
+    // sum_j M0 (.) dM1 per key row: the MP lanes of a row are adjacent
+#pragma unroll
+    for (int u = 0; u < NMP; ++u) {
+      float x = ddacc[u];
+#pragma unroll
+      for (int m = 1; m < MP; m <<= 1) x += __shfl_xor(x, m, 64);
+      const int e = tid + NT * u;
+      if (e < DK * MP && e % MP == 0) sdD[e / MP] = x;
+    }
+    __syncthreads();
+  } else {
   // slab loads in registers: the next slab's are issued as soon as the
   // current one is in LDS, so they travel while the slab is processed
   constexpr int NVE = (C * SW + NT - 1) / NT, NME = (DK * SW + NT - 1) / NT;
@@ -1038,17 +1252,43 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
     }
     __syncthreads();
   }
+  }  // slab phase
 
   // ---- 4. post: through T, the decays and K K^T / Q K^T --------------------
+  // tile u of this wave: C x DK tiles (mt, nt) and C x C tiles; the fast
+  // slab phase gives wave w row tile w, the others deal tiles round robin
+  auto tile_cd = [&](int u, int* mt, int* nt) -> bool {
+    if constexpr (S::FAST) {
+      *mt = wave;
+      *nt = u;
+      return true;
+    } else {
+      const int t = wave + NW * u;
+      *mt = t / NDT;
+      *nt = t % NDT;
+      return t < NCD;
+    }
+  };
+  auto tile_cc = [&](int u, int* mt, int* nt) -> bool {
+    if constexpr (S::FAST) {
+      *mt = wave;
+      *nt = u;
+      return true;
+    } else {
+      const int t = wave + NW * u;
+      *mt = t / NB;
+      *nt = t % NB;
+      return t < NCC;
+    }
+  };
   // dq = dQ~ (.) gamma + dq_P ; dk = dK~ (.) e^{g_C - g} + dX (.) b gamma + ...
   // dg collects the per-(row, channel) gate gradient.
   floatx4 oq[NU], ok[NU], og[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int t = wave + NW * u;
     oq[u] = ok[u] = og[u] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (t >= NCD) continue;
-    const int mt = t / NDT, nt = t % NDT;
+    int mt, nt;
+    if (!tile_cd(u, &mt, &nt)) continue;
     floatx4 cs;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -1067,9 +1307,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   // dW into LDS (dW = -aW), dP decayed into sP (overwrites P)
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int t = wave + NW * u;
-    if (t >= NCD) continue;
-    const int mt = t / NDT, nt = t % NDT;
+    int mt, nt;
+    if (!tile_cd(u, &mt, &nt)) continue;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       sDW[(16 * mt + 4 * lg + s) * LDD + 16 * nt + l16] = -aW[u][s];
@@ -1077,9 +1316,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   __syncthreads();  // all P reads of the slab phase are done
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
-    const int t = wave + NW * u;
-    if (t >= NCC) continue;
-    const int mt = t / NB, nt = t % NB;
+    int mt, nt;
+    if (!tile_cc(u, &mt, &nt)) continue;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int r = 16 * mt + 4 * lg + s, i = 16 * nt + l16;
@@ -1091,19 +1329,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   floatx4 oX[NU];
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
-    const int t = wave + NW * u;
-    if (t >= NCC) continue;
-    const int mt = t / NB, nt = t % NB;
+    int mt, nt;
+    if (!tile_cc(u, &mt, &nt)) continue;
     aT[u] = tmma<OP, DK>([&](int r, int d) { return sDW[r * LDD + d]; },
                          [&](int d, int i) { return Xr(i, d); },
                          16 * mt, 16 * nt, l16, lg, aT[u]);
   }
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int t = wave + NW * u;
     oX[u] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (t >= NCD) continue;
-    const int mt = t / NDT, nt = t % NDT;
+    int mt, nt;
+    if (!tile_cd(u, &mt, &nt)) continue;
     oX[u] = tmma<OP, C>([&](int i, int r) { return sT[r * LDC + i]; },
                         [&](int r, int d) { return sDW[r * LDD + d]; },
                         16 * mt, 16 * nt, l16, lg, oX[u]);
@@ -1131,9 +1367,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   float* sDT = sP;
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
-    const int t = wave + NW * u;
-    if (t >= NCC) continue;
-    const int mt = t / NB, nt = t % NB;
+    int mt, nt;
+    if (!tile_cc(u, &mt, &nt)) continue;
 #pragma unroll
     for (int s = 0; s < 4; ++s) sDT[(16 * mt + 4 * lg + s) * LDC + 16 * nt + l16] = aT[u][s];
   }
@@ -1142,9 +1377,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   float* sZ2 = sR;
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
-    const int t = wave + NW * u;
-    if (t >= NCC) continue;
-    const int mt = t / NB, nt = t % NB;
+    int mt, nt;
+    if (!tile_cc(u, &mt, &nt)) continue;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = tmma<OP, C>([&](int r, int cc) { return sDT[r * LDC + cc]; },
                       [&](int cc, int i) { return sT[i * LDC + cc]; },
@@ -1158,9 +1392,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   float* sDA = sP;
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
-    const int t = wave + NW * u;
-    if (t >= NCC) continue;
-    const int mt = t / NB, nt = t % NB;
+    int mt, nt;
+    if (!tile_cc(u, &mt, &nt)) continue;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = tmma<OP, C>([&](int a, int r) { return sT[r * LDC + a]; },
                       [&](int r, int b) { return sZ2[r * LDC + b]; },
@@ -1170,9 +1403,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   __syncthreads();  // every read of dT is done before dA overwrites it
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
-    const int t = wave + NW * u;
-    if (t >= NCC) continue;
-    const int mt = t / NB, nt = t % NB;
+    int mt, nt;
+    if (!tile_cc(u, &mt, &nt)) continue;
     floatx4 pb;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -1191,9 +1423,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   // dk_A1 = (b dA o Gamma) K, dk_A2 = (b dA o Gamma)^T K, and the dX terms
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int t = wave + NW * u;
-    if (t >= NCD) continue;
-    const int mt = t / NDT, nt = t % NDT;
+    int mt, nt;
+    if (!tile_cd(u, &mt, &nt)) continue;
     floatx4 t1 = {0.f, 0.f, 0.f, 0.f}, t2 = {0.f, 0.f, 0.f, 0.f};
     t1 = tmma<OP, C>([&](int r, int i) { return sDA[r * LDC + i]; },
                      [&](int i, int d) { return Kr(i, d) * dn(i, d); },
@@ -1228,9 +1459,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   float* sdg = sR;  // [C][DK+1] gate gradient per (row, channel)
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int t = wave + NW * u;
-    if (t >= NCD) continue;
-    const int mt = t / NDT, nt = t % NDT;
+    int mt, nt;
+    if (!tile_cd(u, &mt, &nt)) continue;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int r = 16 * mt + 4 * lg + s, d = 16 * nt + l16;
@@ -1295,13 +1525,20 @@ constexpr int kSlab = 16;  // value columns per slab of the gradient kernel
 // per-channel gate (8.4 against 8.0 ms), whose accumulators then spill.
 constexpr int kGradWaves = 4;
 
+// value columns per slab: 32 on the fast path (bf16 inputs, per-token
+// gates, 64-token chunks), kSlab otherwise
+template <int C, typename IO, int GATE>
+constexpr int grad_slab() {
+  return (io<IO>::bytes == 2 && GATE != GDN_GATE_CHANNEL && C == 64) ? 32 : kSlab;
+}
+
 template <int C, int DK, typename IO, int GATE>
 hipError_t run_bwd(const Problem& p, const void* q, const void* k,
                    const void* v, const void* beta, const void* la,
                    const float* s0, const void* d_o, const float* ds_final,
                    void* dq, void* dk, void* dv, float* dbeta, float* dla,
                    float* ds0, char* ws, hipStream_t s) {
-  constexpr int SW = kSlab;
+  constexpr int SW = grad_slab<C, IO, GATE>();
   if constexpr (!GradSmem<C, DK, IO, GATE, SW>::fits) {
     return hipErrorNotSupported;
   } else {
@@ -1410,9 +1647,12 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
 template <int C, int DK, typename IO>
 bool fits_gate(int gate) {
   switch (gate) {
-    case GDN_GATE_NONE: return GradSmem<C, DK, IO, GDN_GATE_NONE, kSlab>::fits;
-    case GDN_GATE_SCALAR: return GradSmem<C, DK, IO, GDN_GATE_SCALAR, kSlab>::fits;
-    default: return GradSmem<C, DK, IO, GDN_GATE_CHANNEL, kSlab>::fits;
+    case GDN_GATE_NONE:
+      return GradSmem<C, DK, IO, GDN_GATE_NONE, grad_slab<C, IO, GDN_GATE_NONE>()>::fits;
+    case GDN_GATE_SCALAR:
+      return GradSmem<C, DK, IO, GDN_GATE_SCALAR, grad_slab<C, IO, GDN_GATE_SCALAR>()>::fits;
+    default:
+      return GradSmem<C, DK, IO, GDN_GATE_CHANNEL, grad_slab<C, IO, GDN_GATE_CHANNEL>()>::fits;
   }
 }
 

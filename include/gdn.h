@@ -330,7 +330,12 @@ gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes);
  *   dbeta    : [B, T, H] fp32.
  *   dlog_alpha : fp32, shaped like log_alpha; NULL allowed for GATE_NONE.
  *   ds0      : [nseq, H, dk, dv] fp32 or NULL to skip.
- * The result is deterministic (no floating-point atomics). */
+ * The result is deterministic (no floating-point atomics).
+ * Supported set: as gdn_chunk_fwd, except fp32 inputs (io_dtype GDN_F32)
+ * with the per-channel gate at dk = 128 and chunk = 64, which return
+ * GDN_ERR_UNSUPPORTED (the gradient kernel's LDS plan, fp32 rows and the
+ * per-channel decays of a 64 x 128 chunk, does not fit in 160 KiB); chunk
+ * 32 or bf16 inputs cover that case. */
 gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k,
                          const void* v, const void* beta,
                          const void* log_alpha, const float* s0,
