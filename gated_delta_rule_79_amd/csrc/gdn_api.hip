@@ -3,6 +3,7 @@
 // status means no work was launched.  No exception crosses the ABI.
 
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 
 #include <algorithm>
@@ -19,6 +20,41 @@ namespace {
 
 std::atomic<int> g_fail_launch{0};  // gdn_test_set_fail_launch
 
+// ------------------------------------------------------------ diagnostics ---
+// With GDN_LOG set (non-empty, not "0") every refused call writes one line
+// to stderr naming the entry point, the status and the check's source line,
+// and every launch writes the resolved problem and the dispatch choices.
+// The variable is read at each call; the library is silent otherwise.
+
+thread_local const char* t_entry = "gdn";
+
+struct EntryScope {  // names the running entry point for the log lines
+  const char* prev;
+  explicit EntryScope(const char* name) : prev(t_entry) { t_entry = name; }
+  ~EntryScope() { t_entry = prev; }
+};
+
+bool log_on() {
+  const char* e = getenv("GDN_LOG");
+  return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+}
+
+gdn_status fail_at(gdn_status s, int line) {
+  if (log_on())
+    fprintf(stderr, "gdn: %s: %s (check at gdn_api.hip:%d)\n", t_entry, gdn_status_str(s),
+            line);
+  return s;
+}
+
+#define GDN_ENTRY() EntryScope gdn_entry_scope_(__func__)
+#define GDN_FAIL(s) fail_at((s), __LINE__)
+
+const char* dtype_name(int d) { return d == GDN_BF16 ? "bf16" : "f32"; }
+
+const char* gate_name(int g) {
+  return g == GDN_GATE_NONE ? "none" : g == GDN_GATE_SCALAR ? "scalar" : "channel";
+}
+
 bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
@@ -26,14 +62,14 @@ bool aligned16(const void* p) {
 // A pointer that must be present when its tensor has elements.
 gdn_status need(const void* p, int64_t elems) {
   if (elems == 0) return GDN_OK;
-  if (p == nullptr) return GDN_ERR_NULL;
-  if (!aligned16(p)) return GDN_ERR_ALIGN;
+  if (p == nullptr) return GDN_FAIL(GDN_ERR_NULL);
+  if (!aligned16(p)) return GDN_FAIL(GDN_ERR_ALIGN);
   return GDN_OK;
 }
 
 // An optional pointer: NULL is fine, otherwise it must be aligned.
 gdn_status opt(const void* p) {
-  if (p != nullptr && !aligned16(p)) return GDN_ERR_ALIGN;
+  if (p != nullptr && !aligned16(p)) return GDN_FAIL(GDN_ERR_ALIGN);
   return GDN_OK;
 }
 
@@ -50,26 +86,26 @@ bool dtype_ok(int d) { return d == GDN_F32 || d == GDN_BF16; }
 // Shared checks of the chunked entry points; fills *out.  lnh > 0: each
 // token takes 2^lnh delta steps (k, v, beta per step), out->T counts steps.
 gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out, int lnh = 0) {
-  if (p == nullptr) return GDN_ERR_NULL;
-  if (!dtype_ok(p->io_dtype) || !dtype_ok(p->gate_dtype)) return GDN_ERR_DTYPE;
+  if (p == nullptr) return GDN_FAIL(GDN_ERR_NULL);
+  if (!dtype_ok(p->io_dtype) || !dtype_ok(p->gate_dtype)) return GDN_FAIL(GDN_ERR_DTYPE);
   if (p->gate < GDN_GATE_NONE || p->gate > GDN_GATE_CHANNEL)
-    return GDN_ERR_UNSUPPORTED;
-  if (p->B < 1 || p->H < 1 || p->T < 0 || p->nseq < 0) return GDN_ERR_SHAPE;
-  if (!dk_ok(p->dk) || !dv_ok(p->dv)) return GDN_ERR_UNSUPPORTED;
+    return GDN_FAIL(GDN_ERR_UNSUPPORTED);
+  if (p->B < 1 || p->H < 1 || p->T < 0 || p->nseq < 0) return GDN_FAIL(GDN_ERR_SHAPE);
+  if (!dk_ok(p->dk) || !dv_ok(p->dv)) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
   if (p->chunk != 16 && p->chunk != 32 && p->chunk != 64)
-    return GDN_ERR_UNSUPPORTED;
+    return GDN_FAIL(GDN_ERR_UNSUPPORTED);
   if (p->nseq > 0) {
-    if (p->B != 1) return GDN_ERR_SHAPE;
-    if (p->cu_seqlens == nullptr) return GDN_ERR_NULL;
+    if (p->B != 1) return GDN_FAIL(GDN_ERR_SHAPE);
+    if (p->cu_seqlens == nullptr) return GDN_FAIL(GDN_ERR_NULL);
     if ((reinterpret_cast<uintptr_t>(p->cu_seqlens) & 3u) != 0)
-      return GDN_ERR_ALIGN;
+      return GDN_FAIL(GDN_ERR_ALIGN);
   } else if (p->cu_seqlens != nullptr) {
-    return GDN_ERR_SHAPE;
+    return GDN_FAIL(GDN_ERR_SHAPE);
   }
   // element counts must stay far inside int64 and the grid limits
   const int64_t tok = (static_cast<int64_t>(p->B) * p->T) << lnh;
-  if (tok * p->H * 256 > (int64_t(1) << 46)) return GDN_ERR_SHAPE;
-  if ((static_cast<int64_t>(p->T) << lnh) > (int64_t(1) << 30)) return GDN_ERR_SHAPE;
+  if (tok * p->H * 256 > (int64_t(1) << 46)) return GDN_FAIL(GDN_ERR_SHAPE);
+  if ((static_cast<int64_t>(p->T) << lnh) > (int64_t(1) << 30)) return GDN_FAIL(GDN_ERR_SHAPE);
   out->B = p->B;
   out->T = p->T << lnh;
   out->lnh = lnh;
@@ -89,10 +125,10 @@ gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out, int lnh 
   out->gate = p->gate;
   const int64_t per_seq = (static_cast<int64_t>(out->T) + p->chunk - 1) / p->chunk;
   out->nchunks = out->varlen ? per_seq + p->nseq : per_seq * p->B;
-  if (out->nchunks * p->H > (int64_t(1) << 31) - 1) return GDN_ERR_SHAPE;
+  if (out->nchunks * p->H > (int64_t(1) << 31) - 1) return GDN_FAIL(GDN_ERR_SHAPE);
   out->seg = gdn::plan_segments(*out);
   out->nsegs = gdn::seg_slots_host(*out);
-  if (out->nsegs * p->H * 32 > (int64_t(1) << 31) - 1) return GDN_ERR_SHAPE;
+  if (out->nsegs * p->H * 32 > (int64_t(1) << 31) - 1) return GDN_FAIL(GDN_ERR_SHAPE);
   return GDN_OK;
 }
 
@@ -114,8 +150,19 @@ gdn_status check_fwd_pointers(const gdn::Problem& p, const void* q,
   return GDN_OK;
 }
 
-gdn_status launched(hipError_t e) {
-  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+// Status of a launch; with GDN_LOG the resolved problem and its dispatch.
+gdn_status launched(const gdn::Problem& p, hipError_t e) {
+  if (log_on()) {
+    fprintf(stderr,
+            "gdn: %s: B=%d T=%d H=%d dk=%d dv=%d chunk=%d io=%s gate=%s/%s nseq=%d%s "
+            "chunks=%lld segment_chunks=%d segments=%lld steps_per_token=%d%s%s -> %s\n",
+            t_entry, p.B, p.T, p.H, p.dk, p.dv, p.chunk, dtype_name(p.io), gate_name(p.gate),
+            dtype_name(p.gdt), p.nseq, p.varlen ? " (varlen)" : "",
+            static_cast<long long>(p.nchunks), p.seg, static_cast<long long>(p.nsegs),
+            1 << p.lnh, p.qknorm ? " qk_l2norm" : "", p.beta_w ? " write_strength" : "",
+            hipGetErrorName(e));
+  }
+  return e == hipSuccess ? GDN_OK : GDN_FAIL(GDN_ERR_HIP);
 }
 
 // ------------------------------------------------------- stage timing ---
@@ -227,8 +274,9 @@ void gdn_profile_enable(int enable) {
 }
 
 gdn_status gdn_profile_read(double* total_ms, int32_t* count) {
+  GDN_ENTRY();
   try {
-    if (total_ms == nullptr || count == nullptr) return GDN_ERR_NULL;
+    if (total_ms == nullptr || count == nullptr) return GDN_FAIL(GDN_ERR_NULL);
     for (int i = 0; i < GDN_STAGE_COUNT; ++i) {
       total_ms[i] = 0.0;
       count[i] = 0;
@@ -251,7 +299,7 @@ gdn_status gdn_profile_read(double* total_ms, int32_t* count) {
     P.done.clear();
     return st;
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -278,14 +326,15 @@ const char* gdn_status_str(int s) {
 void gdn_test_set_fail_launch(int enable) { g_fail_launch.store(enable != 0); }
 
 gdn_status gdn_chunk_fwd_workspace(const gdn_problem* p, size_t* bytes) {
+  GDN_ENTRY();
   try {
-    if (bytes == nullptr) return GDN_ERR_NULL;
+    if (bytes == nullptr) return GDN_FAIL(GDN_ERR_NULL);
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
     *bytes = gdn::fwd_workspace_bytes(pp);
     return GDN_OK;
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -294,20 +343,21 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
                          const void* log_alpha, const float* s0, void* o,
                          float* s_final, void* ws, size_t ws_bytes,
                          void* stream) {
+  GDN_ENTRY();
   try {
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
     GDN_TRY(check_fwd_pointers(pp, q, k, v, beta, log_alpha, s0, o, s_final));
     const size_t need_ws = gdn::fwd_workspace_bytes(pp);
     if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
-      return GDN_ERR_WORKSPACE;
+      return GDN_FAIL(GDN_ERR_WORKSPACE);
     GDN_TRY(opt(ws));
-    if (g_fail_launch.load()) return GDN_ERR_HIP;
-    return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o,
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
+    return launched(pp, gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o,
                                     s_final, ws,
                                     static_cast<hipStream_t>(stream)));
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -359,21 +409,22 @@ gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* p, const void* q, const void
                                  const void* v, const void* beta,
                                  const void* log_alpha, const float* s0, void* o,
                                  float* s_final, void* stream) {
+  GDN_ENTRY();
   try {
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
     GDN_TRY(check_fwd_pointers(pp, q, k, v, beta, log_alpha, s0, o, s_final));
-    if (gdn::fwd_workspace_bytes(pp) > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_SCRATCH;
-    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    if (gdn::fwd_workspace_bytes(pp) > GDN_NOALLOC_SCRATCH_BYTES) return GDN_FAIL(GDN_ERR_SCRATCH);
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = -1;
     if ((st != nullptr ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev)) != hipSuccess)
-      return GDN_ERR_HIP;
+      return GDN_FAIL(GDN_ERR_HIP);
     void* ws = nullptr;
-    if (scratch_on(dev, &ws) != hipSuccess) return GDN_ERR_HIP;
-    return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o, s_final, ws, st));
+    if (scratch_on(dev, &ws) != hipSuccess) return GDN_FAIL(GDN_ERR_HIP);
+    return launched(pp, gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o, s_final, ws, st));
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -404,14 +455,15 @@ size_t conv_workspace_bytes(const gdn::Problem& p) {
 extern "C" {
 
 gdn_status gdn_chunk_fwd_qknorm_workspace(const gdn_problem* p, size_t* bytes) {
+  GDN_ENTRY();
   try {
-    if (bytes == nullptr) return GDN_ERR_NULL;
+    if (bytes == nullptr) return GDN_FAIL(GDN_ERR_NULL);
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
     *bytes = qknorm_workspace_bytes(pp);
     return GDN_OK;
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -421,15 +473,16 @@ gdn_status gdn_chunk_fwd_qknorm(const gdn_problem* p, const void* q, const void*
                                 const void* log_alpha, const float* s0, void* o,
                                 float* s_final, void* ws, size_t ws_bytes,
                                 void* stream) {
+  GDN_ENTRY();
   try {
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
     GDN_TRY(check_fwd_pointers(pp, q, k, v, beta, log_alpha, s0, o, s_final));
     const size_t need_ws = qknorm_workspace_bytes(pp);
     if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
-      return GDN_ERR_WORKSPACE;
+      return GDN_FAIL(GDN_ERR_WORKSPACE);
     GDN_TRY(opt(ws));
-    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (pp.gate == GDN_GATE_CHANNEL) {
       char* w = static_cast<char*>(ws);
@@ -438,26 +491,27 @@ gdn_status gdn_chunk_fwd_qknorm(const gdn_problem* p, const void* q, const void*
       char* fw = kn + rows_bytes(pp, pp.dk);
       hipError_t e = gdn::launch_prologue(pp, pp.dk, 0, q, nullptr, true, qn, st);
       if (e == hipSuccess) e = gdn::launch_prologue(pp, pp.dk, 0, k, nullptr, true, kn, st);
-      if (e != hipSuccess) return GDN_ERR_HIP;
-      return launched(gdn::launch_fwd(pp, qn, kn, v, beta, log_alpha, s0, o, s_final, fw, st));
+      if (e != hipSuccess) return GDN_FAIL(GDN_ERR_HIP);
+      return launched(pp, gdn::launch_fwd(pp, qn, kn, v, beta, log_alpha, s0, o, s_final, fw, st));
     }
     pp.qknorm = true;
-    return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o, s_final, ws, st));
+    return launched(pp, gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o, s_final, ws, st));
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
 gdn_status gdn_chunk_fwd_conv_workspace(const gdn_problem* p, int32_t width, size_t* bytes) {
+  GDN_ENTRY();
   try {
-    if (bytes == nullptr) return GDN_ERR_NULL;
-    if (width < 1 || width > 8) return GDN_ERR_UNSUPPORTED;
+    if (bytes == nullptr) return GDN_FAIL(GDN_ERR_NULL);
+    if (width < 1 || width > 8) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
     *bytes = conv_workspace_bytes(pp);
     return GDN_OK;
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -468,8 +522,9 @@ gdn_status gdn_chunk_fwd_conv(const gdn_problem* p, int32_t width, const void* x
                               const float* wk, const float* wv, const void* beta,
                               const void* log_alpha, const float* s0, void* o,
                               float* s_final, void* ws, size_t ws_bytes, void* stream) {
+  GDN_ENTRY();
   try {
-    if (width < 1 || width > 8) return GDN_ERR_UNSUPPORTED;
+    if (width < 1 || width > 8) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
     GDN_TRY(check_fwd_pointers(pp, xq, xk, xv, beta, log_alpha, s0, o, s_final));
@@ -477,9 +532,9 @@ gdn_status gdn_chunk_fwd_conv(const gdn_problem* p, int32_t width, const void* x
     GDN_TRY(need(wk, static_cast<int64_t>(pp.H) * pp.dk * width));
     GDN_TRY(need(wv, static_cast<int64_t>(pp.H) * pp.dv * width));
     const size_t need_ws = conv_workspace_bytes(pp);
-    if (ws == nullptr || ws_bytes < need_ws) return GDN_ERR_WORKSPACE;
+    if (ws == nullptr || ws_bytes < need_ws) return GDN_FAIL(GDN_ERR_WORKSPACE);
     GDN_TRY(opt(ws));
-    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* qn = static_cast<char*>(ws);
     char* kn = qn + rows_bytes(pp, pp.dk);
@@ -488,33 +543,34 @@ gdn_status gdn_chunk_fwd_conv(const gdn_problem* p, int32_t width, const void* x
     hipError_t e = gdn::launch_prologue(pp, pp.dk, width, xq, wq, true, qn, st);
     if (e == hipSuccess) e = gdn::launch_prologue(pp, pp.dk, width, xk, wk, true, kn, st);
     if (e == hipSuccess) e = gdn::launch_prologue(pp, pp.dv, width, xv, wv, false, vn, st);
-    if (e != hipSuccess) return GDN_ERR_HIP;
-    return launched(gdn::launch_fwd(pp, qn, kn, vn, beta, log_alpha, s0, o, s_final, fw, st));
+    if (e != hipSuccess) return GDN_FAIL(GDN_ERR_HIP);
+    return launched(pp, gdn::launch_fwd(pp, qn, kn, vn, beta, log_alpha, s0, o, s_final, fw, st));
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
 // Draft trees: one tree per chunk, no segment split, per-token gates only.
 static gdn_status check_tree(const gdn_problem* p, gdn::Problem* out) {
-  if (p == nullptr) return GDN_ERR_NULL;
-  if (p->gate == GDN_GATE_CHANNEL) return GDN_ERR_UNSUPPORTED;
+  if (p == nullptr) return GDN_FAIL(GDN_ERR_NULL);
+  if (p->gate == GDN_GATE_CHANNEL) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
   GDN_TRY(check_chunk_problem(p, out));
-  if (!out->varlen && p->T > p->chunk) return GDN_ERR_SHAPE;
+  if (!out->varlen && p->T > p->chunk) return GDN_FAIL(GDN_ERR_SHAPE);
   out->seg = 0;
   out->nsegs = out->nseq;
   return GDN_OK;
 }
 
 gdn_status gdn_tree_verify_workspace(const gdn_problem* p, size_t* bytes) {
+  GDN_ENTRY();
   try {
-    if (bytes == nullptr) return GDN_ERR_NULL;
+    if (bytes == nullptr) return GDN_FAIL(GDN_ERR_NULL);
     gdn::Problem pp;
     GDN_TRY(check_tree(p, &pp));
     *bytes = gdn::fwd_workspace_bytes(pp);
     return GDN_OK;
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -522,22 +578,23 @@ gdn_status gdn_tree_verify(const gdn_problem* p, const int32_t* parent, const vo
                            const void* k, const void* v, const void* beta,
                            const void* log_alpha, const float* state, void* o,
                            void* ws, size_t ws_bytes, void* stream) {
+  GDN_ENTRY();
   try {
     gdn::Problem pp;
     GDN_TRY(check_tree(p, &pp));
     GDN_TRY(check_fwd_pointers(pp, q, k, v, beta, log_alpha, state, o, nullptr));
     GDN_TRY(need(parent, static_cast<int64_t>(pp.B) * pp.T));
-    if ((reinterpret_cast<uintptr_t>(parent) & 3u) != 0) return GDN_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(parent) & 3u) != 0) return GDN_FAIL(GDN_ERR_ALIGN);
     const size_t need_ws = gdn::fwd_workspace_bytes(pp);
     if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
-      return GDN_ERR_WORKSPACE;
+      return GDN_FAIL(GDN_ERR_WORKSPACE);
     GDN_TRY(opt(ws));
-    if (g_fail_launch.load()) return GDN_ERR_HIP;
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
     pp.parent = parent;
-    return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, state, o, nullptr, ws,
+    return launched(pp, gdn::launch_fwd(pp, q, k, v, beta, log_alpha, state, o, nullptr, ws,
                                     static_cast<hipStream_t>(stream)));
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -545,6 +602,7 @@ gdn_status gdn_tree_commit(const gdn_problem* p, const int32_t* parent,
                            const int32_t* accepted, const void* k, const void* v,
                            const void* beta, const void* log_alpha, float* state,
                            void* stream) {
+  GDN_ENTRY();
   try {
     gdn::Problem pp;
     GDN_TRY(check_tree(p, &pp));
@@ -559,34 +617,35 @@ gdn_status gdn_tree_commit(const gdn_problem* p, const int32_t* parent,
     GDN_TRY(need(state, static_cast<int64_t>(pp.nseq) * pp.H * pp.dk * pp.dv));
     if ((reinterpret_cast<uintptr_t>(parent) & 3u) != 0 ||
         (reinterpret_cast<uintptr_t>(accepted) & 3u) != 0)
-      return GDN_ERR_ALIGN;
-    if (g_fail_launch.load()) return GDN_ERR_HIP;
-    return launched(gdn::launch_tree_commit(pp, parent, accepted, k, v, beta, log_alpha,
+      return GDN_FAIL(GDN_ERR_ALIGN);
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
+    return launched(pp, gdn::launch_tree_commit(pp, parent, accepted, k, v, beta, log_alpha,
                                             state, static_cast<hipStream_t>(stream)));
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
 // Householder-product transitions: nh in {1, 2, 4} delta steps per token,
 // per-token gates only.
 static gdn_status check_product(const gdn_problem* p, int32_t nh, gdn::Problem* out) {
-  if (p == nullptr) return GDN_ERR_NULL;
-  if (nh != 1 && nh != 2 && nh != 4) return GDN_ERR_UNSUPPORTED;
-  if (p->gate == GDN_GATE_CHANNEL) return GDN_ERR_UNSUPPORTED;
+  if (p == nullptr) return GDN_FAIL(GDN_ERR_NULL);
+  if (nh != 1 && nh != 2 && nh != 4) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
+  if (p->gate == GDN_GATE_CHANNEL) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
   return check_chunk_problem(p, out, nh == 1 ? 0 : (nh == 2 ? 1 : 2));
 }
 
 gdn_status gdn_chunk_fwd_product_workspace(const gdn_problem* p, int32_t nh,
                                            size_t* bytes) {
+  GDN_ENTRY();
   try {
-    if (bytes == nullptr) return GDN_ERR_NULL;
+    if (bytes == nullptr) return GDN_FAIL(GDN_ERR_NULL);
     gdn::Problem pp;
     GDN_TRY(check_product(p, nh, &pp));
     *bytes = gdn::fwd_workspace_bytes(pp);
     return GDN_OK;
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -595,33 +654,35 @@ gdn_status gdn_chunk_fwd_product(const gdn_problem* p, int32_t nh, const void* q
                                  const void* log_alpha, const float* s0, void* o,
                                  float* s_final, void* ws, size_t ws_bytes,
                                  void* stream) {
+  GDN_ENTRY();
   try {
     gdn::Problem pp;
     GDN_TRY(check_product(p, nh, &pp));
     GDN_TRY(check_fwd_pointers(pp, q, k, v, beta, log_alpha, s0, o, s_final));
     const size_t need_ws = gdn::fwd_workspace_bytes(pp);
     if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
-      return GDN_ERR_WORKSPACE;
+      return GDN_FAIL(GDN_ERR_WORKSPACE);
     GDN_TRY(opt(ws));
-    if (g_fail_launch.load()) return GDN_ERR_HIP;
-    return launched(gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o,
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
+    return launched(pp, gdn::launch_fwd(pp, q, k, v, beta, log_alpha, s0, o,
                                     s_final, ws,
                                     static_cast<hipStream_t>(stream)));
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
 gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes) {
+  GDN_ENTRY();
   try {
-    if (bytes == nullptr) return GDN_ERR_NULL;
+    if (bytes == nullptr) return GDN_FAIL(GDN_ERR_NULL);
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
-    if (!gdn::bwd_supported(pp)) return GDN_ERR_UNSUPPORTED;
+    if (!gdn::bwd_supported(pp)) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
     *bytes = gdn::bwd_workspace_bytes(pp);
     return GDN_OK;
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -631,10 +692,11 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k,
                          const void* d_o, const float* ds_final, void* dq,
                          void* dk, void* dv, float* dbeta, float* dlog_alpha,
                          float* ds0, void* ws, size_t ws_bytes, void* stream) {
+  GDN_ENTRY();
   try {
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
-    if (!gdn::bwd_supported(pp)) return GDN_ERR_UNSUPPORTED;
+    if (!gdn::bwd_supported(pp)) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
     const int64_t tok = static_cast<int64_t>(pp.B) * pp.T * pp.H;
     GDN_TRY(need(q, tok * pp.dk));
     GDN_TRY(need(k, tok * pp.dk));
@@ -657,14 +719,14 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k,
     GDN_TRY(opt(ds0));
     const size_t need_ws = gdn::bwd_workspace_bytes(pp);
     if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
-      return GDN_ERR_WORKSPACE;
+      return GDN_FAIL(GDN_ERR_WORKSPACE);
     GDN_TRY(opt(ws));
-    if (g_fail_launch.load()) return GDN_ERR_HIP;
-    return launched(gdn::launch_bwd(pp, q, k, v, beta, log_alpha, s0, d_o,
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
+    return launched(pp, gdn::launch_bwd(pp, q, k, v, beta, log_alpha, s0, d_o,
                                     ds_final, dq, dk, dv, dbeta, dlog_alpha,
                                     ds0, ws, static_cast<hipStream_t>(stream)));
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -676,15 +738,15 @@ namespace {
 gdn_status check_decode(const gdn_problem* p, const void* q, const void* k, const void* v,
                         const void* beta, const void* log_alpha, const float* state,
                         const void* o, gdn::Problem* pp) {
-  if (p == nullptr) return GDN_ERR_NULL;
-  if (!dtype_ok(p->io_dtype) || !dtype_ok(p->gate_dtype)) return GDN_ERR_DTYPE;
+  if (p == nullptr) return GDN_FAIL(GDN_ERR_NULL);
+  if (!dtype_ok(p->io_dtype) || !dtype_ok(p->gate_dtype)) return GDN_FAIL(GDN_ERR_DTYPE);
   if (p->gate < GDN_GATE_NONE || p->gate > GDN_GATE_CHANNEL)
-    return GDN_ERR_UNSUPPORTED;
-  if (p->B < 1 || p->H < 1) return GDN_ERR_SHAPE;
-  if (!dk_ok(p->dk) || !dv_ok(p->dv)) return GDN_ERR_UNSUPPORTED;
+    return GDN_FAIL(GDN_ERR_UNSUPPORTED);
+  if (p->B < 1 || p->H < 1) return GDN_FAIL(GDN_ERR_SHAPE);
+  if (!dk_ok(p->dk) || !dv_ok(p->dv)) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
   // one workgroup per (sequence, head, 64-column slab): within the grid limit
   if (static_cast<int64_t>(p->B) * p->H * ((p->dv + 63) / 64) > (int64_t(1) << 31) - 1)
-    return GDN_ERR_SHAPE;
+    return GDN_FAIL(GDN_ERR_SHAPE);
   *pp = gdn::Problem{};
   pp->B = p->B;
   pp->T = 1;
@@ -715,14 +777,15 @@ gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k,
                            const void* v, const void* beta,
                            const void* log_alpha, float* state, void* o,
                            void* stream) {
+  GDN_ENTRY();
   try {
     gdn::Problem pp;
     GDN_TRY(check_decode(p, q, k, v, beta, log_alpha, state, o, &pp));
-    if (g_fail_launch.load()) return GDN_ERR_HIP;
-    return launched(gdn::launch_decode(pp, q, k, v, beta, log_alpha, state, o,
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
+    return launched(pp, gdn::launch_decode(pp, q, k, v, beta, log_alpha, state, o,
                                        static_cast<hipStream_t>(stream)));
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -731,6 +794,7 @@ gdn_status gdn2_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
                           const void* v, const void* erase, const void* write,
                           const void* log_alpha, const float* s0, void* o,
                           float* s_final, void* ws, size_t ws_bytes, void* stream) {
+  GDN_ENTRY();
   try {
     gdn::Problem pp;
     GDN_TRY(check_chunk_problem(p, &pp));
@@ -738,30 +802,31 @@ gdn_status gdn2_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
     GDN_TRY(need(write, static_cast<int64_t>(pp.B) * pp.T * pp.H));
     const size_t need_ws = gdn::fwd_workspace_bytes(pp);
     if (need_ws > 0 && (ws == nullptr || ws_bytes < need_ws))
-      return GDN_ERR_WORKSPACE;
+      return GDN_FAIL(GDN_ERR_WORKSPACE);
     GDN_TRY(opt(ws));
-    if (g_fail_launch.load()) return GDN_ERR_HIP;
     pp.beta_w = write;
-    return launched(gdn::launch_fwd(pp, q, k, v, erase, log_alpha, s0, o, s_final, ws,
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
+    return launched(pp, gdn::launch_fwd(pp, q, k, v, erase, log_alpha, s0, o, s_final, ws,
                                     static_cast<hipStream_t>(stream)));
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
 gdn_status gdn2_decode_step(const gdn_problem* p, const void* q, const void* k,
                             const void* v, const void* erase, const void* write,
                             const void* log_alpha, float* state, void* o, void* stream) {
+  GDN_ENTRY();
   try {
     gdn::Problem pp;
     GDN_TRY(check_decode(p, q, k, v, erase, log_alpha, state, o, &pp));
     GDN_TRY(need(write, static_cast<int64_t>(pp.B) * pp.H));
-    if (g_fail_launch.load()) return GDN_ERR_HIP;
     pp.beta_w = write;
-    return launched(gdn::launch_decode(pp, q, k, v, erase, log_alpha, state, o,
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
+    return launched(pp, gdn::launch_decode(pp, q, k, v, erase, log_alpha, state, o,
                                        static_cast<hipStream_t>(stream)));
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 
@@ -769,15 +834,16 @@ gdn_status gdn_decode_step_product(const gdn_problem* p, int32_t nh, const void*
                                    const void* k, const void* v, const void* beta,
                                    const void* log_alpha, float* state, void* o,
                                    void* stream) {
+  GDN_ENTRY();
   try {
-    if (p == nullptr) return GDN_ERR_NULL;
-    if (!dtype_ok(p->io_dtype) || !dtype_ok(p->gate_dtype)) return GDN_ERR_DTYPE;
-    if (p->gate != GDN_GATE_NONE && p->gate != GDN_GATE_SCALAR) return GDN_ERR_UNSUPPORTED;
-    if (nh != 1 && nh != 2 && nh != 4) return GDN_ERR_UNSUPPORTED;
-    if (p->B < 1 || p->H < 1) return GDN_ERR_SHAPE;
-    if (!dk_ok(p->dk) || !dv_ok(p->dv)) return GDN_ERR_UNSUPPORTED;
+    if (p == nullptr) return GDN_FAIL(GDN_ERR_NULL);
+    if (!dtype_ok(p->io_dtype) || !dtype_ok(p->gate_dtype)) return GDN_FAIL(GDN_ERR_DTYPE);
+    if (p->gate != GDN_GATE_NONE && p->gate != GDN_GATE_SCALAR) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
+    if (nh != 1 && nh != 2 && nh != 4) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
+    if (p->B < 1 || p->H < 1) return GDN_FAIL(GDN_ERR_SHAPE);
+    if (!dk_ok(p->dk) || !dv_ok(p->dv)) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
     if (static_cast<int64_t>(p->B) * p->H * ((p->dv + 63) / 64) > (int64_t(1) << 31) - 1)
-      return GDN_ERR_SHAPE;
+      return GDN_FAIL(GDN_ERR_SHAPE);
     gdn::Problem pp{};
     pp.B = p->B;
     pp.T = 1;
@@ -797,11 +863,11 @@ gdn_status gdn_decode_step_product(const gdn_problem* p, int32_t nh, const void*
     else GDN_TRY(opt(log_alpha));
     GDN_TRY(need(state, nhd * p->dk * p->dv));
     GDN_TRY(need(o, nhd * p->dv));
-    if (g_fail_launch.load()) return GDN_ERR_HIP;
-    return launched(gdn::launch_decode_product(pp, nh, q, k, v, beta, log_alpha, state, o,
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
+    return launched(pp, gdn::launch_decode_product(pp, nh, q, k, v, beta, log_alpha, state, o,
                                                static_cast<hipStream_t>(stream)));
   } catch (...) {
-    return GDN_ERR_HIP;
+    return GDN_FAIL(GDN_ERR_HIP);
   }
 }
 

@@ -65,6 +65,13 @@
  *     launch returns GDN_ERR_HIP.  Device faults surface at the caller's
  *     next synchronisation (asynchronous HIP semantics).  No function
  *     aborts or lets an exception escape.
+ *   Diagnostics: the library writes nothing unless the environment variable
+ *     GDN_LOG is set to a non-empty value other than "0" (read at every
+ *     call).  Then each refused call writes one line to stderr with the
+ *     entry point, the status and the source line of the failed check, and
+ *     each launch writes the resolved problem and its dispatch choices
+ *     (chunk count, segment length and count, steps per token, the
+ *     normalising and write-strength variants) with the launch's HIP status.
  */
 #ifndef GDN_H_
 #define GDN_H_

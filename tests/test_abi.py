@@ -429,3 +429,40 @@ def test_conv_forward_validation(lib):
     assert call(wq=A + 4) == 5
     assert call(xq=None) == 1
     assert call(nbytes=n.value - 1) == 6
+
+
+def test_log_is_silent_by_default(lib, capfd, monkeypatch):
+    monkeypatch.delenv("GDN_LOG", raising=False)
+    assert fwd(lib, prob(dk=48)) == _lib.GDN_ERR_UNSUPPORTED
+    assert fwd(lib, prob()) == _lib.GDN_ERR_HIP
+    monkeypatch.setenv("GDN_LOG", "0")
+    assert fwd(lib, prob(dk=48)) == _lib.GDN_ERR_UNSUPPORTED
+    assert capfd.readouterr().err == ""
+
+
+def test_log_names_refusals_and_dispatch(lib, capfd, monkeypatch):
+    # GDN_LOG is read at every call: refusals name the entry point, the status
+    # and the check; a launch (here the test hook's failed one) names the
+    # resolved problem with its segment plan
+    monkeypatch.setenv("GDN_LOG", "1")
+    assert fwd(lib, prob(dk=48)) == _lib.GDN_ERR_UNSUPPORTED
+    err = capfd.readouterr().err.strip().splitlines()
+    assert len(err) == 2, err   # the workspace query and the call refuse
+    assert err[0].startswith("gdn: gdn_chunk_fwd_workspace: GDN_ERR_UNSUPPORTED")
+    assert err[1].startswith("gdn: gdn_chunk_fwd: GDN_ERR_UNSUPPORTED")
+    assert "check at gdn_api.hip:" in err[1]
+
+    assert fwd(lib, prob(T=4096, H=16, seg_chunks=5)) == _lib.GDN_ERR_HIP
+    line, refused = capfd.readouterr().err.strip().splitlines()
+    assert refused.startswith("gdn: gdn_chunk_fwd: GDN_ERR_HIP")
+    assert line.startswith("gdn: gdn_chunk_fwd: B=1 T=4096 H=16 dk=128 dv=128 chunk=64"), line
+    assert "io=bf16 gate=scalar/bf16" in line and "chunks=64 segment_chunks=5" in line
+    assert "segments=13" in line and line.endswith("-> hipErrorLaunchFailure")
+
+    n = ctypes.c_size_t(0)
+    p = prob(T=64, H=2, dk=64, dv=64)
+    assert lib.gdn_chunk_fwd_workspace(ctypes.byref(p), ctypes.byref(n)) == 0
+    st = lib.gdn2_chunk_fwd(ctypes.byref(p), A, A, A, A, A, A, None, A, None, A, n.value, None)
+    assert st == _lib.GDN_ERR_HIP
+    line = capfd.readouterr().err.strip().splitlines()[0]
+    assert line.startswith("gdn: gdn2_chunk_fwd: ") and "write_strength" in line, line
