@@ -500,6 +500,29 @@ __device__ __forceinline__ float tile_colsum(const floatx4& x) {
   return c;
 }
 
+// Per-element form of the two products of a C x C lower-triangular matrix G
+// with a key-side matrix under the per-channel pairwise decay, for the 16x16
+// output tile (mt, nt) in the MFMA accumulator layout (row 4 lg + s, column
+// l16), used where a chunk's channel span is too wide to factor:
+//   a(r, d) = sum_{i <= r} G[r][i] A(i, d) e^{g[r][d] - g[i][d]}
+//   b(r, d) = sum_{i >= r} G[i][r] B(i, d) e^{g[i][d] - g[r][d]}
+template <typename FA, typename FB>
+__device__ inline void pair_decay_products(const float* G, int ldg, FA A, FB B, const float* g,
+                                           int DK, int C, int mt, int nt, int l16, int lg,
+                                           floatx4* a, floatx4* b) {
+  const int d = 16 * nt + l16;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int r = 16 * mt + 4 * lg + s;
+    const float gr = g[r * DK + d];
+    float x = 0.f, y = 0.f;
+    for (int i = 0; i <= r; ++i) x += G[r * ldg + i] * A(i, d) * fast_exp(gr - g[i * DK + d]);
+    for (int i = r; i < C; ++i) y += G[i * ldg + r] * B(i, d) * fast_exp(g[i * DK + d] - gr);
+    (*a)[s] = x;
+    (*b)[s] = y;
+  }
+}
+
 template <int C, int DK, typename IO, int GATE, int SW>
 struct GradSmem {
   static constexpr int ib = io<IO>::bytes;
@@ -540,11 +563,12 @@ struct GradSmem {
   // and M0, dM1 ([DK][SW]) as bf16 rows for the contractions over the slab
   static constexpr bool BROWS = !CH && ib == 2 && SW == 16;
   static constexpr size_t slabb_bytes = BROWS ? (4 * size_t(C) + 2 * size_t(DK)) * SW * 2 : 0;
-  // bf16 inputs, per-token gates, 64-token chunks, 32-column slabs: the
-  // slab lives only as bf16 rows, each operand in the layout its products
-  // read as 16-byte fragments (contraction index contiguous): V, dO, E, dE
-  // [C][PR]; M0, dM1 [DK][PD]; M0^T, dM1^T [SW][PT]; dO^T, Z^T, dE^T [SW][PC]
-  static constexpr bool FAST = !CH && ib == 2 && C == 64 && SW == 32;
+  // bf16 inputs, 64-token chunks, 32-column slabs (16 for the per-channel
+  // gate, whose cumulative gates take 32 KB of LDS): the slab lives only as
+  // bf16 rows, each operand in the layout its products read as 16-byte
+  // fragments (contraction index contiguous): V, dO, E, dE [C][PR]; M0, dM1
+  // [DK][PD]; M0^T, dM1^T [SW][PT]; dO^T, Z^T, dE^T [SW][PC]
+  static constexpr bool FAST = ib == 2 && C == 64 && SW == (CH ? 16 : 32);
   static constexpr int PR = SW + 8, PD = SW, PT = DK + 8, PC = C + 8;
   static constexpr size_t fast_bytes =
       (4 * size_t(C) * PR + 2 * size_t(DK) * PD + 2 * size_t(SW) * PT + 3 * size_t(SW) * PC) * 2;
@@ -659,17 +683,20 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
       sg[e] = r < len ? load_gate(la, ((tok0 + r) * H + h) * DK + cc, gbf) : 0.f;
     }
   }
-  for (int e = tid; e < C * VPR; e += NT) {
-    const int r = e / VPR, cv = (e % VPR) * VW;
-    uint4 rk = make_uint4(0, 0, 0, 0), rq = make_uint4(0, 0, 0, 0);
-    if (r < len) {
-      const int64_t off = (((tok0 + r) * H + h) * DK + cv) * ib;
-      rk = *reinterpret_cast<const uint4*>(static_cast<const char*>(k) + off);
-      rq = *reinterpret_cast<const uint4*>(static_cast<const char*>(q) + off);
+  auto load_kq = [&]() {
+    for (int e = tid; e < C * VPR; e += NT) {
+      const int r = e / VPR, cv = (e % VPR) * VW;
+      uint4 rk = make_uint4(0, 0, 0, 0), rq = make_uint4(0, 0, 0, 0);
+      if (r < len) {
+        const int64_t off = (((tok0 + r) * H + h) * DK + cv) * ib;
+        rk = *reinterpret_cast<const uint4*>(static_cast<const char*>(k) + off);
+        rq = *reinterpret_cast<const uint4*>(static_cast<const char*>(q) + off);
+      }
+      *reinterpret_cast<uint4*>(sK + (size_t(r) * LDK + cv) * ib) = rk;
+      *reinterpret_cast<uint4*>(sQ + (size_t(r) * LDK + cv) * ib) = rq;
     }
-    *reinterpret_cast<uint4*>(sK + (size_t(r) * LDK + cv) * ib) = rk;
-    *reinterpret_cast<uint4*>(sQ + (size_t(r) * LDK + cv) * ib) = rq;
-  }
+  };
+  load_kq();
   __syncthreads();
   if constexpr (CH) {
     for (int cc = tid; cc < DK; cc += NT) {
@@ -918,20 +945,32 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
         *reinterpret_cast<bf16x4*>(fDM1 + d * PD + j0) = db;
       }
     };
+    if constexpr (CH) {
+      // the per-element decays of the two key operands, applied once per
+      // chunk: X = K (.) e^{g} over Q's rows, K~ = K (.) e^{g_C - g} over
+      // K's rows (K and Q are loaded again for the post phase)
+      for (int e = tid; e < C * DK; e += NT) {
+        const int r = e / DK, d = e % DK;
+        const float kv = Kr(r, d), g = sg[r * DK + d];
+        lds_st<IO>(sQ, size_t(r) * LDK + d, kv * fast_exp(g));
+        lds_st<IO>(sK, size_t(r) * LDK + d, kv * fast_exp(sg[(C - 1) * DK + d] - g));
+      }
+      __syncthreads();
+    }
     const int r0 = 16 * wave;
     floatx4 dbacc = {0.f, 0.f, 0.f, 0.f};
-    load(0);
+    // the per-channel gate's registers do not leave room for the next
+    // slab's loads in flight: it loads each slab just before staging it
+    if constexpr (!CH) load(0);
     for (int s0 = 0; s0 < dv; s0 += SW) {
+      if constexpr (CH) load(s0);
       stage();
-      if (s0 + SW < dv) load(s0 + SW);
+      if (!CH && s0 + SW < dv) load(s0 + SW);
       __syncthreads();
-      // A. Z (into Z^T) and dE (rows and dE^T)
-      opvec<OP> kf[NKDF], pt[2];
-#pragma unroll
-      for (int kb = 0; kb < NKDF; ++kb) {
-        const int k0 = 32 * kb + 8 * lg;
-        kf[kb] = k0 < DK ? lds_vec8<IO>(sK, size_t(r0 + l16) * LDK + k0) : zero_vec<OP>();
-      }
+      // A. Z (into Z^T) and dE (rows and dE^T).  Per-token gates scale the
+      // rows of K M0 and K dM1; with the per-channel gate Q's rows hold
+      // K (.) e^{g} and K's rows K (.) e^{g_C - g} during the slab phase
+      opvec<OP> pt[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float a[8];
@@ -946,8 +985,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
 #pragma unroll
         for (int kb = 0; kb < NKDF; ++kb) {
           const int k0 = 32 * kb + 8 * lg;
-          xm = mma32(kf[kb], k0 < DK ? fr(fM0t, j * PT + k0) : zero_vec<OP>(), xm);
-          a2 = mma32(kf[kb], k0 < DK ? fr(fDM1t, j * PT + k0) : zero_vec<OP>(), a2);
+          const bool in = k0 < DK;  // lanes past DK (DK = 16) carry zeros
+          const size_t ko = size_t(r0 + l16) * LDK + k0;
+          const opvec<OP> xf = in ? lds_vec8<IO>(CH ? sQ : sK, ko) : zero_vec<OP>();
+          const opvec<OP> kt = in ? lds_vec8<IO>(sK, ko) : zero_vec<OP>();
+          xm = mma32(xf, in ? fr(fM0t, j * PT + k0) : zero_vec<OP>(), xm);
+          a2 = mma32(kt, in ? fr(fDM1t, j * PT + k0) : zero_vec<OP>(), a2);
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) a1 = mma32(pt[kb], fr(fDOt, j * PC + 32 * kb + 8 * lg), a1);
@@ -956,8 +999,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
         for (int q = 0; q < 4; ++q) {
           const int r = r0 + 4 * lg + q;
           const float vr = static_cast<float>(fV[r * PR + j]);
-          zb[q] = static_cast<__bf16>(sbeta[r] * (vr - gq(r, 0) * xm[q]));
-          eb[q] = static_cast<__bf16>(a1[q] + gk(r, 0) * a2[q]);
+          const float sx = CH ? 1.f : gq(r, 0), sk = CH ? 1.f : gk(r, 0);
+          zb[q] = static_cast<__bf16>(sbeta[r] * (vr - sx * xm[q]));
+          eb[q] = static_cast<__bf16>(a1[q] + sk * a2[q]);
           fDE[r * PR + j] = eb[q];
         }
         *reinterpret_cast<bf16x4*>(fZt + j * PC + r0 + 4 * lg) = zb;
@@ -999,22 +1043,25 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
         dbacc += tile_rowsum(pv);
       }
       __syncthreads();
-      // C. contractions over the slab's 32 columns (one K block)
-      const opvec<OP> fdo = fr(fDO, (r0 + l16) * PR + 8 * lg);
-      const opvec<OP> fde = fr(fDE, (r0 + l16) * PR + 8 * lg);
-      const opvec<OP> fe = fr(fE, (r0 + l16) * PR + 8 * lg);
+      // C. contractions over the slab's columns (one K block of 32; a
+      // 16-column slab fills K groups 0 and 1, the others carry zeros)
+      const bool kin = 8 * lg < SW;
+      auto fs = [&](const __bf16* base, int idx) { return kin ? fr(base, idx) : zero_vec<OP>(); };
+      const opvec<OP> fdo = fs(fDO, (r0 + l16) * PR + 8 * lg);
+      const opvec<OP> fde = fs(fDE, (r0 + l16) * PR + 8 * lg);
+      const opvec<OP> fe = fs(fE, (r0 + l16) * PR + 8 * lg);
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const opvec<OP> fm = fr(fM0, (16 * u + l16) * PD + 8 * lg);
-        const opvec<OP> fd = fr(fDM1, (16 * u + l16) * PD + 8 * lg);
+        const opvec<OP> fm = fs(fM0, (16 * u + l16) * PD + 8 * lg);
+        const opvec<OP> fd = fs(fDM1, (16 * u + l16) * PD + 8 * lg);
         aQ[u] = mma32(fdo, fm, aQ[u]);
         aW[u] = mma32(fde, fm, aW[u]);
         aK[u] = mma32(fe, fd, aK[u]);
       }
 #pragma unroll
       for (int u = 0; u < NUC; ++u) {
-        aP[u] = mma32(fdo, fr(fE, (16 * u + l16) * PR + 8 * lg), aP[u]);
-        aT[u] = mma32(fde, fr(fV, (16 * u + l16) * PR + 8 * lg), aT[u]);
+        aP[u] = mma32(fdo, fs(fE, (16 * u + l16) * PR + 8 * lg), aP[u]);
+        aT[u] = mma32(fde, fs(fV, (16 * u + l16) * PR + 8 * lg), aT[u]);
       }
       __syncthreads();
     }
@@ -1038,6 +1085,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
       const int e = tid + NT * u;
       if (e < DK * MP && e % MP == 0) sdD[e / MP] = x;
     }
+    if constexpr (CH) load_kq();
     __syncthreads();
   } else {
   // slab loads in registers: the next slab's are issued as soon as the
@@ -1286,6 +1334,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   floatx4 oq[NU], ok[NU], og[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
+    if constexpr (CH) __builtin_amdgcn_sched_barrier(0);  // tiles one at a time (registers)
     oq[u] = ok[u] = og[u] = floatx4{0.f, 0.f, 0.f, 0.f};
     int mt, nt;
     if (!tile_cd(u, &mt, &nt)) continue;
@@ -1307,6 +1356,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   // dW into LDS (dW = -aW), dP decayed into sP (overwrites P)
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
+    if constexpr (CH) __builtin_amdgcn_sched_barrier(0);  // tiles one at a time (registers)
     int mt, nt;
     if (!tile_cd(u, &mt, &nt)) continue;
 #pragma unroll
@@ -1316,6 +1366,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   __syncthreads();  // all P reads of the slab phase are done
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
+    if constexpr (CH) __builtin_amdgcn_sched_barrier(0);  // tiles one at a time (registers)
     int mt, nt;
     if (!tile_cc(u, &mt, &nt)) continue;
 #pragma unroll
@@ -1329,6 +1380,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   floatx4 oX[NU];
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
+    if constexpr (CH) __builtin_amdgcn_sched_barrier(0);  // tiles one at a time (registers)
     int mt, nt;
     if (!tile_cc(u, &mt, &nt)) continue;
     aT[u] = tmma<OP, DK>([&](int r, int d) { return sDW[r * LDD + d]; },
@@ -1337,6 +1389,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   }
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
+    if constexpr (CH) __builtin_amdgcn_sched_barrier(0);  // tiles one at a time (registers)
     oX[u] = floatx4{0.f, 0.f, 0.f, 0.f};
     int mt, nt;
     if (!tile_cd(u, &mt, &nt)) continue;
@@ -1344,19 +1397,23 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
                         [&](int r, int d) { return sDW[r * LDD + d]; },
                         16 * mt, 16 * nt, l16, lg, oX[u]);
     // dq_P = (dP o Gamma) K  (channel: factored around the midpoint)
-    floatx4 tq = {0.f, 0.f, 0.f, 0.f};
-    tq = tmma<OP, C>([&](int r, int i) { return sP[r * LDC + i]; },
-                     [&](int i, int d) { return Kr(i, d) * dn(i, d); },
-                     16 * mt, 16 * nt, l16, lg, tq);
-    // dk_P = (dP o Gamma)^T Q
-    floatx4 tk = {0.f, 0.f, 0.f, 0.f};
-    tk = tmma<OP, C>([&](int i, int r) { return sP[r * LDC + i]; },
-                     [&](int r, int d) { return Qr(r, d) * up(r, d); },
-                     16 * mt, 16 * nt, l16, lg, tk);
+    floatx4 tq = {0.f, 0.f, 0.f, 0.f}, tk = tq;
+    if (exact) {  // channel spans beyond the factored range: per element
+      pair_decay_products(sP, LDC, Kr, Qr, sg, DK, C, mt, nt, l16, lg, &tq, &tk);
+    } else {
+      tq = tmma<OP, C>([&](int r, int i) { return sP[r * LDC + i]; },
+                       [&](int i, int d) { return Kr(i, d) * dn(i, d); },
+                       16 * mt, 16 * nt, l16, lg, tq);
+      // dk_P = (dP o Gamma)^T Q
+      tk = tmma<OP, C>([&](int i, int r) { return sP[r * LDC + i]; },
+                       [&](int r, int d) { return Qr(r, d) * up(r, d); },
+                       16 * mt, 16 * nt, l16, lg, tk);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int r = 16 * mt + 4 * lg + s, d = 16 * nt + l16;
-      const float vq = tq[s] * up(r, d), vk = tk[s] * dn(r, d);
+      const float vq = exact ? tq[s] : tq[s] * up(r, d);
+      const float vk = exact ? tk[s] : tk[s] * dn(r, d);
       oq[u][s] += vq;
       ok[u][s] += vk;
       og[u][s] += Qr(r, d) * vq - Kr(r, d) * vk;
@@ -1367,6 +1424,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   float* sDT = sP;
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
+    if constexpr (CH) __builtin_amdgcn_sched_barrier(0);  // tiles one at a time (registers)
     int mt, nt;
     if (!tile_cc(u, &mt, &nt)) continue;
 #pragma unroll
@@ -1377,6 +1435,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   float* sZ2 = sR;
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
+    if constexpr (CH) __builtin_amdgcn_sched_barrier(0);  // tiles one at a time (registers)
     int mt, nt;
     if (!tile_cc(u, &mt, &nt)) continue;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1392,6 +1451,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   float* sDA = sP;
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
+    if constexpr (CH) __builtin_amdgcn_sched_barrier(0);  // tiles one at a time (registers)
     int mt, nt;
     if (!tile_cc(u, &mt, &nt)) continue;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1403,6 +1463,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   __syncthreads();  // every read of dT is done before dA overwrites it
 #pragma unroll
   for (int u = 0; u < NUC; ++u) {
+    if constexpr (CH) __builtin_amdgcn_sched_barrier(0);  // tiles one at a time (registers)
     int mt, nt;
     if (!tile_cc(u, &mt, &nt)) continue;
     floatx4 pb;
@@ -1423,20 +1484,26 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   // dk_A1 = (b dA o Gamma) K, dk_A2 = (b dA o Gamma)^T K, and the dX terms
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
+    if constexpr (CH) __builtin_amdgcn_sched_barrier(0);  // tiles one at a time (registers)
     int mt, nt;
     if (!tile_cd(u, &mt, &nt)) continue;
     floatx4 t1 = {0.f, 0.f, 0.f, 0.f}, t2 = {0.f, 0.f, 0.f, 0.f};
-    t1 = tmma<OP, C>([&](int r, int i) { return sDA[r * LDC + i]; },
-                     [&](int i, int d) { return Kr(i, d) * dn(i, d); },
-                     16 * mt, 16 * nt, l16, lg, t1);
-    t2 = tmma<OP, C>([&](int i, int r) { return sDA[r * LDC + i]; },
-                     [&](int r, int d) { return Kr(r, d) * up(r, d); },
-                     16 * mt, 16 * nt, l16, lg, t2);
+    if (exact) {
+      pair_decay_products(sDA, LDC, Kr, Kr, sg, DK, C, mt, nt, l16, lg, &t1, &t2);
+    } else {
+      t1 = tmma<OP, C>([&](int r, int i) { return sDA[r * LDC + i]; },
+                       [&](int i, int d) { return Kr(i, d) * dn(i, d); },
+                       16 * mt, 16 * nt, l16, lg, t1);
+      t2 = tmma<OP, C>([&](int i, int r) { return sDA[r * LDC + i]; },
+                       [&](int r, int d) { return Kr(r, d) * up(r, d); },
+                       16 * mt, 16 * nt, l16, lg, t2);
+    }
     floatx4 pb;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int r = 16 * mt + 4 * lg + s, d = 16 * nt + l16;
-      const float v1 = t1[s] * up(r, d), v2 = t2[s] * dn(r, d);
+      const float v1 = exact ? t1[s] : t1[s] * up(r, d);
+      const float v2 = exact ? t2[s] : t2[s] * dn(r, d);
       const float kr = Kr(r, d), eq = gq(r, d);
       ok[u][s] += v1 + v2 + oX[u][s] * sbeta[r] * eq;
       og[u][s] += kr * (v1 - v2) + oX[u][s] * sbeta[r] * eq * kr;
@@ -1459,6 +1526,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   float* sdg = sR;  // [C][DK+1] gate gradient per (row, channel)
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
+    if constexpr (CH) __builtin_amdgcn_sched_barrier(0);  // tiles one at a time (registers)
     int mt, nt;
     if (!tile_cd(u, &mt, &nt)) continue;
 #pragma unroll
@@ -1525,8 +1593,9 @@ constexpr int kSlab = 16;  // value columns per slab of the gradient kernel
 // per-channel gate (8.4 against 8.0 ms), whose accumulators then spill.
 constexpr int kGradWaves = 4;
 
-// value columns per slab: 32 on the fast path (bf16 inputs, per-token
-// gates, 64-token chunks), kSlab otherwise
+// value columns per slab: 32 with bf16 inputs, per-token gates and 64-token
+// chunks, kSlab otherwise (bf16 with the per-channel gate and 64-token
+// chunks takes the same fast slab phase at kSlab columns)
 template <int C, typename IO, int GATE>
 constexpr int grad_slab() {
   return (io<IO>::bytes == 2 && GATE != GDN_GATE_CHANNEL && C == 64) ? 32 : kSlab;

@@ -82,7 +82,7 @@ def test_fp32_ragged(gpu_lib, C, gate):
     check(inp, "fp32_ragged")
 
 
-@pytest.mark.parametrize("dk,dv", [(64, 32), (128, 128), (128, 256)])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 48), (64, 32), (128, 128), (128, 256)])
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
 def test_bf16_shapes(gpu_lib, dk, dv, gate):
     inp = synth.make_inputs(1, 150, 2, dk, dv, dtype=torch.bfloat16, gate=gate,
@@ -187,6 +187,40 @@ def test_channel_gate_near_factored_limit(gpu_lib, side, C):
     inp.log_alpha[..., [0, 5, 77, 127]] = -side * 160.0 / (C - 1)
     inp.f64["log_alpha"] = inp.log_alpha.double().numpy()
     check(inp, f"channel_near_limit C={C} side={side}")
+
+
+@pytest.mark.parametrize("C,dtype,dk", [(16, torch.float32, 64), (32, torch.float32, 64),
+                                         (64, torch.float32, 64), (64, torch.bfloat16, 128)])
+@pytest.mark.parametrize("which", ["all", "some"])
+def test_channel_gate_exact_path(gpu_lib, C, dtype, dk, which):
+    # log alpha = -60 on every channel (erasure) or on four of them: the
+    # chunk's channel span is far beyond the factored products' range, so
+    # the per-element path runs in every product of the gradient kernel
+    inp = synth.make_inputs(1, 2 * C + 9, 2, dk, 64, dtype=dtype, gate="channel", chunk=C,
+                            seed=70 + C, s0_std=0.5, with_do=True, with_ds=True)
+    if which == "some":
+        inp.log_alpha[..., [1, 6, 30, dk - 1]] = -60.0
+        inp.f64["log_alpha"] = inp.log_alpha.double().numpy()
+        check(inp, f"channel_exact C={C} some")
+        return
+    inp.log_alpha.fill_(-60.0)
+    inp.f64["log_alpha"] = inp.log_alpha.double().numpy()
+    log(f"[bwd] channel_exact C={C} all q={tuple(inp.q.shape)} {inp.q.dtype}")
+    got, ref = run_bwd(inp), ref_bwd(inp)
+    tol = TOL[inp.q.dtype]
+    errs = {nm: slice_err(np64(x), y) for nm, x, y in
+            zip(("dq", "dk", "dv"), got[:3], ref[:3])}
+    errs["dbeta"] = slice_err(np64(got[3])[..., None], ref[3][..., None])
+    errs["ds0"] = state_err(np64(got[5]), ref[5])
+    # every decay across tokens is e^-60, so the true d log alpha is ~1e-26:
+    # its error is measured against the size of the terms whose rounding it
+    # carries, the products dq (.) q and dk (.) k of each slice
+    f = inp.f64
+    scale = max(np.abs(ref[0] * f["q"]).max(), np.abs(ref[1] * f["k"]).max())
+    errs["dlog_alpha_abs"] = float(np.abs(np64(got[4]) - ref[4]).max() / scale)
+    log("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f" tol={tol}")
+    for k, v in errs.items():
+        assert v < tol, (k, v)
 
 
 @pytest.mark.parametrize("L", [1, 3])
