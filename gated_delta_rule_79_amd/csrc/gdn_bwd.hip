@@ -123,7 +123,7 @@ template <int C, int DK, typename IO, int GATE, bool ZERO = false>
 __global__ __launch_bounds__(128) void bwd_scan_kernel(
     ChunkMap map, SegMap sm, int H, int dv, int64_t nchunks, const void* __restrict__ d_o,
     const float* __restrict__ ds_final, float* __restrict__ ds0,
-    FwdBuffers buf, float* __restrict__ dstates, const float* __restrict__ seg_in,
+    FwdBuffers buf, void* __restrict__ dstates, const float* __restrict__ seg_in,
     float* __restrict__ seg_out) {
   using OP = IO;
   using X = RevOps<C, DK, OP, GATE>;
@@ -180,12 +180,13 @@ __global__ __launch_bounds__(128) void bwd_scan_kernel(
     auto step = [&](const X& cur, X& nxt, int p) {
       if (kPrefetch && p + 1 < n) load_rev<C, DK, OP, GATE>(nxt, buf, chl - p - 1, lane, lg);
       if constexpr (!ZERO) {
-        float* st = dstates + (chl - p) * static_cast<int64_t>(DK) * dv;
+        const int64_t st = (chl - p) * static_cast<int64_t>(DK) * dv;
 #pragma unroll
         for (int a = 0; a < NDT; ++a)
 #pragma unroll
           for (int s = 0; s < 4; ++s)
-            st[static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] = dM[a][s];
+            io<IO>::store(dstates, st + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col,
+                          dM[a][s]);
       }
       opvec<OP> Mb[NKD];
 #pragma unroll
@@ -587,8 +588,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
-    const void* __restrict__ d_o, const float* __restrict__ states,
-    const float* __restrict__ dstates, void* __restrict__ dq,
+    const void* __restrict__ d_o, const void* __restrict__ states,
+    const void* __restrict__ dstates, void* __restrict__ dq,
     void* __restrict__ dk, void* __restrict__ dvv, float* __restrict__ dbeta,
     float* __restrict__ dla) {
   using OP = IO;
@@ -655,8 +656,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int64_t ch = static_cast<int64_t>(h) * nchunks + c;
-  const float* M0g = states + ch * DK * dv;
-  const float* dM1g = dstates + ch * DK * dv;
+  // chunk-start state and chunk-end state gradient, stored in the input dtype
+  const int64_t m0 = ch * DK * dv;
 
   // ---- 0. gates, beta, K and Q rows ----------------------------------------
   if (tid == 0) s_span_bits = 0;
@@ -873,7 +874,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
     constexpr int PR = S::PR, PD = S::PD, PT = S::PT, PC = S::PC;
     constexpr int NKDF = (DK + 31) / 32;
     constexpr int VP = SW / 8, NVP = (C * VP + NT - 1) / NT;   // bf16 pieces
-    constexpr int MP = SW / 4, NMP = (DK * MP + NT - 1) / NT;  // fp32 pieces
+    constexpr int MP = SW / 8, NMP = (DK * MP + NT - 1) / NT;  // state pieces
     __bf16* fV = reinterpret_cast<__bf16*>(sR);
     __bf16* fDO = fV + C * PR;
     __bf16* fE = fDO + C * PR;
@@ -905,11 +906,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
       }
 #pragma unroll
       for (int u = 0; u < NMP; ++u) {
-        const int e = tid + NT * u, d = e / MP, col = s0 + 4 * (e % MP);
+        const int e = tid + NT * u, d = e / MP, col = s0 + 8 * (e % MP);
         rm[u] = rd[u] = make_uint4(0, 0, 0, 0);
         if (e < DK * MP && col < dv) {
-          rm[u] = *reinterpret_cast<const uint4*>(M0g + static_cast<int64_t>(d) * dv + col);
-          rd[u] = *reinterpret_cast<const uint4*>(dM1g + static_cast<int64_t>(d) * dv + col);
+          const int64_t off = (m0 + static_cast<int64_t>(d) * dv + col) * 2;
+          rm[u] = *reinterpret_cast<const uint4*>(static_cast<const char*>(states) + off);
+          rd[u] = *reinterpret_cast<const uint4*>(static_cast<const char*>(dstates) + off);
         }
       }
     };
@@ -929,20 +931,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
       for (int u = 0; u < NMP; ++u) {
         const int e = tid + NT * u;
         if (e >= DK * MP) continue;
-        const int d = e / MP, j0 = 4 * (e % MP);
-        const float* m = reinterpret_cast<const float*>(&rm[u]);
-        const float* dm = reinterpret_cast<const float*>(&rd[u]);
-        bf16x4 mb, db;
+        const int d = e / MP, j0 = 8 * (e % MP);
+        const __bf16* m = reinterpret_cast<const __bf16*>(&rm[u]);
+        const __bf16* dm = reinterpret_cast<const __bf16*>(&rd[u]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          ddacc[u] += m[q] * dm[q];
-          mb[q] = static_cast<__bf16>(m[q]);
-          db[q] = static_cast<__bf16>(dm[q]);
-          fM0t[(j0 + q) * PT + d] = mb[q];
-          fDM1t[(j0 + q) * PT + d] = db[q];
+        for (int q = 0; q < 8; ++q) {
+          ddacc[u] += static_cast<float>(m[q]) * static_cast<float>(dm[q]);
+          fM0t[(j0 + q) * PT + d] = m[q];
+          fDM1t[(j0 + q) * PT + d] = dm[q];
         }
-        *reinterpret_cast<bf16x4*>(fM0 + d * PD + j0) = mb;
-        *reinterpret_cast<bf16x4*>(fDM1 + d * PD + j0) = db;
+        *reinterpret_cast<uint4*>(fM0 + d * PD + j0) = rm[u];
+        *reinterpret_cast<uint4*>(fDM1 + d * PD + j0) = rd[u];
       }
     };
     if constexpr (CH) {
@@ -1110,8 +1109,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
       const int d = e / SW, j = e % SW;
       mm[u] = dd[u] = 0.f;
       if (e < DK * SW) {
-        mm[u] = M0g[static_cast<int64_t>(d) * dv + s0 + j];
-        dd[u] = dM1g[static_cast<int64_t>(d) * dv + s0 + j];
+        mm[u] = io<IO>::load(states, m0 + static_cast<int64_t>(d) * dv + s0 + j);
+        dd[u] = io<IO>::load(dstates, m0 + static_cast<int64_t>(d) * dv + s0 + j);
       }
     }
   };
@@ -1575,15 +1574,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
 
 // ------------------------------------------------------------ dispatch ---
 
-struct BwdWs {
-  FwdBuffers buf;
-  ChunkMap map;
-  float* states;
-  float* dstates;
-};
-
+// Chunk-start states and chunk-end state gradients, one [dk][dv] matrix
+// per chunk-head in the input dtype.
 inline size_t bwd_states_bytes(const Problem& p) {
-  return FwdLayout::al(size_t(p.nchunks) * p.H * p.dk * p.dv * 4);
+  return FwdLayout::al(size_t(p.nchunks) * p.H * p.dk * p.dv * (p.io == GDN_BF16 ? 2 : 4));
 }
 
 constexpr int kSlab = 16;  // value columns per slab of the gradient kernel
@@ -1615,8 +1609,8 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
   char* map_base = ws;
   char* ops = ws + chunk_map_bytes(p);
   const FwdBuffers buf = make_buffers(ops, L);
-  float* states = reinterpret_cast<float*>(ops + size_t(p.nchunks) * p.H * L.per_ch);
-  float* dstates = reinterpret_cast<float*>(reinterpret_cast<char*>(states) + bwd_states_bytes(p));
+  char* states = ops + size_t(p.nchunks) * p.H * L.per_ch;
+  char* dstates = states + bwd_states_bytes(p);
   const ChunkMap map = make_chunk_map(p, map_base);
   const bool gbf = p.gdt == GDN_BF16;
   hipError_t e;
@@ -1632,8 +1626,7 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
   const bool rseg = p.seg > 0 && static_cast<int64_t>(p.nseq) * p.H * (p.dv / 16) < kRevSplitBelow;
   const SegMap rsm = rseg ? sm : make_seg_map(p, map_base, 0);
   const int64_t nwork = (rseg ? p.nsegs : p.nseq) * p.H * (p.dv / 16);
-  const SegBuffers sb = make_seg_buffers(
-      p, reinterpret_cast<char*>(dstates) + bwd_states_bytes(p), opstore<IO>::bytes);
+  const SegBuffers sb = make_seg_buffers(p, dstates + bwd_states_bytes(p), opstore<IO>::bytes);
   if (p.nchunks > 0) {
     {
       StageScope scope(GDN_STAGE_FWD_PREP, s);

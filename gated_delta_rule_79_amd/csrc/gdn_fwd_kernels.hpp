@@ -1838,14 +1838,16 @@ __device__ __forceinline__ opvec<OP> q_frag_raw(const char* sq, int rt, int jb, 
 // so that the wait for the next chunk's copies never waits on them.
 //
 // STATES = true (backward recomputation): no outputs; every chunk-start
-// state is stored in fp32 into `states` ([chunk-head][DK][dv]).
+// state is stored into `states` ([chunk-head][DK][dv]) in the input dtype
+// (the chain itself stays fp32; the gradient kernel multiplies the stored
+// states on the matrix cores in that dtype).
 template <int C, int DK, typename IO, int GATE, bool STATES = false>
 __global__ __launch_bounds__(64 * kScanWaves)
 void fwd_scan_kernel(
     ChunkMap map, SegMap sm, int H, int dv, int64_t nchunks,
     const void* __restrict__ q, const float* __restrict__ s0,
     void* __restrict__ o, float* __restrict__ s_final, FwdBuffers buf,
-    SegBuffers sb, float* __restrict__ states, int lnh) {
+    SegBuffers sb, void* __restrict__ states, int lnh) {
   using OP = IO;
   constexpr bool OUT = !STATES;
   constexpr bool RAWQ = OUT && GATE != GDN_GATE_CHANNEL;
@@ -1945,7 +1947,7 @@ void fwd_scan_kernel(
   };
   auto step = [&](const char* ops, int j) {
     if constexpr (STATES) {
-      float* stp = states + (ch0 + j) * static_cast<int64_t>(DK) * dv;
+      const int64_t st0 = (ch0 + j) * static_cast<int64_t>(DK) * dv;
 #pragma unroll
       for (int s = 0; s < SPW; ++s) {
         if (!own[s]) continue;
@@ -1954,7 +1956,8 @@ void fwd_scan_kernel(
         for (int a = 0; a < NDT; ++a)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            stp[static_cast<int64_t>(16 * a + 4 * lg + e) * dv + col] = M[s][a][e];
+            io<IO>::store(states, st0 + static_cast<int64_t>(16 * a + 4 * lg + e) * dv + col,
+                          M[s][a][e]);
       }
     }
     opvec<OP> Mb[SPW][NKD], Eb[SPW][NKC];
