@@ -323,6 +323,226 @@ __global__ __launch_bounds__(128) void bwd_scan_kernel(
   }
 }
 
+// Reverse state pass for bf16 operands with the chunk operands shared in
+// LDS: one workgroup per (segment, head, group of kRevSlabs 16-column slabs),
+// one wave per slab.  The per-chunk operands (decays, K~, -W^T, P^T, Q~^T:
+// one contiguous stretch of the chunk's workspace) are copied once per
+// workgroup straight into LDS, double-buffered, together with the group's
+// dO columns, instead of once per slab.  Each wave forms its slab's
+// chain-free terms R = P^T dO and G = Q~^T dO from LDS in the same step as
+// the chain, so no helper wave is needed.  Modes as bwd_scan_kernel.
+constexpr int kRevSlabs = 4;
+
+template <int C, int DK>
+struct RevLds {
+  static constexpr int NB = C / 16, NKD = (DK + 31) / 32, NKC = (C + 31) / 32, NDT = DK / 16;
+  static constexpr size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+  // the workspace's [g | K~ | -W^T | P^T | Q~^T] stretch (bf16 fragments)
+  static constexpr size_t oG = 0;
+  static constexpr size_t oKF = al(size_t(C + DK) * 4);
+  static constexpr size_t oWT = oKF + al(size_t(NB) * NKD * 1024);
+  static constexpr size_t oPT = oWT + al(size_t(NDT) * NKC * 1024);
+  static constexpr size_t oQT = oPT + al(size_t(NB) * NKC * 1024);
+  static constexpr size_t REG = oQT + al(size_t(NDT) * NKC * 1024);
+  // dO rows of the group's columns, [C][16 kRevSlabs] bf16
+  static constexpr int DOP = 2 * kRevSlabs;  // 16-byte pieces per row
+  static constexpr size_t oDO = REG;
+  static constexpr size_t STAGE = oDO + size_t(C) * DOP * 16;
+  static constexpr size_t total = 2 * STAGE;
+  static_assert(REG % 16 == 0 && STAGE % 16 == 0, "16-byte pieces");
+};
+
+template <int C, int DK, int GATE, bool ZERO = false>
+__global__ __launch_bounds__(64 * kRevSlabs) void bwd_scan_lds_kernel(
+    ChunkMap map, SegMap sm, int H, int dv, int64_t nchunks, const void* __restrict__ d_o,
+    const float* __restrict__ ds_final, float* __restrict__ ds0,
+    FwdBuffers buf, void* __restrict__ dstates, const float* __restrict__ seg_in,
+    float* __restrict__ seg_out) {
+  using OP = bf16_t;
+  using L = RevLds<C, DK>;
+  constexpr int NB = L::NB, NKD = L::NKD, NKC = L::NKC, NDT = L::NDT;
+  constexpr int NT = 64 * kRevSlabs;
+  constexpr bool CH = GATE == GDN_GATE_CHANNEL;
+  constexpr int NDO = (C * L::DOP + NT - 1) / NT;  // dO pieces per thread
+  __shared__ __attribute__((aligned(16))) char smem[L::total];
+
+  const int w = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int ndvt = dv / 16;
+  const int ngrp = (ndvt + kRevSlabs - 1) / kRevSlabs;
+  const int grp = w % ngrp;
+  const int chain = w / ngrp;
+  const int h = chain % H;
+  const int slot = chain / H;
+  const SegInfo si = seg_info(sm, map, slot);
+  if (si.seq < 0 || (ZERO && si.j == 0)) return;  // whole workgroup, before any barrier
+  const int seq = si.seq;
+  const int tid = threadIdx.x;
+  // wave index in a scalar register: branches on it are scalar branches,
+  // never EXEC masks (matrix instructions ignore EXEC)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int vt = grp * kRevSlabs + wave;
+  const bool active = vt < ndvt;  // wave-uniform
+  const int col = 16 * vt + l16;
+  const int c0 = 16 * grp * kRevSlabs;  // first column of the group
+  const int64_t sbase = (static_cast<int64_t>(seq) * H + h) * DK * dv;
+  const size_t sl = (static_cast<size_t>(slot) * H + h) * ndvt + vt;
+  const int ce = si.c1;
+  const int n = si.c1 - si.c0;
+  const int64_t chl = static_cast<int64_t>(h) * nchunks + ce - 1;  // step 0
+
+  floatx4 dM[NDT];
+#pragma unroll
+  for (int a = 0; a < NDT; ++a) dM[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (active && !ZERO) {
+    if (si.last) {
+      if (ds_final) {
+#pragma unroll
+        for (int a = 0; a < NDT; ++a)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            dM[a][s] = ds_final[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col];
+      }
+    } else {
+      const floatx4* src = reinterpret_cast<const floatx4*>(seg_in) + sl * NDT * 64;
+#pragma unroll
+      for (int a = 0; a < NDT; ++a) dM[a] = src[a * 64 + lane];
+    }
+  }
+
+  // operands of step j into stage buffer `lds`; the dO pieces travel in
+  // registers and are written after the current step (rows past the chunk
+  // and columns past dv are zero)
+  uint4 dop[NDO];
+  auto copy = [&](char* lds, int j) {
+    lds_copy<NT, L::REG>(lds, buf.at(chl - j, buf.off_g), wave, lane);
+    const ChunkInfo ci = chunk_info(map, ce - 1 - j);
+#pragma unroll
+    for (int u = 0; u < NDO; ++u) {
+      const int e = tid + NT * u, r = e / L::DOP, pc = e % L::DOP;
+      dop[u] = make_uint4(0, 0, 0, 0);
+      if (e < C * L::DOP && r < ci.len && c0 + 8 * pc < dv)
+        dop[u] = *reinterpret_cast<const uint4*>(
+            static_cast<const char*>(d_o) + (((ci.tok0 + r) * H + h) * dv + c0 + 8 * pc) * 2);
+    }
+  };
+  auto put_do = [&](char* lds) {
+#pragma unroll
+    for (int u = 0; u < NDO; ++u) {
+      const int e = tid + NT * u;
+      if (e < C * L::DOP) *reinterpret_cast<uint4*>(lds + L::oDO + size_t(e) * 16) = dop[u];
+    }
+  };
+  auto lfrag = [&](const char* lds, size_t off, int f) {
+    return *reinterpret_cast<const opvec<OP>*>(lds + off + (size_t(f) * 64 + lane) * 16);
+  };
+
+  auto step = [&](const char* lds, int j) {
+    if (!active) return;
+    // chain-free terms of this chunk: R = P^T dO, G = Q~^T dO
+    opvec<OP> Df[NKC];
+#pragma unroll
+    for (int jb = 0; jb < NKC; ++jb) {
+      float x[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int r = 32 * jb + perm_k(lg, s);
+        x[s] = r < C ? static_cast<float>(reinterpret_cast<const __bf16*>(lds + L::oDO)[
+                           r * 16 * kRevSlabs + 16 * wave + l16])
+                     : 0.f;
+      }
+      Df[jb] = frag<OP>::from_floats(x);
+    }
+    floatx4 dE[NB], Gm[NDT];
+#pragma unroll
+    for (int it = 0; it < NB; ++it) {
+      dE[it] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jb = 0; jb < NKC; ++jb)
+        if (32 * jb + 31 >= 16 * it) dE[it] = mma32(lfrag(lds, L::oPT, it * NKC + jb), Df[jb], dE[it]);
+    }
+#pragma unroll
+    for (int a = 0; a < NDT; ++a) {
+      Gm[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jb = 0; jb < NKC; ++jb) Gm[a] = mma32(lfrag(lds, L::oQT, a * NKC + jb), Df[jb], Gm[a]);
+    }
+    // the gradient at the chunk end
+    if constexpr (!ZERO) {
+      const int64_t st = (chl - j) * static_cast<int64_t>(DK) * dv;
+#pragma unroll
+      for (int a = 0; a < NDT; ++a)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          io<OP>::store(dstates, st + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col,
+                        dM[a][s]);
+    }
+    // dE = R + K~ dM1;  dM0 = D dM1 + G - W^T dE
+    opvec<OP> Mb[NKD];
+#pragma unroll
+    for (int jb = 0; jb < NKD; ++jb) {
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      Mb[jb] = pack2<OP>(dM[2 * jb], 2 * jb + 1 < NDT ? dM[2 * jb + 1] : z);
+    }
+#pragma unroll
+    for (int it = 0; it < NB; ++it)
+#pragma unroll
+      for (int jb = 0; jb < NKD; ++jb) dE[it] = mma32(lfrag(lds, L::oKF, it * NKD + jb), Mb[jb], dE[it]);
+    opvec<OP> Eb[NKC];
+#pragma unroll
+    for (int jb = 0; jb < NKC; ++jb) {
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      Eb[jb] = pack2<OP>(dE[2 * jb], 2 * jb + 1 < NB ? dE[2 * jb + 1] : z);
+    }
+    const float* gam = reinterpret_cast<const float*>(lds + L::oG) + C;
+#pragma unroll
+    for (int a = 0; a < NDT; ++a) {
+      floatx4 gc;
+      if constexpr (CH) gc = *reinterpret_cast<const floatx4*>(gam + 16 * a + 4 * lg);
+      else if constexpr (GATE == GDN_GATE_SCALAR) gc = floatx4{gam[0], gam[0], gam[0], gam[0]};
+      else gc = floatx4{1.f, 1.f, 1.f, 1.f};
+      dM[a] = dM[a] * gc + Gm[a];
+#pragma unroll
+      for (int jb = 0; jb < NKC; ++jb) dM[a] = mma32(lfrag(lds, L::oWT, a * NKC + jb), Eb[jb], dM[a]);
+    }
+  };
+
+  char* sA = smem;
+  char* sB = smem + L::STAGE;
+  if (n > 0) {
+    copy(sA, 0);
+    put_do(sA);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int j = 0; j < n; j += 2) {
+    if (j + 1 < n) copy(sB, j + 1);
+    step(sA, j);
+    if (j + 1 < n) put_do(sB);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (j + 1 < n) {
+      if (j + 2 < n) copy(sA, j + 2);
+      step(sB, j + 1);
+      if (j + 2 < n) put_do(sA);
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+  }
+  if (!active) return;
+  if (ZERO) {
+    floatx4* dst = reinterpret_cast<floatx4*>(seg_out) + sl * NDT * 64;
+#pragma unroll
+    for (int a = 0; a < NDT; ++a) dst[a * 64 + lane] = dM[a];
+  } else if (ds0 && si.j == 0) {
+#pragma unroll
+    for (int a = 0; a < NDT; ++a)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        ds0[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] = dM[a][s];
+  }
+}
+
 // Reverse chain over the segments of one (sequence, head, 16-column slab):
 // the gradient entering segment j from the right is g_j (g_last = dS_final),
 // and g_{j-1} = Phi_j^T g_j + b_j with b_j the segment's ZERO-mode result.
@@ -1673,11 +1893,24 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
     // through the transposed transitions (into the entering-state buffer),
     // then every segment from its entering gradient
     StageScope scope(GDN_STAGE_BWD_SCAN, s);
+    // bf16: the LDS-shared pass, kRevSlabs slabs per workgroup
+    constexpr bool kLds = io<IO>::bytes == 2;
+    const int64_t chains = (rseg ? p.nsegs : p.nseq) * p.H;
+    const int64_t nlds = chains * ((p.dv / 16 + kRevSlabs - 1) / kRevSlabs);
+    if constexpr (kLds) {
+      if (RevLds<C, DK>::REG != L.g + L.kf + L.wt + L.pt + L.qt) return hipErrorInvalidValue;
+    }
     if (rseg && p.nchunks > 0) {
-      hipLaunchKernelGGL((bwd_scan_kernel<C, DK, IO, GATE, true>),
-                         dim3(static_cast<unsigned>(nwork)), dim3(128), 0, s, map, rsm,
-                         p.H, p.dv, p.nchunks, d_o, ds_final, ds0, buf, dstates,
-                         static_cast<const float*>(nullptr), sb.trm);
+      if constexpr (kLds)
+        hipLaunchKernelGGL((bwd_scan_lds_kernel<C, DK, GATE, true>),
+                           dim3(static_cast<unsigned>(nlds)), dim3(64 * kRevSlabs), 0, s, map,
+                           rsm, p.H, p.dv, p.nchunks, d_o, ds_final, ds0, buf, dstates,
+                           static_cast<const float*>(nullptr), sb.trm);
+      else
+        hipLaunchKernelGGL((bwd_scan_kernel<C, DK, IO, GATE, true>),
+                           dim3(static_cast<unsigned>(nwork)), dim3(128), 0, s, map, rsm,
+                           p.H, p.dv, p.nchunks, d_o, ds_final, ds0, buf, dstates,
+                           static_cast<const float*>(nullptr), sb.trm);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((bwd_combine_kernel<DK, IO>),
@@ -1687,10 +1920,16 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_scan_kernel<C, DK, IO, GATE>),
-                       dim3(static_cast<unsigned>(nwork)), dim3(128), 0, s, map, rsm,
-                       p.H, p.dv, p.nchunks, d_o, ds_final, ds0, buf, dstates,
-                       static_cast<const float*>(sb.ss), static_cast<float*>(nullptr));
+    if constexpr (kLds)
+      hipLaunchKernelGGL((bwd_scan_lds_kernel<C, DK, GATE>),
+                         dim3(static_cast<unsigned>(nlds)), dim3(64 * kRevSlabs), 0, s, map, rsm,
+                         p.H, p.dv, p.nchunks, d_o, ds_final, ds0, buf, dstates,
+                         static_cast<const float*>(sb.ss), static_cast<float*>(nullptr));
+    else
+      hipLaunchKernelGGL((bwd_scan_kernel<C, DK, IO, GATE>),
+                         dim3(static_cast<unsigned>(nwork)), dim3(128), 0, s, map, rsm,
+                         p.H, p.dv, p.nchunks, d_o, ds_final, ds0, buf, dstates,
+                         static_cast<const float*>(sb.ss), static_cast<float*>(nullptr));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
