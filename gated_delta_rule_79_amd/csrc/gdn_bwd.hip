@@ -18,8 +18,9 @@
 //   is d log alpha (the chunk-end decay D feeds the chunk's last row).
 //
 // Kernels, all on the caller's stream:
-//   1. prep (the forward prep with BWD = true): the forward operands plus the
-//      reverse recurrence's fragments K~, -W^T, P^T, Q~^T.
+//   1. prep (a forward prep with BWD = true; the per-token gates take the
+//      scalar-gate prep): the forward operands plus the reverse recurrence's
+//      fragments K~, -W^T, P^T, Q~^T.
 //   2. forward state pass in STATES mode: the state at every chunk start.
 //   3. reverse state pass (bwd_scan_kernel): dM across chunks, one workgroup
 //      per (sequence, head, 16-column slab of dv); stores dM at every chunk
@@ -1850,9 +1851,16 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
   if (p.nchunks > 0) {
     {
       StageScope scope(GDN_STAGE_FWD_PREP, s);
-      hipLaunchKernelGGL((fwd_prep_kernel<C, DK, IO, GATE, true>),
-                         dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(256), 0, s,
-                         map, p.H, p.dv, p.nchunks, q, k, v, beta, la, gbf, buf, nullptr);
+      if constexpr (GATE == GDN_GATE_CHANNEL)
+        hipLaunchKernelGGL((fwd_prep_kernel<C, DK, IO, GATE, true>),
+                           dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(256), 0, s,
+                           map, p.H, p.dv, p.nchunks, q, k, v, beta, la, gbf, buf, nullptr);
+      else
+        hipLaunchKernelGGL((fwd_prep_sg_kernel<C, DK, IO, GATE, true>),
+                           dim3(static_cast<unsigned>(p.nchunks * p.H)),
+                           dim3(64 * prep_waves(C)), 0, s, map, p.H, p.dv, p.nchunks, q, k, v,
+                           beta, la, gbf, buf, 0, false, static_cast<const int32_t*>(nullptr),
+                           static_cast<const void*>(nullptr));
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -980,7 +980,10 @@ struct PrepSgSmem {
 // T = (I + A)^-1 only ever chains ancestors.  The state carried past the
 // chunk is not meaningful for a tree: its decays are set to zero.  Parent
 // entries outside [-1, r) are read as -1.
-template <int C, int DK, typename IO, int GATE>
+//
+// BWD (backward recomputation): also the reverse recurrence's operands, the
+// K~ rows, -W^T, P^T and Q~^T fragments (the layouts of the general prep).
+template <int C, int DK, typename IO, int GATE, bool BWD = false>
 __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v,
@@ -1251,7 +1254,7 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int it = 2 * jb + half;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f}, acct = acc;
         const floatx4 gi4 = it < NB ? *reinterpret_cast<const floatx4*>(sg2 + 16 * it + 4 * lg)
                                     : floatx4{0.f, 0.f, 0.f, 0.f};
         if (it <= rt && it < NB) {
@@ -1262,6 +1265,30 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
             opvec<OP> kf = zero_vec<OP>();
             if (k0 < DK) kf = *reinterpret_cast<const opvec<OP>*>(sK + ri * LDKB + k0 * ib);
             acc = mma32(kf, qpre[u][kb], acc);
+            if constexpr (BWD) acct = mma32(qpre[u][kb], kf, acct);
+          }
+        }
+        if constexpr (BWD) {
+          // P^T fragment (it, rt / 2): row i = 16 it + l16, slots 4 (rt & 1)
+          // .. + 3 are the rows r = 16 rt + 4 lg + e (zero above the
+          // diagonal); with an odd tile count the missing half is zero
+          if (it < NB) {
+            const int i = 16 * it + l16;
+            const float gi = sg2[i];
+            const floatx4 gr4 = *reinterpret_cast<const floatx4*>(sg2 + 16 * rt + 4 * lg);
+            floatx4 pt;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int rr = 16 * rt + 4 * lg + e;
+              float val = acct[e];
+              if constexpr (GATE == GDN_GATE_SCALAR) val *= __builtin_amdgcn_exp2f(gr4[e] - gi);
+              pt[e] = (it <= rt && i <= rr) ? val : 0.f;
+            }
+            char* dst = buf.at(ch, buf.off_pt) + ((size_t(it) * NKC + (rt >> 1)) * 64 + lane) * 8 * ob;
+            *reinterpret_cast<typename acc4<OP>::type*>(dst + (rt & 1) * 4 * ob) = from_f4<OP>(pt);
+            if ((NB & 1) && rt == NB - 1)
+              *reinterpret_cast<typename acc4<OP>::type*>(dst + 4 * ob) =
+                  from_f4<OP>(floatx4{0.f, 0.f, 0.f, 0.f});
           }
         }
 #pragma unroll
@@ -1381,18 +1408,47 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
     }
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f}, acct = acc;
       if (16 * a < DK) {
 #pragma unroll
         for (int kb = 0; kb < NKC; ++kb) {
           if (32 * kb > 16 * rt + 15) continue;
           acc = mma32(xf[kb], tf[rt][kb], acc);
+          if constexpr (BWD) acct = mma32(tf[rt][kb], xf[kb], acct);
         }
       }
       // slots 4 half .. +3 of the lane's fragment (zero past DK)
       *reinterpret_cast<typename acc4<OP>::type*>(
           buf.at(ch, buf.off_w) + ((size_t(rt) * NKD + jb) * 64 + lane) * 8 * ob + half * 4 * ob) =
           from_f4<OP>(-acc);
+      if constexpr (BWD) {
+        // -W^T fragment (a, rt / 2): row dk = 16 a + l16, slots 4 (rt & 1)
+        // .. + 3 are the tokens 16 rt + 4 lg + e
+        if (16 * a < DK) {
+          char* dst = buf.at(ch, buf.off_wt) + ((size_t(a) * NKC + (rt >> 1)) * 64 + lane) * 8 * ob;
+          *reinterpret_cast<typename acc4<OP>::type*>(dst + (rt & 1) * 4 * ob) = from_f4<OP>(-acct);
+          if ((NB & 1) && rt == NB - 1)
+            *reinterpret_cast<typename acc4<OP>::type*>(dst + 4 * ob) =
+                from_f4<OP>(floatx4{0.f, 0.f, 0.f, 0.f});
+        }
+      }
+    }
+  }
+  if constexpr (BWD) {
+    // K~ fragments: rows i, slots dk = 32 jb + perm_k (zero past DK)
+    char* dkf = buf.at(ch, buf.off_kf);
+    for (int e = tid; e < NB * NKD * 64; e += NT) {
+      const int ln = e & 63, fr = e >> 6;
+      const int rt = fr / NKD, jb = fr % NKD;
+      const int i = 16 * rt + (ln & 15), g = ln >> 4;
+      float vals[8];
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const int d = 32 * jb + perm_k(g, s2);
+        vals[s2] = d < DK ? lds_ld<IO>(sK + i * LDKB, d) * sks[i] : 0.f;
+      }
+      *reinterpret_cast<opvec<OP>*>(dkf + (size_t(fr) * 64 + ln) * 8 * ob) =
+          frag<OP>::from_floats(vals);
     }
   }
 
@@ -1433,6 +1489,42 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
         *reinterpret_cast<typename acc4<OP>::type*>(
             U + ((size_t(rt) * ndvt + vt) * 64 + lane) * 4 * ob) = from_f4<OP>(acc);
       }
+    }
+  }
+
+  if constexpr (BWD) {
+    // ---- 7. Q~^T fragments (rows dk, slots tokens 32 jb + perm_k): the q
+    //      rows go through the V staging area (zero past the chunk)
+    constexpr int LDQB = DK * ib + 16;
+    static_assert(LDQB <= LDVB, "q rows fit the V staging rows");
+    __syncthreads();  // every wave is done with V
+    for (int e = tid; e < C * KP; e += NT) {
+      const int r = e / KP, pc = e % KP;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (r < len)
+        x = *reinterpret_cast<const uint4*>(
+            static_cast<const char*>(q) + ((tok0 + r) * H + h) * DK * ib + pc * 16);
+      *reinterpret_cast<uint4*>(sV + r * LDQB + pc * 16) = x;
+    }
+    __syncthreads();
+    char* dqt = buf.at(ch, buf.off_qt);
+    for (int e = tid; e < NDT * NKC * 64; e += NT) {
+      const int ln = e & 63, fr = e >> 6;
+      const int a = fr / NKC, jb = fr % NKC;
+      const int d = 16 * a + (ln & 15), g = ln >> 4;
+      float vals[8];
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const int r = 32 * jb + perm_k(g, s2);
+        float x = 0.f;
+        if (r < C) {
+          x = lds_ld<IO>(sV + r * LDQB, d);
+          if constexpr (GATE == GDN_GATE_SCALAR) x *= __builtin_amdgcn_exp2f(sg2[r]);
+        }
+        vals[s2] = x;
+      }
+      *reinterpret_cast<opvec<OP>*>(dqt + (size_t(fr) * 64 + ln) * 8 * ob) =
+          frag<OP>::from_floats(vals);
     }
   }
 }
