@@ -876,6 +876,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   // never EXEC masks (matrix instructions ignore EXEC)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  // fast slab phase: the wave's row tile and, with two waves per row tile,
+  // its half of the column / key / chunk tiles (constants with one wave)
+  constexpr int HWG = S::FAST ? NW / NB : 1;
+  const int frt = HWG == 1 ? wave : wave % NB;
+  const int fhw = HWG == 1 ? 0 : wave / NB;
   const int64_t ch = static_cast<int64_t>(h) * nchunks + c;
   // chunk-start state and chunk-end state gradient, stored in the input dtype
   const int64_t m0 = ch * DK * dv;
@@ -1091,7 +1096,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
     // + diag(e^{g_C - g}) K dM1, B: E = T Z and dY = T^T dE (dv, dbeta),
     // C: the contractions over the slab's columns.  All operands are read as
     // 16-byte fragments except T, T^T and P^T, built from the fp32 matrices.
-    static_assert(NB == NW, "one row tile per wave");
+    // NW = NB: wave w owns row tile w of every product; NW = 2 NB: two
+    // waves share a row tile and split its column tiles (phases A, B), its
+    // key tiles and chunk tiles (phase C)
+    static_assert(NW == NB || NW == 2 * NB, "one or two waves per row tile");
     constexpr int PR = S::PR, PD = S::PD, PT = S::PT, PC = S::PC;
     constexpr int NKDF = (DK + 31) / 32;
     constexpr int VP = SW / 8, NVP = (C * VP + NT - 1) / NT;   // bf16 pieces
@@ -1177,7 +1185,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
       }
       __syncthreads();
     }
-    const int r0 = 16 * wave;
+    constexpr int HW = NW / NB;
+    const int r0 = 16 * frt, hw = fhw;
     floatx4 dbacc = {0.f, 0.f, 0.f, 0.f};
     // the per-channel gate's registers do not leave room for the next
     // slab's loads in flight: it loads each slab just before staging it
@@ -1199,7 +1208,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
         pt[kb] = frag<OP>::from_floats(a);
       }
 #pragma unroll
-      for (int nt = 0; nt < SW / 16; ++nt) {
+      for (int nt = hw; nt < SW / 16; nt += HW) {
         const int j = 16 * nt + l16;
         floatx4 xm = {0.f, 0.f, 0.f, 0.f}, a1 = xm, a2 = xm;
 #pragma unroll
@@ -1243,7 +1252,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
         ttf[kb] = frag<OP>::from_floats(b);
       }
 #pragma unroll
-      for (int nt = 0; nt < SW / 16; ++nt) {
+      for (int nt = hw; nt < SW / 16; nt += HW) {
         const int j = 16 * nt + l16;
         floatx4 ee = {0.f, 0.f, 0.f, 0.f}, yy = ee;
 #pragma unroll
@@ -1264,7 +1273,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
       }
       __syncthreads();
       // C. contractions over the slab's columns (one K block of 32; a
-      // 16-column slab fills K groups 0 and 1, the others carry zeros)
+      // 16-column slab fills K groups 0 and 1, the others carry zeros);
+      // this wave's key tiles hw NU .. and chunk tiles hw NUC ..
       const bool kin = 8 * lg < SW;
       auto fs = [&](const __bf16* base, int idx) { return kin ? fr(base, idx) : zero_vec<OP>(); };
       const opvec<OP> fdo = fs(fDO, (r0 + l16) * PR + 8 * lg);
@@ -1272,29 +1282,39 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
       const opvec<OP> fe = fs(fE, (r0 + l16) * PR + 8 * lg);
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const opvec<OP> fm = fs(fM0, (16 * u + l16) * PD + 8 * lg);
-        const opvec<OP> fd = fs(fDM1, (16 * u + l16) * PD + 8 * lg);
+        const int kt = hw * NU + u;
+        const opvec<OP> fm = fs(fM0, (16 * kt + l16) * PD + 8 * lg);
+        const opvec<OP> fd = fs(fDM1, (16 * kt + l16) * PD + 8 * lg);
         aQ[u] = mma32(fdo, fm, aQ[u]);
         aW[u] = mma32(fde, fm, aW[u]);
         aK[u] = mma32(fe, fd, aK[u]);
       }
 #pragma unroll
       for (int u = 0; u < NUC; ++u) {
-        aP[u] = mma32(fdo, fs(fE, (16 * u + l16) * PR + 8 * lg), aP[u]);
-        aT[u] = mma32(fde, fs(fV, (16 * u + l16) * PR + 8 * lg), aT[u]);
+        const int ct = hw * NUC + u;
+        aP[u] = mma32(fdo, fs(fE, (16 * ct + l16) * PR + 8 * lg), aP[u]);
+        aT[u] = mma32(fde, fs(fV, (16 * ct + l16) * PR + 8 * lg), aT[u]);
       }
       __syncthreads();
     }
     // Y = diag(b) V: the scale of aT's columns
 #pragma unroll
     for (int u = 0; u < NUC; ++u) {
-      const float bi = sbeta[16 * u + l16];
+      const float bi = sbeta[16 * (hw * NUC + u) + l16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) aT[u][q] *= bi;
     }
-    if (l16 == 0) {
+    // dbeta's slab part: the column halves' row sums, added in a fixed order
+    if (l16 == 0 && hw == HW - 1) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) sdb[r0 + 4 * lg + q] = dbacc[q];
+    }
+    if constexpr (HW == 2) {
+      __syncthreads();
+      if (l16 == 0 && hw == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sdb[r0 + 4 * lg + q] = dbacc[q] + sdb[r0 + 4 * lg + q];
+      }
     }
     // sum_j M0 (.) dM1 per key row: the MP lanes of a row are adjacent
 #pragma unroll
@@ -1527,8 +1547,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   // slab phase gives wave w row tile w, the others deal tiles round robin
   auto tile_cd = [&](int u, int* mt, int* nt) -> bool {
     if constexpr (S::FAST) {
-      *mt = wave;
-      *nt = u;
+      *mt = frt;
+      *nt = fhw * NU + u;
       return true;
     } else {
       const int t = wave + NW * u;
@@ -1539,8 +1559,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(
   };
   auto tile_cc = [&](int u, int* mt, int* nt) -> bool {
     if constexpr (S::FAST) {
-      *mt = wave;
-      *nt = u;
+      *mt = frt;
+      *nt = fhw * NUC + u;
       return true;
     } else {
       const int t = wave + NW * u;
@@ -1808,12 +1828,23 @@ constexpr int kSlab = 16;  // value columns per slab of the gradient kernel
 // per-channel gate (8.4 against 8.0 ms), whose accumulators then spill.
 constexpr int kGradWaves = 4;
 
+// waves of the gradient kernel: 8 on the fast slab phase with per-token
+// gates and dk >= 32 (two waves per row tile), kGradWaves otherwise
+template <int C, int DK, typename IO, int GATE>
+constexpr int grad_waves();
+
 // value columns per slab: 32 with bf16 inputs, per-token gates and 64-token
 // chunks, kSlab otherwise (bf16 with the per-channel gate and 64-token
 // chunks takes the same fast slab phase at kSlab columns)
 template <int C, typename IO, int GATE>
 constexpr int grad_slab() {
   return (io<IO>::bytes == 2 && GATE != GDN_GATE_CHANNEL && C == 64) ? 32 : kSlab;
+}
+
+template <int C, int DK, typename IO, int GATE>
+constexpr int grad_waves() {
+  return (GradSmem<C, DK, IO, GATE, grad_slab<C, IO, GATE>()>::FAST &&
+          GATE != GDN_GATE_CHANNEL && DK >= 32) ? 8 : kGradWaves;
 }
 
 template <int C, int DK, typename IO, int GATE>
@@ -1943,8 +1974,9 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
   }
   if (p.nchunks > 0) {
     StageScope scope(GDN_STAGE_BWD_GRAD, s);
-    hipLaunchKernelGGL((bwd_grad_kernel<C, DK, IO, GATE, SW, kGradWaves>),
-                       dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(64 * kGradWaves), 0, s,
+    constexpr int NW = grad_waves<C, DK, IO, GATE>();
+    hipLaunchKernelGGL((bwd_grad_kernel<C, DK, IO, GATE, SW, NW>),
+                       dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(64 * NW), 0, s,
                        map, p.H, p.dv, p.nchunks, q, k, v, beta, la, gbf, d_o,
                        states, dstates, dq, dk, dv, dbeta, dla);
     e = hipGetLastError();
