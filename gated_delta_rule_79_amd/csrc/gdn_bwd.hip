@@ -1828,8 +1828,8 @@ constexpr int kSlab = 16;  // value columns per slab of the gradient kernel
 // per-channel gate (8.4 against 8.0 ms), whose accumulators then spill.
 constexpr int kGradWaves = 4;
 
-// waves of the gradient kernel: 8 on the fast slab phase with per-token
-// gates and dk >= 32 (two waves per row tile), kGradWaves otherwise
+// waves of the gradient kernel: 8 on the fast slab phase with dk >= 32 (two
+// waves per row tile), kGradWaves otherwise
 template <int C, int DK, typename IO, int GATE>
 constexpr int grad_waves();
 
@@ -1844,7 +1844,7 @@ constexpr int grad_slab() {
 template <int C, int DK, typename IO, int GATE>
 constexpr int grad_waves() {
   return (GradSmem<C, DK, IO, GATE, grad_slab<C, IO, GATE>()>::FAST &&
-          GATE != GDN_GATE_CHANNEL && DK >= 32) ? 8 : kGradWaves;
+          DK >= 32) ? 8 : kGradWaves;
 }
 
 template <int C, int DK, typename IO, int GATE>
