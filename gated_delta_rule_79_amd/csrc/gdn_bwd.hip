@@ -1883,8 +1883,8 @@ hipError_t run_bwd(const Problem& p, const void* q, const void* k,
     {
       StageScope scope(GDN_STAGE_FWD_PREP, s);
       if constexpr (GATE == GDN_GATE_CHANNEL)
-        hipLaunchKernelGGL((fwd_prep_kernel<C, DK, IO, GATE, true>),
-                           dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(256), 0, s,
+        hipLaunchKernelGGL((fwd_prep_kernel<C, DK, IO, GATE, true, kPrepChWaves>),
+                           dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(64 * kPrepChWaves), 0, s,
                            map, p.H, p.dv, p.nchunks, q, k, v, beta, la, gbf, buf, nullptr);
       else
         hipLaunchKernelGGL((fwd_prep_sg_kernel<C, DK, IO, GATE, true>),

@@ -163,8 +163,8 @@ hipError_t run_fwd(const Problem& p, const void* q, const void* k,
   if (p.nchunks > 0) {
     StageScope scope(GDN_STAGE_FWD_PREP, s);
     if constexpr (GATE == GDN_GATE_CHANNEL)
-      hipLaunchKernelGGL((fwd_prep_kernel<C, DK, IO, GATE>),
-                         dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(256),
+      hipLaunchKernelGGL((fwd_prep_kernel<C, DK, IO, GATE, false, kPrepChWaves>),
+                         dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(64 * kPrepChWaves),
                          0, s, map, p.H, p.dv, p.nchunks, q, k, v, beta, la,
                          p.gdt == GDN_BF16, buf, p.beta_w);
     else

@@ -190,8 +190,12 @@ __device__ inline float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
-template <int C, int DK, typename IO, int GATE, bool BWD = false>
-__global__ __launch_bounds__(256) void fwd_prep_kernel(
+// Waves of the per-channel prep: its LDS plan allows one workgroup per CU,
+// so eight waves give every SIMD two to interleave.
+constexpr int kPrepChWaves = 8;
+
+template <int C, int DK, typename IO, int GATE, bool BWD = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void fwd_prep_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
@@ -208,6 +212,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   constexpr int LDT = S::LDT, LDK = S::LDK, LDC = S::LDC, LDV = S::LDV;
   constexpr int VW = 16 / ib;       // elements per 16-byte vector
   constexpr int VPR = DK / VW;      // vectors per K row
+  constexpr int NT = 64 * NW;       // threads
 
   __shared__ __attribute__((aligned(16))) char smem[S::total];
   __shared__ int s_span_bits;
@@ -266,11 +271,11 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   constexpr int NPF = NB == 1 ? 1 : (NB == 2 ? 2 : 6);
   constexpr int NPT = BWD ? num_pt_frags(NB, NKC) : 0;  // P^T fragments
   constexpr int JOBS = NT2 + NPF + NPT;
-  constexpr int MAXJ = (JOBS + 3) / 4;
+  constexpr int MAXJ = (JOBS + NW - 1) / NW;
   opvec<OP> qpre[MAXJ][NKD];
 #pragma unroll
   for (int u = 0; u < MAXJ; ++u) {
-    const int job = wave + 4 * u;
+    const int job = wave + NW * u;
     if (job >= NT2 && job < NT2 + NPF) {
       int f = job - NT2, rt = 0;
       for (rt = 0; rt < NB; ++rt) {
@@ -306,11 +311,11 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   }
   // K rows, and the per-channel log gates, as 16-byte pieces: every load is
   // issued before the first LDS store, so the loads travel together
-  constexpr int NKP = (C * VPR + 255) / 256;
+  constexpr int NKP = (C * VPR + NT - 1) / NT;
   uint4 kraw[NKP];
 #pragma unroll
   for (int u = 0; u < NKP; ++u) {
-    const int e = tid + 256 * u;
+    const int e = tid + NT * u;
     const int r = e / VPR, cv = (e % VPR) * VW;
     kraw[u] = make_uint4(0, 0, 0, 0);
     if (e < C * VPR && r < len)
@@ -318,13 +323,13 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
           static_cast<const char*>(k) + (((tok0 + r) * H + h) * DK + cv) * ib);
   }
   if constexpr (CH) {
-    constexpr int NGP = (C * DK / 4 + 255) / 256;  // pieces per thread (fp32 gates)
+    constexpr int NGP = (C * DK / 4 + NT - 1) / NT;  // pieces per thread (fp32 gates)
     const int per = gbf ? 8 : 4;                    // gate elements per piece
     const int np = C * DK / per;
     uint4 graw[NGP];
 #pragma unroll
     for (int u = 0; u < NGP; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + NT * u;
       const int r = (e * per) / DK, col = (e * per) % DK;
       graw[u] = make_uint4(0, 0, 0, 0);
       if (e < np && r < len)
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
     }
 #pragma unroll
     for (int u = 0; u < NGP; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + NT * u;
       if (e < np) {
         float x[8];
         if (gbf) unpack16<bf16_t>(graw[u], x);
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   }
 #pragma unroll
   for (int u = 0; u < NKP; ++u) {
-    const int e = tid + 256 * u;
+    const int e = tid + NT * u;
     if (e >= C * VPR) continue;
     const int r = e / VPR, cv = (e % VPR) * VW;
     *reinterpret_cast<uint4*>(sK + (size_t(r) * LDK + cv) * ib) = kraw[u];
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   }
   __syncthreads();
   if constexpr (CH) {
-    for (int col = tid; col < DK; col += 256) {
+    for (int col = tid; col < DK; col += NT) {
       float x = 0.f, mx = -3.0e38f, mn = 3.0e38f;
       for (int r = 0; r < C; ++r) {
         x += sg[r * DK + col];
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   if constexpr (CH) exact = __int_as_float(s_span_bits) > kChannelHalfSpan;
   if constexpr (S::EF) {
     if (!exact) {  // the same for the whole workgroup
-      for (int e = tid; e < C * DK; e += 256) {
+      for (int e = tid; e < C * DK; e += NT) {
         const int r = e / DK, d = e % DK;
         const float gm = sg[e] - smid[d];
         sEu[r * S::LDE + d] = static_cast<__bf16>(fast_exp(gm));
@@ -398,7 +403,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   if (!exact) {
 #pragma unroll
     for (int u = 0; u < MAXJ; ++u) {
-      const int job = wave + 4 * u;
+      const int job = wave + NW * u;
       if (job >= JOBS) continue;
       if (job < NT2) {
         int t = job, rt = 0;
@@ -545,7 +550,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
     }
   } else if constexpr (CH) {
     // exact per-element path for extreme per-channel decay spans
-    for (int e = tid; e < C * C; e += 256) {
+    for (int e = tid; e < C * C; e += NT) {
       const int r = e / C, i = e % C;
       float pv = 0.f, av = 0.f;
       if (i <= r && r < len) {
@@ -560,7 +565,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
       sA[r * LDC + i] = (i < r) ? av * sbeta[r] : 0.f;
     }
     __syncthreads();
-    for (int e = tid; e < NB * NKC * 64; e += 256) {
+    for (int e = tid; e < NB * NKC * 64; e += NT) {
       const int ln = e & 63, fr = e >> 6;
       const int rt = fr / NKC, jb = fr % NKC;
       if (32 * jb > 16 * rt + 15) continue;
@@ -575,7 +580,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
           frag<OP>::from_floats(vals);
     }
     if constexpr (BWD) {
-      for (int e = tid; e < NB * NKC * 64; e += 256) {
+      for (int e = tid; e < NB * NKC * 64; e += NT) {
         const int ln = e & 63, fr = e >> 6;
         const int it = fr / NKC, jb = fr % NKC;
         if (32 * jb + 31 < 16 * it) continue;
@@ -612,13 +617,13 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
     }
   } else {
     const int t3 = tid - 64;
-    for (int e = t3; e < C * C; e += 192) {
+    for (int e = t3; e < C * C; e += NT - 64) {
       const int r = e / C, i = e % C;
       if ((i >> 4) > (r >> 4)) sT[r * LDC + i] = 0.f;
     }
     // K~^T fragments: rows dk, tokens in the permuted order
     char* dk_ = buf.at(ch, buf.off_k);
-    for (int e = t3; e < NDT * NKC * 64; e += 192) {
+    for (int e = t3; e < NDT * NKC * 64; e += NT - 64) {
       const int ln = e & 63, fr = e >> 6;
       const int a = fr / NKC, jb = fr % NKC;
       const int m = ln & 15, g = ln >> 4;
@@ -644,11 +649,11 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
       char* dq = buf.at(ch, buf.off_q);
       // slots 0..3 and 4..7 of a lane are channels 32 jb + 4 g .. + 3 and
       // 16 further on: two 4-element loads, all issued before any use
-      constexpr int NQF = NB * NKD * 64, NQI = (NQF + 191) / 192;
+      constexpr int NQF = NB * NKD * 64, NQI = (NQF + NT - 65) / (NT - 64);
       float qv[NQI][8];
 #pragma unroll
       for (int u = 0; u < NQI; ++u) {
-        const int e = t3 + 192 * u;
+        const int e = t3 + (NT - 64) * u;
         const int ln = e & 63, fr = e >> 6;
         const int rt = fr / NKD, jb = fr % NKD;
         const int r = 16 * rt + (ln & 15), dk0 = 32 * jb + 4 * (ln >> 4);
@@ -662,7 +667,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
       }
 #pragma unroll
       for (int u = 0; u < NQI; ++u) {
-        const int e = t3 + 192 * u;
+        const int e = t3 + (NT - 64) * u;
         if (e >= NQF) continue;
         const int ln = e & 63, fr = e >> 6;
         const int rt = fr / NKD, jb = fr % NKD;
@@ -682,7 +687,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
       // K~ fragments (rows i, k = dk permuted) and Q~^T fragments (rows dk,
       // k = r permuted) for the reverse recurrence
       char* dkf = buf.at(ch, buf.off_kf);
-      for (int e = t3; e < NB * NKD * 64; e += 192) {
+      for (int e = t3; e < NB * NKD * 64; e += NT - 64) {
         const int ln = e & 63, fr = e >> 6;
         const int rt = fr / NKD, jb = fr % NKD;
         const int m = ln & 15, g = ln >> 4;
@@ -703,7 +708,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
             frag<OP>::from_floats(vals);
       }
       char* dqt = buf.at(ch, buf.off_qt);
-      for (int e = t3; e < NDT * NKC * 64; e += 192) {
+      for (int e = t3; e < NDT * NKC * 64; e += NT - 64) {
         const int ln = e & 63, fr = e >> 6;
         const int a = fr / NKC, jb = fr % NKC;
         const int m = ln & 15, g = ln >> 4;
@@ -730,7 +735,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
       if constexpr (GATE == GDN_GATE_SCALAR) x = fast_exp(sg[t3]);
       gam[t3] = x;
     }
-    for (int d = t3; d < DK; d += 192) {
+    for (int d = t3; d < DK; d += NT - 64) {
       float x = 1.f;
       if constexpr (GATE == GDN_GATE_SCALAR) x = fast_exp(sg[C - 1]);
       if constexpr (CH) x = fast_exp(sg[(C - 1) * DK + d]);
@@ -767,7 +772,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   // ---- 5. -W fragments: W^T = X^T T^T with X = diag(b gamma) K ------------
   {
     char* dst = buf.at(ch, buf.off_w);
-    for (int job = wave; job < NKD * NB; job += 4) {
+    for (int job = wave; job < NKD * NB; job += NW) {
       const int jb = job / NB, rt = job % NB;
       floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
       const int r = 16 * rt + l16;
@@ -819,7 +824,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
   if constexpr (BWD) {
     // -W^T fragments (rows dk, k = tokens permuted) from W = T X tiles
     char* dst = buf.at(ch, buf.off_wt);
-    for (int job = wave; job < NDT * NKC; job += 4) {
+    for (int job = wave; job < NDT * NKC; job += NW) {
       const int a = job / NKC, jb = job % NKC;
       const int dk = 16 * a + l16;
       float out[8];
@@ -864,13 +869,13 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
     const int ndt = dv / 16;
     constexpr int SV = 64 / VW;  // 16-byte vectors per slab row
     // the next slab's V pieces are loaded while the current one is used
-    constexpr int NVS = (C * SV + 255) / 256;
+    constexpr int NVS = (C * SV + NT - 1) / NT;
     uint4 vraw[NVS];
     auto load_v = [&](int slab) {
       const int ncol = min(64, dv - slab);
 #pragma unroll
       for (int u = 0; u < NVS; ++u) {
-        const int e = tid + 256 * u;
+        const int e = tid + NT * u;
         const int i = e / SV, cv = (e % SV) * VW;
         vraw[u] = make_uint4(0, 0, 0, 0);
         if (e < C * SV && i < len && cv < ncol)
@@ -883,7 +888,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
       const int ncol = min(64, dv - slab);
 #pragma unroll
       for (int u = 0; u < NVS; ++u) {
-        const int e = tid + 256 * u;
+        const int e = tid + NT * u;
         if (e >= C * SV) continue;
         const int i = e / SV, cv = (e % SV) * VW;
         float x[8];
@@ -894,7 +899,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(
       if (slab + 64 < dv) load_v(slab + 64);
       __syncthreads();
       const int nvt = ncol / 16;
-      for (int job = wave; job < NB * nvt; job += 4) {
+      for (int job = wave; job < NB * nvt; job += NW) {
         const int rt = job / nvt, vt = job % nvt;
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
         const int r = 16 * rt + l16;
