@@ -22,6 +22,8 @@ Other entry points (same JSON shape, their own metric string):
     --mode decode_product  gdn_decode_step_product (--nh steps per token)
     --qk-l2norm     (forward) gdn_chunk_fwd_qknorm on q, k rows that are not
                     unit vectors (log-uniform row scales in [0.05, 20])
+    --conv W        (forward) gdn_chunk_fwd_conv, short convolution of width W:
+                    the workload's q, k, v are the projections
 
 Algorithmic work per (token, head), chunk C:
     flops = 6 dk dv + C (3 dk + 2 dv) + C^2 / 3
@@ -644,10 +646,12 @@ def copy_bandwidth(nbytes=1 << 30, reps=10):
     return 2 * nbytes / (times[len(times) // 2] * 1e-3) / 1e9
 
 
-def cpu_baseline(inp, budget_s, qknorm=False):
+def cpu_baseline(inp, budget_s, qknorm=False, taps=None):
     """The fp64 oracle, as it stands, on every (sequence, head) chain of the
     workload, P workers; tokens/s of the whole workload.  qknorm: q and k rows
-    go through the oracle's L2 normalisation first (timed)."""
+    go through the oracle's L2 normalisation first (timed); taps (wq, wk, wv,
+    numpy fp64 [H, d, W]): q, k, v go through the oracle's convolution
+    prologue first (timed)."""
     import numpy as np
     import oracle
     f = inp.f64
@@ -658,11 +662,13 @@ def cpu_baseline(inp, budget_s, qknorm=False):
         (b, a, e, n), h = u
         la = None if f["log_alpha"] is None else f["log_alpha"][b, a:e, h]
         m0 = np.zeros((dk, dv)) if f["s0"] is None else f["s0"][n, h]
-        qc, kc = f["q"][b, a:e, h], f["k"][b, a:e, h]
+        qc, kc, vc = f["q"][b, a:e, h], f["k"][b, a:e, h], f["v"][b, a:e, h]
         if qknorm:
             qc, kc = oracle.l2_normalize(qc), oracle.l2_normalize(kc)
-        oracle.gdn_fwd_chain(qc, kc, f["v"][b, a:e, h], f["beta"][b, a:e, h], la, m0,
-                             inp.gate)
+        if taps is not None:   # one chain as a [1, len, 1, d] batch
+            pro = lambda x, w, nz: oracle.conv_prologue(x[None, :, None], w[h][None], nz)[0, :, 0]
+            qc, kc, vc = pro(qc, taps[0], True), pro(kc, taps[1], True), pro(vc, taps[2], False)
+        oracle.gdn_fwd_chain(qc, kc, vc, f["beta"][b, a:e, h], la, m0, inp.gate)
 
     return cpu_oracle_rate(job, units, lambda u: (u[0][2] - u[0][1]) / H, budget_s,
                            "oracle token recurrence over every (sequence, head) chain")
@@ -681,6 +687,9 @@ def main():
                     help="delta steps per token for --mode product")
     ap.add_argument("--qk-l2norm", action="store_true",
                     help="forward with q and k L2-normalised inside the kernels")
+    ap.add_argument("--conv", type=int, default=0,
+                    help="(forward) gdn_chunk_fwd_conv with this short-convolution width: "
+                         "the workload's q, k, v are the projections")
     ap.add_argument("--batch", type=int, default=0,
                     help="(forward) override the workload's batch size B")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -743,16 +752,20 @@ def main_fwd(args):
     dv = inp.v.shape[-1]
     C = inp.chunk
     nseq = B if inp.cu_seqlens is None else inp.cu_seqlens.numel() - 1
-    wl = args.workload + (f"_b{B}" if args.batch else "") + ("_qknorm" if qkn else "")
+    wl = (args.workload + (f"_b{B}" if args.batch else "") + ("_qknorm" if qkn else "") +
+          (f"_conv{args.conv}" if args.conv else ""))
+    taps = synth.conv_taps(H, dk, dv, args.conv, inp.seed) if args.conv else None
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_budget, qknorm=qkn)
+        cpu = cpu_baseline(inp, args.cpu_budget, qknorm=qkn,
+                           taps=None if taps is None else [t.double().numpy() for t in taps])
         cpu["value"] = round(cpu["value"], 1)
         cpu["single_worker_value"] = round(cpu["single_worker_value"], 1)
 
     d = inp.to("cuda")
     plan = gdn.FwdPlan(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, chunk=C,
-                       cu_seqlens=d.cu_seqlens, qk_l2norm=qkn)
+                       cu_seqlens=d.cu_seqlens, qk_l2norm=qkn,
+                       conv_taps=None if taps is None else [t.cuda() for t in taps])
     evict = cache_evictor()
     for _ in range(args.warmup):
         evict()
@@ -803,10 +816,10 @@ def main_fwd(args):
     prep_kernel = "fwd_prep_kernel" if inp.gate == "channel" else "fwd_prep_sg_kernel"
     names = {"fwd_prep": prep_kernel, "fwd_scan": "fwd_scan_kernel",
              "fwd_trans": "fwd_trans_kernel", "fwd_combine": "fwd_combine_kernel",
-             "chunk_map": "chunk_map_kernel"}
+             "chunk_map": "chunk_map_kernel", "prologue": "prologue_kernel"}
     dom = max(per_kernel, key=per_kernel.get)
     src_hash = source_hash(FWD_SOURCES)
-    traffic = None if qkn else measured_traffic(wl, "fwd_call", src_hash)
+    traffic = None if (qkn or args.conv) else measured_traffic(wl, "fwd_call", src_hash)
     achieved = byts / (cold_ms * 1e-3) / 1e9
     roofline = {
         # the forward call as one unit: its algorithmic bytes over the median
@@ -828,7 +841,9 @@ def main_fwd(args):
         "source_hash": src_hash,
     }
     out = {
-        "metric": ("tokens/sec gdn_chunk_fwd_qknorm (T=4096,H=16,d=128 bf16); % HBM roofline"
+        "metric": (f"tokens/sec gdn_chunk_fwd_conv (T={T},H={H},d={dk},W={args.conv}); "
+                   "% HBM roofline" if args.conv else
+                   "tokens/sec gdn_chunk_fwd_qknorm (T=4096,H=16,d=128 bf16); % HBM roofline"
                    if qkn else
                    "tokens/sec gdn_chunk_fwd (T=4096,H=16,d=128 bf16); % MFMA/HBM roofline"),
         "value": round(tokens / (cold_ms * 1e-3), 1),

@@ -346,10 +346,12 @@ class FwdPlan:
 
     def __init__(self, q, k, v, beta, log_alpha=None, s0=None, chunk: int = 64,
                  cu_seqlens=None, output_final_state: bool = True,
-                 qk_l2norm: bool = False, seg_chunks: int = 0):
+                 qk_l2norm: bool = False, seg_chunks: int = 0, conv_taps=None):
+        # conv_taps = (wq, wk, wv): q, k, v are the projections of
+        # gdn_chunk_fwd_conv (short convolution, SiLU, L2 norm of q and k)
         lib = _lib.load()
         _check_cu(cu_seqlens, q)
-        self._keep = (q, k, v, beta, log_alpha, s0, cu_seqlens)
+        self._keep = (q, k, v, beta, log_alpha, s0, cu_seqlens, conv_taps)
         self.problem = _problem(q, v, beta, log_alpha, chunk, cu_seqlens,
                                 seg_chunks=seg_chunks)
         nseq = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -358,16 +360,26 @@ class FwdPlan:
         self.s_final = (torch.empty((nseq, H, dk, dv), dtype=torch.float32,
                                     device=q.device) if output_final_state else None)
         need = ctypes.c_size_t(0)
-        wsq = lib.gdn_chunk_fwd_qknorm_workspace if qk_l2norm else lib.gdn_chunk_fwd_workspace
-        _lib.check(wsq(ctypes.byref(self.problem), ctypes.byref(need)), "workspace query")
+        if conv_taps is not None:
+            width = conv_taps[0].shape[-1]
+            _lib.check(lib.gdn_chunk_fwd_conv_workspace(ctypes.byref(self.problem), width,
+                                                        ctypes.byref(need)), "workspace query")
+        else:
+            wsq = (lib.gdn_chunk_fwd_qknorm_workspace if qk_l2norm
+                   else lib.gdn_chunk_fwd_workspace)
+            _lib.check(wsq(ctypes.byref(self.problem), ctypes.byref(need)), "workspace query")
         self.workspace = torch.empty(max(need.value, 1), dtype=torch.uint8,
                                      device=q.device)
-        self._name = "gdn_chunk_fwd_qknorm" if qk_l2norm else "gdn_chunk_fwd"
+        tail = (_ptr(beta), _ptr(log_alpha), _ptr(s0), _ptr(self.o), _ptr(self.s_final),
+                _ptr(self.workspace), self.workspace.numel(), _stream(q.device))
+        if conv_taps is not None:
+            self._name = "gdn_chunk_fwd_conv"
+            self._args = (ctypes.byref(self.problem), width, _ptr(q), _ptr(k), _ptr(v),
+                          *(_ptr(w) for w in conv_taps)) + tail
+        else:
+            self._name = "gdn_chunk_fwd_qknorm" if qk_l2norm else "gdn_chunk_fwd"
+            self._args = (ctypes.byref(self.problem), _ptr(q), _ptr(k), _ptr(v)) + tail
         self._fn = getattr(lib, self._name)
-        self._args = (ctypes.byref(self.problem), _ptr(q), _ptr(k), _ptr(v),
-                      _ptr(beta), _ptr(log_alpha), _ptr(s0), _ptr(self.o),
-                      _ptr(self.s_final), _ptr(self.workspace),
-                      self.workspace.numel(), _stream(q.device))
 
     def run(self):
         st = self._fn(*self._args)

@@ -112,6 +112,9 @@ gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out, int lnh 
   out->qknorm = false;
   out->parent = nullptr;
   out->beta_w = nullptr;
+  out->conv_w = 0;
+  out->conv_tk = nullptr;
+  out->conv_tv = nullptr;
   out->H = p->H;
   out->dk = p->dk;
   out->dv = p->dv;
@@ -155,12 +158,13 @@ gdn_status launched(const gdn::Problem& p, hipError_t e) {
   if (log_on()) {
     fprintf(stderr,
             "gdn: %s: B=%d T=%d H=%d dk=%d dv=%d chunk=%d io=%s gate=%s/%s nseq=%d%s "
-            "chunks=%lld segment_chunks=%d segments=%lld steps_per_token=%d%s%s -> %s\n",
+            "chunks=%lld segment_chunks=%d segments=%lld steps_per_token=%d%s%s conv_width=%d "
+            "-> %s\n",
             t_entry, p.B, p.T, p.H, p.dk, p.dv, p.chunk, dtype_name(p.io), gate_name(p.gate),
             dtype_name(p.gdt), p.nseq, p.varlen ? " (varlen)" : "",
             static_cast<long long>(p.nchunks), p.seg, static_cast<long long>(p.nsegs),
             1 << p.lnh, p.qknorm ? " qk_l2norm" : "", p.beta_w ? " write_strength" : "",
-            hipGetErrorName(e));
+            p.conv_w, hipGetErrorName(e));
   }
   return e == hipSuccess ? GDN_OK : GDN_FAIL(GDN_ERR_HIP);
 }
@@ -446,8 +450,12 @@ size_t qknorm_workspace_bytes(const gdn::Problem& p) {
   return pro + gdn::fwd_workspace_bytes(p);
 }
 
+// Per-token gates: the prep convolves k and v itself, q takes one prologue
+// pass; the per-channel gate's prep takes all three rows processed.
 size_t conv_workspace_bytes(const gdn::Problem& p) {
-  return 2 * rows_bytes(p, p.dk) + rows_bytes(p, p.dv) + gdn::fwd_workspace_bytes(p);
+  const size_t pro = p.gate == GDN_GATE_CHANNEL
+                         ? 2 * rows_bytes(p, p.dk) + rows_bytes(p, p.dv) : rows_bytes(p, p.dk);
+  return pro + gdn::fwd_workspace_bytes(p);
 }
 
 }  // namespace
@@ -534,9 +542,22 @@ gdn_status gdn_chunk_fwd_conv(const gdn_problem* p, int32_t width, const void* x
     const size_t need_ws = conv_workspace_bytes(pp);
     if (ws == nullptr || ws_bytes < need_ws) return GDN_FAIL(GDN_ERR_WORKSPACE);
     GDN_TRY(opt(ws));
+    if (pp.gate != GDN_GATE_CHANNEL) {  // the prep convolves k and v
+      pp.conv_w = width;
+      pp.conv_tk = wk;
+      pp.conv_tv = wv;
+    }
     if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* qn = static_cast<char*>(ws);
+    if (pp.conv_w > 0) {
+      // q through the prologue pass; k and v convolved in the prep's staging
+      char* fw = qn + rows_bytes(pp, pp.dk);
+      if (gdn::launch_prologue(pp, pp.dk, width, xq, wq, true, qn, st) != hipSuccess)
+        return GDN_FAIL(GDN_ERR_HIP);
+      return launched(pp, gdn::launch_fwd(pp, qn, xk, xv, beta, log_alpha, s0, o, s_final, fw,
+                                          st));
+    }
     char* kn = qn + rows_bytes(pp, pp.dk);
     char* vn = kn + rows_bytes(pp, pp.dk);
     char* fw = vn + rows_bytes(pp, pp.dv);

@@ -168,10 +168,18 @@ hipError_t run_fwd(const Problem& p, const void* q, const void* k,
                          0, s, map, p.H, p.dv, p.nchunks, q, k, v, beta, la,
                          p.gdt == GDN_BF16, buf, p.beta_w);
     else
-      hipLaunchKernelGGL((fwd_prep_sg_kernel<C, DK, IO, GATE>),
-                         dim3(static_cast<unsigned>(p.nchunks * p.H)), dim3(64 * prep_waves(C)),
-                         0, s, map, p.H, p.dv, p.nchunks, q, k, v, beta, la,
-                         p.gdt == GDN_BF16, buf, p.lnh, p.qknorm, p.parent, p.beta_w);
+      if (p.conv_w > 0)
+        hipLaunchKernelGGL((fwd_prep_sg_kernel<C, DK, IO, GATE, false, true>),
+                           dim3(static_cast<unsigned>(p.nchunks * p.H)),
+                           dim3(64 * prep_waves(C)), 0, s, map, p.H, p.dv, p.nchunks, q, k, v,
+                           beta, la, p.gdt == GDN_BF16, buf, p.lnh, p.qknorm, p.parent,
+                           p.beta_w, p.conv_w, p.conv_tk, p.conv_tv);
+      else
+        hipLaunchKernelGGL((fwd_prep_sg_kernel<C, DK, IO, GATE>),
+                           dim3(static_cast<unsigned>(p.nchunks * p.H)),
+                           dim3(64 * prep_waves(C)), 0, s, map, p.H, p.dv, p.nchunks, q, k, v,
+                           beta, la, p.gdt == GDN_BF16, buf, p.lnh, p.qknorm, p.parent,
+                           p.beta_w);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

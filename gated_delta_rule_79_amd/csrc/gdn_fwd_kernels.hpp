@@ -946,7 +946,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_prep_kernel(
 // tiles for eight waves, and smaller workgroups keep more chunks in flight
 constexpr int prep_waves(int C) { return C == 16 ? 2 : (C == 32 ? 4 : 8); }
 
-template <int C, int DK, typename IO>
+template <int C, int DK, typename IO, bool CONV = false>
 struct PrepSgSmem {
   static constexpr int ib = io<IO>::bytes;
   static constexpr int LDKB = DK * ib + 16;        // K row pitch (bytes)
@@ -965,7 +965,12 @@ struct PrepSgSmem {
   static constexpr size_t ks_off = xs_off + size_t(C) * 4;
   static constexpr size_t qn_off = ks_off + size_t(C) * 4;   // 1 / |q_r|
   static constexpr size_t anc_off = qn_off + size_t(C) * 4;  // tree ancestor sets
-  static constexpr size_t total = anc_off + size_t(C) * 8;
+  // fused convolution taps (widths up to 8): over the A and T matrices'
+  // bytes (free while K and V are staged) when they fit, else their own
+  static constexpr size_t tap_bytes = CONV ? size_t(DK + VCOLS) * 8 * 4 : 0;
+  static constexpr bool tap_in_at = 2 * size_t(C) * LDC * 4 >= tap_bytes;
+  static constexpr size_t tap_off = tap_in_at ? a_off : anc_off + size_t(C) * 8;
+  static constexpr size_t total = tap_in_at ? anc_off + size_t(C) * 8 : tap_off + tap_bytes;
   static_assert(total <= 160 * 1024, "prep LDS budget");
 };
 
@@ -985,19 +990,24 @@ struct PrepSgSmem {
 // T = (I + A)^-1 only ever chains ancestors.  The state carried past the
 // chunk is not meaningful for a tree: its decays are set to zero.  Parent
 // entries outside [-1, r) are read as -1.
+// CONV (fused short convolution, width cw): K and V rows are staged as the causal
+// depthwise convolution of k and v over the cw tokens ending at the row (taps
+// ctk, ctv [H, d, cw]; no tokens before the sequence start) through SiLU, and
+// K rows are then L2-normalised; q arrives already processed.
 //
 // BWD (backward recomputation): also the reverse recurrence's operands, the
 // K~ rows, -W^T, P^T and Q~^T fragments (the layouts of the general prep).
-template <int C, int DK, typename IO, int GATE, bool BWD = false>
+template <int C, int DK, typename IO, int GATE, bool BWD = false, bool CONV = false>
 __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
     ChunkMap map, int H, int dv, int64_t nchunks, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ beta, const void* __restrict__ la, bool gbf,
     FwdBuffers buf, int lnh, bool qkn, const int32_t* __restrict__ parent,
-    const void* __restrict__ beta_w) {
+    const void* __restrict__ beta_w, int cw = 0, const float* __restrict__ ctk = nullptr,
+    const float* __restrict__ ctv = nullptr) {
   static_assert(GATE != GDN_GATE_CHANNEL, "per-token gates only");
   using OP = IO;
-  using S = PrepSgSmem<C, DK, IO>;
+  using S = PrepSgSmem<C, DK, IO, CONV>;
   constexpr int ib = S::ib;
   constexpr int ob = opstore<OP>::bytes;
   constexpr int NB = C / 16, NKD = (DK + 31) / 32, NKC = (C + 31) / 32, NDT = DK / 16;
@@ -1076,19 +1086,74 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
   constexpr int VPM = S::VCOLS * ib / 16;      // pieces per staged V row
   constexpr int NKL = (C * KP + NT - 1) / NT;   // K pieces per thread
   constexpr int NVL = (C * VPM + NT - 1) / NT;  // V pieces per thread (max)
+  // fused convolution: the 16-byte piece of row r at element column col0 of
+  // x ([tokens, H, D]) convolved with its taps over the rows r, r - 1, ..
+  // back to the sequence start, through SiLU
+  int64_t sstart = 0;
+  if constexpr (CONV)
+    sstart = map.varlen ? chunk_info(map, ld_table(map.first, ci.seq)).tok0
+                        : static_cast<int64_t>(ci.seq) * map.T;
+  // taps of this head in LDS, tap-major ([cw][columns]: a piece's channels
+  // are adjacent); over the A and T bytes they are written before step 1 and
+  // again in step 6, where both are dead: K's columns, then V's staged ones
+  float* stk = reinterpret_cast<float*>(smem + S::tap_off);
+  float* stv = stk + (CONV ? DK * cw : 0);
+  auto stage_taps = [&](float* dst, const float* taps, int D, int c0, int nc) {
+    for (int e = tid; e < nc * cw; e += NT) {
+      const int c = e / cw, j = e - (e / cw) * cw;
+      dst[j * nc + c] = taps[(static_cast<int64_t>(h) * D + c0 + c) * cw + j];
+    }
+  };
+  // the piece of row r at columns col .. col + 16 / ib of x ([tokens, H, D])
+  // convolved over rows r, r - 1, .. (not before the sequence start) with
+  // the LDS taps st ([cw][nc], column col - c0), through SiLU
+  auto conv_piece = [&](const void* x, const float* st, int nc, int D, int col, int c0, int r,
+                        float* acc) {
+    constexpr int VE = 16 / ib;
+#pragma unroll
+    for (int s2 = 0; s2 < VE; ++s2) acc[s2] = 0.f;
+    const int64_t t = tok0 + r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // widths up to 8; all loads issued together
+      if (j < cw && t - j >= sstart) {
+        float xv[VE];
+        unpack16<IO>(*reinterpret_cast<const uint4*>(
+                         static_cast<const char*>(x) + (((t - j) * H + h) * D + col) * ib),
+                     xv);
+        const float* tj = st + j * nc + (col - c0);
+#pragma unroll
+        for (int s2 = 0; s2 < VE; ++s2) acc[s2] += tj[s2] * xv[s2];
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < VE; ++s2) acc[s2] = acc[s2] / (1.f + expf(-acc[s2]));
+  };
   auto stage_v = [&](int c0) {
     // columns [c0, c0 + VCOLS) of V; pieces past dv or the chunk are zero
     const int VP = min(S::VCOLS, dv - c0) * ib / 16;
+    const int nvc = min(S::VCOLS, dv - c0);
+    if constexpr (CONV) {
+      if (c0 > 0) {  // the taps of these columns (A and T are dead by now)
+        stage_taps(stv, ctv, dv, c0, nvc);
+        __syncthreads();
+      }
+    }
     uint4 raw[NVL];
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
       const int e = tid + NT * u;
       const int r = e / VPM, pc = e % VPM;
       raw[u] = make_uint4(0, 0, 0, 0);
-      if (e < C * VPM && r < len && pc < VP)
-        raw[u] = *reinterpret_cast<const uint4*>(
-            static_cast<const char*>(v) +
-            (((tok0 + r) * H + h) * static_cast<int64_t>(dv) + c0) * ib + pc * 16);
+      if (e < C * VPM && r < len && pc < VP) {
+        if constexpr (CONV) {
+          float x[16 / ib];
+          conv_piece(v, stv, nvc, dv, c0 + pc * (16 / ib), c0, r, x);
+          raw[u] = pack16<IO>(x);
+        } else
+          raw[u] = *reinterpret_cast<const uint4*>(
+              static_cast<const char*>(v) +
+              (((tok0 + r) * H + h) * static_cast<int64_t>(dv) + c0) * ib + pc * 16);
+      }
     }
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
@@ -1096,25 +1161,44 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
       if (e < C * VPM) *reinterpret_cast<uint4*>(sV + (e / VPM) * LDVB + (e % VPM) * 16) = raw[u];
     }
   };
+  if constexpr (CONV) {
+    stage_taps(stk, ctk, DK, 0, DK);
+    stage_taps(stv, ctv, dv, 0, min(S::VCOLS, dv));
+    __syncthreads();
+  }
   {
     uint4 raw[NKL];
+    float kc[CONV ? NKL : 1][16 / ib];  // convolved K pieces, unrounded until normalised
 #pragma unroll
     for (int u = 0; u < NKL; ++u) {
       const int e = tid + NT * u;
       const int r = e / KP, pc = e % KP;
       raw[u] = make_uint4(0, 0, 0, 0);
-      if (e < C * KP && r < len)
-        raw[u] = *reinterpret_cast<const uint4*>(
-            static_cast<const char*>(k) + ((tok0 + r) * H + h) * DK * ib + pc * 16);
+      if constexpr (CONV) {
+#pragma unroll
+        for (int s2 = 0; s2 < 16 / ib; ++s2) kc[u][s2] = 0.f;
+      }
+      if (e < C * KP && r < len) {
+        if constexpr (CONV)
+          conv_piece(k, stk, DK, DK, pc * (16 / ib), 0, r, kc[u]);
+        else
+          raw[u] = *reinterpret_cast<const uint4*>(
+              static_cast<const char*>(k) + ((tok0 + r) * H + h) * DK * ib + pc * 16);
+      }
     }
     stage_v(0);
-    if (qkn) {
+    if (qkn || CONV) {
       // the KP pieces of a row sit in KP aligned consecutive lanes
       static_assert(KP <= 64 && (KP & (KP - 1)) == 0, "K row pieces per wave");
 #pragma unroll
       for (int u = 0; u < NKL; ++u) {
         float x[16 / ib];
-        unpack16<IO>(raw[u], x);
+        if constexpr (CONV) {
+#pragma unroll
+          for (int s2 = 0; s2 < 16 / ib; ++s2) x[s2] = kc[u][s2];
+        } else {
+          unpack16<IO>(raw[u], x);
+        }
         float ss = 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < 16 / ib; ++s2) ss += x[s2] * x[s2];

@@ -30,6 +30,13 @@ struct Problem {
                               // decoupled erase/write rule (gate_dtype, like
                               // beta, which is then the erase strength);
                               // nullptr: beta does both
+  int conv_w;                 // forward, per-token gates: > 0 fuses the short
+                              // causal convolution of k and v (width conv_w,
+                              // fp32 taps [H, d, conv_w]) and SiLU into the
+                              // prep's staging, k rows then L2-normalised;
+                              // q arrives processed.  0 otherwise.
+  const float* conv_tk;       // device taps of k and v
+  const float* conv_tv;
   // derived
   int64_t nchunks;            // chunk slots per head (upper bound in varlen)
   int seg;                    // chunks per segment of the forward state pass

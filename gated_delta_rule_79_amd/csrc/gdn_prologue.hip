@@ -15,10 +15,11 @@
 // The result is written in the input dtype for the chunked forward.
 //
 // One workgroup holds rows of one head: a row is D / 8 consecutive lanes,
-// each with 8 channels, so the row's sum of squares is a few shuffles (D / 8
-// is a power of two that divides 64 whenever the row is normalised).  The
-// pass is a stream over x and y; each input row is read W times, from L2
-// after the first.
+// each with 8 channels read and written as 16-byte pieces, so the row's sum
+// of squares is a few shuffles (D / 8 is a power of two that divides 64
+// whenever the row is normalised).  The head's taps sit in LDS tap-major.
+// The pass is a stream over x and y; each input row is read W times, from
+// L2 after the first.
 
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
@@ -27,16 +28,37 @@ namespace gdn {
 
 namespace {
 
+constexpr int kMaxWidth = 8;
+constexpr int kMaxD = 256;
+
+// 8 channels starting at element i of a row (16-byte aligned pieces).
 template <typename IO>
 __device__ inline void load8(const void* p, int64_t i, float* x) {
+  if constexpr (io<IO>::bytes == 2) {
+    const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const char*>(p) + i * 2);
+    const __bf16* b = reinterpret_cast<const __bf16*>(&r);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = io<IO>::load(p, i + e);
+    for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(b[e]);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
 }
 
 template <typename IO>
 __device__ inline void store8(void* p, int64_t i, const float* x) {
+  if constexpr (io<IO>::bytes == 2) {
+    uint4 r;
+    __bf16* b = reinterpret_cast<__bf16*>(&r);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) io<IO>::store(p, i + e, x[e]);
+    for (int e = 0; e < 8; ++e) b[e] = static_cast<__bf16>(x[e]);
+    *reinterpret_cast<uint4*>(static_cast<char*>(p) + i * 2) = r;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + i + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  }
 }
 
 // First token of the sequence holding token t.
@@ -56,11 +78,20 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     int64_t ntok, int T, int H, int D, int W, const int32_t* __restrict__ cu, int nseq,
     const void* __restrict__ x, const float* __restrict__ taps, bool conv, bool normalize,
     void* __restrict__ y) {
+  // this head's taps, tap-major ([W][D]): a lane's 8 channels are adjacent
+  __shared__ __attribute__((aligned(16))) float st[kMaxWidth * kMaxD];
   const int G = D / 8;             // 8-channel groups per row
   const int rows = 256 / G;        // rows per workgroup
   const int tid = threadIdx.x;
   const int r = tid / G, g = tid - (tid / G) * G;
   const int h = blockIdx.y;
+  if (conv) {  // uniform
+    for (int e = tid; e < D * W; e += 256) {
+      const int c = e / W, j = e - (e / W) * W;
+      st[j * D + c] = taps[(static_cast<int64_t>(h) * D + c) * W + j];
+    }
+    __syncthreads();
+  }
   const int64_t t = static_cast<int64_t>(blockIdx.x) * rows + r;
   const bool act = r < rows && t < ntok;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -68,12 +99,15 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     const int64_t col = static_cast<int64_t>(h) * D + 8 * g;
     if (conv) {
       const int64_t s0 = seq_start(t, T, cu, nseq);
-      const float* tp = taps + col * W;
-      for (int j = 0; j < W && t - j >= s0; ++j) {
-        float xv[8];
-        load8<IO>(x, (t - j) * H * D + col, xv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += tp[e * W + j] * xv[e];
+      for (int j = 0; j < kMaxWidth; ++j) {  // all loads issued together
+        if (j < W && t - j >= s0) {
+          float xv[8];
+          load8<IO>(x, (t - j) * H * D + col, xv);
+          const float* tj = st + j * D + 8 * g;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += tj[e] * xv[e];
+        }
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = acc[e] / (1.f + expf(-acc[e]));

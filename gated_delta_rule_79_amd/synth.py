@@ -282,6 +282,14 @@ WORKLOADS = {
 }
 
 
+def conv_taps(H: int, dk: int, dv: int, W: int, seed: int):
+    """Short-convolution taps (q, k, v) for gdn_chunk_fwd_conv: fp32 [H, d, W]
+    drawn from N(0, 1 / W) on a stream of their own (PCG64(seed + 6007))."""
+    r = np.random.Generator(np.random.PCG64(seed + 6007))
+    mk = lambda d: torch.from_numpy(r.standard_normal((H, d, W)) / np.sqrt(W)).float()
+    return mk(dk), mk(dk), mk(dv)
+
+
 def workload(name: str, **overrides) -> Inputs:
     kw = dict(WORKLOADS[name])
     kw.update(overrides)

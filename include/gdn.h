@@ -217,8 +217,10 @@ gdn_status gdn_chunk_fwd_qknorm(const gdn_problem* p, const void* q, const void*
  * (causal and depthwise; tap j weighs the input j tokens back; no history
  * before a sequence's first token, so packed sequences never see each
  * other; no bias), q and k rows are then L2-normalised, and gdn_chunk_fwd
- * runs on the results, which a prologue pass writes into the workspace in
- * the input dtype.
+ * runs on the results.  With the scalar gate or no gate the k and v rows are
+ * convolved (and k normalised) as the forward stages each chunk, and only q
+ * goes through a prologue pass that writes it into the workspace in the
+ * input dtype; with the per-channel gate the prologue pass writes all three.
  *   width       : taps per channel, 1 .. 8 (else GDN_ERR_UNSUPPORTED).
  *   xq, xk      : [B, T, H, dk] io_dtype;  xv : [B, T, H, dv] io_dtype.
  *   wq, wk      : [H, dk, width] fp32;     wv : [H, dv, width] fp32.

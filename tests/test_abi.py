@@ -406,18 +406,33 @@ def test_gdn2_validation_before_launch(lib):
     assert lib.gdn2_decode_step(None, A, A, A, A, A, A, A, A, None) == 1
 
 
-def test_conv_forward_validation(lib):
-    """gdn_chunk_fwd_conv: width 1..8, taps required, workspace = three
-    prologue tensors on top of the forward's."""
+def test_conv_forward_validation(lib, capfd, monkeypatch):
+    """gdn_chunk_fwd_conv: width 1..8, taps required; workspace = the q
+    prologue rows on top of the forward's (per-token gates: the prep
+    convolves k and v itself), all three rows with the per-channel gate."""
+    al = lambda x: (x + 255) // 256 * 256
+    for gate, extra in ((_lib.GDN_GATE_SCALAR, al(100 * 2 * 128 * 2)),
+                        (_lib.GDN_GATE_NONE, al(100 * 2 * 128 * 2)),
+                        (_lib.GDN_GATE_CHANNEL, 2 * al(100 * 2 * 128 * 2) + al(100 * 2 * 64 * 2))):
+        pg = prob(T=100, dv=64, gate=gate)
+        m, f = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        assert lib.gdn_chunk_fwd_conv_workspace(ctypes.byref(pg), 4, ctypes.byref(m)) == 0
+        assert lib.gdn_chunk_fwd_workspace(ctypes.byref(pg), ctypes.byref(f)) == 0
+        assert m.value == f.value + extra, gate
+        # the dispatch line names the fused width (0: separate prologue passes)
+        monkeypatch.setenv("GDN_LOG", "1")
+        st = lib.gdn_chunk_fwd_conv(ctypes.byref(pg), 4, A, A, A, A, A, A, A, A, None, A, None,
+                                    A, m.value, None)
+        monkeypatch.delenv("GDN_LOG")
+        assert st == _lib.GDN_ERR_HIP
+        line = capfd.readouterr().err.strip().splitlines()[0]
+        want = 0 if gate == _lib.GDN_GATE_CHANNEL else 4
+        assert f"conv_width={want} " in line, line
     p = prob(T=100, dv=64)
     n = ctypes.c_size_t(0)
     assert lib.gdn_chunk_fwd_conv_workspace(ctypes.byref(p), 0, ctypes.byref(n)) == 4
     assert lib.gdn_chunk_fwd_conv_workspace(ctypes.byref(p), 9, ctypes.byref(n)) == 4
     assert lib.gdn_chunk_fwd_conv_workspace(ctypes.byref(p), 4, ctypes.byref(n)) == 0
-    f = ctypes.c_size_t(0)
-    assert lib.gdn_chunk_fwd_workspace(ctypes.byref(p), ctypes.byref(f)) == 0
-    al = lambda x: (x + 255) // 256 * 256
-    assert n.value == f.value + 2 * al(100 * 2 * 128 * 2) + al(100 * 2 * 64 * 2)
 
     def call(width=4, wq=A, wk=A, wv=A, xq=A, nbytes=None):
         return lib.gdn_chunk_fwd_conv(ctypes.byref(p), width, xq, A, A, wq, wk, wv, A, A,

@@ -27,9 +27,18 @@ def _asan_runtime():
     return path if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path) else None
 
 
+def _stale(lib):
+    srcs = [os.path.join(build.CSRC, f) for f in os.listdir(build.CSRC)]
+    srcs += [os.path.join(build.INCLUDE, f) for f in os.listdir(build.INCLUDE)]
+    newest = max(os.path.getmtime(f) for f in srcs if f.endswith((".hip", ".hpp", ".h")))
+    return os.path.getmtime(lib) < newest
+
+
 def test_abi_under_sanitizers():
     if not os.path.exists(build.ASAN_LIB):
         pytest.skip("host-sanitized library not built (build.py --sanitize)")
+    if _stale(build.ASAN_LIB):
+        pytest.skip("host-sanitized library older than the sources (build.py --sanitize)")
     rt = _asan_runtime()
     if rt is None:
         pytest.skip("AddressSanitizer runtime not found")

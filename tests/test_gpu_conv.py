@@ -22,12 +22,6 @@ from gpu_util import TOL, log, np64, par_map, slice_err, state_err
 pytestmark = pytest.mark.gpu
 
 
-def taps(H, dk, dv, W, seed):
-    r = np.random.Generator(np.random.PCG64(seed + 6007))
-    mk = lambda d: torch.from_numpy(r.standard_normal((H, d, W)) / np.sqrt(W)).float()
-    return mk(dk), mk(dk), mk(dv)
-
-
 def inputs(B, T, H, dk, dv, W, seed, **kw):
     """make_inputs' problem, with its q, k, v used as the projections and
     taps of width W."""
@@ -38,7 +32,7 @@ def inputs(B, T, H, dk, dv, W, seed, **kw):
         t = getattr(inp, name)
         setattr(inp, name, (t.float() * sc).to(t.dtype))
         inp.f64[name] = getattr(inp, name).double().numpy()
-    return inp, taps(H, dk, dv, W, seed)
+    return inp, synth.conv_taps(H, dk, dv, W, seed)
 
 
 def run(inp, w, **kw):
