@@ -49,5 +49,6 @@ from .gdn_oracle import (  # noqa: F401
     short_conv,
     silu,
     conv_prologue,
+    conv_prologue_bwd,
     gdn_fwd_conv,
 )

@@ -58,7 +58,8 @@ Parity pins (tests/test_oracle_pins.py): chunked brute-force form, orthonormal
 retrieval, beta = 0 gate product, DeltaNet limit, norm bound, alpha -> 0
 erasure, gated-linear-attention limit, SGD reading, T = 1 closed form,
 equal-channel reduction, boundary semantics, finite differences for the
-adjoint, plus a hand-worked golden example.  Nothing here is "parity
+adjoint and for the prologue path's adjoint, plus a hand-worked golden
+example.  Nothing here is "parity
 unpinned" except the matches of the per-channel gate, the Householder
 products, the draft trees and Gated DeltaNet-2 to external definitions.
 """
@@ -231,6 +232,46 @@ def conv_prologue(x, taps, normalize, cu_seqlens=None):
     the L2 normalisation per (token, head)."""
     y = silu(short_conv(x, taps, cu_seqlens))
     return l2_normalize(y) if normalize else y
+
+
+def conv_prologue_bwd(x, taps, normalize, dy, cu_seqlens=None):
+    """Adjoint of :func:`conv_prologue`: the gradients of
+    L = sum dy * conv_prologue(x, taps, normalize) with respect to x [B,T,H,D]
+    and taps [H,D,W], taking the path's three steps back in reverse order:
+
+      y = a / |a|        da = (dy - y (y . dy)) / |a|   (an all-zero row: 0)
+      a = z sigmoid(z)   dz = da (s + a (1 - s)),  s = sigmoid(z)
+      z[t] = sum_j taps[:, :, j] x[t - j]  (inside each sequence)
+                         dx[t - j] += taps[:, :, j] dz[t]
+                         dtaps[:, :, j] += dz[t] x[t - j]
+
+    The pages define the forward path only; this is its chain rule.
+    Returns (dx, dtaps)."""
+    x = np.asarray(x, dtype=np.float64)
+    taps = np.asarray(taps, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    B, T, H, D = x.shape
+    W = taps.shape[-1]
+    z = short_conv(x, taps, cu_seqlens)
+    sg = 1.0 / (1.0 + np.exp(-z))
+    a = z * sg
+    if normalize:
+        n = np.sqrt(np.sum(a * a, axis=-1, keepdims=True))
+        y = np.divide(a, n, out=np.zeros_like(a), where=n > 0)
+        proj = dy - y * np.sum(y * dy, axis=-1, keepdims=True)
+        da = np.divide(proj, n, out=np.zeros_like(a), where=n > 0)
+    else:
+        da = dy
+    dz = da * (sg + a * (1.0 - sg))
+    dx = np.zeros_like(x)
+    dtaps = np.zeros_like(taps)
+    for b, t0, t1, _ in _segments(B, T, cu_seqlens):
+        for t in range(t0, t1):
+            for j in range(W):
+                if t - j >= t0:
+                    dx[b, t - j] += taps[:, :, j] * dz[b, t]
+                    dtaps[:, :, j] += dz[b, t] * x[b, t - j]
+    return dx, dtaps
 
 
 def gdn_fwd_conv(xq, xk, xv, wq, wk, wv, beta, log_alpha, s0=None,

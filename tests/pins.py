@@ -516,3 +516,49 @@ def silu_identities(silu):
                abs(one[1] - 1.0 / (1.0 + np.exp(-1.0))),
                abs(one[2] - 40.0) / 40.0,
                abs(one[3]))
+
+
+# ------------------------------------- adjoint of the prologue path ---
+# Checked against central finite differences of the forward path (a
+# callable with the signature of oracle.conv_prologue) and a closed form.
+
+def prologue_bwd_fd(bwd, fwd, normalize, varlen, seed=46, W=3, eps=1e-6):
+    """Largest error of the adjoint's dx and dtaps against central finite
+    differences of L = sum dy * fwd(x, taps), relative to the gradient's
+    largest entry.  varlen: two packed sequences (5 and 4 tokens)."""
+    r = rng(seed)
+    T, H, D = 9, 2, 3
+    cu = np.array([0, 5, 9]) if varlen else None
+    x = r.standard_normal((1, T, H, D))
+    w = r.standard_normal((H, D, W))
+    dy = r.standard_normal((1, T, H, D))
+    dx, dw = bwd(x, w, normalize, dy, cu)
+    L = lambda xx, ww: float(np.sum(dy * fwd(xx, ww, normalize, cu)))
+
+    def fd(arr, which):
+        g = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            p, m = arr.copy(), arr.copy()
+            p[i] += eps
+            m[i] -= eps
+            g[i] = (L(p, w) - L(m, w)) / (2 * eps) if which == "x" else \
+                   (L(x, p) - L(x, m)) / (2 * eps)
+        return g
+
+    gx, gw = fd(x, "x"), fd(w, "w")
+    return max(np.max(np.abs(dx - gx)) / np.max(np.abs(gx)),
+               np.max(np.abs(dw - gw)) / np.max(np.abs(gw)))
+
+
+def prologue_bwd_width_one(bwd, seed=47):
+    """Width 1 with unit taps and no normalisation: y = silu(x), so
+    dx = dy silu'(x) and dtaps = sum_t dy silu'(x) x, with
+    silu'(x) = s (1 + x (1 - s)), s = 1 / (1 + e^-x)."""
+    r = rng(seed)
+    x = r.standard_normal((2, 6, 2, 4))
+    dy = r.standard_normal((2, 6, 2, 4))
+    s = 1.0 / (1.0 + np.exp(-x))
+    d = dy * s * (1.0 + x * (1.0 - s))
+    dx, dw = bwd(x, np.ones((2, 4, 1)), False, dy, None)
+    return max(np.max(np.abs(dx - d)),
+               np.max(np.abs(dw[:, :, 0] - np.sum(d * x, axis=(0, 1)))))

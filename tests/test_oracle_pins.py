@@ -464,3 +464,25 @@ def test_conv_forward_composes_the_paths():
     o2, s2 = oracle.gdn_fwd(path(xq, wq, True), path(xk, wk, True), path(xv, wv, False),
                             beta, la, None, "scalar")
     assert np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(s - s2)) < 1e-12
+
+
+# ------------------------------------- adjoint of the prologue path ---
+
+@pytest.mark.parametrize("normalize", [True, False])
+@pytest.mark.parametrize("varlen", [False, True])
+def test_prologue_bwd_matches_finite_differences(normalize, varlen):
+    assert pins.prologue_bwd_fd(oracle.conv_prologue_bwd, oracle.conv_prologue,
+                                normalize, varlen) < 1e-7
+
+
+def test_prologue_bwd_width_one_closed_form():
+    assert pins.prologue_bwd_width_one(oracle.conv_prologue_bwd) < 1e-14
+
+
+def test_prologue_bwd_zero_row_has_zero_gradient():
+    # zero taps make every row zero; the normalised path's rows stay zero and
+    # their gradient reaching x is zero; dtaps still sees dy through SiLU'(0)
+    r = pins.rng(48)
+    x, dy = r.standard_normal((1, 5, 1, 3)), r.standard_normal((1, 5, 1, 3))
+    dx, dw = oracle.conv_prologue_bwd(x, np.zeros((1, 3, 2)), True, dy)
+    assert np.all(dx == 0.0) and np.all(dw == 0.0)

@@ -297,3 +297,40 @@ def test_reference_oracle_passes_conv_pins():
 @pytest.mark.parametrize("name", sorted(CONV_MUTANTS))
 def test_conv_mutant_is_caught(name):
     assert not _conv_pins_pass(_mutant(*CONV_MUTANTS[name]))
+
+
+# ------------------------------------- adjoint of the prologue path ---
+
+def _prologue_bwd_pins_pass(mod):
+    ok = True
+    for normalize in (True, False):
+        for varlen in (False, True):
+            ok &= pins.prologue_bwd_fd(mod.conv_prologue_bwd, ref_mod.conv_prologue,
+                                       normalize, varlen) < 1e-7
+    ok &= pins.prologue_bwd_width_one(mod.conv_prologue_bwd) < 1e-14
+    return bool(ok)
+
+
+PROLOGUE_BWD_MUTANTS = {
+    "norm projection sign flipped": (
+        "        proj = dy - y * np.sum(y * dy, axis=-1, keepdims=True)\n",
+        "        proj = dy + y * np.sum(y * dy, axis=-1, keepdims=True)\n"),
+    "SiLU derivative without its second term": (
+        "    dz = da * (sg + a * (1.0 - sg))\n",
+        "    dz = da * sg\n"),
+    "convolution adjoint reversed in time": (
+        "                    dx[b, t - j] += taps[:, :, j] * dz[b, t]\n",
+        "                    dx[b, t - j] += taps[:, :, W - 1 - j] * dz[b, t]\n"),
+    "tap gradient against the current token": (
+        "                    dtaps[:, :, j] += dz[b, t] * x[b, t - j]\n",
+        "                    dtaps[:, :, j] += dz[b, t] * x[b, t]\n"),
+}
+
+
+def test_reference_oracle_passes_prologue_bwd_pins():
+    assert _prologue_bwd_pins_pass(ref_mod)
+
+
+@pytest.mark.parametrize("name", sorted(PROLOGUE_BWD_MUTANTS))
+def test_prologue_bwd_mutant_is_caught(name):
+    assert not _prologue_bwd_pins_pass(_mutant(*PROLOGUE_BWD_MUTANTS[name]))
