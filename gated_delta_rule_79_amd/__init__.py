@@ -176,6 +176,79 @@ def chunk_fwd_conv(xq, xk, xv, wq, wk, wv, beta, log_alpha=None, s0=None, chunk:
     return o, sf
 
 
+def _prologue_problem(x, cu_seqlens):
+    """A problem whose dk or dv is x's channel count (the prologue entry
+    points read B, T, H, the dtype and the packing; dk, dv name d)."""
+    d = x.shape[-1]
+    dk = d if d in (16, 32, 64, 128) else 16
+    p = _lib.GdnProblem()
+    B, T, H = x.shape[:3]
+    nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    for name, val in dict(B=B, T=T, H=H, dk=dk, dv=d, chunk=64, nseq=nseq,
+                          cu_seqlens=_ptr(cu_seqlens), io_dtype=_dtype_code(x),
+                          gate_dtype=_lib.GDN_F32, gate=_lib.GDN_GATE_NONE,
+                          seg_chunks=0).items():
+        setattr(p, name, val)
+    return p
+
+
+def prologue_fwd(x, taps, normalize: bool, cu_seqlens=None):
+    """One projection's prologue (gdn_prologue_fwd): silu(conv(x)) and, with
+    normalize, its rows over |.|.  x [B,T,H,d]; taps [H,d,W] fp32."""
+    lib = _lib.load()
+    _check_cu(cu_seqlens, x)
+    if taps.dtype != torch.float32:
+        raise ValueError("taps must be fp32")
+    p = _prologue_problem(x, cu_seqlens)
+    y = torch.empty_like(x)
+    st = lib.gdn_prologue_fwd(ctypes.byref(p), x.shape[-1], taps.shape[-1], int(normalize),
+                              _ptr(x), _ptr(taps), _ptr(y), _stream(x.device))
+    _lib.check(st, "gdn_prologue_fwd")
+    return y
+
+
+def prologue_bwd(x, taps, dy, normalize: bool, cu_seqlens=None):
+    """Backward of :func:`prologue_fwd` (gdn_prologue_bwd): returns
+    (dx [B,T,H,d] in x's dtype, dtaps [H,d,W] fp32)."""
+    lib = _lib.load()
+    _check_cu(cu_seqlens, x)
+    if dy.shape != x.shape or dy.dtype != x.dtype:
+        raise ValueError("dy must match x")
+    if taps.dtype != torch.float32:
+        raise ValueError("taps must be fp32")
+    p = _prologue_problem(x, cu_seqlens)
+    d, w = x.shape[-1], taps.shape[-1]
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.gdn_prologue_bwd_workspace(ctypes.byref(p), d, w, ctypes.byref(need)),
+               "gdn_prologue_bwd_workspace")
+    ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=x.device)
+    dx = torch.empty_like(x)
+    dtaps = torch.empty(taps.shape, dtype=torch.float32, device=x.device)
+    st = lib.gdn_prologue_bwd(ctypes.byref(p), d, w, int(normalize), _ptr(x), _ptr(taps),
+                              _ptr(dy), _ptr(dx), _ptr(dtaps), _ptr(ws), ws.numel(),
+                              _stream(x.device))
+    _lib.check(st, "gdn_prologue_bwd")
+    return dx, dtaps
+
+
+def chunk_bwd_conv(xq, xk, xv, wq, wk, wv, beta, log_alpha, s0, do, ds_final=None,
+                   chunk: int = 64, cu_seqlens=None, need_ds0: bool = True):
+    """Backward of :func:`chunk_fwd_conv`: the three prologues again
+    (gdn_prologue_fwd), gdn_chunk_bwd on their outputs, then each path's
+    gdn_prologue_bwd.  Returns (dxq, dxk, dxv, dwq, dwk, dwv, dbeta,
+    dlog_alpha, ds0)."""
+    q = prologue_fwd(xq, wq, True, cu_seqlens)
+    k = prologue_fwd(xk, wk, True, cu_seqlens)
+    v = prologue_fwd(xv, wv, False, cu_seqlens)
+    dq, dk, dv, dbeta, dla, ds0 = chunk_bwd(q, k, v, beta, log_alpha, s0, do, ds_final,
+                                            chunk=chunk, cu_seqlens=cu_seqlens,
+                                            need_ds0=need_ds0)
+    dxq, dwq = prologue_bwd(xq, wq, dq, True, cu_seqlens)
+    dxk, dwk = prologue_bwd(xk, wk, dk, True, cu_seqlens)
+    dxv, dwv = prologue_bwd(xv, wv, dv, False, cu_seqlens)
+    return dxq, dxk, dxv, dwq, dwk, dwv, dbeta, dla, ds0
+
+
 def gdn2_chunk_fwd(q, k, v, erase, write, log_alpha=None, s0=None, chunk: int = 64,
                    cu_seqlens=None, output_final_state: bool = True,
                    workspace: Optional[torch.Tensor] = None, seg_chunks: int = 0):

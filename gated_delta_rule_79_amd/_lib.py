@@ -31,7 +31,8 @@ EXPORTED = (
     "gdn_chunk_fwd_qknorm", "gdn_tree_verify_workspace", "gdn_tree_verify",
     "gdn_tree_commit", "gdn_decode_step_product", "gdn_chunk_fwd_noalloc",
     "gdn2_chunk_fwd", "gdn2_decode_step", "gdn_chunk_fwd_qknorm_workspace",
-    "gdn_chunk_fwd_conv_workspace", "gdn_chunk_fwd_conv",
+    "gdn_chunk_fwd_conv_workspace", "gdn_chunk_fwd_conv", "gdn_prologue_fwd",
+    "gdn_prologue_bwd_workspace", "gdn_prologue_bwd",
 )
 STAGE_COUNT = 12
 STAGES = ("chunk_map", "fwd_prep", "fwd_scan", "decode", "bwd_states",
@@ -117,6 +118,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_chunk_fwd_conv_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
     lib.gdn_chunk_fwd_conv.restype = i32
     lib.gdn_chunk_fwd_conv.argtypes = [pp, i32] + [vp] * 12 + [sz, vp]
+    lib.gdn_prologue_fwd.restype = i32
+    lib.gdn_prologue_fwd.argtypes = [pp, i32, i32, i32, vp, vp, vp, vp]
+    lib.gdn_prologue_bwd_workspace.restype = i32
+    lib.gdn_prologue_bwd_workspace.argtypes = [pp, i32, i32, ctypes.POINTER(sz)]
+    lib.gdn_prologue_bwd.restype = i32
+    lib.gdn_prologue_bwd.argtypes = [pp, i32, i32, i32] + [vp] * 6 + [sz, vp]
     lib.gdn_tree_commit.restype = i32
     lib.gdn_tree_commit.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
     if path is None:

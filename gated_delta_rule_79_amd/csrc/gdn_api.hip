@@ -572,6 +572,75 @@ gdn_status gdn_chunk_fwd_conv(const gdn_problem* p, int32_t width, const void* x
 }
 
 // Draft trees: one tree per chunk, no segment split, per-token gates only.
+// The prologue entry points: d is the problem's dk or dv, widths 1 .. 8;
+// the normalised path needs d in {16, 32, 64, 128} (a row's lanes reduce by
+// shuffles).
+static gdn_status check_prologue(const gdn_problem* p, int32_t d, int32_t width,
+                                 int32_t normalize, gdn::Problem* out) {
+  GDN_TRY(check_chunk_problem(p, out));
+  if (d != out->dk && d != out->dv) return GDN_FAIL(GDN_ERR_SHAPE);
+  if (width < 1 || width > 8) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
+  if (normalize && !dk_ok(d)) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
+  return GDN_OK;
+}
+
+gdn_status gdn_prologue_fwd(const gdn_problem* p, int32_t d, int32_t width, int32_t normalize,
+                            const void* x, const float* taps, void* y, void* stream) {
+  GDN_ENTRY();
+  try {
+    gdn::Problem pp;
+    GDN_TRY(check_prologue(p, d, width, normalize, &pp));
+    const int64_t rows = static_cast<int64_t>(pp.B) * pp.T * pp.H;
+    GDN_TRY(need(x, rows * d));
+    GDN_TRY(need(y, rows * d));
+    GDN_TRY(need(taps, static_cast<int64_t>(pp.H) * d * width));
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
+    return launched(pp, gdn::launch_prologue(pp, d, width, x, taps, normalize != 0, y,
+                                             static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_FAIL(GDN_ERR_HIP);
+  }
+}
+
+gdn_status gdn_prologue_bwd_workspace(const gdn_problem* p, int32_t d, int32_t width,
+                                      size_t* bytes) {
+  GDN_ENTRY();
+  try {
+    if (bytes == nullptr) return GDN_FAIL(GDN_ERR_NULL);
+    gdn::Problem pp;
+    GDN_TRY(check_prologue(p, d, width, 0, &pp));
+    *bytes = gdn::prologue_bwd_workspace_bytes(pp, d, width);
+    return GDN_OK;
+  } catch (...) {
+    return GDN_FAIL(GDN_ERR_HIP);
+  }
+}
+
+gdn_status gdn_prologue_bwd(const gdn_problem* p, int32_t d, int32_t width, int32_t normalize,
+                            const void* x, const float* taps, const void* dy, void* dx,
+                            float* dtaps, void* ws, size_t ws_bytes, void* stream) {
+  GDN_ENTRY();
+  try {
+    gdn::Problem pp;
+    GDN_TRY(check_prologue(p, d, width, normalize, &pp));
+    const int64_t rows = static_cast<int64_t>(pp.B) * pp.T * pp.H;
+    GDN_TRY(need(x, rows * d));
+    GDN_TRY(need(dy, rows * d));
+    GDN_TRY(need(dx, rows * d));
+    GDN_TRY(need(taps, static_cast<int64_t>(pp.H) * d * width));
+    if (dtaps == nullptr) return GDN_FAIL(GDN_ERR_NULL);
+    GDN_TRY(opt(dtaps));
+    const size_t need_ws = gdn::prologue_bwd_workspace_bytes(pp, d, width);
+    if (ws == nullptr || ws_bytes < need_ws) return GDN_FAIL(GDN_ERR_WORKSPACE);
+    GDN_TRY(opt(ws));
+    if (g_fail_launch.load()) return launched(pp, hipErrorLaunchFailure);  // test hook
+    return launched(pp, gdn::launch_prologue_bwd(pp, d, width, x, taps, normalize != 0, dy, dx,
+                                                 dtaps, ws, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return GDN_FAIL(GDN_ERR_HIP);
+  }
+}
+
 static gdn_status check_tree(const gdn_problem* p, gdn::Problem* out) {
   if (p == nullptr) return GDN_FAIL(GDN_ERR_NULL);
   if (p->gate == GDN_GATE_CHANNEL) return GDN_FAIL(GDN_ERR_UNSUPPORTED);

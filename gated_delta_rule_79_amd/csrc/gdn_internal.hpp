@@ -83,6 +83,13 @@ hipError_t launch_tree_commit(const Problem& p, const int32_t* parent,
 // [B * T, H, D] in p.io.
 hipError_t launch_prologue(const Problem& p, int D, int W, const void* x, const float* taps,
                            bool normalize, void* y, hipStream_t s);
+// Adjoint of the prologue path (dz, then dx with per-block tap partials,
+// then the partials summed in block order); workspace: dz in fp32 and the
+// partials.
+size_t prologue_bwd_workspace_bytes(const Problem& p, int D, int W);
+hipError_t launch_prologue_bwd(const Problem& p, int D, int W, const void* x, const float* taps,
+                               bool normalize, const void* dy, void* dx, float* dtaps, void* ws,
+                               hipStream_t s);
 
 // Forward (gdn_fwd.hip).
 size_t fwd_workspace_bytes(const Problem& p);

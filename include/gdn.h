@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 typedef enum {
   GDN_OK = 0,
@@ -233,6 +233,35 @@ gdn_status gdn_chunk_fwd_conv(const gdn_problem* p, int32_t width, const void* x
                               const float* wk, const float* wv, const void* beta,
                               const void* log_alpha, const float* s0, void* o,
                               float* s_final, void* ws, size_t ws_bytes, void* stream);
+
+/* One projection's prologue on its own (the step gdn_chunk_fwd_conv applies
+ * to each of q, k, v; "Gated Delta Networks: Improving Mamba2 with Delta
+ * Rule", "Method"):  y = silu(conv(x)) with the causal depthwise convolution
+ * above, then y / |y| per (token, head) when normalize is non-zero.
+ *   d           : the channels of x and y, the problem's dk or dv (else
+ *                 GDN_ERR_SHAPE); with normalize, d in {16, 32, 64, 128}.
+ *   width       : 1 .. 8 (else GDN_ERR_UNSUPPORTED).
+ *   x, y        : [B, T, H, d] io_dtype (packed sequences as in the chunked
+ *                 calls, no history across a sequence start).
+ *   taps        : [H, d, width] fp32.
+ * Only B, T, H, dk, dv, io_dtype, nseq and cu_seqlens of the problem are
+ * used (its other fields must still be valid).  Errors as gdn_chunk_fwd. */
+gdn_status gdn_prologue_fwd(const gdn_problem* p, int32_t d, int32_t width, int32_t normalize,
+                            const void* x, const float* taps, void* y, void* stream);
+
+/* Backward of gdn_prologue_fwd: given dy = dL/dy, writes dx = dL/dx
+ * ([B, T, H, d] io_dtype) and dtaps = dL/dtaps ([H, d, width] fp32,
+ * overwritten).  The pages define the forward path only; this is its chain
+ * rule (the normalisation's projection, SiLU's derivative, the transposed
+ * convolution).  The tap gradient sums over every token in a fixed order
+ * (deterministic; no atomics).  Workspace: gdn_prologue_bwd_workspace bytes
+ * (the fp32 gradient before SiLU and per-block tap partials).  Errors as
+ * gdn_chunk_fwd; GDN_ERR_NULL for a NULL dtaps. */
+gdn_status gdn_prologue_bwd_workspace(const gdn_problem* p, int32_t d, int32_t width,
+                                      size_t* bytes);
+gdn_status gdn_prologue_bwd(const gdn_problem* p, int32_t d, int32_t width, int32_t normalize,
+                            const void* x, const float* taps, const void* dy, void* dx,
+                            float* dtaps, void* ws, size_t ws_bytes, void* stream);
 
 /* Householder-product transitions (the GDN review's "Future work" and its
  * closing section name products of Householder matrices as a way to graft

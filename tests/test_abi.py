@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 7
+    assert lib.gdn_abi_version() == 8
     for s in range(8):
         txt = lib.gdn_status_str(s).decode()
         assert txt.startswith("GDN_")
@@ -481,3 +481,40 @@ def test_log_names_refusals_and_dispatch(lib, capfd, monkeypatch):
     assert st == _lib.GDN_ERR_HIP
     line = capfd.readouterr().err.strip().splitlines()[0]
     assert line.startswith("gdn: gdn2_chunk_fwd: ") and "write_strength" in line, line
+
+
+def test_prologue_entry_points_validate(lib):
+    """gdn_prologue_fwd / gdn_prologue_bwd: d is the problem's dk or dv,
+    widths 1..8, the normalised path needs a power-of-two d up to 128; the
+    backward's workspace is the fp32 pre-SiLU gradient plus the per-block
+    tap partials (blocks of (256 / d) runs of 64 tokens)."""
+    p = prob(T=100, dk=64, dv=48)
+
+    def fwd_(d=64, width=4, norm=1, x=A, taps=A, y=A):
+        return lib.gdn_prologue_fwd(ctypes.byref(p), d, width, norm, x, taps, y, None)
+    assert fwd_() == _lib.GDN_ERR_HIP                  # valid: reaches the launch hook
+    assert fwd_(d=48, norm=0) == _lib.GDN_ERR_HIP
+    assert fwd_(d=32) == _lib.GDN_ERR_SHAPE           # neither dk nor dv
+    assert fwd_(width=0) == _lib.GDN_ERR_UNSUPPORTED
+    assert fwd_(width=9) == _lib.GDN_ERR_UNSUPPORTED
+    assert fwd_(d=48, norm=1) == _lib.GDN_ERR_UNSUPPORTED   # rows not a power of two
+    assert fwd_(x=None) == _lib.GDN_ERR_NULL
+    assert fwd_(taps=A + 4) == _lib.GDN_ERR_ALIGN
+
+    n = ctypes.c_size_t(0)
+    for d, w in ((64, 4), (48, 3)):
+        assert lib.gdn_prologue_bwd_workspace(ctypes.byref(p), d, w, ctypes.byref(n)) == 0
+        ntok, H = 100, 2
+        per = (256 // d) * 64
+        nblk = (ntok + per - 1) // per
+        assert n.value == (ntok * H * d * 4 + 255) // 256 * 256 + nblk * H * d * w * 4
+    assert lib.gdn_prologue_bwd_workspace(ctypes.byref(p), 64, 4, None) == _lib.GDN_ERR_NULL
+    assert lib.gdn_prologue_bwd_workspace(ctypes.byref(p), 64, 4, ctypes.byref(n)) == 0
+
+    def bwd_(dtaps=A, nbytes=None, dy=A):
+        return lib.gdn_prologue_bwd(ctypes.byref(p), 64, 4, 1, A, A, dy, A, dtaps, A,
+                                    n.value if nbytes is None else nbytes, None)
+    assert bwd_() == _lib.GDN_ERR_HIP
+    assert bwd_(dtaps=None) == _lib.GDN_ERR_NULL
+    assert bwd_(dy=None) == _lib.GDN_ERR_NULL
+    assert bwd_(nbytes=n.value - 1) == _lib.GDN_ERR_WORKSPACE
