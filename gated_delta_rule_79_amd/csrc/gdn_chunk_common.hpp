@@ -168,6 +168,45 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes
                                            static_cast<int>(bytes), kBufFlags);
 }
 
+// An offset past every range set up here: such a load reads zero and
+// touches no memory.
+constexpr uint32_t kOob = 0x80000000u;
+
+// 16 bytes at byte offset `off` of a buffer (zero when out of range).
+__device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// 8 consecutive operand elements at byte offset `off` of a buffer.
+template <typename OP>
+__device__ inline opvec<OP> bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (opstore<OP>::bytes == 2) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  } else {
+    const floatx4 x = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    const floatx4 y =
+        __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+    return floatx8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  }
+}
+
+// A gate value (bf16 or fp32 by a run-time flag) requested without a branch:
+// both widths are loaded, the other one from an empty range, so no wait for
+// the data is placed before gate_value() uses it.  Element `i` of the `n`
+// elements at p; i >= n reads zero.
+struct RawGate {
+  uint16_t h16;
+  uint32_t f32;
+};
+__device__ inline RawGate gate_issue(const void* p, uint32_t n, uint32_t i, bool bf16) {
+  const uint32_t j = i < n ? i : kOob / 4;
+  return {__builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p, bf16 ? 2 * n : 0), 2 * j, 0, 0),
+          __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p, bf16 ? 0 : 4 * n), 4 * j, 0, 0)};
+}
+__device__ inline float gate_value(const RawGate& g, bool bf16) {
+  return bf16 ? bf16_bits_to_float(g.h16) : __uint_as_float(g.f32);
+}
+
 // Two runs of 4 operand elements at byte offsets a and b of a buffer.
 template <typename OP>
 __device__ inline opvec<OP> bload4x2(__amdgpu_buffer_rsrc_t r, uint32_t a, uint32_t b) {

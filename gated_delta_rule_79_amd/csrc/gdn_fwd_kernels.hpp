@@ -1044,8 +1044,7 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
   const int64_t ch = static_cast<int64_t>(h) * nchunks + c;
 
   // jobs: the NT2 lower tiles of A (diagonal included), then the P
-  // fragments (rt, jb) with 32 jb <= 16 rt + 15; their q rows are
-  // requested first
+  // fragments (rt, jb) with 32 jb <= 16 rt + 15
   constexpr int NT2 = NB * (NB + 1) / 2;
   constexpr int NPF = NB == 1 ? 1 : (NB == 2 ? 2 : 6);
   constexpr int JOBS = NT2 + NPF;
@@ -1061,27 +1060,27 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
     }
   };
   const int nhm = (1 << lnh) - 1;
+  // The staging loads are raw buffer loads over this chunk and head (rows
+  // past the chunk, or given the out-of-range offset, read as zero): with no
+  // branch around them, each wait for data sits at its first use.
   // q row of step r: the token's q on its last step, zero elsewhere
-  auto q_row_frag = [&](int r, int k0) -> opvec<OP> {
+  const int64_t qt0 = tok0 >> lnh;
+  const uint32_t krow = static_cast<uint32_t>(H) * DK * ib;  // bytes between tokens
+  const auto rq = make_rsrc(static_cast<const char*>(q) + (qt0 * H + h) * DK * ib,
+                            static_cast<uint32_t>(((tok0 + len - 1) >> lnh) - qt0) * krow +
+                                DK * ib);
+  auto q_row_frag = [&](int r, int k0, bool want) -> opvec<OP> {
     const int64_t t = tok0 + r;
-    if (r >= len || k0 >= DK || (t & nhm) != nhm) return zero_vec<OP>();
-    return gload8<IO>(q, ((t >> lnh) * H + h) * DK + k0);
+    const bool on = want && r < len && k0 < DK && (t & nhm) == nhm;
+    return bload8<OP>(rq, on ? static_cast<uint32_t>((t >> lnh) - qt0) * krow + k0 * ib : kOob);
   };
   opvec<OP> qpre[MAXJ][NKD];
-#pragma unroll
-  for (int u = 0; u < MAXJ; ++u) {
-    const int job = wave + PW * u;
-    if (job >= NT2 && job < JOBS) {
-      int rt = 0, jb = 0;
-      p_job(job, &rt, &jb);
-#pragma unroll
-      for (int kb = 0; kb < NKD; ++kb)
-        qpre[u][kb] = q_row_frag(16 * rt + l16, kb * 32 + lg * 8);
-    }
-  }
 
-  // ---- 0. K rows and the first V columns into LDS; beta and base-2
-  //      cumulative log gate.  Every load is issued before any store.
+  // ---- 0. K rows into LDS; beta and base-2 cumulative log gate.  The
+  //      loads go out in the order their data is needed: the gate values,
+  //      K (LDS, before step 1), the P jobs' q rows (step 1, after the A
+  //      tiles), then the first V columns, which are only written to LDS
+  //      after step 2, so that neither q nor V holds up the K stores.
   constexpr int KP = DK * ib / 16;             // 16-byte pieces per K row
   constexpr int VPM = S::VCOLS * ib / 16;      // pieces per staged V row
   constexpr int NKL = (C * KP + NT - 1) / NT;   // K pieces per thread
@@ -1128,8 +1127,9 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
 #pragma unroll
     for (int s2 = 0; s2 < VE; ++s2) acc[s2] = acc[s2] / (1.f + expf(-acc[s2]));
   };
-  auto stage_v = [&](int c0) {
-    // columns [c0, c0 + VCOLS) of V; pieces past dv or the chunk are zero
+  // columns [c0, c0 + VCOLS) of V into registers; pieces past dv or the
+  // chunk are zero
+  auto load_v = [&](int c0, uint4* raw) {
     const int VP = min(S::VCOLS, dv - c0) * ib / 16;
     const int nvc = min(S::VCOLS, dv - c0);
     if constexpr (CONV) {
@@ -1138,34 +1138,66 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
         __syncthreads();
       }
     }
-    uint4 raw[NVL];
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
       const int e = tid + NT * u;
       const int r = e / VPM, pc = e % VPM;
-      raw[u] = make_uint4(0, 0, 0, 0);
-      if (e < C * VPM && r < len && pc < VP) {
-        if constexpr (CONV) {
+      if constexpr (CONV) {
+        raw[u] = make_uint4(0, 0, 0, 0);
+        if (e < C * VPM && r < len && pc < VP) {
           float x[16 / ib];
           conv_piece(v, stv, nvc, dv, c0 + pc * (16 / ib), c0, r, x);
           raw[u] = pack16<IO>(x);
-        } else
-          raw[u] = *reinterpret_cast<const uint4*>(
-              static_cast<const char*>(v) +
-              (((tok0 + r) * H + h) * static_cast<int64_t>(dv) + c0) * ib + pc * 16);
+        }
+      } else {
+        const uint32_t vrow = static_cast<uint32_t>(H) * dv * ib;
+        const auto rv = make_rsrc(
+            static_cast<const char*>(v) + ((tok0 * H + h) * static_cast<int64_t>(dv) + c0) * ib,
+            (len - 1) * vrow + (dv - c0) * ib);
+        raw[u] = bload16(rv, e < C * VPM && pc < VP ? r * vrow + pc * 16 : kOob);
       }
     }
+  };
+  auto store_v = [&](const uint4* raw) {
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
       const int e = tid + NT * u;
       if (e < C * VPM) *reinterpret_cast<uint4*>(sV + (e / VPM) * LDVB + (e % VPM) * 16) = raw[u];
     }
   };
+  auto stage_v = [&](int c0) {
+    uint4 raw[NVL];
+    load_v(c0, raw);
+    store_v(raw);
+  };
   if constexpr (CONV) {
     stage_taps(stk, ctk, DK, 0, DK);
     stage_taps(stv, ctv, dv, 0, min(S::VCOLS, dv));
     __syncthreads();
   }
+  // wave 0, lane = row: beta, the write strength (decoupled erase / write;
+  // U only) and the base-2 log gate
+  // (every wave requests them, so that no branch separates the requests
+  // from wave 0's use)
+  RawGate rgb{}, rgw{}, rgx{};
+  {
+    const int gsz = gbf ? 2 : 4;
+    const uint32_t n = static_cast<uint32_t>(len - 1) * H + 1;
+    const int64_t at = (tok0 * H + h) * gsz;
+    rgb = gate_issue(static_cast<const char*>(beta) + at, n, lane * H, gbf);
+    rgw = gate_issue(static_cast<const char*>(beta_w != nullptr ? beta_w : beta) + at,
+                     beta_w != nullptr ? n : 0, lane * H, gbf);
+    if constexpr (GATE == GDN_GATE_SCALAR) {
+      // the decay acts on a token's first step
+      const int64_t t = tok0 + lane;
+      const uint32_t nx = static_cast<uint32_t>(((tok0 + len - 1) >> lnh) - qt0) * H + 1;
+      rgx = gate_issue(static_cast<const char*>(la) + (qt0 * H + h) * gsz, nx,
+                       lane < len && (t & nhm) == 0 ? static_cast<uint32_t>((t >> lnh) - qt0) * H
+                                                    : nx,
+                       gbf);
+    }
+  }
+  uint4 vraw[NVL];  // the first V columns (not with the fused convolution)
   {
     uint4 raw[NKL];
     float kc[CONV ? NKL : 1][16 / ib];  // convolved K pieces, unrounded until normalised
@@ -1177,16 +1209,29 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
       if constexpr (CONV) {
 #pragma unroll
         for (int s2 = 0; s2 < 16 / ib; ++s2) kc[u][s2] = 0.f;
-      }
-      if (e < C * KP && r < len) {
-        if constexpr (CONV)
-          conv_piece(k, stk, DK, DK, pc * (16 / ib), 0, r, kc[u]);
-        else
-          raw[u] = *reinterpret_cast<const uint4*>(
-              static_cast<const char*>(k) + ((tok0 + r) * H + h) * DK * ib + pc * 16);
+        if (e < C * KP && r < len) conv_piece(k, stk, DK, DK, pc * (16 / ib), 0, r, kc[u]);
+      } else {
+        const auto rk = make_rsrc(static_cast<const char*>(k) + (tok0 * H + h) * DK * ib,
+                                  (len - 1) * krow + DK * ib);
+        raw[u] = bload16(rk, e < C * KP ? r * krow + pc * 16 : kOob);
       }
     }
-    stage_v(0);
+    // every slot is requested (slots of A jobs out of range), so that the
+    // K stores wait for K alone on every wave
+#pragma unroll
+    for (int u = 0; u < MAXJ; ++u) {
+      const int job = wave + PW * u;
+      const bool pj = job >= NT2 && job < JOBS;
+      int rt = 0, jb = 0;
+      p_job(pj ? job : NT2, &rt, &jb);
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb)
+        qpre[u][kb] = q_row_frag(16 * rt + l16, kb * 32 + lg * 8, pj);
+    }
+    if constexpr (CONV)
+      stage_v(0);
+    else
+      load_v(0, vraw);
     if (qkn || CONV) {
       // the KP pieces of a row sit in KP aligned consecutive lanes
       static_assert(KP <= 64 && (KP & (KP - 1)) == 0, "K row pieces per wave");
@@ -1241,14 +1286,10 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
   }
   float bw = 0.f;  // decoupled erase / write: the write strength (U only)
   if (wave == 0) {
-    float x = 0.f, b = 0.f;
-    if (lane < len) {
-      b = load_gate(beta, (tok0 + lane) * H + h, gbf);
-      if (beta_w != nullptr) bw = load_gate(beta_w, (tok0 + lane) * H + h, gbf);
-      if constexpr (GATE == GDN_GATE_SCALAR)
-        if (((tok0 + lane) & nhm) == 0)  // the decay acts on a token's first step
-          x = load_gate(la, ((tok0 + lane) >> lnh) * H + h, gbf) * kLog2e;
-    }
+    float x = 0.f;
+    const float b = gate_value(rgb, gbf);
+    bw = gate_value(rgw, gbf);  // zero without a write strength
+    if constexpr (GATE == GDN_GATE_SCALAR) x = gate_value(rgx, gbf) * kLog2e;
     if (!tree) {
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -1428,6 +1469,12 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
     }
   }
   __syncthreads();
+
+  if constexpr (!CONV) {
+    // the first V columns; step 6 reads them behind step 3's barriers
+    store_v(vraw);
+    if constexpr (NB < 2) __syncthreads();
+  }
 
   // ---- 3. blocks below the diagonal, one diagonal d = b - a at a time ---
   for (int d = 1; d < NB; ++d) {
