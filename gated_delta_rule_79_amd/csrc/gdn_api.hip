@@ -135,6 +135,23 @@ gdn_status check_chunk_problem(const gdn_problem* p, gdn::Problem* out, int lnh 
   return GDN_OK;
 }
 
+// The backward's problem.  The gradient kernel's LDS plan for fp32 rows with
+// the per-channel gate at dk = 128 does not fit a 64-token chunk; the
+// gradients are those of the recurrence whatever the chunk length (only the
+// order of rounding differs), so that case runs on 32-token chunks, with a
+// fixed segment length kept at the same number of tokens.
+gdn_status check_bwd_problem(const gdn_problem* p, gdn::Problem* out) {
+  GDN_TRY(check_chunk_problem(p, out));
+  if (gdn::bwd_supported(*out)) return GDN_OK;
+  if (p->chunk != 64) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
+  gdn_problem half = *p;
+  half.chunk = 32;
+  if (half.seg_chunks > 0) half.seg_chunks = half.seg_chunks > (1 << 29) ? (1 << 30) : 2 * half.seg_chunks;
+  GDN_TRY(check_chunk_problem(&half, out));
+  if (!gdn::bwd_supported(*out)) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
+  return GDN_OK;
+}
+
 gdn_status check_fwd_pointers(const gdn::Problem& p, const void* q,
                               const void* k, const void* v, const void* beta,
                               const void* la, const float* s0, const void* o,
@@ -767,8 +784,7 @@ gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes) {
   try {
     if (bytes == nullptr) return GDN_FAIL(GDN_ERR_NULL);
     gdn::Problem pp;
-    GDN_TRY(check_chunk_problem(p, &pp));
-    if (!gdn::bwd_supported(pp)) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
+    GDN_TRY(check_bwd_problem(p, &pp));
     *bytes = gdn::bwd_workspace_bytes(pp);
     return GDN_OK;
   } catch (...) {
@@ -785,8 +801,7 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k,
   GDN_ENTRY();
   try {
     gdn::Problem pp;
-    GDN_TRY(check_chunk_problem(p, &pp));
-    if (!gdn::bwd_supported(pp)) return GDN_FAIL(GDN_ERR_UNSUPPORTED);
+    GDN_TRY(check_bwd_problem(p, &pp));
     const int64_t tok = static_cast<int64_t>(pp.B) * pp.T * pp.H;
     GDN_TRY(need(q, tok * pp.dk));
     GDN_TRY(need(k, tok * pp.dk));

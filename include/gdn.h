@@ -369,11 +369,13 @@ gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes);
  *   dlog_alpha : fp32, shaped like log_alpha; NULL allowed for GATE_NONE.
  *   ds0      : [nseq, H, dk, dv] fp32 or NULL to skip.
  * The result is deterministic (no floating-point atomics).
- * Supported set: as gdn_chunk_fwd, except fp32 inputs (io_dtype GDN_F32)
- * with the per-channel gate at dk = 128 and chunk = 64, which return
- * GDN_ERR_UNSUPPORTED (the gradient kernel's LDS plan, fp32 rows and the
- * per-channel decays of a 64 x 128 chunk, does not fit in 160 KiB); chunk
- * 32 or bf16 inputs cover that case. */
+ * Supported set: as gdn_chunk_fwd.  For fp32 inputs (io_dtype GDN_F32) with
+ * the per-channel gate at dk = 128 and chunk = 64 the gradient kernel's LDS
+ * plan (fp32 rows and per-channel decays of a 64 x 128 chunk) does not fit
+ * in 160 KiB, so that case runs on 32-token chunks (a positive seg_chunks
+ * is doubled to keep its length in tokens): the gradients are the same
+ * function of the inputs, rounded in another order, and the workspace query
+ * returns that plan's size. */
 gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k,
                          const void* v, const void* beta,
                          const void* log_alpha, const float* s0,

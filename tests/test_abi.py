@@ -255,6 +255,28 @@ def test_bwd_validation(lib):
     assert lib.gdn_chunk_bwd(ctypes.byref(p), *bad, A, n.value, None) == _lib.GDN_ERR_NULL
 
 
+def test_bwd_fp32_channel_dk128_c64_runs_on_32_token_chunks(lib):
+    # the 64-token LDS plan does not fit fp32 rows with the per-channel gate
+    # at dk = 128: the backward takes that case on 32-token chunks, so its
+    # workspace is the 32-token plan's (a fixed segment length kept in tokens)
+    def bwd_ws(**kw):
+        p = prob(T=300, io_dtype=_lib.GDN_F32, gate_dtype=_lib.GDN_F32,
+                 gate=_lib.GDN_GATE_CHANNEL, **kw)
+        n = ctypes.c_size_t(0)
+        assert lib.gdn_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(n)) == 0
+        return n.value
+    assert bwd_ws(chunk=64) == bwd_ws(chunk=32) > 0
+    assert bwd_ws(chunk=64, seg_chunks=2) == bwd_ws(chunk=32, seg_chunks=4)
+    assert bwd_ws(chunk=64, seg_chunks=-1) == bwd_ws(chunk=32, seg_chunks=-1)
+    # bf16 rows keep their 64-token plan
+    p = prob(T=300, gate=_lib.GDN_GATE_CHANNEL)
+    q = prob(T=300, gate=_lib.GDN_GATE_CHANNEL, chunk=32)
+    n, m = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.gdn_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert lib.gdn_chunk_bwd_workspace(ctypes.byref(q), ctypes.byref(m)) == 0
+    assert n.value != m.value
+
+
 def test_python_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         _lib.load(str(tmp_path / "missing.so"))

@@ -96,12 +96,15 @@ def test_fp32_dk128_channel_small_chunk(gpu_lib):
     check(inp, "fp32_dk128_channel_C32")
 
 
-def test_fp32_dk128_channel_c64_unsupported(gpu_lib):
-    inp = synth.make_inputs(1, 70, 2, 128, 64, dtype=torch.float32, gate="channel",
-                            chunk=64, seed=33, with_do=True)
-    with pytest.raises(gdn.GdnError) as e:
-        run_bwd(inp)
-    assert e.value.status == 4  # GDN_ERR_UNSUPPORTED
+@pytest.mark.parametrize("seg", [0, 1])
+def test_fp32_dk128_channel_c64(gpu_lib, seg):
+    # the library runs this case on 32-token chunks (the 64-token LDS plan
+    # does not fit for fp32 rows); varlen with a ragged tail, and a fixed
+    # segment length that it rescales to the same number of tokens
+    inp = synth.make_inputs(1, 0, 2, 128, 64, dtype=torch.float32, gate="channel",
+                            chunk=64, seed=33, lengths=[150, 0, 70], s0_std=0.1,
+                            with_do=True, with_ds=True)
+    check(inp, "fp32_dk128_channel_C64", seg_chunks=seg)
 
 
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
