@@ -166,12 +166,17 @@ __global__ __launch_bounds__(128) void bwd_scan_kernel(
 #pragma unroll
       for (int a = 0; a < NDT; ++a) dM[a] = floatx4{0.f, 0.f, 0.f, 0.f};
     } else if (si.last) {
+      // the test on ds_final outside the loads, so that they issue together
+      if (ds_final != nullptr) {
 #pragma unroll
-      for (int a = 0; a < NDT; ++a)
+        for (int a = 0; a < NDT; ++a)
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          dM[a][s] = ds_final
-              ? ds_final[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col] : 0.f;
+          for (int s = 0; s < 4; ++s)
+            dM[a][s] = ds_final[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col];
+      } else {
+#pragma unroll
+        for (int a = 0; a < NDT; ++a) dM[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
     } else {
       const floatx4* src = reinterpret_cast<const floatx4*>(seg_in) + sl * NDT * 64;
 #pragma unroll
@@ -572,12 +577,16 @@ __global__ __launch_bounds__(64) void bwd_combine_kernel(
   const int64_t sbase = (static_cast<int64_t>(seq) * H + h) * DK * dv;
 
   floatx4 g[NDT];
+  if (ds_final != nullptr) {
 #pragma unroll
-  for (int a = 0; a < NDT; ++a)
+    for (int a = 0; a < NDT; ++a)
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      g[a][s] = ds_final ? ds_final[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col]
-                         : 0.f;
+      for (int s = 0; s < 4; ++s)
+        g[a][s] = ds_final[sbase + static_cast<int64_t>(16 * a + 4 * lg + s) * dv + col];
+  } else {
+#pragma unroll
+    for (int a = 0; a < NDT; ++a) g[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
   for (int j = se0 - 1; j > sb0; --j) {
     const size_t sh = static_cast<size_t>(j) * H + h;
     // Phi_j rows into LDS, element (r, c) at r * LP + c

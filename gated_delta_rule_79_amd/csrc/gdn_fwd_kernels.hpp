@@ -2306,12 +2306,19 @@ __global__ __launch_bounds__(64 * ((DK + 31) / 32)) void fwd_combine_kernel(
   const int col = 16 * vt + l16;
   const int64_t sbase = (static_cast<int64_t>(seq) * H + h) * DK * dv;
 
+  // the test on s0 outside the loads, so that they are issued together
+  // (a select per element made the compiler wait on each load in turn)
   floatx4 M[NT];
+  if (s0 != nullptr) {
 #pragma unroll
-  for (int u = 0; u < NT; ++u)
+    for (int u = 0; u < NT; ++u)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      M[u][e] = s0 ? s0[sbase + static_cast<int64_t>(16 * (t0 + u) + 4 * lg + e) * dv + col] : 0.f;
+      for (int e = 0; e < 4; ++e)
+        M[u][e] = s0[sbase + static_cast<int64_t>(16 * (t0 + u) + 4 * lg + e) * dv + col];
+  } else {
+#pragma unroll
+    for (int u = 0; u < NT; ++u) M[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   struct Ahead {
     opvec<OP> phi[NT][NKD];
