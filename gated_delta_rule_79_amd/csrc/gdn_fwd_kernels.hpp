@@ -2062,8 +2062,8 @@ __device__ __forceinline__ opvec<OP> q_frag_raw(const char* sq, int rt, int jb, 
 // the outputs transposed so that each lane ends up with 4 consecutive
 // columns of one token row (one 8-byte store in bf16).  The operands of the
 // transposed products are the same register fragments with the roles of A
-// and B swapped.  A chunk's stores are issued at the start of the next one,
-// so that the wait for the next chunk's copies never waits on them.
+// and B swapped.  A chunk's stores are issued at the start of the next
+// step, so they have the whole step to complete before the wait at its end.
 //
 // STATES = true (backward recomputation): no outputs; every chunk-start
 // state is stored into `states` ([chunk-head][DK][dv]) in the input dtype
@@ -2173,7 +2173,14 @@ void fwd_scan_kernel(
     copy_chunk<C, DK, OP, GATE, OUT, NTH, GS>(lds, buf, ch0 + j, ci, q, qp, H, h, ndvt, g0,
                                               nu, wave, lane, lnh);
   };
-  auto step = [&](const char* ops, int j) {
+  // The next chunk's copies (into buffer nxt, chunk jn >= 0) are issued
+  // between the chain and the output products: issued before the chain,
+  // the waves' copy instructions held up its start (the chain is the
+  // step's critical part); after it they overlap the output products, which
+  // read only this chunk's operands (headline: 27.5 -> 25.2 us).  Without
+  // outputs nothing follows the chain, so the copies go first.
+  auto step = [&](const char* ops, int j, char* nxt, int jn) {
+    if (!OUT && jn >= 0) copy(nxt, jn);
     if constexpr (STATES) {
       const int64_t st0 = (ch0 + j) * static_cast<int64_t>(DK) * dv;
 #pragma unroll
@@ -2190,6 +2197,7 @@ void fwd_scan_kernel(
     }
     opvec<OP> Mb[SPW][NKD], Eb[SPW][NKC];
     chain_lds<C, DK, OP, GATE, SPW, OUT, RAWQ, GS>(ops, M, has_u, us, Mb, Eb, lane, lg);
+    if (OUT && jn >= 0) copy(nxt, jn);
     if constexpr (OUT) {
       const ChunkInfo ci = chunk_info(map, si.c0 + j);
       const opvec<OP>* sQ = reinterpret_cast<const opvec<OP>*>(ops + L::oQ);
@@ -2231,14 +2239,12 @@ void fwd_scan_kernel(
     __syncthreads();
     for (int j = 0; j < n; j += 2) {
       store_out();
-      if (j + 1 < n) copy(sB, j + 1);
-      step(sA, j);
+      step(sA, j, sB, j + 1 < n ? j + 1 : -1);
       wait_vmcnt<0>();
       __syncthreads();
       if (j + 1 < n) {
         store_out();
-        if (j + 2 < n) copy(sA, j + 2);
-        step(sB, j + 1);
+        step(sB, j + 1, sA, j + 2 < n ? j + 2 : -1);
         wait_vmcnt<0>();
         __syncthreads();
       }
@@ -2250,7 +2256,7 @@ void fwd_scan_kernel(
       copy(sA, j);
       wait_vmcnt<0>();
       __syncthreads();
-      step(sA, j);
+      step(sA, j, nullptr, -1);
     }
   }
   store_out();
