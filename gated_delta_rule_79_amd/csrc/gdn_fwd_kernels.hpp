@@ -2002,6 +2002,21 @@ void fwd_trans_kernel(
   }
 
   const size_t sh = static_cast<size_t>(slot) * H + h;
+  // Phi leaves as operand fragments: lane holds Phi(16a + 4lg + e, pc), and
+  // operand fragment (a, jb) lane L' slot t stands for
+  // Phi(16a + L'%16, 32jb + perm_k(L'/16, t)), so a slab fills one half
+  // (slots 4 half ..) of every lane of the fragments (a, jb).  The wave
+  // scatters its values into an LDS image of the fragments and reads back
+  // the halves it owns, lane L' its own 8 bytes (bf16), which go out as one
+  // store per fragment instead of 32 two-byte stores per lane (the other half
+  // may belong to a slab of another wave or workgroup).  A wave's LDS
+  // accesses complete in order, so no barrier separates its writes from its
+  // reads; the one before keeps the image clear of the chunk buffers still
+  // being read.
+  using E = typename io<IO>::storage;
+  constexpr int FB = 8 * static_cast<int>(sizeof(E));  // bytes per fragment lane
+  constexpr bool STAGE = NDT * NKD * 64 * FB <= L::BYTES;
+  if constexpr (STAGE) __syncthreads();
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     if (!own[s]) continue;
@@ -2010,10 +2025,8 @@ void fwd_trans_kernel(
 #pragma unroll
       for (int a = 0; a < NDT; ++a) dst[a * 64 + lane] = M[s][a];
     } else {
-      // lane holds Phi(16a + 4lg + e, pc); operand fragment (a, jb) lane L'
-      // slot t stands for Phi(16a + L'%16, 32jb + perm_k(L'/16, t))
-      using E = typename io<IO>::storage;
-      E* dst = reinterpret_cast<E*>(sb.trp + sh * sb.trp_bytes);
+      char* dst = sb.trp + sh * sb.trp_bytes;
+      E* img = reinterpret_cast<E*>(STAGE ? sA : dst);
       const int cp = vt0 + s - ndvt, jb = cp >> 1, half = cp & 1;
       const int t = (l16 & 3) + 4 * half;
 #pragma unroll
@@ -2022,9 +2035,26 @@ void fwd_trans_kernel(
         for (int e = 0; e < 4; ++e) {
           const int Lp = 4 * lg + e + 16 * (l16 >> 2);
           const size_t off = ((static_cast<size_t>(a) * NKD + jb) * 64 + Lp) * 8;
-          io<IO>::store(dst, off + t, M[s][a][e]);
-          if (DK == 16) io<IO>::store(dst, off + t + 4, 0.f);  // K slots past DK
+          io<IO>::store(img, off + t, M[s][a][e]);
+          if (DK == 16) io<IO>::store(img, off + t + 4, 0.f);  // K slots past DK
         }
+      if constexpr (STAGE) {
+        // lane's own half (both halves when DK = 16: the second is zero)
+        constexpr int HB = DK == 16 ? FB : FB / 2;
+        const int hoff = DK == 16 ? 0 : half * (FB / 2);
+#pragma unroll
+        for (int a = 0; a < NDT; ++a) {
+          const size_t off = ((static_cast<size_t>(a) * NKD + jb) * 64 + lane) * FB + hoff;
+          if constexpr (HB == 8) {
+            *reinterpret_cast<uint2*>(dst + off) = *reinterpret_cast<const uint2*>(sA + off);
+          } else {
+            *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(sA + off);
+            if constexpr (HB == 32)
+              *reinterpret_cast<uint4*>(dst + off + 16) =
+                  *reinterpret_cast<const uint4*>(sA + off + 16);
+          }
+        }
+      }
     }
   }
 }
