@@ -1097,7 +1097,8 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
   // again in step 6, where both are dead: K's columns, then V's staged ones
   float* stk = reinterpret_cast<float*>(smem + S::tap_off);
   float* stv = stk + (CONV ? DK * cw : 0);
-  auto stage_taps = [&](float* dst, const float* taps, int D, int c0, int nc) {
+  auto stage_taps = [&](float* dst, const float* taps, int D, int c0,
+                        int nc) __attribute__((always_inline)) {
     for (int e = tid; e < nc * cw; e += NT) {
       const int c = e / cw, j = e - (e / cw) * cw;
       dst[j * nc + c] = taps[(static_cast<int64_t>(h) * D + c0 + c) * cw + j];
@@ -1107,7 +1108,7 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
   // convolved over rows r, r - 1, .. (not before the sequence start) with
   // the LDS taps st ([cw][nc], column col - c0), through SiLU
   auto conv_piece = [&](const void* x, const float* st, int nc, int D, int col, int c0, int r,
-                        float* acc) {
+                        float* acc) __attribute__((always_inline)) {
     constexpr int VE = 16 / ib;
 #pragma unroll
     for (int s2 = 0; s2 < VE; ++s2) acc[s2] = 0.f;
@@ -1128,8 +1129,11 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
     for (int s2 = 0; s2 < VE; ++s2) acc[s2] = acc[s2] / (1.f + expf(-acc[s2]));
   };
   // columns [c0, c0 + VCOLS) of V into registers; pieces past dv or the
-  // chunk are zero
-  auto load_v = [&](int c0, uint4* raw) {
+  // chunk are zero.  The staging lambdas are always inlined: stage_v, with
+  // the convolution and two call sites, was compiled as a call, which put
+  // every array it reaches (the K, V and q pieces) in scratch memory and
+  // doubled the convolution prep's time (headline shape: 113 -> 56 us)
+  auto load_v = [&](int c0, uint4* raw) __attribute__((always_inline)) {
     const int VP = min(S::VCOLS, dv - c0) * ib / 16;
     const int nvc = min(S::VCOLS, dv - c0);
     if constexpr (CONV) {
@@ -1158,14 +1162,14 @@ __global__ __launch_bounds__(64 * prep_waves(C)) void fwd_prep_sg_kernel(
       }
     }
   };
-  auto store_v = [&](const uint4* raw) {
+  auto store_v = [&](const uint4* raw) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
       const int e = tid + NT * u;
       if (e < C * VPM) *reinterpret_cast<uint4*>(sV + (e / VPM) * LDVB + (e % VPM) * 16) = raw[u];
     }
   };
-  auto stage_v = [&](int c0) {
+  auto stage_v = [&](int c0) __attribute__((always_inline)) {
     uint4 raw[NVL];
     load_v(c0, raw);
     store_v(raw);
