@@ -236,6 +236,16 @@ def test_segmented_state_recompute(gpu_lib, L, gate):
     check(inp, name=f"segmented L={L}", seg_chunks=L)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_segmented_phi_halves_from_different_workgroups(gpu_lib, dtype):
+    # dv = 144, dk = 128: the transition pass's first slab group ends inside
+    # Phi, so two workgroups write the halves of its last fragment column;
+    # the split reverse pass applies every segment's Phi^T
+    inp = synth.make_inputs(1, 400, 2, 128, 144, dtype=dtype, gate="scalar", chunk=32,
+                            seed=47, s0_std=0.1, with_do=True, with_ds=True)
+    check(inp, name="segmented phi halves", seg_chunks=2)
+
+
 def test_segmented_state_recompute_varlen_bf16(gpu_lib):
     inp = synth.make_inputs(1, 0, 2, 128, 128, dtype=torch.bfloat16, gate="scalar",
                             chunk=64, seed=42, s0_std=0.05, with_do=True, with_ds=True,

@@ -284,6 +284,21 @@ def test_segmented_bf16(gpu_lib, dk, dv, gate):
     check(inp, name="segmented_bf16", seg_chunks=3)
 
 
+# The transition pass writes a segment's map Phi as operand fragments, one
+# 8-byte half of a fragment lane per 16-column slab; with dv / 16 + dk / 16
+# slabs per (segment, head) in groups of 16, a fragment's two halves can come
+# from different waves (odd dv / 16) or different workgroups (dv = 144,
+# dk = 128: group 0 ends inside Phi).
+@pytest.mark.parametrize("dk,dv,dtype,C", [(128, 144, torch.bfloat16, 64),
+                                           (64, 208, torch.bfloat16, 32),
+                                           (64, 48, torch.bfloat16, 64),
+                                           (128, 144, torch.float32, 32)])
+def test_segmented_phi_halves_from_different_slabs(gpu_lib, dk, dv, dtype, C):
+    inp = synth.make_inputs(1, 400, 2, dk, dv, dtype=dtype, gate="scalar", chunk=C,
+                            seed=46, s0_std=0.1)
+    check(inp, name=f"segmented_phi_halves dk={dk} dv={dv}", seg_chunks=2)
+
+
 @pytest.mark.parametrize("gate", ["scalar", "none", "channel"])
 def test_segmented_varlen(gpu_lib, gate):
     inp = synth.make_inputs(1, 0, 2, 128, 64, dtype=torch.bfloat16, gate=gate,
