@@ -2043,6 +2043,9 @@ void fwd_trans_kernel(
           if (DK == 16) io<IO>::store(img, off + t + 4, 0.f);  // K slots past DK
         }
       if constexpr (STAGE) {
+        // the lanes read what other lanes wrote: keep the compiler from
+        // moving a lane's reads above its own writes
+        __builtin_amdgcn_wave_barrier();
         // lane's own half (both halves when DK = 16: the second is zero)
         constexpr int HB = DK == 16 ? FB : FB / 2;
         const int hoff = DK == 16 ? 0 : half * (FB / 2);
