@@ -17,7 +17,7 @@ import torch
 import gated_delta_rule_79_amd as gdn
 import oracle
 from gated_delta_rule_79_amd import synth
-from gpu_util import TOL, log, np64, slice_err, state_err
+from gpu_util import TOL, log, np64, par_map, slice_err, state_err
 
 pytestmark = pytest.mark.gpu
 
@@ -136,3 +136,59 @@ def test_block_backward_through_the_prologues(gpu_lib, gate, dtype):
     log("    " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()))
     for k_, v_ in errs.items():
         assert v_ < TOL[dtype], (k_, v_)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_block_backward_training_batch_all_heads(gpu_lib, gate):
+    # the packed training batch (16384 tokens in sequences of 512 to 8192,
+    # H16, dk128, dv256, bf16) through the block backward: every head's
+    # projection and tap gradients and the gate and state gradients against
+    # the oracle's composed adjoints (run head by head in forked workers)
+    H, dk, dv, W = 16, 128, 256, 4
+    inp = synth.make_inputs(1, 16384, H, dk, dv, dtype=torch.bfloat16, gate=gate, chunk=64,
+                            seed=317, varlen=(16384, 512, 8192), s0_std=0.05, with_do=True,
+                            with_ds=True)
+    cu = inp.cu_seqlens.numpy()
+    r = np.random.Generator(np.random.PCG64(318))
+    T = inp.q.shape[1]
+    xs = [torch.from_numpy(2.0 * r.standard_normal((1, T, H, d))).to(torch.bfloat16)
+          for d in (dk, dk, dv)]
+    wq, wk, wv = synth.conv_taps(H, dk, dv, W, 319)
+    log(f"[prologue] block backward, packed training batch, gate={gate}, lengths="
+        f"{np.diff(cu).tolist()}")
+    d = inp.to("cuda")
+    got = gdn.chunk_bwd_conv(*(x.cuda() for x in xs), wq.cuda(), wk.cuda(), wv.cuda(),
+                             d.beta, d.log_alpha, d.s0, d.do, d.ds_final, chunk=64,
+                             cu_seqlens=d.cu_seqlens)
+    torch.cuda.synchronize()
+    g = [None if x is None else np64(x) for x in got]
+    f = inp.f64
+    xf = [x.double().numpy() for x in xs]
+    tf = [w.double().numpy() for w in (wq, wk, wv)]
+
+    def job(h):
+        hs = slice(h, h + 1)
+        sub = lambda a: a[:, :, hs]
+        q = oracle.conv_prologue(sub(xf[0]), tf[0][hs], True, cu)
+        k = oracle.conv_prologue(sub(xf[1]), tf[1][hs], True, cu)
+        v = oracle.conv_prologue(sub(xf[2]), tf[2][hs], False, cu)
+        dq, dkk, dvv, db, dla, ds0 = oracle.gdn_bwd(
+            q, k, v, sub(f["beta"]), sub(f["log_alpha"]), f["s0"][:, hs], sub(f["do"]),
+            f["ds_final"][:, hs], gate, cu_seqlens=cu)
+        dxq, dwq = oracle.conv_prologue_bwd(sub(xf[0]), tf[0][hs], True, dq, cu)
+        dxk, dwk = oracle.conv_prologue_bwd(sub(xf[1]), tf[1][hs], True, dkk, cu)
+        dxv, dwv = oracle.conv_prologue_bwd(sub(xf[2]), tf[2][hs], False, dvv, cu)
+        la = sub(g[7])
+        errs = {"dxq": slice_err(sub(g[0]), dxq, cu), "dxk": slice_err(sub(g[1]), dxk, cu),
+                "dxv": slice_err(sub(g[2]), dxv, cu), "dwq": taps_err(g[3][hs], dwq),
+                "dwk": taps_err(g[4][hs], dwk), "dwv": taps_err(g[5][hs], dwv),
+                "dbeta": slice_err(sub(g[6])[..., None], db[..., None], cu),
+                "dlog_alpha": slice_err(la if la.ndim == 4 else la[..., None],
+                                        dla if dla.ndim == 4 else dla[..., None], cu),
+                "ds0": state_err(g[8][:, hs], ds0)}
+        return h, errs
+
+    for h, errs in par_map(job, range(H)):
+        log(f"    head {h}: " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()))
+        for k_, v_ in errs.items():
+            assert v_ < TOL[torch.bfloat16], (h, k_, v_)
