@@ -122,6 +122,32 @@ def test_headline_shape_all_heads(gpu_lib):
         assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16], (h, eo, es)
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_training_batch_all_heads(gpu_lib, gate):
+    # the packed training batch (16384 tokens in sequences of 512 to 8192,
+    # H16, dk128, dv256, bf16) with separate erase and write strengths:
+    # every head against the oracle
+    inp = synth.make_gdn2_inputs(1, 16384, 16, 128, 256, dtype=torch.bfloat16, gate=gate,
+                                 chunk=64, seed=99, varlen=(16384, 512, 8192), s0_std=0.05)
+    cu = inp.cu_seqlens.numpy()
+    log(f"[gdn2] packed training batch gate={gate} lengths={np.diff(cu).tolist()}")
+    o, sf = run(inp)
+    f = inp.f64
+    xo, xs = np64(o), np64(sf)
+
+    def job(h):
+        hs = slice(h, h + 1)
+        sub = lambda a: a[:, :, hs]
+        o_ref, s_ref = oracle.gdn2_fwd(sub(f["q"]), sub(f["k"]), sub(f["v"]), sub(f["beta"]),
+                                       sub(f["write"]), sub(f["log_alpha"]), f["s0"][:, hs],
+                                       gate, cu_seqlens=cu)
+        return h, slice_err(xo[:, :, hs], o_ref, cu), state_err(xs[:, hs], s_ref)
+
+    for h, eo, es in par_map(job, range(16)):
+        log(f"    head {h}: err o={eo:.3e} s={es:.3e}")
+        assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16], (h, eo, es)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("gate", ["scalar", "none", "channel"])
 def test_decode(gpu_lib, dtype, gate):

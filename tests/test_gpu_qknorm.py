@@ -86,6 +86,37 @@ def test_qknorm_headline_full_size(gpu_lib):
     check(inp, name="t4096_h16")
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_qknorm_training_batch_all_heads(gpu_lib, gate):
+    # the packed training batch (16384 tokens in sequences of 512 to 8192,
+    # H16, dk128, dv256, bf16) with raw q, k rows: the scalar gate
+    # normalises inside the prep, the per-channel gate through the prologue
+    # pass; every head against the oracle
+    inp = synth.make_inputs(1, 16384, 16, 128, 256, dtype=torch.bfloat16, gate=gate,
+                            chunk=64, seed=79, varlen=(16384, 512, 8192), s0_std=0.05,
+                            raw_qk=RAW)
+    cu = inp.cu_seqlens.numpy()
+    log(f"[qknorm] packed training batch gate={gate} lengths={np.diff(cu).tolist()}")
+    d = dev(inp)
+    o, sf = gdn.chunk_fwd(d.q, d.k, d.v, d.beta, d.log_alpha, d.s0, chunk=64,
+                          cu_seqlens=d.cu_seqlens, qk_l2norm=True)
+    torch.cuda.synchronize()
+    f = inp.f64
+    xo, xs = np64(o), np64(sf)
+
+    def job(h):
+        hs = slice(h, h + 1)
+        sub = lambda a: a[:, :, hs]
+        o_ref, s_ref = oracle.gdn_fwd_qknorm(sub(f["q"]), sub(f["k"]), sub(f["v"]),
+                                             sub(f["beta"]), sub(f["log_alpha"]),
+                                             f["s0"][:, hs], gate, cu_seqlens=cu)
+        return h, slice_err(xo[:, :, hs], o_ref, cu), state_err(xs[:, hs], s_ref)
+
+    for h, eo, es in par_map(job, range(16)):
+        log(f"    head {h}: err o={eo:.3e} s={es:.3e}")
+        assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16], (h, eo, es)
+
+
 def test_qknorm_of_unit_rows_is_the_plain_forward(gpu_lib):
     # rows that are already unit vectors: the same result as gdn_chunk_fwd up
     # to the rounding of the norm
