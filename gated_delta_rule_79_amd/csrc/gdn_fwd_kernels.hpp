@@ -2123,6 +2123,10 @@ void fwd_scan_kernel(
   using E = typename io<IO>::storage;
   __shared__ __attribute__((aligned(16))) char sA[L::BYTES];
   __shared__ __attribute__((aligned(16))) char sB[DB ? L::BYTES : 16];
+  // bf16 chunk-start states: each wave's [DK][16] slab image, so that the
+  // states leave as 16-byte row pieces
+  constexpr bool STG = STATES && DB;
+  __shared__ __attribute__((aligned(16))) __bf16 sStg[STG ? NW * DK * 16 : 8];
 
   const int ndvt = dv / 16;
   const int ngrp = (ndvt + GS - 1) / GS;
@@ -2223,13 +2227,39 @@ void fwd_scan_kernel(
 #pragma unroll
       for (int s = 0; s < SPW; ++s) {
         if (!own[s]) continue;
-        const int col = 16 * (vt0 + s) + l16;
+        if constexpr (STG) {
+          // the slab through the wave's LDS image: a lane holds 4 rows of
+          // one column per row tile, a store wants 8 columns of one row
+          // (32 two-byte stores per lane and chunk before: the state pass of
+          // the 16k backward batch 271 -> 246 us)
+          __bf16* img = sStg + wave * DK * 16;
 #pragma unroll
-        for (int a = 0; a < NDT; ++a)
+          for (int a = 0; a < NDT; ++a)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            io<IO>::store(states, st0 + static_cast<int64_t>(16 * a + 4 * lg + e) * dv + col,
-                          M[s][a][e]);
+            for (int e = 0; e < 4; ++e)
+              img[(16 * a + 4 * lg + e) * 16 + l16] = static_cast<__bf16>(M[s][a][e]);
+          // the lanes read what other lanes of the wave wrote (a wave's LDS
+          // accesses complete in order; this keeps the compiler's order too)
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int it = 0; it < (2 * DK + 63) / 64; ++it) {
+            const int pc = 64 * it + lane, r = pc >> 1, hh = pc & 1;
+            if (pc < 2 * DK)
+              *reinterpret_cast<uint4*>(static_cast<char*>(states) +
+                                        (st0 + static_cast<int64_t>(r) * dv + 16 * (vt0 + s) +
+                                         8 * hh) * 2) =
+                  *reinterpret_cast<const uint4*>(img + r * 16 + 8 * hh);
+          }
+          __builtin_amdgcn_wave_barrier();
+        } else {
+          const int col = 16 * (vt0 + s) + l16;
+#pragma unroll
+          for (int a = 0; a < NDT; ++a)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              io<IO>::store(states, st0 + static_cast<int64_t>(16 * a + 4 * lg + e) * dv + col,
+                            M[s][a][e]);
+        }
       }
     }
     opvec<OP> Mb[SPW][NKD], Eb[SPW][NKC];
